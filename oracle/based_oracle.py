@@ -1,0 +1,274 @@
+"""fp64 CPU oracle for the Based sequence-mixing layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check in ``__graft_entry__`` and
+the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+HIP kernels and imports nothing from the GPU package; it takes plain arrays
+and returns plain fp64 NumPy arrays.
+
+Sources (the web pages that describe the method):
+
+* [README]  "based" -- HazyResearch/based project README (Chinese translation
+  on dongaigc.com), introduction: Based combines a short sliding-window
+  softmax attention (window 64, exact softmax locally) with a dense, global
+  linear attention that approximates softmax for all other tokens.
+* [BLOG]    "Базированная модель, часть 2" (Telegram channel botka_chronics),
+  the paragraph on linear attention and the feature-map pseudocode after it:
+  exp(q.k) is replaced by its 2nd-order Taylor expansion 1 + qk + (qk)^2/2,
+  realised as a dot product of feature vectors [1, x, x x^T / sqrt(2)], where
+  the quadratic block lists every ordered pair (x_a x_b for a, then b).
+  The paragraph on the state: the recurrent form keeps a KV-state for the
+  numerator and a K-state for the denominator of the softmax simulation.
+* [TRAIN]   HazyResearch/based ``train/`` README, "training views": the
+  quadratic PyTorch view, the flash-linear-attention kernel and the
+  fast-transformers kernel are interchangeable implementations of one
+  computation (here: the quadratic, recurrent and chunked forms below).
+
+Readings where the pages are silent (all listed in the design doc as well):
+
+* no temperature inside phi; the inputs carry whatever scale they have;
+* causal means inclusive (j <= i), for both attentions;
+* the window holds ``window`` keys including the query's own position;
+* linear attention is normalised (numerator / denominator) with no epsilon:
+  every kernel value 1 + x + x^2/2 = ((1 + x)^2 + 1)/2 is at least 1/2, so the
+  denominator of row i is at least (i + 1)/2;
+* the window softmax uses scale * q.k with a caller-given scale (1.0 in the
+  workloads), the exact exponential that the Taylor map approximates;
+* linear attention and window attention are two separate outputs.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+closed forms, invariants, textbook special cases, SciPy's softmax and
+hand-derived fixtures in ``tests/golden/``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+D_K = 16
+D_PHI = 1 + D_K + D_K * D_K  # 273 Taylor features for d_k = 16
+
+_INV_SQRT2 = 1.0 / np.sqrt(2.0)
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of whatever the caller holds (fp32, bf16 via torch, fp64)."""
+    if hasattr(x, "detach"):  # torch tensor: widen on the torch side, exactly
+        import torch
+
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Feature map  [BLOG, feature-map pseudocode]
+# --------------------------------------------------------------------------
+def phi(x) -> np.ndarray:
+    """Second-order Taylor feature map, applied along the last axis.
+
+    phi(x) = [1, x_1..x_d, (x_a * x_b / sqrt(2) for a in 1..d for b in 1..d)],
+    i.e. the constant, the linear block, then every ordered pair with the
+    first index outermost.  Length 1 + d + d^2 (273 for d = 16).  Feature
+    index of x_a x_b / sqrt(2) is 1 + d + d*a + b (0-based a, b).
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    lead = x.shape[:-1]
+    quad = (x[..., :, None] * x[..., None, :]).reshape(lead + (d * d,)) * _INV_SQRT2
+    return np.concatenate([np.ones(lead + (1,)), x, quad], axis=-1)
+
+
+def taylor_kernel(s) -> np.ndarray:
+    """1 + s + s^2/2: the 2nd-order Taylor expansion of exp(s) [BLOG]."""
+    s = _f64(s)
+    return 1.0 + s + 0.5 * s * s
+
+
+# --------------------------------------------------------------------------
+# Causal linear attention  [README intro; BLOG linear-attention paragraph]
+# --------------------------------------------------------------------------
+def linattn_quadratic(q, k, v, kernel: str = "features"):
+    """Quadratic masked form, the definition of record.
+
+    y_i = sum_{j<=i} K(q_i, k_j) v_j / sum_{j<=i} K(q_i, k_j), computed per
+    (batch, head) from the full L x L kernel matrix with the upper triangle
+    zeroed.  ``kernel="features"`` forms K as the 273-dim dot product
+    phi(q_i).phi(k_j); ``kernel="taylor"`` forms it as 1 + x + x^2/2 with
+    x = q_i.k_j.  Returns (y, den) with den[..., i] the denominator.
+    Shapes: q, k [..., L, d_k]; v [..., L, d_v].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if kernel == "features":
+        A = phi(q) @ np.swapaxes(phi(k), -1, -2)
+    elif kernel == "taylor":
+        A = taylor_kernel(q @ np.swapaxes(k, -1, -2))
+    else:
+        raise ValueError(kernel)
+    L = q.shape[-2]
+    A = A * np.tril(np.ones((L, L)))
+    den = A.sum(axis=-1)
+    y = (A @ v) / den[..., None]
+    return y, den
+
+
+def linattn_recurrent(q, k, v, S0=None, z0=None):
+    """Recurrent (constant-state) form [BLOG, paragraph on the state].
+
+    Start from S = S0 (273 x d_v, zero if None) and z = z0 (273, zero if
+    None).  For i = 0..L-1: S += phi(k_i) v_i^T; z += phi(k_i);
+    y_i = phi(q_i)^T S / phi(q_i)^T z.  Returns (y, den, S, z).
+    A pure Python loop over positions: meant for short L.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    L, dv = q.shape[-2], v.shape[-1]
+    S = np.zeros(lead + (D_PHI, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (D_PHI,)) if z0 is None else _f64(z0).copy()
+    pq, pk = phi(q), phi(k)
+    y = np.empty(lead + (L, dv))
+    den = np.empty(lead + (L,))
+    for i in range(L):
+        S += pk[..., i, :, None] * v[..., i, None, :]
+        z += pk[..., i, :]
+        num = np.einsum("...f,...fd->...d", pq[..., i, :], S)
+        den[..., i] = np.einsum("...f,...f->...", pq[..., i, :], z)
+        y[..., i, :] = num / den[..., i, None]
+    return y, den, S, z
+
+
+def linattn_chunked(q, k, v, chunk: int, S0=None, z0=None):
+    """Chunked form: per chunk, the in-chunk masked quadratic term plus a
+    readout of the state accumulated over all earlier chunks, then the
+    state update [TRAIN, training views: the chunked kernels compute the
+    same result as the quadratic view].
+
+    For a chunk c of positions P: num_i = phi(q_i)^T S + sum_{j in P, j<=i}
+    (phi(q_i).phi(k_j)) v_j, den_i likewise with z and 1, and then
+    S += phi(K_P)^T V_P, z += sum_{j in P} phi(k_j).  Returns (y, den, S, z).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    L, dv = q.shape[-2], v.shape[-1]
+    S = np.zeros(lead + (D_PHI, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (D_PHI,)) if z0 is None else _f64(z0).copy()
+    y = np.empty(lead + (L, dv))
+    den = np.empty(lead + (L,))
+    for c0 in range(0, L, chunk):
+        c1 = min(L, c0 + chunk)
+        pq, pk, vc = phi(q[..., c0:c1, :]), phi(k[..., c0:c1, :]), v[..., c0:c1, :]
+        n = c1 - c0
+        A = (pq @ np.swapaxes(pk, -1, -2)) * np.tril(np.ones((n, n)))
+        num = pq @ S + A @ vc
+        dn = pq @ z[..., :, None]
+        dn = dn[..., 0] + A.sum(axis=-1)
+        y[..., c0:c1, :] = num / dn[..., None]
+        den[..., c0:c1] = dn
+        S = S + np.swapaxes(pk, -1, -2) @ vc
+        z = z + pk.sum(axis=-2)
+    return y, den, S, z
+
+
+def linattn_state(k, v):
+    """Final state after a sequence: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j)
+    [BLOG, paragraph on the state].  Shapes [..., 273, d_v] and [..., 273]."""
+    pk, v = phi(k), _f64(v)
+    return np.swapaxes(pk, -1, -2) @ v, pk.sum(axis=-2)
+
+
+# --------------------------------------------------------------------------
+# Sliding-window softmax attention  [README intro]
+# --------------------------------------------------------------------------
+def swa(q, k, v, window: int = 64, scale: float = 1.0, weight: str = "exp"):
+    """Causal sliding-window attention.
+
+    Row i attends to keys j with max(0, i - window + 1) <= j <= i (``window``
+    keys including itself).  With s_j = scale * q_i.k_j:
+    ``weight="exp"``: p_j = exp(s_j - max_j s_j) and y_i = sum p_j v_j / sum p_j,
+    the exact softmax; ``weight="taylor"``: p_j = 1 + s_j + s_j^2/2 (no max
+    shift: the Taylor weights are not shift-invariant), which ties this
+    function to the linear attention when the window covers the sequence.
+    Vectorised over rows with a (L, window) band of key indices.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    L = q.shape[-2]
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    idx = np.arange(L)[:, None] - (window - 1) + np.arange(window)[None, :]  # (L, W)
+    valid = idx >= 0
+    idxc = np.where(valid, idx, 0)
+    kb = k[..., idxc, :]  # [..., L, W, d]
+    vb = v[..., idxc, :]
+    s = scale * np.einsum("...ld,...lwd->...lw", q, kb)
+    if weight == "exp":
+        s = np.where(valid, s, -np.inf)
+        m = s.max(axis=-1, keepdims=True)
+        p = np.exp(s - m)
+    elif weight == "taylor":
+        p = np.where(valid, taylor_kernel(s), 0.0)
+    else:
+        raise ValueError(weight)
+    return np.einsum("...lw,...lwd->...ld", p, vb) / p.sum(axis=-1)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Recurrent decode  [BLOG, paragraph on the state; README intro]
+# --------------------------------------------------------------------------
+class DecodeState:
+    """Generation state of one Based layer for B sequences x H heads.
+
+    S [B,H,273,d_v] and z [B,H,273] (the KV-state and K-state), a ring of the
+    last ``window`` keys/values [B,H,window,d] where position t lives in slot
+    t mod window, and t [B], the index of the next token of each sequence.
+    """
+
+    def __init__(self, S, z, ring_k, ring_v, t):
+        self.S = _f64(S).copy()
+        self.z = _f64(z).copy()
+        self.ring_k = _f64(ring_k).copy()
+        self.ring_v = _f64(ring_v).copy()
+        self.t = np.asarray(t, dtype=np.int64).copy()
+        self.window = self.ring_k.shape[-2]
+
+    @classmethod
+    def prefill(cls, k, v, window: int = 64):
+        """State after consuming a context k, v [B,H,n,.] (all sequences n long)."""
+        k, v = _f64(k), _f64(v)
+        B, H, n, _ = k.shape
+        S, z = linattn_state(k, v)
+        rk = np.zeros((B, H, window, k.shape[-1]))
+        rv = np.zeros((B, H, window, v.shape[-1]))
+        for t in range(max(0, n - window), n):
+            rk[:, :, t % window] = k[:, :, t]
+            rv[:, :, t % window] = v[:, :, t]
+        return cls(S, z, rk, rv, np.full(B, n))
+
+    def step(self, q, k, v, scale: float = 1.0):
+        """Consume one token per sequence: q, k [B,H,d_k], v [B,H,d_v].
+
+        The state is updated with (k, v) first, so the token attends to
+        itself; y_lin = phi(q)^T S / phi(q)^T z; (k, v) goes to ring slot
+        t mod window; y_swa is the exact softmax over positions
+        max(0, t - window + 1) .. t held in the ring.  Returns (y_lin, y_swa).
+        """
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        pk, pq = phi(k), phi(q)
+        self.S += pk[..., :, None] * v[..., None, :]
+        self.z += pk
+        num = np.einsum("bhf,bhfd->bhd", pq, self.S)
+        den = np.einsum("bhf,bhf->bh", pq, self.z)
+        y_lin = num / den[..., None]
+        W = self.window
+        B = q.shape[0]
+        y_swa = np.empty_like(y_lin)
+        for b in range(B):
+            t = int(self.t[b])
+            self.ring_k[b, :, t % W] = k[b]
+            self.ring_v[b, :, t % W] = v[b]
+            slots = [p % W for p in range(max(0, t - W + 1), t + 1)]
+            kb = self.ring_k[b][:, slots]  # [H, n, d_k]
+            vb = self.ring_v[b][:, slots]
+            s = scale * np.einsum("hd,hnd->hn", q[b], kb)
+            p = np.exp(s - s.max(axis=-1, keepdims=True))
+            y_swa[b] = np.einsum("hn,hnd->hd", p, vb) / p.sum(axis=-1)[:, None]
+        self.t += 1
+        return y_lin, y_swa

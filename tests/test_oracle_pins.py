@@ -1,0 +1,264 @@
+"""Pins for the fp64 oracle: closed forms, invariants, textbook special cases,
+SciPy's softmax, brute force and hand-worked fixtures.  None of these re-types
+the oracle's own formulas; each is chosen so that a plausible slip (a dropped
+term, a wrong sign, an off-by-one in the causal mask or the window, a wrong
+feature scale, a transposed operand) fails at least one of them."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import based_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def rand(*shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def e(axis, d=16):
+    x = np.zeros(d)
+    x[axis] = 1.0
+    return x
+
+
+# ---------------------------------------------------------------- feature map
+def test_phi_shape_and_layout():
+    x = rand(16)
+    p = O.phi(x)
+    assert p.shape == (273,)
+    assert p[0] == 1.0
+    np.testing.assert_array_equal(p[1:17], x)
+    # quadratic block: index 17 + 16 a + b holds x_a x_b / sqrt 2
+    for a, b in [(0, 0), (0, 15), (15, 0), (3, 7), (7, 3), (15, 15)]:
+        assert p[17 + 16 * a + b] == pytest.approx(x[a] * x[b] / np.sqrt(2), rel=1e-15)
+
+
+def test_phi_dot_is_taylor_closed_form():
+    """phi(q).phi(k) = 1 + s + s^2/2 with s = q.k (blog pseudocode, last line)."""
+    for _ in range(50):
+        q, k = rand(16, scale=0.7), rand(16, scale=0.7)
+        s = float(q @ k)
+        got = float(O.phi(q) @ O.phi(k))
+        assert got == pytest.approx(1 + s + s * s / 2, rel=1e-14)
+
+
+@pytest.mark.parametrize(
+    "q,k,want",
+    [
+        (np.zeros(16), rand(16), 1.0),  # q = 0 -> only the constant feature
+        (e(0), e(0), 2.5),  # s = 1
+        (e(0), -e(0), 0.5),  # s = -1: the minimum of 1 + s + s^2/2
+        (e(0) + e(5), e(0) + e(5), 5.0),  # s = 2
+        (e(2), e(9), 1.0),  # orthogonal
+    ],
+)
+def test_phi_special_values(q, k, want):
+    assert float(O.phi(q) @ O.phi(k)) == pytest.approx(want, rel=1e-15)
+
+
+def test_taylor_kernel_lower_bound():
+    s = np.linspace(-10, 10, 2001)
+    w = O.taylor_kernel(s)
+    assert w.min() == pytest.approx(0.5)
+    assert s[np.argmin(w)] == pytest.approx(-1.0)
+    np.testing.assert_allclose(w, ((1 + s) ** 2 + 1) / 2, rtol=1e-14)
+
+
+# ------------------------------------------------------- linear attention forms
+def _tiny(B=2, H=3, L=37, dv=5, s=0.4):
+    return rand(B, H, L, 16, scale=s), rand(B, H, L, 16, scale=s), rand(B, H, L, dv)
+
+
+def test_golden_hand_example():
+    g = json.load(open(os.path.join(GOLD, "linattn_hand.json")))
+    q = np.array([e(0) * a for a in g["q_axis0"]])[None, None]
+    k = np.array([e(0) * a for a in g["k_axis0"]])[None, None]
+    v = np.array(g["v"])[None, None]
+    for kern in ("features", "taylor"):
+        y, den = O.linattn_quadratic(q, k, v, kernel=kern)
+        np.testing.assert_allclose(y[0, 0], g["y"], rtol=1e-15, atol=1e-15)
+        np.testing.assert_allclose(den[0, 0], g["den"], rtol=1e-15)
+    y, den, S, z = O.linattn_recurrent(q, k, v)
+    np.testing.assert_allclose(y[0, 0], g["y"], rtol=1e-15, atol=1e-15)
+    for row, val in g["S_rows"].items():
+        np.testing.assert_allclose(S[0, 0, int(row)], val, rtol=1e-15)
+    for row, val in g["z_rows"].items():
+        assert z[0, 0, int(row)] == pytest.approx(val, abs=1e-15)
+    others = [r for r in range(273) if str(r) not in g["S_rows"]]
+    assert np.all(S[0, 0, others] == 0)
+    assert np.all(z[0, 0, [r for r in range(273) if str(r) not in g["z_rows"]]] == 0)
+
+
+def test_forms_agree():
+    q, k, v = _tiny()
+    yf, denf = O.linattn_quadratic(q, k, v, kernel="features")
+    yt, dent = O.linattn_quadratic(q, k, v, kernel="taylor")
+    yr, denr, S, z = O.linattn_recurrent(q, k, v)
+    np.testing.assert_allclose(yt, yf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(yr, yf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(denr, denf, rtol=1e-12)
+    L = q.shape[-2]
+    for C in (1, 7, 16, 64, L):
+        yc, denc, Sc, zc = O.linattn_chunked(q, k, v, C)
+        np.testing.assert_allclose(yc, yf, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Sc, S, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(zc, z, rtol=1e-12, atol=1e-12)
+
+
+def test_state_matches_recurrence():
+    q, k, v = _tiny(L=23)
+    _, _, S, z = O.linattn_recurrent(q, k, v)
+    S2, z2 = O.linattn_state(k, v)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z2, z, rtol=1e-12, atol=1e-12)
+    # z's constant row counts tokens exactly; its linear rows are sums of k
+    assert np.all(z2[..., 0] == 23)
+    np.testing.assert_allclose(z2[..., 1:17], k.sum(axis=-2), rtol=1e-12, atol=1e-12)
+
+
+def test_resume_from_state():
+    """Running on a prefix, then continuing from its state, equals one run."""
+    q, k, v = _tiny(L=40)
+    y, _, S, z = O.linattn_chunked(q, k, v, 8)
+    _, _, S1, z1 = O.linattn_chunked(q[..., :17, :], k[..., :17, :], v[..., :17, :], 5)
+    y2, _, S2, z2 = O.linattn_chunked(q[..., 17:, :], k[..., 17:, :], v[..., 17:, :], 6, S1, z1)
+    np.testing.assert_allclose(y2, y[..., 17:, :], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+
+
+def test_denominator_lower_bound():
+    """Each kernel value is >= 1/2, so den_i >= (i+1)/2 > 0; no epsilon needed."""
+    q, k, v = _tiny(L=64, s=1.5)
+    _, den = O.linattn_quadratic(q, k, v, kernel="taylor")
+    i = np.arange(64)
+    assert np.all(den >= (i + 1) / 2 - 1e-12)
+    # adversarial: q.k = -1 for every pair gives exactly (i+1)/2
+    qa = np.broadcast_to(e(0), (1, 1, 8, 16))
+    ka = np.broadcast_to(-e(0), (1, 1, 8, 16))
+    _, den = O.linattn_quadratic(qa, ka, rand(1, 1, 8, 3), kernel="features")
+    np.testing.assert_allclose(den[0, 0], (np.arange(8) + 1) / 2, rtol=1e-15)
+
+
+def test_zero_query_gives_cumulative_mean():
+    """q = 0: every kernel value is 1, so y_i is the mean of v_0..v_i."""
+    _, k, v = _tiny(L=30)
+    q = np.zeros_like(k)
+    want = np.cumsum(v, axis=-2) / np.arange(1, 31)[:, None]
+    for fn in (lambda: O.linattn_quadratic(q, k, v)[0], lambda: O.linattn_chunked(q, k, v, 7)[0]):
+        np.testing.assert_allclose(fn(), want, rtol=1e-12, atol=1e-13)
+    # and likewise for k = 0
+    np.testing.assert_allclose(O.linattn_recurrent(k, q, v)[0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_normalisation_properties():
+    q, k, v = _tiny()
+    y, _ = O.linattn_quadratic(q, k, v)
+    # constant values pass through, weights sum to one
+    c = np.full_like(v, 3.25)
+    np.testing.assert_allclose(O.linattn_quadratic(q, k, c)[0], c, rtol=1e-13)
+    # affine equivariance in v
+    y2, _ = O.linattn_quadratic(q, k, -2.0 * v + 0.5)
+    np.testing.assert_allclose(y2, -2.0 * y + 0.5, rtol=1e-12, atol=1e-12)
+    # L = 1: y_0 = v_0
+    np.testing.assert_allclose(O.linattn_quadratic(q[..., :1, :], k[..., :1, :], v[..., :1, :])[0], v[..., :1, :], rtol=1e-14)
+    # permuting batch/head permutes outputs
+    perm = [2, 0, 1]
+    np.testing.assert_allclose(O.linattn_quadratic(q[:, perm], k[:, perm], v[:, perm])[0], y[:, perm], rtol=1e-14)
+
+
+def test_causality():
+    """Changing token t changes no output before t (and does change row t)."""
+    q, k, v = _tiny(L=20)
+    y, _ = O.linattn_quadratic(q, k, v)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[..., 11, :] += 1.0
+    k2[..., 11, :] -= 1.0
+    v2[..., 11, :] += 5.0
+    ya, _ = O.linattn_quadratic(q2, k2, v2)
+    np.testing.assert_array_equal(ya[..., :11, :], y[..., :11, :])
+    assert np.all(np.abs(ya[..., 11, :] - y[..., 11, :]).max(axis=-1) > 1e-3)
+
+
+# --------------------------------------------------------- sliding window attn
+def _swa_bruteforce(q, k, v, window, scale):
+    """Full L x L score matrix, -inf outside the band, SciPy softmax rows."""
+    L = q.shape[-2]
+    s = scale * q @ np.swapaxes(k, -1, -2)
+    i, j = np.arange(L)[:, None], np.arange(L)[None, :]
+    band = (j <= i) & (j > i - window)
+    s = np.where(band, s, -np.inf)
+    return scipy.special.softmax(s, axis=-1) @ v
+
+
+@pytest.mark.parametrize("L,window,scale", [(1, 64, 1.0), (50, 64, 1.0), (130, 64, 1.0), (130, 17, 0.7), (70, 1, 1.0), (9, 200, 2.0)])
+def test_swa_matches_scipy_softmax(L, window, scale):
+    q, k, v = rand(2, 2, L, 16), rand(2, 2, L, 16), rand(2, 2, L, 7)
+    np.testing.assert_allclose(O.swa(q, k, v, window, scale), _swa_bruteforce(q, k, v, window, scale), rtol=1e-12, atol=1e-13)
+
+
+def test_swa_golden_hand_example():
+    g = json.load(open(os.path.join(GOLD, "swa_hand.json")))
+    q = np.array([e(0)] * 3)[None, None]
+    k = np.array([e(0) * c for c in g["k_axis0"]])[None, None]
+    v = np.array(g["v"])[None, None]
+    np.testing.assert_allclose(O.swa(q, k, v, g["window"])[0, 0], g["y"], rtol=1e-14, atol=1e-15)
+
+
+def test_swa_special_cases():
+    q, k, v = rand(1, 2, 90, 16), rand(1, 2, 90, 16), rand(1, 2, 90, 4)
+    # window 1: each row sees only itself
+    np.testing.assert_allclose(O.swa(q, k, v, 1), v, rtol=1e-14)
+    # q = 0: uniform weights over the last min(i+1, W) rows -> sliding mean
+    W = 64
+    cs = np.concatenate([np.zeros((1, 2, 1, 4)), np.cumsum(v, axis=-2)], axis=-2)
+    i = np.arange(90)
+    lo = np.maximum(0, i - W + 1)
+    want = (cs[..., i + 1, :] - cs[..., lo, :]) / (i + 1 - lo)[:, None]
+    np.testing.assert_allclose(O.swa(np.zeros_like(q), k, v, W), want, rtol=1e-11, atol=1e-12)
+    # huge scores stay finite (max-shifted softmax)
+    y = O.swa(q * 40, k * 40, v, W)
+    assert np.all(np.isfinite(y))
+
+
+def test_swa_taylor_weights_tie_to_linear_attention():
+    """With weights 1 + s + s^2/2 and a window covering the sequence, the window
+    attention is the causal Taylor linear attention."""
+    q, k, v = _tiny(L=45)
+    np.testing.assert_allclose(O.swa(q, k, v, window=45, weight="taylor"), O.linattn_quadratic(q, k, v)[0], rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------- decode
+def test_decode_matches_forward():
+    B, H, n, steps, dv, W = 2, 3, 70, 75, 6, 64
+    q, k, v = rand(B, H, n + steps, 16, scale=0.5), rand(B, H, n + steps, 16, scale=0.5), rand(B, H, n + steps, dv)
+    st = O.DecodeState.prefill(k[..., :n, :], v[..., :n, :], W)
+    assert np.all(st.t == n)
+    assert np.all(st.z[..., 0] == n)
+    y_lin_ref, _ = O.linattn_quadratic(q, k, v, kernel="taylor")
+    y_swa_ref = _swa_bruteforce(q, k, v, W, 1.0)
+    for s in range(steps):
+        yl, ys = st.step(q[..., n + s, :], k[..., n + s, :], v[..., n + s, :])
+        np.testing.assert_allclose(yl, y_lin_ref[..., n + s, :], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(ys, y_swa_ref[..., n + s, :], rtol=1e-11, atol=1e-12)
+    S, z = O.linattn_state(k, v)
+    np.testing.assert_allclose(st.S, S, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(st.z, z, rtol=1e-11, atol=1e-11)
+    assert np.all(st.t == n + steps)
+
+
+def test_decode_from_empty_context():
+    """Prefill of zero tokens; the first steps see fewer than W keys."""
+    B, H, steps, dv = 1, 2, 5, 3
+    q, k, v = rand(B, H, steps, 16), rand(B, H, steps, 16), rand(B, H, steps, dv)
+    st = O.DecodeState.prefill(k[..., :0, :], v[..., :0, :], 64)
+    yq, _ = O.linattn_quadratic(q, k, v)
+    for s in range(steps):
+        yl, ys = st.step(q[..., s, :], k[..., s, :], v[..., s, :])
+        np.testing.assert_allclose(yl, yq[..., s, :], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ys, _swa_bruteforce(q, k, v, 64, 1.0)[..., s, :], rtol=1e-12, atol=1e-13)
