@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the Based layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one layer forward over the 360M-shaped workload (B=8, H=16,
+L=2048, d_k=16, d_v=64, bf16 q/k/v, fp32 outputs): the causal Taylor linear
+attention (based_linattn_fwd) plus the window-64 softmax attention
+(based_swa_fwd) on the same inputs.  ``value`` is sequence positions per
+second (B*L per step; every position covers all 16 heads).
+
+Inputs are resident in HBM before timing starts.  Eight copies of the input
+set are cycled so that successive steps do not find their inputs in the
+256 MB last-level (Infinity) cache.  Kernels run on torch's current stream;
+per-kernel durations come from events recorded on that stream around every
+launch in the timed region.
+
+Also reported (same JSON line): the roofline of the dominant kernel, the other
+forward workloads (1.3B-shaped, 32k long-context), recurrent decode
+(256 sequences x 16 heads, 1000 steps) and the fp64 CPU oracle timed on a
+bounded sample of the step's workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6  # dense bf16 matrix peak
+METRIC = "Based layer fwd tokens/s @L=2k-32k + decode tokens/s; % MFMA/HBM roofline"
+
+D_PHI = 273
+
+
+def lin_bytes(dv, es=2):
+    """Algorithmic HBM bytes per (position, head) of the linear attention:
+    q, k, v read once, y (fp32) written once."""
+    return (2 * 16 + dv) * es + 4 * dv
+
+
+def lin_flops(dv):
+    """Algorithmic flops per (position, head): state update 2*D*dv, readout
+    2*D*dv, z update D, denominator 2*D (D = 273 Taylor features)."""
+    return 4 * D_PHI * dv + 3 * D_PHI
+
+
+def swa_bytes(dv, es=2):
+    return (2 * 16 + dv) * es + 4 * dv
+
+
+def decode_bytes(dv=64, window=64, es=2):
+    """Per head-step: S and z read + written (fp32), the ring's other
+    window-1 slots read, q/k/v read, one ring slot written, y_lin and y_swa written."""
+    return (2 * D_PHI * dv * 4 + 2 * D_PHI * 4 + (window - 1) * (16 + dv) * es + (2 * 16 + dv) * es
+            + (16 + dv) * es + 2 * dv * 4)
+
+
+class StreamTimer:
+    """Events on the current stream around every launch of each named kernel."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def mean_ms(self, name):
+        p = self.pairs[name]
+        return sum(s.elapsed_time(e) for s, e in p) / len(p)
+
+
+def bench_fwd(lal, cfg, steps, warmup, nbuf=8):
+    """Time `steps` layer forwards (linattn + swa); returns a dict."""
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    sets = []
+    for i in range(nbuf):
+        sets.append(tuple(t.to("cuda") for t in (q, k, v)))
+    B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
+    y_lin = torch.empty(B, H, L, dv, device="cuda")
+    y_swa = torch.empty(B, H, L, dv, device="cuda")
+    ws_bytes = lal.linattn_workspace_bytes(B, H, L, dv)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i, timer=None):
+        qq, kk, vv = sets[i % nbuf]
+        f1 = lambda: lal.linattn_fwd(qq, kk, vv, y=y_lin, workspace=ws)
+        f2 = lambda: lal.swa_fwd(qq, kk, vv, cfg.window, y=y_swa)
+        if timer is None:
+            f1()
+            f2()
+        else:
+            timer.run("linattn", f1)
+            timer.run("swa", f2)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    timer = StreamTimer()
+    t0.record()
+    for i in range(steps):
+        step(i, timer)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    tl, ts = timer.mean_ms("linattn"), timer.mean_ms("swa")
+    th = B * H * L
+    es = 2 if cfg.dtype == "bf16" else 4
+    lb, sb = lin_bytes(dv, es) * th, swa_bytes(dv, es) * th
+    return {
+        "workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
+        "dtype": cfg.dtype, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+        "linattn_us": tl * 1e3, "swa_us": ts * 1e3,
+        "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9,
+        "linattn_alg_tflops": lin_flops(dv) * th / (tl * 1e-3) / 1e12,
+        "linattn_bytes": lb, "swa_bytes": sb, "linattn_flops": lin_flops(dv) * th,
+    }
+
+
+def bench_decode(lal, cfg, warmup=5):
+    """Prefill (untimed), then cfg.steps decode steps timed as one block."""
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
+    _, _, st = lal.decode_init(qc.cuda(), kc.cuda(), vc.cuda(), cfg.window)
+    del qc, kc, vc
+    qd, kd, vd = qs.cuda(), ks.cuda(), vs.cuda()
+    B, H, dv = cfg.B, cfg.H, cfg.dv
+    y_lin = torch.empty(B, H, dv, device="cuda")
+    y_swa = torch.empty(B, H, dv, device="cuda")
+    for s in range(warmup):  # advances the state; the timed steps continue from it
+        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = cfg.steps - warmup
+    t0.record()
+    for s in range(warmup, cfg.steps):
+        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / n
+    byts = decode_bytes(dv, cfg.window) * B * H
+    return {
+        "workload": "decode", "sequences": B, "heads": H, "context": cfg.ctx, "steps_timed": n,
+        "us_per_step": us, "tokens_per_s": B / (us * 1e-6), "hbm_gbs": byts / (us * 1e-6) / 1e9,
+        "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": byts,
+    }
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 oracle (chunked linear attention + banded window softmax) on a
+    bounded sample of the step's heads, on this host's cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import based_oracle as O
+
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(heads) and time.perf_counter() - t0 < budget_s:
+        b, h = heads[done]
+        O.linattn_chunked(q[b, h], k[b, h], v[b, h], 64)
+        O.swa(q[b, h], k[b, h], v[b, h], cfg.window)
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    tok_heads_per_s = done * cfg.L / dt
+    return {
+        "value": tok_heads_per_s / cfg.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs of the step workload ({cfg.L} positions each), "
+                  f"fp64 chunked linear attention + banded window softmax, {dt:.1f} s; tokens/s = "
+                  f"position-heads/s / {cfg.H} heads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and decode")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(batch/head sharding of the layer needs no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import linear_attention_lm_amd as lal
+
+    cfg = synth.FWD_CONFIGS["based360m"]
+    main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
+    print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step, linattn {main_res['linattn_us']:.1f} us, "
+          f"swa {main_res['swa_us']:.1f} us", file=sys.stderr, flush=True)
+    extra, decode = [], None
+    if not args.no_extra:
+        for name in ("based1p3b", "long32k"):
+            r = bench_fwd(lal, synth.FWD_CONFIGS[name], max(10, args.steps // 2), args.warmup, nbuf=4)
+            extra.append(r)
+            print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        decode = bench_decode(lal, synth.DECODE_CONFIG)
+        print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu else cpu_baseline(cfg)
+
+    # dominant kernel of the step: the one with the larger share of the time
+    dom = "linattn" if main_res["linattn_us"] >= main_res["swa_us"] else "swa"
+    achieved = main_res[f"{dom}_hbm_gbs"]
+    out = {
+        "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q,k,v; no trained weights)",
+        "config": {"workload": "based360m layer fwd: linear attention + window-64 softmax attention",
+                   "B": cfg.B, "H": cfg.H, "L": cfg.L, "d_k": 16, "d_v": cfg.dv, "window": cfg.window,
+                   "inputs": "bf16", "outputs": "fp32"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "mfma_alg_frac": main_res["linattn_alg_tflops"] / MFMA_BF16_PEAK_TFS},
+        "kernels": {k: main_res[k] for k in ("linattn_us", "swa_us", "linattn_hbm_gbs", "swa_hbm_gbs",
+                                              "linattn_alg_tflops")},
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+        "decode": decode,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * based.h -- C ABI of the Based sequence-mixing layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer pairs two attentions over the same q, k, v (HazyResearch/based
+ * README, introduction):
+ *   - a global causal linear attention whose kernel is the 2nd-order Taylor
+ *     expansion of exp(q.k), realised by the feature map
+ *       phi(x) = [1, x_1..x_16, x_a x_b / sqrt(2) for a = 1..16, b = 1..16]
+ *     (273 features for d_k = 16; blog post "Базированная модель, часть 2",
+ *     feature-map pseudocode), normalised:
+ *       y_i = sum_{j<=i} phi(q_i).phi(k_j) v_j / sum_{j<=i} phi(q_i).phi(k_j);
+ *   - an exact softmax attention over a short causal sliding window (64).
+ * The recurrent form keeps a numerator KV-state S = sum_j phi(k_j) v_j^T and a
+ * denominator K-state z = sum_j phi(k_j) (same blog post, paragraph on the
+ * state); the decode entry point advances that state one token at a time.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are dense, row-major, [B, H, L, d] with d fastest (d = d_k, d_qk or
+ * d_v), base pointers 16-byte aligned, living in device memory of the current
+ * HIP device.  Inputs q, k, v have the element type `dtype`; outputs and
+ * states are fp32.  Causal means inclusive: row i sees positions j <= i.
+ *
+ * State layout (S_in, S_out, decode S: [B, H, 273, d_v]; z: [B, H, 273]):
+ * row 0 is the constant feature, row 1 + a the linear feature x_a, row
+ * 17 + 16 a + b the quadratic feature x_a x_b / sqrt(2) (a, b in 0..15).
+ * States written by this library are symmetric in (a, b).  A state read by
+ * this library enters every output only through S[ab] + S[ba].
+ *
+ * Ownership: the caller allocates and frees every buffer; the library never
+ * allocates, keeps no mutable global state and is re-entrant on distinct
+ * buffers.  All work is enqueued asynchronously on `stream` (a hipStream_t;
+ * NULL is the default stream); nothing synchronises and nothing copies
+ * between host and device.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a
+ * failed check returns a negative BASED_ERR_* code and touches no memory.
+ * A failed kernel launch returns BASED_ERR_HIP.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  NaN and Inf inputs are not
+ * checked; they propagate to the outputs they reach.
+ */
+#ifndef BASED_H
+#define BASED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BASED_ABI_VERSION 1
+
+/* element type of q, k, v (and of the decode ring buffers) */
+enum {
+  BASED_F32 = 0,  /* fp32: arithmetic in fp32 throughout                       */
+  BASED_BF16 = 1  /* bf16: products on bf16 matrix cores, accumulation in fp32 */
+};
+
+enum {
+  BASED_OK = 0,
+  BASED_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  BASED_ERR_SHAPE = -2,       /* a size is out of range                         */
+  BASED_ERR_UNSUPPORTED = -3, /* a head dimension this library does not handle  */
+  BASED_ERR_DTYPE = -4,       /* dtype is not BASED_F32 or BASED_BF16           */
+  BASED_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned          */
+  BASED_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required        */
+  BASED_ERR_WINDOW = -7,      /* window outside 1..64                           */
+  BASED_ERR_HIP = -8,         /* a HIP runtime call or kernel launch failed     */
+  BASED_ERR_ALIAS = -9        /* an output overlaps an input it must not overlap */
+};
+
+#define BASED_DK 16        /* q/k head dimension of the Taylor linear attention */
+#define BASED_DPHI 273     /* 1 + 16 + 16*16 Taylor features                    */
+#define BASED_MAX_WINDOW 64
+
+/* ABI version compiled into the library (BASED_ABI_VERSION). */
+int based_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* based_status_string(int status);
+
+/*
+ * Bytes of device workspace based_linattn_fwd needs for this shape (0 when
+ * none).  Depends only on the arguments.  Returns 0 for invalid arguments
+ * as well; based_linattn_fwd reports those.
+ */
+size_t based_linattn_workspace_bytes(int B, int H, int L, int d_k, int d_v, int dtype);
+
+/*
+ * Causal Taylor linear attention, forward (blog post, linear-attention
+ * paragraph and feature-map pseudocode; README intro "dense, global linear
+ * attention").
+ *
+ *   q, k   [B,H,L,d_k] dtype, d_k must be 16
+ *   v      [B,H,L,d_v] dtype, d_v in {16, 32, 48, ..., 128}
+ *   y      [B,H,L,d_v] fp32 out: y_i = (phi(q_i)^T S_i) / (phi(q_i)^T z_i) with
+ *          S_i = S_in + sum_{j<=i} phi(k_j) v_j^T, z_i likewise
+ *   S_in   [B,H,273,d_v] fp32 or NULL (zero state)  -- initial state, e.g. the
+ *   z_in   [B,H,273]     fp32 or NULL (zero state)     S_out of an earlier call
+ *          S_in and z_in must be both NULL or both set.
+ *   S_out  [B,H,273,d_v] fp32 or NULL  -- state after position L-1
+ *   z_out  [B,H,273]     fp32 or NULL     (both NULL or both set)
+ *   B, H >= 1; L >= 0 (L = 0 only copies the state through).
+ *   workspace: device memory of at least based_linattn_workspace_bytes(...)
+ *          bytes (may be NULL when that is 0); contents on entry are ignored.
+ *
+ * With zero initial state the denominator of row i is at least (i + 1) / 2,
+ * so no epsilon is added.  y must not overlap q, k, v, S_in or z_in;
+ * S_out/z_out may alias S_in/z_in (in-place state update).
+ */
+int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
+                      const float* S_in, const float* z_in, float* S_out, float* z_out,
+                      int B, int H, int L, int d_k, int d_v, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal sliding-window softmax attention, forward (README intro: exact
+ * softmax attention over a short window).
+ *
+ *   q, k   [B,H,L,d_qk] dtype, d_qk in {16, 32, ..., 128}
+ *   v      [B,H,L,d_v]  dtype, d_v in {16, 32, ..., 128}
+ *   y      [B,H,L,d_v]  fp32 out
+ *   Row i attends to the `window` positions max(0, i-window+1) .. i (itself
+ *   included) with weights softmax_j(scale * q_i.k_j).  1 <= window <= 64.
+ *   B, H >= 1, L >= 0.  y must not overlap q, k or v.
+ */
+int based_swa_fwd(const void* q, const void* k, const void* v, float* y,
+                  int B, int H, int L, int d_qk, int d_v, int window, float scale,
+                  int dtype, void* stream);
+
+/*
+ * Fill the decode ring buffers from a context and set the positions
+ * (the set-up of generation after a prefill).
+ *
+ *   k      [B,H,L,d_k] dtype, v [B,H,L,d_v] dtype -- the context (L >= 0)
+ *   ring_k [B,H,window,d_k] dtype out, ring_v [B,H,window,d_v] dtype out:
+ *          slot (t mod window) receives position t for the last min(L, window)
+ *          positions; other slots are left untouched (they are never read).
+ *   pos    [B] int32 out: set to L.
+ * The linear-attention state comes from based_linattn_fwd's S_out / z_out
+ * over the same context.
+ */
+int based_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos,
+                         int B, int H, int L, int d_k, int d_v, int window, int dtype,
+                         void* stream);
+
+/*
+ * One generation step of the layer for B sequences x H heads (blog post,
+ * paragraph on the state: constant-size KV-state and K-state instead of a
+ * KV cache; README intro: window attention over the last 64 tokens).
+ *
+ *   q, k   [B,H,d_k] dtype (d_k = 16), v [B,H,d_v] dtype (d_v in {16..128})
+ *   S      [B,H,273,d_v] fp32 in/out, z [B,H,273] fp32 in/out
+ *   ring_k [B,H,window,d_k] dtype in/out, ring_v [B,H,window,d_v] in/out
+ *   pos    [B] int32 in/out: position t of this token; incremented by one.
+ *   y_lin  [B,H,d_v] fp32 out, y_swa [B,H,d_v] fp32 out
+ * Per (b, h), with t = pos[b]:
+ *   S += phi(k) v^T;  z += phi(k);  y_lin = phi(q)^T S / phi(q)^T z
+ *   ring slot (t mod window) <- (k, v)
+ *   y_swa = sum_j p_j v_j / sum_j p_j over positions max(0, t-window+1)..t,
+ *           p_j = exp(scale * q.k_j - max)
+ * The token attends to itself in both attentions.  1 <= window <= 64; the
+ * ring's slot count equals `window`.  Sequences are independent: each may be
+ * at a different position.
+ */
+int based_decode_step(const void* q, const void* k, const void* v,
+                      float* S, float* z, void* ring_k, void* ring_v, int32_t* pos,
+                      float* y_lin, float* y_swa,
+                      int B, int H, int d_k, int d_v, int window, float scale, int dtype,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASED_H */

@@ -1,0 +1,213 @@
+"""Based sequence-mixing layer on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/based.h`` (``libbased.so``,
+built in-tree by ``python -m linear_attention_lm_amd.build``).  The wrappers
+only check and marshal arguments; every step of the computation runs in the
+library's HIP kernels on the caller's current HIP stream.  PyTorch provides
+device memory and streams.
+
+The library is loaded on first use (so that the build script in this package
+can run before it exists); if it is missing, that first call fails loudly --
+there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd",
+    "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbased.so")
+DK = 16
+DPHI = 273
+F32, BF16 = 0, 1
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "based_abi_version": (_i, []),
+    "based_status_string": (ctypes.c_char_p, [_i]),
+    "based_linattn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "based_linattn_fwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
+    "based_swa_fwd": (_i, [_vp] * 4 + [_i] * 6 + [_f, _i, _vp]),
+    "based_decode_prefill": (_i, [_vp] * 5 + [_i] * 7 + [_vp]),
+    "based_decode_step": (_i, [_vp] * 10 + [_i] * 5 + [_f, _i, _vp]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first (python -m linear_attention_lm_amd.build)")
+    so = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(so, name)
+        fn.restype, fn.argtypes = res, args
+    return so
+
+
+_LIB = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
+
+
+class BasedError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(f"based: {_lib().based_status_string(code).decode()} (status {code})")
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise BasedError(code)
+
+
+def abi_version() -> int:
+    return _lib().based_abi_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must be on one device")
+    return dev
+
+
+def linattn_workspace_bytes(B, H, L, dv, dtype=torch.bfloat16) -> int:
+    return _lib().based_linattn_workspace_bytes(B, H, L, DK, dv, BF16 if dtype == torch.bfloat16 else F32)
+
+
+def linattn_fwd(q, k, v, S_in=None, z_in=None, *, return_state=False, y=None, S_out=None, z_out=None,
+                workspace=None):
+    """Causal Taylor linear attention.  q, k [B,H,L,16], v [B,H,L,dv] (fp32 or
+    bf16, same dtype).  Returns y [B,H,L,dv] fp32, or (y, S, z) with the final
+    state [B,H,273,dv], [B,H,273] when ``return_state``."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    _dev(q, k, v, S_in, z_in, y, S_out, z_out, workspace)
+    if y is None:
+        y = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if return_state and S_out is None:
+        S_out = torch.empty(B, H, DPHI, dv, device=q.device, dtype=torch.float32)
+        z_out = torch.empty(B, H, DPHI, device=q.device, dtype=torch.float32)
+    dt = _dtype_code(q)
+    need = _lib().based_linattn_workspace_bytes(B, H, L, dk, dv, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().based_linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in), _ptr(z_in), _ptr(S_out),
+                                 _ptr(z_out), B, H, L, dk, dv, dt, _ptr(workspace), wbytes, _stream()))
+    return (y, S_out, z_out) if (return_state or S_out is not None) else y
+
+
+def swa_fwd(q, k, v, window: int = 64, scale: float = 1.0, *, y=None):
+    """Causal sliding-window softmax attention over ``window`` positions."""
+    B, H, L, dqk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,d] and v [B,H,L,dv] of one dtype")
+    _dev(q, k, v, y)
+    if y is None:
+        y = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    _check(_lib().based_swa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), B, H, L, dqk, dv, window, float(scale),
+                             _dtype_code(q), _stream()))
+    return y
+
+
+@dataclass
+class DecodeState:
+    """Caller-owned generation state: S [B,H,273,dv] fp32, z [B,H,273] fp32,
+    ring_k [B,H,W,16], ring_v [B,H,W,dv] (input dtype), pos [B] int32."""
+
+    S: torch.Tensor
+    z: torch.Tensor
+    ring_k: torch.Tensor
+    ring_v: torch.Tensor
+    pos: torch.Tensor
+
+    @property
+    def window(self) -> int:
+        return self.ring_k.shape[2]
+
+
+def decode_prefill(k, v, state: DecodeState) -> None:
+    """Fill the ring buffers of ``state`` from a context k, v [B,H,L,.] and set pos = L."""
+    B, H, L, dk = k.shape
+    _dev(k, v, state.ring_k, state.ring_v, state.pos)
+    _check(_lib().based_decode_prefill(_ptr(k), _ptr(v), _ptr(state.ring_k), _ptr(state.ring_v), _ptr(state.pos),
+                                    B, H, L, dk, v.shape[-1], state.window, _dtype_code(k), _stream()))
+
+
+def decode_init(q, k, v, window: int = 64):
+    """Consume a context (q, k, v [B,H,L,.]): returns (y_lin, y_swa, state)
+    where the outputs are the context's own layer outputs and ``state`` is
+    ready for :func:`decode_step` at position L."""
+    B, H, L, _ = k.shape
+    dv = v.shape[-1]
+    y_lin, S, z = linattn_fwd(q, k, v, return_state=True)
+    y_swa = swa_fwd(q, k, v, window)
+    st = DecodeState(S, z, torch.zeros(B, H, window, DK, device=k.device, dtype=k.dtype),
+                     torch.zeros(B, H, window, dv, device=k.device, dtype=k.dtype),
+                     torch.zeros(B, device=k.device, dtype=torch.int32))
+    decode_prefill(k, v, st)
+    return y_lin, y_swa, st
+
+
+def decode_step(state: DecodeState, q, k, v, scale: float = 1.0, *, y_lin=None, y_swa=None):
+    """One token per sequence: q, k [B,H,16], v [B,H,dv].  Updates ``state`` in
+    place (including pos += 1) and returns (y_lin, y_swa) [B,H,dv] fp32."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    _dev(q, k, v, state.S, state.z, state.ring_k, state.ring_v, state.pos, y_lin, y_swa)
+    if y_lin is None:
+        y_lin = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
+    if y_swa is None:
+        y_swa = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
+    _check(_lib().based_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(state.S), _ptr(state.z), _ptr(state.ring_k),
+                                 _ptr(state.ring_v), _ptr(state.pos), _ptr(y_lin), _ptr(y_swa), B, H, dk, dv,
+                                 state.window, float(scale), _dtype_code(q), _stream()))
+    return y_lin, y_swa

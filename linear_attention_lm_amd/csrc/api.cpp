@@ -1,0 +1,143 @@
+// C ABI of the Based layer: argument validation and dispatch to the kernels.
+// Every check runs on the host before anything is enqueued; a failed check
+// returns a negative status and touches no memory.
+#include "../../include/based.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launchers.h"
+
+#define BASED_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dv(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Span a, Span b) { return a.lo && b.lo && a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+size_t elem_size(int dtype) { return dtype == BASED_BF16 ? 2 : 4; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? BASED_OK : BASED_ERR_HIP; }
+
+}  // namespace
+
+BASED_API int based_abi_version(void) { return BASED_ABI_VERSION; }
+
+BASED_API const char* based_status_string(int status) {
+  switch (status) {
+    case BASED_OK: return "ok";
+    case BASED_ERR_NULL: return "a required pointer is NULL";
+    case BASED_ERR_SHAPE: return "a size is out of range";
+    case BASED_ERR_UNSUPPORTED: return "unsupported head dimension (d_k must be 16; d_v, d_qk multiples of 16 up to 128)";
+    case BASED_ERR_DTYPE: return "dtype must be BASED_F32 or BASED_BF16";
+    case BASED_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case BASED_ERR_WORKSPACE: return "workspace missing or too small";
+    case BASED_ERR_WINDOW: return "window must be in 1..64";
+    case BASED_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case BASED_ERR_ALIAS: return "an output overlaps an input";
+  }
+  return "unknown status";
+}
+
+BASED_API size_t based_linattn_workspace_bytes(int B, int H, int L, int d_k, int d_v, int dtype) {
+  (void)B; (void)H; (void)L; (void)d_k; (void)d_v; (void)dtype;
+  return 0;
+}
+
+BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, float* y, const float* S_in,
+                                const float* z_in, float* S_out, float* z_out, int B, int H, int L, int d_k,
+                                int d_v, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (L > 0 && (!q || !k || !v || !y)) return BASED_ERR_NULL;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
+  const void* ptrs[] = {q, k, v, y, S_in, z_in, S_out, z_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t need = based_linattn_workspace_bytes(B, H, L, d_k, d_v, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BASED_ERR_WORKSPACE;
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  const Span ys = span(y, BH * L * d_v * 4);
+  const Span in[] = {span(q, BH * L * d_k * es), span(k, BH * L * d_k * es), span(v, BH * L * d_v * es),
+                     span(S_in, BH * BASED_DPHI * d_v * 4), span(z_in, BH * BASED_DPHI * 4)};
+  for (const Span& s : in)
+    if (L > 0 && overlap(ys, s)) return BASED_ERR_ALIAS;
+  if (S_out && (overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[0]) ||
+                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[1]) ||
+                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[2])))
+    return BASED_ERR_ALIAS;
+
+  based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
+  if (L == 0 && !S_out) return BASED_OK;
+  return status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
+BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* y, int B, int H, int L, int d_qk,
+                            int d_v, int window, float scale, int dtype, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (!valid_dv(d_qk) || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
+  if ((long long)B * H * ((L + 31) / 32) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (L == 0) return BASED_OK;
+  if (!q || !k || !v || !y) return BASED_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return BASED_ERR_ALIGN;
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  const Span ys = span(y, BH * L * d_v * 4);
+  if (overlap(ys, span(q, BH * L * d_qk * es)) || overlap(ys, span(k, BH * L * d_qk * es)) ||
+      overlap(ys, span(v, BH * L * d_v * es)))
+    return BASED_ERR_ALIAS;
+  based::SwaArgs a{q, k, v, y, B, H, L, d_qk, d_v, window, scale};
+  return status_of(based::launch_swa_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
+BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos, int B,
+                                   int H, int L, int d_k, int d_v, int window, int dtype, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if ((long long)B * H > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
+  if (!ring_k || !ring_v || !pos || (L > 0 && (!k || !v))) return BASED_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(ring_k) || !aligned16(ring_v) || !aligned16(pos))
+    return BASED_ERR_ALIGN;
+  return status_of(
+      based::launch_decode_prefill(k, v, ring_k, ring_v, pos, B, H, L, d_v, window, dtype == BASED_BF16,
+                                   (hipStream_t)stream));
+}
+
+BASED_API int based_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* ring_k,
+                                void* ring_v, int32_t* pos, float* y_lin, float* y_swa, int B, int H, int d_k,
+                                int d_v, int window, float scale, int dtype, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1) return BASED_ERR_SHAPE;
+  if ((long long)B * H > (1LL << 30) || B > 0x7fffffff) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
+  const void* ptrs[] = {q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa};
+  for (const void* p : ptrs)
+    if (!p) return BASED_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  const Span outs[] = {span(S, BH * BASED_DPHI * d_v * 4), span(z, BH * BASED_DPHI * 4),
+                       span(ring_k, BH * window * d_k * es), span(ring_v, BH * window * d_v * es),
+                       span(pos, (size_t)B * 4), span(y_lin, BH * d_v * 4), span(y_swa, BH * d_v * 4)};
+  const Span ins[] = {span(q, BH * d_k * es), span(k, BH * d_k * es), span(v, BH * d_v * es)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Span& s : ins)
+      if (overlap(outs[i], s)) return BASED_ERR_ALIAS;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return BASED_ERR_ALIAS;
+  }
+  based::DecodeArgs a{q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_v, window, scale};
+  return status_of(based::launch_decode_step(a, dtype == BASED_BF16, (hipStream_t)stream));
+}

@@ -1,0 +1,81 @@
+// Device-side helpers shared by the Based layer kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace based {
+
+// Raw bf16 storage: the upper 16 bits of an fp32.
+typedef uint16_t bf16_t;
+
+struct f32x4_t { float x, y, z, w; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  __bf16 r = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, r);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Load n consecutive elements (n a multiple of 4 for fp32, 8 for bf16, 16-byte
+// aligned) as fp32.
+template <int N>
+__device__ __forceinline__ void load_row(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    float4 t = *reinterpret_cast<const float4*>(p + i);
+    out[i] = t.x; out[i + 1] = t.y; out[i + 2] = t.z; out[i + 3] = t.w;
+  }
+}
+template <int N>
+__device__ __forceinline__ void load_row(const bf16_t* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < N; i += 8) {
+    uint4 t = *reinterpret_cast<const uint4*>(p + i);
+    uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[i + 2 * j] = __uint_as_float(w[j] << 16);
+      out[i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+
+// Feature bookkeeping.  The state crosses the ABI in the 273-row layout of
+// phi = [1, x_a, x_a x_b / sqrt2 (a-major)].  Inside the kernels the
+// quadratic block is kept once per unordered pair a <= b ("compact" form,
+// 1 + 16 + 136 = 153 rows):
+//   key side   psi'(k) = [1, k_a, k_a^2, k_a k_b (a < b)]
+//   query side psi(q)  = [1, q_a, q_a^2 / 2, q_a q_b (a < b)]
+// so that psi(q).psi'(k) = 1 + q.k + (q.k)^2 / 2 = phi(q).phi(k).  Conversion:
+//   T[aa] = sqrt2 * S[aa],  T[ab] = (S[ab] + S[ba]) / sqrt2,  S[ab] = T[ab] / sqrt2.
+constexpr int DK = 16;
+constexpr int DPHI = 273;
+constexpr int NQUAD = DK * (DK + 1) / 2;  // 136
+constexpr int NCOMPACT = 1 + DK + NQUAD;  // 153
+
+// Index of the unordered pair (a <= b) in the row-major upper triangle.
+__host__ __device__ constexpr int pair_index(int a, int b) { return a * DK - a * (a - 1) / 2 + (b - a); }
+
+constexpr float SQRT2 = 1.41421356237309505f;
+constexpr float INV_SQRT2 = 0.70710678118654752f;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+}  // namespace based

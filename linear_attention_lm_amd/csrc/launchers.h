@@ -1,0 +1,39 @@
+// Host-side launchers of the Based kernels; called by the C ABI after its
+// argument checks.  Every launcher enqueues on `stream` and returns the HIP
+// status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace based {
+
+struct LinattnArgs {
+  const void* q; const void* k; const void* v; float* y;
+  const float* S_in; const float* z_in; float* S_out; float* z_out;
+  int B, H, L, dv;
+  void* workspace; size_t workspace_bytes;
+};
+
+// fp32 (and generic) chunked linear attention on the vector ALUs.
+hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t stream);
+
+struct SwaArgs {
+  const void* q; const void* k; const void* v; float* y;
+  int B, H, L, dqk, dv, window; float scale;
+};
+hipError_t launch_swa_valu(const SwaArgs& a, bool bf16, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q; const void* k; const void* v;
+  float* S; float* z; void* ring_k; void* ring_v; int32_t* pos;
+  float* y_lin; float* y_swa;
+  int B, H, dv, window; float scale;
+};
+hipError_t launch_decode_step(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
+hipError_t launch_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos,
+                                 int B, int H, int L, int dv, int window, bool bf16, hipStream_t stream);
+
+}  // namespace based

@@ -1,0 +1,132 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/based.h declares, and rejects bad arguments on the host with the
+documented status codes before anything reaches the GPU (no compute here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "based.h")
+
+import linear_attention_lm_amd as lal  # noqa: E402
+
+ERR = dict(NULL=-1, SHAPE=-2, UNSUPPORTED=-3, DTYPE=-4, ALIGN=-5, WORKSPACE=-6, WINDOW=-7, HIP=-8, ALIAS=-9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(based_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def so():
+    return lal.load_library()
+
+
+def test_every_declared_symbol_is_exported(so):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_header_status_codes_match():
+    text = open(HEADER).read()
+    for name, code in ERR.items():
+        assert re.search(rf"BASED_ERR_{name}\s*=\s*{code}\b", text), name
+
+
+def test_version_and_strings(so):
+    assert so.based_abi_version() == 1
+    for code in [0, *ERR.values(), 12345]:
+        s = so.based_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+P = 0x10000  # fake, 16-byte aligned device addresses: validation never dereferences them
+
+
+def fwd(so, q=P, k=2 * P, v=3 * P, y=4 * P, S_in=None, z_in=None, S_out=None, z_out=None, B=1, H=2, L=256,
+        dk=16, dv=64, dt=1, ws=None, wsb=0):
+    return so.based_linattn_fwd(q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, dk, dv, dt, ws, wsb, None)
+
+
+def test_linattn_validation(so):
+    assert fwd(so, dt=2) == ERR["DTYPE"]
+    assert fwd(so, B=0) == ERR["SHAPE"]
+    assert fwd(so, H=-1) == ERR["SHAPE"]
+    assert fwd(so, L=-5) == ERR["SHAPE"]
+    assert fwd(so, dk=8) == ERR["UNSUPPORTED"]
+    for dv in (0, 8, 24, 144, 256):
+        assert fwd(so, dv=dv) == ERR["UNSUPPORTED"], dv
+    assert fwd(so, q=None) == ERR["NULL"]
+    assert fwd(so, y=None) == ERR["NULL"]
+    assert fwd(so, S_in=5 * P) == ERR["NULL"]  # S_in without z_in
+    assert fwd(so, z_out=5 * P) == ERR["NULL"]  # z_out without S_out
+    assert fwd(so, v=3 * P + 8) == ERR["ALIGN"]
+    assert fwd(so, y=1 * P) == ERR["ALIAS"]  # y overlaps q
+    assert fwd(so, y=2 * P + 64) == ERR["ALIAS"]  # y overlaps k
+
+
+def test_swa_validation(so):
+    f = lambda **kw: so.based_swa_fwd(kw.get("q", P), kw.get("k", 2 * P), kw.get("v", 3 * P), kw.get("y", 4 * P),
+                                      kw.get("B", 1), kw.get("H", 1), kw.get("L", 100), kw.get("dqk", 16),
+                                      kw.get("dv", 64), kw.get("window", 64), 1.0, kw.get("dt", 1), None)
+    assert f(dt=-1) == ERR["DTYPE"]
+    assert f(window=0) == ERR["WINDOW"]
+    assert f(window=65) == ERR["WINDOW"]
+    assert f(dqk=20) == ERR["UNSUPPORTED"]
+    assert f(dv=256) == ERR["UNSUPPORTED"]
+    assert f(k=None) == ERR["NULL"]
+    assert f(q=P + 4) == ERR["ALIGN"]
+    assert f(y=3 * P) == ERR["ALIAS"]
+    assert f(L=0, q=None, k=None, v=None, y=None) == 0  # nothing to do, nothing touched
+
+
+def test_decode_validation(so):
+    def f(**kw):
+        a = dict(q=P, k=2 * P, v=3 * P, S=4 * P, z=40 * P, rk=50 * P, rv=60 * P, pos=70 * P, yl=80 * P, ys=90 * P,
+                 B=2, H=2, dk=16, dv=64, window=64, dt=1)
+        a.update(kw)
+        return so.based_decode_step(a["q"], a["k"], a["v"], a["S"], a["z"], a["rk"], a["rv"], a["pos"], a["yl"],
+                                    a["ys"], a["B"], a["H"], a["dk"], a["dv"], a["window"], 1.0, a["dt"], None)
+
+    assert f(dt=7) == ERR["DTYPE"]
+    assert f(B=0) == ERR["SHAPE"]
+    assert f(dk=32) == ERR["UNSUPPORTED"]
+    assert f(window=100) == ERR["WINDOW"]
+    assert f(pos=None) == ERR["NULL"]
+    assert f(ys=90 * P + 2) == ERR["ALIGN"]
+    assert f(ys=80 * P) == ERR["ALIAS"]  # both outputs in one buffer
+    assert f(S=P) == ERR["ALIAS"]  # state overlaps an input
+
+
+def test_prefill_validation(so):
+    f = lambda **kw: so.based_decode_prefill(kw.get("k", P), kw.get("v", 2 * P), kw.get("rk", 3 * P),
+                                             kw.get("rv", 4 * P), kw.get("pos", 5 * P), 1, 1, kw.get("L", 10), 16,
+                                             64, kw.get("window", 64), kw.get("dt", 0), None)
+    assert f(dt=3) == ERR["DTYPE"]
+    assert f(L=-1) == ERR["SHAPE"]
+    assert f(window=0) == ERR["WINDOW"]
+    assert f(rk=None) == ERR["NULL"]
+    assert f(pos=5 * P + 1) == ERR["ALIGN"]
+
+
+def test_workspace_query_is_pure(so):
+    a = so.based_linattn_workspace_bytes(8, 16, 2048, 16, 64, 1)
+    assert a == so.based_linattn_workspace_bytes(8, 16, 2048, 16, 64, 1)
+    assert so.based_linattn_workspace_bytes(0, 16, 2048, 16, 64, 1) == 0
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and has no CPU code path."""
+    pkg = os.path.join(ROOT, "linear_attention_lm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn

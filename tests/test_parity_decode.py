@@ -1,0 +1,106 @@
+"""GPU parity of recurrent decode (based_decode_prefill + based_decode_step)
+against the oracle's DecodeState, on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import based_oracle as O
+from parity_util import TOL, report, rowinf_rel, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_decode(based, cfg, seqs=None, check_steps=None, seed=0):
+    """Prefill on the GPU (linear attention state export + ring fill), then
+    cfg.steps decode steps; compare the sampled sequences with the oracle."""
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, seed)
+    say(f"decode B{cfg.B} H{cfg.H} ctx{cfg.ctx} steps{cfg.steps} dv{cfg.dv} {cfg.dtype}")
+    seqs = list(range(cfg.B)) if seqs is None else seqs
+    check_steps = set(range(cfg.steps)) if check_steps is None else set(check_steps)
+    tol = TOL[qc.dtype]
+    _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window)
+    ref = O.DecodeState.prefill(kc[seqs], vc[seqs], cfg.window)
+    errs = []
+    qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
+    for s in range(cfg.steps):
+        yl, ys = based.decode_step(st, qd[s], kd[s], vd[s])
+        rl, rs = ref.step(qs[s, seqs], ks[s, seqs], vs[s, seqs])
+        if s in check_steps:
+            el, es = rowinf_rel(yl[seqs], rl), rowinf_rel(ys[seqs], rs)
+            errs.append((el, es))
+            assert el <= tol and es <= tol, (s, el, es)
+    torch.cuda.synchronize()
+    report(f"decode y_lin B{cfg.B} ctx{cfg.ctx}", max(e[0] for e in errs), tol)
+    report(f"decode y_swa B{cfg.B} ctx{cfg.ctx}", max(e[1] for e in errs), tol)
+    assert rowinf_rel(st.S[seqs], ref.S) <= tol
+    assert rowinf_rel(st.z[seqs][..., None], ref.z[..., None]) <= tol
+    assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_small_wraps_ring(based, dtype):
+    cfg = synth.DecodeConfig("small", B=3, H=4, ctx=100, steps=70, dtype=dtype)
+    run_decode(based, cfg)
+
+
+def test_decode_from_empty_context(based):
+    """No prefill tokens: the first steps see fewer than 64 keys."""
+    cfg = synth.DecodeConfig("empty", B=2, H=2, ctx=0, steps=80)
+    run_decode(based, cfg)
+
+
+@pytest.mark.parametrize("dv,window", [(128, 64), (32, 17), (48, 1)])
+def test_decode_shapes(based, dv, window):
+    cfg = synth.DecodeConfig("shape", B=2, H=20, ctx=37, steps=30, dv=dv, window=window)
+    run_decode(based, cfg)
+
+
+def test_decode_sequences_at_different_positions(based):
+    """Sequence 0 resumes after 10 context tokens, sequence 1 after 30."""
+    cfg = synth.DecodeConfig("mixed", B=2, H=3, ctx=30, steps=70)
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg)
+    dev = lambda *ts: [t.contiguous().to(DEV) for t in ts]
+    _, _, sa = based.decode_init(*dev(qc[:, :, :10], kc[:, :, :10], vc[:, :, :10]))
+    _, _, sb = based.decode_init(*dev(qc, kc, vc))
+    st = based.DecodeState(*[torch.cat([a[:1], b[1:]]).contiguous()
+                             for a, b in zip((sa.S, sa.z, sa.ring_k, sa.ring_v, sa.pos),
+                                             (sb.S, sb.z, sb.ring_k, sb.ring_v, sb.pos))])
+    ra = O.DecodeState.prefill(kc[:, :, :10], vc[:, :, :10])
+    rb = O.DecodeState.prefill(kc, vc)
+    ref = O.DecodeState(np.concatenate([ra.S[:1], rb.S[1:]]), np.concatenate([ra.z[:1], rb.z[1:]]),
+                        np.concatenate([ra.ring_k[:1], rb.ring_k[1:]]),
+                        np.concatenate([ra.ring_v[:1], rb.ring_v[1:]]), [10, 30])
+    for s in range(cfg.steps):
+        yl, ys = based.decode_step(st, *dev(qs[s], ks[s], vs[s]))
+        rl, rs = ref.step(qs[s], ks[s], vs[s])
+        assert rowinf_rel(yl, rl) <= 2e-3 and rowinf_rel(ys, rs) <= 2e-3, s
+    assert st.pos.cpu().tolist() == [10 + cfg.steps, 30 + cfg.steps]
+
+
+def test_decode_full_workload_sampled(based):
+    """256 sequences x 16 heads, 2048-token context, d_v 64, bf16 ring: the
+    first 72 steps (past one full ring turn), oracle on sampled sequences."""
+    cfg = synth.DECODE_CONFIG.replace(steps=72)
+    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=[0, 1, 2, 62, 63, 64, 65, 71])
+
+
+def test_decode_snapshot_restore(based):
+    """Copying the state out and back in resumes bit-identically."""
+    cfg = synth.DecodeConfig("snap", B=2, H=4, ctx=50, steps=20)
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg)
+    _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV))
+    qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
+    for s in range(10):
+        based.decode_step(st, qd[s], kd[s], vd[s])
+    snap = [t.cpu().clone() for t in (st.S, st.z, st.ring_k, st.ring_v, st.pos)]
+    outs_a = [based.decode_step(st, qd[s], kd[s], vd[s]) for s in range(10, 20)]
+    outs_a = [(a.cpu(), b.cpu()) for a, b in outs_a]
+    st2 = based.DecodeState(*[t.to(DEV) for t in snap])
+    outs_b = [based.decode_step(st2, qd[s], kd[s], vd[s]) for s in range(10, 20)]
+    torch.cuda.synchronize()
+    for (a1, b1), (a2, b2) in zip(outs_a, outs_b):
+        assert torch.equal(a1, a2.cpu()) and torch.equal(b1, b2.cpu())

@@ -1,0 +1,223 @@
+"""GPU parity of the forward entry points (based_linattn_fwd, based_swa_fwd)
+against the fp64 oracle, on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import based_oracle as O
+from parity_util import TOL, report, rowinf_rel, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def inputs(cfg, seed=0):
+    return synth.fwd_inputs(cfg, seed)
+
+
+def check_linattn(based, cfg, heads=None, seed=0, chunk=64):
+    """Full-size GPU call; oracle on all heads, or on the sampled (b, h) heads."""
+    q, k, v = inputs(cfg, seed)
+    say(f"linattn {cfg.name} B{cfg.B} H{cfg.H} L{cfg.L} dv{cfg.dv} {cfg.dtype}")
+    y, S, z = based.linattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), return_state=True)
+    torch.cuda.synchronize()
+    tol = TOL[q.dtype]
+    sel = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if heads is None else heads
+    bi = [b for b, _ in sel]
+    hi = [h for _, h in sel]
+    qs, ks, vs = q[bi, hi], k[bi, hi], v[bi, hi]
+    y_ref, _, S_ref, z_ref = O.linattn_chunked(qs, ks, vs, chunk)
+    err = rowinf_rel(y[bi, hi], y_ref)
+    report(f"linattn y {cfg.name}", err, tol)
+    assert err <= tol
+    errS = rowinf_rel(S[bi, hi], S_ref)
+    errz = rowinf_rel(z[bi, hi][..., None], z_ref[..., None])
+    report(f"linattn S_out {cfg.name}", errS, tol)
+    assert errS <= tol and errz <= tol
+    return y
+
+
+def check_swa(based, cfg, heads=None, seed=0, window=64):
+    q, k, v = inputs(cfg, seed)
+    say(f"swa {cfg.name} B{cfg.B} H{cfg.H} L{cfg.L} dv{cfg.dv} {cfg.dtype} window{window}")
+    y = based.swa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window)
+    torch.cuda.synchronize()
+    sel = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if heads is None else heads
+    bi = [b for b, _ in sel]
+    hi = [h for _, h in sel]
+    y_ref = O.swa(q[bi, hi], k[bi, hi], v[bi, hi], window)
+    err = rowinf_rel(y[bi, hi], y_ref)
+    report(f"swa y {cfg.name} w{window}", err, TOL[q.dtype])
+    assert err <= TOL[q.dtype]
+
+
+# ---------------------------------------------------------------- the workloads
+def test_tiny_fp32(based):
+    cfg = synth.FWD_CONFIGS["tiny"]
+    check_linattn(based, cfg)
+    check_swa(based, cfg)
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("based360m", [(0, 0), (3, 7), (7, 15)]),
+    ("based1p3b", [(0, 0), (2, 9), (3, 15)]),
+    ("long32k", [(0, 0), (0, 11)]),
+])
+def test_full_size_sampled_heads(based, name, heads):
+    cfg = synth.FWD_CONFIGS[name]
+    check_linattn(based, cfg, heads)
+    check_swa(based, cfg, heads)
+
+
+# ------------------------------------------------------ shapes, tails and edges
+SMALL = synth.FwdConfig("small", B=2, H=3, L=1000, dv=64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 130, 1000])
+def test_lengths(based, dtype, L):
+    cfg = SMALL.replace(L=L, dtype=dtype, name=f"L{L}")
+    check_linattn(based, cfg)
+    check_swa(based, cfg)
+
+
+@pytest.mark.parametrize("dv", [16, 32, 48, 80, 96, 112, 128])
+def test_value_dims(based, dv):
+    cfg = SMALL.replace(L=300, dv=dv, name=f"dv{dv}")
+    check_linattn(based, cfg)
+    check_swa(based, cfg)
+
+
+@pytest.mark.parametrize("window", [1, 2, 17, 63, 64])
+def test_windows(based, window):
+    check_swa(based, SMALL.replace(L=200, name=f"w{window}"), window=window)
+
+
+@pytest.mark.parametrize("dqk", [32, 128])
+def test_swa_wider_qk(based, dqk):
+    cfg = SMALL.replace(L=150, dk=dqk, name=f"dqk{dqk}")
+    check_swa(based, cfg)
+
+
+def test_swa_scale(based):
+    cfg = SMALL.replace(L=150)
+    q, k, v = inputs(cfg)
+    y = based.swa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), 64, scale=0.37)
+    err = rowinf_rel(y, O.swa(q, k, v, 64, 0.37))
+    report("swa scale 0.37", err, 2e-3)
+    assert err <= 2e-3
+
+
+def test_heavy_tailed_small(based):
+    cfg = SMALL.replace(L=2000, heavy_frac=0.01, name="heavy")
+    check_linattn(based, cfg)
+    check_swa(based, cfg)
+
+
+def test_empty_sequence(based):
+    q = torch.zeros(1, 2, 0, 16, device=DEV, dtype=torch.bfloat16)
+    v = torch.zeros(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    y, S, z = based.linattn_fwd(q, q, v, return_state=True)
+    assert y.shape == (1, 2, 0, 64)
+    torch.cuda.synchronize()
+    assert torch.all(S == 0) and torch.all(z == 0)
+    assert based.swa_fwd(q, q, v).shape == (1, 2, 0, 64)
+
+
+# --------------------------------------------------------- state and resume
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_resume_from_exported_state(based, dtype):
+    """fwd(x[:n]) -> (S, z) -> fwd(x[n:], S_in, z_in) equals fwd(x)."""
+    cfg = SMALL.replace(L=700, dtype=dtype)
+    q, k, v = [t.to(DEV) for t in inputs(cfg)]
+    y = based.linattn_fwd(q, k, v)
+    n = 333
+    _, S1, z1 = based.linattn_fwd(q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous(),
+                                  return_state=True)
+    y2, S2, z2 = based.linattn_fwd(q[:, :, n:].contiguous(), k[:, :, n:].contiguous(), v[:, :, n:].contiguous(),
+                                   S1, z1, return_state=True)
+    yq, _, S_ref, z_ref = O.linattn_chunked(*inputs(cfg), 64)
+    tol = TOL[q.dtype]
+    err = rowinf_rel(y2, yq[:, :, n:])
+    report(f"resume {dtype}", err, tol)
+    assert err <= tol
+    assert rowinf_rel(y[:, :, n:], yq[:, :, n:]) <= tol
+    assert rowinf_rel(S2, S_ref) <= tol
+
+
+def test_state_in_place_update(based):
+    """S_out may alias S_in: the state advances in place."""
+    cfg = SMALL.replace(L=200)
+    q, k, v = [t.to(DEV) for t in inputs(cfg)]
+    _, S, z = based.linattn_fwd(q[:, :, :90].contiguous(), k[:, :, :90].contiguous(), v[:, :, :90].contiguous(),
+                                return_state=True)
+    based.linattn_fwd(q[:, :, 90:].contiguous(), k[:, :, 90:].contiguous(), v[:, :, 90:].contiguous(), S, z,
+                      S_out=S, z_out=z)
+    S_ref, z_ref = O.linattn_state(*inputs(cfg)[1:])
+    assert rowinf_rel(S, S_ref) <= 2e-3
+    assert rowinf_rel(z[..., None], z_ref[..., None]) <= 2e-3
+
+
+def test_nonsymmetric_initial_state(based):
+    """A state enters only through S[ab] + S[ba] (documented): an arbitrary
+    S_in gives the oracle's result for that S_in."""
+    cfg = SMALL.replace(L=150, dtype="f32")
+    q, k, v = inputs(cfg)
+    g = torch.Generator().manual_seed(5)
+    S0 = torch.randn(cfg.B, cfg.H, 273, cfg.dv, generator=g)
+    z0 = torch.rand(cfg.B, cfg.H, 273, generator=g) + 50.0
+    y = based.linattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), S0.to(DEV), z0.to(DEV))
+    y_ref = O.linattn_recurrent(q, k, v, S0, z0)[0]
+    err = rowinf_rel(y, y_ref)
+    report("non-symmetric S_in", err, 1e-5)
+    assert err <= 1e-5
+
+
+# ------------------------------------------------------------------ robustness
+def test_no_writes_outside_outputs(based):
+    """Guard bands around y and the state stay untouched."""
+    cfg = SMALL.replace(L=333)
+    q, k, v = [t.to(DEV) for t in inputs(cfg)]
+    G = 4096
+    n = cfg.B * cfg.H * cfg.L * cfg.dv
+    buf = torch.full((n + 2 * G,), 7.5, device=DEV)
+    y = buf[G:G + n].view(cfg.B, cfg.H, cfg.L, cfg.dv)
+    ns = cfg.B * cfg.H * 273 * cfg.dv
+    sbuf = torch.full((ns + 2 * G,), -3.0, device=DEV)
+    zbuf = torch.full((cfg.B * cfg.H * 273 + 2 * G,), -3.0, device=DEV)
+    based.linattn_fwd(q, k, v, y=y, S_out=sbuf[G:G + ns].view(cfg.B, cfg.H, 273, cfg.dv),
+                      z_out=zbuf[G:G + cfg.B * cfg.H * 273].view(cfg.B, cfg.H, 273))
+    ys = torch.full((n + 2 * G,), 7.5, device=DEV)
+    based.swa_fwd(q, k, v, y=ys[G:G + n].view(cfg.B, cfg.H, cfg.L, cfg.dv))
+    torch.cuda.synchronize()
+    for b, val in ((buf, 7.5), (sbuf, -3.0), (zbuf, -3.0), (ys, 7.5)):
+        assert torch.all(b[:G] == val) and torch.all(b[-G:] == val)
+
+
+def test_repeat_runs_bitwise_identical(based):
+    cfg = synth.FWD_CONFIGS["based360m"]
+    q, k, v = [t.to(DEV) for t in inputs(cfg)]
+    a = based.linattn_fwd(q, k, v)
+    b = based.linattn_fwd(q, k, v)
+    sa = based.swa_fwd(q, k, v)
+    sb = based.swa_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+def test_nan_stays_near_its_rows(based):
+    """A NaN in v at position p = 150 reaches linear-attention rows >= p and
+    window rows p..p+63.  Matrix-core tiles of 64 positions may also carry it
+    to other rows of the tiles that hold position p (0 x NaN = NaN), never
+    further: rows before 128 stay finite, and window rows from 256 on."""
+    cfg = SMALL.replace(L=300, B=1, H=1)
+    q, k, v = inputs(cfg)
+    v[0, 0, 150, 3] = float("nan")
+    y = based.linattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    s = based.swa_fwd(q.to(DEV), k.to(DEV), v.to(DEV)).cpu()
+    assert torch.isfinite(y[0, 0, :128]).all() and torch.isnan(y[0, 0, 150:, 3]).all()
+    assert torch.isfinite(y[0, 0, :, [0, 1, 2, 4]]).all()
+    assert torch.isfinite(s[0, 0, :128]).all() and torch.isfinite(s[0, 0, 256:]).all()
+    assert torch.isnan(s[0, 0, 150:214, 3]).all()
