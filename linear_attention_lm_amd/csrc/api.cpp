@@ -46,8 +46,9 @@ BASED_API const char* based_status_string(int status) {
 }
 
 BASED_API size_t based_linattn_workspace_bytes(int B, int H, int L, int d_k, int d_v, int dtype) {
-  (void)B; (void)H; (void)L; (void)d_k; (void)d_v; (void)dtype;
-  return 0;
+  if (dtype != BASED_BF16 || B < 1 || H < 1 || L < 0 || d_k != BASED_DK) return 0;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return 0;
+  return based::linattn_mfma_workspace(B, H, L, d_v);
 }
 
 BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, float* y, const float* S_in,
@@ -77,6 +78,8 @@ BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, flo
 
   based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
   if (L == 0 && !S_out) return BASED_OK;
+  if (dtype == BASED_BF16 && based::linattn_mfma_supported(d_v))
+    return status_of(based::launch_linattn_mfma(a, (hipStream_t)stream));
   return status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 

@@ -19,6 +19,12 @@ struct LinattnArgs {
 // fp32 (and generic) chunked linear attention on the vector ALUs.
 hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t stream);
 
+// bf16 chunked linear attention on the matrix cores (d_v in {32, 64, 96, 128}).
+bool linattn_mfma_supported(int dv);
+size_t linattn_mfma_workspace(int B, int H, int L, int dv);
+void linattn_mfma_plan(int BH, int L, int* nseg, int* seg_chunks);
+hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
+
 struct SwaArgs {
   const void* q; const void* k; const void* v; float* y;
   int B, H, L, dqk, dv, window; float scale;

@@ -1,0 +1,699 @@
+// Causal Taylor linear attention, chunked, on bf16 matrix cores (gfx950
+// v_mfma_f32_16x16x32_bf16) with fp32 accumulation: the bf16 path of
+// based_linattn_fwd.
+//
+// Method (blog post "Базированная модель, часть 2": exp(q.k) is replaced by
+// 1 + q.k + (q.k)^2/2 = phi(q).phi(k); paragraph on the state: a numerator
+// KV-state and a denominator K-state; HazyResearch/based train README,
+// training views: the chunked kernels compute what the quadratic view does):
+// for a chunk c of C = 64 positions,
+//   num_i = phi(q_i)^T S_c + sum_{j<=i in c} (1 + x_ij + x_ij^2/2) v_j
+//   den_i = phi(q_i)^T z_c + sum_{j<=i in c} (1 + x_ij + x_ij^2/2),  x_ij = q_i.k_j
+//   y_i = num_i / den_i;  S_{c+1} = S_c + phi(K_c)^T V_c,  z_{c+1} likewise.
+//
+// Design for MI355X:
+// * The quadratic block of phi is symmetric, so the state keeps one row per
+//   unordered pair a <= b (136 rows instead of 256) -- 160 feature slots with
+//   the 16 linear features; the constant feature (sum of v, token count) is
+//   carried in fp32 on the vector ALUs.  Slot r = 32kb + 8g + s holds the
+//   feature of pattern (kb, s) shifted by 4g (cyclic on the 16 coordinates):
+//   the lane group g of a matrix-core operand then builds its 8 features from
+//   a register copy of q rotated by 4g, with compile-time register indices.
+//   The pairs {a, a+8} are fixed by the shift by 8 and appear in two slots,
+//   each with query weight 1/2.
+// * bf16 has an 8-bit significand: q, k, v are exact, products q_a q_b and
+//   the fp32 state are not.  Every inexact operand is split into hi + lo bf16
+//   (exact for a product of two bf16 values) and the matrix product takes the
+//   hi*hi + hi*lo + lo*hi passes, so the result carries ~16 significant bits.
+// * Workgroup = 4 wavefronts; one workgroup per (batch*head, sequence
+//   segment).  Per chunk: readout + in-chunk term (wavefront w owns positions
+//   16w..16w+15 and every value column), then the state update (wavefront w
+//   owns a contiguous quarter of the 10 x (d_v/16) state tiles, which stay in
+//   accumulator registers across chunks), then the state is re-split into
+//   bf16 hi/lo in LDS for the next chunk's readout.  The next chunk's inputs
+//   are loaded from HBM into registers while the current one computes.
+// * Long sequences are split into segments so that the grid fills the GPU: a
+//   state-only pass computes each segment's state increment into the
+//   workspace, a scan turns those into prefix states, and every segment then
+//   starts from its prefix.
+#include "based_device.h"
+#include "launchers.h"
+
+namespace based {
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;         // positions per chunk
+constexpr int NTHR = 256;     // 4 wavefronts
+constexpr int NF = 160;       // feature slots (linear + quadratic), constant kept apart
+constexpr int NKB = NF / 32;  // K-blocks of 32 slots in the readout
+constexpr int QS = 20;        // fp32 q row stride in LDS (floats)
+constexpr int QKB = 24;       // bf16 q/k row stride in LDS (elements)
+constexpr int KT = C + 4;     // fp32 k^T row stride
+constexpr int VT = C + 8;     // bf16 v^T row stride
+constexpr int TT = NF + 8;    // bf16 state^T row stride
+constexpr int ONES = 16;      // k^T row holding 1.0 (second factor of linear features)
+
+enum SlotType : uint8_t { LIN = 0, DIAG = 1, OFF = 2, HALF = 3 };
+
+struct SlotTables {
+  uint8_t a[NF], b[NF], type[NF];  // feature of slot r: coordinates and kind
+  int16_t phi_slot[DPHI];          // slot holding phi row f (-1: constant row)
+};
+
+__host__ __device__ constexpr int slot_d(int kb, int s) { return 2 * (kb - 1) + 1 + s / 4; }
+
+constexpr SlotTables make_tables() {
+  SlotTables t{};
+  for (int r = 0; r < NF; ++r) {
+    const int kb = r / 32, g = (r % 32) / 8, s = r % 8;
+    int A = 0, B = 0, ty = 0;
+    if (kb == 0) {
+      A = s % 4;
+      B = A;
+      ty = s < 4 ? LIN : DIAG;
+    } else {
+      const int d = slot_d(kb, s);
+      A = s % 4;
+      B = A + d;
+      ty = d == 8 ? HALF : OFF;
+    }
+    t.a[r] = (uint8_t)((A + 4 * g) % 16);
+    t.b[r] = (uint8_t)((B + 4 * g) % 16);
+    t.type[r] = (uint8_t)ty;
+  }
+  t.phi_slot[0] = -1;
+  for (int f = 1; f < DPHI; ++f) {
+    int want_a = 0, want_b = 0, want_t = 0;
+    if (f < 1 + DK) {
+      want_a = f - 1; want_b = f - 1; want_t = LIN;
+    } else {
+      const int a = (f - 1 - DK) / DK, b = (f - 1 - DK) % DK;
+      want_a = a < b ? a : b; want_b = a < b ? b : a;
+      want_t = a == b ? DIAG : OFF;
+    }
+    t.phi_slot[f] = -2;
+    for (int r = 0; r < NF && t.phi_slot[f] == -2; ++r) {
+      const int ty = t.type[r];
+      const int lo = t.a[r] < t.b[r] ? t.a[r] : t.b[r], hi = t.a[r] < t.b[r] ? t.b[r] : t.a[r];
+      if (want_t == LIN ? (ty == LIN && t.a[r] == want_a)
+                        : (want_t == DIAG ? (ty == DIAG && t.a[r] == want_a)
+                                          : ((ty == OFF || ty == HALF) && lo == want_a && hi == want_b)))
+        t.phi_slot[f] = (int16_t)r;
+    }
+  }
+  return t;
+}
+constexpr SlotTables kTables = make_tables();
+__constant__ SlotTables c_tab = make_tables();
+
+constexpr bool tables_ok() {
+  for (int f = 1; f < DPHI; ++f)
+    if (kTables.phi_slot[f] < 0) return false;
+  // every unordered pair covered exactly once (HALF pairs: twice)
+  int cnt[DK][DK] = {};
+  for (int r = 0; r < NF; ++r) {
+    if (kTables.type[r] == LIN) continue;
+    const int a = kTables.a[r], b = kTables.b[r];
+    const int lo = a < b ? a : b, hi = a < b ? b : a;
+    cnt[lo][hi] += kTables.type[r] == HALF ? 1 : 2;
+  }
+  for (int a = 0; a < DK; ++a)
+    for (int b = a; b < DK; ++b)
+      if (cnt[a][b] != 2) return false;
+  return true;
+}
+static_assert(tables_ok(), "feature slot layout must cover every pair");
+
+// Value of the compact state (key-side convention: sum over tokens of
+// [k_a | k_a^2 | k_a k_b] v) for slot r, column c, from a 273-row phi state.
+__device__ __forceinline__ float compact_from_phi(const float* S, int r, int c, int ld) {
+  const int a = c_tab.a[r], b = c_tab.b[r], ty = c_tab.type[r];
+  if (ty == LIN) return S[(size_t)(1 + a) * ld + c];
+  if (ty == DIAG) return SQRT2 * S[(size_t)(1 + DK + DK * a + a) * ld + c];
+  return (S[(size_t)(1 + DK + DK * a + b) * ld + c] + S[(size_t)(1 + DK + DK * b + a) * ld + c]) * INV_SQRT2;
+}
+
+struct Params {
+  const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
+  const float* S_in; const float* z_in; float* S_out; float* z_out;
+  float* ws;        // [BH][nseg][NF+1][DV] compact state records (row NF = constant row)
+  float* wsz;       // [BH][nseg][NF+1] likewise for z (entry NF = constant: token count)
+  int L, nseg, seg_chunks;
+};
+
+template <int NT, bool FULL>
+struct Smem {
+  static constexpr int DV = 16 * NT;
+  float qs[FULL ? 2 : 1][C][QS];
+  bf16_t qb[FULL ? 2 : 1][C][QKB];
+  bf16_t kb[FULL ? 2 : 1][C][QKB];
+  float kt[2][DK + 1][KT];
+  bf16_t vt[2][DV][VT];
+  bf16_t tt[FULL ? 2 : 1][DV][TT];  // state^T, hi and lo; reused as fp32 staging at the end
+  float t0[DV];
+  float zf[NF];
+};
+
+__device__ __forceinline__ void split8(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)p[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(p[i] - (float)h);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Registers holding one chunk's inputs on their way from HBM to LDS.
+template <int NT>
+struct Prefetch {
+  static constexpr int NV = NT / 2;  // uint4 of v per thread
+  uint4 qk;
+  uint4 v[NV];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_chunk(const Params& p, size_t bh, int t0, int n, Prefetch<NT>& pf) {
+  constexpr int DV = 16 * NT;
+  const int tid = threadIdx.x;
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  {
+    const int u = tid & 127, j = u >> 1, h = u & 1;
+    const bf16_t* src = (tid < 128 ? p.q : p.k) + (bh * p.L + t0 + j) * DK + 8 * h;
+    pf.qk = j < n ? *reinterpret_cast<const uint4*>(src) : zero;
+  }
+#pragma unroll
+  for (int i = 0; i < Prefetch<NT>::NV; ++i) {
+    const int u = tid + NTHR * i;
+    const int j = u / (DV / 8), c8 = u % (DV / 8);
+    pf.v[i] = j < n ? *reinterpret_cast<const uint4*>(p.v + (bh * p.L + t0 + j) * DV + 8 * c8) : zero;
+  }
+}
+
+template <int NT, bool FULL>
+__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, int buf, const Prefetch<NT>& pf) {
+  constexpr int DV = 16 * NT;
+  const int tid = threadIdx.x;
+  {
+    const int u = tid & 127, j = u >> 1, h = u & 1;
+    const uint32_t w[4] = {pf.qk.x, pf.qk.y, pf.qk.z, pf.qk.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    if (tid < 128) {
+      if constexpr (FULL) {
+        *reinterpret_cast<uint4*>(&S.qb[buf][j][8 * h]) = pf.qk;
+        *reinterpret_cast<float4*>(&S.qs[buf][j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(&S.qs[buf][j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    } else {
+      if constexpr (FULL) *reinterpret_cast<uint4*>(&S.kb[buf][j][8 * h]) = pf.qk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S.kt[buf][8 * h + i][j] = f[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Prefetch<NT>::NV; ++i) {
+    const int u = tid + NTHR * i;
+    const int j = u / (DV / 8), c8 = u % (DV / 8);
+    const uint32_t w[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S.vt[buf][8 * c8 + 2 * e][j] = (bf16_t)(w[e] & 0xffffu);
+      S.vt[buf][8 * c8 + 2 * e + 1][j] = (bf16_t)(w[e] >> 16);
+    }
+  }
+}
+
+// The wavefront-W part of the state: pairs [W*PPW, (W+1)*PPW) of the
+// (feature tile m in 0..9) x (column tile n) grid, m-major.
+template <int NT>
+struct Own {
+  static constexpr int PPW = 10 * NT / 4;
+};
+
+// State update of one chunk for wavefront W: tacc += psi'(K)^T V over the
+// chunk, and the z increments of the feature tiles whose column tile 0 it owns.
+template <int NT, bool FULL, int W>
+__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, int buf, f32x4 (&tacc)[Own<NT>::PPW],
+                                             float (&zinc)[3]) {
+  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
+  constexpr int M0 = P0 / NT, M1 = (P0 + PPW - 1) / NT;
+  constexpr int NM = M1 - M0 + 1;
+  static_assert(NM <= 3, "a wavefront spans at most 3 feature tiles");
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  bf16x8 ahi[NM][2], alo[NM][2];
+#pragma unroll
+  for (int mm = 0; mm < NM; ++mm) {
+    const int r = 16 * (M0 + mm) + r16;
+    const int ty = c_tab.type[r];
+    const int ia = c_tab.a[r];
+    const int ib = ty == LIN ? ONES : (ty == DIAG ? ia : c_tab.b[r]);
+    float zs = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float4* pa = reinterpret_cast<const float4*>(&S.kt[buf][ia][32 * ks + 8 * g]);
+      const float4* pb = reinterpret_cast<const float4*>(&S.kt[buf][ib][32 * ks + 8 * g]);
+      const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+      float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
+                     a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zs += pr[i];
+      split8(pr, ahi[mm][ks], alo[mm][ks]);
+    }
+    zinc[mm] = zs;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 bv[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      bv[n] = *reinterpret_cast<const bf16x8*>(&S.vt[buf][16 * n + r16][32 * ks + 8 * g]);
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
+      tacc[j] = mfma(ahi[m][ks], bv[n], tacc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
+      tacc[j] = mfma(alo[m][ks], bv[n], tacc[j]);
+    }
+  }
+}
+
+// Re-split the owned state tiles into bf16 hi/lo rows of S.tt and add the z
+// increments (the caller has synchronised: nobody reads tt/zf meanwhile).
+template <int NT, bool FULL, int W, bool WITH_Z = true>
+__device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW],
+                                              const float (&zinc)[3]) {
+  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
+  constexpr int M0 = P0 / NT, M1 = (P0 + PPW - 1) / NT;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  if constexpr (FULL) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int m = (P0 + j) / NT, n = (P0 + j) % NT;
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)tacc[j][i];
+        hi[i] = h;
+        lo[i] = (__bf16)(tacc[j][i] - (float)h);
+      }
+      *reinterpret_cast<bf16x4*>(&S.tt[0][16 * n + r16][16 * m + 4 * g]) = hi;
+      *reinterpret_cast<bf16x4*>(&S.tt[1][16 * n + r16][16 * m + 4 * g]) = lo;
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm <= M1 - M0; ++mm) {
+    const int m = M0 + mm;
+    if (WITH_Z && m * NT >= P0) {  // this wavefront owns (m, column tile 0): it keeps z of tile m
+      float z = zinc[mm];
+      z += __shfl_xor(z, 16, 64);
+      z += __shfl_xor(z, 32, 64);
+      if (g == 0) S.zf[16 * m + r16] += z;
+    }
+  }
+}
+
+// Initial state tiles of wavefront W: from a compact state in the workspace
+// ([NF+1][DV], row NF = constant), else from the caller's phi-layout S_in,
+// else zero.
+template <int NT, bool FULL, int W>
+__device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
+  constexpr int DV = 16 * NT;
+  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int m = (P0 + j) / NT, n = (P0 + j) % NT;
+    const int c = 16 * n + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * m + 4 * g + i;
+      tacc[j][i] = compact ? compact[(size_t)r * DV + c] : (Sin ? compact_from_phi(Sin, r, c, DV) : 0.f);
+    }
+  }
+}
+
+// Write the owned state tiles (and, from every thread, t0 / zf / z0) to a
+// compact [NF+1][DV] + [NF+1] workspace record.
+template <int NT, bool FULL>
+__device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW], float z0,
+                                              float* dst, float* dz) {
+  constexpr int DV = 16 * NT;
+  constexpr int PPW = Own<NT>::PPW;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int pp = w * PPW + j, m = pp / NT, nn = pp % NT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
+  }
+  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = S.t0[c];
+  for (int r = tid; r < NF; r += NTHR) dz[r] = S.zf[r];
+  if (tid == 0) dz[NF] = z0;
+}
+
+template <int NT, bool FULL>
+__global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
+  constexpr int DV = 16 * NT;
+  constexpr int PPW = Own<NT>::PPW;
+  __shared__ Smem<NT, FULL> S;
+
+  const int nseg_here = FULL ? p.nseg : p.nseg - 1;
+  const size_t bh = blockIdx.x / nseg_here;
+  const int seg = blockIdx.x % nseg_here;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tok_begin = seg * p.seg_chunks * C;
+  const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
+
+  // ---- initial state.  One segment: the caller's S_in/z_in.  Several: the
+  // state-only pass (segment s < nseg-1) starts segment 0 from S_in and the
+  // others from zero and records increments; the main pass starts segment s
+  // from the prefix record ws[s].  So S_in is read only before the main pass
+  // and S_out (written by the last segment) may alias it.
+  const size_t rec = (size_t)(NF + 1) * DV;
+  const float* src = nullptr;   // compact record to start from
+  const float* srcz = nullptr;
+  const float* Sin = nullptr;
+  const float* zin = nullptr;
+  if (p.nseg > 1 && FULL) {
+    src = p.ws + (bh * p.nseg + seg) * rec;
+    srcz = p.wsz + (bh * p.nseg + seg) * (size_t)(NF + 1);
+  } else if (FULL || seg == 0) {
+    Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
+    zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
+  }
+  f32x4 tacc[PPW];
+  switch (w) {
+    case 0: init_state<NT, FULL, 0>(src, Sin, tacc); break;
+    case 1: init_state<NT, FULL, 1>(src, Sin, tacc); break;
+    case 2: init_state<NT, FULL, 2>(src, Sin, tacc); break;
+    default: init_state<NT, FULL, 3>(src, Sin, tacc); break;
+  }
+  for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
+  for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
+  float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
+  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = 1.f;
+  __syncthreads();
+  if constexpr (!FULL) {
+    if (seg == 0)  // record 0: the initial state of the whole sequence
+      write_compact<NT, FULL>(S, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
+  }
+  {
+    const float zinc[3] = {0.f, 0.f, 0.f};
+    switch (w) {
+      case 0: publish_state<NT, FULL, 0, false>(S, tacc, zinc); break;
+      case 1: publish_state<NT, FULL, 1, false>(S, tacc, zinc); break;
+      case 2: publish_state<NT, FULL, 2, false>(S, tacc, zinc); break;
+      default: publish_state<NT, FULL, 3, false>(S, tacc, zinc); break;
+    }
+  }
+
+  Prefetch<NT> pf;
+  int buf = 0;
+  if (tok_begin < tok_end) {
+    load_chunk<NT>(p, bh, tok_begin, min(C, tok_end - tok_begin), pf);
+    store_chunk<NT, FULL>(S, 0, pf);
+  }
+
+  for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
+    const int n = min(C, tok_end - t0);
+    __syncthreads();  // chunk inputs, state hi/lo, t0 and zf visible
+    const int tn = t0 + C;
+    if (tn < tok_end) load_chunk<NT>(p, bh, tn, min(C, tok_end - tn), pf);
+
+    // ---- constant row of the state: column sums of v over the chunk
+    float vsum = 0.f;
+    if (tid < DV) {
+#pragma unroll
+      for (int j = 0; j < C; j += 8) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[buf][tid][j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsum += (float)x[e];
+      }
+    }
+
+    if constexpr (FULL) {
+      // ---- readout of the state before the chunk: positions 16w + r16
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float qr[16];
+      {
+        const int tok = 16 * w + r16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 x = *reinterpret_cast<const float4*>(&S.qs[buf][tok][4 * ((g + m) & 3)]);
+          qr[4 * m] = x.x; qr[4 * m + 1] = x.y; qr[4 * m + 2] = x.z; qr[4 * m + 3] = x.w;
+        }
+      }
+      float dpart = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float f[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (kb == 0) {
+            f[s] = s < 4 ? qr[s] : 0.5f * qr[s - 4] * qr[s - 4];
+          } else {
+            const int d = slot_d(kb, s), A = s % 4, B = (A + d) % 16;
+            f[s] = (d == 8 ? 0.5f : 1.f) * qr[A] * qr[B];
+          }
+        }
+        const float4 z0v = *reinterpret_cast<const float4*>(&S.zf[32 * kb + 8 * g]);
+        const float4 z1v = *reinterpret_cast<const float4*>(&S.zf[32 * kb + 8 * g + 4]);
+        dpart += f[0] * z0v.x + f[1] * z0v.y + f[2] * z0v.z + f[3] * z0v.w + f[4] * z1v.x + f[5] * z1v.y +
+                 f[6] * z1v.z + f[7] * z1v.w;
+        bf16x8 ahi, alo;
+        split8(f, ahi, alo);
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) {
+          const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(&S.tt[0][16 * nn + r16][32 * kb + 8 * g]);
+          const bf16x8 blo = *reinterpret_cast<const bf16x8*>(&S.tt[1][16 * nn + r16][32 * kb + 8 * g]);
+          acc[nn] = mfma(ahi, bhi, acc[nn]);
+          acc[nn] = mfma(ahi, blo, acc[nn]);
+          acc[nn] = mfma(alo, bhi, acc[nn]);
+        }
+      }
+
+      // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
+      const bf16x8 zero8 = {};
+      const bf16x8 qbv = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.qb[buf][16 * w + r16][8 * g]) : zero8;
+      float rsum = 0.f;
+      bf16x4 xh[4], xl[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        xh[m] = bf16x4{};
+        xl[m] = bf16x4{};
+        if (m <= w) {
+          const bf16x8 kav = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.kb[buf][16 * m + r16][8 * g]) : zero8;
+          const f32x4 x = mfma(kav, qbv, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = 1.f + x[i] + 0.5f * x[i] * x[i];
+            if (m == w && 4 * g + i > r16) a = 0.f;  // key after query
+            rsum += a;
+            const __bf16 h = (__bf16)a;
+            xh[m][i] = h;
+            xl[m][i] = (__bf16)(a - (float)h);
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb <= w) {
+          bf16x8 ah, al;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ah[i] = xh[2 * kb][i]; ah[4 + i] = xh[2 * kb + 1][i];
+            al[i] = xl[2 * kb][i]; al[4 + i] = xl[2 * kb + 1][i];
+          }
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&S.vt[buf][16 * nn + r16][32 * kb + 4 * g]);
+            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&S.vt[buf][16 * nn + r16][32 * kb + 16 + 4 * g]);
+            bf16x8 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { bv[i] = v0[i]; bv[4 + i] = v1[i]; }
+            acc[nn] = mfma(ah, bv, acc[nn]);
+            acc[nn] = mfma(al, bv, acc[nn]);
+          }
+        }
+      }
+
+      // ---- normalise and store: acc[nn][i] is position 16w + 4g + i, column 16nn + r16
+      dpart += __shfl_xor(dpart, 16, 64);
+      dpart += __shfl_xor(dpart, 32, 64);
+      rsum += __shfl_xor(rsum, 16, 64);
+      rsum += __shfl_xor(rsum, 32, 64);
+      const float den_tok = z0 + dpart + rsum;  // denominator of position 16w + r16
+      float rden[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rden[i] = 1.f / __shfl(den_tok, 4 * g + i, 64);
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) {
+        const int col = 16 * nn + r16;
+        const float c0 = S.t0[col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = 16 * w + 4 * g + i;
+          if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = (acc[nn][i] + c0) * rden[i];
+        }
+      }
+    }
+
+    // ---- state update with this chunk (registers only)
+    float zinc[3];
+    switch (w) {
+      case 0: update_chunk<NT, FULL, 0>(S, buf, tacc, zinc); break;
+      case 1: update_chunk<NT, FULL, 1>(S, buf, tacc, zinc); break;
+      case 2: update_chunk<NT, FULL, 2>(S, buf, tacc, zinc); break;
+      default: update_chunk<NT, FULL, 3>(S, buf, tacc, zinc); break;
+    }
+    z0 += (float)n;
+    __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
+    if (tid < DV) S.t0[tid] += vsum;
+    switch (w) {
+      case 0: publish_state<NT, FULL, 0>(S, tacc, zinc); break;
+      case 1: publish_state<NT, FULL, 1>(S, tacc, zinc); break;
+      case 2: publish_state<NT, FULL, 2>(S, tacc, zinc); break;
+      default: publish_state<NT, FULL, 3>(S, tacc, zinc); break;
+    }
+    if (tn < tok_end) store_chunk<NT, FULL>(S, buf ^ 1, pf);
+    buf ^= 1;
+  }
+  __syncthreads();
+
+  // ---- segment result: the record after segment s (state-only pass) or S_out
+  if constexpr (!FULL) {
+    write_compact<NT, FULL>(S, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
+                            p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
+  } else {
+    if (p.S_out && seg == p.nseg - 1) {
+      float* stage = reinterpret_cast<float*>(&S.tt[0][0][0]);  // [NF][DV] fp32
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) {
+        const int pp = w * PPW + j, m = pp / NT, nn = pp % NT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage[(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
+      }
+      __syncthreads();
+      float* So = p.S_out + bh * DPHI * DV;
+      for (int e = tid; e < DPHI * DV; e += NTHR) {
+        const int f = e / DV, c = e % DV;
+        const int r = c_tab.phi_slot[f];
+        float val;
+        if (r < 0) val = S.t0[c];
+        else val = c_tab.type[r] == LIN ? stage[r * DV + c] : stage[r * DV + c] * INV_SQRT2;
+        So[e] = val;
+      }
+      float* zo = p.z_out + bh * DPHI;
+      for (int f = tid; f < DPHI; f += NTHR) {
+        const int r = c_tab.phi_slot[f];
+        zo[f] = r < 0 ? z0 : (c_tab.type[r] == LIN ? S.zf[r] : S.zf[r] * INV_SQRT2);
+      }
+    }
+  }
+}
+
+// Prefix over the segment records of each (batch, head): record s holds the
+// increment of segment s-1 (record 1: the initial state plus that
+// increment); after the scan record s is the state at the start of segment s.
+__global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH) {
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t per_head = (size_t)rec + (NF + 1);
+  if (e >= per_head * BH) return;
+  const size_t bh = e / per_head, o = e % per_head;
+  float* base;
+  size_t stride;
+  if (o < (size_t)rec) {
+    base = ws + bh * nseg * (size_t)rec + o;
+    stride = rec;
+  } else {
+    base = wsz + bh * nseg * (size_t)(NF + 1) + (o - rec);
+    stride = NF + 1;
+  }
+  float run = base[stride];
+  for (int s = 2; s < nseg; ++s) {
+    run += base[s * stride];
+    base[s * stride] = run;
+  }
+}
+
+}  // namespace mfma
+
+using namespace mfma;
+
+// Segments per (batch, head): enough workgroups to cover the GPU's 256
+// compute units, each segment at least 4 chunks long.
+void linattn_mfma_plan(int BH, int L, int* nseg, int* seg_chunks) {
+  const int nch = (L + C - 1) / C;
+  int want = (256 + BH - 1) / BH;
+  int cap = nch / 4;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  const int sc = (nch + want - 1) / want;
+  *seg_chunks = sc < 1 ? 1 : sc;
+  *nseg = nch == 0 ? 1 : (nch + *seg_chunks - 1) / *seg_chunks;
+}
+
+bool linattn_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 || dv == 128; }
+
+size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
+  if (!linattn_mfma_supported(dv)) return 0;
+  int nseg, sc;
+  linattn_mfma_plan(B * H, L, &nseg, &sc);
+  if (nseg <= 1) return 0;
+  return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
+}
+
+template <int NT>
+static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
+  constexpr int DV = 16 * NT;
+  Params p{};
+  p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y;
+  p.S_in = a.S_in; p.z_in = a.z_in; p.S_out = a.S_out; p.z_out = a.z_out;
+  p.L = a.L;
+  linattn_mfma_plan(a.B * a.H, a.L, &p.nseg, &p.seg_chunks);
+  const int BH = a.B * a.H;
+  if (p.nseg > 1) {
+    p.ws = (float*)a.workspace;
+    p.wsz = p.ws + (size_t)BH * p.nseg * (NF + 1) * DV;
+    hipLaunchKernelGGL((linattn_mfma_kernel<NT, false>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (p.nseg > 2) {
+      const size_t total = (size_t)BH * ((size_t)(NF + 1) * DV + NF + 1);
+      hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p.ws, p.wsz,
+                         p.nseg, (NF + 1) * DV, BH);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL((linattn_mfma_kernel<NT, true>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t s) {
+  switch (a.dv) {
+    case 32: return launch_nt<2>(a, s);
+    case 64: return launch_nt<4>(a, s);
+    case 96: return launch_nt<6>(a, s);
+    case 128: return launch_nt<8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace based

@@ -36,7 +36,7 @@ def run_decode(based, cfg, seqs=None, check_steps=None, seed=0):
     report(f"decode y_lin B{cfg.B} ctx{cfg.ctx}", max(e[0] for e in errs), tol)
     report(f"decode y_swa B{cfg.B} ctx{cfg.ctx}", max(e[1] for e in errs), tol)
     assert rowinf_rel(st.S[seqs], ref.S) <= tol
-    assert rowinf_rel(st.z[seqs][..., None], ref.z[..., None]) <= tol
+    assert rowinf_rel(st.z[seqs], ref.z) <= tol
     assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
     return st
 
