@@ -99,7 +99,8 @@ BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* 
       overlap(ys, span(v, BH * L * d_v * es)))
     return BASED_ERR_ALIAS;
   based::SwaArgs a{q, k, v, y, B, H, L, d_qk, d_v, window, scale};
-  return status_of(based::launch_swa_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
+  if (dtype == BASED_BF16) return status_of(based::launch_swa_mfma(a, (hipStream_t)stream));
+  return status_of(based::launch_swa_valu(a, false, (hipStream_t)stream));
 }
 
 BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos, int B,

@@ -22,7 +22,7 @@ hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t stre
 // bf16 chunked linear attention on the matrix cores (d_v in {32, 64, 96, 128}).
 bool linattn_mfma_supported(int dv);
 size_t linattn_mfma_workspace(int B, int H, int L, int dv);
-void linattn_mfma_plan(int BH, int L, int* nseg, int* seg_chunks);
+void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
 
 struct SwaArgs {
@@ -30,6 +30,7 @@ struct SwaArgs {
   int B, H, L, dqk, dv, window; float scale;
 };
 hipError_t launch_swa_valu(const SwaArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_swa_mfma(const SwaArgs& a, hipStream_t stream);  // bf16 inputs
 
 struct DecodeArgs {
   const void* q; const void* k; const void* v;

@@ -145,18 +145,25 @@ struct Params {
   int L, nseg, seg_chunks;
 };
 
+// LDS.  vt is v^T with the 8-position groups of row `col` XOR-swizzled by
+// (col / 8) % 8, so that the transposing writes of a wavefront spread over all
+// banks while 8 consecutive positions stay contiguous for 16-byte reads.
 template <int NT, bool FULL>
 struct Smem {
   static constexpr int DV = 16 * NT;
-  float qs[FULL ? 2 : 1][C][QS];
-  bf16_t qb[FULL ? 2 : 1][C][QKB];
-  bf16_t kb[FULL ? 2 : 1][C][QKB];
-  float kt[2][DK + 1][KT];
-  bf16_t vt[2][DV][VT];
-  bf16_t tt[FULL ? 2 : 1][DV][TT];  // state^T, hi and lo; reused as fp32 staging at the end
-  float t0[DV];
-  float zf[NF];
+  alignas(16) float qs[FULL ? C : 1][QS];
+  alignas(16) bf16_t qb[FULL ? C : 1][QKB];
+  alignas(16) bf16_t kb[FULL ? C : 1][QKB];
+  alignas(16) float kt[DK + 1][KT];
+  alignas(16) bf16_t vt[DV][VT];
+  alignas(16) bf16_t tt[FULL ? 2 : 1][DV][TT];  // state^T, hi and lo; reused as fp32 staging at the end
+  alignas(16) float t0[DV];
+  alignas(16) float vpart[NTHR];  // partial column sums of v
+  alignas(16) float zf[NF];
 };
+
+// Column of v^T row `col` holding position t (see Smem).
+__device__ __forceinline__ int vt_pos(int col, int t) { return ((((t >> 3) ^ (col >> 3)) & 7) << 3) | (t & 7); }
 
 __device__ __forceinline__ void split8(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -179,26 +186,52 @@ struct Prefetch {
   uint4 v[NV];
 };
 
+// Buffer descriptors of one head's q, k, v: reads past the end of the
+// sequence return zero, which pads the last chunk.
+struct HeadRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v;
+};
+constexpr int RSRC_DW3 = 0x00020000;
+
+__device__ __forceinline__ HeadRsrc head_rsrc(const Params& p, size_t bh, int DV) {
+  const int nq = p.L * DK * 2, nv = p.L * DV * 2;
+  HeadRsrc r;
+  r.q = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + bh * p.L * DK), (short)0, nq, RSRC_DW3);
+  r.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + bh * p.L * DK), (short)0, nq, RSRC_DW3);
+  r.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DV), (short)0, nv, RSRC_DW3);
+  return r;
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Thread -> (position, 8 columns) of the v loads: a wavefront covers 8
+// positions x 8 column groups per load (DV = 64) so that its transposing LDS
+// writes hit distinct banks after the swizzle.
 template <int NT>
-__device__ __forceinline__ void load_chunk(const Params& p, size_t bh, int t0, int n, Prefetch<NT>& pf) {
+__device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
-  const uint4 zero = {0u, 0u, 0u, 0u};
   {
     const int u = tid & 127, j = u >> 1, h = u & 1;
-    const bf16_t* src = (tid < 128 ? p.q : p.k) + (bh * p.L + t0 + j) * DK + 8 * h;
-    pf.qk = j < n ? *reinterpret_cast<const uint4*>(src) : zero;
+    const int off = ((t0 + j) * DK + 8 * h) * 2;
+    if (tid < 128) {
+      if (q_too) pf.qk = bload(r.q, off);
+    } else {
+      pf.qk = bload(r.k, off);
+    }
   }
 #pragma unroll
   for (int i = 0; i < Prefetch<NT>::NV; ++i) {
     const int u = tid + NTHR * i;
     const int j = u / (DV / 8), c8 = u % (DV / 8);
-    pf.v[i] = j < n ? *reinterpret_cast<const uint4*>(p.v + (bh * p.L + t0 + j) * DV + 8 * c8) : zero;
+    pf.v[i] = bload(r.v, ((t0 + j) * DV + 8 * c8) * 2);
   }
 }
 
 template <int NT, bool FULL>
-__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, int buf, const Prefetch<NT>& pf) {
+__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
   {
@@ -212,14 +245,14 @@ __device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, int buf, const Pr
     }
     if (tid < 128) {
       if constexpr (FULL) {
-        *reinterpret_cast<uint4*>(&S.qb[buf][j][8 * h]) = pf.qk;
-        *reinterpret_cast<float4*>(&S.qs[buf][j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(&S.qs[buf][j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+        *reinterpret_cast<uint4*>(&S.qb[j][8 * h]) = pf.qk;
+        *reinterpret_cast<float4*>(&S.qs[j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(&S.qs[j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
       }
     } else {
-      if constexpr (FULL) *reinterpret_cast<uint4*>(&S.kb[buf][j][8 * h]) = pf.qk;
+      if constexpr (FULL) *reinterpret_cast<uint4*>(&S.kb[j][8 * h]) = pf.qk;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) S.kt[buf][8 * h + i][j] = f[i];
+      for (int i = 0; i < 8; ++i) S.kt[8 * h + i][j] = f[i];
     }
   }
 #pragma unroll
@@ -227,10 +260,11 @@ __device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, int buf, const Pr
     const int u = tid + NTHR * i;
     const int j = u / (DV / 8), c8 = u % (DV / 8);
     const uint32_t w[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
+    const int pc = vt_pos(8 * c8, j);  // the same for the 8 columns of this group
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      S.vt[buf][8 * c8 + 2 * e][j] = (bf16_t)(w[e] & 0xffffu);
-      S.vt[buf][8 * c8 + 2 * e + 1][j] = (bf16_t)(w[e] >> 16);
+      S.vt[8 * c8 + 2 * e][pc] = (bf16_t)(w[e] & 0xffffu);
+      S.vt[8 * c8 + 2 * e + 1][pc] = (bf16_t)(w[e] >> 16);
     }
   }
 }
@@ -245,49 +279,46 @@ struct Own {
 // State update of one chunk for wavefront W: tacc += psi'(K)^T V over the
 // chunk, and the z increments of the feature tiles whose column tile 0 it owns.
 template <int NT, bool FULL, int W>
-__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, int buf, f32x4 (&tacc)[Own<NT>::PPW],
-                                             float (&zinc)[3]) {
+__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Own<NT>::PPW], float (&zinc)[3],
+                                             const int (&ia_)[3], const int (&ib_)[3]) {
   constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
   constexpr int M0 = P0 / NT, M1 = (P0 + PPW - 1) / NT;
   constexpr int NM = M1 - M0 + 1;
   static_assert(NM <= 3, "a wavefront spans at most 3 feature tiles");
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  bf16x8 ahi[NM][2], alo[NM][2];
 #pragma unroll
-  for (int mm = 0; mm < NM; ++mm) {
-    const int r = 16 * (M0 + mm) + r16;
-    const int ty = c_tab.type[r];
-    const int ia = c_tab.a[r];
-    const int ib = ty == LIN ? ONES : (ty == DIAG ? ia : c_tab.b[r]);
-    float zs = 0.f;
+  for (int mm = 0; mm < NM; ++mm) zinc[mm] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const float4* pa = reinterpret_cast<const float4*>(&S.kt[buf][ia][32 * ks + 8 * g]);
-      const float4* pb = reinterpret_cast<const float4*>(&S.kt[buf][ib][32 * ks + 8 * g]);
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 ahi[NM], alo[NM];
+#pragma unroll
+    for (int mm = 0; mm < NM; ++mm) {
+      const float4* pa = reinterpret_cast<const float4*>(&S.kt[ia_[mm]][32 * ks + 8 * g]);
+      const float4* pb = reinterpret_cast<const float4*>(&S.kt[ib_[mm]][32 * ks + 8 * g]);
       const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
       float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
                      a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
+      float zs = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) zs += pr[i];
-      split8(pr, ahi[mm][ks], alo[mm][ks]);
+      zinc[mm] += zs;
+      split8(pr, ahi[mm], alo[mm]);
     }
-    zinc[mm] = zs;
-  }
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
     bf16x8 bv[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      bv[n] = *reinterpret_cast<const bf16x8*>(&S.vt[buf][16 * n + r16][32 * ks + 8 * g]);
-#pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
-      tacc[j] = mfma(ahi[m][ks], bv[n], tacc[j]);
+    for (int n = 0; n < NT; ++n) {
+      const int col = 16 * n + r16;
+      bv[n] = *reinterpret_cast<const bf16x8*>(&S.vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
-      tacc[j] = mfma(alo[m][ks], bv[n], tacc[j]);
+      tacc[j] = mfma(ahi[m], bv[n], tacc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
+      tacc[j] = mfma(alo[m], bv[n], tacc[j]);
     }
   }
 }
@@ -366,8 +397,12 @@ __device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&t
   if (tid == 0) dz[NF] = z0;
 }
 
+// Two wavefronts per SIMD (two workgroups per CU) where the LDS footprint
+// allows it (d_v <= 64), one otherwise.
+template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
+
 template <int NT, bool FULL>
-__global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
+__global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PPW = Own<NT>::PPW;
   __shared__ Smem<NT, FULL> S;
@@ -406,7 +441,7 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
   for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
   for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
   float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
-  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = 1.f;
+  for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = 1.f;
   __syncthreads();
   if constexpr (!FULL) {
     if (seg == 0)  // record 0: the initial state of the whole sequence
@@ -422,28 +457,45 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
     }
   }
 
+  // update-operand rows of this wavefront's feature tiles (loop invariant)
+  int ia[3], ib[3];
+  {
+    const int m0 = (w * PPW) / NT;
+#pragma unroll
+    for (int mm = 0; mm < 3; ++mm) {
+      const int r = min(16 * (m0 + mm) + r16, NF - 1);
+      const int ty = c_tab.type[r];
+      ia[mm] = c_tab.a[r];
+      ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
+    }
+  }
+
+  const HeadRsrc rs = head_rsrc(p, bh, DV);
   Prefetch<NT> pf;
-  int buf = 0;
   if (tok_begin < tok_end) {
-    load_chunk<NT>(p, bh, tok_begin, min(C, tok_end - tok_begin), pf);
-    store_chunk<NT, FULL>(S, 0, pf);
+    load_chunk<NT>(rs, tok_begin, FULL, pf);
+    store_chunk<NT, FULL>(S, pf);
   }
 
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
     const int n = min(C, tok_end - t0);
     __syncthreads();  // chunk inputs, state hi/lo, t0 and zf visible
     const int tn = t0 + C;
-    if (tn < tok_end) load_chunk<NT>(p, bh, tn, min(C, tok_end - tn), pf);
+    if (tn < tok_end) load_chunk<NT>(rs, tn, FULL, pf);
 
-    // ---- constant row of the state: column sums of v over the chunk
-    float vsum = 0.f;
-    if (tid < DV) {
+    // ---- constant row of the state: column sums of v over the chunk, in
+    // NTHR / DV partial sums per column (order within a row is irrelevant)
+    {
+      constexpr int PARTS = NTHR / DV, SPAN = C / PARTS;
+      const int col = tid % DV, part = tid / DV;
+      float vs = 0.f;
 #pragma unroll
-      for (int j = 0; j < C; j += 8) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[buf][tid][j]);
+      for (int j = 0; j < SPAN; j += 8) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[col][part * SPAN + j]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vsum += (float)x[e];
+        for (int e = 0; e < 8; ++e) vs += (float)x[e];
       }
+      S.vpart[tid] = vs;
     }
 
     if constexpr (FULL) {
@@ -456,7 +508,7 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
         const int tok = 16 * w + r16;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float4 x = *reinterpret_cast<const float4*>(&S.qs[buf][tok][4 * ((g + m) & 3)]);
+          const float4 x = *reinterpret_cast<const float4*>(&S.qs[tok][4 * ((g + m) & 3)]);
           qr[4 * m] = x.x; qr[4 * m + 1] = x.y; qr[4 * m + 2] = x.z; qr[4 * m + 3] = x.w;
         }
       }
@@ -491,7 +543,7 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
 
       // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
       const bf16x8 zero8 = {};
-      const bf16x8 qbv = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.qb[buf][16 * w + r16][8 * g]) : zero8;
+      const bf16x8 qbv = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.qb[16 * w + r16][8 * g]) : zero8;
       float rsum = 0.f;
       bf16x4 xh[4], xl[4];
 #pragma unroll
@@ -499,7 +551,7 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
         xh[m] = bf16x4{};
         xl[m] = bf16x4{};
         if (m <= w) {
-          const bf16x8 kav = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.kb[buf][16 * m + r16][8 * g]) : zero8;
+          const bf16x8 kav = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.kb[16 * m + r16][8 * g]) : zero8;
           const f32x4 x = mfma(kav, qbv, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -523,8 +575,9 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
           }
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
-            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&S.vt[buf][16 * nn + r16][32 * kb + 4 * g]);
-            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&S.vt[buf][16 * nn + r16][32 * kb + 16 + 4 * g]);
+            const int col = 16 * nn + r16;
+            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&S.vt[col][vt_pos(col, 32 * kb + 4 * g)]);
+            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&S.vt[col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
             bf16x8 bv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) { bv[i] = v0[i]; bv[4 + i] = v1[i]; }
@@ -558,22 +611,26 @@ __global__ __launch_bounds__(NTHR, 1) void linattn_mfma_kernel(Params p) {
     // ---- state update with this chunk (registers only)
     float zinc[3];
     switch (w) {
-      case 0: update_chunk<NT, FULL, 0>(S, buf, tacc, zinc); break;
-      case 1: update_chunk<NT, FULL, 1>(S, buf, tacc, zinc); break;
-      case 2: update_chunk<NT, FULL, 2>(S, buf, tacc, zinc); break;
-      default: update_chunk<NT, FULL, 3>(S, buf, tacc, zinc); break;
+      case 0: update_chunk<NT, FULL, 0>(S, tacc, zinc, ia, ib); break;
+      case 1: update_chunk<NT, FULL, 1>(S, tacc, zinc, ia, ib); break;
+      case 2: update_chunk<NT, FULL, 2>(S, tacc, zinc, ia, ib); break;
+      default: update_chunk<NT, FULL, 3>(S, tacc, zinc, ia, ib); break;
     }
     z0 += (float)n;
     __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
-    if (tid < DV) S.t0[tid] += vsum;
+    if (tid < DV) {
+      float vs = 0.f;
+#pragma unroll
+      for (int part = 0; part < NTHR / DV; ++part) vs += S.vpart[part * DV + tid];
+      S.t0[tid] += vs;
+    }
     switch (w) {
       case 0: publish_state<NT, FULL, 0>(S, tacc, zinc); break;
       case 1: publish_state<NT, FULL, 1>(S, tacc, zinc); break;
       case 2: publish_state<NT, FULL, 2>(S, tacc, zinc); break;
       default: publish_state<NT, FULL, 3>(S, tacc, zinc); break;
     }
-    if (tn < tok_end) store_chunk<NT, FULL>(S, buf ^ 1, pf);
-    buf ^= 1;
+    if (tn < tok_end) store_chunk<NT, FULL>(S, pf);
   }
   __syncthreads();
 
@@ -637,11 +694,13 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
 
 using namespace mfma;
 
-// Segments per (batch, head): enough workgroups to cover the GPU's 256
-// compute units, each segment at least 4 chunks long.
-void linattn_mfma_plan(int BH, int L, int* nseg, int* seg_chunks) {
+// Segments per (batch, head): enough workgroups to fill the GPU's 256
+// compute units (two per CU where they fit: d_v <= 64), each segment at
+// least 4 chunks long.
+void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
   const int nch = (L + C - 1) / C;
-  int want = (256 + BH - 1) / BH;
+  const int slots = dv <= 64 ? 512 : 256;
+  int want = (slots + BH - 1) / BH;
   int cap = nch / 4;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
@@ -656,7 +715,7 @@ bool linattn_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 ||
 size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
   if (!linattn_mfma_supported(dv)) return 0;
   int nseg, sc;
-  linattn_mfma_plan(B * H, L, &nseg, &sc);
+  linattn_mfma_plan(B * H, L, dv, &nseg, &sc);
   if (nseg <= 1) return 0;
   return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
 }
@@ -668,7 +727,7 @@ static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y;
   p.S_in = a.S_in; p.z_in = a.z_in; p.S_out = a.S_out; p.z_out = a.z_out;
   p.L = a.L;
-  linattn_mfma_plan(a.B * a.H, a.L, &p.nseg, &p.seg_chunks);
+  linattn_mfma_plan(a.B * a.H, a.L, DV, &p.nseg, &p.seg_chunks);
   const int BH = a.B * a.H;
   if (p.nseg > 1) {
     p.ws = (float*)a.workspace;

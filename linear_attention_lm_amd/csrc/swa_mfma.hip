@@ -1,0 +1,239 @@
+// Causal sliding-window softmax attention on bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation): the bf16 path of
+// based_swa_fwd.
+//
+// Definition (HazyResearch/based README, introduction: exact softmax
+// attention over a short window of recent tokens): row i attends to
+// positions max(0, i - window + 1) .. i with weights exp(s_j - max s) / sum,
+// s_j = scale * q_i.k_j.
+//
+// Layout of the work: a workgroup (4 wavefronts) walks a segment of a
+// (batch, head) sequence in blocks of 64 queries.  The keys/values of the
+// current and the previous block sit in an LDS ring (each K/V row is read
+// from HBM once per segment); wavefront w owns queries 16w..16w+15 of the
+// block, whose keys span 5 tiles of 16.  Scores are computed transposed
+// (keys x queries) so that each lane holds 4 keys of one query: the softmax
+// row statistics need only in-register work plus two cross-lane steps, and
+// the probabilities already sit in the A-operand layout of the P.V product
+// (keys permuted consistently in the B operand).  P is fp32; it enters the
+// matrix product as hi + lo bf16 (exact to ~16 bits), V is exact in bf16.
+#include "based_device.h"
+#include "launchers.h"
+
+namespace based {
+namespace swa_mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QB = 64;         // queries per block
+constexpr int NTHR = 256;      // 4 wavefronts
+constexpr int RING = 2 * QB;   // key positions held in LDS
+constexpr int VTS = RING + 8;  // v^T row stride (bf16)
+constexpr int SEG_BLOCKS = 8;  // query blocks per workgroup
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int RSRC_DW3 = 0x00020000;
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Ring column of key position p in v^T row `col`: 8-position groups are
+// XOR-swizzled by (col / 8) so the transposing writes spread over the banks.
+__device__ __forceinline__ int vt_pos(int col, int p) {
+  const int r = p & (RING - 1);
+  return ((((r >> 3) ^ (col >> 3)) & 15) << 3) | (r & 7);
+}
+
+struct Params {
+  const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
+  int L, dqk, window, nseg;
+  float scale;
+};
+
+// Dynamic LDS: k ring [RING][dqk + 8] bf16, then v^T ring [DV][VTS] bf16.
+template <int NT>
+__global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
+  constexpr int DV = 16 * NT;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int ks_stride = p.dqk + 8;
+  bf16_t* kring = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* vt = kring + RING * ks_stride;
+
+  const size_t bh = blockIdx.x / p.nseg;
+  const int seg = blockIdx.x % p.nseg;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int nblk = (p.L + QB - 1) / QB;
+  const int b_begin = seg * SEG_BLOCKS, b_end = min(nblk, b_begin + SEG_BLOCKS);
+
+  const int qbytes = p.L * p.dqk * 2;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + bh * p.L * p.dqk), (short)0, qbytes, RSRC_DW3);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + bh * p.L * p.dqk), (short)0, qbytes, RSRC_DW3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DV), (short)0, p.L * DV * 2, RSRC_DW3);
+
+  // Stage keys/values of block b into the ring (positions 64b .. 64b+63;
+  // positions outside 0..L-1 read as zero and are masked later).
+  auto stage = [&](int b) {
+    const int pos0 = b * QB;
+    const int kchunks = QB * p.dqk / 8;  // 16-byte pieces of the k block
+    for (int u = tid; u < kchunks; u += NTHR) {
+      const int j = u / (p.dqk / 8), c8 = u % (p.dqk / 8);
+      const int pos = pos0 + j;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (pos >= 0) x = bload(rk, (pos * p.dqk + 8 * c8) * 2);
+      *reinterpret_cast<uint4*>(&kring[(pos & (RING - 1)) * ks_stride + 8 * c8]) = x;
+    }
+    constexpr int vchunks = QB * DV / 8;
+    for (int u = tid; u < vchunks; u += NTHR) {
+      const int j = u % QB, c8 = u / QB;  // a wavefront writes 64 positions of one column group
+      const int pos = pos0 + j;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (pos >= 0) x = bload(rv, (pos * DV + 8 * c8) * 2);
+      const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+      const int col0 = 8 * c8;
+      const int pc = vt_pos(col0, pos);  // same for the 8 columns of this group
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(col0 + 2 * e) * VTS + pc] = (bf16_t)(wv[e] & 0xffffu);
+        vt[(col0 + 2 * e + 1) * VTS + pc] = (bf16_t)(wv[e] >> 16);
+      }
+    }
+  };
+
+  if (b_begin < b_end) stage(b_begin - 1);
+  const bf16x8 zero8 = {};
+  for (int b = b_begin; b < b_end; ++b) {
+    stage(b);
+    __syncthreads();
+
+    const int q0 = b * QB + 16 * w;  // first query of this wavefront
+    const int qi = q0 + r16;         // the query column this lane holds
+    // scores X^T (keys x queries) for the 5 key tiles of 16 ending at q0 + 15
+    f32x4 x[5];
+#pragma unroll
+    for (int m = 0; m < 5; ++m) x[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d0 = 0; d0 < p.dqk; d0 += 32) {
+      const int d = d0 + 8 * g;
+      const bf16x8 qv = d < p.dqk ? __builtin_bit_cast(bf16x8, bload(rq, (qi * p.dqk + d) * 2)) : zero8;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        const int key = q0 - 64 + 16 * m + r16;
+        const bf16x8 kv = d < p.dqk ? *reinterpret_cast<const bf16x8*>(&kring[(key & (RING - 1)) * ks_stride + d]) : zero8;
+        x[m] = mfma(kv, qv, x[m]);
+      }
+    }
+    // softmax statistics of query qi over its window
+    float mx = -INFINITY;
+    float s[5][4];
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = q0 - 64 + 16 * m + 4 * g + i;
+        const bool ok = key <= qi && key > qi - p.window && key >= 0;
+        s[m][i] = ok ? p.scale * x[m][i] : -INFINITY;
+        mx = fmaxf(mx, s[m][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float den = 0.f;
+    bf16x4 ph[6], pl[6];
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = s[m][i] == -INFINITY ? 0.f : __expf(s[m][i] - mx);
+        const __bf16 h = (__bf16)e;
+        const __bf16 l = (__bf16)(e - (float)h);
+        ph[m][i] = h;
+        pl[m][i] = l;
+        den += (float)h + (float)l;
+      }
+    ph[5] = bf16x4{};
+    pl[5] = bf16x4{};
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
+
+    // Y = P V over the three 32-key blocks (tile pairs (0,1), (2,3), (4,-))
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+      bf16x8 ah, al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ah[i] = ph[2 * kb][i]; ah[4 + i] = ph[2 * kb + 1][i];
+        al[i] = pl[2 * kb][i]; al[4 + i] = pl[2 * kb + 1][i];
+      }
+      const int k0 = q0 - 64 + 32 * kb + 4 * g;  // keys of slots 0..3; slots 4..7 are 16 later
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) {
+        const int col = 16 * nn + r16;
+        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&vt[col * VTS + vt_pos(col, k0)]);
+        bf16x4 v1 = bf16x4{};
+        if (kb < 2) v1 = *reinterpret_cast<const bf16x4*>(&vt[col * VTS + vt_pos(col, k0 + 16)]);
+        bf16x8 bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { bv[i] = v0[i]; bv[4 + i] = v1[i]; }
+        acc[nn] = mfma(ah, bv, acc[nn]);
+        acc[nn] = mfma(al, bv, acc[nn]);
+      }
+    }
+    float rden[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rden[i] = 1.f / __shfl(den, 4 * g + i, 64);
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+      const int col = 16 * nn + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qq = q0 + 4 * g + i;
+        if (qq < p.L) p.y[(bh * p.L + qq) * DV + col] = acc[nn][i] * rden[i];
+      }
+    }
+    __syncthreads();  // the ring slot of block b-1 is reused by block b+1
+  }
+}
+
+template <int NT>
+static hipError_t launch_nt(const SwaArgs& a, hipStream_t s) {
+  constexpr int DV = 16 * NT;
+  Params p{};
+  p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y;
+  p.L = a.L; p.dqk = a.dqk; p.window = a.window; p.scale = a.scale;
+  const int nblk = (a.L + QB - 1) / QB;
+  p.nseg = (nblk + SEG_BLOCKS - 1) / SEG_BLOCKS;
+  const size_t lds = (size_t)RING * (a.dqk + 8) * 2 + (size_t)DV * VTS * 2;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)swa_mfma_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(swa_mfma_kernel<NT>, dim3((unsigned)(a.B * a.H * p.nseg)), dim3(NTHR), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace swa_mfma
+
+hipError_t launch_swa_mfma(const SwaArgs& a, hipStream_t s) {
+  if (a.L == 0) return hipSuccess;
+  switch (a.dv) {
+    case 16: return swa_mfma::launch_nt<1>(a, s);
+    case 32: return swa_mfma::launch_nt<2>(a, s);
+    case 48: return swa_mfma::launch_nt<3>(a, s);
+    case 64: return swa_mfma::launch_nt<4>(a, s);
+    case 80: return swa_mfma::launch_nt<5>(a, s);
+    case 96: return swa_mfma::launch_nt<6>(a, s);
+    case 112: return swa_mfma::launch_nt<7>(a, s);
+    case 128: return swa_mfma::launch_nt<8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace based
