@@ -24,6 +24,9 @@ bounded sample of the step's workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -64,6 +67,62 @@ def decode_bytes(dv=64, window=64, es=2):
     window-1 slots read, q/k/v read, one ring slot written, y_lin and y_swa written."""
     return (2 * D_PHI * dv * 4 + 2 * D_PHI * 4 + (window - 1) * (16 + dv) * es + (2 * 16 + dv) * es
             + (16 + dv) * es + 2 * dv * 4)
+
+
+# Kernel sources each timed operation is built from (a profile taken on other
+# sources no longer describes the kernel).
+OP_SOURCES = {
+    "linattn": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
+    "swa": ["swa_mfma.hip", "launchers.h", "based_device.h"],
+    "decode": ["decode.hip", "launchers.h", "based_device.h"],
+}
+# rocprofv3 kernel-name fragments of each operation's launches
+OP_KERNELS = {
+    "linattn": ["linattn_mfma_kernel", "seg_scan_kernel"],
+    "swa": ["swa_mfma_kernel"],
+    "decode": ["decode_step_kernel"],
+}
+COPY_BYTES = 512 << 20
+
+
+def source_hash(op):
+    h = hashlib.sha256()
+    for f in OP_SOURCES[op]:
+        with open(os.path.join(ROOT, "linear_attention_lm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(reps=10):
+    """A plain device copy of COPY_BYTES: the bandwidth this GPU reaches on a
+    streaming kernel, and the reference that scales the FETCH_SIZE /
+    WRITE_SIZE counters to bytes."""
+    src = torch.empty(COPY_BYTES // 4, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "us": ms * 1e3,
+            "gbs": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
+
+
+def load_traffic(op):
+    """Measured HBM bytes per call of `op` from the committed counter profile,
+    or None when the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash(op):
+        return None
+    return rec["bytes_per_call"]
 
 
 class StreamTimer:
@@ -190,6 +249,114 @@ def cpu_baseline(cfg, budget_s=12.0):
     }
 
 
+def _counter_rows(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, calls, command):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE) into profiles/traffic_<op>.json: HBM bytes per call
+    of each timed operation, scaled by the counters' reading for the copy
+    calibration kernel of known size."""
+    def per_dispatch(rows, counter):
+        """(dispatch id, kernel name) -> bytes (summed over the counter's instances)."""
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0  # KiB -> B
+        return acc
+
+    def by_kernel(acc, lo, hi):
+        out = {}
+        for (i, name), val in sorted(acc.items()):
+            if lo <= i <= hi:
+                out.setdefault(name, []).append(val)
+        return out
+
+    fetch_all = per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write_all = per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
+    everything = by_kernel(fetch_all, 0, 1 << 60)
+    copy_names = [k for k in everything if "copy" in k.lower() or "elementwise" in k.lower()]
+    big = [k for k in copy_names if max(everything[k]) > 0.5 * COPY_BYTES]
+    if not big:
+        raise SystemExit("no copy calibration kernel found in the FETCH_SIZE run")
+    cname = big[0]
+    cw = by_kernel(write_all, 0, 1 << 60)[cname]
+    f_copy = sorted(everything[cname])[len(everything[cname]) // 2]
+    w_copy = sorted(cw)[len(cw) // 2]
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    # the step workload runs first; its last dispatch is the calls-th window-attention launch
+    swa_ids = sorted(i for (i, n) in fetch_all if "swa_mfma_kernel" in n)
+    step_end = swa_ids[calls - 1]
+    windows = {"linattn": (0, step_end), "swa": (0, step_end), "decode": (step_end + 1, 1 << 60)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    workloads = {"linattn": "based360m", "swa": "based360m", "decode": "decode (256 x 16 heads)"}
+    for op, frags in OP_KERNELS.items():
+        tot_f = tot_w = 0.0
+        detail = {}
+        fetch = by_kernel(fetch_all, *windows[op])
+        write = by_kernel(write_all, *windows[op])
+        for name, vals in fetch.items():
+            if any(fr in name for fr in frags):
+                wv = write.get(name, [0.0])
+                med_f = sorted(vals)[len(vals) // 2] * f_scale
+                med_w = sorted(wv)[len(wv) // 2] * w_scale
+                detail[name.split("(")[0]] = {"fetch_bytes": med_f, "write_bytes": med_w, "dispatches": len(vals)}
+                tot_f += med_f
+                tot_w += med_w
+        if not detail:
+            continue
+        rec = {"op": op, "workload": workloads[op], "source_hash": source_hash(op), "command": command,
+               "copy_kernel": cname.split("(")[0], "copy_fetch_factor": f_scale, "copy_write_factor": w_scale,
+               "bytes_per_call": tot_f + tot_w, "fetch_bytes_per_call": tot_f, "write_bytes_per_call": tot_w,
+               "kernels": detail}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{op}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec, indent=1))
+
+
+def summarize_stats(stats_dir, command, calls):
+    """profiles/kernel_stats.md from a rocprofv3 --kernel-trace --stats run of
+    this script: average duration of every kernel.  The step workload runs
+    first and ends with its `calls`-th window-attention launch; its
+    dispatches are reported apart from the rest."""
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    swa_starts = [int(r["Start_Timestamp"]) for r in rows if "swa_mfma_kernel" in r["Kernel_Name"]]
+    step_end = swa_starts[calls - 1] if len(swa_starts) >= calls else -1
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        grid = r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]
+        blk = r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"]
+        phase = "step" if ("based" in name and int(r["Start_Timestamp"]) <= step_end) else ""
+        groups.setdefault((name, grid, blk, phase), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", f"Command: `{command}`", "",
+             "Rows marked *step* are the timed layer step (360M-shaped workload, B8 H16 L2048 d_v64 bf16);",
+             "the others are the 1.3B-shaped and 32k workloads, the decode loop and set-up kernels.", "",
+             "| kernel | grid (threads) | block | step | calls | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid, blk, phase), d in groups.items():
+        lines.append(f"| `{name}` | {grid} | {blk} | {phase} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
+                     f"{max(d):.1f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", "kernel_stats.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,7 +364,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and decode")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<op>.json from two rocprofv3 --pmc runs of this script")
+    ap.add_argument("--pmc-command", default="", help="the command that produced the --pmc runs (recorded)")
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
+                    help="write profiles/kernel_stats.md from a rocprofv3 --kernel-trace --stats run of this script")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.pmc_command, args.steps + args.warmup)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.steps + args.warmup, args.pmc_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(batch/head sharding of the layer needs no communication; see DESIGN.md)", file=sys.stderr)
@@ -208,6 +386,8 @@ def main():
     import linear_attention_lm_amd as lal
 
     cfg = synth.FWD_CONFIGS["based360m"]
+    copy = copy_calibration()
+    print(f"[bench] copy calibration: {copy['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step, linattn {main_res['linattn_us']:.1f} us, "
           f"swa {main_res['swa_us']:.1f} us", file=sys.stderr, flush=True)
@@ -218,12 +398,14 @@ def main():
             extra.append(r)
             print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         decode = bench_decode(lal, synth.DECODE_CONFIG)
+        decode["traffic_bytes_per_step"] = load_traffic("decode")
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(cfg)
 
     # dominant kernel of the step: the one with the larger share of the time
     dom = "linattn" if main_res["linattn_us"] >= main_res["swa_us"] else "swa"
     achieved = main_res[f"{dom}_hbm_gbs"]
+    traffic = load_traffic(dom)
     out = {
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
@@ -233,10 +415,12 @@ def main():
                    "B": cfg.B, "H": cfg.H, "L": cfg.L, "d_k": 16, "d_v": cfg.dv, "window": cfg.window,
                    "inputs": "bf16", "outputs": "fp32"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes": main_res[f"{dom}_bytes"],
                      "mfma_alg_frac": main_res["linattn_alg_tflops"] / MFMA_BF16_PEAK_TFS},
         "kernels": {k: main_res[k] for k in ("linattn_us", "swa_us", "linattn_hbm_gbs", "swa_hbm_gbs",
                                               "linattn_alg_tflops")},
+        "copy_calibration": copy,
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "decode": decode,

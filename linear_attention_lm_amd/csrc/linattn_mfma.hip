@@ -498,6 +498,10 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       S.vpart[tid] = vs;
     }
 
+    // normalised outputs of this chunk; stored only after the next chunk's
+    // inputs have been consumed, so that waiting for those loads never waits
+    // for these stores (vector memory operations complete in order)
+    float yv[FULL ? NT : 1][4];
     if constexpr (FULL) {
       // ---- readout of the state before the chunk: positions 16w + r16
       f32x4 acc[NT];
@@ -598,13 +602,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int i = 0; i < 4; ++i) rden[i] = 1.f / __shfl(den_tok, 4 * g + i, 64);
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) {
-        const int col = 16 * nn + r16;
-        const float c0 = S.t0[col];
+        const float c0 = S.t0[16 * nn + r16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = 16 * w + 4 * g + i;
-          if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = (acc[nn][i] + c0) * rden[i];
-        }
+        for (int i = 0; i < 4; ++i) yv[nn][i] = (acc[nn][i] + c0) * rden[i];
       }
     }
 
@@ -631,6 +631,17 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       default: publish_state<NT, FULL, 3>(S, tacc, zinc); break;
     }
     if (tn < tok_end) store_chunk<NT, FULL>(S, pf);
+    if constexpr (FULL) {
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) {
+        const int col = 16 * nn + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = 16 * w + 4 * g + i;
+          if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = yv[nn][i];
+        }
+      }
+    }
   }
   __syncthreads();
 
