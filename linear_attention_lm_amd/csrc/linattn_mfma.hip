@@ -269,72 +269,85 @@ __device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT
   }
 }
 
-// The wavefront-W part of the state: pairs [W*PPW, (W+1)*PPW) of the
-// (feature tile m in 0..9) x (column tile n) grid, m-major.
+// The state is 10 feature tiles x NT column tiles of 16x16.  Wavefront w owns
+// feature tiles w and w + 4 for every column tile (slots 0 and 1) and feature
+// tile 8 + w/2 for the column-tile half w%2 (slot 2): 2.5 NT tiles each, and
+// the same code shape in every wavefront (tile indices are wave-uniform values).
 template <int NT>
 struct Own {
-  static constexpr int PPW = 10 * NT / 4;
+  static constexpr int PPW = 2 * NT + NT / 2;
+  static_assert(NT % 2 == 0, "column tiles come in pairs");
 };
 
-// State update of one chunk for wavefront W: tacc += psi'(K)^T V over the
-// chunk, and the z increments of the feature tiles whose column tile 0 it owns.
-template <int NT, bool FULL, int W>
+// Feature tile m and column tile n of owned pair j of wavefront w.
+template <int NT>
+__device__ __forceinline__ void pair_mn(int w, int j, int& m, int& n) {
+  if (j < NT) { m = w; n = j; }
+  else if (j < 2 * NT) { m = w + 4; n = j - NT; }
+  else { m = 8 + (w >> 1); n = (w & 1) * (NT / 2) + (j - 2 * NT); }
+}
+
+// State update of one chunk: tacc += psi'(K)^T V over the chunk, and the z
+// increments of the owned feature tiles (zinc[slot]).
+template <int NT, bool FULL>
 __device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Own<NT>::PPW], float (&zinc)[3],
                                              const int (&ia_)[3], const int (&ib_)[3]) {
-  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
-  constexpr int M0 = P0 / NT, M1 = (P0 + PPW - 1) / NT;
-  constexpr int NM = M1 - M0 + 1;
-  static_assert(NM <= 3, "a wavefront spans at most 3 feature tiles");
-  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  constexpr int H = NT / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int n2 = (w & 1) * H;  // first column tile of slot 2
 #pragma unroll
-  for (int mm = 0; mm < NM; ++mm) zinc[mm] = 0.f;
+  for (int ms = 0; ms < 3; ++ms) zinc[ms] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 ahi[NM], alo[NM];
+    bf16x8 ahi[3], alo[3];
 #pragma unroll
-    for (int mm = 0; mm < NM; ++mm) {
-      const float4* pa = reinterpret_cast<const float4*>(&S.kt[ia_[mm]][32 * ks + 8 * g]);
-      const float4* pb = reinterpret_cast<const float4*>(&S.kt[ib_[mm]][32 * ks + 8 * g]);
+    for (int ms = 0; ms < 3; ++ms) {
+      const float4* pa = reinterpret_cast<const float4*>(&S.kt[ia_[ms]][32 * ks + 8 * g]);
+      const float4* pb = reinterpret_cast<const float4*>(&S.kt[ib_[ms]][32 * ks + 8 * g]);
       const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
       float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
                      a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
       float zs = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) zs += pr[i];
-      zinc[mm] += zs;
-      split8(pr, ahi[mm], alo[mm]);
+      zinc[ms] += zs;
+      split8(pr, ahi[ms], alo[ms]);
     }
-    bf16x8 bv[NT];
+    bf16x8 bv[NT], bv2[H];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int col = 16 * n + r16;
       bv[n] = *reinterpret_cast<const bf16x8*>(&S.vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
-      tacc[j] = mfma(ahi[m], bv[n], tacc[j]);
+    for (int n = 0; n < H; ++n) {
+      const int col = 16 * (n2 + n) + r16;
+      bv2[n] = *reinterpret_cast<const bf16x8*>(&S.vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const int m = (P0 + j) / NT - M0, n = (P0 + j) % NT;
-      tacc[j] = mfma(alo[m], bv[n], tacc[j]);
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) tacc[n] = mfma(pass ? alo[0] : ahi[0], bv[n], tacc[n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) tacc[NT + n] = mfma(pass ? alo[1] : ahi[1], bv[n], tacc[NT + n]);
+#pragma unroll
+      for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(pass ? alo[2] : ahi[2], bv2[n], tacc[2 * NT + n]);
     }
   }
 }
 
 // Re-split the owned state tiles into bf16 hi/lo rows of S.tt and add the z
 // increments (the caller has synchronised: nobody reads tt/zf meanwhile).
-template <int NT, bool FULL, int W, bool WITH_Z = true>
+template <int NT, bool FULL, bool WITH_Z = true>
 __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW],
                                               const float (&zinc)[3]) {
-  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
-  constexpr int M0 = P0 / NT, M1 = (P0 + PPW - 1) / NT;
-  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  constexpr int PPW = Own<NT>::PPW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   if constexpr (FULL) {
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      const int m = (P0 + j) / NT, n = (P0 + j) % NT;
+      int m, n;
+      pair_mn<NT>(w, j, m, n);
       bf16x4 hi, lo;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -346,29 +359,32 @@ __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&t
       *reinterpret_cast<bf16x4*>(&S.tt[1][16 * n + r16][16 * m + 4 * g]) = lo;
     }
   }
+  if constexpr (WITH_Z) {
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
-  for (int mm = 0; mm <= M1 - M0; ++mm) {
-    const int m = M0 + mm;
-    if (WITH_Z && m * NT >= P0) {  // this wavefront owns (m, column tile 0): it keeps z of tile m
-      float z = zinc[mm];
-      z += __shfl_xor(z, 16, 64);
-      z += __shfl_xor(z, 32, 64);
-      if (g == 0) S.zf[16 * m + r16] += z;
+    for (int ms = 0; ms < 3; ++ms) {
+      if (ms < 2 || (w & 1) == 0) {  // the owner of column tile 0 keeps z of the feature tile
+        float z = zinc[ms];
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        if (g == 0) S.zf[16 * mt[ms] + r16] += z;
+      }
     }
   }
 }
 
-// Initial state tiles of wavefront W: from a compact state in the workspace
+// Initial owned state tiles: from a compact state in the workspace
 // ([NF+1][DV], row NF = constant), else from the caller's phi-layout S_in,
 // else zero.
-template <int NT, bool FULL, int W>
+template <int NT>
 __device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
   constexpr int DV = 16 * NT;
-  constexpr int PPW = Own<NT>::PPW, P0 = W * PPW;
-  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  constexpr int PPW = Own<NT>::PPW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
-    const int m = (P0 + j) / NT, n = (P0 + j) % NT;
+    int m, n;
+    pair_mn<NT>(w, j, m, n);
     const int c = 16 * n + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -378,8 +394,6 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
   }
 }
 
-// Write the owned state tiles (and, from every thread, t0 / zf / z0) to a
-// compact [NF+1][DV] + [NF+1] workspace record.
 template <int NT, bool FULL>
 __device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW], float z0,
                                               float* dst, float* dz) {
@@ -388,7 +402,8 @@ __device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&t
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
-    const int pp = w * PPW + j, m = pp / NT, nn = pp % NT;
+    int m, nn;
+    pair_mn<NT>(w, j, m, nn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
   }
@@ -432,12 +447,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
   }
   f32x4 tacc[PPW];
-  switch (w) {
-    case 0: init_state<NT, FULL, 0>(src, Sin, tacc); break;
-    case 1: init_state<NT, FULL, 1>(src, Sin, tacc); break;
-    case 2: init_state<NT, FULL, 2>(src, Sin, tacc); break;
-    default: init_state<NT, FULL, 3>(src, Sin, tacc); break;
-  }
+  init_state<NT>(src, Sin, tacc);
   for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
   for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
   float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
@@ -449,21 +459,16 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   }
   {
     const float zinc[3] = {0.f, 0.f, 0.f};
-    switch (w) {
-      case 0: publish_state<NT, FULL, 0, false>(S, tacc, zinc); break;
-      case 1: publish_state<NT, FULL, 1, false>(S, tacc, zinc); break;
-      case 2: publish_state<NT, FULL, 2, false>(S, tacc, zinc); break;
-      default: publish_state<NT, FULL, 3, false>(S, tacc, zinc); break;
-    }
+    publish_state<NT, FULL, false>(S, tacc, zinc);
   }
 
   // update-operand rows of this wavefront's feature tiles (loop invariant)
   int ia[3], ib[3];
   {
-    const int m0 = (w * PPW) / NT;
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
     for (int mm = 0; mm < 3; ++mm) {
-      const int r = min(16 * (m0 + mm) + r16, NF - 1);
+      const int r = 16 * mt[mm] + r16;
       const int ty = c_tab.type[r];
       ia[mm] = c_tab.a[r];
       ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
@@ -610,12 +615,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 
     // ---- state update with this chunk (registers only)
     float zinc[3];
-    switch (w) {
-      case 0: update_chunk<NT, FULL, 0>(S, tacc, zinc, ia, ib); break;
-      case 1: update_chunk<NT, FULL, 1>(S, tacc, zinc, ia, ib); break;
-      case 2: update_chunk<NT, FULL, 2>(S, tacc, zinc, ia, ib); break;
-      default: update_chunk<NT, FULL, 3>(S, tacc, zinc, ia, ib); break;
-    }
+    update_chunk<NT, FULL>(S, tacc, zinc, ia, ib);
     z0 += (float)n;
     __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
     if (tid < DV) {
@@ -624,12 +624,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int part = 0; part < NTHR / DV; ++part) vs += S.vpart[part * DV + tid];
       S.t0[tid] += vs;
     }
-    switch (w) {
-      case 0: publish_state<NT, FULL, 0>(S, tacc, zinc); break;
-      case 1: publish_state<NT, FULL, 1>(S, tacc, zinc); break;
-      case 2: publish_state<NT, FULL, 2>(S, tacc, zinc); break;
-      default: publish_state<NT, FULL, 3>(S, tacc, zinc); break;
-    }
+    publish_state<NT, FULL>(S, tacc, zinc);
     if (tn < tok_end) store_chunk<NT, FULL>(S, pf);
     if constexpr (FULL) {
 #pragma unroll
@@ -654,7 +649,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       float* stage = reinterpret_cast<float*>(&S.tt[0][0][0]);  // [NF][DV] fp32
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
-        const int pp = w * PPW + j, m = pp / NT, nn = pp % NT;
+        int m, nn;
+        pair_mn<NT>(w, j, m, nn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) stage[(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
       }
