@@ -165,13 +165,34 @@ struct Smem {
 // Column of v^T row `col` holding position t (see Smem).
 __device__ __forceinline__ int vt_pos(int col, int t) { return ((((t >> 3) ^ (col >> 3)) & 7) << 3) | (t & 7); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// hi + lo bf16 split of two fp32 values, packed: hi = RNE(x), lo = RNE(x - hi)
+// (one v_cvt_pk_bf16_f32 per pair for each part; hi is widened back to fp32
+// by a shift / mask).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+}
+
 __device__ __forceinline__ void split8(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 h = (__bf16)p[i];
-    hi[i] = h;
-    lo[i] = (__bf16)(p[i] - (float)h);
-  }
+  uint4 h, l;
+  split2(p[0], p[1], h.x, l.x);
+  split2(p[2], p[3], h.y, l.y);
+  split2(p[4], p[5], h.z, l.z);
+  split2(p[6], p[7], h.w, l.w);
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void split4(float a, float b, float c, float d, bf16x4& hi, bf16x4& lo) {
+  uint2 h, l;
+  split2(a, b, h.x, l.x);
+  split2(c, d, h.y, l.y);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, l);
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -349,12 +370,7 @@ __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&t
       int m, n;
       pair_mn<NT>(w, j, m, n);
       bf16x4 hi, lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 h = (__bf16)tacc[j][i];
-        hi[i] = h;
-        lo[i] = (__bf16)(tacc[j][i] - (float)h);
-      }
+      split4(tacc[j][0], tacc[j][1], tacc[j][2], tacc[j][3], hi, lo);
       *reinterpret_cast<bf16x4*>(&S.tt[0][16 * n + r16][16 * m + 4 * g]) = hi;
       *reinterpret_cast<bf16x4*>(&S.tt[1][16 * n + r16][16 * m + 4 * g]) = lo;
     }
@@ -562,15 +578,14 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
         if (m <= w) {
           const bf16x8 kav = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.kb[16 * m + r16][8 * g]) : zero8;
           const f32x4 x = mfma(kav, qbv, f32x4{0.f, 0.f, 0.f, 0.f});
+          float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float a = 1.f + x[i] + 0.5f * x[i] * x[i];
-            if (m == w && 4 * g + i > r16) a = 0.f;  // key after query
-            rsum += a;
-            const __bf16 h = (__bf16)a;
-            xh[m][i] = h;
-            xl[m][i] = (__bf16)(a - (float)h);
+            a[i] = 1.f + x[i] + 0.5f * x[i] * x[i];
+            if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
+            rsum += a[i];
           }
+          split4(a[0], a[1], a[2], a[3], xh[m], xl[m]);
         }
       }
 #pragma unroll
@@ -604,7 +619,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       const float den_tok = z0 + dpart + rsum;  // denominator of position 16w + r16
       float rden[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rden[i] = 1.f / __shfl(den_tok, 4 * g + i, 64);
+      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(__shfl(den_tok, 4 * g + i, 64));
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) {
         const float c0 = S.t0[16 * nn + r16];

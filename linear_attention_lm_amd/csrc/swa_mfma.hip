@@ -37,6 +37,16 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// hi + lo bf16 split of two fp32 values, packed: hi = RNE(x), lo = RNE(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+}
+
 constexpr int RSRC_DW3 = 0x00020000;
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
@@ -144,16 +154,19 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
     float den = 0.f;
     bf16x4 ph[6], pl[6];
 #pragma unroll
-    for (int m = 0; m < 5; ++m)
+    for (int m = 0; m < 5; ++m) {
+      float e[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = s[m][i] == -INFINITY ? 0.f : __expf(s[m][i] - mx);
-        const __bf16 h = (__bf16)e;
-        const __bf16 l = (__bf16)(e - (float)h);
-        ph[m][i] = h;
-        pl[m][i] = l;
-        den += (float)h + (float)l;
+        e[i] = s[m][i] == -INFINITY ? 0.f : __expf(s[m][i] - mx);
+        den += e[i];
       }
+      uint2 h, l;
+      split2(e[0], e[1], h.x, l.x);
+      split2(e[2], e[3], h.y, l.y);
+      ph[m] = __builtin_bit_cast(bf16x4, h);
+      pl[m] = __builtin_bit_cast(bf16x4, l);
+    }
     ph[5] = bf16x4{};
     pl[5] = bf16x4{};
     den += __shfl_xor(den, 16, 64);
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
     }
     float rden[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rden[i] = 1.f / __shfl(den, 4 * g + i, 64);
+    for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(__shfl(den, 4 * g + i, 64));
 #pragma unroll
     for (int nn = 0; nn < NT; ++nn) {
       const int col = 16 * nn + r16;
