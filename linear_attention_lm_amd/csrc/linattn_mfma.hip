@@ -156,7 +156,9 @@ struct Smem {
   alignas(16) bf16_t kb[FULL ? C : 1][QKB];
   alignas(16) float kt[DK + 1][KT];
   alignas(16) bf16_t vt[DV][VT];
-  alignas(16) bf16_t tt[FULL ? 2 : 1][DV][TT];  // state^T, hi and lo; reused as fp32 staging at the end
+  // state^T, hi and lo; row DV holds the denominator state z, row DV + 1
+  // zeros (the z column tile of the readout); reused as fp32 staging at the end
+  alignas(16) bf16_t tt[FULL ? 2 : 1][DV + 2][TT];
   alignas(16) float t0[DV];
   alignas(16) float vpart[NTHR];  // partial column sums of v
   alignas(16) float zf[NF];
@@ -308,16 +310,23 @@ __device__ __forceinline__ void pair_mn(int w, int j, int& m, int& n) {
   else { m = 8 + (w >> 1); n = (w & 1) * (NT / 2) + (j - 2 * NT); }
 }
 
-// State update of one chunk: tacc += psi'(K)^T V over the chunk, and the z
-// increments of the owned feature tiles (zinc[slot]).
+// bf16 B operand whose column 0 is all ones (lanes of column 0), else zero:
+// multiplying by it sums the A operand's rows into column 0.
+__device__ __forceinline__ bf16x8 ones_col0(int r16) {
+  const uint32_t one2 = r16 == 0 ? 0x3f803f80u : 0u;  // bf16 1.0 twice
+  return __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+}
+
+// State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
+// denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
+// (column 0 of each tz tile; the other columns stay zero).
 template <int NT, bool FULL>
-__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Own<NT>::PPW], float (&zinc)[3],
+__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3],
                                              const int (&ia_)[3], const int (&ib_)[3]) {
   constexpr int H = NT / 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int n2 = (w & 1) * H;  // first column tile of slot 2
-#pragma unroll
-  for (int ms = 0; ms < 3; ++ms) zinc[ms] = 0.f;
+  const bf16x8 ones = ones_col0(r16);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 ahi[3], alo[3];
@@ -328,10 +337,6 @@ __device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Ow
       const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
       float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
                      a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
-      float zs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zs += pr[i];
-      zinc[ms] += zs;
       split8(pr, ahi[ms], alo[ms]);
     }
     bf16x8 bv[NT], bv2[H];
@@ -353,16 +358,20 @@ __device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Ow
       for (int n = 0; n < NT; ++n) tacc[NT + n] = mfma(pass ? alo[1] : ahi[1], bv[n], tacc[NT + n]);
 #pragma unroll
       for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(pass ? alo[2] : ahi[2], bv2[n], tacc[2 * NT + n]);
+      tz[0] = mfma(pass ? alo[0] : ahi[0], ones, tz[0]);
+      tz[1] = mfma(pass ? alo[1] : ahi[1], ones, tz[1]);
+      if ((w & 1) == 0) tz[2] = mfma(pass ? alo[2] : ahi[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
     }
   }
 }
 
-// Re-split the owned state tiles into bf16 hi/lo rows of S.tt and add the z
-// increments (the caller has synchronised: nobody reads tt/zf meanwhile).
-template <int NT, bool FULL, bool WITH_Z = true>
+// Re-split the owned state tiles (and the denominator state) into bf16 hi/lo
+// rows of S.tt (the caller has synchronised: nobody reads tt meanwhile).
+template <int NT, bool FULL>
 __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW],
-                                              const float (&zinc)[3]) {
+                                              const f32x4 (&tz)[3]) {
   constexpr int PPW = Own<NT>::PPW;
+  constexpr int DV = 16 * NT;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   if constexpr (FULL) {
 #pragma unroll
@@ -374,19 +383,32 @@ __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&t
       *reinterpret_cast<bf16x4*>(&S.tt[0][16 * n + r16][16 * m + 4 * g]) = hi;
       *reinterpret_cast<bf16x4*>(&S.tt[1][16 * n + r16][16 * m + 4 * g]) = lo;
     }
-  }
-  if constexpr (WITH_Z) {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+    if (r16 == 0) {
+      const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
-    for (int ms = 0; ms < 3; ++ms) {
-      if (ms < 2 || (w & 1) == 0) {  // the owner of column tile 0 keeps z of the feature tile
-        float z = zinc[ms];
-        z += __shfl_xor(z, 16, 64);
-        z += __shfl_xor(z, 32, 64);
-        if (g == 0) S.zf[16 * mt[ms] + r16] += z;
+      for (int ms = 0; ms < 3; ++ms) {
+        if (ms < 2 || (w & 1) == 0) {
+          bf16x4 hi, lo;
+          split4(tz[ms][0], tz[ms][1], tz[ms][2], tz[ms][3], hi, lo);
+          *reinterpret_cast<bf16x4*>(&S.tt[0][DV][16 * mt[ms] + 4 * g]) = hi;
+          *reinterpret_cast<bf16x4*>(&S.tt[1][DV][16 * mt[ms] + 4 * g]) = lo;
+        }
       }
     }
   }
+}
+
+// The denominator state of the owned feature tiles back into S.zf.
+template <int NT, bool FULL>
+__device__ __forceinline__ void store_z(Smem<NT, FULL>& S, const f32x4 (&tz)[3]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  if (r16 != 0) return;
+  const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+  for (int ms = 0; ms < 3; ++ms)
+    if (ms < 2 || (w & 1) == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.zf[16 * mt[ms] + 4 * g + i] = tz[ms][i];
 }
 
 // Initial owned state tiles: from a compact state in the workspace
@@ -468,15 +490,22 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
   float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
   for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = 1.f;
+  if constexpr (FULL)
+    for (int j = tid; j < 2 * TT; j += NTHR) S.tt[j / TT][DV + 1][j % TT] = (bf16_t)0;
   __syncthreads();
+  f32x4 tz[3];  // denominator state of the owned feature tiles, in column 0
+  {
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+    for (int ms = 0; ms < 3; ++ms)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tz[ms][i] = r16 == 0 ? S.zf[16 * mt[ms] + 4 * g + i] : 0.f;
+  }
   if constexpr (!FULL) {
     if (seg == 0)  // record 0: the initial state of the whole sequence
       write_compact<NT, FULL>(S, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   }
-  {
-    const float zinc[3] = {0.f, 0.f, 0.f};
-    publish_state<NT, FULL, false>(S, tacc, zinc);
-  }
+  publish_state<NT, FULL>(S, tacc, tz);
 
   // update-operand rows of this wavefront's feature tiles (loop invariant)
   int ia[3], ib[3];
@@ -537,7 +566,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           qr[4 * m] = x.x; qr[4 * m + 1] = x.y; qr[4 * m + 2] = x.z; qr[4 * m + 3] = x.w;
         }
       }
-      float dpart = 0.f;
+      f32x4 accz = {0.f, 0.f, 0.f, 0.f};  // column 0: denominator of each position
+      const int zrow = DV + (r16 == 0 ? 0 : 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float f[8];
@@ -550,12 +580,15 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
             f[s] = (d == 8 ? 0.5f : 1.f) * qr[A] * qr[B];
           }
         }
-        const float4 z0v = *reinterpret_cast<const float4*>(&S.zf[32 * kb + 8 * g]);
-        const float4 z1v = *reinterpret_cast<const float4*>(&S.zf[32 * kb + 8 * g + 4]);
-        dpart += f[0] * z0v.x + f[1] * z0v.y + f[2] * z0v.z + f[3] * z0v.w + f[4] * z1v.x + f[5] * z1v.y +
-                 f[6] * z1v.z + f[7] * z1v.w;
         bf16x8 ahi, alo;
         split8(f, ahi, alo);
+        {
+          const bf16x8 zhi = *reinterpret_cast<const bf16x8*>(&S.tt[0][zrow][32 * kb + 8 * g]);
+          const bf16x8 zlo = *reinterpret_cast<const bf16x8*>(&S.tt[1][zrow][32 * kb + 8 * g]);
+          accz = mfma(ahi, zhi, accz);
+          accz = mfma(ahi, zlo, accz);
+          accz = mfma(alo, zhi, accz);
+        }
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
           const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(&S.tt[0][16 * nn + r16][32 * kb + 8 * g]);
@@ -569,7 +602,6 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
       const bf16x8 zero8 = {};
       const bf16x8 qbv = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.qb[16 * w + r16][8 * g]) : zero8;
-      float rsum = 0.f;
       bf16x4 xh[4], xl[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -583,7 +615,6 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           for (int i = 0; i < 4; ++i) {
             a[i] = 1.f + x[i] + 0.5f * x[i] * x[i];
             if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
-            rsum += a[i];
           }
           split4(a[0], a[1], a[2], a[3], xh[m], xl[m]);
         }
@@ -596,6 +627,11 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           for (int i = 0; i < 4; ++i) {
             ah[i] = xh[2 * kb][i]; ah[4 + i] = xh[2 * kb + 1][i];
             al[i] = xl[2 * kb][i]; al[4 + i] = xl[2 * kb + 1][i];
+          }
+          {
+            const bf16x8 ones = ones_col0(r16);  // row sums of the weights -> denominator
+            accz = mfma(ah, ones, accz);
+            accz = mfma(al, ones, accz);
           }
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
@@ -612,14 +648,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       }
 
       // ---- normalise and store: acc[nn][i] is position 16w + 4g + i, column 16nn + r16
-      dpart += __shfl_xor(dpart, 16, 64);
-      dpart += __shfl_xor(dpart, 32, 64);
-      rsum += __shfl_xor(rsum, 16, 64);
-      rsum += __shfl_xor(rsum, 32, 64);
-      const float den_tok = z0 + dpart + rsum;  // denominator of position 16w + r16
-      float rden[4];
+      float rden[4];  // position 16w + 4g + i: its denominator sits in column 0 (lane 16g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(__shfl(den_tok, 4 * g + i, 64));
+      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(z0 + __shfl(accz[i], lane & 48, 64));
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) {
         const float c0 = S.t0[16 * nn + r16];
@@ -629,8 +660,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     }
 
     // ---- state update with this chunk (registers only)
-    float zinc[3];
-    update_chunk<NT, FULL>(S, tacc, zinc, ia, ib);
+    update_chunk<NT, FULL>(S, tacc, tz, ia, ib);
     z0 += (float)n;
     __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
     if (tid < DV) {
@@ -639,7 +669,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int part = 0; part < NTHR / DV; ++part) vs += S.vpart[part * DV + tid];
       S.t0[tid] += vs;
     }
-    publish_state<NT, FULL>(S, tacc, zinc);
+    publish_state<NT, FULL>(S, tacc, tz);
     if (tn < tok_end) store_chunk<NT, FULL>(S, pf);
     if constexpr (FULL) {
 #pragma unroll
@@ -656,6 +686,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   __syncthreads();
 
   // ---- segment result: the record after segment s (state-only pass) or S_out
+  store_z<NT, FULL>(S, tz);
+  __syncthreads();
   if constexpr (!FULL) {
     write_compact<NT, FULL>(S, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
                             p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
