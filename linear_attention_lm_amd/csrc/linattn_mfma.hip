@@ -253,29 +253,18 @@ __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too
   }
 }
 
-template <int NT, bool FULL>
-__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT>& pf) {
+// k^T (fp32) and v^T (bf16, swizzled) of one chunk from the prefetch registers.
+template <int NT>
+__device__ __forceinline__ void store_kv(float (*kt)[KT], bf16_t (*vt)[VT], const Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
-  {
+  if (tid >= 128) {
     const int u = tid & 127, j = u >> 1, h = u & 1;
     const uint32_t w[4] = {pf.qk.x, pf.qk.y, pf.qk.z, pf.qk.w};
-    float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-    if (tid < 128) {
-      if constexpr (FULL) {
-        *reinterpret_cast<uint4*>(&S.qb[j][8 * h]) = pf.qk;
-        *reinterpret_cast<float4*>(&S.qs[j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(&S.qs[j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
-      }
-    } else {
-      if constexpr (FULL) *reinterpret_cast<uint4*>(&S.kb[j][8 * h]) = pf.qk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) S.kt[8 * h + i][j] = f[i];
+      kt[8 * h + 2 * i][j] = __uint_as_float(w[i] << 16);
+      kt[8 * h + 2 * i + 1][j] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
 #pragma unroll
@@ -286,10 +275,33 @@ __device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT
     const int pc = vt_pos(8 * c8, j);  // the same for the 8 columns of this group
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      S.vt[8 * c8 + 2 * e][pc] = (bf16_t)(w[e] & 0xffffu);
-      S.vt[8 * c8 + 2 * e + 1][pc] = (bf16_t)(w[e] >> 16);
+      vt[8 * c8 + 2 * e][pc] = (bf16_t)(w[e] & 0xffffu);
+      vt[8 * c8 + 2 * e + 1][pc] = (bf16_t)(w[e] >> 16);
     }
   }
+}
+
+template <int NT, bool FULL>
+__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT>& pf) {
+  const int tid = threadIdx.x;
+  if constexpr (FULL) {
+    const int u = tid & 127, j = u >> 1, h = u & 1;
+    if (tid < 128) {
+      const uint32_t w[4] = {pf.qk.x, pf.qk.y, pf.qk.z, pf.qk.w};
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+      *reinterpret_cast<uint4*>(&S.qb[j][8 * h]) = pf.qk;
+      *reinterpret_cast<float4*>(&S.qs[j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(&S.qs[j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+      *reinterpret_cast<uint4*>(&S.kb[j][8 * h]) = pf.qk;
+    }
+  }
+  store_kv<NT>(S.kt, S.vt, pf);
 }
 
 // The state is 10 feature tiles x NT column tiles of 16x16.  Wavefront w owns
@@ -320,9 +332,9 @@ __device__ __forceinline__ bf16x8 ones_col0(int r16) {
 // State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
 // (column 0 of each tz tile; the other columns stay zero).
-template <int NT, bool FULL>
-__device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3],
-                                             const int (&ia_)[3], const int (&ib_)[3]) {
+template <int NT>
+__device__ __forceinline__ void update_chunk(const float (*kt)[KT], const bf16_t (*vt)[VT], f32x4 (&tacc)[Own<NT>::PPW],
+                                             f32x4 (&tz)[3], const int (&ia_)[3], const int (&ib_)[3]) {
   constexpr int H = NT / 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int n2 = (w & 1) * H;  // first column tile of slot 2
@@ -332,8 +344,8 @@ __device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Ow
     bf16x8 ahi[3], alo[3];
 #pragma unroll
     for (int ms = 0; ms < 3; ++ms) {
-      const float4* pa = reinterpret_cast<const float4*>(&S.kt[ia_[ms]][32 * ks + 8 * g]);
-      const float4* pb = reinterpret_cast<const float4*>(&S.kt[ib_[ms]][32 * ks + 8 * g]);
+      const float4* pa = reinterpret_cast<const float4*>(&kt[ia_[ms]][32 * ks + 8 * g]);
+      const float4* pb = reinterpret_cast<const float4*>(&kt[ib_[ms]][32 * ks + 8 * g]);
       const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
       float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
                      a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
@@ -343,12 +355,12 @@ __device__ __forceinline__ void update_chunk(Smem<NT, FULL>& S, f32x4 (&tacc)[Ow
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int col = 16 * n + r16;
-      bv[n] = *reinterpret_cast<const bf16x8*>(&S.vt[col][vt_pos(col, 32 * ks + 8 * g)]);
+      bv[n] = *reinterpret_cast<const bf16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
     for (int n = 0; n < H; ++n) {
       const int col = 16 * (n2 + n) + r16;
-      bv2[n] = *reinterpret_cast<const bf16x8*>(&S.vt[col][vt_pos(col, 32 * ks + 8 * g)]);
+      bv2[n] = *reinterpret_cast<const bf16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -399,8 +411,8 @@ __device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&t
 }
 
 // The denominator state of the owned feature tiles back into S.zf.
-template <int NT, bool FULL>
-__device__ __forceinline__ void store_z(Smem<NT, FULL>& S, const f32x4 (&tz)[3]) {
+template <int NT>
+__device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   if (r16 != 0) return;
   const int mt[3] = {w, w + 4, 8 + (w >> 1)};
@@ -408,7 +420,7 @@ __device__ __forceinline__ void store_z(Smem<NT, FULL>& S, const f32x4 (&tz)[3])
   for (int ms = 0; ms < 3; ++ms)
     if (ms < 2 || (w & 1) == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S.zf[16 * mt[ms] + 4 * g + i] = tz[ms][i];
+      for (int i = 0; i < 4; ++i) zf[16 * mt[ms] + 4 * g + i] = tz[ms][i];
 }
 
 // Initial owned state tiles: from a compact state in the workspace
@@ -432,9 +444,9 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
   }
 }
 
-template <int NT, bool FULL>
-__device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW], float z0,
-                                              float* dst, float* dz) {
+template <int NT>
+__device__ __forceinline__ void write_compact(const float* t0, const float* zf, const f32x4 (&tacc)[Own<NT>::PPW],
+                                              float z0, float* dst, float* dz) {
   constexpr int DV = 16 * NT;
   constexpr int PPW = Own<NT>::PPW;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
@@ -445,8 +457,8 @@ __device__ __forceinline__ void write_compact(Smem<NT, FULL>& S, const f32x4 (&t
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
   }
-  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = S.t0[c];
-  for (int r = tid; r < NF; r += NTHR) dz[r] = S.zf[r];
+  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = t0[c];
+  for (int r = tid; r < NF; r += NTHR) dz[r] = zf[r];
   if (tid == 0) dz[NF] = z0;
 }
 
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   }
   if constexpr (!FULL) {
     if (seg == 0)  // record 0: the initial state of the whole sequence
-      write_compact<NT, FULL>(S, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
+      write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   }
   publish_state<NT, FULL>(S, tacc, tz);
 
@@ -660,7 +672,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     }
 
     // ---- state update with this chunk (registers only)
-    update_chunk<NT, FULL>(S, tacc, tz, ia, ib);
+    update_chunk<NT>(S.kt, S.vt, tacc, tz, ia, ib);
     z0 += (float)n;
     __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
     if (tid < DV) {
@@ -686,11 +698,11 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   __syncthreads();
 
   // ---- segment result: the record after segment s (state-only pass) or S_out
-  store_z<NT, FULL>(S, tz);
+  store_z<NT>(S.zf, tz);
   __syncthreads();
   if constexpr (!FULL) {
-    write_compact<NT, FULL>(S, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
-                            p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
+    write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
+                      p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
   } else {
     if (p.S_out && seg == p.nseg - 1) {
       float* stage = reinterpret_cast<float*>(&S.tt[0][0][0]);  // [NF][DV] fp32
@@ -718,6 +730,111 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// State-only pass over segment s < nseg - 1 of a (batch, head): the segment's
+// increment of the compact state (segment 0 starts from S_in, so its record
+// carries the initial state too).  Update only, so one barrier per chunk:
+// k^T / v^T are double-buffered in LDS and the inputs are prefetched into
+// registers two chunks ahead.
+template <int NT>
+struct StateSmem {
+  static constexpr int DV = 16 * NT;
+  alignas(16) float kt[2][DK + 1][KT];
+  alignas(16) bf16_t vt[2][DV][VT];
+  alignas(16) float vpart[NTHR];
+  alignas(16) float t0[DV];
+  alignas(16) float zf[NF];
+};
+
+template <int NT>
+__global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
+  constexpr int DV = 16 * NT;
+  constexpr int PPW = Own<NT>::PPW;
+  constexpr int PARTS = NTHR / DV, SPAN = C / PARTS;
+  __shared__ StateSmem<NT> S;
+
+  const int nsm = p.nseg - 1;
+  const size_t bh = blockIdx.x / nsm;
+  const int seg = blockIdx.x % nsm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tok_begin = seg * p.seg_chunks * C;
+  const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
+  const size_t rec = (size_t)(NF + 1) * DV;
+
+  const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
+  const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
+  f32x4 tacc[PPW];
+  init_state<NT>(nullptr, Sin, tacc);
+  for (int c = tid; c < DV; c += NTHR) S.t0[c] = Sin ? Sin[c] : 0.f;
+  for (int r = tid; r < NF; r += NTHR) S.zf[r] = zin ? compact_from_phi(zin, r, 0, 1) : 0.f;
+  float z0 = zin ? zin[0] : 0.f;
+  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = 1.f;
+  __syncthreads();
+  f32x4 tz[3];
+  {
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+    for (int ms = 0; ms < 3; ++ms)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tz[ms][i] = r16 == 0 ? S.zf[16 * mt[ms] + 4 * g + i] : 0.f;
+  }
+  if (seg == 0)  // record 0: the initial state of the whole sequence
+    write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
+  int ia[3], ib[3];
+  {
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+    for (int mm = 0; mm < 3; ++mm) {
+      const int r = 16 * mt[mm] + r16;
+      const int ty = c_tab.type[r];
+      ia[mm] = c_tab.a[r];
+      ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
+    }
+  }
+
+  const HeadRsrc rs = head_rsrc(p, bh, DV);
+  const int col = tid % DV, part = tid / DV;
+  float vs = 0.f;  // this thread's share of the column sums of v (constant row)
+  Prefetch<NT> pa, pb;
+  if (tok_begin < tok_end) {
+    load_chunk<NT>(rs, tok_begin, false, pa);
+    store_kv<NT>(S.kt[0], S.vt[0], pa);
+  }
+  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, pb);
+
+  // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare` receives t + 2C
+  auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
+    __syncthreads();
+    if (t + 2 * C < tok_end) load_chunk<NT>(rs, t + 2 * C, false, spare);
+#pragma unroll
+    for (int j = 0; j < SPAN; j += 8) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[buf][col][part * SPAN + j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vs += (float)x[e];
+    }
+    update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
+    if (t + C < tok_end) store_kv<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], next);
+  };
+  for (int t = tok_begin; t < tok_end; t += 2 * C) {
+    step(t, 0, pb, pa);
+    if (t + C < tok_end) step(t + C, 1, pa, pb);
+  }
+  z0 += (float)(tok_end - tok_begin);
+  __syncthreads();
+  S.vpart[tid] = vs;
+  store_z<NT>(S.zf, tz);
+  __syncthreads();
+  if (tid < DV) {
+    float sum = S.t0[tid];
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) sum += S.vpart[q * DV + tid];
+    S.t0[tid] = sum;
+  }
+  __syncthreads();
+  write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
+                    p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
 }
 
 // Prefix over the segment records of each (batch, head): record s holds the
@@ -786,7 +903,7 @@ static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
   if (p.nseg > 1) {
     p.ws = (float*)a.workspace;
     p.wsz = p.ws + (size_t)BH * p.nseg * (NF + 1) * DV;
-    hipLaunchKernelGGL((linattn_mfma_kernel<NT, false>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (p.nseg > 2) {
       const size_t total = (size_t)BH * ((size_t)(NF + 1) * DV + NF + 1);
