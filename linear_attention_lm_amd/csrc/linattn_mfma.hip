@@ -1,5 +1,5 @@
-// Causal Taylor linear attention, chunked, on bf16 matrix cores (gfx950
-// v_mfma_f32_16x16x32_bf16) with fp32 accumulation: the bf16 path of
+// Causal Taylor linear attention, chunked, on the matrix cores of gfx950
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation): the bf16 path of
 // based_linattn_fwd.
 //
 // Method (blog post "Базированная модель, часть 2": exp(q.k) is replaced by
@@ -21,16 +21,20 @@
 //   a register copy of q rotated by 4g, with compile-time register indices.
 //   The pairs {a, a+8} are fixed by the shift by 8 and appear in two slots,
 //   each with query weight 1/2.
-// * bf16 has an 8-bit significand: q, k, v are exact, products q_a q_b and
-//   the fp32 state are not.  Every inexact operand is split into hi + lo bf16
-//   (exact for a product of two bf16 values) and the matrix product takes the
-//   hi*hi + hi*lo + lo*hi passes, so the result carries ~16 significant bits.
+// * Operands are fp16 (11-bit significand; bf16 inputs convert exactly):
+//   features are products of two fp16 values rounded once (v_pk_mul_f16),
+//   the fp32 state is rounded once to fp16 for the readout, and the in-chunk
+//   weights 1 + x + x^2/2 are split into fp16 hi + lo (two passes).  The
+//   state copy is scaled by a power of two chosen from its largest entry, so
+//   its fp16 range never limits the sequence length; the query weights 1/2
+//   ride on that copy, so query features are plain products.  Range of the
+//   inputs: |q|, |k| < 2^7 per coordinate, |q.k| < 2^8, |v| < 2^15.
 // * Workgroup = 4 wavefronts; one workgroup per (batch*head, sequence
 //   segment).  Per chunk: readout + in-chunk term (wavefront w owns positions
 //   16w..16w+15 and every value column), then the state update (wavefront w
 //   owns a contiguous quarter of the 10 x (d_v/16) state tiles, which stay in
-//   accumulator registers across chunks), then the state is re-split into
-//   bf16 hi/lo in LDS for the next chunk's readout.  The next chunk's inputs
+//   accumulator registers across chunks), then the state is written to LDS
+//   as scaled fp16 for the next chunk's readout.  The next chunk's inputs
 //   are loaded from HBM into registers while the current one computes.
 // * Long sequences are split into segments so that the grid fills the GPU: a
 //   state-only pass computes each segment's state increment into the
@@ -42,20 +46,23 @@
 namespace based {
 namespace mfma {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;         // positions per chunk
 constexpr int NTHR = 256;     // 4 wavefronts
 constexpr int NF = 160;       // feature slots (linear + quadratic), constant kept apart
 constexpr int NKB = NF / 32;  // K-blocks of 32 slots in the readout
-constexpr int QS = 20;        // fp32 q row stride in LDS (floats)
-constexpr int QKB = 24;       // bf16 q/k row stride in LDS (elements)
-constexpr int KT = C + 4;     // fp32 k^T row stride
-constexpr int VT = C + 8;     // bf16 v^T row stride
-constexpr int TT = NF + 8;    // bf16 state^T row stride
+constexpr int QH = 24;        // fp16 q / k row stride in LDS (elements)
+constexpr int KT = C + 8;     // fp16 k^T row stride
+constexpr int VT = C + 8;     // fp16 v^T row stride
+constexpr int TT = NF + 8;    // fp16 state^T row stride
 constexpr int ONES = 16;      // k^T row holding 1.0 (second factor of linear features)
+constexpr int SCALE_TOP = 13; // the scaled fp16 state stays below 2^(SCALE_TOP + 1)
 
 enum SlotType : uint8_t { LIN = 0, DIAG = 1, OFF = 2, HALF = 3 };
 
@@ -145,60 +152,56 @@ struct Params {
   int L, nseg, seg_chunks;
 };
 
-// LDS.  vt is v^T with the 8-position groups of row `col` XOR-swizzled by
-// (col / 8) % 8, so that the transposing writes of a wavefront spread over all
-// banks while 8 consecutive positions stay contiguous for 16-byte reads.
-template <int NT, bool FULL>
+// LDS of the main pass.  vt is v^T with the 8-position groups of row `col`
+// XOR-swizzled by (col / 8) % 8, so that the transposing writes of a
+// wavefront spread over all banks while 8 consecutive positions stay
+// contiguous for 16-byte reads.
+template <int NT>
 struct Smem {
   static constexpr int DV = 16 * NT;
-  alignas(16) float qs[FULL ? C : 1][QS];
-  alignas(16) bf16_t qb[FULL ? C : 1][QKB];
-  alignas(16) bf16_t kb[FULL ? C : 1][QKB];
-  alignas(16) float kt[DK + 1][KT];
-  alignas(16) bf16_t vt[DV][VT];
-  // state^T, hi and lo; row DV holds the denominator state z, row DV + 1
-  // zeros (the z column tile of the readout); reused as fp32 staging at the end
-  alignas(16) bf16_t tt[FULL ? 2 : 1][DV + 2][TT];
-  alignas(16) float t0[DV];
-  alignas(16) float vpart[NTHR];  // partial column sums of v
-  alignas(16) float zf[NF];
+  alignas(16) half_t qh[C][QH];          // q, row-major
+  alignas(16) half_t kh[C][QH];          // k, row-major
+  alignas(16) half_t kt[DK + 1][KT];     // k^T; row ONES = 1
+  alignas(16) half_t vt[DV][VT];         // v^T, swizzled
+  alignas(16) half_t tt[DV + 1][TT];     // scaled state^T; row DV: denominator state
+  alignas(16) float t0[DV];              // constant row of the state (sum of v)
+  alignas(16) float vpart[NTHR];         // partial column sums of v
+  alignas(16) float zf[NF];              // denominator state (set-up and result)
+  alignas(16) float wmax[4];             // per-wavefront largest state magnitude
 };
+
+// Wavefront index as a scalar, so that every branch on it is a uniform
+// (scalar) branch: a matrix-core instruction under such a branch is skipped,
+// never issued with part of EXEC cleared -- the matrix cores ignore EXEC and
+// would write their result from whatever the skipped vector code left in the
+// operand registers.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Column of v^T row `col` holding position t (see Smem).
 __device__ __forceinline__ int vt_pos(int col, int t) { return ((((t >> 3) ^ (col >> 3)) & 7) << 3) | (t & 7); }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
-// hi + lo bf16 split of two fp32 values, packed: hi = RNE(x), lo = RNE(x - hi)
-// (one v_cvt_pk_bf16_f32 per pair for each part; hi is widened back to fp32
-// by a shift / mask).
+__device__ __forceinline__ f16x2 h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Two bf16 packed in a word -> two fp16 packed in a word (exact in fp16's
+// normal range).
+__device__ __forceinline__ uint32_t h2_from_bf2(uint32_t w) {
+  const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return u32(__builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ uint4 h8_from_bf8(const uint4& x) {
+  return make_uint4(h2_from_bf2(x.x), h2_from_bf2(x.y), h2_from_bf2(x.z), h2_from_bf2(x.w));
+}
+
+// fp16 hi + lo of two fp32 values: hi = RNE(x), lo = RNE(x - hi).
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
-}
-
-__device__ __forceinline__ void split8(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
-  uint4 h, l;
-  split2(p[0], p[1], h.x, l.x);
-  split2(p[2], p[3], h.y, l.y);
-  split2(p[4], p[5], h.z, l.z);
-  split2(p[6], p[7], h.w, l.w);
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
-}
-
-__device__ __forceinline__ void split4(float a, float b, float c, float d, bf16x4& hi, bf16x4& lo) {
-  uint2 h, l;
-  split2(a, b, h.x, l.x);
-  split2(c, d, h.y, l.y);
-  hi = __builtin_bit_cast(bf16x4, h);
-  lo = __builtin_bit_cast(bf16x4, l);
-}
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  const f16x2 h = __builtin_convertvector((f32x2{a, b}), f16x2);
+  hi = u32(h);
+  lo = u32(__builtin_convertvector((f32x2{a - (float)h[0], b - (float)h[1]}), f16x2));
 }
 
 // Registers holding one chunk's inputs on their way from HBM to LDS.
@@ -231,7 +234,8 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
 
 // Thread -> (position, 8 columns) of the v loads: a wavefront covers 8
 // positions x 8 column groups per load (DV = 64) so that its transposing LDS
-// writes hit distinct banks after the swizzle.
+// writes hit distinct banks after the swizzle.  Threads 0..127 load q (when
+// asked), threads 128..255 load k, 8 elements each.
 template <int NT>
 __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
@@ -253,55 +257,32 @@ __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too
   }
 }
 
-// k^T (fp32) and v^T (bf16, swizzled) of one chunk from the prefetch registers.
+// One chunk from the prefetch registers into LDS as fp16: k^T and v^T, and
+// (when given) the row-major copies of q and k.
 template <int NT>
-__device__ __forceinline__ void store_kv(float (*kt)[KT], bf16_t (*vt)[VT], const Prefetch<NT>& pf) {
+__device__ __forceinline__ void store_chunk(half_t (*kt)[KT], half_t (*vt)[VT], half_t (*qh)[QH], half_t (*kh)[QH],
+                                            const Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
+  const int u = tid & 127, j = u >> 1, h = u & 1;
   if (tid >= 128) {
-    const int u = tid & 127, j = u >> 1, h = u & 1;
-    const uint32_t w[4] = {pf.qk.x, pf.qk.y, pf.qk.z, pf.qk.w};
+    const uint4 k8 = h8_from_bf8(pf.qk);
+    if (kh) *reinterpret_cast<uint4*>(&kh[j][8 * h]) = k8;
+    const f16x8 e = __builtin_bit_cast(f16x8, k8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kt[8 * h + 2 * i][j] = __uint_as_float(w[i] << 16);
-      kt[8 * h + 2 * i + 1][j] = __uint_as_float(w[i] & 0xffff0000u);
-    }
+    for (int i = 0; i < 8; ++i) kt[8 * h + i][j] = e[i];
+  } else if (qh) {
+    *reinterpret_cast<uint4*>(&qh[j][8 * h]) = h8_from_bf8(pf.qk);
   }
 #pragma unroll
   for (int i = 0; i < Prefetch<NT>::NV; ++i) {
-    const int u = tid + NTHR * i;
-    const int j = u / (DV / 8), c8 = u % (DV / 8);
-    const uint32_t w[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
-    const int pc = vt_pos(8 * c8, j);  // the same for the 8 columns of this group
+    const int uu = tid + NTHR * i;
+    const int jj = uu / (DV / 8), c8 = uu % (DV / 8);
+    const f16x8 e = __builtin_bit_cast(f16x8, h8_from_bf8(pf.v[i]));
+    const int pc = vt_pos(8 * c8, jj);  // the same for the 8 columns of this group
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vt[8 * c8 + 2 * e][pc] = (bf16_t)(w[e] & 0xffffu);
-      vt[8 * c8 + 2 * e + 1][pc] = (bf16_t)(w[e] >> 16);
-    }
+    for (int c = 0; c < 8; ++c) vt[8 * c8 + c][pc] = e[c];
   }
-}
-
-template <int NT, bool FULL>
-__device__ __forceinline__ void store_chunk(Smem<NT, FULL>& S, const Prefetch<NT>& pf) {
-  const int tid = threadIdx.x;
-  if constexpr (FULL) {
-    const int u = tid & 127, j = u >> 1, h = u & 1;
-    if (tid < 128) {
-      const uint32_t w[4] = {pf.qk.x, pf.qk.y, pf.qk.z, pf.qk.w};
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
-      *reinterpret_cast<uint4*>(&S.qb[j][8 * h]) = pf.qk;
-      *reinterpret_cast<float4*>(&S.qs[j][8 * h]) = make_float4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<float4*>(&S.qs[j][8 * h + 4]) = make_float4(f[4], f[5], f[6], f[7]);
-    } else {
-      *reinterpret_cast<uint4*>(&S.kb[j][8 * h]) = pf.qk;
-    }
-  }
-  store_kv<NT>(S.kt, S.vt, pf);
 }
 
 // The state is 10 feature tiles x NT column tiles of 16x16.  Wavefront w owns
@@ -322,98 +303,111 @@ __device__ __forceinline__ void pair_mn(int w, int j, int& m, int& n) {
   else { m = 8 + (w >> 1); n = (w & 1) * (NT / 2) + (j - 2 * NT); }
 }
 
-// bf16 B operand whose column 0 is all ones (lanes of column 0), else zero:
-// multiplying by it sums the A operand's rows into column 0.
-__device__ __forceinline__ bf16x8 ones_col0(int r16) {
-  const uint32_t one2 = r16 == 0 ? 0x3f803f80u : 0u;  // bf16 1.0 twice
-  return __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+__device__ __forceinline__ f16x8 ones8() {
+  const uint32_t one2 = 0x3c003c00u;  // fp16 1.0 twice
+  return __builtin_bit_cast(f16x8, make_uint4(one2, one2, one2, one2));
 }
 
 // State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
-// (column 0 of each tz tile; the other columns stay zero).
+// (every column of a tz tile holds it).
 template <int NT>
-__device__ __forceinline__ void update_chunk(const float (*kt)[KT], const bf16_t (*vt)[VT], f32x4 (&tacc)[Own<NT>::PPW],
-                                             f32x4 (&tz)[3], const int (&ia_)[3], const int (&ib_)[3]) {
+__device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t (*vt)[VT],
+                                             f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3], const int (&ia)[3],
+                                             const int (&ib)[3]) {
   constexpr int H = NT / 2;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int n2 = (w & 1) * H;  // first column tile of slot 2
-  const bf16x8 ones = ones_col0(r16);
+  const f16x8 ones = ones8();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 ahi[3], alo[3];
+    f16x8 a[3];
 #pragma unroll
     for (int ms = 0; ms < 3; ++ms) {
-      const float4* pa = reinterpret_cast<const float4*>(&kt[ia_[ms]][32 * ks + 8 * g]);
-      const float4* pb = reinterpret_cast<const float4*>(&kt[ib_[ms]][32 * ks + 8 * g]);
-      const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-      float pr[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
-                     a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
-      split8(pr, ahi[ms], alo[ms]);
+      const f16x8 x = *reinterpret_cast<const f16x8*>(&kt[ia[ms]][32 * ks + 8 * g]);
+      const f16x8 y = *reinterpret_cast<const f16x8*>(&kt[ib[ms]][32 * ks + 8 * g]);
+      a[ms] = x * y;
     }
-    bf16x8 bv[NT], bv2[H];
+    f16x8 bv[NT], bv2[H];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int col = 16 * n + r16;
-      bv[n] = *reinterpret_cast<const bf16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
+      bv[n] = *reinterpret_cast<const f16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
     for (int n = 0; n < H; ++n) {
       const int col = 16 * (n2 + n) + r16;
-      bv2[n] = *reinterpret_cast<const bf16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
+      bv2[n] = *reinterpret_cast<const f16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
     }
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int n = 0; n < NT; ++n) tacc[n] = mfma(a[0], bv[n], tacc[n]);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) tacc[n] = mfma(pass ? alo[0] : ahi[0], bv[n], tacc[n]);
+    for (int n = 0; n < NT; ++n) tacc[NT + n] = mfma(a[1], bv[n], tacc[NT + n]);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) tacc[NT + n] = mfma(pass ? alo[1] : ahi[1], bv[n], tacc[NT + n]);
-#pragma unroll
-      for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(pass ? alo[2] : ahi[2], bv2[n], tacc[2 * NT + n]);
-      tz[0] = mfma(pass ? alo[0] : ahi[0], ones, tz[0]);
-      tz[1] = mfma(pass ? alo[1] : ahi[1], ones, tz[1]);
-      if ((w & 1) == 0) tz[2] = mfma(pass ? alo[2] : ahi[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
-    }
+    for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(a[2], bv2[n], tacc[2 * NT + n]);
+    tz[0] = mfma(a[0], ones, tz[0]);
+    tz[1] = mfma(a[1], ones, tz[1]);
+    if ((w & 1) == 0) tz[2] = mfma(a[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
   }
 }
 
-// Re-split the owned state tiles (and the denominator state) into bf16 hi/lo
-// rows of S.tt (the caller has synchronised: nobody reads tt meanwhile).
-template <int NT, bool FULL>
-__device__ __forceinline__ void publish_state(Smem<NT, FULL>& S, const f32x4 (&tacc)[Own<NT>::PPW],
-                                              const f32x4 (&tz)[3]) {
-  constexpr int PPW = Own<NT>::PPW;
+// Largest magnitude of this wavefront's state entries, into wmax[w].
+template <int NT>
+__device__ __forceinline__ void post_max(float* wmax, const f32x4 (&tacc)[Own<NT>::PPW], const f32x4 (&tz)[3]) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < Own<NT>::PPW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(tacc[j][i]));
+#pragma unroll
+  for (int ms = 0; ms < 3; ++ms)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(tz[ms][i]));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+}
+
+// Power-of-two scale of the published state from the block's largest entry
+// M (wmax, after a barrier): entries times 2^-e stay below 2^(SCALE_TOP+1).
+// Returns 2^e, the factor that undoes it.
+__device__ __forceinline__ float state_scale(const float* wmax, float& down) {
+  const float4 mm = *reinterpret_cast<const float4*>(wmax);
+  const float M = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
+  int e = (int)((__float_as_uint(M) >> 23) & 0xffu) - 127 - SCALE_TOP;
+  e = e < -126 ? -126 : e;
+  down = __uint_as_float((uint32_t)(127 - e) << 23);
+  return __uint_as_float((uint32_t)(127 + e) << 23);
+}
+
+// Write the owned state tiles (and the denominator state) into tt as fp16,
+// times `down` and the slot's query weight (the caller has synchronised:
+// nobody reads tt meanwhile).
+template <int NT>
+__device__ __forceinline__ void publish_state(half_t (*tt)[TT], const f32x4 (&tacc)[Own<NT>::PPW],
+                                              const f32x4 (&tz)[3], const float (&qw)[3], float down) {
   constexpr int DV = 16 * NT;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
-  if constexpr (FULL) {
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const float f[3] = {down * qw[0], down * qw[1], down * qw[2]};
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      int m, n;
-      pair_mn<NT>(w, j, m, n);
-      bf16x4 hi, lo;
-      split4(tacc[j][0], tacc[j][1], tacc[j][2], tacc[j][3], hi, lo);
-      *reinterpret_cast<bf16x4*>(&S.tt[0][16 * n + r16][16 * m + 4 * g]) = hi;
-      *reinterpret_cast<bf16x4*>(&S.tt[1][16 * n + r16][16 * m + 4 * g]) = lo;
-    }
-    if (r16 == 0) {
-      const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
+    int m, n;
+    pair_mn<NT>(w, j, m, n);
+    const float s = f[j < NT ? 0 : (j < 2 * NT ? 1 : 2)];
+    *reinterpret_cast<f16x4*>(&tt[16 * n + r16][16 * m + 4 * g]) = __builtin_convertvector(tacc[j] * s, f16x4);
+  }
+  if (r16 == 0) {
+    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
-      for (int ms = 0; ms < 3; ++ms) {
-        if (ms < 2 || (w & 1) == 0) {
-          bf16x4 hi, lo;
-          split4(tz[ms][0], tz[ms][1], tz[ms][2], tz[ms][3], hi, lo);
-          *reinterpret_cast<bf16x4*>(&S.tt[0][DV][16 * mt[ms] + 4 * g]) = hi;
-          *reinterpret_cast<bf16x4*>(&S.tt[1][DV][16 * mt[ms] + 4 * g]) = lo;
-        }
-      }
-    }
+    for (int ms = 0; ms < 3; ++ms)
+      if (ms < 2 || (w & 1) == 0)
+        *reinterpret_cast<f16x4*>(&tt[DV][16 * mt[ms] + 4 * g]) = __builtin_convertvector(tz[ms] * f[ms], f16x4);
   }
 }
 
-// The denominator state of the owned feature tiles back into S.zf.
+// The denominator state of the owned feature tiles back into zf.
 template <int NT>
 __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   if (r16 != 0) return;
   const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
@@ -429,10 +423,9 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
 template <int NT>
 __device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
   constexpr int DV = 16 * NT;
-  constexpr int PPW = Own<NT>::PPW;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
 #pragma unroll
-  for (int j = 0; j < PPW; ++j) {
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, n;
     pair_mn<NT>(w, j, m, n);
     const int c = 16 * n + r16;
@@ -444,14 +437,40 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
   }
 }
 
+// Denominator state of the owned feature tiles from zf (every column).
+__device__ __forceinline__ void load_tz(const float* zf, f32x4 (&tz)[3]) {
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4;
+  const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+  for (int ms = 0; ms < 3; ++ms)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tz[ms][i] = zf[16 * mt[ms] + 4 * g + i];
+}
+
+// Loop-invariant per-lane data of the owned feature tiles: the k^T rows
+// whose product is the key feature of the lane's slot (update operand rows),
+// and the query weight of the slots whose rows the lane publishes.
+__device__ __forceinline__ void slot_rows(int (&ia)[3], int (&ib)[3], float (&qw)[3]) {
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+  for (int mm = 0; mm < 3; ++mm) {
+    const int r = 16 * mt[mm] + r16;
+    const int ty = c_tab.type[r];
+    ia[mm] = c_tab.a[r];
+    ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
+    const int tw = c_tab.type[16 * mt[mm] + 4 * g];  // rows 4g..4g+3 share the kind
+    qw[mm] = (tw == DIAG || tw == HALF) ? 0.5f : 1.f;
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ void write_compact(const float* t0, const float* zf, const f32x4 (&tacc)[Own<NT>::PPW],
                                               float z0, float* dst, float* dz) {
   constexpr int DV = 16 * NT;
-  constexpr int PPW = Own<NT>::PPW;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, w = wave_index(), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
-  for (int j = 0; j < PPW; ++j) {
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, nn;
     pair_mn<NT>(w, j, m, nn);
 #pragma unroll
@@ -462,207 +481,208 @@ __device__ __forceinline__ void write_compact(const float* t0, const float* zf, 
   if (tid == 0) dz[NF] = z0;
 }
 
-// Two wavefronts per SIMD (two workgroups per CU) where the LDS footprint
+// The final state in the caller's 273-row phi layout, straight from the
+// accumulator registers: slot r of a pair (a, b) writes rows (a, b) and
+// (b, a) when it is the slot that represents that pair.
+template <int NT>
+__device__ __forceinline__ void write_phi_state(const float* t0, const float* zf, const f32x4 (&tacc)[Own<NT>::PPW],
+                                                float z0, float* So, float* zo) {
+  constexpr int DV = 16 * NT;
+  const int tid = threadIdx.x, w = wave_index(), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
+    int m, nn;
+    pair_mn<NT>(w, j, m, nn);
+    const int c = 16 * nn + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * m + 4 * g + i;
+      const int a = c_tab.a[r], b = c_tab.b[r], ty = c_tab.type[r];
+      if (ty == LIN) {
+        So[(size_t)(1 + a) * DV + c] = tacc[j][i];
+      } else {
+        const int f1 = 1 + DK + DK * a + b, f2 = 1 + DK + DK * b + a;
+        if (c_tab.phi_slot[f1] == r) {
+          const float val = tacc[j][i] * INV_SQRT2;
+          So[(size_t)f1 * DV + c] = val;
+          if (f2 != f1) So[(size_t)f2 * DV + c] = val;
+        }
+      }
+    }
+  }
+  for (int c = tid; c < DV; c += NTHR) So[c] = t0[c];
+  for (int f = tid; f < DPHI; f += NTHR) {
+    const int r = c_tab.phi_slot[f];
+    zo[f] = r < 0 ? z0 : (c_tab.type[r] == LIN ? zf[r] : zf[r] * INV_SQRT2);
+  }
+}
+
+// Two wavefronts per SIMD (two workgroups per CU) where the register budget
 // allows it (d_v <= 64), one otherwise.
 template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
-template <int NT, bool FULL>
+template <int NT>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
-  constexpr int PPW = Own<NT>::PPW;
-  __shared__ Smem<NT, FULL> S;
+  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
+  __shared__ Smem<NT> S;
 
-  const int nseg_here = FULL ? p.nseg : p.nseg - 1;
-  const size_t bh = blockIdx.x / nseg_here;
-  const int seg = blockIdx.x % nseg_here;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const size_t bh = blockIdx.x / p.nseg;
+  const int seg = blockIdx.x % p.nseg;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
 
-  // ---- initial state.  One segment: the caller's S_in/z_in.  Several: the
-  // state-only pass (segment s < nseg-1) starts segment 0 from S_in and the
-  // others from zero and records increments; the main pass starts segment s
-  // from the prefix record ws[s].  So S_in is read only before the main pass
-  // and S_out (written by the last segment) may alias it.
+  // ---- initial state.  One segment: the caller's S_in / z_in.  Several: the
+  // prefix record ws[seg] (the state-only pass and the scan wrote it; S_in is
+  // read only before this pass, so S_out may alias it).
   const size_t rec = (size_t)(NF + 1) * DV;
-  const float* src = nullptr;   // compact record to start from
+  const float* src = nullptr;
   const float* srcz = nullptr;
   const float* Sin = nullptr;
   const float* zin = nullptr;
-  if (p.nseg > 1 && FULL) {
+  if (p.nseg > 1) {
     src = p.ws + (bh * p.nseg + seg) * rec;
     srcz = p.wsz + (bh * p.nseg + seg) * (size_t)(NF + 1);
-  } else if (FULL || seg == 0) {
+  } else {
     Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
     zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
   }
-  f32x4 tacc[PPW];
+  f32x4 tacc[Own<NT>::PPW];
   init_state<NT>(src, Sin, tacc);
   for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
   for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
   float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
-  for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = 1.f;
-  if constexpr (FULL)
-    for (int j = tid; j < 2 * TT; j += NTHR) S.tt[j / TT][DV + 1][j % TT] = (bf16_t)0;
-  __syncthreads();
-  f32x4 tz[3];  // denominator state of the owned feature tiles, in column 0
-  {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
-#pragma unroll
-    for (int ms = 0; ms < 3; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tz[ms][i] = r16 == 0 ? S.zf[16 * mt[ms] + 4 * g + i] : 0.f;
-  }
-  if constexpr (!FULL) {
-    if (seg == 0)  // record 0: the initial state of the whole sequence
-      write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
-  }
-  publish_state<NT, FULL>(S, tacc, tz);
-
-  // update-operand rows of this wavefront's feature tiles (loop invariant)
+  for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = (half_t)1.f;
   int ia[3], ib[3];
-  {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
-#pragma unroll
-    for (int mm = 0; mm < 3; ++mm) {
-      const int r = 16 * mt[mm] + r16;
-      const int ty = c_tab.type[r];
-      ia[mm] = c_tab.a[r];
-      ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
-    }
-  }
-
+  float qw[3];
+  slot_rows(ia, ib, qw);
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   Prefetch<NT> pf;
-  if (tok_begin < tok_end) {
-    load_chunk<NT>(rs, tok_begin, FULL, pf);
-    store_chunk<NT, FULL>(S, pf);
-  }
+  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
+  __syncthreads();
+  f32x4 tz[3];  // denominator state of the owned feature tiles
+  load_tz(S.zf, tz);
+  post_max<NT>(S.wmax, tacc, tz);
+  __syncthreads();
+  float down;
+  float up = state_scale(S.wmax, down);
+  publish_state<NT>(S.tt, tacc, tz, qw, down);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
 
+  const f16x8 ones = ones8();
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
     const int n = min(C, tok_end - t0);
-    __syncthreads();  // chunk inputs, state hi/lo, t0 and zf visible
+    __syncthreads();  // chunk inputs, published state, t0 visible
     const int tn = t0 + C;
-    if (tn < tok_end) load_chunk<NT>(rs, tn, FULL, pf);
+    if (tn < tok_end) load_chunk<NT>(rs, tn, true, pf);
 
     // ---- constant row of the state: column sums of v over the chunk, in
-    // NTHR / DV partial sums per column (order within a row is irrelevant)
+    // PARTS partial sums per column (order within a row is irrelevant)
     {
-      constexpr int PARTS = NTHR / DV, SPAN = C / PARTS;
       const int col = tid % DV, part = tid / DV;
       float vs = 0.f;
+      if (part < PARTS) {
 #pragma unroll
-      for (int j = 0; j < SPAN; j += 8) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[col][part * SPAN + j]);
+        for (int j = 0; j < SPAN; j += 8) {
+          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[col][part * SPAN + j]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vs += (float)x[e];
+          for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
+        }
       }
       S.vpart[tid] = vs;
     }
 
-    // normalised outputs of this chunk; stored only after the next chunk's
-    // inputs have been consumed, so that waiting for those loads never waits
-    // for these stores (vector memory operations complete in order)
-    float yv[FULL ? NT : 1][4];
-    if constexpr (FULL) {
-      // ---- readout of the state before the chunk: positions 16w + r16
-      f32x4 acc[NT];
+    // ---- readout of the state before the chunk: positions 16w + r16
+    f32x4 acc[NT];
 #pragma unroll
-      for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float qr[16];
+    for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 accz = {0.f, 0.f, 0.f, 0.f};  // every column: denominator of the row's position
+    {
+      uint32_t q2[8];  // q of this position as fp16 pairs, rotated by 4g coordinates
       {
         const int tok = 16 * w + r16;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float4 x = *reinterpret_cast<const float4*>(&S.qs[tok][4 * ((g + m) & 3)]);
-          qr[4 * m] = x.x; qr[4 * m + 1] = x.y; qr[4 * m + 2] = x.z; qr[4 * m + 3] = x.w;
+        for (int pc = 0; pc < 4; ++pc) {
+          const uint2 x = *reinterpret_cast<const uint2*>(&S.qh[tok][4 * ((pc + g) & 3)]);
+          q2[2 * pc] = x.x;
+          q2[2 * pc + 1] = x.y;
         }
       }
-      f32x4 accz = {0.f, 0.f, 0.f, 0.f};  // column 0: denominator of each position
-      const int zrow = DV + (r16 == 0 ? 0 : 1);
+      uint32_t qo[5];  // odd pairs: (q[2j+1], q[2j+2])
+#pragma unroll
+      for (int j = 0; j < 5; ++j) qo[j] = (uint32_t)((((uint64_t)q2[j + 1] << 32) | q2[j]) >> 16);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        float f[8];
+        uint4 fw;
+        if (kb == 0) {
+          fw = make_uint4(q2[0], q2[1], u32(h2(q2[0]) * h2(q2[0])), u32(h2(q2[1]) * h2(q2[1])));
+        } else {
+          fw = make_uint4(u32(h2(q2[0]) * h2(qo[kb - 1])), u32(h2(q2[1]) * h2(qo[kb])),
+                          u32(h2(q2[0]) * h2(q2[kb])), u32(h2(q2[1]) * h2(q2[kb + 1])));
+        }
+        const f16x8 af = __builtin_bit_cast(f16x8, fw);
+        accz = mfma(af, *reinterpret_cast<const f16x8*>(&S.tt[DV][32 * kb + 8 * g]), accz);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (kb == 0) {
-            f[s] = s < 4 ? qr[s] : 0.5f * qr[s - 4] * qr[s - 4];
-          } else {
-            const int d = slot_d(kb, s), A = s % 4, B = (A + d) % 16;
-            f[s] = (d == 8 ? 0.5f : 1.f) * qr[A] * qr[B];
-          }
-        }
-        bf16x8 ahi, alo;
-        split8(f, ahi, alo);
-        {
-          const bf16x8 zhi = *reinterpret_cast<const bf16x8*>(&S.tt[0][zrow][32 * kb + 8 * g]);
-          const bf16x8 zlo = *reinterpret_cast<const bf16x8*>(&S.tt[1][zrow][32 * kb + 8 * g]);
-          accz = mfma(ahi, zhi, accz);
-          accz = mfma(ahi, zlo, accz);
-          accz = mfma(alo, zhi, accz);
-        }
-#pragma unroll
-        for (int nn = 0; nn < NT; ++nn) {
-          const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(&S.tt[0][16 * nn + r16][32 * kb + 8 * g]);
-          const bf16x8 blo = *reinterpret_cast<const bf16x8*>(&S.tt[1][16 * nn + r16][32 * kb + 8 * g]);
-          acc[nn] = mfma(ahi, bhi, acc[nn]);
-          acc[nn] = mfma(ahi, blo, acc[nn]);
-          acc[nn] = mfma(alo, bhi, acc[nn]);
-        }
+        for (int nn = 0; nn < NT; ++nn)
+          acc[nn] = mfma(af, *reinterpret_cast<const f16x8*>(&S.tt[16 * nn + r16][32 * kb + 8 * g]), acc[nn]);
       }
+    }
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) acc[nn] *= up;
+    accz *= up;
 
-      // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
-      const bf16x8 zero8 = {};
-      const bf16x8 qbv = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.qb[16 * w + r16][8 * g]) : zero8;
-      bf16x4 xh[4], xl[4];
+    // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
+    {
+      const f16x8 zero8 = {};
+      const f16x8 qv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.qh[16 * w + r16][8 * g]) : zero8;
+      uint2 xh[4], xl[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        xh[m] = bf16x4{};
-        xl[m] = bf16x4{};
+        xh[m] = make_uint2(0u, 0u);
+        xl[m] = make_uint2(0u, 0u);
         if (m <= w) {
-          const bf16x8 kav = g < 2 ? *reinterpret_cast<const bf16x8*>(&S.kb[16 * m + r16][8 * g]) : zero8;
-          const f32x4 x = mfma(kav, qbv, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f16x8 kv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.kh[16 * m + r16][8 * g]) : zero8;
+          const f32x4 x = mfma(kv, qv, f32x4{0.f, 0.f, 0.f, 0.f});
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             a[i] = 1.f + x[i] + 0.5f * x[i] * x[i];
             if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
           }
-          split4(a[0], a[1], a[2], a[3], xh[m], xl[m]);
+          split2(a[0], a[1], xh[m].x, xl[m].x);
+          split2(a[2], a[3], xh[m].y, xl[m].y);
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= w) {
-          bf16x8 ah, al;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ah[i] = xh[2 * kb][i]; ah[4 + i] = xh[2 * kb + 1][i];
-            al[i] = xl[2 * kb][i]; al[4 + i] = xl[2 * kb + 1][i];
-          }
-          {
-            const bf16x8 ones = ones_col0(r16);  // row sums of the weights -> denominator
-            accz = mfma(ah, ones, accz);
-            accz = mfma(al, ones, accz);
-          }
+          const f16x8 ah = __builtin_bit_cast(f16x8, make_uint4(xh[2 * kb].x, xh[2 * kb].y, xh[2 * kb + 1].x, xh[2 * kb + 1].y));
+          const f16x8 al = __builtin_bit_cast(f16x8, make_uint4(xl[2 * kb].x, xl[2 * kb].y, xl[2 * kb + 1].x, xl[2 * kb + 1].y));
+          accz = mfma(ah, ones, accz);
+          accz = mfma(al, ones, accz);
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
-            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&S.vt[col][vt_pos(col, 32 * kb + 4 * g)]);
-            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&S.vt[col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
-            bf16x8 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { bv[i] = v0[i]; bv[4 + i] = v1[i]; }
+            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 4 * g)]);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
+            const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
             acc[nn] = mfma(ah, bv, acc[nn]);
             acc[nn] = mfma(al, bv, acc[nn]);
           }
         }
       }
+    }
 
-      // ---- normalise and store: acc[nn][i] is position 16w + 4g + i, column 16nn + r16
-      float rden[4];  // position 16w + 4g + i: its denominator sits in column 0 (lane 16g)
+    // ---- normalise: acc[nn][i] is position 16w + 4g + i, column 16nn + r16;
+    // stored only after the next chunk's inputs have been consumed, so that
+    // waiting for those loads never waits for these stores (vector memory
+    // operations complete in order)
+    float yv[NT][4];
+    {
+      float rden[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(z0 + __shfl(accz[i], lane & 48, 64));
+      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(z0 + accz[i]);
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) {
         const float c0 = S.t0[16 * nn + r16];
@@ -674,61 +694,34 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     // ---- state update with this chunk (registers only)
     update_chunk<NT>(S.kt, S.vt, tacc, tz, ia, ib);
     z0 += (float)n;
-    __syncthreads();  // every read of tt, zf, t0 and the chunk buffers done
+    post_max<NT>(S.wmax, tacc, tz);
+    __syncthreads();  // every read of tt, t0 and the chunk buffers done; wmax complete
     if (tid < DV) {
       float vs = 0.f;
 #pragma unroll
-      for (int part = 0; part < NTHR / DV; ++part) vs += S.vpart[part * DV + tid];
+      for (int part = 0; part < PARTS; ++part) vs += S.vpart[part * DV + tid];
       S.t0[tid] += vs;
     }
-    publish_state<NT, FULL>(S, tacc, tz);
-    if (tn < tok_end) store_chunk<NT, FULL>(S, pf);
-    if constexpr (FULL) {
+    up = state_scale(S.wmax, down);
+    publish_state<NT>(S.tt, tacc, tz, qw, down);
+    if (tn < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
 #pragma unroll
-      for (int nn = 0; nn < NT; ++nn) {
-        const int col = 16 * nn + r16;
+    for (int nn = 0; nn < NT; ++nn) {
+      const int col = 16 * nn + r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = 16 * w + 4 * g + i;
-          if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = yv[nn][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int pos = 16 * w + 4 * g + i;
+        if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = yv[nn][i];
       }
     }
   }
-  __syncthreads();
 
-  // ---- segment result: the record after segment s (state-only pass) or S_out
-  store_z<NT>(S.zf, tz);
-  __syncthreads();
-  if constexpr (!FULL) {
-    write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
-                      p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
-  } else {
-    if (p.S_out && seg == p.nseg - 1) {
-      float* stage = reinterpret_cast<float*>(&S.tt[0][0][0]);  // [NF][DV] fp32
-#pragma unroll
-      for (int j = 0; j < PPW; ++j) {
-        int m, nn;
-        pair_mn<NT>(w, j, m, nn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stage[(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
-      }
-      __syncthreads();
-      float* So = p.S_out + bh * DPHI * DV;
-      for (int e = tid; e < DPHI * DV; e += NTHR) {
-        const int f = e / DV, c = e % DV;
-        const int r = c_tab.phi_slot[f];
-        float val;
-        if (r < 0) val = S.t0[c];
-        else val = c_tab.type[r] == LIN ? stage[r * DV + c] : stage[r * DV + c] * INV_SQRT2;
-        So[e] = val;
-      }
-      float* zo = p.z_out + bh * DPHI;
-      for (int f = tid; f < DPHI; f += NTHR) {
-        const int r = c_tab.phi_slot[f];
-        zo[f] = r < 0 ? z0 : (c_tab.type[r] == LIN ? S.zf[r] : S.zf[r] * INV_SQRT2);
-      }
-    }
+  // ---- the last segment writes the final state
+  if (p.S_out && seg == p.nseg - 1) {
+    __syncthreads();  // t0 complete
+    store_z<NT>(S.zf, tz);
+    __syncthreads();
+    write_phi_state<NT>(S.t0, S.zf, tacc, z0, p.S_out + bh * DPHI * DV, p.z_out + bh * DPHI);
   }
 }
 
@@ -741,8 +734,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 template <int NT>
 struct StateSmem {
   static constexpr int DV = 16 * NT;
-  alignas(16) float kt[2][DK + 1][KT];
-  alignas(16) bf16_t vt[2][DV][VT];
+  alignas(16) half_t kt[2][DK + 1][KT];
+  alignas(16) half_t vt[2][DV][VT];
   alignas(16) float vpart[NTHR];
   alignas(16) float t0[DV];
   alignas(16) float zf[NF];
@@ -751,48 +744,33 @@ struct StateSmem {
 template <int NT>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
   constexpr int DV = 16 * NT;
-  constexpr int PPW = Own<NT>::PPW;
-  constexpr int PARTS = NTHR / DV, SPAN = C / PARTS;
+  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
   __shared__ StateSmem<NT> S;
 
   const int nsm = p.nseg - 1;
   const size_t bh = blockIdx.x / nsm;
   const int seg = blockIdx.x % nsm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x;
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
   const size_t rec = (size_t)(NF + 1) * DV;
 
   const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
-  f32x4 tacc[PPW];
+  f32x4 tacc[Own<NT>::PPW];
   init_state<NT>(nullptr, Sin, tacc);
   for (int c = tid; c < DV; c += NTHR) S.t0[c] = Sin ? Sin[c] : 0.f;
   for (int r = tid; r < NF; r += NTHR) S.zf[r] = zin ? compact_from_phi(zin, r, 0, 1) : 0.f;
   float z0 = zin ? zin[0] : 0.f;
-  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = 1.f;
+  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = (half_t)1.f;
   __syncthreads();
   f32x4 tz[3];
-  {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
-#pragma unroll
-    for (int ms = 0; ms < 3; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tz[ms][i] = r16 == 0 ? S.zf[16 * mt[ms] + 4 * g + i] : 0.f;
-  }
+  load_tz(S.zf, tz);
   if (seg == 0)  // record 0: the initial state of the whole sequence
     write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   int ia[3], ib[3];
-  {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
-#pragma unroll
-    for (int mm = 0; mm < 3; ++mm) {
-      const int r = 16 * mt[mm] + r16;
-      const int ty = c_tab.type[r];
-      ia[mm] = c_tab.a[r];
-      ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
-    }
-  }
+  float qw[3];
+  slot_rows(ia, ib, qw);
 
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   const int col = tid % DV, part = tid / DV;
@@ -800,7 +778,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   Prefetch<NT> pa, pb;
   if (tok_begin < tok_end) {
     load_chunk<NT>(rs, tok_begin, false, pa);
-    store_kv<NT>(S.kt[0], S.vt[0], pa);
+    store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, pa);
   }
   if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, pb);
 
@@ -808,14 +786,16 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
     __syncthreads();
     if (t + 2 * C < tok_end) load_chunk<NT>(rs, t + 2 * C, false, spare);
+    if (part < PARTS) {
 #pragma unroll
-    for (int j = 0; j < SPAN; j += 8) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(&S.vt[buf][col][part * SPAN + j]);
+      for (int j = 0; j < SPAN; j += 8) {
+        const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vs += (float)x[e];
+        for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
+      }
     }
     update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
-    if (t + C < tok_end) store_kv<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], next);
+    if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], nullptr, nullptr, next);
   };
   for (int t = tok_begin; t < tok_end; t += 2 * C) {
     step(t, 0, pb, pa);
@@ -912,7 +892,7 @@ static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((linattn_mfma_kernel<NT, true>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((linattn_mfma_kernel<NT>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
