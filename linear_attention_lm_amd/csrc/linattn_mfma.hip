@@ -348,10 +348,20 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
     tz[0] = mfma(a[0], ones, tz[0]);
     tz[1] = mfma(a[1], ones, tz[1]);
     if ((w & 1) == 0) tz[2] = mfma(a[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
+    // keep the operands of the two K-steps from being live at once
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Largest magnitude of this wavefront's state entries, into wmax[w].
+// DPP move of a lane value (row_mask / bank_mask all, out-of-row sources read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Largest magnitude of this wavefront's state entries, into wmax[w]: quad and
+// row reductions in DPP, then the four row results through scalar registers
+// (non-negative floats order like their bit patterns).
 template <int NT>
 __device__ __forceinline__ void post_max(float* wmax, const f32x4 (&tacc)[Own<NT>::PPW], const f32x4 (&tz)[3]) {
   float m = 0.f;
@@ -363,44 +373,66 @@ __device__ __forceinline__ void post_max(float* wmax, const f32x4 (&tacc)[Own<NT
   for (int ms = 0; ms < 3; ++ms)
 #pragma unroll
     for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(tz[ms][i]));
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  m = fmaxf(m, dpp<0xb1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp<0x4e>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp<0x114>(m));  // row_shr:4
+  m = fmaxf(m, dpp<0x118>(m));  // row_shr:8 -> lane 15 of each row holds the row maximum
+  const int b = __float_as_int(m);
+  const uint32_t r0 = __builtin_amdgcn_readlane(b, 15), r1 = __builtin_amdgcn_readlane(b, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(b, 47), r3 = __builtin_amdgcn_readlane(b, 63);
+  const uint32_t mx = max(max(r0, r1), max(r2, r3));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = __uint_as_float(mx);
 }
 
 // Power-of-two scale of the published state from the block's largest entry
-// M (wmax, after a barrier): entries times 2^-e stay below 2^(SCALE_TOP+1).
-// Returns 2^e, the factor that undoes it.
-__device__ __forceinline__ float state_scale(const float* wmax, float& down) {
-  const float4 mm = *reinterpret_cast<const float4*>(wmax);
-  const float M = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
-  int e = (int)((__float_as_uint(M) >> 23) & 0xffu) - 127 - SCALE_TOP;
+// M (wmax, after a barrier).  No scale (e = 0) while M is in [2^-4, 2^14):
+// entries then stay below fp16's largest value and those that fall below its
+// normal range are negligible next to M.  Otherwise entries times 2^-e stay
+// below 2^(SCALE_TOP + 1).  Returns e; down = 2^-e, up = 2^e.
+__device__ __forceinline__ int state_scale(const float* wmax, float& down, float& up) {
+  const uint4 mm = *reinterpret_cast<const uint4*>(wmax);
+  const uint32_t mb = max(max(mm.x, mm.y), max(mm.z, mm.w));  // non-negative: order as integers
+  const int E = (int)((mb >> 23) & 0xffu) - 127;                 // floor(log2 M) (-127: zero)
+  int e = (E >= -4 && E < 14) ? 0 : E - SCALE_TOP;
   e = e < -126 ? -126 : e;
   down = __uint_as_float((uint32_t)(127 - e) << 23);
-  return __uint_as_float((uint32_t)(127 + e) << 23);
+  up = __uint_as_float((uint32_t)(127 + e) << 23);
+  return e;
 }
 
 // Write the owned state tiles (and the denominator state) into tt as fp16,
-// times `down` and the slot's query weight (the caller has synchronised:
-// nobody reads tt meanwhile).
+// times `down` unless e = 0 (the caller has synchronised: nobody reads tt
+// meanwhile).
 template <int NT>
 __device__ __forceinline__ void publish_state(half_t (*tt)[TT], const f32x4 (&tacc)[Own<NT>::PPW],
-                                              const f32x4 (&tz)[3], const float (&qw)[3], float down) {
+                                              const f32x4 (&tz)[3], int e, float down) {
   constexpr int DV = 16 * NT;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
-  const float f[3] = {down * qw[0], down * qw[1], down * qw[2]};
+  const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+  if (e == 0) {
 #pragma unroll
-  for (int j = 0; j < Own<NT>::PPW; ++j) {
-    int m, n;
-    pair_mn<NT>(w, j, m, n);
-    const float s = f[j < NT ? 0 : (j < 2 * NT ? 1 : 2)];
-    *reinterpret_cast<f16x4*>(&tt[16 * n + r16][16 * m + 4 * g]) = __builtin_convertvector(tacc[j] * s, f16x4);
-  }
-  if (r16 == 0) {
-    const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+    for (int j = 0; j < Own<NT>::PPW; ++j) {
+      int m, n;
+      pair_mn<NT>(w, j, m, n);
+      *reinterpret_cast<f16x4*>(&tt[16 * n + r16][16 * m + 4 * g]) = __builtin_convertvector(tacc[j], f16x4);
+    }
+    if (r16 == 0)
 #pragma unroll
-    for (int ms = 0; ms < 3; ++ms)
-      if (ms < 2 || (w & 1) == 0)
-        *reinterpret_cast<f16x4*>(&tt[DV][16 * mt[ms] + 4 * g]) = __builtin_convertvector(tz[ms] * f[ms], f16x4);
+      for (int ms = 0; ms < 3; ++ms)
+        if (ms < 2 || (w & 1) == 0)
+          *reinterpret_cast<f16x4*>(&tt[DV][16 * mt[ms] + 4 * g]) = __builtin_convertvector(tz[ms], f16x4);
+  } else {
+#pragma unroll
+    for (int j = 0; j < Own<NT>::PPW; ++j) {
+      int m, n;
+      pair_mn<NT>(w, j, m, n);
+      *reinterpret_cast<f16x4*>(&tt[16 * n + r16][16 * m + 4 * g]) = __builtin_convertvector(tacc[j] * down, f16x4);
+    }
+    if (r16 == 0)
+#pragma unroll
+      for (int ms = 0; ms < 3; ++ms)
+        if (ms < 2 || (w & 1) == 0)
+          *reinterpret_cast<f16x4*>(&tt[DV][16 * mt[ms] + 4 * g]) = __builtin_convertvector(tz[ms] * down, f16x4);
   }
 }
 
@@ -448,10 +480,9 @@ __device__ __forceinline__ void load_tz(const float* zf, f32x4 (&tz)[3]) {
 }
 
 // Loop-invariant per-lane data of the owned feature tiles: the k^T rows
-// whose product is the key feature of the lane's slot (update operand rows),
-// and the query weight of the slots whose rows the lane publishes.
-__device__ __forceinline__ void slot_rows(int (&ia)[3], int (&ib)[3], float (&qw)[3]) {
-  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+// whose product is the key feature of the lane's slot (update operand rows).
+__device__ __forceinline__ void slot_rows(int (&ia)[3], int (&ib)[3]) {
+  const int lane = threadIdx.x & 63, w = wave_index(), r16 = lane & 15;
   const int mt[3] = {w, w + 4, 8 + (w >> 1)};
 #pragma unroll
   for (int mm = 0; mm < 3; ++mm) {
@@ -459,8 +490,6 @@ __device__ __forceinline__ void slot_rows(int (&ia)[3], int (&ib)[3], float (&qw
     const int ty = c_tab.type[r];
     ia[mm] = c_tab.a[r];
     ib[mm] = ty == LIN ? ONES : (ty == DIAG ? ia[mm] : c_tab.b[r]);
-    const int tw = c_tab.type[16 * mt[mm] + 4 * g];  // rows 4g..4g+3 share the kind
-    qw[mm] = (tw == DIAG || tw == HALF) ? 0.5f : 1.f;
   }
 }
 
@@ -555,8 +584,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
   for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = (half_t)1.f;
   int ia[3], ib[3];
-  float qw[3];
-  slot_rows(ia, ib, qw);
+  slot_rows(ia, ib);
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   Prefetch<NT> pf;
   if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
@@ -565,12 +593,13 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   load_tz(S.zf, tz);
   post_max<NT>(S.wmax, tacc, tz);
   __syncthreads();
-  float down;
-  float up = state_scale(S.wmax, down);
-  publish_state<NT>(S.tt, tacc, tz, qw, down);
+  float down, up;
+  int e = state_scale(S.wmax, down, up);
+  publish_state<NT>(S.tt, tacc, tz, e, down);
   if (tok_begin < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
 
   const f16x8 ones = ones8();
+  const int pos = 16 * w + r16;  // the chunk position whose outputs this lane holds
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
     const int n = min(C, tok_end - t0);
     __syncthreads();  // chunk inputs, published state, t0 visible
@@ -587,55 +616,61 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
         for (int j = 0; j < SPAN; j += 8) {
           const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[col][part * SPAN + j]);
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
+          for (int k2 = 0; k2 < 8; k2 += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[k2], x[k2 + 1]}, f16x2{1, 1}, vs, false);
         }
       }
       S.vpart[tid] = vs;
     }
 
-    // ---- readout of the state before the chunk: positions 16w + r16
+    // ---- readout of the state before the chunk, transposed (value columns x
+    // positions): acc[nn][i] is column 16nn + 4g + i of position `pos`; every
+    // entry of accz is the denominator of `pos`
     f32x4 acc[NT];
 #pragma unroll
     for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 accz = {0.f, 0.f, 0.f, 0.f};  // every column: denominator of the row's position
+    f32x4 accz = {0.f, 0.f, 0.f, 0.f};
     {
       uint32_t q2[8];  // q of this position as fp16 pairs, rotated by 4g coordinates
-      {
-        const int tok = 16 * w + r16;
 #pragma unroll
-        for (int pc = 0; pc < 4; ++pc) {
-          const uint2 x = *reinterpret_cast<const uint2*>(&S.qh[tok][4 * ((pc + g) & 3)]);
-          q2[2 * pc] = x.x;
-          q2[2 * pc + 1] = x.y;
-        }
+      for (int pc = 0; pc < 4; ++pc) {
+        const uint2 x = *reinterpret_cast<const uint2*>(&S.qh[pos][4 * ((pc + g) & 3)]);
+        q2[2 * pc] = x.x;
+        q2[2 * pc + 1] = x.y;
       }
       uint32_t qo[5];  // odd pairs: (q[2j+1], q[2j+2])
 #pragma unroll
       for (int j = 0; j < 5; ++j) qo[j] = (uint32_t)((((uint64_t)q2[j + 1] << 32) | q2[j]) >> 16);
+      // query weight 1/2 of the square and {a, a+8} slots on the first factor
+      const f16x2 half2 = {(half_t)0.5f, (half_t)0.5f};
+      const uint32_t qh0 = u32(h2(q2[0]) * half2), qh1 = u32(h2(q2[1]) * half2);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         uint4 fw;
         if (kb == 0) {
-          fw = make_uint4(q2[0], q2[1], u32(h2(q2[0]) * h2(q2[0])), u32(h2(q2[1]) * h2(q2[1])));
+          fw = make_uint4(q2[0], q2[1], u32(h2(qh0) * h2(q2[0])), u32(h2(qh1) * h2(q2[1])));
         } else {
           fw = make_uint4(u32(h2(q2[0]) * h2(qo[kb - 1])), u32(h2(q2[1]) * h2(qo[kb])),
-                          u32(h2(q2[0]) * h2(q2[kb])), u32(h2(q2[1]) * h2(q2[kb + 1])));
+                          u32(h2(kb == NKB - 1 ? qh0 : q2[0]) * h2(q2[kb])),
+                          u32(h2(kb == NKB - 1 ? qh1 : q2[1]) * h2(q2[kb + 1])));
         }
-        const f16x8 af = __builtin_bit_cast(f16x8, fw);
-        accz = mfma(af, *reinterpret_cast<const f16x8*>(&S.tt[DV][32 * kb + 8 * g]), accz);
+        const f16x8 fb = __builtin_bit_cast(f16x8, fw);
+        accz = mfma(*reinterpret_cast<const f16x8*>(&S.tt[DV][32 * kb + 8 * g]), fb, accz);
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn)
-          acc[nn] = mfma(af, *reinterpret_cast<const f16x8*>(&S.tt[16 * nn + r16][32 * kb + 8 * g]), acc[nn]);
+          acc[nn] = mfma(*reinterpret_cast<const f16x8*>(&S.tt[16 * nn + r16][32 * kb + 8 * g]), fb, acc[nn]);
       }
     }
+    if (e != 0) {
 #pragma unroll
-    for (int nn = 0; nn < NT; ++nn) acc[nn] *= up;
-    accz *= up;
+      for (int nn = 0; nn < NT; ++nn) acc[nn] *= up;
+      accz *= up;
+    }
 
-    // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15
+    // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15, then
+    // Y^T += V^T P^T with the weights P = 1 + x + x^2/2 split into fp16 hi + lo
     {
       const f16x8 zero8 = {};
-      const f16x8 qv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.qh[16 * w + r16][8 * g]) : zero8;
+      const f16x8 qv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.qh[pos][8 * g]) : zero8;
       uint2 xh[4], xl[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -647,7 +682,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            a[i] = 1.f + x[i] + 0.5f * x[i] * x[i];
+            a[i] = __builtin_fmaf(x[i], __builtin_fmaf(x[i], 0.5f, 1.f), 1.f);
             if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
           }
           split2(a[0], a[1], xh[m].x, xl[m].x);
@@ -657,37 +692,37 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= w) {
-          const f16x8 ah = __builtin_bit_cast(f16x8, make_uint4(xh[2 * kb].x, xh[2 * kb].y, xh[2 * kb + 1].x, xh[2 * kb + 1].y));
-          const f16x8 al = __builtin_bit_cast(f16x8, make_uint4(xl[2 * kb].x, xl[2 * kb].y, xl[2 * kb + 1].x, xl[2 * kb + 1].y));
-          accz = mfma(ah, ones, accz);
-          accz = mfma(al, ones, accz);
+          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(xh[2 * kb].x, xh[2 * kb].y, xh[2 * kb + 1].x, xh[2 * kb + 1].y));
+          const f16x8 pl = __builtin_bit_cast(f16x8, make_uint4(xl[2 * kb].x, xl[2 * kb].y, xl[2 * kb + 1].x, xl[2 * kb + 1].y));
+          accz = mfma(ones, ph, accz);
+          accz = mfma(ones, pl, accz);
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
             const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 4 * g)]);
             const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
-            const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-            acc[nn] = mfma(ah, bv, acc[nn]);
-            acc[nn] = mfma(al, bv, acc[nn]);
+            const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            acc[nn] = mfma(va, ph, acc[nn]);
+            acc[nn] = mfma(va, pl, acc[nn]);
           }
         }
       }
     }
 
-    // ---- normalise: acc[nn][i] is position 16w + 4g + i, column 16nn + r16;
-    // stored only after the next chunk's inputs have been consumed, so that
-    // waiting for those loads never waits for these stores (vector memory
-    // operations complete in order)
-    float yv[NT][4];
+    // ---- normalise and store.  The next chunk's loads were issued before
+    // these stores, so waiting for them never waits for the stores (vector
+    // memory operations complete in order).
     {
-      float rden[4];
+      const float rden = __builtin_amdgcn_rcpf(z0 + accz[0]);
+      if (pos < n) {
+        float* yrow = p.y + (bh * p.L + t0 + pos) * DV + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(z0 + accz[i]);
-#pragma unroll
-      for (int nn = 0; nn < NT; ++nn) {
-        const float c0 = S.t0[16 * nn + r16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yv[nn][i] = (acc[nn][i] + c0) * rden[i];
+        for (int nn = 0; nn < NT; ++nn) {
+          const float4 c0 = *reinterpret_cast<const float4*>(&S.t0[16 * nn + 4 * g]);
+          *reinterpret_cast<float4*>(yrow + 16 * nn) =
+              make_float4((acc[nn][0] + c0.x) * rden, (acc[nn][1] + c0.y) * rden, (acc[nn][2] + c0.z) * rden,
+                          (acc[nn][3] + c0.w) * rden);
+        }
       }
     }
 
@@ -702,18 +737,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int part = 0; part < PARTS; ++part) vs += S.vpart[part * DV + tid];
       S.t0[tid] += vs;
     }
-    up = state_scale(S.wmax, down);
-    publish_state<NT>(S.tt, tacc, tz, qw, down);
+    e = state_scale(S.wmax, down, up);
+    publish_state<NT>(S.tt, tacc, tz, e, down);
     if (tn < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
-#pragma unroll
-    for (int nn = 0; nn < NT; ++nn) {
-      const int col = 16 * nn + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = 16 * w + 4 * g + i;
-        if (pos < n) p.y[(bh * p.L + t0 + pos) * DV + col] = yv[nn][i];
-      }
-    }
   }
 
   // ---- the last segment writes the final state
@@ -769,8 +795,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   if (seg == 0)  // record 0: the initial state of the whole sequence
     write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   int ia[3], ib[3];
-  float qw[3];
-  slot_rows(ia, ib, qw);
+  slot_rows(ia, ib);
 
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   const int col = tid % DV, part = tid / DV;
@@ -834,10 +859,20 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
     base = wsz + bh * nseg * (size_t)(NF + 1) + (o - rec);
     stride = NF + 1;
   }
+  // records are loaded 8 at a time before any is written, so the loads of a
+  // group are in flight together
   float run = base[stride];
-  for (int s = 2; s < nseg; ++s) {
-    run += base[s * stride];
-    base[s * stride] = run;
+  for (int s0 = 2; s0 < nseg; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = s0 + i < nseg ? base[(size_t)(s0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i < nseg) {
+        run += x[i];
+        base[(size_t)(s0 + i) * stride] = run;
+      }
+    }
   }
 }
 
