@@ -50,12 +50,12 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 1
+#define BASED_ABI_VERSION 2
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
   BASED_F32 = 0,  /* fp32: arithmetic in fp32 throughout                       */
-  BASED_BF16 = 1  /* bf16: products on bf16 matrix cores, accumulation in fp32 */
+  BASED_BF16 = 1  /* bf16: products on the matrix cores, accumulation in fp32 */
 };
 
 enum {
@@ -109,6 +109,14 @@ size_t based_linattn_workspace_bytes(int B, int H, int L, int d_k, int d_v, int 
  * With zero initial state the denominator of row i is at least (i + 1) / 2,
  * so no epsilon is added.  y must not overlap q, k, v, S_in or z_in;
  * S_out/z_out may alias S_in/z_in (in-place state update).
+ *
+ * BASED_BF16 with d_v in {32, 64, 96, 128} runs on the matrix cores with fp16
+ * operands (bf16 inputs convert exactly): Taylor features and the state copy
+ * read out by each chunk are rounded to fp16 once (relative 2^-11; the state
+ * is scaled by a power of two, so its size is not limited), the in-chunk
+ * weights are split into fp16 hi + lo, and all sums are fp32.  Inputs must
+ * stay in fp16 range there: |q|, |k| < 128 per coordinate, |q.k| < 256 and
+ * |v| < 32768.  Other d_v, and BASED_F32, use fp32 vector arithmetic.
  */
 int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
                       const float* S_in, const float* z_in, float* S_out, float* z_out,
@@ -129,6 +137,28 @@ int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
 int based_swa_fwd(const void* q, const void* k, const void* v, float* y,
                   int B, int H, int L, int d_qk, int d_v, int window, float scale,
                   int dtype, void* stream);
+
+/*
+ * The Based layer's two attentions over the same q, k, v in one pass: the
+ * outputs of based_linattn_fwd (y_lin, with its state arguments) and of
+ * based_swa_fwd with d_qk = d_k (y_swa) from a single read of the inputs
+ * (README intro: the layer pairs a global linear attention with a short
+ * sliding-window softmax attention).
+ *
+ *   q, k, v, S_in, z_in, S_out, z_out, workspace: as for based_linattn_fwd
+ *          (workspace size from based_linattn_workspace_bytes)
+ *   y_lin  [B,H,L,d_v] fp32 out -- based_linattn_fwd's y
+ *   y_swa  [B,H,L,d_v] fp32 out -- based_swa_fwd's y (d_qk = d_k = 16)
+ *   window, scale: as for based_swa_fwd.
+ * Neither output may overlap an input, a state or the other output.
+ * BASED_BF16 with d_v in {32, 64, 96, 128} is one fused matrix-core pass (with
+ * the input ranges of based_linattn_fwd); otherwise the two attentions run
+ * as separate kernels.
+ */
+int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
+                    const float* S_in, const float* z_in, float* S_out, float* z_out,
+                    int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Fill the decode ring buffers from a context and set the positions

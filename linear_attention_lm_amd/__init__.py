@@ -20,7 +20,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd",
+    "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd", "layer_fwd",
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
 
@@ -36,6 +36,7 @@ _SIGNATURES = {
     "based_linattn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "based_linattn_fwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
     "based_swa_fwd": (_i, [_vp] * 4 + [_i] * 6 + [_f, _i, _vp]),
+    "based_layer_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
     "based_decode_prefill": (_i, [_vp] * 5 + [_i] * 7 + [_vp]),
     "based_decode_step": (_i, [_vp] * 10 + [_i] * 5 + [_f, _i, _vp]),
 }
@@ -158,6 +159,37 @@ def swa_fwd(q, k, v, window: int = 64, scale: float = 1.0, *, y=None):
     return y
 
 
+def layer_fwd(q, k, v, window: int = 64, scale: float = 1.0, S_in=None, z_in=None, *, return_state=False,
+              y_lin=None, y_swa=None, S_out=None, z_out=None, workspace=None):
+    """Both attentions of the layer over the same q, k [B,H,L,16], v [B,H,L,dv]
+    in one pass: returns (y_lin, y_swa), plus the final linear-attention state
+    (S, z) when ``return_state`` -- the outputs of :func:`linattn_fwd` and of
+    :func:`swa_fwd` with the same arguments."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    _dev(q, k, v, S_in, z_in, y_lin, y_swa, S_out, z_out, workspace)
+    if y_lin is None:
+        y_lin = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if y_swa is None:
+        y_swa = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if return_state and S_out is None:
+        S_out = torch.empty(B, H, DPHI, dv, device=q.device, dtype=torch.float32)
+        z_out = torch.empty(B, H, DPHI, device=q.device, dtype=torch.float32)
+    dt = _dtype_code(q)
+    need = _lib().based_linattn_workspace_bytes(B, H, L, dk, dv, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().based_layer_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y_lin), _ptr(y_swa), _ptr(S_in), _ptr(z_in),
+                                  _ptr(S_out), _ptr(z_out), B, H, L, dk, dv, window, float(scale), dt,
+                                  _ptr(workspace), wbytes, _stream()))
+    if return_state or S_out is not None:
+        return y_lin, y_swa, S_out, z_out
+    return y_lin, y_swa
+
+
 @dataclass
 class DecodeState:
     """Caller-owned generation state: S [B,H,273,dv] fp32, z [B,H,273] fp32,
@@ -188,8 +220,7 @@ def decode_init(q, k, v, window: int = 64):
     ready for :func:`decode_step` at position L."""
     B, H, L, _ = k.shape
     dv = v.shape[-1]
-    y_lin, S, z = linattn_fwd(q, k, v, return_state=True)
-    y_swa = swa_fwd(q, k, v, window)
+    y_lin, y_swa, S, z = layer_fwd(q, k, v, window, return_state=True)
     st = DecodeState(S, z, torch.zeros(B, H, window, DK, device=k.device, dtype=k.dtype),
                      torch.zeros(B, H, window, dv, device=k.device, dtype=k.dtype),
                      torch.zeros(B, device=k.device, dtype=torch.int32))

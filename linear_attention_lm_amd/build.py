@@ -22,7 +22,12 @@ LIB = os.path.join(PKG, "libbased.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-mfma-vgpr-form: matrix-core operands and results in VGPRs (AGPRs
+# only as spill space).  With the default AGPR form this toolchain's -O3
+# build of the occupancy-1 linear-attention kernels (d_v 96 and 128) gave
+# results off by ~5e-3 in every chunk after the first; the VGPR form (and -O1)
+# give the exact results, and the d_v <= 64 kernels compile identically.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 CXXFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
             "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
 

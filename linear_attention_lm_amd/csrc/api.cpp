@@ -83,6 +83,49 @@ BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, flo
   return status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 
+BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
+                               const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
+                               int L, int d_k, int d_v, int window, float scale, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if ((long long)B * H * ((L + 31) / 32) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
+  if (L > 0 && (!q || !k || !v || !y_lin || !y_swa)) return BASED_ERR_NULL;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
+  const void* ptrs[] = {q, k, v, y_lin, y_swa, S_in, z_in, S_out, z_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t need = based_linattn_workspace_bytes(B, H, L, d_k, d_v, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BASED_ERR_WORKSPACE;
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  const Span outs[] = {span(y_lin, BH * L * d_v * 4), span(y_swa, BH * L * d_v * 4)};
+  const Span ins[] = {span(q, BH * L * d_k * es), span(k, BH * L * d_k * es), span(v, BH * L * d_v * es),
+                      span(S_in, BH * BASED_DPHI * d_v * 4), span(z_in, BH * BASED_DPHI * 4),
+                      span(S_out, BH * BASED_DPHI * d_v * 4), span(z_out, BH * BASED_DPHI * 4)};
+  if (L > 0) {
+    if (overlap(outs[0], outs[1])) return BASED_ERR_ALIAS;
+    for (const Span& o : outs)
+      for (const Span& s : ins)
+        if (overlap(o, s)) return BASED_ERR_ALIAS;
+  }
+  if (S_out && (overlap(ins[5], ins[0]) || overlap(ins[5], ins[1]) || overlap(ins[5], ins[2])))
+    return BASED_ERR_ALIAS;
+
+  based::LinattnArgs a{q, k, v, y_lin, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
+  if (L == 0 && !S_out) return BASED_OK;
+  if (dtype == BASED_BF16 && based::linattn_mfma_supported(d_v))
+    return status_of(based::launch_layer_mfma(a, y_swa, window, scale, (hipStream_t)stream));
+  if (int st = status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream)); st != BASED_OK)
+    return st;
+  if (L == 0) return BASED_OK;
+  based::SwaArgs sa{q, k, v, y_swa, B, H, L, d_k, d_v, window, scale};
+  if (dtype == BASED_BF16) return status_of(based::launch_swa_mfma(sa, (hipStream_t)stream));
+  return status_of(based::launch_swa_valu(sa, false, (hipStream_t)stream));
+}
+
 BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* y, int B, int H, int L, int d_qk,
                             int d_v, int window, float scale, int dtype, void* stream) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;

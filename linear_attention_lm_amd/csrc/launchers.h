@@ -24,6 +24,9 @@ bool linattn_mfma_supported(int dv);
 size_t linattn_mfma_workspace(int B, int H, int L, int dv);
 void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
+// The same pass with the sliding-window softmax of the same q, k, v fused in
+// (d_qk = d_k = 16), written to y_swa.
+hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t stream);
 
 struct SwaArgs {
   const void* q; const void* k; const void* v; float* y;

@@ -150,19 +150,24 @@ struct Params {
   float* ws;        // [BH][nseg][NF+1][DV] compact state records (row NF = constant row)
   float* wsz;       // [BH][nseg][NF+1] likewise for z (entry NF = constant: token count)
   int L, nseg, seg_chunks;
+  float* y_swa;     // sliding-window softmax output of the fused layer pass
+  int window;
+  float swa_scale;
 };
 
 // LDS of the main pass.  vt is v^T with the 8-position groups of row `col`
 // XOR-swizzled by (col / 8) % 8, so that the transposing writes of a
 // wavefront spread over all banks while 8 consecutive positions stay
-// contiguous for 16-byte reads.
-template <int NT>
+// contiguous for 16-byte reads.  With the sliding window (SWA) the row-major
+// k and v^T keep the previous chunk too (NB = 2 buffers).
+template <int NT, bool SWA>
 struct Smem {
   static constexpr int DV = 16 * NT;
+  static constexpr int NB = SWA ? 2 : 1;
   alignas(16) half_t qh[C][QH];          // q, row-major
-  alignas(16) half_t kh[C][QH];          // k, row-major
+  alignas(16) half_t kh[NB][C][QH];      // k, row-major
   alignas(16) half_t kt[DK + 1][KT];     // k^T; row ONES = 1
-  alignas(16) half_t vt[DV][VT];         // v^T, swizzled
+  alignas(16) half_t vt[NB][DV][VT];     // v^T, swizzled
   alignas(16) half_t tt[DV + 1][TT];     // scaled state^T; row DV: denominator state
   alignas(16) float t0[DV];              // constant row of the state (sum of v)
   alignas(16) float vpart[NTHR];         // partial column sums of v
@@ -550,11 +555,11 @@ __device__ __forceinline__ void write_phi_state(const float* t0, const float* zf
 // allows it (d_v <= 64), one otherwise.
 template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
-template <int NT>
+template <int NT, bool SWA>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
-  __shared__ Smem<NT> S;
+  __shared__ Smem<NT, SWA> S;
 
   const size_t bh = blockIdx.x / p.nseg;
   const int seg = blockIdx.x % p.nseg;
@@ -587,6 +592,16 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   slot_rows(ia, ib);
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   Prefetch<NT> pf;
+  if constexpr (SWA) {
+    // the window of the segment's first chunk reaches into the chunk before
+    if (tok_begin > 0) {
+      load_chunk<NT>(rs, tok_begin - C, false, pf);
+      store_chunk<NT>(S.kt, S.vt[1], nullptr, S.kh[1], pf);
+    } else {
+      for (int j = tid; j < C * QH / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.kh[1][0][0])[j] = 0u;
+      for (int j = tid; j < DV * VT / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.vt[1][0][0])[j] = 0u;
+    }
+  }
   if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
   __syncthreads();
   f32x4 tz[3];  // denominator state of the owned feature tiles
@@ -596,7 +611,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   float down, up;
   int e = state_scale(S.wmax, down, up);
   publish_state<NT>(S.tt, tacc, tz, e, down);
-  if (tok_begin < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt, S.vt[0], S.qh, S.kh[0], pf);
+  int cur = 0;  // buffer of the current chunk's k and v^T (the other: previous chunk)
 
   const f16x8 ones = ones8();
   const int pos = 16 * w + r16;  // the chunk position whose outputs this lane holds
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       if (part < PARTS) {
 #pragma unroll
         for (int j = 0; j < SPAN; j += 8) {
-          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[col][part * SPAN + j]);
+          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[cur][col][part * SPAN + j]);
 #pragma unroll
           for (int k2 = 0; k2 < 8; k2 += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[k2], x[k2 + 1]}, f16x2{1, 1}, vs, false);
         }
@@ -668,21 +684,28 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 
     // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15, then
     // Y^T += V^T P^T with the weights P = 1 + x + x^2/2 split into fp16 hi + lo
+    const f16x8 zero8 = {};
+    const f16x8 qv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.qh[pos][8 * g]) : zero8;
+    f32x4 xc[4];  // scores against the chunk's key tiles m <= w: key 16m + 4g + i, query `pos`
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      xc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m <= w) {
+        const f16x8 kv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.kh[cur][16 * m + r16][8 * g]) : zero8;
+        xc[m] = mfma(kv, qv, xc[m]);
+      }
+    }
     {
-      const f16x8 zero8 = {};
-      const f16x8 qv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.qh[pos][8 * g]) : zero8;
       uint2 xh[4], xl[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         xh[m] = make_uint2(0u, 0u);
         xl[m] = make_uint2(0u, 0u);
         if (m <= w) {
-          const f16x8 kv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.kh[16 * m + r16][8 * g]) : zero8;
-          const f32x4 x = mfma(kv, qv, f32x4{0.f, 0.f, 0.f, 0.f});
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            a[i] = __builtin_fmaf(x[i], __builtin_fmaf(x[i], 0.5f, 1.f), 1.f);
+            a[i] = __builtin_fmaf(xc[m][i], __builtin_fmaf(xc[m][i], 0.5f, 1.f), 1.f);
             if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
           }
           split2(a[0], a[1], xh[m].x, xl[m].x);
@@ -699,8 +722,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 4 * g)]);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
+            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[cur][col][vt_pos(col, 32 * kb + 4 * g)]);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[cur][col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
             const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
             acc[nn] = mfma(va, ph, acc[nn]);
             acc[nn] = mfma(va, pl, acc[nn]);
@@ -726,8 +749,94 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       }
     }
 
+    // ---- sliding-window softmax of the same q, k, v (fused layer pass): the
+    // keys of query `pos` are the chunk's tiles m <= w (scores xc) and the
+    // previous chunk's tiles m >= w; 5 tiles and 3 key blocks per wavefront
+    if constexpr (SWA) {
+      const int prev = cur ^ 1;
+      f32x4 xp[4];  // scores against the previous chunk's key tiles m >= w
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        xp[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m >= w) {
+          const f16x8 kv = g < 2 ? *reinterpret_cast<const f16x8*>(&S.kh[prev][16 * m + r16][8 * g]) : zero8;
+          xp[m] = mfma(kv, qv, xp[m]);
+        }
+      }
+      // key k (relative to the chunk start) is in the window of query pos
+      // when pos - window < k <= pos and the key exists (t0 + k >= 0)
+      const int lo = pos - p.window;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kc = 16 * m + 4 * g + i, kp = kc - C;
+          const bool okc = m <= w && kc <= pos && kc > lo;
+          const bool okp = m >= w && kp > lo && t0 + kp >= 0;
+          xc[m][i] = okc ? p.swa_scale * xc[m][i] : -INFINITY;
+          xp[m][i] = okp ? p.swa_scale * xp[m][i] : -INFINITY;
+          mx = fmaxf(mx, fmaxf(xc[m][i], xp[m][i]));
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float den = 0.f;
+      uint2 ch[4], cl[4], phh[4], pll[4];  // fp16 hi / lo weights: chunk tiles, previous tiles
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float ec[4], ep[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ec[i] = xc[m][i] == -INFINITY ? 0.f : __expf(xc[m][i] - mx);
+          ep[i] = xp[m][i] == -INFINITY ? 0.f : __expf(xp[m][i] - mx);
+          den += ec[i] + ep[i];
+        }
+        split2(ec[0], ec[1], ch[m].x, cl[m].x);
+        split2(ec[2], ec[3], ch[m].y, cl[m].y);
+        split2(ep[0], ep[1], phh[m].x, pll[m].x);
+        split2(ep[2], ep[3], phh[m].y, pll[m].y);
+      }
+      den += __shfl_xor(den, 16, 64);
+      den += __shfl_xor(den, 32, 64);
+      f32x4 accs[NT];
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) accs[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // key blocks: previous chunk (0,1), (2,3); this chunk (0,1), (2,3)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const bool is_prev = blk < 2;
+        const int kb = blk & 1;
+        const bool live = is_prev ? 2 * kb + 1 >= w : 2 * kb <= w;
+        if (live) {
+          const uint2* hh = is_prev ? phh : ch;
+          const uint2* ll = is_prev ? pll : cl;
+          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(hh[2 * kb].x, hh[2 * kb].y, hh[2 * kb + 1].x, hh[2 * kb + 1].y));
+          const f16x8 pl = __builtin_bit_cast(f16x8, make_uint4(ll[2 * kb].x, ll[2 * kb].y, ll[2 * kb + 1].x, ll[2 * kb + 1].y));
+          const int b = is_prev ? prev : cur;
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            const int col = 16 * nn + r16;
+            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[b][col][vt_pos(col, 32 * kb + 4 * g)]);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[b][col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
+            const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            accs[nn] = mfma(va, ph, accs[nn]);
+            accs[nn] = mfma(va, pl, accs[nn]);
+          }
+        }
+      }
+      const float rs_ = __builtin_amdgcn_rcpf(den);
+      if (pos < n) {
+        float* yrow = p.y_swa + (bh * p.L + t0 + pos) * DV + 4 * g;
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn)
+          *reinterpret_cast<float4*>(yrow + 16 * nn) =
+              make_float4(accs[nn][0] * rs_, accs[nn][1] * rs_, accs[nn][2] * rs_, accs[nn][3] * rs_);
+      }
+    }
+
     // ---- state update with this chunk (registers only)
-    update_chunk<NT>(S.kt, S.vt, tacc, tz, ia, ib);
+    update_chunk<NT>(S.kt, S.vt[cur], tacc, tz, ia, ib);
     z0 += (float)n;
     post_max<NT>(S.wmax, tacc, tz);
     __syncthreads();  // every read of tt, t0 and the chunk buffers done; wmax complete
@@ -739,7 +848,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     }
     e = state_scale(S.wmax, down, up);
     publish_state<NT>(S.tt, tacc, tz, e, down);
-    if (tn < tok_end) store_chunk<NT>(S.kt, S.vt, S.qh, S.kh, pf);
+    if constexpr (SWA) cur ^= 1;  // the next chunk replaces the previous one
+    if (tn < tok_end) store_chunk<NT>(S.kt, S.vt[cur], S.qh, S.kh[cur], pf);
   }
 
   // ---- the last segment writes the final state
@@ -906,13 +1016,14 @@ size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
   return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
 }
 
-template <int NT>
-static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
+template <int NT, bool SWA>
+static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
   constexpr int DV = 16 * NT;
   Params p{};
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y;
   p.S_in = a.S_in; p.z_in = a.z_in; p.S_out = a.S_out; p.z_out = a.z_out;
   p.L = a.L;
+  p.y_swa = y_swa; p.window = window; p.swa_scale = scale;
   linattn_mfma_plan(a.B * a.H, a.L, DV, &p.nseg, &p.seg_chunks);
   const int BH = a.B * a.H;
   if (p.nseg > 1) {
@@ -927,16 +1038,26 @@ static hipError_t launch_nt(const LinattnArgs& a, hipStream_t s) {
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((linattn_mfma_kernel<NT>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((linattn_mfma_kernel<NT, SWA>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t s) {
   switch (a.dv) {
-    case 32: return launch_nt<2>(a, s);
-    case 64: return launch_nt<4>(a, s);
-    case 96: return launch_nt<6>(a, s);
-    case 128: return launch_nt<8>(a, s);
+    case 32: return launch_nt<2, false>(a, nullptr, 0, 0.f, s);
+    case 64: return launch_nt<4, false>(a, nullptr, 0, 0.f, s);
+    case 96: return launch_nt<6, false>(a, nullptr, 0, 0.f, s);
+    case 128: return launch_nt<8, false>(a, nullptr, 0, 0.f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+  switch (a.dv) {
+    case 32: return launch_nt<2, true>(a, y_swa, window, scale, s);
+    case 64: return launch_nt<4, true>(a, y_swa, window, scale, s);
+    case 96: return launch_nt<6, true>(a, y_swa, window, scale, s);
+    case 128: return launch_nt<8, true>(a, y_swa, window, scale, s);
   }
   return hipErrorInvalidValue;
 }

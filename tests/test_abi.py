@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 1
+    assert so.based_abi_version() == 2
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -130,3 +130,24 @@ def test_product_path_has_no_oracle_or_fallback():
             if fn.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), fn
+
+
+def test_layer_validation(so):
+    def f(**kw):
+        a = dict(q=P, k=2 * P, v=3 * P, y_lin=4 * P, y_swa=6 * P, S_in=None, z_in=None, S_out=None, z_out=None,
+                 B=1, H=1, L=100, dk=16, dv=64, window=64, scale=1.0, dt=1, ws=None, wsb=0)
+        a.update(kw)
+        return so.based_layer_fwd(a["q"], a["k"], a["v"], a["y_lin"], a["y_swa"], a["S_in"], a["z_in"], a["S_out"],
+                                  a["z_out"], a["B"], a["H"], a["L"], a["dk"], a["dv"], a["window"], a["scale"],
+                                  a["dt"], a["ws"], a["wsb"], None)
+    assert f(dt=3) == ERR["DTYPE"]
+    assert f(B=0) == ERR["SHAPE"]
+    assert f(dk=32) == ERR["UNSUPPORTED"]
+    assert f(dv=72) == ERR["UNSUPPORTED"]
+    assert f(window=0) == ERR["WINDOW"] and f(window=65) == ERR["WINDOW"]
+    assert f(y_swa=None) == ERR["NULL"]
+    assert f(S_in=8 * P) == ERR["NULL"]
+    assert f(y_swa=6 * P + 4) == ERR["ALIGN"]
+    assert f(y_swa=4 * P + 256) == ERR["ALIAS"]  # the two outputs overlap
+    assert f(y_lin=3 * P) == ERR["ALIAS"]        # output over v
+    assert f(L=4096, B=8, H=16) == ERR["WORKSPACE"]  # segmented sizes need a workspace
