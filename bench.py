@@ -5,9 +5,11 @@
 
 A step is one layer forward over the 360M-shaped workload (B=8, H=16,
 L=2048, d_k=16, d_v=64, bf16 q/k/v, fp32 outputs): the causal Taylor linear
-attention (based_linattn_fwd) plus the window-64 softmax attention
-(based_swa_fwd) on the same inputs.  ``value`` is sequence positions per
-second (B*L per step; every position covers all 16 heads).
+attention and the window-64 softmax attention on the same inputs, in one
+based_layer_fwd call (the state-only pass, the segment scan and the fused
+main pass).  ``value`` is sequence positions per second (B*L per step; every
+position covers all 16 heads).  The two attentions are also timed as
+separate calls (based_linattn_fwd, based_swa_fwd) for comparison.
 
 Inputs are resident in HBM before timing starts.  Eight copies of the input
 set are cycled so that successive steps do not find their inputs in the
@@ -58,8 +60,18 @@ def lin_flops(dv):
     return 4 * D_PHI * dv + 3 * D_PHI
 
 
+def swa_flops(dv, window=64, dqk=16):
+    """Window attention per (position, head): scores 2*W*d_qk, weighted sum 2*W*dv."""
+    return 2 * window * (dqk + dv)
+
+
 def swa_bytes(dv, es=2):
     return (2 * 16 + dv) * es + 4 * dv
+
+
+def layer_bytes(dv, es=2):
+    """Both attentions in one pass: q, k, v read once, y_lin and y_swa written."""
+    return (2 * 16 + dv) * es + 2 * 4 * dv
 
 
 def decode_bytes(dv=64, window=64, es=2):
@@ -72,16 +84,16 @@ def decode_bytes(dv=64, window=64, es=2):
 # Kernel sources each timed operation is built from (a profile taken on other
 # sources no longer describes the kernel).
 OP_SOURCES = {
-    "linattn": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
-    "swa": ["swa_mfma.hip", "launchers.h", "based_device.h"],
+    "layer": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
     "decode": ["decode.hip", "launchers.h", "based_device.h"],
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
-    "linattn": ["linattn_mfma_kernel", "seg_scan_kernel"],
-    "swa": ["swa_mfma_kernel"],
+    "layer": ["linattn_mfma_kernel<4, true>", "linattn_state_kernel<4>", "seg_scan_kernel"],
     "decode": ["decode_step_kernel"],
 }
+# the step's last launch of each call (marks the end of the timed step in a trace)
+STEP_KERNEL = "linattn_mfma_kernel<4, true>"
 COPY_BYTES = 512 << 20
 
 
@@ -144,8 +156,9 @@ class StreamTimer:
         return sum(s.elapsed_time(e) for s, e in p) / len(p)
 
 
-def bench_fwd(lal, cfg, steps, warmup, nbuf=8):
-    """Time `steps` layer forwards (linattn + swa); returns a dict."""
+def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
+    """Time `steps` layer forwards: one based_layer_fwd call per step, or
+    (fused=False) based_linattn_fwd then based_swa_fwd.  Returns a dict."""
     q, k, v = synth.fwd_inputs(cfg, 0)
     sets = []
     for i in range(nbuf):
@@ -158,6 +171,10 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8):
 
     def step(i, timer=None):
         qq, kk, vv = sets[i % nbuf]
+        if fused:
+            f = lambda: lal.layer_fwd(qq, kk, vv, cfg.window, y_lin=y_lin, y_swa=y_swa, workspace=ws)
+            f() if timer is None else timer.run("layer", f)
+            return
         f1 = lambda: lal.linattn_fwd(qq, kk, vv, y=y_lin, workspace=ws)
         f2 = lambda: lal.swa_fwd(qq, kk, vv, cfg.window, y=y_swa)
         if timer is None:
@@ -179,18 +196,21 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    tl, ts = timer.mean_ms("linattn"), timer.mean_ms("swa")
     th = B * H * L
     es = 2 if cfg.dtype == "bf16" else 4
-    lb, sb = lin_bytes(dv, es) * th, swa_bytes(dv, es) * th
-    return {
-        "workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
-        "dtype": cfg.dtype, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
-        "linattn_us": tl * 1e3, "swa_us": ts * 1e3,
-        "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9,
-        "linattn_alg_tflops": lin_flops(dv) * th / (tl * 1e-3) / 1e12,
-        "linattn_bytes": lb, "swa_bytes": sb, "linattn_flops": lin_flops(dv) * th,
-    }
+    out = {"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
+           "dtype": cfg.dtype, "fused": fused, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)}
+    if fused:
+        tl = timer.mean_ms("layer")
+        lb = layer_bytes(dv, es) * th
+        out.update({"layer_us": tl * 1e3, "layer_bytes": lb, "layer_hbm_gbs": lb / (tl * 1e-3) / 1e9,
+                    "layer_alg_tflops": (lin_flops(dv) + swa_flops(dv)) * th / (tl * 1e-3) / 1e12})
+    else:
+        tl, ts = timer.mean_ms("linattn"), timer.mean_ms("swa")
+        lb, sb = lin_bytes(dv, es) * th, swa_bytes(dv, es) * th
+        out.update({"linattn_us": tl * 1e3, "swa_us": ts * 1e3, "linattn_bytes": lb, "swa_bytes": sb,
+                    "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9})
+    return out
 
 
 def bench_decode(lal, cfg, warmup=5):
@@ -291,12 +311,12 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
     f_copy = sorted(everything[cname])[len(everything[cname]) // 2]
     w_copy = sorted(cw)[len(cw) // 2]
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    # the step workload runs first; its last dispatch is the calls-th window-attention launch
-    swa_ids = sorted(i for (i, n) in fetch_all if "swa_mfma_kernel" in n)
-    step_end = swa_ids[calls - 1]
-    windows = {"linattn": (0, step_end), "swa": (0, step_end), "decode": (step_end + 1, 1 << 60)}
+    # the step workload runs first; its last dispatch is the calls-th launch of the fused main pass
+    step_ids = sorted(i for (i, n) in fetch_all if STEP_KERNEL in n)
+    step_end = step_ids[calls - 1]
+    windows = {"layer": (0, step_end), "decode": (step_end + 1, 1 << 60)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    workloads = {"linattn": "based360m", "swa": "based360m", "decode": "decode (256 x 16 heads)"}
+    workloads = {"layer": "based360m", "decode": "decode (256 x 16 heads)"}
     for op, frags in OP_KERNELS.items():
         tot_f = tot_w = 0.0
         detail = {}
@@ -324,7 +344,7 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
 def summarize_stats(stats_dir, command, calls):
     """profiles/kernel_stats.md from a rocprofv3 --kernel-trace --stats run of
     this script: average duration of every kernel.  The step workload runs
-    first and ends with its `calls`-th window-attention launch; its
+    first and ends with its `calls`-th launch of the fused main pass; its
     dispatches are reported apart from the rest."""
     files = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
     rows = []
@@ -332,8 +352,8 @@ def summarize_stats(stats_dir, command, calls):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    swa_starts = [int(r["Start_Timestamp"]) for r in rows if "swa_mfma_kernel" in r["Kernel_Name"]]
-    step_end = swa_starts[calls - 1] if len(swa_starts) >= calls else -1
+    step_starts = [int(r["Start_Timestamp"]) for r in rows if STEP_KERNEL in r["Kernel_Name"]]
+    step_end = step_starts[calls - 1] if len(step_starts) >= calls else -1
     groups = {}
     for r in rows:
         name = r["Kernel_Name"].split("(")[0].replace("void ", "")
@@ -344,7 +364,8 @@ def summarize_stats(stats_dir, command, calls):
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", f"Command: `{command}`", "",
              "Rows marked *step* are the timed layer step (360M-shaped workload, B8 H16 L2048 d_v64 bf16);",
-             "the others are the 1.3B-shaped and 32k workloads, the decode loop and set-up kernels.", "",
+             "the others are the separate-call comparison, the 1.3B-shaped and 32k workloads, the decode",
+             "loop and set-up kernels.", "",
              "| kernel | grid (threads) | block | step | calls | avg us | min us | max us |",
              "|---|---|---|---|---|---|---|---|"]
     for (name, grid, blk, phase), d in groups.items():
@@ -389,10 +410,13 @@ def main():
     copy = copy_calibration()
     print(f"[bench] copy calibration: {copy['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
-    print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step, linattn {main_res['linattn_us']:.1f} us, "
-          f"swa {main_res['swa_us']:.1f} us", file=sys.stderr, flush=True)
-    extra, decode = [], None
+    print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
+          file=sys.stderr, flush=True)
+    extra, decode, separate = [], None, None
     if not args.no_extra:
+        separate = bench_fwd(lal, cfg, max(10, args.steps // 2), args.warmup, fused=False)
+        print(f"[bench] {cfg.name} separate calls: linattn {separate['linattn_us']:.1f} us, swa "
+              f"{separate['swa_us']:.1f} us", file=sys.stderr, flush=True)
         for name in ("based1p3b", "long32k"):
             r = bench_fwd(lal, synth.FWD_CONFIGS[name], max(10, args.steps // 2), args.warmup, nbuf=4)
             extra.append(r)
@@ -402,24 +426,23 @@ def main():
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(cfg)
 
-    # dominant kernel of the step: the one with the larger share of the time
-    dom = "linattn" if main_res["linattn_us"] >= main_res["swa_us"] else "swa"
-    achieved = main_res[f"{dom}_hbm_gbs"]
-    traffic = load_traffic(dom)
+    # the step is one operation (state-only pass + segment scan + fused main pass)
+    achieved = main_res["layer_hbm_gbs"]
     out = {
         "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q,k,v; no trained weights)",
-        "config": {"workload": "based360m layer fwd: linear attention + window-64 softmax attention",
+        "config": {"workload": "based360m layer fwd: linear attention + window-64 softmax attention, one fused pass",
                    "B": cfg.B, "H": cfg.H, "L": cfg.L, "d_k": 16, "d_v": cfg.dv, "window": cfg.window,
                    "inputs": "bf16", "outputs": "fp32"},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes": main_res[f"{dom}_bytes"],
-                     "mfma_alg_frac": main_res["linattn_alg_tflops"] / MFMA_BF16_PEAK_TFS},
-        "kernels": {k: main_res[k] for k in ("linattn_us", "swa_us", "linattn_hbm_gbs", "swa_hbm_gbs",
-                                              "linattn_alg_tflops")},
+        "roofline": {"kernel": "layer", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic("layer"),
+                     "alg_bytes": main_res["layer_bytes"],
+                     "mfma_alg_frac": main_res["layer_alg_tflops"] / MFMA_BF16_PEAK_TFS},
+        "kernels": {"layer_us": main_res["layer_us"], "layer_hbm_gbs": main_res["layer_hbm_gbs"],
+                    "layer_alg_tflops": main_res["layer_alg_tflops"]},
+        "separate_calls": separate,
         "copy_calibration": copy,
         "cpu_baseline": cpu,
         "other_workloads": extra,
