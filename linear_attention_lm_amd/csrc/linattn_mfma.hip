@@ -160,7 +160,7 @@ struct Params {
 // wavefront spread over all banks while 8 consecutive positions stay
 // contiguous for 16-byte reads.  With the sliding window (SWA) the row-major
 // k and v^T keep the previous chunk too (NB = 2 buffers).
-template <int NT, bool SWA>
+template <int NT, int SWA>
 struct Smem {
   static constexpr int DV = 16 * NT;
   static constexpr int NB = SWA ? 2 : 1;
@@ -364,6 +364,23 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
+// Maximum / sum over the four 16-lane rows of a wavefront (lanes l, l^16,
+// l^32, l^48), by row swaps in registers: v_permlane16_swap pairs rows 0-1
+// and 2-3, v_permlane32_swap the two halves.  Every lane applies the same
+// operand order, so all four get the same bits.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Largest magnitude of this wavefront's state entries, into wmax[w]: quad and
 // row reductions in DPP, then the four row results through scalar registers
 // (non-negative floats order like their bit patterns).
@@ -555,7 +572,9 @@ __device__ __forceinline__ void write_phi_state(const float* t0, const float* zf
 // allows it (d_v <= 64), one otherwise.
 template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
-template <int NT, bool SWA>
+// SWA: 0 = linear attention only; 1 = with the window attention, window 64;
+// 2 = with the window attention, any window.
+template <int NT, int SWA>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
@@ -616,6 +635,18 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 
   const f16x8 ones = ones8();
   const int pos = 16 * w + r16;  // the chunk position whose outputs this lane holds
+  // Diagonal tile masks (key 4g + i against query r16 of the same 16-tile),
+  // kept as floats so they stay in vector registers: a weight factor for the
+  // linear attention and additive 0 / -inf masks for the window's current and
+  // previous-chunk diagonal tiles (the window-64 case).
+  float dkeep[4], dcur[4], dprev[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool after = 4 * g + i > r16;
+    dkeep[i] = after ? 0.f : 1.f;
+    dcur[i] = after ? -INFINITY : 0.f;
+    dprev[i] = after ? 0.f : -INFINITY;
+  }
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
     const int n = min(C, tok_end - t0);
     __syncthreads();  // chunk inputs, published state, t0 visible
@@ -696,27 +727,30 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       }
     }
     {
-      uint2 xh[4], xl[4];
+      uint4 ah[2], al[2];  // fp16 hi / lo weights of key blocks (tiles 2kb, 2kb + 1)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ah[kb] = al[kb] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        xh[m] = make_uint2(0u, 0u);
-        xl[m] = make_uint2(0u, 0u);
         if (m <= w) {
           float a[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[i] = __builtin_fmaf(xc[m][i], __builtin_fmaf(xc[m][i], 0.5f, 1.f), 1.f);
-            if (m == w && 4 * g + i > r16) a[i] = 0.f;  // key after query
-          }
-          split2(a[0], a[1], xh[m].x, xl[m].x);
-          split2(a[2], a[3], xh[m].y, xl[m].y);
+          for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(xc[m][i], __builtin_fmaf(xc[m][i], 0.5f, 1.f), 1.f);
+          if (m == w)  // key after query
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] *= dkeep[i];
+          uint32_t h0, l0, h1, l1;
+          split2(a[0], a[1], h0, l0);
+          split2(a[2], a[3], h1, l1);
+          if (m & 1) { ah[m >> 1].z = h0; ah[m >> 1].w = h1; al[m >> 1].z = l0; al[m >> 1].w = l1; }
+          else { ah[m >> 1].x = h0; ah[m >> 1].y = h1; al[m >> 1].x = l0; al[m >> 1].y = l1; }
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= w) {
-          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(xh[2 * kb].x, xh[2 * kb].y, xh[2 * kb + 1].x, xh[2 * kb + 1].y));
-          const f16x8 pl = __builtin_bit_cast(f16x8, make_uint4(xl[2 * kb].x, xl[2 * kb].y, xl[2 * kb + 1].x, xl[2 * kb + 1].y));
+          const f16x8 ph = __builtin_bit_cast(f16x8, ah[kb]);
+          const f16x8 pl = __builtin_bit_cast(f16x8, al[kb]);
           accz = mfma(ones, ph, accz);
           accz = mfma(ones, pl, accz);
 #pragma unroll
@@ -763,42 +797,73 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           xp[m] = mfma(kv, qv, xp[m]);
         }
       }
-      // key k (relative to the chunk start) is in the window of query pos
-      // when pos - window < k <= pos and the key exists (t0 + k >= 0)
-      const int lo = pos - p.window;
+      // Scores in the base-2 domain, s = scale * log2(e) * x, so that the
+      // weights are exp2(s - max); keys outside the window get s = -inf and
+      // weight 0.  Key 4g + i of tile m lies rel = 16(m - w) + 4g + i - r16
+      // positions from the query in this chunk (rel - 64 in the previous
+      // one); it is in the window when -window < rel <= 0 and it exists.
+      // With the full window (64) only the two diagonal tiles are partial.
+      const float c2 = p.swa_scale * 1.4426950408889634f;
+      const bool have_prev = t0 > 0;
+      if constexpr (SWA == 1) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (m < w) xc[m] *= c2;
+          if (m == w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xc[m][i] = __builtin_fmaf(xc[m][i], c2, dcur[i]);
+          if (m > w) xp[m] = have_prev ? xp[m] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          if (m == w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xp[m][i] = have_prev ? __builtin_fmaf(xp[m][i], c2, dprev[i]) : -INFINITY;
+        }
+      } else {
+        const uint32_t W = (uint32_t)p.window;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rel = 16 * (m - w) + 4 * g + i - r16;
+            if (m <= w) xc[m][i] = (uint32_t)(-rel) < W ? c2 * xc[m][i] : -INFINITY;
+            if (m >= w) xp[m][i] = have_prev && (uint32_t)(C - rel) < W ? c2 * xp[m][i] : -INFINITY;
+          }
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kc = 16 * m + 4 * g + i, kp = kc - C;
-          const bool okc = m <= w && kc <= pos && kc > lo;
-          const bool okp = m >= w && kp > lo && t0 + kp >= 0;
-          xc[m][i] = okc ? p.swa_scale * xc[m][i] : -INFINITY;
-          xp[m][i] = okp ? p.swa_scale * xp[m][i] : -INFINITY;
-          mx = fmaxf(mx, fmaxf(xc[m][i], xp[m][i]));
-        }
+        if (m <= w) mx = fmaxf(mx, fmaxf(fmaxf(xc[m][0], xc[m][1]), fmaxf(xc[m][2], xc[m][3])));
+        if (m >= w) mx = fmaxf(mx, fmaxf(fmaxf(xp[m][0], xp[m][1]), fmaxf(xp[m][2], xp[m][3])));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       float den = 0.f;
-      uint2 ch[4], cl[4], phh[4], pll[4];  // fp16 hi / lo weights: chunk tiles, previous tiles
+      // fp16 hi / lo weights per key block: this chunk's blocks, the previous chunk's
+      uint4 ch[2], cl[2], qh_[2], ql_[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ch[kb] = cl[kb] = qh_[kb] = ql_[kb] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        float ec[4], ep[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ec[i] = xc[m][i] == -INFINITY ? 0.f : __expf(xc[m][i] - mx);
-          ep[i] = xp[m][i] == -INFINITY ? 0.f : __expf(xp[m][i] - mx);
-          den += ec[i] + ep[i];
+        for (int side = 0; side < 2; ++side) {  // 0: this chunk, 1: previous chunk
+          if (side == 0 ? m <= w : m >= w) {
+            const f32x4& x = side == 0 ? xc[m] : xp[m];
+            float e4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              e4[i] = __builtin_amdgcn_exp2f(x[i] - mx);
+              den += e4[i];
+            }
+            uint32_t h0, l0, h1, l1;
+            split2(e4[0], e4[1], h0, l0);
+            split2(e4[2], e4[3], h1, l1);
+            uint4& H = side == 0 ? ch[m >> 1] : qh_[m >> 1];
+            uint4& Lo = side == 0 ? cl[m >> 1] : ql_[m >> 1];
+            if (m & 1) { H.z = h0; H.w = h1; Lo.z = l0; Lo.w = l1; }
+            else { H.x = h0; H.y = h1; Lo.x = l0; Lo.y = l1; }
+          }
         }
-        split2(ec[0], ec[1], ch[m].x, cl[m].x);
-        split2(ec[2], ec[3], ch[m].y, cl[m].y);
-        split2(ep[0], ep[1], phh[m].x, pll[m].x);
-        split2(ep[2], ep[3], phh[m].y, pll[m].y);
       }
-      den += __shfl_xor(den, 16, 64);
-      den += __shfl_xor(den, 32, 64);
+      den = rows_sum(den);
       f32x4 accs[NT];
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) accs[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -809,10 +874,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
         const int kb = blk & 1;
         const bool live = is_prev ? 2 * kb + 1 >= w : 2 * kb <= w;
         if (live) {
-          const uint2* hh = is_prev ? phh : ch;
-          const uint2* ll = is_prev ? pll : cl;
-          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(hh[2 * kb].x, hh[2 * kb].y, hh[2 * kb + 1].x, hh[2 * kb + 1].y));
-          const f16x8 pl = __builtin_bit_cast(f16x8, make_uint4(ll[2 * kb].x, ll[2 * kb].y, ll[2 * kb + 1].x, ll[2 * kb + 1].y));
+          const f16x8 ph = __builtin_bit_cast(f16x8, is_prev ? qh_[kb] : ch[kb]);
+          const f16x8 pl = __builtin_bit_cast(f16x8, is_prev ? ql_[kb] : cl[kb]);
           const int b = is_prev ? prev : cur;
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
@@ -1016,7 +1079,7 @@ size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
   return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
 }
 
-template <int NT, bool SWA>
+template <int NT, int SWA>
 static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
   constexpr int DV = 16 * NT;
   Params p{};
@@ -1044,22 +1107,27 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
 
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t s) {
   switch (a.dv) {
-    case 32: return launch_nt<2, false>(a, nullptr, 0, 0.f, s);
-    case 64: return launch_nt<4, false>(a, nullptr, 0, 0.f, s);
-    case 96: return launch_nt<6, false>(a, nullptr, 0, 0.f, s);
-    case 128: return launch_nt<8, false>(a, nullptr, 0, 0.f, s);
+    case 32: return launch_nt<2, 0>(a, nullptr, 0, 0.f, s);
+    case 64: return launch_nt<4, 0>(a, nullptr, 0, 0.f, s);
+    case 96: return launch_nt<6, 0>(a, nullptr, 0, 0.f, s);
+    case 128: return launch_nt<8, 0>(a, nullptr, 0, 0.f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int SWA>
+static hipError_t launch_layer(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+  switch (a.dv) {
+    case 32: return launch_nt<2, SWA>(a, y_swa, window, scale, s);
+    case 64: return launch_nt<4, SWA>(a, y_swa, window, scale, s);
+    case 96: return launch_nt<6, SWA>(a, y_swa, window, scale, s);
+    case 128: return launch_nt<8, SWA>(a, y_swa, window, scale, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
-  switch (a.dv) {
-    case 32: return launch_nt<2, true>(a, y_swa, window, scale, s);
-    case 64: return launch_nt<4, true>(a, y_swa, window, scale, s);
-    case 96: return launch_nt<6, true>(a, y_swa, window, scale, s);
-    case 128: return launch_nt<8, true>(a, y_swa, window, scale, s);
-  }
-  return hipErrorInvalidValue;
+  return window >= C ? launch_layer<1>(a, y_swa, window, scale, s) : launch_layer<2>(a, y_swa, window, scale, s);
 }
 
 }  // namespace based
