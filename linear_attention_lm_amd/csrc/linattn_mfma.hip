@@ -601,6 +601,12 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
     zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
   }
+  // the segment's first chunk (and, with the window, the chunk before it)
+  // from HBM first, so that their latency overlaps the state set-up
+  const HeadRsrc rs = head_rsrc(p, bh, DV);
+  Prefetch<NT> pf, pp;
+  if (SWA && tok_begin > 0) load_chunk<NT>(rs, tok_begin - C, false, pp);
+  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
   f32x4 tacc[Own<NT>::PPW];
   init_state<NT>(src, Sin, tacc);
   for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
@@ -609,19 +615,15 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = (half_t)1.f;
   int ia[3], ib[3];
   slot_rows(ia, ib);
-  const HeadRsrc rs = head_rsrc(p, bh, DV);
-  Prefetch<NT> pf;
   if constexpr (SWA) {
     // the window of the segment's first chunk reaches into the chunk before
     if (tok_begin > 0) {
-      load_chunk<NT>(rs, tok_begin - C, false, pf);
-      store_chunk<NT>(S.kt, S.vt[1], nullptr, S.kh[1], pf);
+      store_chunk<NT>(S.kt, S.vt[1], nullptr, S.kh[1], pp);
     } else {
       for (int j = tid; j < C * QH / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.kh[1][0][0])[j] = 0u;
       for (int j = tid; j < DV * VT / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.vt[1][0][0])[j] = 0u;
     }
   }
-  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
   __syncthreads();
   f32x4 tz[3];  // denominator state of the owned feature tiles
   load_tz(S.zf, tz);
@@ -954,6 +956,11 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
   const size_t rec = (size_t)(NF + 1) * DV;
 
+  // the first two chunks from HBM first, overlapping the state set-up
+  const HeadRsrc rs = head_rsrc(p, bh, DV);
+  Prefetch<NT> pa, pb;
+  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, false, pa);
+  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, pb);
   const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
   f32x4 tacc[Own<NT>::PPW];
@@ -970,15 +977,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   int ia[3], ib[3];
   slot_rows(ia, ib);
 
-  const HeadRsrc rs = head_rsrc(p, bh, DV);
   const int col = tid % DV, part = tid / DV;
   float vs = 0.f;  // this thread's share of the column sums of v (constant row)
-  Prefetch<NT> pa, pb;
-  if (tok_begin < tok_end) {
-    load_chunk<NT>(rs, tok_begin, false, pa);
-    store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, pa);
-  }
-  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, pb);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, pa);
 
   // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare` receives t + 2C
   auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
