@@ -89,11 +89,11 @@ OP_SOURCES = {
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
-    "layer": ["linattn_mfma_kernel<4, true>", "linattn_state_kernel<4>", "seg_scan_kernel"],
+    "layer": ["linattn_mfma_kernel<4, 1>", "linattn_state_kernel<4>", "seg_scan_kernel"],
     "decode": ["decode_step_kernel"],
 }
 # the step's last launch of each call (marks the end of the timed step in a trace)
-STEP_KERNEL = "linattn_mfma_kernel<4, true>"
+STEP_KERNEL = "linattn_mfma_kernel<4, 1>"
 COPY_BYTES = 512 << 20
 
 

@@ -63,6 +63,10 @@ constexpr int VT = C + 8;     // fp16 v^T row stride
 constexpr int TT = NF + 8;    // fp16 state^T row stride
 constexpr int ONES = 16;      // k^T row holding 1.0 (second factor of linear features)
 constexpr int SCALE_TOP = 13; // the scaled fp16 state stays below 2^(SCALE_TOP + 1)
+// Up to this many segments per head the main pass sums the segment
+// increments before its segment itself; beyond, a scan pass writes each
+// segment's starting state.
+constexpr int MAX_SUM = 3;
 
 enum SlotType : uint8_t { LIN = 0, DIAG = 1, OFF = 2, HALF = 3 };
 
@@ -475,7 +479,8 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
 // ([NF+1][DV], row NF = constant), else from the caller's phi-layout S_in,
 // else zero.
 template <int NT>
-__device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
+__device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW],
+                                           int ncompact = 1) {
   constexpr int DV = 16 * NT;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -487,6 +492,22 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * m + 4 * g + i;
       tacc[j][i] = compact ? compact[(size_t)r * DV + c] : (Sin ? compact_from_phi(Sin, r, c, DV) : 0.f);
+    }
+  }
+  // further records (consecutive, (NF + 1) * DV floats apart; at most
+  // MAX_SUM - 1 of them) are added on, their loads all in flight together
+#pragma unroll
+  for (int k = 1; k < MAX_SUM; ++k) {
+    if (k < ncompact) {
+      const float* rc = compact + (size_t)k * (NF + 1) * DV;
+#pragma unroll
+      for (int j = 0; j < Own<NT>::PPW; ++j) {
+        int m, n;
+        pair_mn<NT>(w, j, m, n);
+        const int c = 16 * n + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tacc[j][i] += rc[(size_t)(16 * m + 4 * g + i) * DV + c];
+      }
     }
   }
 }
@@ -594,9 +615,16 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   const float* srcz = nullptr;
   const float* Sin = nullptr;
   const float* zin = nullptr;
-  if (p.nseg > 1) {
-    src = p.ws + (bh * p.nseg + seg) * rec;
-    srcz = p.wsz + (bh * p.nseg + seg) * (size_t)(NF + 1);
+  // Without the scan (nseg <= MAX_SUM + 1), segment s > 0 starts from the sum
+  // of records 1..s: record 1 holds S_in plus segment 0's increment, record
+  // j > 1 segment j-1's increment.
+  const bool scanned = p.nseg > MAX_SUM + 1;
+  int nsrc = 1;
+  if (p.nseg > 1 && (scanned || seg > 0)) {
+    const int first = scanned ? seg : 1;
+    nsrc = scanned ? 1 : seg;
+    src = p.ws + (bh * p.nseg + first) * rec;
+    srcz = p.wsz + (bh * p.nseg + first) * (size_t)(NF + 1);
   } else {
     Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
     zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
@@ -608,10 +636,29 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   if (SWA && tok_begin > 0) load_chunk<NT>(rs, tok_begin - C, false, pp);
   if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
   f32x4 tacc[Own<NT>::PPW];
-  init_state<NT>(src, Sin, tacc);
-  for (int c = tid; c < DV; c += NTHR) S.t0[c] = src ? src[(size_t)NF * DV + c] : (Sin ? Sin[c] : 0.f);
-  for (int r = tid; r < NF; r += NTHR) S.zf[r] = srcz ? srcz[r] : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
-  float z0 = srcz ? srcz[NF] : (zin ? zin[0] : 0.f);
+  init_state<NT>(src, Sin, tacc, nsrc);
+  for (int c = tid; c < DV; c += NTHR) {
+    float t = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < MAX_SUM; ++k2)
+      if (src && k2 < nsrc) t += src[(size_t)k2 * rec + (size_t)NF * DV + c];
+    S.t0[c] = src ? t : (Sin ? Sin[c] : 0.f);
+  }
+  for (int r = tid; r < NF; r += NTHR) {
+    float t = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < MAX_SUM; ++k2)
+      if (srcz && k2 < nsrc) t += srcz[(size_t)k2 * (NF + 1) + r];
+    S.zf[r] = srcz ? t : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
+  }
+  float z0 = 0.f;
+  if (srcz) {
+#pragma unroll
+    for (int k2 = 0; k2 < MAX_SUM; ++k2)
+      if (k2 < nsrc) z0 += srcz[(size_t)k2 * (NF + 1) + NF];
+  } else if (zin) {
+    z0 = zin[0];
+  }
   for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = (half_t)1.f;
   int ia[3], ib[3];
   slot_rows(ia, ib);
@@ -931,7 +978,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 // increment of the compact state (segment 0 starts from S_in, so its record
 // carries the initial state too).  Update only, so one barrier per chunk:
 // k^T / v^T are double-buffered in LDS and the inputs are prefetched into
-// registers two chunks ahead.
+// registers three chunks ahead.
 template <int NT>
 struct StateSmem {
   static constexpr int DV = 16 * NT;
@@ -956,11 +1003,12 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
   const size_t rec = (size_t)(NF + 1) * DV;
 
-  // the first two chunks from HBM first, overlapping the state set-up
+  // the first three chunks from HBM first, overlapping the state set-up
   const HeadRsrc rs = head_rsrc(p, bh, DV);
-  Prefetch<NT> pa, pb;
-  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, false, pa);
-  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, pb);
+  Prefetch<NT> p0, p1, p2, p3;
+  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, false, p0);
+  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, p1);
+  if (tok_begin + 2 * C < tok_end) load_chunk<NT>(rs, tok_begin + 2 * C, false, p2);
   const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
   f32x4 tacc[Own<NT>::PPW];
@@ -972,19 +1020,20 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   __syncthreads();
   f32x4 tz[3];
   load_tz(S.zf, tz);
-  if (seg == 0)  // record 0: the initial state of the whole sequence
+  if (seg == 0 && p.nseg > MAX_SUM + 1)  // record 0 (for the scan): the initial state of the sequence
     write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   int ia[3], ib[3];
   slot_rows(ia, ib);
 
   const int col = tid % DV, part = tid / DV;
   float vs = 0.f;  // this thread's share of the column sums of v (constant row)
-  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, pa);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, p0);
 
-  // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare` receives t + 2C
+  // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare`
+  // receives t + 3C: three chunks in flight from HBM while one is updated
   auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
     __syncthreads();
-    if (t + 2 * C < tok_end) load_chunk<NT>(rs, t + 2 * C, false, spare);
+    if (t + 3 * C < tok_end) load_chunk<NT>(rs, t + 3 * C, false, spare);
     if (part < PARTS) {
 #pragma unroll
       for (int j = 0; j < SPAN; j += 8) {
@@ -996,9 +1045,11 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
     update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
     if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], nullptr, nullptr, next);
   };
-  for (int t = tok_begin; t < tok_end; t += 2 * C) {
-    step(t, 0, pb, pa);
-    if (t + C < tok_end) step(t + C, 1, pa, pb);
+  for (int t = tok_begin; t < tok_end; t += 4 * C) {
+    step(t, 0, p1, p3);
+    if (t + C < tok_end) step(t + C, 1, p2, p0);
+    if (t + 2 * C < tok_end) step(t + 2 * C, 0, p3, p1);
+    if (t + 3 * C < tok_end) step(t + 3 * C, 1, p0, p2);
   }
   z0 += (float)(tok_end - tok_begin);
   __syncthreads();
@@ -1095,7 +1146,7 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
     p.wsz = p.ws + (size_t)BH * p.nseg * (NF + 1) * DV;
     hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    if (p.nseg > 2) {
+    if (p.nseg > MAX_SUM + 1) {
       const size_t total = (size_t)BH * ((size_t)(NF + 1) * DV + NF + 1);
       hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p.ws, p.wsz,
                          p.nseg, (NF + 1) * DV, BH);
