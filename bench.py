@@ -277,6 +277,11 @@ def _counter_rows(d):
     return rows
 
 
+def short_name(kernel):
+    """A rocprofv3 kernel name without its argument list."""
+    return kernel.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
 def summarize_pmc(fetch_dir, write_dir, calls, command):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE) into profiles/traffic_<op>.json: HBM bytes per call
@@ -327,13 +332,13 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
                 wv = write.get(name, [0.0])
                 med_f = sorted(vals)[len(vals) // 2] * f_scale
                 med_w = sorted(wv)[len(wv) // 2] * w_scale
-                detail[name.split("(")[0]] = {"fetch_bytes": med_f, "write_bytes": med_w, "dispatches": len(vals)}
+                detail[short_name(name)] = {"fetch_bytes": med_f, "write_bytes": med_w, "dispatches": len(vals)}
                 tot_f += med_f
                 tot_w += med_w
         if not detail:
             continue
         rec = {"op": op, "workload": workloads[op], "source_hash": source_hash(op), "command": command,
-               "copy_kernel": cname.split("(")[0], "copy_fetch_factor": f_scale, "copy_write_factor": w_scale,
+               "copy_kernel": short_name(cname), "copy_fetch_factor": f_scale, "copy_write_factor": w_scale,
                "bytes_per_call": tot_f + tot_w, "fetch_bytes_per_call": tot_f, "write_bytes_per_call": tot_w,
                "kernels": detail}
         with open(os.path.join(ROOT, "profiles", f"traffic_{op}.json"), "w") as fh:
@@ -356,7 +361,7 @@ def summarize_stats(stats_dir, command, calls):
     step_end = step_starts[calls - 1] if len(step_starts) >= calls else -1
     groups = {}
     for r in rows:
-        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        name = short_name(r["Kernel_Name"])
         grid = r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]
         blk = r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"]
         phase = "step" if ("based" in name and int(r["Start_Timestamp"]) <= step_end) else ""

@@ -10,26 +10,81 @@
 // The step streams the 273 x d_v fp32 state through once (read, update,
 // write back) and is bound by HBM bandwidth.  Layout of the work: one
 // workgroup per sequence (so the position counter can be advanced race-free),
-// one wavefront per head.  Inside a wavefront, lane (rg, cg) owns columns
-// 4cg..4cg+3 of every state row with row-group rg: a wavefront instruction
-// touches RG whole 16-byte-per-lane row segments, each row read and written
-// exactly once with 16-byte accesses.
+// one wavefront per head at a time (MAXW wavefronts stride over the heads).
+// phi(k) and phi(q) are formed once per head into LDS.  Inside a wavefront,
+// lane (rg, cg) owns columns 4cg..4cg+3 of the state rows rg + RG i: a
+// wavefront instruction touches RG whole rows with 16-byte-per-lane accesses,
+// each row is read and written exactly once, and rows stream in batches of NB
+// with the next batch's loads in flight (the compiler would otherwise wait
+// for each row's load before issuing the next, one row per round trip).  The
+// ring's value rows are read the same way, four columns per lane.
 #include "based_device.h"
 #include "launchers.h"
 
 namespace based {
 namespace {
 
-constexpr int MAXW = 16;  // wavefronts (heads in flight) per workgroup
+constexpr int MAXW = 8;  // wavefronts (heads in flight) per workgroup
+
+// Raw buffer resources (range-checked: loads past the end read 0, stores
+// past the end are dropped), so that a row's offset is a scalar operand and
+// the per-lane offset stays fixed: no per-row address registers.
+constexpr int RSRC_DW3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, RSRC_DW3);
+}
+__device__ __forceinline__ float4 bload_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// Non-temporal load (cache-policy bit NT): each state row is read once per
+// step, and the whole state (273 MB at 4,096 heads of d_v 64) does not fit
+// the caches, so its lines are not worth keeping.  Measured 4 % faster per
+// step than the default policy; non-temporal stores were slower.
+__device__ __forceinline__ float4 bload_stream(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+__device__ __forceinline__ void bstore_f4(float4 x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, x), r, voff,
+                                         soff, 0);
+}
+
+// Four consecutive elements as fp32 (one 8-byte bf16 / 16-byte fp32 load).
+__device__ __forceinline__ float4 bload4(const float*, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return bload_f4(r, voff, soff);
+}
+__device__ __forceinline__ float4 bload4(const bf16_t*, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  return make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
+                     __uint_as_float(t.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const bf16_t* p) {
+  const uint2 t = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
+                     __uint_as_float(t.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ float4 fma4(float a, float4 x, float4 acc) {
+  return make_float4(__builtin_fmaf(a, x.x, acc.x), __builtin_fmaf(a, x.y, acc.y), __builtin_fmaf(a, x.z, acc.z),
+                     __builtin_fmaf(a, x.w, acc.w));
+}
 
 template <typename T, int DV>
 __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ S,
     float* __restrict__ z, T* __restrict__ ring_k, T* __restrict__ ring_v, int32_t* __restrict__ pos,
     float* __restrict__ y_lin, float* __restrict__ y_swa, int H, int window, float scale) {
-  constexpr int CG = DV / 4;   // column groups of 4 floats
-  constexpr int RG = 64 / CG;  // row groups per wavefront
+  constexpr int CG = DV / 4;                     // lanes per state row (4 columns each)
+  constexpr int RG = 64 / CG;                    // rows per wavefront instruction
+  constexpr int NI = (DPHI + RG - 1) / RG;       // state rows per lane
+  constexpr int NB = 16;                         // state rows per load batch
+  constexpr int NBATCH = (NI + NB - 1) / NB;
+  constexpr int NR = (64 + RG - 1) / RG;         // ring rows per lane (window <= 64)
+  constexpr int RB = 8, NRB = (NR + RB - 1) / RB;  // ring rows per load batch
+  constexpr int NZ = (DPHI + 63) / 64;           // z rows per lane
+  constexpr int ES = sizeof(T);
   __shared__ float qk_s[MAXW][2][DK];
+  __shared__ float2 phi_s[MAXW][DPHI];  // (phi(k)_f, phi(q)_f) of the wavefront's head
   __shared__ float4 red_s[MAXW][64];
   __shared__ float p_s[MAXW][64];
   __shared__ int t_s;
@@ -41,50 +96,67 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
   const int t = t_s;
   const int cg = lane % CG, rg = lane / CG;
   const bool active = rg < RG;
+  const int slot = t % window;  // the ring slot of token t (it held token t - window)
+  // per-lane byte offsets: row rg, columns 4cg..4cg+3 (inactive lanes past the end)
+  const int voff_s = active ? (rg * DV + 4 * cg) * 4 : DPHI * DV * 4;
+  const int voff_r = active ? (rg * DV + 4 * cg) * ES : 64 * DV * ES;
 
   for (int h = wave; h < H; h += nw) {
     const size_t bh = (size_t)b * H + h;
-    float qr[DK], kr[DK];
+    const auto rS = rsrc(S + bh * DPHI * DV, DPHI * DV * 4);
+    const auto rZ = rsrc(z + bh * DPHI, DPHI * 4);
+    const auto rK = rsrc(ring_k + bh * (size_t)window * DK, window * DK * ES);
+    const auto rV = rsrc(ring_v + bh * (size_t)window * DV, window * DV * ES);
+
+    // ---- loads whose latency the set-up hides: q, k, this lane's four v
+    // columns, z rows lane + 64j, the ring's key rows (lane j: slot j).  The
+    // slot of token t is never used: token t takes its place.
+    float qr[DK], kr[DK], kk[DK];
     load_row<DK>(q + bh * DK, qr);
     load_row<DK>(k + bh * DK, kr);
+    const float4 vr = active ? load4(v + bh * DV + 4 * cg) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float zl[NZ];
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) zl[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rZ, lane * 4, 256 * j, 0));
+#pragma unroll
+    for (int d = 0; d < DK; d += 4) {
+      const float4 x = bload4((const T*)nullptr, rK, lane * DK * ES, d * ES);
+      kk[d] = x.x; kk[d + 1] = x.y; kk[d + 2] = x.z; kk[d + 3] = x.w;
+    }
+    // position held by slot `lane` (negative: never written)
+    const int held = t - ((t - lane) % window + window) % window;
+    const bool key_live = lane < window && held >= 0;
+    if (lane == slot) {
+#pragma unroll
+      for (int d = 0; d < DK; ++d) kk[d] = kr[d];
+    }
+    // scores of the window's keys (q and the key rows are dead after this)
+    float sc = -INFINITY;
+    if (key_live) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < DK; ++d) acc = __builtin_fmaf(qr[d], kk[d], acc);
+      sc = scale * acc;
+    }
+    // ring value rows rg + RG i in batches of RB: batch 0 now, the rest while summing
+    auto ring_issue = [&](int bt, float4 (&buf)[RB]) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) buf[i] = bload4((const T*)nullptr, rV, voff_r, RG * (bt * RB + i) * DV * ES);
+    };
+    float4 ra[RB], rb[RB];
+    ring_issue(0, ra);
+
+    // ---- features of k and q into LDS; z += phi(k), den = phi(q).z
     if (lane < DK) {
       qk_s[wave][0][lane] = to_f32(q[bh * DK + lane]);
       qk_s[wave][1][lane] = to_f32(k[bh * DK + lane]);
     }
     __builtin_amdgcn_wave_barrier();
-    float vr[4];
-    {
-      const T* vp = v + bh * DV + 4 * cg;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vr[j] = to_f32(vp[j]);
-    }
-
-    // ---- linear attention: stream the state rows through once
-    float* Sh = S + bh * DPHI * DV + 4 * cg;
-    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      auto row = [&](int f, float pk, float pq) {
-        float4 s = *reinterpret_cast<const float4*>(Sh + (size_t)f * DV);
-        s.x += pk * vr[0]; s.y += pk * vr[1]; s.z += pk * vr[2]; s.w += pk * vr[3];
-        *reinterpret_cast<float4*>(Sh + (size_t)f * DV) = s;
-        num.x += pq * s.x; num.y += pq * s.y; num.z += pq * s.z; num.w += pq * s.w;
-      };
-      for (int f = rg; f < 1 + DK; f += RG) {
-        const float pk = f == 0 ? 1.f : qk_s[wave][1][f - 1];
-        const float pq = f == 0 ? 1.f : qk_s[wave][0][f - 1];
-        row(f, pk, pq);
-      }
-      for (int a = rg; a < DK; a += RG) {
-        const float ka = qk_s[wave][1][a] * INV_SQRT2, qa = qk_s[wave][0][a] * INV_SQRT2;
-#pragma unroll
-        for (int bb = 0; bb < DK; ++bb) row(1 + DK + DK * a + bb, ka * kr[bb], qa * qr[bb]);
-      }
-    }
-    // denominator: z rows spread over all 64 lanes
     float den = 0.f;
-    {
-      float* zh = z + bh * DPHI;
-      for (int f = lane; f < DPHI; f += 64) {
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) {
+      const int f = lane + 64 * j;
+      if (f < DPHI) {
         float pk, pq;
         if (f == 0) {
           pk = pq = 1.f;
@@ -96,13 +168,94 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
           pk = qk_s[wave][1][a] * qk_s[wave][1][bb] * INV_SQRT2;
           pq = qk_s[wave][0][a] * qk_s[wave][0][bb] * INV_SQRT2;
         }
-        const float zn = zh[f] + pk;
-        zh[f] = zn;
+        phi_s[wave][f] = make_float2(pk, pq);
+        const float zn = zl[j] + pk;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zn), rZ, lane * 4, 256 * j, 0);
         den += pq * zn;
       }
     }
     den = wave_sum(den);
-    red_s[wave][lane] = make_float4(num.x, num.y, num.z, num.w);
+
+    // ---- window softmax attention over the ring
+    const float m = wave_max(sc);
+    const float pw = sc == -INFINITY ? 0.f : __expf(sc - m);
+    const float psum = wave_sum(pw);
+    p_s[wave][lane] = pw;
+    __builtin_amdgcn_wave_barrier();
+    {
+      float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      auto ring_acc = [&](int bt, const float4 (&buf)[RB]) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int ii = bt * RB + i, j = rg + RG * ii;
+          if (ii < NR && active && j < window) {
+            const float pj = p_s[wave][j];
+            // empty slots (weight 0) may hold anything
+            if (pj != 0.f) a4 = fma4(pj, j == slot ? vr : buf[i], a4);
+          }
+        }
+      };
+#pragma unroll 1
+      for (int bt = 0; bt < NRB; bt += 2) {
+        if (bt + 1 < NRB) ring_issue(bt + 1, rb);
+        ring_acc(bt, ra);
+        if (bt + 1 < NRB) {
+          if (bt + 2 < NRB) ring_issue(bt + 2, ra);
+          ring_acc(bt + 1, rb);
+        }
+      }
+      red_s[wave][lane] = a4;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (active && rg == 0) {
+      float4 acc = red_s[wave][lane];
+      for (int r = 1; r < RG; ++r) {
+        const float4 o = red_s[wave][r * CG + cg];
+        acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+      }
+      const float inv = 1.f / psum;
+      *reinterpret_cast<float4*>(y_swa + bh * DV + 4 * cg) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // token t enters the ring (its slot was not read above)
+    if (lane < DK) ring_k[(bh * window + slot) * DK + lane] = k[bh * DK + lane];
+    for (int c = lane; c < DV; c += 64) ring_v[(bh * window + slot) * DV + c] = v[bh * DV + c];
+
+    // ---- linear attention: stream the state rows rg + RG i through once, NB
+    // rows per batch with the next batch's loads in flight (rows past the end
+    // read 0 and are not written)
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+      float4 ba[NB], bb[NB];
+      auto issue = [&](int bt, float4 (&buf)[NB]) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) buf[i] = bload_stream(rS, voff_s, RG * (bt * NB + i) * DV * 4);
+      };
+      auto process = [&](int bt, const float4 (&buf)[NB]) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int f = rg + RG * (bt * NB + i);
+          if (active && f < DPHI) {
+            const float2 ph = phi_s[wave][f];
+            const float4 sn = fma4(ph.x, vr, buf[i]);
+            bstore_f4(sn, rS, voff_s, RG * (bt * NB + i) * DV * 4);
+            num = fma4(ph.y, sn, num);
+          }
+        }
+      };
+      issue(0, ba);
+#pragma unroll 1
+      for (int bt = 0; bt < NBATCH; bt += 2) {
+        if (bt + 1 < NBATCH) issue(bt + 1, bb);
+        process(bt, ba);
+        if (bt + 1 < NBATCH) {
+          if (bt + 2 < NBATCH) issue(bt + 2, ba);
+          process(bt + 1, bb);
+        }
+      }
+    }
+    red_s[wave][lane] = num;
     __builtin_amdgcn_wave_barrier();
     if (active && rg == 0) {
       float4 acc = red_s[wave][lane];
@@ -111,50 +264,9 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
         acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
       }
       const float inv = 1.f / den;
-      acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-      *reinterpret_cast<float4*>(y_lin + bh * DV + 4 * cg) = acc;
+      *reinterpret_cast<float4*>(y_lin + bh * DV + 4 * cg) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
-
-    // ---- window softmax attention over the ring (slot = position mod window)
-    const int slot = t % window;
-    T* rk = ring_k + bh * (size_t)window * DK;
-    T* rv = ring_v + bh * (size_t)window * DV;
-    float sc = -INFINITY;
-    if (lane < window) {
-      const int p = t - ((t - lane) % window + window) % window;  // position held by this slot
-      if (p >= 0) {
-        float kk[DK];
-        if (lane == slot) {
-#pragma unroll
-          for (int d = 0; d < DK; ++d) kk[d] = kr[d];
-        } else {
-#pragma unroll
-          for (int d = 0; d < DK; ++d) kk[d] = to_f32(rk[(size_t)lane * DK + d]);
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int d = 0; d < DK; ++d) acc += qr[d] * kk[d];
-        sc = scale * acc;
-      }
-    }
-    const float m = wave_max(sc);
-    const float p = (sc == -INFINITY) ? 0.f : __expf(sc - m);
-    const float psum = wave_sum(p);
-    p_s[wave][lane] = p;
-    __builtin_amdgcn_wave_barrier();
-    const float inv = 1.f / psum;
-    for (int c = lane; c < DV; c += 64) {
-      const float vcur = to_f32(v[bh * DV + c]);
-      float acc = 0.f;
-      for (int j = 0; j < window; ++j) {
-        const float vj = (j == slot) ? vcur : to_f32(rv[(size_t)j * DV + c]);
-        acc += p_s[wave][j] * vj;
-      }
-      y_swa[bh * DV + c] = acc * inv;
-    }
-    // the new token enters the ring after every slot was read
-    if (lane < DK) rk[(size_t)slot * DK + lane] = k[bh * DK + lane];
-    for (int c = lane; c < DV; c += 64) rv[(size_t)slot * DV + c] = v[bh * DV + c];
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
