@@ -34,11 +34,15 @@ Readings where the pages are silent (all listed in the design doc as well):
   denominator of row i is at least (i + 1)/2;
 * the window softmax uses scale * q.k with a caller-given scale (1.0 in the
   workloads), the exact exponential that the Taylor map approximates;
-* linear attention and window attention are two separate outputs.
+* linear attention and window attention are two separate outputs;
+* the backward is the exact derivative of these forwards with respect to
+  q, k and v (no initial state), as the training views imply.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, invariants, textbook special cases, SciPy's softmax and
-hand-derived fixtures in ``tests/golden/``.
+hand-derived fixtures in ``tests/golden/``; the gradients against central
+finite differences of the forwards, torch fp64 autograd through plain torch
+forwards, and the value-shift identity.
 """
 
 from __future__ import annotations
@@ -208,6 +212,86 @@ def swa(q, k, v, window: int = 64, scale: float = 1.0, weight: str = "exp"):
     else:
         raise ValueError(weight)
     return np.einsum("...lw,...lwd->...ld", p, vb) / p.sum(axis=-1)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Gradients of the two attentions  [TRAIN, training views: the layer is
+# trained through these forwards, so the backward is their exact derivative]
+# --------------------------------------------------------------------------
+def linattn_bwd(q, k, v, dy):
+    """Gradients of the normalised causal linear attention (no initial state)
+    with respect to q, k and v, for an upstream gradient dy of y.
+
+    Written from the quadratic definition (``linattn_quadratic``): with the
+    kernel matrix A_ij = 1 + x_ij + x_ij^2/2 (x = q_i.k_j, j <= i, else 0),
+    num = A V, den = A 1 and y = num / den, the chain rule gives, per row i,
+      g_i = dy_i / den_i             (through the numerator)
+      h_i = -(dy_i . y_i) / den_i    (through the denominator)
+      dA_ij = g_i . v_j + h_i        (j <= i)
+      dV = A^T G,  dX = dA * (1 + X)  (the kernel's derivative in x),
+      dQ = dX K,   dK = dX^T Q.
+    Returns (dq, dk, dv) as fp64 arrays shaped like q, k, v.
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    L = q.shape[-2]
+    mask = np.tril(np.ones((L, L)))
+    X = q @ np.swapaxes(k, -1, -2)
+    A = taylor_kernel(X) * mask
+    den = A.sum(axis=-1)
+    y = (A @ v) / den[..., None]
+    g = dy / den[..., None]
+    h = -(dy * y).sum(axis=-1) / den
+    dA = (g @ np.swapaxes(v, -1, -2) + h[..., None]) * mask
+    dX = dA * (1.0 + X)
+    dq = dX @ k
+    dk = np.swapaxes(dX, -1, -2) @ q
+    dv = np.swapaxes(A, -1, -2) @ g
+    return dq, dk, dv
+
+
+def swa_bwd(q, k, v, dy, window: int = 64, scale: float = 1.0):
+    """Gradients of the sliding-window softmax attention (``swa``, exact
+    exponential weights) with respect to q, k and v.
+
+    Per row i over its band of keys j (max(0, i - window + 1) <= j <= i):
+    p_ij = softmax_j(s_ij) with s_ij = scale * q_i.k_j, y_i = sum_j p_ij v_j;
+      dP_ij = dy_i . v_j,  D_i = sum_j p_ij dP_ij (= dy_i . y_i),
+      dS_ij = p_ij (dP_ij - D_i)   (softmax Jacobian),
+      dq_i = scale * sum_j dS_ij k_j,
+      dk_j = scale * sum_i dS_ij q_i,  dv_j = sum_i p_ij dy_i  (sums over the
+      rows whose band holds j).
+    Returns (dq, dk, dv) as fp64 arrays shaped like q, k, v.
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    L = q.shape[-2]
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    idx = np.arange(L)[:, None] - (window - 1) + np.arange(window)[None, :]  # (L, W)
+    valid = idx >= 0
+    idxc = np.where(valid, idx, 0)
+    kb = k[..., idxc, :]
+    vb = v[..., idxc, :]
+    s = scale * np.einsum("...ld,...lwd->...lw", q, kb)
+    s = np.where(valid, s, -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p = p / p.sum(axis=-1, keepdims=True)
+    dP = np.einsum("...ld,...lwd->...lw", dy, vb)
+    D = (p * dP).sum(axis=-1, keepdims=True)
+    dS = np.where(valid, p * (dP - D), 0.0)
+    dq = scale * np.einsum("...lw,...lwd->...ld", dS, kb)
+    # scatter the band back onto key positions
+    lead = q.shape[:-2]
+    dk = np.zeros(lead + k.shape[-2:])
+    dv = np.zeros(lead + v.shape[-2:])
+    contrib_k = scale * dS[..., None] * q[..., :, None, :]  # [..., L, W, d]
+    contrib_v = np.where(valid[..., None], p[..., None] * dy[..., :, None, :], 0.0)
+    for w in range(window):
+        rows = np.nonzero(valid[:, w])[0]
+        if rows.size == 0:
+            continue
+        dk[..., idx[rows, w], :] += contrib_k[..., rows, w, :]
+        dv[..., idx[rows, w], :] += contrib_v[..., rows, w, :]
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

@@ -262,3 +262,98 @@ def test_decode_from_empty_context():
         yl, ys = st.step(q[..., s, :], k[..., s, :], v[..., s, :])
         np.testing.assert_allclose(yl, yq[..., s, :], rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(ys, _swa_bruteforce(q, k, v, 64, 1.0)[..., s, :], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ gradients
+def _fd_grads(loss, arrays, eps=1e-6):
+    """Central finite differences of a scalar loss, element by element."""
+    out = []
+    for arr in arrays:
+        g = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = arr[i]
+            arr[i] = old + eps
+            lp = loss()
+            arr[i] = old - eps
+            lm = loss()
+            arr[i] = old
+            g[i] = (lp - lm) / (2 * eps)
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("L,dv", [(1, 3), (6, 4), (9, 2)])
+def test_linattn_bwd_finite_differences(L, dv):
+    """Gradients against central differences of the Taylor-kernel forward
+    (the taylor form of the quadratic definition, itself pinned above)."""
+    q, k, v, dy = rand(2, L, 16, scale=0.3), rand(2, L, 16, scale=0.3), rand(2, L, dv), rand(2, L, dv)
+    loss = lambda: float((O.linattn_quadratic(q, k, v, "taylor")[0] * dy).sum())
+    fd = _fd_grads(loss, [q, k, v])
+    for got, want in zip(O.linattn_bwd(q, k, v, dy), fd):
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("L,window,scale", [(7, 3, 0.7), (5, 1, 1.0), (6, 64, 1.3)])
+def test_swa_bwd_finite_differences(L, window, scale):
+    q, k, v, dy = rand(2, L, 16, scale=0.5), rand(2, L, 16, scale=0.5), rand(2, L, 5), rand(2, L, 5)
+    loss = lambda: float((O.swa(q, k, v, window, scale) * dy).sum())
+    fd = _fd_grads(loss, [q, k, v])
+    for got, want in zip(O.swa_bwd(q, k, v, dy, window, scale), fd):
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+def test_bwd_against_torch_autograd():
+    """torch fp64 autograd through plain torch forwards (the masked Taylor
+    kernel with a row normalisation; torch's own softmax under a band mask)."""
+    torch = pytest.importorskip("torch")
+    L, dv, W, scale = 40, 8, 9, 0.8
+    q, k, v, dy = rand(L, 16, scale=0.3), rand(L, 16, scale=0.3), rand(L, dv), rand(L, dv)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    x = tq @ tk.T
+    w = torch.tril(1 + x + x * x / 2)
+    y = (w @ tv) / w.sum(-1, keepdim=True)
+    (y * torch.tensor(dy)).sum().backward()
+    for got, want in zip(O.linattn_bwd(q, k, v, dy), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    i, j = torch.arange(L)[:, None], torch.arange(L)[None, :]
+    band = (j <= i) & (j > i - W)
+    s = (scale * tq @ tk.T).masked_fill(~band, float("-inf"))
+    y = torch.softmax(s, dim=-1) @ tv
+    (y * torch.tensor(dy)).sum().backward()
+    for got, want in zip(O.swa_bwd(q, k, v, dy, W, scale), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_bwd_shift_identity():
+    """Both outputs are convex combinations of the values, so shifting every
+    v_j by c shifts every y_i by c: sum_j dv_j = sum_i dy_i exactly."""
+    L, dv = 50, 6
+    q, k, v, dy = rand(L, 16, scale=0.3), rand(L, 16, scale=0.3), rand(L, dv), rand(L, dv)
+    _, _, dv_lin = O.linattn_bwd(q, k, v, dy)
+    np.testing.assert_allclose(dv_lin.sum(0), dy.sum(0), rtol=1e-12, atol=1e-12)
+    _, _, dv_swa = O.swa_bwd(q, k, v, dy, 7, 1.1)
+    np.testing.assert_allclose(dv_swa.sum(0), dy.sum(0), rtol=1e-12, atol=1e-12)
+
+
+def test_swa_bwd_special_cases():
+    """Window 1: y = v, so dv = dy and q, k get nothing.  A zero upstream
+    gradient gives zero everywhere."""
+    L = 12
+    q, k, v, dy = rand(L, 16), rand(L, 16), rand(L, 4), rand(L, 4)
+    dq, dk, dv = O.swa_bwd(q, k, v, dy, 1, 1.0)
+    np.testing.assert_array_equal(dv, dy)
+    assert not dq.any() and not dk.any()
+    for g in O.swa_bwd(q, k, v, np.zeros_like(dy), 5, 1.0) + O.linattn_bwd(q * 0.2, k * 0.2, v, np.zeros_like(dy)):
+        assert not g.any()
+
+
+def test_linattn_bwd_first_position():
+    """Row 0 sees only itself: y_0 = v_0 whatever q_0, k_0 are, so the first
+    row's upstream gradient reaches only dv_0 (with L = 1, dq = dk = 0)."""
+    q, k, v, dy = rand(1, 16), rand(1, 16), rand(1, 5), rand(1, 5)
+    dq, dk, dv = O.linattn_bwd(q, k, v, dy)
+    np.testing.assert_allclose(dv, dy, rtol=1e-15)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
