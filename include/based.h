@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 2
+#define BASED_ABI_VERSION 3
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -137,6 +137,56 @@ int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
 int based_swa_fwd(const void* q, const void* k, const void* v, float* y,
                   int B, int H, int L, int d_qk, int d_v, int window, float scale,
                   int dtype, void* stream);
+
+/*
+ * Bytes of device workspace based_linattn_bwd needs for this shape (0 for
+ * invalid arguments; based_linattn_bwd reports those).
+ */
+size_t based_linattn_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int dtype);
+
+/*
+ * Causal Taylor linear attention, backward: gradients of based_linattn_fwd's
+ * y (zero initial state) with respect to q, k and v -- the derivative of the
+ * forward above, which the based/train README's training views train
+ * through.
+ *
+ *   q, k, v    as for based_linattn_fwd (d_k = 16)
+ *   y          [B,H,L,d_v] fp32 -- based_linattn_fwd's output for these q, k, v
+ *   dy         [B,H,L,d_v] fp32 -- gradient of the loss with respect to y
+ *   dq, dk     [B,H,L,16]  fp32 out;  dv [B,H,L,d_v] fp32 out
+ *   workspace: at least based_linattn_bwd_workspace_bytes(...) bytes of
+ *          device memory; contents on entry are ignored.
+ *
+ * With x_ij = q_i.k_j, K_ij = 1 + x_ij + x_ij^2/2, den_i = sum_{j<=i} K_ij,
+ * g_i = dy_i / den_i and h_i = -(dy_i . y_i) / den_i:
+ *   dq_i = sum_{j<=i} c_ij k_j,  dk_j = sum_{i>=j} c_ij q_i,
+ *   dv_j = sum_{i>=j} K_ij g_i,  c_ij = (g_i . v_j + h_i)(1 + x_ij).
+ * No output may overlap an input, another output or the workspace.
+ * Numerics: BASED_F32 is fp32 throughout; BASED_BF16 as for the forward.
+ */
+int based_linattn_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy,
+                      float* dq, float* dk, float* dv, int B, int H, int L, int d_k, int d_v, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sliding-window softmax attention, backward: gradients of based_swa_fwd's y
+ * with respect to q, k and v (the exact softmax Jacobian).
+ *
+ *   q, k       [B,H,L,d_qk] dtype, d_qk must be 16 (the layer's)
+ *   v          [B,H,L,d_v]  dtype, d_v in {16, 32, ..., 128}
+ *   y          [B,H,L,d_v]  fp32 -- based_swa_fwd's output for these inputs
+ *   dy         [B,H,L,d_v]  fp32 -- gradient of the loss with respect to y
+ *   dq, dk, dv fp32 out, shaped like q, k, v
+ *   window, scale: as for based_swa_fwd.
+ * With p_ij the window softmax weights, dP_ij = dy_i . v_j and D_i = dy_i . y_i:
+ *   dS_ij = p_ij (dP_ij - D_i); dq_i = scale sum_j dS_ij k_j;
+ *   dk_j = scale sum_i dS_ij q_i; dv_j = sum_i p_ij dy_i.
+ * Arithmetic is fp32 for both dtypes.  No output may overlap an input or
+ * another output.
+ */
+int based_swa_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy,
+                  float* dq, float* dk, float* dv, int B, int H, int L, int d_qk, int d_v,
+                  int window, float scale, int dtype, void* stream);
 
 /*
  * The Based layer's two attentions over the same q, k, v in one pass: the

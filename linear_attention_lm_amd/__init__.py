@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd", "layer_fwd",
+    "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd",
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
 
@@ -39,6 +40,9 @@ _SIGNATURES = {
     "based_layer_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
     "based_decode_prefill": (_i, [_vp] * 5 + [_i] * 7 + [_vp]),
     "based_decode_step": (_i, [_vp] * 10 + [_i] * 5 + [_f, _i, _vp]),
+    "based_linattn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "based_linattn_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
+    "based_swa_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
 }
 
 
@@ -188,6 +192,52 @@ def layer_fwd(q, k, v, window: int = 64, scale: float = 1.0, S_in=None, z_in=Non
     if return_state or S_out is not None:
         return y_lin, y_swa, S_out, z_out
     return y_lin, y_swa
+
+
+def _grads_out(q, k, v, dq, dk, dv):
+    mk = lambda t, like: torch.empty(like.shape, device=like.device, dtype=torch.float32) if t is None else t
+    return mk(dq, q), mk(dk, k), mk(dv, v)
+
+
+def _check_bwd_args(q, k, v, y, dy):
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    if y.shape != v.shape or dy.shape != v.shape or y.dtype != torch.float32 or dy.dtype != torch.float32:
+        raise ValueError("y and dy must be fp32 shaped like v")
+
+
+def linattn_bwd_workspace_bytes(B, H, L, dv, dtype=torch.bfloat16) -> int:
+    return _lib().based_linattn_bwd_workspace_bytes(B, H, L, DK, dv, BF16 if dtype == torch.bfloat16 else F32)
+
+
+def linattn_bwd(q, k, v, y, dy, *, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv), fp32, of :func:`linattn_fwd`'s output y (zero
+    initial state) for the upstream gradient dy (fp32, shaped like y)."""
+    _check_bwd_args(q, k, v, y, dy)
+    B, H, L, dk_ = q.shape
+    dvw = v.shape[-1]
+    _dev(q, k, v, y, dy, dq, dk, dv, workspace)
+    dq, dk, dv = _grads_out(q, k, v, dq, dk, dv)
+    dt = _dtype_code(q)
+    need = _lib().based_linattn_bwd_workspace_bytes(B, H, L, dk_, dvw, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().based_linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 B, H, L, dk_, dvw, dt, _ptr(workspace), wbytes, _stream()))
+    return dq, dk, dv
+
+
+def swa_bwd(q, k, v, y, dy, window: int = 64, scale: float = 1.0, *, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv), fp32, of :func:`swa_fwd`'s output y (d_qk = 16)
+    for the upstream gradient dy."""
+    _check_bwd_args(q, k, v, y, dy)
+    B, H, L, dqk = q.shape
+    _dev(q, k, v, y, dy, dq, dk, dv)
+    dq, dk, dv = _grads_out(q, k, v, dq, dk, dv)
+    _check(_lib().based_swa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), B, H,
+                             L, dqk, v.shape[-1], window, float(scale), _dtype_code(q), _stream()))
+    return dq, dk, dv
 
 
 @dataclass

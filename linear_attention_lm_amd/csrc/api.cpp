@@ -146,6 +146,73 @@ BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* 
   return status_of(based::launch_swa_valu(a, false, (hipStream_t)stream));
 }
 
+// Shared checks of the two backward entry points: inputs q, k, v (dtype), y
+// and dy (fp32), outputs gq, gk, gv (fp32) that overlap nothing else.
+static int check_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy, const float* gq,
+                     const float* gk, const float* gv, int B, int H, int L, int d_v, int dtype) {
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  if (!q || !k || !v || !y || !dy || !gq || !gk || !gv) return BASED_ERR_NULL;
+  const void* ptrs[] = {q, k, v, y, dy, gq, gk, gv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const Span in[] = {span(q, BH * L * BASED_DK * es), span(k, BH * L * BASED_DK * es), span(v, BH * L * d_v * es),
+                     span(y, BH * L * d_v * 4), span(dy, BH * L * d_v * 4)};
+  const Span out[] = {span(gq, BH * L * BASED_DK * 4), span(gk, BH * L * BASED_DK * 4), span(gv, BH * L * d_v * 4)};
+  for (int o = 0; o < 3; ++o) {
+    for (const Span& s : in)
+      if (overlap(out[o], s)) return BASED_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(out[o], out[o2])) return BASED_ERR_ALIAS;
+  }
+  return BASED_OK;
+}
+
+BASED_API size_t based_linattn_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int dtype) {
+  if ((dtype != BASED_F32 && dtype != BASED_BF16) || B < 1 || H < 1 || L < 1 || d_k != BASED_DK || !valid_dv(d_v))
+    return 0;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return 0;
+  return based::linattn_bwd_workspace(B, H, L, d_v, dtype == BASED_BF16);
+}
+
+BASED_API int based_linattn_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy,
+                                float* dq, float* dk, float* dv, int B, int H, int L, int d_k, int d_v, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if ((long long)B * H * ((L + 63) / 64) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (L == 0) return BASED_OK;
+  if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
+  const size_t need = based_linattn_bwd_workspace_bytes(B, H, L, d_k, d_v, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BASED_ERR_WORKSPACE;
+  if (workspace && need > 0) {
+    const Span ws = span(workspace, need);
+    const size_t BH = (size_t)B * H, es = elem_size(dtype);
+    const Span all[] = {span(q, BH * L * BASED_DK * es), span(k, BH * L * BASED_DK * es), span(v, BH * L * d_v * es),
+                        span(y, BH * L * d_v * 4), span(dy, BH * L * d_v * 4), span(dq, BH * L * BASED_DK * 4),
+                        span(dk, BH * L * BASED_DK * 4), span(dv, BH * L * d_v * 4)};
+    for (const Span& s : all)
+      if (overlap(ws, s)) return BASED_ERR_ALIAS;
+  }
+  based::LinattnBwdArgs a{q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, workspace, workspace_bytes};
+  return status_of(based::launch_linattn_bwd(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
+BASED_API int based_swa_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy, float* dq,
+                            float* dk, float* dv, int B, int H, int L, int d_qk, int d_v, int window, float scale,
+                            int dtype, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_qk != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
+  if ((long long)B * H * ((L + 63) / 64) > 0x7fffffffLL || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (L == 0) return BASED_OK;
+  if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
+  based::SwaBwdArgs a{q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, window, scale};
+  return status_of(based::launch_swa_bwd(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
 BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos, int B,
                                    int H, int L, int d_k, int d_v, int window, int dtype, void* stream) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;

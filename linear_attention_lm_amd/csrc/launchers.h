@@ -35,6 +35,25 @@ struct SwaArgs {
 hipError_t launch_swa_valu(const SwaArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_swa_mfma(const SwaArgs& a, hipStream_t stream);  // bf16 inputs
 
+// Backward of the window softmax (d_qk = 16): gradients gq, gk, gv (fp32) of
+// y with respect to q, k, v, given the forward output y and its gradient dy.
+struct SwaBwdArgs {
+  const void* q; const void* k; const void* v; const float* y; const float* dy;
+  float* gq; float* gk; float* gv;
+  int B, H, L, dv, window; float scale;
+};
+hipError_t launch_swa_bwd(const SwaBwdArgs& a, bool bf16, hipStream_t stream);
+
+// Backward of the linear attention (zero initial state), likewise.
+struct LinattnBwdArgs {
+  const void* q; const void* k; const void* v; const float* y; const float* dy;
+  float* gq; float* gk; float* gv;
+  int B, H, L, dv;
+  void* workspace; size_t workspace_bytes;
+};
+size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16);
+hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q; const void* k; const void* v;
   float* S; float* z; void* ring_k; void* ring_v; int32_t* pos;

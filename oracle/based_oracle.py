@@ -249,6 +249,33 @@ def linattn_bwd(q, k, v, dy):
     return dq, dk, dv
 
 
+def linattn_bwd_rows(q, k, v, dy, rows, chunk: int = 256):
+    """The gradients of ``linattn_bwd`` at selected positions only, for
+    sequences too long for the L x L matrices: dq_i, dk_i and dv_i for each
+    position i in ``rows``.  Same definition, evaluated by rows: the row
+    denominators and outputs come from the chunked forward (``linattn_chunked``,
+    equal to the quadratic form), then g and h for every row, then
+      dq_i = sum_{j<=i} (g_i.v_j + h_i)(1 + x_ij) k_j,
+      dk_j = sum_{i>=j} (g_i.v_j + h_i)(1 + x_ij) q_i,
+      dv_j = sum_{i>=j} K_ij g_i.
+    Shapes: q, k [L, d_k], v, dy [L, d_v] (one head).  Returns three arrays
+    [len(rows), d] in the order of ``rows``."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    y, den, _, _ = linattn_chunked(q, k, v, chunk)
+    g = dy / den[:, None]
+    h = -(dy * y).sum(axis=-1) / den
+    dq, dk, dv = [], [], []
+    for i in rows:
+        x = k[: i + 1] @ q[i]  # x_ij, j <= i
+        c = (v[: i + 1] @ g[i] + h[i]) * (1.0 + x)
+        dq.append(c @ k[: i + 1])
+        xs = q[i:] @ k[i]  # x_si, s >= i (key i)
+        cs = (g[i:] @ v[i] + h[i:]) * (1.0 + xs)
+        dk.append(cs @ q[i:])
+        dv.append(taylor_kernel(xs) @ g[i:])
+    return np.array(dq), np.array(dk), np.array(dv)
+
+
 def swa_bwd(q, k, v, dy, window: int = 64, scale: float = 1.0):
     """Gradients of the sliding-window softmax attention (``swa``, exact
     exponential weights) with respect to q, k and v.
@@ -283,14 +310,13 @@ def swa_bwd(q, k, v, dy, window: int = 64, scale: float = 1.0):
     lead = q.shape[:-2]
     dk = np.zeros(lead + k.shape[-2:])
     dv = np.zeros(lead + v.shape[-2:])
-    contrib_k = scale * dS[..., None] * q[..., :, None, :]  # [..., L, W, d]
-    contrib_v = np.where(valid[..., None], p[..., None] * dy[..., :, None, :], 0.0)
     for w in range(window):
         rows = np.nonzero(valid[:, w])[0]
         if rows.size == 0:
             continue
-        dk[..., idx[rows, w], :] += contrib_k[..., rows, w, :]
-        dv[..., idx[rows, w], :] += contrib_v[..., rows, w, :]
+        # key idx[rows, w] receives row i's term of band slot w
+        dk[..., idx[rows, w], :] += scale * dS[..., rows, w, None] * q[..., rows, :]
+        dv[..., idx[rows, w], :] += p[..., rows, w, None] * dy[..., rows, :]
     return dq, dk, dv
 
 

@@ -12,7 +12,9 @@ Recipe (the same for every workload):
 * q and k are multiplied by ``qk_std``, v by ``v_std``;
 * heavy tails: ``round(frac * rows)`` token rows of q, and independently of k,
   picked without replacement by ``randperm``, are multiplied by ``mult``;
-* finally everything is cast to the workload dtype with round-to-nearest-even.
+* finally everything is cast to the workload dtype with round-to-nearest-even;
+* upstream gradients dy for the backward: fp32 ``randn`` [B,H,L,dv] from a
+  generator seeded with ``seed + 1_000_003`` (independent of q, k, v).
 
 The workloads stand in for the activations of the 360M / 1.3B Based models
 that the pages train on the Pile (d_k = 16 feature dim, 16 heads, d_v 64/128),
@@ -25,7 +27,8 @@ import dataclasses
 
 import torch
 
-__all__ = ["FwdConfig", "DecodeConfig", "FWD_CONFIGS", "DECODE_CONFIG", "fwd_inputs", "decode_inputs"]
+__all__ = ["FwdConfig", "DecodeConfig", "FWD_CONFIGS", "DECODE_CONFIG", "fwd_inputs", "decode_inputs",
+           "upstream_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -127,3 +130,9 @@ def decode_inputs(cfg: DecodeConfig, seed: int = 0):
             out.append(torch.randn(cfg.B, cfg.H, d, generator=g) * cfg.std)
     steps = tuple(torch.stack(s).to(dt).contiguous() for s in (qs, ks, vs))
     return tuple(ctx), steps
+
+
+def upstream_grad(cfg: FwdConfig, seed: int = 0) -> torch.Tensor:
+    """dy [B,H,L,dv], fp32 N(0,1): the loss gradient fed to the backward."""
+    g = torch.Generator("cpu").manual_seed(seed + 1_000_003)
+    return torch.randn(cfg.B, cfg.H, cfg.L, cfg.dv, generator=g).contiguous()

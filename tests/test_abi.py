@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 2
+    assert so.based_abi_version() == 3
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -151,3 +151,48 @@ def test_layer_validation(so):
     assert f(y_swa=4 * P + 256) == ERR["ALIAS"]  # the two outputs overlap
     assert f(y_lin=3 * P) == ERR["ALIAS"]        # output over v
     assert f(L=4096, B=8, H=16) == ERR["WORKSPACE"]  # segmented sizes need a workspace
+
+
+def bwd_args(q=P, k=2 * P, v=3 * P, y=4 * P, dy=5 * P, dq=6 * P, dk=7 * P, dv=8 * P):
+    return [q, k, v, y, dy, dq, dk, dv]
+
+
+def test_linattn_bwd_validation(so):
+    B, H, L = 1, 2, 100
+    ws = 0x200000
+    need = so.based_linattn_bwd_workspace_bytes(B, H, L, 16, 64, 1)
+    assert need > 0
+    call = lambda args, dk=16, dv=64, dt=1, w=ws, wb=need, L=L: so.based_linattn_bwd(
+        *args, B, H, L, dk, dv, dt, w, wb, None)
+    big = 0x100000  # spacing so that the fake buffers do not overlap
+    ok = bwd_args(*(big * (i + 1) for i in range(8)))
+    assert call(ok, dt=2) == ERR["DTYPE"]
+    assert call(ok, dk=32) == ERR["UNSUPPORTED"]
+    assert call(ok, dv=40) == ERR["UNSUPPORTED"]
+    assert call(ok, L=0) == 0  # nothing to do
+    assert call(bwd_args(*(big * (i + 1) for i in range(7)), None)) == ERR["NULL"]
+    bad = list(ok)
+    bad[5] = big + 8
+    assert call(bad) == ERR["ALIGN"]
+    alias = list(ok)
+    alias[6] = alias[0]  # dk on top of q
+    assert call(alias) == ERR["ALIAS"]
+    assert call(ok, w=None) == ERR["WORKSPACE"]
+    assert call(ok, wb=need - 1) == ERR["WORKSPACE"]
+    assert call(ok, w=ok[3]) == ERR["ALIAS"]  # workspace on top of y
+    assert so.based_linattn_bwd_workspace_bytes(B, H, L, 16, 64, 7) == 0
+
+
+def test_swa_bwd_validation(so):
+    big = 0x100000
+    ok = bwd_args(*(big * (i + 1) for i in range(8)))
+    call = lambda args, dqk=16, dv=64, window=64, dt=1: so.based_swa_bwd(*args, 1, 2, 100, dqk, dv, window, 1.0,
+                                                                          dt, None)
+    assert call(ok, dt=5) == ERR["DTYPE"]
+    assert call(ok, dqk=32) == ERR["UNSUPPORTED"]
+    assert call(ok, window=0) == ERR["WINDOW"]
+    assert call(ok, window=65) == ERR["WINDOW"]
+    out_overlap = list(ok)
+    out_overlap[7] = out_overlap[5]  # dv on top of dq
+    assert call(out_overlap) == ERR["ALIAS"]
+    assert call(bwd_args(*(big * (i + 1) for i in range(4)), None, *(big * (i + 6) for i in range(3)))) == ERR["NULL"]

@@ -357,3 +357,13 @@ def test_linattn_bwd_first_position():
     dq, dk, dv = O.linattn_bwd(q, k, v, dy)
     np.testing.assert_allclose(dv, dy, rtol=1e-15)
     assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+
+
+def test_linattn_bwd_rows_matches_full():
+    """The row-sampled gradient (for long sequences) against the full one."""
+    L, dv = 300, 8
+    q, k, v, dy = rand(L, 16, scale=0.25), rand(L, 16, scale=0.25), rand(L, dv), rand(L, dv)
+    full = O.linattn_bwd(q, k, v, dy)
+    rows = [0, 5, 63, 64, 299]
+    for got, want in zip(O.linattn_bwd_rows(q, k, v, dy, rows, 64), full):
+        np.testing.assert_allclose(got, want[rows], rtol=1e-12, atol=1e-13)
