@@ -52,6 +52,9 @@ struct LinattnBwdArgs {
   void* workspace; size_t workspace_bytes;
 };
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16);
+// bf16 on the matrix cores for d_v in {32, 64, 96, 128} (slices of 32 columns)
+bool linattn_bwd_mfma_supported(int dv);
+hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t stream);
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t stream);
 
 struct DecodeArgs {

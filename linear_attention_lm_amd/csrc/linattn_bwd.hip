@@ -210,13 +210,14 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16) {
-  (void)dv;
-  (void)bf16;
-  return (size_t)B * H * L * 2 * sizeof(float);  // den and h per position
+  // per position: den and h (both forms), and dy . y (matrix-core form)
+  const size_t per = bf16 && linattn_bwd_mfma_supported(dv) ? 3 : 2;
+  return (size_t)B * H * L * per * sizeof(float);
 }
 
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
+  if (bf16 && linattn_bwd_mfma_supported(a.dv)) return launch_linattn_bwd_mfma(a, s);
   return bf16 ? launch_direct_dv<bf16_t>(a, s) : launch_direct_dv<float>(a, s);
 }
 

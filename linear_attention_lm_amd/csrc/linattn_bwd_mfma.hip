@@ -1,0 +1,724 @@
+// Causal Taylor linear attention, backward on the matrix cores (bf16 inputs,
+// d_v in {32, 64, 96, 128}).
+//
+// Gradients of the normalised forward y_i = num_i / den_i (blog post
+// "Базированная модель, часть 2": Taylor kernel 1 + x + x^2/2 as the feature
+// dot product phi(q).phi(k); based/train README: the training views train
+// through this forward).  With g_i = dy_i / den_i and h_i = -(dy_i . y_i) / den_i
+// the kernel entries' gradient is dK_ij = g_i . v_j + h_i, and in feature form
+//   dq_i = J_phi(q_i)^T [ S_i g_i + z_i h_i ]            (S, z: prefix states)
+//   dk_j = J_phi(k_j)^T [ R_j v_j + r_j ],  dv_j = R_j^T phi(k_j)
+// with the suffix states R_j = sum_{i>=j} phi(q_i) g_i^T, r_j = sum_{i>=j} phi(q_i) h_i.
+//
+// Features here are the 272 non-constant rows of phi without the 1/sqrt2
+// (tile 0: x_b; tile 1 + a: x_a x_b; b = 0..15 within a tile), so the
+// quadratic block of every state is symmetric in (a, b) and the Jacobian
+// contractions are lane-local: a lane holding u[(b, a)] for its four a and
+// every b adds u[(b, a)] x_b into the gradient of x_a.  The 1/2 of the
+// quadratic term sits on the side that is not differentiated.
+//
+// Passes (chunks of 64 positions; one workgroup of 4 wavefronts per (head,
+// slice of 32 value columns); dq and dk shares of the slices are added
+// atomically when there are several):
+//   dy_dot_y: D_i = dy_i . y_i.
+//   query pass, chunks in order: den_i (state z plus the in-chunk kernel
+//     sums), h_i and g_i; dq_i from u = S g + z h through the lane-local
+//     contraction, plus the in-chunk term sum_j dK_ij (1 + x_ij) k_j; then the
+//     state update S += phi(K)^T V, z += phi(K)^T 1.  Writes den and h.
+//   key pass, chunks in reverse: dk_j from u = R v + r, dv_j from
+//   R^T phi~(k_j) + sum_{i later} g_i, plus the in-chunk terms; then
+//   R += phi(Q)^T G, r += phi(Q)^T h.
+// Operands are fp16 (bf16 inputs convert exactly); g, h and the in-chunk
+// weights are split into fp16 hi + lo; the state copies read by the matrix
+// cores are fp16 scaled by a power of two; all sums are fp32.
+#include "based_device.h"
+#include "launchers.h"
+
+namespace based {
+namespace bwdm {
+
+typedef _Float16 half_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int C = 64;                // positions per chunk
+constexpr int NTHR = 256;            // 4 wavefronts
+constexpr int SW = 32;               // value columns per slice
+constexpr int NFT = 17;              // feature tiles: linear, then quadratic rows a = 0..15
+constexpr int NF = 16 * NFT;         // 272
+constexpr int NKS = (NF + 31) / 32;  // 9 steps of 32 features (the last half zero)
+constexpr int QH = 24;               // fp16 stride of q / k rows
+constexpr int XT = C + 8;            // fp16 stride of transposed chunk rows
+constexpr int RS = SW + 8;           // fp16 stride of slice rows
+constexpr int FS = 32 * NKS + 8;     // fp16 stride of the feature rows of a column-major state copy
+constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for w = 0)
+constexpr int SCALE_TOP = 13;
+
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int own_count(int w) { return w == 0 ? 5 : 4; }
+__device__ __forceinline__ int own_tile(int w, int j) { return j < 4 ? w + 4 * j : 16; }
+
+__device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ f16x8 ld8(const half_t* p) { return *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ f16x8 cat44(const half_t* a, const half_t* b) {
+  const uint2 x = *reinterpret_cast<const uint2*>(a), y = *reinterpret_cast<const uint2*>(b);
+  return __builtin_bit_cast(f16x8, make_uint4(x.x, x.y, y.x, y.y));
+}
+__device__ __forceinline__ f16x8 ones8() {
+  const uint32_t one2 = 0x3c003c00u;
+  return __builtin_bit_cast(f16x8, make_uint4(one2, one2, one2, one2));
+}
+
+__device__ __forceinline__ uint32_t h2_from_bf2(uint32_t w) {
+  const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return u32(__builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ uint4 h8_from_bf8(const uint4& x) {
+  return make_uint4(h2_from_bf2(x.x), h2_from_bf2(x.y), h2_from_bf2(x.z), h2_from_bf2(x.w));
+}
+
+// fp16 hi + lo of two fp32 values: hi = RNE(x), lo = RNE(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f16x2 h = __builtin_convertvector((f32x2{a, b}), f16x2);
+  hi = u32(h);
+  lo = u32(__builtin_convertvector((f32x2{a - (float)h[0], b - (float)h[1]}), f16x2));
+}
+// hi / lo operands of 8 weights: tile values t0 (K indices 0..3) and t1 (4..7)
+__device__ __forceinline__ void split8(const f32x4& t0, const f32x4& t1, f16x8& hi, f16x8& lo) {
+  uint32_t h[4], l[4];
+  split2(t0[0], t0[1], h[0], l[0]);
+  split2(t0[2], t0[3], h[1], l[1]);
+  split2(t1[0], t1[1], h[2], l[2]);
+  split2(t1[2], t1[3], h[3], l[3]);
+  hi = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(f16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// Sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float wave_max_abs(float m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  return m;
+}
+
+// Exponent e of the fp16 state copy (entries times 2^-e): none while the
+// largest magnitude M lies in [2^-4, 2^14), else M 2^-e lands in [2^13, 2^14).
+__device__ __forceinline__ int scale_exp(float M) {
+  if (!(M >= 0x1p-100f)) return 0;
+  if (M >= 0x1p-4f && M < 0x1p14f) return 0;
+  const int ex = (int)((__float_as_uint(M) >> 23) & 0xffu) - 127;
+  return ex - SCALE_TOP;
+}
+
+struct Params {
+  const bf16_t* q; const bf16_t* k; const bf16_t* v; const float* y; const float* dy;
+  float* Dy;            // dy . y per position
+  float* den; float* h; // per position, from the query pass
+  float* gq; float* gk; float* gv;
+  int L, dvf, nslice;
+};
+
+// ---------------------------------------------------------------- dy . y
+__global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __restrict__ y, float* __restrict__ D,
+                                size_t n, int dvf) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < dvf; c += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(dy + i * dvf + c);
+      const float4 b = *reinterpret_cast<const float4*>(y + i * dvf + c);
+      s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    }
+    D[i] = s;
+  }
+}
+
+__global__ void zero_kernel(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- chunk loads
+// Thread -> data: q (threads 0..127) or k (128..255) row (tid & 127) / 2, 8
+// coordinates; v and dy of the slice: row tid / 4, columns 8 (tid % 4) ..
+struct Pre {
+  uint4 qk;
+  uint4 v;
+  float4 dy0, dy1;
+  float aux;   // query pass: D of position tid (tid < 64); key pass: den of row tid / 4
+  float aux2;  // key pass: h of position tid (tid < 64)
+};
+
+__device__ __forceinline__ void load_common(const Params& p, size_t bh, int s, int t0, Pre& pf) {
+  const int tid = threadIdx.x, L = p.L;
+  {
+    const int r = (tid & 127) >> 1, half = tid & 1, t = t0 + r;
+    const bf16_t* src = (tid < 128 ? p.q : p.k) + ((size_t)bh * L + t) * DK + 8 * half;
+    pf.qk = t < L ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  {
+    const int r = tid >> 2, cq = tid & 3, t = t0 + r;
+    const size_t off = ((size_t)bh * L + t) * p.dvf + (size_t)s * SW + 8 * cq;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    pf.v = t < L ? *reinterpret_cast<const uint4*>(p.v + off) : make_uint4(0u, 0u, 0u, 0u);
+    pf.dy0 = t < L ? *reinterpret_cast<const float4*>(p.dy + off) : z4;
+    pf.dy1 = t < L ? *reinterpret_cast<const float4*>(p.dy + off + 4) : z4;
+  }
+}
+
+// ---------------------------------------------------------------- query pass
+struct QSmem {
+  alignas(16) half_t qh[C][QH];            // q rows
+  alignas(16) half_t kh[C][QH];            // k rows
+  alignas(16) half_t kt[DK][XT];           // k^T
+  alignas(16) half_t vt[SW][XT];           // v^T (slice)
+  alignas(16) half_t vh[C][RS];            // v rows (slice)
+  alignas(16) half_t gh[C][RS], gl[C][RS];  // g hi / lo (slice)
+  alignas(16) half_t st[NF][RS];           // state S, feature rows, scaled by 2^-e
+  alignas(16) float zs[NF];                // state z (fp32)
+  float dys[C];                            // D of the chunk's positions
+  float dens[C];                           // den of the chunk's positions
+  float wmax[4];
+};
+
+__device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
+  const int tid = threadIdx.x;
+  {
+    const int r = (tid & 127) >> 1, half = tid & 1;
+    const uint4 x = h8_from_bf8(pf.qk);
+    if (tid < 128) {
+      *reinterpret_cast<uint4*>(&S.qh[r][8 * half]) = x;
+    } else {
+      *reinterpret_cast<uint4*>(&S.kh[r][8 * half]) = x;
+      const f16x8 e = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S.kt[8 * half + i][r] = e[i];
+    }
+  }
+  {
+    const int r = tid >> 2, cq = tid & 3;
+    const uint4 x = h8_from_bf8(pf.v);
+    *reinterpret_cast<uint4*>(&S.vh[r][8 * cq]) = x;
+    const f16x8 e = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S.vt[8 * cq + i][r] = e[i];
+  }
+  if (tid < C) S.dys[tid] = pf.aux;
+}
+
+__global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
+  __shared__ QSmem S;
+  const size_t bh = blockIdx.x / p.nslice;
+  const int s = blockIdx.x % p.nslice;
+  const bool first = s == 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const int pos = 16 * w + r16;  // position (query) of the lane in transposed tiles
+  const int L = p.L;
+
+  for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.st[0][0])[e] = 0u;
+  for (int e = tid; e < NF; e += NTHR) S.zs[e] = 0.f;
+  f32x4 acc[MAXOWN][2], zacc[MAXOWN];
+#pragma unroll
+  for (int j = 0; j < MAXOWN; ++j) {
+    acc[j][0] = acc[j][1] = zacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float up = 1.f;
+  Pre pf;
+  load_common(p, bh, s, 0, pf);
+  pf.aux = tid < C && tid < L ? p.Dy[(size_t)bh * L + tid] : 0.f;
+  __syncthreads();
+  q_store(S, pf);
+  const f16x8 zero8 = {};
+  const f16x8 ones = ones8();
+
+  for (int t0 = 0; t0 < L; t0 += C) {
+    const int n = min(C, L - t0);
+    const float4 dy0 = pf.dy0, dy1 = pf.dy1;  // this chunk's dy (the prefetch below replaces pf)
+    __syncthreads();  // chunk inputs and the state copy visible
+    if (t0 + C < L) {
+      load_common(p, bh, s, t0 + C, pf);
+      pf.aux = tid < C && t0 + C + tid < L ? p.Dy[(size_t)bh * L + t0 + C + tid] : 0.f;
+    }
+
+    // ---- scores X^T (keys x queries) of the chunk's key tiles m <= w, the
+    // kernel weights K = 1 + x + x^2/2 below the diagonal, their row sums
+    const f16x8 qv = g < 2 ? ld8(&S.qh[pos][8 * g]) : zero8;
+    f32x4 xc[4];
+    float dpart = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      xc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m <= w) {
+        const f16x8 kv = g < 2 ? ld8(&S.kh[16 * m + r16][8 * g]) : zero8;
+        xc[m] = mfma(kv, qv, xc[m]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = xc[m][i];
+          if (m < w || 4 * g + i <= r16) dpart += 1.f + x + 0.5f * x * x;
+        }
+      }
+    }
+    // ---- the state's share of den: z_lin . q + q^T Z2 q / 2, this lane's four rows a
+    float qf[DK];
+    {
+      const f16x8 q0 = ld8(&S.qh[pos][0]), q1 = ld8(&S.qh[pos][8]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qf[i] = (float)q0[i];
+        qf[8 + i] = (float)q1[i];
+      }
+    }
+    {
+      const uint2 qa2 = *reinterpret_cast<const uint2*>(&S.qh[pos][4 * g]);
+      const f16x8 qa8 = __builtin_bit_cast(f16x8, make_uint4(qa2.x, qa2.y, 0u, 0u));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = 4 * g + i;
+        const float qa = (float)qa8[i];
+        float zq = 0.f;
+#pragma unroll
+        for (int b = 0; b < DK; b += 4) {
+          const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[DK + DK * a + b]);
+          zq += z4.x * qf[b] + z4.y * qf[b + 1] + z4.z * qf[b + 2] + z4.w * qf[b + 3];
+        }
+        dpart += qa * (S.zs[a] + 0.5f * zq);
+      }
+    }
+    const float den = rows_sum(dpart) + (float)t0;
+    const float hval = -S.dys[pos] / den;
+    if (g == 0) {
+      S.dens[pos] = den;
+      if (first && pos < n) {
+        p.den[(size_t)bh * L + t0 + pos] = den;
+        p.h[(size_t)bh * L + t0 + pos] = hval;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- g = dy / den of the wavefront's rows, fp16 hi / lo
+    {
+      const int row = 16 * w + (lane >> 2), cq = lane & 3;
+      const float rden = 1.f / S.dens[row];
+      uint32_t hi[4], lo[4];
+      split2(dy0.x * rden, dy0.y * rden, hi[0], lo[0]);
+      split2(dy0.z * rden, dy0.w * rden, hi[1], lo[1]);
+      split2(dy1.x * rden, dy1.y * rden, hi[2], lo[2]);
+      split2(dy1.z * rden, dy1.w * rden, hi[3], lo[3]);
+      *reinterpret_cast<uint4*>(&S.gh[row][8 * cq]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&S.gl[row][8 * cq]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- dq from the state: u^T = S^T-readout (features x this position),
+    // plus z h; lane-local contraction into dq[4g + i]
+    f32x4 dqa = {0.f, 0.f, 0.f, 0.f};
+    const f16x8 gbh = ld8(&S.gh[pos][8 * g]), gbl = ld8(&S.gl[pos][8 * g]);
+#pragma unroll
+    for (int m = 0; m < NFT; ++m) {
+      const f16x8 sa = ld8(&S.st[16 * m + r16][8 * g]);
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      u = mfma(sa, gbh, u);
+      u = mfma(sa, gbl, u);
+      u *= up;
+      if (first) {
+        const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[16 * m + 4 * g]);
+        u += f32x4{z4.x, z4.y, z4.z, z4.w} * hval;
+      }
+      if (m == 0) dqa += u;
+      else dqa += u * qf[m - 1];
+    }
+
+    // ---- in-chunk term: dK^T = V G^T (+ h), c = dK (1 + x) below the
+    // diagonal, dq += K^T c over key blocks (tiles 2kb, 2kb + 1)
+    {
+      f32x4 cw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        cw[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m <= w) {
+          const f16x8 va = ld8(&S.vh[16 * m + r16][8 * g]);
+          f32x4 da = {0.f, 0.f, 0.f, 0.f};
+          da = mfma(va, gbh, da);
+          da = mfma(va, gbl, da);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dk = da[i] + (first ? hval : 0.f);
+            cw[m][i] = (m < w || 4 * g + i <= r16) ? dk * (1.f + xc[m][i]) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb <= w) {
+          f16x8 bh8, bl8;
+          split8(cw[2 * kb], cw[2 * kb + 1], bh8, bl8);
+          const f16x8 ka = cat44(&S.kt[r16][32 * kb + 4 * g], &S.kt[r16][32 * kb + 16 + 4 * g]);
+          dqa = mfma(ka, bh8, dqa);
+          dqa = mfma(ka, bl8, dqa);
+        }
+      }
+    }
+    if (pos < n) {
+      float* dst = p.gq + ((size_t)bh * L + t0 + pos) * DK + 4 * g;
+      if (p.nslice == 1) {
+        *reinterpret_cast<float4*>(dst) = make_float4(dqa[0], dqa[1], dqa[2], dqa[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, dqa[i]);
+      }
+    }
+
+    // ---- state update with the chunk: S^T += V^T phi(K), z += phi(K)^T 1
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 kb = ld8(&S.kt[r16][32 * ks + 8 * g]);
+          const f16x8 fb = mt == 0 ? kb : ld8(&S.kt[mt - 1][32 * ks + 8 * g]) * kb;
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn)
+            acc[j][nn] = mfma(ld8(&S.vt[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+          zacc[j] = mfma(ones, fb, zacc[j]);
+        }
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j)
+      if (j < own_count(w))
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
+    mx = wave_max_abs(mx);
+    if (lane == 0) S.wmax[w] = mx;
+    __syncthreads();  // every read of the state copy and the chunk buffers done
+    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
+    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    up = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const f32x4 a = acc[j][nn] * down;
+          uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
+          uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
+          *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
+        }
+        if (g == 0) S.zs[16 * mt + r16] = zacc[j][0];
+      }
+    }
+    if (t0 + C < L) q_store(S, pf);
+  }
+}
+
+// ---------------------------------------------------------------- key pass
+struct KSmem {
+  alignas(16) half_t qh[C][QH];              // q rows
+  alignas(16) half_t qt[DK][XT];             // q^T
+  alignas(16) half_t kh[C][QH];              // k rows
+  alignas(16) half_t vh[C][RS];              // v rows (slice)
+  alignas(16) half_t gh[C][RS], gl[C][RS];    // g rows hi / lo (slice)
+  alignas(16) half_t gth[SW][XT], gtl[SW][XT];  // g^T hi / lo
+  alignas(16) half_t hh[XT], hl[XT];         // h over the chunk's positions, hi / lo
+  alignas(16) half_t rf[NF][RS];             // state R, feature rows, scaled by 2^-e
+  alignas(16) half_t rc[SW][FS];             // state R, column rows (features 272.. zero), scaled
+  alignas(16) float rs[NF];                  // state r (fp32)
+  alignas(16) float g0[SW];                  // sum of g over the later positions
+  alignas(16) float hs[C];                   // h of the chunk's positions
+  float wmax[4];
+};
+
+__device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
+  const int tid = threadIdx.x;
+  {
+    const int r = (tid & 127) >> 1, half = tid & 1;
+    const uint4 x = h8_from_bf8(pf.qk);
+    if (tid < 128) {
+      *reinterpret_cast<uint4*>(&S.qh[r][8 * half]) = x;
+      const f16x8 e = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S.qt[8 * half + i][r] = e[i];
+    } else {
+      *reinterpret_cast<uint4*>(&S.kh[r][8 * half]) = x;
+    }
+  }
+  {
+    const int r = tid >> 2, cq = tid & 3;
+    *reinterpret_cast<uint4*>(&S.vh[r][8 * cq]) = h8_from_bf8(pf.v);
+    const float rden = 1.f / pf.aux;
+    uint32_t hi[4], lo[4];
+    split2(pf.dy0.x * rden, pf.dy0.y * rden, hi[0], lo[0]);
+    split2(pf.dy0.z * rden, pf.dy0.w * rden, hi[1], lo[1]);
+    split2(pf.dy1.x * rden, pf.dy1.y * rden, hi[2], lo[2]);
+    split2(pf.dy1.z * rden, pf.dy1.w * rden, hi[3], lo[3]);
+    *reinterpret_cast<uint4*>(&S.gh[r][8 * cq]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(&S.gl[r][8 * cq]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    const f16x8 eh = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    const f16x8 el = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      S.gth[8 * cq + i][r] = eh[i];
+      S.gtl[8 * cq + i][r] = el[i];
+    }
+  }
+  if (tid < C) {
+    const float hv = pf.aux2;
+    S.hs[tid] = hv;
+    const _Float16 hhi = (_Float16)hv;
+    S.hh[tid] = hhi;
+    S.hl[tid] = (_Float16)(hv - (float)hhi);
+  }
+}
+
+__device__ __forceinline__ void k_load(const Params& p, size_t bh, int s, int t0, Pre& pf) {
+  const int tid = threadIdx.x, L = p.L;
+  load_common(p, bh, s, t0, pf);
+  const int r = t0 + (tid >> 2);
+  pf.aux = r < L ? p.den[(size_t)bh * L + r] : 1.f;
+  pf.aux2 = tid < C && t0 + tid < L ? p.h[(size_t)bh * L + t0 + tid] : 0.f;
+}
+
+__global__ __launch_bounds__(NTHR) void key_pass_kernel(Params p) {
+  __shared__ KSmem S;
+  const size_t bh = blockIdx.x / p.nslice;
+  const int s = blockIdx.x % p.nslice;
+  const bool first = s == 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const int kpos = 16 * w + r16;  // key of the lane in transposed tiles
+  const int L = p.L;
+
+  for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
+  for (int e = tid; e < SW * FS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rc[0][0])[e] = 0u;
+  for (int e = tid; e < NF; e += NTHR) S.rs[e] = 0.f;
+  if (tid < SW) S.g0[tid] = 0.f;
+  f32x4 acc[MAXOWN][2], racc[MAXOWN];
+#pragma unroll
+  for (int j = 0; j < MAXOWN; ++j) {
+    acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float up = 1.f;
+  const int last = ((L - 1) / C) * C;
+  Pre pf;
+  k_load(p, bh, s, last, pf);
+  __syncthreads();
+  k_store(S, pf);
+  const f16x8 zero8 = {};
+
+  for (int t0 = last; t0 >= 0; t0 -= C) {
+    const int n = min(C, L - t0);
+    __syncthreads();  // chunk inputs and the state copies visible
+    if (t0 > 0) k_load(p, bh, s, t0 - C, pf);
+
+    float kf[DK];
+    {
+      const f16x8 k0 = ld8(&S.kh[kpos][0]), k1 = ld8(&S.kh[kpos][8]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kf[i] = (float)k0[i];
+        kf[8 + i] = (float)k1[i];
+      }
+    }
+    // ---- dk from the state: u^T = R-readout with v_j (+ r), lane-local contraction
+    f32x4 dka = {0.f, 0.f, 0.f, 0.f};
+    const f16x8 vb = ld8(&S.vh[kpos][8 * g]);
+#pragma unroll
+    for (int m = 0; m < NFT; ++m) {
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      u = mfma(ld8(&S.rf[16 * m + r16][8 * g]), vb, u);
+      u *= up;
+      if (first) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&S.rs[16 * m + 4 * g]);
+        u += f32x4{r4.x, r4.y, r4.z, r4.w};
+      }
+      if (m == 0) dka += u;
+      else dka += u * kf[m - 1];
+    }
+    // ---- dv from the state: R^T phi~(k_j) with phi~ = [k_a, k_a k_b / 2], plus sum g
+    f32x4 dva[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      const f16x8 kb8 = ld8(&S.kh[kpos][8 * (g & 1)]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int mt = 2 * ks + (g >> 1);  // feature tile of this lane group's 8 features
+        f16x8 fb = zero8;
+        if (mt == 0) {
+          fb = kb8;
+        } else if (mt <= 16) {
+          const _Float16 ka = S.kh[kpos][mt - 1] * (_Float16)0.5f;
+          fb = kb8 * ka;
+        }
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) dva[nn] = mfma(ld8(&S.rc[16 * nn + r16][32 * ks + 8 * g]), fb, dva[nn]);
+      }
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const float4 g4 = *reinterpret_cast<const float4*>(&S.g0[16 * nn + 4 * g]);
+        dva[nn] = dva[nn] * up + f32x4{g4.x, g4.y, g4.z, g4.w};
+      }
+    }
+    // ---- in-chunk terms: queries i >= j in the query tiles m >= w
+    {
+      const f16x8 kv = g < 2 ? ld8(&S.kh[kpos][8 * g]) : zero8;
+      f32x4 cw[4], aw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        cw[m] = aw[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m >= w) {
+          const f16x8 qa = g < 2 ? ld8(&S.qh[16 * m + r16][8 * g]) : zero8;
+          f32x4 x = {0.f, 0.f, 0.f, 0.f};
+          x = mfma(qa, kv, x);  // [query 16m + 4g + i][key]
+          f32x4 da = {0.f, 0.f, 0.f, 0.f};
+          da = mfma(ld8(&S.gh[16 * m + r16][8 * g]), vb, da);
+          da = mfma(ld8(&S.gl[16 * m + r16][8 * g]), vb, da);
+          const float4 h4 = *reinterpret_cast<const float4*>(&S.hs[16 * m + 4 * g]);
+          const float hq[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool keep = m > w || 4 * g + i >= r16;
+            const float xx = x[i];
+            aw[m][i] = keep ? 1.f + xx + 0.5f * xx * xx : 0.f;
+            cw[m][i] = keep ? (da[i] + (first ? hq[i] : 0.f)) * (1.f + xx) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb + 1 >= w) {
+          f16x8 ch, cl, ah, al;
+          split8(cw[2 * kb], cw[2 * kb + 1], ch, cl);
+          split8(aw[2 * kb], aw[2 * kb + 1], ah, al);
+          const f16x8 qa = cat44(&S.qt[r16][32 * kb + 4 * g], &S.qt[r16][32 * kb + 16 + 4 * g]);
+          dka = mfma(qa, ch, dka);
+          dka = mfma(qa, cl, dka);
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) {
+            const int c = 16 * nn + r16;
+            const f16x8 gah = cat44(&S.gth[c][32 * kb + 4 * g], &S.gth[c][32 * kb + 16 + 4 * g]);
+            const f16x8 gal = cat44(&S.gtl[c][32 * kb + 4 * g], &S.gtl[c][32 * kb + 16 + 4 * g]);
+            dva[nn] = mfma(gah, ah, dva[nn]);
+            dva[nn] = mfma(gah, al, dva[nn]);
+            dva[nn] = mfma(gal, ah, dva[nn]);
+          }
+        }
+      }
+    }
+    if (kpos < n) {
+      float* dst = p.gk + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
+      if (p.nslice == 1) {
+        *reinterpret_cast<float4*>(dst) = make_float4(dka[0], dka[1], dka[2], dka[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, dka[i]);
+      }
+      float* dv = p.gv + ((size_t)bh * L + t0 + kpos) * p.dvf + (size_t)s * SW + 4 * g;
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn)
+        *reinterpret_cast<float4*>(dv + 16 * nn) = make_float4(dva[nn][0], dva[nn][1], dva[nn][2], dva[nn][3]);
+    }
+
+    // ---- state update with the chunk: R^T += G^T phi(Q), r += phi(Q)^T h
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
+          const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) {
+            acc[j][nn] = mfma(ld8(&S.gth[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+            acc[j][nn] = mfma(ld8(&S.gtl[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+          }
+          if (first) {
+            racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
+            racc[j] = mfma(ld8(&S.hl[32 * ks + 8 * g]), fb, racc[j]);
+          }
+        }
+      }
+    }
+    float gsum = 0.f;
+    if (tid < SW)
+      for (int r = 0; r < C; ++r) gsum += (float)S.gh[r][tid] + (float)S.gl[r][tid];
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j)
+      if (j < own_count(w))
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
+    mx = wave_max_abs(mx);
+    if (lane == 0) S.wmax[w] = mx;
+    __syncthreads();  // every read of the state copies and the chunk buffers done
+    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
+    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    up = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const f32x4 a = acc[j][nn] * down;
+          const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
+          const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
+          *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+          S.rc[16 * nn + 4 * g + 0][16 * mt + r16] = h01[0];
+          S.rc[16 * nn + 4 * g + 1][16 * mt + r16] = h01[1];
+          S.rc[16 * nn + 4 * g + 2][16 * mt + r16] = h23[0];
+          S.rc[16 * nn + 4 * g + 3][16 * mt + r16] = h23[1];
+        }
+        if (first && g == 0) S.rs[16 * mt + r16] = racc[j][0];
+      }
+    }
+    if (tid < SW) S.g0[tid] += gsum;
+    if (t0 > 0) k_store(S, pf);
+  }
+}
+
+}  // namespace bwdm
+
+bool linattn_bwd_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 || dv == 128; }
+
+hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
+  using namespace bwdm;
+  const size_t BH = (size_t)a.B * a.H, npos = BH * a.L;
+  Params p{};
+  p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y; p.dy = a.dy;
+  p.Dy = (float*)a.workspace;
+  p.den = p.Dy + npos;
+  p.h = p.den + npos;
+  p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
+  p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
+  const size_t zblocks = (npos * DK + 255) / 256, dblocks = (npos + 255) / 256;
+  const unsigned zb = (unsigned)(zblocks < 65536 ? zblocks : 65536);
+  if (p.nslice > 1) {
+    hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gq, npos * DK);
+    hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gk, npos * DK);
+  }
+  hipLaunchKernelGGL(dy_dot_y_kernel, dim3((unsigned)(dblocks < 65536 ? dblocks : 65536)), dim3(256), 0, s,
+                     a.dy, a.y, p.Dy, npos, a.dv);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(query_pass_kernel, dim3((unsigned)(BH * p.nslice)), dim3(NTHR), 0, s, p);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(key_pass_kernel, dim3((unsigned)(BH * p.nslice)), dim3(NTHR), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace based

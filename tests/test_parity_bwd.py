@@ -128,9 +128,13 @@ def test_bwd_long_sampled_rows(based):
             err = np.abs(got - r).max() / np.abs(r).max()
             report(f"lin {name} long32k head {h} sampled rows", err, TOL[q.dtype])
             assert err <= TOL[q.dtype], (name, err)
-    # the value-shift identity over the whole sequence: sum_j dv_j = sum_i dy_i
+    # the value-shift identity over the whole sequence, sum_j dv_j = sum_i dy_i,
+    # per head in the same infinity-norm relative measure
     s = grads[2].double().sum(dim=2).cpu().numpy()
-    np.testing.assert_allclose(s, dy.double().sum(dim=2).numpy(), rtol=1e-3, atol=1e-2)
+    want = dy.double().sum(dim=2).numpy()
+    err = float((np.abs(s - want).max(axis=-1) / np.abs(want).max(axis=-1)).max())
+    report("lin sum of dv vs sum of dy, long32k (every head)", err, TOL[q.dtype])
+    assert err <= TOL[q.dtype], err
     y = based.swa_fwd(qd, kd, vd)
     grads = based.swa_bwd(qd, kd, vd, y, dyd)
     torch.cuda.synchronize()
