@@ -43,6 +43,8 @@ struct SwaBwdArgs {
   int B, H, L, dv, window; float scale;
 };
 hipError_t launch_swa_bwd(const SwaBwdArgs& a, bool bf16, hipStream_t stream);
+bool swa_bwd_mfma_supported(int dv);  // bf16, d_v in {32, 64, 96, 128}
+hipError_t launch_swa_bwd_mfma(const SwaBwdArgs& a, hipStream_t stream);
 
 // Backward of the linear attention (zero initial state), likewise.
 struct LinattnBwdArgs {

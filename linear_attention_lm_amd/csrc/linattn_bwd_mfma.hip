@@ -131,16 +131,22 @@ struct Params {
 };
 
 // ---------------------------------------------------------------- dy . y
+// 16 lanes per position, four consecutive columns each (64 columns per pass),
+// so that a wavefront reads four whole rows per instruction.
 __global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __restrict__ y, float* __restrict__ D,
                                 size_t n, int dvf) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+  const int sub = threadIdx.x & 15;
+  const size_t stride = (size_t)gridDim.x * blockDim.x / 16;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; i < n; i += stride) {
     float s = 0.f;
-    for (int c = 0; c < dvf; c += 4) {
+    for (int c = 4 * sub; c < dvf; c += 64) {
       const float4 a = *reinterpret_cast<const float4*>(dy + i * dvf + c);
       const float4 b = *reinterpret_cast<const float4*>(y + i * dvf + c);
       s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
     }
-    D[i] = s;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+    if (sub == 0) D[i] = s;
   }
 }
 
@@ -706,7 +712,7 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   p.h = p.den + npos;
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
-  const size_t zblocks = (npos * DK + 255) / 256, dblocks = (npos + 255) / 256;
+  const size_t zblocks = (npos * DK + 255) / 256, dblocks = (npos * 16 + 255) / 256;
   const unsigned zb = (unsigned)(zblocks < 65536 ? zblocks : 65536);
   if (p.nslice > 1) {
     hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gq, npos * DK);

@@ -1,5 +1,6 @@
 // Sliding-window softmax attention, backward (fp32 vector arithmetic, any
-// input dtype; d_qk = 16).
+// input dtype; d_qk = 16): the form for fp32 inputs and for widths the
+// matrix-core kernel does not take.
 //
 // Gradients of y_i = sum_j p_ij v_j, p_ij = softmax_j(scale q_i.k_j) over the
 // causal band max(0, i - W + 1) <= j <= i (HazyResearch/based README intro:
@@ -255,6 +256,7 @@ hipError_t launch_dv(const SwaBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_swa_bwd(const SwaBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
+  if (bf16 && swa_bwd_mfma_supported(a.dv)) return launch_swa_bwd_mfma(a, s);
   return bf16 ? launch_dv<bf16_t>(a, s) : launch_dv<float>(a, s);
 }
 
