@@ -24,6 +24,10 @@ bool linattn_mfma_supported(int dv);
 size_t linattn_mfma_workspace(int B, int H, int L, int dv);
 void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
+// The state-only pass alone (zero initial state; bf16, d_v in {32, 64, 96, 128}):
+// compact segment increments at ws, as the main pass's records.
+hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
+                                        int seg_chunks, hipStream_t stream);
 // The same pass with the sliding-window softmax of the same q, k, v fused in
 // (d_qk = d_k = 16), written to y_swa.
 hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t stream);
@@ -56,6 +60,7 @@ struct LinattnBwdArgs {
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16);
 // bf16 on the matrix cores for d_v in {32, 64, 96, 128} (slices of 32 columns)
 bool linattn_bwd_mfma_supported(int dv);
+size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv);
 hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t stream);
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t stream);
 

@@ -210,9 +210,8 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16) {
-  // per position: den and h (both forms), and dy . y (matrix-core form)
-  const size_t per = bf16 && linattn_bwd_mfma_supported(dv) ? 3 : 2;
-  return (size_t)B * H * L * per * sizeof(float);
+  if (bf16 && linattn_bwd_mfma_supported(dv)) return linattn_bwd_mfma_workspace(B, H, L, dv);
+  return (size_t)B * H * L * 2 * sizeof(float);  // den and h per position
 }
 
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {

@@ -55,6 +55,51 @@ constexpr int RS = SW + 8;           // fp16 stride of slice rows
 constexpr int FS = 32 * NKS + 8;     // fp16 stride of the feature rows of a column-major state copy
 constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for w = 0)
 constexpr int SCALE_TOP = 13;
+constexpr int MAXSEG = 8;            // segments per head at most (records summed directly)
+constexpr int NFC = 160;             // compact slots of the forward's state records
+constexpr int RREC = NF * SW + NF + SW;  // floats of one suffix-state record (R, r, sum g)
+
+// Slot of the forward's compact records holding feature f of this layout
+// (f < 16: x_f; f = 16 + 16a + b: x_a x_b).  The compact layout: slot
+// r = 32 kb + 8 g + s holds pattern (kb, s) with both coordinates shifted by
+// 4g: kb = 0 gives x_a (s < 4) and x_a^2 (s >= 4) for a = s % 4; kb >= 1
+// gives x_a x_{a+d} for a = s % 4, d = 2 (kb - 1) + 1 + s / 4 (mod 16).  A
+// record holds sum_t [k_a | k_a^2 | k_a k_b] v_t in every slot.
+struct FeatureSlots {
+  int16_t slot[NF];
+};
+constexpr FeatureSlots make_feature_slots() {
+  FeatureSlots t{};
+  int sa[NFC] = {}, sb[NFC] = {}, lin[NFC] = {};
+  for (int r = 0; r < NFC; ++r) {
+    const int kb = r / 32, g = (r % 32) / 8, s2 = r % 8;
+    int A = s2 % 4, B = A;
+    if (kb > 0) B = A + 2 * (kb - 1) + 1 + s2 / 4;
+    sa[r] = (A + 4 * g) % 16;
+    sb[r] = (B + 4 * g) % 16;
+    lin[r] = kb == 0 && s2 < 4;
+  }
+  for (int f = 0; f < NF; ++f) {
+    t.slot[f] = -1;
+    for (int r = 0; r < NFC && t.slot[f] < 0; ++r) {
+      if (f < 16) {
+        if (lin[r] && sa[r] == f) t.slot[f] = (int16_t)r;
+      } else {
+        const int a = (f - 16) / 16, b = (f - 16) % 16;
+        if (!lin[r] && ((sa[r] == a && sb[r] == b) || (sa[r] == b && sb[r] == a))) t.slot[f] = (int16_t)r;
+      }
+    }
+  }
+  return t;
+}
+constexpr FeatureSlots kSlots = make_feature_slots();
+constexpr bool slots_ok() {
+  for (int f = 0; f < NF; ++f)
+    if (kSlots.slot[f] < 0) return false;
+  return true;
+}
+static_assert(slots_ok(), "every feature must map to a compact slot");
+__constant__ FeatureSlots c_slots = make_feature_slots();
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int own_count(int w) { return w == 0 ? 5 : 4; }
@@ -127,8 +172,27 @@ struct Params {
   float* Dy;            // dy . y per position
   float* den; float* h; // per position, from the query pass
   float* gq; float* gk; float* gv;
-  int L, dvf, nslice;
+  const float* frec;    // [BH][nseg][NFC + 1][dvf] forward records (record s + 1: segment s)
+  const float* frecz;   // [BH][nseg][NFC + 1]
+  float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
+  int L, dvf, nslice, nseg, seg_chunks;
 };
+
+// Workgroup -> (head, value slice, segment) and the segment's positions.
+struct Unit {
+  size_t bh;
+  int s, seg, t_begin, t_end;
+};
+__device__ __forceinline__ Unit unit_of(const Params& p) {
+  Unit u;
+  const int per_head = p.nslice * p.nseg;
+  u.bh = blockIdx.x / per_head;
+  u.s = (blockIdx.x % per_head) / p.nseg;
+  u.seg = blockIdx.x % p.nseg;
+  u.t_begin = u.seg * p.seg_chunks * C;
+  u.t_end = min(p.L, u.t_begin + p.seg_chunks * C);
+  return u;
+}
 
 // ---------------------------------------------------------------- dy . y
 // 16 lanes per position, four consecutive columns each (64 columns per pass),
@@ -225,8 +289,9 @@ __device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
 
 __global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
   __shared__ QSmem S;
-  const size_t bh = blockIdx.x / p.nslice;
-  const int s = blockIdx.x % p.nslice;
+  const Unit un = unit_of(p);
+  const size_t bh = un.bh;
+  const int s = un.s;
   const bool first = s == 0;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int pos = 16 * w + r16;  // position (query) of the lane in transposed tiles
@@ -240,19 +305,72 @@ __global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
     acc[j][0] = acc[j][1] = zacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float up = 1.f;
+  // largest state magnitude over the workgroup -> scale; state copy to LDS
+  auto publish = [&]() {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j)
+      if (j < own_count(w))
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
+    mx = wave_max_abs(mx);
+    if (lane == 0) S.wmax[w] = mx;
+    __syncthreads();  // every read of the state copy and the chunk buffers done
+    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
+    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    up = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const f32x4 a = acc[j][nn] * down;
+          const uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
+          const uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
+          *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
+        }
+        if (g == 0) S.zs[16 * mt + r16] = zacc[j][0];
+      }
+    }
+  };
+  // the state before the segment: the sum of the forward records of the
+  // earlier segments (slot values sum_t [k_a | k_a^2 | k_a k_b] v_t)
+  if (un.seg > 0) {
+    const size_t rows = NFC + 1;
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
+        float z = 0.f;
+        for (int r = 1; r <= un.seg; ++r) {
+          const size_t rec = (bh * p.nseg + r) * rows + slot;
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][nn][i] += p.frec[rec * p.dvf + s * SW + 16 * nn + 4 * g + i];
+          z += p.frecz[rec];
+        }
+        zacc[j] = f32x4{z, z, z, z};
+      }
+    }
+    publish();
+  }
   Pre pf;
-  load_common(p, bh, s, 0, pf);
-  pf.aux = tid < C && tid < L ? p.Dy[(size_t)bh * L + tid] : 0.f;
+  load_common(p, bh, s, un.t_begin, pf);
+  pf.aux = tid < C && un.t_begin + tid < L ? p.Dy[(size_t)bh * L + un.t_begin + tid] : 0.f;
   __syncthreads();
   q_store(S, pf);
   const f16x8 zero8 = {};
   const f16x8 ones = ones8();
 
-  for (int t0 = 0; t0 < L; t0 += C) {
-    const int n = min(C, L - t0);
+  for (int t0 = un.t_begin; t0 < un.t_end; t0 += C) {
+    const int n = min(C, un.t_end - t0);
     const float4 dy0 = pf.dy0, dy1 = pf.dy1;  // this chunk's dy (the prefetch below replaces pf)
     __syncthreads();  // chunk inputs and the state copy visible
-    if (t0 + C < L) {
+    if (t0 + C < un.t_end) {
       load_common(p, bh, s, t0 + C, pf);
       pf.aux = tid < C && t0 + C + tid < L ? p.Dy[(size_t)bh * L + t0 + C + tid] : 0.f;
     }
@@ -400,35 +518,8 @@ __global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
         }
       }
     }
-    float mx = 0.f;
-#pragma unroll
-    for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w))
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
-    mx = wave_max_abs(mx);
-    if (lane == 0) S.wmax[w] = mx;
-    __syncthreads();  // every read of the state copy and the chunk buffers done
-    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
-    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
-    up = __builtin_amdgcn_ldexpf(1.f, e);
-#pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
-        const int mt = own_tile(w, j);
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const f32x4 a = acc[j][nn] * down;
-          uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
-          uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
-          *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
-        }
-        if (g == 0) S.zs[16 * mt + r16] = zacc[j][0];
-      }
-    }
-    if (t0 + C < L) q_store(S, pf);
+    publish();
+    if (t0 + C < un.t_end) q_store(S, pf);
   }
 }
 
@@ -446,6 +537,7 @@ struct KSmem {
   alignas(16) float rs[NF];                  // state r (fp32)
   alignas(16) float g0[SW];                  // sum of g over the later positions
   alignas(16) float hs[C];                   // h of the chunk's positions
+  float gpart[8][SW];                        // column sums of g over 8-row groups
   float wmax[4];
 };
 
@@ -499,10 +591,110 @@ __device__ __forceinline__ void k_load(const Params& p, size_t bh, int s, int t0
   pf.aux2 = tid < C && t0 + tid < L ? p.h[(size_t)bh * L + t0 + tid] : 0.f;
 }
 
-__global__ __launch_bounds__(NTHR) void key_pass_kernel(Params p) {
+// Suffix-state increment of one segment (>= 1): R += phi(Q)^T G,
+// r += phi(Q)^T h and sum g over its positions; the key pass of segment s
+// starts from the sum of the increments of the segments after it.
+struct KIncSmem {
+  alignas(16) half_t qt[DK][XT];
+  alignas(16) half_t gth[SW][XT], gtl[SW][XT];
+  alignas(16) half_t hh[XT], hl[XT];
+  float gcol[SW];
+};
+
+__global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
+  __shared__ KIncSmem S;
+  const Unit un = unit_of(p);
+  if (un.seg == 0) return;
+  const size_t bh = un.bh;
+  const int s = un.s;
+  const bool first = s == 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  f32x4 acc[MAXOWN][2], racc[MAXOWN];
+#pragma unroll
+  for (int j = 0; j < MAXOWN; ++j) {
+    acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (tid < SW) S.gcol[tid] = 0.f;
+  Pre pf;
+  k_load(p, bh, s, un.t_begin, pf);
+  for (int t0 = un.t_begin; t0 < un.t_end; t0 += C) {
+    __syncthreads();  // the previous chunk's reads done
+    if (tid < 128) {
+      const int r = tid >> 1, half = tid & 1;
+      const f16x8 e = __builtin_bit_cast(f16x8, h8_from_bf8(pf.qk));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S.qt[8 * half + i][r] = e[i];
+    }
+    {
+      const int r = tid >> 2, cq = tid & 3;
+      const float rden = 1.f / pf.aux;
+      const float gv[8] = {pf.dy0.x * rden, pf.dy0.y * rden, pf.dy0.z * rden, pf.dy0.w * rden,
+                           pf.dy1.x * rden, pf.dy1.y * rden, pf.dy1.z * rden, pf.dy1.w * rden};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split2(gv[2 * e], gv[2 * e + 1], hi[e], lo[e]);
+      const f16x8 eh = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      const f16x8 el = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        S.gth[8 * cq + i][r] = eh[i];
+        S.gtl[8 * cq + i][r] = el[i];
+        gpart[i] += gv[i];
+      }
+    }
+    if (tid < C) {
+      const float hv = pf.aux2;
+      const _Float16 hhi = (_Float16)hv;
+      S.hh[tid] = hhi;
+      S.hl[tid] = (_Float16)(hv - (float)hhi);
+    }
+    __syncthreads();
+    if (t0 + C < un.t_end) k_load(p, bh, s, t0 + C, pf);
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
+          const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) {
+            acc[j][nn] = mfma(ld8(&S.gth[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+            acc[j][nn] = mfma(ld8(&S.gtl[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+          }
+          if (first) {
+            racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
+            racc[j] = mfma(ld8(&S.hl[32 * ks + 8 * g]), fb, racc[j]);
+          }
+        }
+      }
+    }
+  }
+  float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + un.seg) * (size_t)RREC;
+#pragma unroll
+  for (int j = 0; j < MAXOWN; ++j) {
+    if (j < own_count(w)) {
+      const int f = 16 * own_tile(w, j) + r16;
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn)
+        *reinterpret_cast<float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g) =
+            make_float4(acc[j][nn][0], acc[j][nn][1], acc[j][nn][2], acc[j][nn][3]);
+      if (first && g == 0) rec[(size_t)NF * SW + f] = racc[j][0];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) atomicAdd(&S.gcol[8 * (tid & 3) + i], gpart[i]);
+  __syncthreads();
+  if (tid < SW) rec[(size_t)NF * SW + NF + tid] = S.gcol[tid];
+}
+
+__global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   __shared__ KSmem S;
-  const size_t bh = blockIdx.x / p.nslice;
-  const int s = blockIdx.x % p.nslice;
+  const Unit un = unit_of(p);
+  const size_t bh = un.bh;
+  const int s = un.s;
   const bool first = s == 0;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int kpos = 16 * w + r16;  // key of the lane in transposed tiles
@@ -518,17 +710,74 @@ __global__ __launch_bounds__(NTHR) void key_pass_kernel(Params p) {
     acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float up = 1.f;
-  const int last = ((L - 1) / C) * C;
+  // largest state magnitude over the workgroup -> scale; both state copies to LDS
+  auto publish = [&]() {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j)
+      if (j < own_count(w))
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
+    mx = wave_max_abs(mx);
+    if (lane == 0) S.wmax[w] = mx;
+    __syncthreads();  // every read of the state copies and the chunk buffers done
+    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
+    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
+    up = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+    for (int j = 0; j < MAXOWN; ++j) {
+      if (j < own_count(w)) {
+        const int mt = own_tile(w, j);
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const f32x4 a = acc[j][nn] * down;
+          const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
+          const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
+          *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+          S.rc[16 * nn + 4 * g + 0][16 * mt + r16] = h01[0];
+          S.rc[16 * nn + 4 * g + 1][16 * mt + r16] = h01[1];
+          S.rc[16 * nn + 4 * g + 2][16 * mt + r16] = h23[0];
+          S.rc[16 * nn + 4 * g + 3][16 * mt + r16] = h23[1];
+        }
+        if (first && g == 0) S.rs[16 * mt + r16] = racc[j][0];
+      }
+    }
+  };
+  // the state after the segment: the sum of the increments of the later segments
+  if (un.seg < p.nseg - 1) {
+    float g0 = 0.f;
+    for (int r = un.seg + 1; r < p.nseg; ++r) {
+      const float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + r) * (size_t)RREC;
+#pragma unroll
+      for (int j = 0; j < MAXOWN; ++j) {
+        if (j < own_count(w)) {
+          const int f = 16 * own_tile(w, j) + r16;
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) {
+            const float4 x = *reinterpret_cast<const float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g);
+            acc[j][nn] += f32x4{x.x, x.y, x.z, x.w};
+          }
+          if (first) racc[j] += rec[(size_t)NF * SW + f];
+        }
+      }
+      if (tid < SW) g0 += rec[(size_t)NF * SW + NF + tid];
+    }
+    if (tid < SW) S.g0[tid] = g0;
+    publish();
+  }
+  const int last = un.t_begin + ((un.t_end - 1 - un.t_begin) / C) * C;
   Pre pf;
   k_load(p, bh, s, last, pf);
   __syncthreads();
   k_store(S, pf);
   const f16x8 zero8 = {};
 
-  for (int t0 = last; t0 >= 0; t0 -= C) {
-    const int n = min(C, L - t0);
+  for (int t0 = last; t0 >= un.t_begin; t0 -= C) {
+    const int n = min(C, un.t_end - t0);
     __syncthreads();  // chunk inputs and the state copies visible
-    if (t0 > 0) k_load(p, bh, s, t0 - C, pf);
+    if (t0 - C >= un.t_begin) k_load(p, bh, s, t0 - C, pf);
 
     float kf[DK];
     {
@@ -658,49 +907,56 @@ __global__ __launch_bounds__(NTHR) void key_pass_kernel(Params p) {
         }
       }
     }
-    float gsum = 0.f;
-    if (tid < SW)
-      for (int r = 0; r < C; ++r) gsum += (float)S.gh[r][tid] + (float)S.gl[r][tid];
-    float mx = 0.f;
+    {
+      // this chunk's column sums of g, eight rows per thread
+      const int c = tid & (SW - 1), part = tid / SW;
+      float gs = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w))
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[j][nn][i]));
-    mx = wave_max_abs(mx);
-    if (lane == 0) S.wmax[w] = mx;
-    __syncthreads();  // every read of the state copies and the chunk buffers done
-    const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
-    const float down = __builtin_amdgcn_ldexpf(1.f, -e);
-    up = __builtin_amdgcn_ldexpf(1.f, e);
-#pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
-        const int mt = own_tile(w, j);
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const f32x4 a = acc[j][nn] * down;
-          const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
-          const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
-          *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
-          S.rc[16 * nn + 4 * g + 0][16 * mt + r16] = h01[0];
-          S.rc[16 * nn + 4 * g + 1][16 * mt + r16] = h01[1];
-          S.rc[16 * nn + 4 * g + 2][16 * mt + r16] = h23[0];
-          S.rc[16 * nn + 4 * g + 3][16 * mt + r16] = h23[1];
-        }
-        if (first && g == 0) S.rs[16 * mt + r16] = racc[j][0];
-      }
+      for (int r = 0; r < 8; ++r) gs += (float)S.gh[8 * part + r][c] + (float)S.gl[8 * part + r][c];
+      S.gpart[part][c] = gs;
     }
-    if (tid < SW) S.g0[tid] += gsum;
-    if (t0 > 0) k_store(S, pf);
+    publish();
+    if (tid < SW) {
+      float gsum = 0.f;
+#pragma unroll
+      for (int part = 0; part < 8; ++part) gsum += S.gpart[part][tid];
+      S.g0[tid] += gsum;
+    }
+    if (t0 - C >= un.t_begin) k_store(S, pf);
   }
 }
 
 }  // namespace bwdm
 
 bool linattn_bwd_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 || dv == 128; }
+
+// Segments per head: enough workgroups for two per CU, at most MAXSEG, and at
+// least four chunks per segment.
+void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
+  const int nch = (L + bwdm::C - 1) / bwdm::C;
+  const int units = BH * (dv / bwdm::SW);
+  int want = (512 + units - 1) / units;
+  if (want > bwdm::MAXSEG) want = bwdm::MAXSEG;
+  int cap = nch / 4;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  const int sc = nch < 1 ? 1 : (nch + want - 1) / want;
+  *seg_chunks = sc;
+  *nseg = nch < 1 ? 1 : (nch + sc - 1) / sc;
+}
+
+size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
+  int nseg, sc;
+  const int BH = B * H;
+  linattn_bwd_mfma_plan(BH, L, dv, &nseg, &sc);
+  size_t floats = (size_t)3 * BH * L;  // D, den, h
+  if (nseg > 1) {
+    floats += (size_t)BH * nseg * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
+    floats += (size_t)BH * (dv / bwdm::SW) * nseg * bwdm::RREC;                      // suffix records
+  }
+  return floats * sizeof(float);
+}
 
 hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   using namespace bwdm;
@@ -712,18 +968,33 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   p.h = p.den + npos;
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
+  linattn_bwd_mfma_plan((int)BH, a.L, a.dv, &p.nseg, &p.seg_chunks);
+  float* frec = p.h + npos;
+  p.frec = frec;
+  p.frecz = frec + BH * p.nseg * (size_t)(NFC + 1) * a.dv;
+  p.krec = const_cast<float*>(p.frecz) + BH * p.nseg * (size_t)(NFC + 1);
+  const unsigned grid = (unsigned)(BH * p.nslice * p.nseg);
   const size_t zblocks = (npos * DK + 255) / 256, dblocks = (npos * 16 + 255) / 256;
   const unsigned zb = (unsigned)(zblocks < 65536 ? zblocks : 65536);
   if (p.nslice > 1) {
     hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gq, npos * DK);
     hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gk, npos * DK);
   }
+  if (p.nseg > 1) {
+    if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, p.nseg, p.seg_chunks, s);
+        e != hipSuccess)
+      return e;
+  }
   hipLaunchKernelGGL(dy_dot_y_kernel, dim3((unsigned)(dblocks < 65536 ? dblocks : 65536)), dim3(256), 0, s,
                      a.dy, a.y, p.Dy, npos, a.dv);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(query_pass_kernel, dim3((unsigned)(BH * p.nslice)), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL(query_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(key_pass_kernel, dim3((unsigned)(BH * p.nslice)), dim3(NTHR), 0, s, p);
+  if (p.nseg > 1) {
+    hipLaunchKernelGGL(key_state_kernel, dim3(grid), dim3(NTHR), 0, s, p);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(key_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 

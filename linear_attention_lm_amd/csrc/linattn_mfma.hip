@@ -1157,6 +1157,33 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
   return hipGetLastError();
 }
 
+// State-only pass on its own (zero initial state): records [BH][nseg][NF + 1][dv]
+// and [BH][nseg][NF + 1] at ws / wsz, record s + 1 = the compact increment of
+// segment s (s < nseg - 1), slot values sum_t [k_a | k_a^2 | k_a k_b] v_t.
+template <int NT>
+static hipError_t launch_state_records_nt(const void* k, const void* v, float* ws, int BH, int L, int nseg,
+                                          int seg_chunks, hipStream_t s) {
+  Params p{};
+  p.k = (const bf16_t*)k; p.v = (const bf16_t*)v;
+  p.L = L; p.nseg = nseg; p.seg_chunks = seg_chunks;
+  p.ws = ws;
+  p.wsz = ws + (size_t)BH * nseg * (NF + 1) * (16 * NT);
+  hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * (nseg - 1)), dim3(NTHR), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
+                                        int seg_chunks, hipStream_t s) {
+  if (nseg < 2) return hipSuccess;
+  switch (dv) {
+    case 32: return launch_state_records_nt<2>(k, v, ws, BH, L, nseg, seg_chunks, s);
+    case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, s);
+    case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, s);
+    case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t s) {
   switch (a.dv) {
     case 32: return launch_nt<2, 0>(a, nullptr, 0, 0.f, s);
