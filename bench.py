@@ -17,7 +17,9 @@ set are cycled so that successive steps do not find their inputs in the
 per-kernel durations come from events recorded on that stream around every
 launch in the timed region.
 
-Also reported (same JSON line): the roofline of the dominant kernel, the other
+Also reported (same JSON line): the roofline of the dominant kernel, the
+layer backward on the step's workload (based_linattn_bwd + based_swa_bwd:
+gradients of both attentions for a seeded upstream gradient), the other
 forward workloads (1.3B-shaped, 32k long-context), recurrent decode
 (256 sequences x 16 heads, 1000 steps) and the fp64 CPU oracle timed on a
 bounded sample of the step's workload on this host's cores.
@@ -74,6 +76,12 @@ def layer_bytes(dv, es=2):
     return (2 * 16 + dv) * es + 2 * 4 * dv
 
 
+def bwd_bytes(dv, es=2):
+    """Algorithmic HBM bytes per (position, head) of one attention's backward:
+    q, k, v read, y and dy (fp32) read, dq, dk, dv (fp32) written."""
+    return (2 * 16 + dv) * es + 2 * 4 * dv + (2 * 16 + dv) * 4
+
+
 def decode_bytes(dv=64, window=64, es=2):
     """Per head-step: S and z read + written (fp32), the ring's other
     window-1 slots read, q/k/v read, one ring slot written, y_lin and y_swa written."""
@@ -85,13 +93,18 @@ def decode_bytes(dv=64, window=64, es=2):
 # sources no longer describes the kernel).
 OP_SOURCES = {
     "layer": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
+    "bwd": ["linattn_bwd_mfma.hip", "swa_bwd_mfma.hip", "linattn_mfma.hip", "launchers.h", "based_device.h"],
     "decode": ["decode.hip", "launchers.h", "based_device.h"],
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
     "layer": ["linattn_mfma_kernel<4, 1>", "linattn_state_kernel<4>", "seg_scan_kernel"],
+    "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "dy_dot_y_kernel",
+            "linattn_state_kernel<4>", "swa_bwd_mfma_kernel<4>", "bwdm::zero_kernel", "swab::zero_kernel"],
     "decode": ["decode_step_kernel"],
 }
+# the backward's last launch of each call
+BWD_KERNEL = "key_pass_kernel"
 # the step's last launch of each call (marks the end of the timed step in a trace)
 STEP_KERNEL = "linattn_mfma_kernel<4, 1>"
 COPY_BYTES = 512 << 20
@@ -213,6 +226,64 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
     return out
 
 
+def bwd_inputs(lal, cfg, nbuf=8):
+    """Input sets of the layer backward: q, k, v, a seeded upstream gradient
+    dy and the forward outputs y_lin, y_swa (made here, before any timing)."""
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    sets = []
+    for _ in range(nbuf):
+        qd, kd, vd, dyd = (t.to("cuda") for t in (q, k, v, dy))
+        y_lin, y_swa = lal.layer_fwd(qd, kd, vd, cfg.window)
+        sets.append((qd, kd, vd, dyd, y_lin, y_swa))
+    torch.cuda.synchronize()
+    return sets
+
+
+def bench_bwd(lal, cfg, steps, warmup, sets):
+    """Time `steps` layer backwards: based_linattn_bwd then based_swa_bwd on
+    one of the prepared input sets per step.  Returns a dict."""
+    nbuf = len(sets)
+    B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
+    ws = torch.empty(max(1, lal.linattn_bwd_workspace_bytes(B, H, L, dv)), dtype=torch.uint8, device="cuda")
+    gq = torch.empty(B, H, L, 16, device="cuda")
+    gk = torch.empty_like(gq)
+    gv = torch.empty(B, H, L, dv, device="cuda")
+
+    def step(i, timer=None):
+        qd, kd, vd, dyd, y_lin, y_swa = sets[i % nbuf]
+        f1 = lambda: lal.linattn_bwd(qd, kd, vd, y_lin, dyd, dq=gq, dk=gk, dv=gv, workspace=ws)
+        f2 = lambda: lal.swa_bwd(qd, kd, vd, y_swa, dyd, cfg.window, dq=gq, dk=gk, dv=gv)
+        if timer is None:
+            f1()
+            f2()
+        else:
+            timer.run("linattn_bwd", f1)
+            timer.run("swa_bwd", f2)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer = StreamTimer()
+    t0.record()
+    for i in range(steps):
+        step(i, timer)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    th = B * H * L
+    tl, ts = timer.mean_ms("linattn_bwd"), timer.mean_ms("swa_bwd")
+    b1 = bwd_bytes(dv) * th
+    return {"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
+            "dtype": cfg.dtype, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+            "linattn_bwd_us": tl * 1e3, "swa_bwd_us": ts * 1e3,
+            "bytes_per_call": b1, "linattn_bwd_hbm_gbs": b1 / (tl * 1e-3) / 1e9,
+            "swa_bwd_hbm_gbs": b1 / (ts * 1e-3) / 1e9,
+            "layer_bwd_hbm_frac": 2 * b1 / ((tl + ts) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic_bytes_per_step": load_traffic("bwd")}
+
+
 def bench_decode(lal, cfg, warmup=5):
     """Prefill (untimed), then cfg.steps decode steps timed as one block."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
@@ -317,11 +388,16 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
     w_copy = sorted(cw)[len(cw) // 2]
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     # the step workload runs first; its last dispatch is the calls-th launch of the fused main pass
-    step_ids = sorted(i for (i, n) in fetch_all if STEP_KERNEL in n)
-    step_end = step_ids[calls - 1]
-    windows = {"layer": (0, step_end), "decode": (step_end + 1, 1 << 60)}
+    # the step's launches end where the backward (run right after it, with as
+    # many calls) begins; the backward's input set-up runs before the step
+    bwd_ids = sorted(i for (i, n) in fetch_all if BWD_KERNEL in n)
+    first_bwd = bwd_ids[0] if bwd_ids else 1 << 60
+    step_end = max(i for (i, n) in fetch_all if STEP_KERNEL in n and i < first_bwd)
+    bwd_end = bwd_ids[calls - 1] if len(bwd_ids) >= calls else step_end
+    windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    workloads = {"layer": "based360m", "decode": "decode (256 x 16 heads)"}
+    workloads = {"layer": "based360m", "bwd": "based360m layer backward (both attentions)",
+                 "decode": "decode (256 x 16 heads)"}
     for op, frags in OP_KERNELS.items():
         tot_f = tot_w = 0.0
         detail = {}
@@ -357,20 +433,30 @@ def summarize_stats(stats_dir, command, calls):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    step_starts = [int(r["Start_Timestamp"]) for r in rows if STEP_KERNEL in r["Kernel_Name"]]
-    step_end = step_starts[calls - 1] if len(step_starts) >= calls else -1
+    bwd_starts = [int(r["Start_Timestamp"]) for r in rows if BWD_KERNEL in r["Kernel_Name"]]
+    first_bwd = bwd_starts[0] if bwd_starts else 1 << 62
+    step_starts = [int(r["Start_Timestamp"]) for r in rows
+                   if STEP_KERNEL in r["Kernel_Name"] and int(r["Start_Timestamp"]) < first_bwd]
+    step_end = step_starts[-1] if step_starts else -1
+    bwd_end = bwd_starts[calls - 1] if len(bwd_starts) >= calls else step_end
     groups = {}
     for r in rows:
         name = short_name(r["Kernel_Name"])
         grid = r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]
         blk = r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"]
-        phase = "step" if ("based" in name and int(r["Start_Timestamp"]) <= step_end) else ""
+        t = int(r["Start_Timestamp"])
+        phase = ""
+        if "based" in name and t <= step_end:
+            phase = "step"
+        elif "based" in name and t <= bwd_end:
+            phase = "bwd"
         groups.setdefault((name, grid, blk, phase), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", f"Command: `{command}`", "",
-             "Rows marked *step* are the timed layer step (360M-shaped workload, B8 H16 L2048 d_v64 bf16);",
-             "the others are the separate-call comparison, the 1.3B-shaped and 32k workloads, the decode",
-             "loop and set-up kernels.", "",
+             "Rows marked *step* are the timed layer step (360M-shaped workload, B8 H16 L2048 d_v64 bf16),",
+             "rows marked *bwd* the layer backward on the same workload (both attentions' gradients);",
+             "the others are set-up, the separate-call comparison, the 1.3B-shaped and 32k workloads and",
+             "the decode loop.", "",
              "| kernel | grid (threads) | block | step | calls | avg us | min us | max us |",
              "|---|---|---|---|---|---|---|---|"]
     for (name, grid, blk, phase), d in groups.items():
@@ -414,11 +500,16 @@ def main():
     cfg = synth.FWD_CONFIGS["based360m"]
     copy = copy_calibration()
     print(f"[bench] copy calibration: {copy['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    bsets = None if args.no_extra else bwd_inputs(lal, cfg)
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
-    extra, decode, separate = [], None, None
+    extra, decode, separate, backward = [], None, None, None
     if not args.no_extra:
+        backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
+        del bsets
+        print(f"[bench] {cfg.name} backward: linattn {backward['linattn_bwd_us']:.1f} us, swa "
+              f"{backward['swa_bwd_us']:.1f} us", file=sys.stderr, flush=True)
         separate = bench_fwd(lal, cfg, max(10, args.steps // 2), args.warmup, fused=False)
         print(f"[bench] {cfg.name} separate calls: linattn {separate['linattn_us']:.1f} us, swa "
               f"{separate['swa_us']:.1f} us", file=sys.stderr, flush=True)
@@ -448,6 +539,7 @@ def main():
         "kernels": {"layer_us": main_res["layer_us"], "layer_hbm_gbs": main_res["layer_hbm_gbs"],
                     "layer_alg_tflops": main_res["layer_alg_tflops"]},
         "separate_calls": separate,
+        "backward": backward,
         "copy_calibration": copy,
         "cpu_baseline": cpu,
         "other_workloads": extra,

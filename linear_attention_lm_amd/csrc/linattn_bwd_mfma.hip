@@ -196,12 +196,17 @@ __device__ __forceinline__ Unit unit_of(const Params& p) {
 
 // ---------------------------------------------------------------- dy . y
 // 16 lanes per position, four consecutive columns each (64 columns per pass),
-// so that a wavefront reads four whole rows per instruction.
+// so that a wavefront reads four whole rows per instruction.  With several
+// value slices it also clears dq and dk, which the slices then add into.
 __global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __restrict__ y, float* __restrict__ D,
-                                size_t n, int dvf) {
+                                size_t n, int dvf, float* __restrict__ gq, float* __restrict__ gk) {
   const int sub = threadIdx.x & 15;
   const size_t stride = (size_t)gridDim.x * blockDim.x / 16;
   for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; i < n; i += stride) {
+    if (gq) {
+      gq[i * DK + sub] = 0.f;
+      gk[i * DK + sub] = 0.f;
+    }
     float s = 0.f;
     for (int c = 4 * sub; c < dvf; c += 64) {
       const float4 a = *reinterpret_cast<const float4*>(dy + i * dvf + c);
@@ -212,11 +217,6 @@ __global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __res
     for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
     if (sub == 0) D[i] = s;
   }
-}
-
-__global__ void zero_kernel(float* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
 }
 
 // ---------------------------------------------------------------- chunk loads
@@ -974,19 +974,14 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   p.frecz = frec + BH * p.nseg * (size_t)(NFC + 1) * a.dv;
   p.krec = const_cast<float*>(p.frecz) + BH * p.nseg * (size_t)(NFC + 1);
   const unsigned grid = (unsigned)(BH * p.nslice * p.nseg);
-  const size_t zblocks = (npos * DK + 255) / 256, dblocks = (npos * 16 + 255) / 256;
-  const unsigned zb = (unsigned)(zblocks < 65536 ? zblocks : 65536);
-  if (p.nslice > 1) {
-    hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gq, npos * DK);
-    hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, s, p.gk, npos * DK);
-  }
+  const size_t dblocks = (npos * 16 + 255) / 256;
   if (p.nseg > 1) {
     if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, p.nseg, p.seg_chunks, s);
         e != hipSuccess)
       return e;
   }
   hipLaunchKernelGGL(dy_dot_y_kernel, dim3((unsigned)(dblocks < 65536 ? dblocks : 65536)), dim3(256), 0, s,
-                     a.dy, a.y, p.Dy, npos, a.dv);
+                     a.dy, a.y, p.Dy, npos, a.dv, p.nslice > 1 ? p.gq : nullptr, p.gk);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(query_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

@@ -310,9 +310,10 @@ __global__ __launch_bounds__(NTHR) void swa_bwd_mfma_kernel(Params p) {
   }
 }
 
-__global__ void zero_kernel(float* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
+// Clears n4 float4 of p (dq, which the key chunks then add into).
+__global__ void zero_kernel(float4* p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 template <int NT>
@@ -321,9 +322,10 @@ hipError_t launch_nt(const SwaBwdArgs& a, hipStream_t s) {
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y; p.dy = a.dy;
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.nch = (a.L + C - 1) / C; p.window = a.window; p.scale = a.scale;
-  const size_t BH = (size_t)a.B * a.H, n = BH * a.L * DK;
-  const size_t zb = (n + 255) / 256;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(zb < 65536 ? zb : 65536)), dim3(256), 0, s, a.gq, n);
+  const size_t BH = (size_t)a.B * a.H, n4 = BH * a.L * DK / 4;
+  const size_t zb = (n4 + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(zb < 4096 ? zb : 4096)), dim3(256), 0, s,
+                     reinterpret_cast<float4*>(a.gq), n4);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((swa_bwd_mfma_kernel<NT>), dim3((unsigned)(BH * p.nch)), dim3(NTHR), 0, s, p);
   return hipGetLastError();
