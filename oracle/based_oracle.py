@@ -19,6 +19,11 @@ Sources (the web pages that describe the method):
   the quadratic block lists every ordered pair (x_a x_b for a, then b).
   The paragraph on the state: the recurrent form keeps a KV-state for the
   numerator and a K-state for the denominator of the softmax simulation.
+* [BLOG1]   "Базированная модель, часть 1" (same channel), the list of what
+  the paper proves: the BaseConv block y = linear(x) * conv(h, x), an
+  elementwise product of a linear map of the input with a learned filter
+  h convolved over the sequence; the README's acknowledgements name the
+  short causal conv1d kernel of Mamba as the convolution used.
 * [TRAIN]   HazyResearch/based ``train/`` README, "training views": the
   quadratic PyTorch view, the flash-linear-attention kernel and the
   fast-transformers kernel are interchangeable implementations of one
@@ -36,7 +41,11 @@ Readings where the pages are silent (all listed in the design doc as well):
   workloads), the exact exponential that the Taylor map approximates;
 * linear attention and window attention are two separate outputs;
 * the backward is the exact derivative of these forwards with respect to
-  q, k and v (no initial state), as the training views imply.
+  q, k and v (no initial state), as the training views imply;
+* BaseConv's convolution is causal and depthwise (one short filter per
+  channel, zero history before the first position, tap s on x_{t-s}), with
+  an optional per-channel bias; linear(x) is computed by the caller (a plain
+  matrix product) and enters as u.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, invariants, textbook special cases, SciPy's softmax and
@@ -318,6 +327,27 @@ def swa_bwd(q, k, v, dy, window: int = 64, scale: float = 1.0):
         dk[..., idx[rows, w], :] += scale * dS[..., rows, w, None] * q[..., rows, :]
         dv[..., idx[rows, w], :] += p[..., rows, w, None] * dy[..., rows, :]
     return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# BaseConv gating  [BLOG1, BaseConv block; README acknowledgements: short
+# causal conv1d]
+# --------------------------------------------------------------------------
+def baseconv(x, u, h, bias=None):
+    """y = u * conv(h, x): the gated short convolution of the BaseConv block.
+
+    x, u [..., L, D] (u = linear(x), computed by the caller); h [D, K] the
+    per-channel filter, tap s applied to x_{t-s}; bias [D] or None.
+    conv(h, x)[t, c] = bias[c] + sum_{s=0}^{K-1} h[c, s] x[t-s, c], with
+    x[t] = 0 before the first position.  Returns y [..., L, D] (fp64).
+    """
+    x, u, h = _f64(x), _f64(u), _f64(h)
+    L = x.shape[-2]
+    conv = np.zeros_like(x) + (0.0 if bias is None else _f64(bias))
+    for s in range(h.shape[1]):
+        if s < L:
+            conv[..., s:, :] += h[:, s] * x[..., : L - s, :]
+    return u * conv
 
 
 # --------------------------------------------------------------------------

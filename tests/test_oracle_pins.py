@@ -367,3 +367,46 @@ def test_linattn_bwd_rows_matches_full():
     rows = [0, 5, 63, 64, 299]
     for got, want in zip(O.linattn_bwd_rows(q, k, v, dy, rows, 64), full):
         np.testing.assert_allclose(got, want[rows], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ BaseConv
+def test_baseconv_matches_numpy_convolve():
+    """Per channel, the causal depthwise convolution is the first L terms of
+    the full linear convolution (numpy.convolve); the gate multiplies."""
+    L, D, K = 37, 5, 4
+    x, u, h, b = rand(2, L, D), rand(2, L, D), rand(D, K), rand(D)
+    y = O.baseconv(x, u, h, b)
+    for bi in range(2):
+        for c in range(D):
+            want = u[bi, :, c] * (np.convolve(x[bi, :, c], h[c])[:L] + b[c])
+            np.testing.assert_allclose(y[bi, :, c], want, rtol=1e-13, atol=1e-13)
+
+
+def test_baseconv_special_cases():
+    L, D = 9, 3
+    x, u = rand(L, D), rand(L, D)
+    # one tap: y = u * (h0 x + b)
+    h, b = rand(D, 1), rand(D)
+    np.testing.assert_allclose(O.baseconv(x, u, h, b), u * (h[:, 0] * x + b), rtol=1e-15)
+    # an impulse at t0 returns the filter, shifted, times the gate
+    h = rand(D, 3)
+    imp = np.zeros((L, D))
+    imp[4] = 1.0
+    y = O.baseconv(imp, np.ones((L, D)), h)
+    assert not y[:4].any() and not y[7:].any()
+    np.testing.assert_allclose(y[4:7], h.T, rtol=1e-15)
+    # filter longer than the sequence: only the taps that reach back exist
+    y = O.baseconv(x[:2], u[:2], rand(D, 4))
+    assert y.shape == (2, D)
+
+
+def test_baseconv_causal_and_linear():
+    L, D, K = 20, 4, 3
+    x, u, h = rand(L, D), rand(L, D), rand(D, K)
+    y = O.baseconv(x, u, h)
+    x2 = x.copy()
+    x2[12:] = rand(L - 12, D)
+    np.testing.assert_array_equal(O.baseconv(x2, u, h)[:12], y[:12])  # no look-ahead
+    z = rand(L, D)
+    np.testing.assert_allclose(O.baseconv(2.0 * x - z, u, h), 2.0 * y - O.baseconv(z, u, h), rtol=1e-12,
+                               atol=1e-12)
