@@ -19,7 +19,9 @@ launch in the timed region.
 
 Also reported (same JSON line): the roofline of the dominant kernel, the
 layer backward on the step's workload (based_linattn_bwd + based_swa_bwd:
-gradients of both attentions for a seeded upstream gradient), the other
+gradients of both attentions for a seeded upstream gradient), the BaseConv
+gate on the 360M model's hidden states (8 x 2048 tokens x 1024 channels,
+3 taps), the other
 forward workloads (1.3B-shaped, 32k long-context), recurrent decode
 (256 sequences x 16 heads, 1000 steps) and the fp64 CPU oracle timed on a
 bounded sample of the step's workload on this host's cores.
@@ -95,6 +97,7 @@ OP_SOURCES = {
     "layer": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
     "bwd": ["linattn_bwd_mfma.hip", "swa_bwd_mfma.hip", "linattn_mfma.hip", "launchers.h", "based_device.h"],
     "decode": ["decode.hip", "launchers.h", "based_device.h"],
+    "baseconv": ["baseconv.hip", "launchers.h", "based_device.h"],
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
@@ -102,6 +105,7 @@ OP_KERNELS = {
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "dy_dot_y_kernel",
             "linattn_state_kernel<4>", "swa_bwd_mfma_kernel<4>", "bwdm::zero_kernel", "swab::zero_kernel"],
     "decode": ["decode_step_kernel"],
+    "baseconv": ["baseconv_kernel"],
 }
 # the backward's last launch of each call
 BWD_KERNEL = "key_pass_kernel"
@@ -284,6 +288,31 @@ def bench_bwd(lal, cfg, steps, warmup, sets):
             "traffic_bytes_per_step": load_traffic("bwd")}
 
 
+def bench_baseconv(lal, cfg, steps, warmup, nbuf=8):
+    """Time the BaseConv gate over `nbuf` resident input sets.  Bytes per
+    element: x and u read once (dtype), y written (fp32)."""
+    x, u, h, b = synth.baseconv_inputs(cfg, 0)
+    sets = [(x.to("cuda"), u.to("cuda")) for _ in range(nbuf)]
+    hd, bd = h.to("cuda"), b.to("cuda")
+    y = torch.empty(cfg.B, cfg.L, cfg.D, device="cuda")
+    for i in range(warmup):
+        lal.baseconv_fwd(*sets[i % nbuf], hd, bd, y=y)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        lal.baseconv_fwd(*sets[i % nbuf], hd, bd, y=y)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1e3
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbytes = cfg.B * cfg.L * cfg.D * (2 * es + 4)
+    return {"workload": cfg.name, "B": cfg.B, "L": cfg.L, "D": cfg.D, "K": cfg.K, "dtype": cfg.dtype,
+            "us_per_call": us, "tokens_per_s": cfg.B * cfg.L / (us * 1e-6), "bytes_per_call": nbytes,
+            "hbm_gbs": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "traffic_bytes_per_call": load_traffic("baseconv")}
+
+
 def bench_decode(lal, cfg, warmup=5):
     """Prefill (untimed), then cfg.steps decode steps timed as one block."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
@@ -394,10 +423,11 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
     first_bwd = bwd_ids[0] if bwd_ids else 1 << 60
     step_end = max(i for (i, n) in fetch_all if STEP_KERNEL in n and i < first_bwd)
     bwd_end = bwd_ids[calls - 1] if len(bwd_ids) >= calls else step_end
-    windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60)}
+    windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60),
+               "baseconv": (bwd_end + 1, 1 << 60)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     workloads = {"layer": "based360m", "bwd": "based360m layer backward (both attentions)",
-                 "decode": "decode (256 x 16 heads)"}
+                 "decode": "decode (256 x 16 heads)", "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)"}
     for op, frags in OP_KERNELS.items():
         tot_f = tot_w = 0.0
         detail = {}
@@ -504,7 +534,7 @@ def main():
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
-    extra, decode, separate, backward = [], None, None, None
+    extra, decode, separate, backward, conv = [], None, None, None, None
     if not args.no_extra:
         backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
         del bsets
@@ -517,6 +547,9 @@ def main():
             r = bench_fwd(lal, synth.FWD_CONFIGS[name], max(10, args.steps // 2), args.warmup, nbuf=4)
             extra.append(r)
             print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        conv = bench_baseconv(lal, synth.CONV_CONFIGS["baseconv360m"], args.steps, args.warmup)
+        print(f"[bench] baseconv: {conv['us_per_call']:.1f} us/call ({conv['hbm_gbs']:.0f} GB/s)", file=sys.stderr,
+              flush=True)
         decode = bench_decode(lal, synth.DECODE_CONFIG)
         decode["traffic_bytes_per_step"] = load_traffic("decode")
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
@@ -540,6 +573,7 @@ def main():
                     "layer_alg_tflops": main_res["layer_alg_tflops"]},
         "separate_calls": separate,
         "backward": backward,
+        "baseconv": conv,
         "copy_calibration": copy,
         "cpu_baseline": cpu,
         "other_workloads": extra,

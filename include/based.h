@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 3
+#define BASED_ABI_VERSION 4
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -74,6 +74,7 @@ enum {
 #define BASED_DK 16        /* q/k head dimension of the Taylor linear attention */
 #define BASED_DPHI 273     /* 1 + 16 + 16*16 Taylor features                    */
 #define BASED_MAX_WINDOW 64
+#define BASED_MAX_CONV 4     /* longest BaseConv filter (taps)                   */
 
 /* ABI version compiled into the library (BASED_ABI_VERSION). */
 int based_abi_version(void);
@@ -187,6 +188,24 @@ int based_linattn_bwd(const void* q, const void* k, const void* v, const float* 
 int based_swa_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy,
                   float* dq, float* dk, float* dv, int B, int H, int L, int d_qk, int d_v,
                   int window, float scale, int dtype, void* stream);
+
+/*
+ * BaseConv gate, forward: the gated short convolution of the BaseConv block
+ * (blog post "Базированная модель, часть 1", BaseConv: y = linear(x) * conv(h, x);
+ * README acknowledgements: a short causal conv1d).  linear(x) is the caller's
+ * projection of x (a plain matrix product) and enters as u.
+ *
+ *   x, u   [B,L,D] dtype, token-major (channels fastest); D a multiple of 4
+ *   h      [D,K] fp32 filter, tap s applied to x_{t-s}; 1 <= K <= BASED_MAX_CONV
+ *   bias   [D] fp32 or NULL
+ *   y      [B,L,D] fp32 out:
+ *            y[b,t,c] = u[b,t,c] * (bias[c] + sum_{s<K} h[c,s] x[b,t-s,c]),
+ *          x before position 0 taken as zero (causal; each sequence apart).
+ *   B >= 1, L >= 0.  y must not overlap x, u, h or bias.
+ * Arithmetic is fp32 for both dtypes.
+ */
+int based_baseconv_fwd(const void* x, const void* u, const float* h, const float* bias, float* y,
+                       int B, int L, int D, int K, int dtype, void* stream);
 
 /*
  * The Based layer's two attentions over the same q, k, v in one pass: the

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd", "layer_fwd",
-    "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd",
+    "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd", "baseconv_fwd",
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
 
@@ -43,6 +43,7 @@ _SIGNATURES = {
     "based_linattn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "based_linattn_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
     "based_swa_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
+    "based_baseconv_fwd": (_i, [_vp] * 5 + [_i] * 5 + [_vp]),
 }
 
 
@@ -238,6 +239,26 @@ def swa_bwd(q, k, v, y, dy, window: int = 64, scale: float = 1.0, *, dq=None, dk
     _check(_lib().based_swa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), B, H,
                              L, dqk, v.shape[-1], window, float(scale), _dtype_code(q), _stream()))
     return dq, dk, dv
+
+
+def baseconv_fwd(x, u, h, bias=None, *, y=None):
+    """BaseConv gate y = u * (bias + causal depthwise conv of x with h):
+    x, u [B,L,D] (fp32 or bf16, same dtype; u = linear(x) from the caller),
+    h [D,K] fp32 (tap s on x_{t-s}), bias [D] fp32 or None.  Returns y
+    [B,L,D] fp32."""
+    if x.dim() != 3 or u.shape != x.shape or u.dtype != x.dtype:
+        raise ValueError("x and u must be [B,L,D] of one dtype")
+    B, L, D = x.shape
+    if h.dim() != 2 or h.shape[0] != D or h.dtype != torch.float32:
+        raise ValueError("h must be fp32 [D,K]")
+    if bias is not None and (bias.shape != (D,) or bias.dtype != torch.float32):
+        raise ValueError("bias must be fp32 [D]")
+    _dev(x, u, h, bias, y)
+    if y is None:
+        y = torch.empty(B, L, D, device=x.device, dtype=torch.float32)
+    _check(_lib().based_baseconv_fwd(_ptr(x), _ptr(u), _ptr(h), _ptr(bias), _ptr(y), B, L, D, h.shape[1],
+                                  _dtype_code(x), _stream()))
+    return y
 
 
 @dataclass

@@ -213,6 +213,28 @@ BASED_API int based_swa_bwd(const void* q, const void* k, const void* v, const f
   return status_of(based::launch_swa_bwd(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 
+BASED_API int based_baseconv_fwd(const void* x, const void* u, const float* h, const float* bias, float* y, int B,
+                                 int L, int D, int K, int dtype, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || L < 0 || D < 4) return BASED_ERR_SHAPE;
+  if (D % 4 != 0 || K < 1 || K > BASED_MAX_CONV) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * L > (1LL << 31) || (long long)D > (1LL << 24) ||
+      (long long)B * ((L + 15) / 16) > 0x7fffffffLL)
+    return BASED_ERR_SHAPE;
+  if (L == 0) return BASED_OK;
+  if (!x || !u || !h || !y) return BASED_ERR_NULL;
+  const void* ptrs[] = {x, u, h, bias, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t n = (size_t)B * L * D, es = elem_size(dtype);
+  const Span ys = span(y, n * 4);
+  if (overlap(ys, span(x, n * es)) || overlap(ys, span(u, n * es)) || overlap(ys, span(h, (size_t)D * K * 4)) ||
+      overlap(ys, span(bias, (size_t)D * 4)))
+    return BASED_ERR_ALIAS;
+  based::BaseConvArgs a{x, u, h, bias, y, B, L, D, K};
+  return status_of(based::launch_baseconv(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
 BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos, int B,
                                    int H, int L, int d_k, int d_v, int window, int dtype, void* stream) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;

@@ -64,6 +64,13 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv);
 hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t stream);
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t stream);
 
+// BaseConv gate: y = u * (bias + causal depthwise conv of x with h [D, K]).
+struct BaseConvArgs {
+  const void* x; const void* u; const float* h; const float* bias; float* y;
+  int B, L, D, K;
+};
+hipError_t launch_baseconv(const BaseConvArgs& a, bool bf16, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q; const void* k; const void* v;
   float* S; float* z; void* ring_k; void* ring_v; int32_t* pos;

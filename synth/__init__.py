@@ -14,7 +14,9 @@ Recipe (the same for every workload):
   picked without replacement by ``randperm``, are multiplied by ``mult``;
 * finally everything is cast to the workload dtype with round-to-nearest-even;
 * upstream gradients dy for the backward: fp32 ``randn`` [B,H,L,dv] from a
-  generator seeded with ``seed + 1_000_003`` (independent of q, k, v).
+  generator seeded with ``seed + 1_000_003`` (independent of q, k, v);
+* BaseConv: x, u [B,L,D] ~ N(0,1) cast to the dtype, filter h [D,K] ~
+  N(0,1)/sqrt(K) and bias [D] ~ N(0,1)/10 in fp32, drawn in that order.
 
 The workloads stand in for the activations of the 360M / 1.3B Based models
 that the pages train on the Pile (d_k = 16 feature dim, 16 heads, d_v 64/128),
@@ -28,7 +30,7 @@ import dataclasses
 import torch
 
 __all__ = ["FwdConfig", "DecodeConfig", "FWD_CONFIGS", "DECODE_CONFIG", "fwd_inputs", "decode_inputs",
-           "upstream_grad"]
+           "upstream_grad", "ConvConfig", "CONV_CONFIGS", "baseconv_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,3 +138,33 @@ def upstream_grad(cfg: FwdConfig, seed: int = 0) -> torch.Tensor:
     """dy [B,H,L,dv], fp32 N(0,1): the loss gradient fed to the backward."""
     g = torch.Generator("cpu").manual_seed(seed + 1_000_003)
     return torch.randn(cfg.B, cfg.H, cfg.L, cfg.dv, generator=g).contiguous()
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvConfig:
+    name: str
+    B: int
+    L: int
+    D: int
+    K: int = 3
+    dtype: str = "bf16"
+
+    def replace(self, **kw) -> "ConvConfig":
+        return dataclasses.replace(self, **kw)
+
+
+CONV_CONFIGS = {
+    # the 360M model's hidden states (width 1024) over the step's 8 x 2048 tokens, 3-tap filter
+    "baseconv360m": ConvConfig("baseconv360m", B=8, L=2048, D=1024, K=3),
+}
+
+
+def baseconv_inputs(cfg: ConvConfig, seed: int = 0):
+    """x, u [B,L,D] (cfg.dtype), h [D,K] and bias [D] (fp32), CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(cfg.B, cfg.L, cfg.D, generator=g)
+    u = torch.randn(cfg.B, cfg.L, cfg.D, generator=g)
+    h = torch.randn(cfg.D, cfg.K, generator=g) / cfg.K ** 0.5
+    bias = torch.randn(cfg.D, generator=g) / 10
+    dt = _DT[cfg.dtype]
+    return x.to(dt).contiguous(), u.to(dt).contiguous(), h.contiguous(), bias.contiguous()

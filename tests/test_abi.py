@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 3
+    assert so.based_abi_version() == 4
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -196,3 +196,19 @@ def test_swa_bwd_validation(so):
     out_overlap[7] = out_overlap[5]  # dv on top of dq
     assert call(out_overlap) == ERR["ALIAS"]
     assert call(bwd_args(*(big * (i + 1) for i in range(4)), None, *(big * (i + 6) for i in range(3)))) == ERR["NULL"]
+
+
+def test_baseconv_validation(so):
+    big = 0x100000
+    x, u, h, b, y = (big * (i + 1) for i in range(5))
+    call = lambda x=x, u=u, h=h, b=b, y=y, B=2, L=100, D=64, K=3, dt=1: so.based_baseconv_fwd(
+        x, u, h, b, y, B, L, D, K, dt, None)
+    assert call(dt=3) == ERR["DTYPE"]
+    assert call(B=0) == ERR["SHAPE"]
+    assert call(D=66) == ERR["UNSUPPORTED"]
+    assert call(K=0) == ERR["UNSUPPORTED"]
+    assert call(K=5) == ERR["UNSUPPORTED"]
+    assert call(L=0) == 0
+    assert call(h=None) == ERR["NULL"]
+    assert call(y=x) == ERR["ALIAS"]
+    assert call(u=big + 4) == ERR["ALIGN"]
