@@ -42,6 +42,10 @@ Readings where the pages are silent (all listed in the design doc as well):
 * linear attention and window attention are two separate outputs;
 * the backward is the exact derivative of these forwards with respect to
   q, k and v (no initial state), as the training views imply;
+* decay (the train README points to an optional decay strategy with no
+  formula on the pages): a per-head factor 0 < gamma <= 1 on the state,
+  S_i = gamma S_{i-1} + phi(k_i) v_i^T and z likewise, so the kernel weight of
+  key j in row i is K_ij gamma^(i-j); gamma = 1 is the layer without decay;
 * BaseConv's convolution is causal and depthwise (one short filter per
   channel, zero history before the first position, tap s on x_{t-s}), with
   an optional per-channel bias; linear(x) is computed by the caller (a plain
@@ -227,6 +231,55 @@ def swa(q, k, v, window: int = 64, scale: float = 1.0, weight: str = "exp"):
 # Gradients of the two attentions  [TRAIN, training views: the layer is
 # trained through these forwards, so the backward is their exact derivative]
 # --------------------------------------------------------------------------
+def linattn_decay_quadratic(q, k, v, gamma, S0=None, z0=None):
+    """Decayed linear attention, quadratic form [TRAIN, decay strategy; the
+    reading: a per-head factor gamma on the state].  Per (batch, head) with
+    decay g = gamma[head] (gamma has one entry per head, the axis before L):
+      y_i = (sum_{j<=i} g^(i-j) K_ij v_j + g^(i+1) phi(q_i)^T S0)
+            / (sum_{j<=i} g^(i-j) K_ij + g^(i+1) phi(q_i)^T z0),
+    K_ij = 1 + x + x^2/2.  Returns (y, den)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    L, dv = q.shape[-2], v.shape[-1]
+    i = np.arange(L)
+    d = (i[:, None] - i[None, :]).astype(np.float64)
+    lead = q.shape[:-2]
+    gb = g.reshape(g.shape + (1,) * 2)  # [H, 1, 1], broadcast over leading batch dims
+    W = np.where(d >= 0, gb ** np.maximum(d, 0), 0.0)
+    A = taylor_kernel(q @ np.swapaxes(k, -1, -2)) * W
+    num = A @ v
+    den = A.sum(axis=-1)
+    if S0 is not None:
+        pq = phi(q)
+        w0 = g.reshape(g.shape + (1,)) ** (i + 1.0)  # [H, L]
+        num = num + w0[..., None] * (pq @ _f64(S0))
+        den = den + w0 * np.einsum("...lf,...f->...l", pq, _f64(z0))
+    return num / den[..., None], den
+
+
+def linattn_decay_recurrent(q, k, v, gamma, S0=None, z0=None):
+    """Decayed linear attention, recurrent form: for i = 0..L-1,
+    S = g S + phi(k_i) v_i^T, z = g z + phi(k_i), y_i = phi(q_i)^T S / phi(q_i)^T z
+    with g = gamma[head].  Returns (y, den, S, z).  Loop over positions."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _f64(gamma)
+    lead = q.shape[:-2]
+    L, dv = q.shape[-2], v.shape[-1]
+    S = np.zeros(lead + (D_PHI, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (D_PHI,)) if z0 is None else _f64(z0).copy()
+    pq, pk = phi(q), phi(k)
+    gS = g.reshape(g.shape + (1, 1))
+    gz = g.reshape(g.shape + (1,))
+    y = np.empty(lead + (L, dv))
+    den = np.empty(lead + (L,))
+    for t in range(L):
+        S = gS * S + pk[..., t, :, None] * v[..., t, None, :]
+        z = gz * z + pk[..., t, :]
+        den[..., t] = np.einsum("...f,...f->...", pq[..., t, :], z)
+        y[..., t, :] = np.einsum("...f,...fd->...d", pq[..., t, :], S) / den[..., t, None]
+    return y, den, S, z
+
+
 def linattn_bwd(q, k, v, dy):
     """Gradients of the normalised causal linear attention (no initial state)
     with respect to q, k and v, for an upstream gradient dy of y.

@@ -410,3 +410,44 @@ def test_baseconv_causal_and_linear():
     z = rand(L, D)
     np.testing.assert_allclose(O.baseconv(2.0 * x - z, u, h), 2.0 * y - O.baseconv(z, u, h), rtol=1e-12,
                                atol=1e-12)
+
+
+# ------------------------------------------------------------ decay variant
+def test_decay_forms_agree_and_reduce():
+    """Quadratic and recurrent decayed forms agree (with an initial state);
+    gamma = 1 is the undecayed layer."""
+    B, H, L, dv = 2, 3, 13, 4
+    q, k, v = rand(B, H, L, 16, scale=0.3), rand(B, H, L, 16, scale=0.3), rand(B, H, L, dv)
+    g = np.array([1.0, 0.93, 0.5])
+    S0, z0 = rand(B, H, 273, dv), np.abs(rand(B, H, 273)) + 5
+    a = O.linattn_decay_quadratic(q, k, v, g, S0, z0)[0]
+    b = O.linattn_decay_recurrent(q, k, v, g, S0, z0)[0]
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.linattn_decay_quadratic(q, k, v, np.ones(H))[0], O.linattn_quadratic(q, k, v)[0],
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_decay_closed_forms():
+    """L = 2: y_1 = (g K10 v0 + K11 v1) / (g K10 + K11).  A vanishing decay
+    leaves each row its own value."""
+    q, k, v = rand(2, 16, scale=0.4), rand(2, 16, scale=0.4), rand(2, 3)
+    g = 0.7
+    K = lambda a, b: 1 + a @ b + (a @ b) ** 2 / 2
+    k10, k11 = K(q[1], k[0]), K(q[1], k[1])
+    want = (g * k10 * v[0] + k11 * v[1]) / (g * k10 + k11)
+    y = O.linattn_decay_quadratic(q[None], k[None], v[None], np.array([g]))[0][0]
+    np.testing.assert_allclose(y[1], want, rtol=1e-14)
+    np.testing.assert_allclose(y[0], v[0], rtol=1e-14)
+    y = O.linattn_decay_quadratic(q[None], k[None], v[None], np.array([1e-30]))[0][0]
+    np.testing.assert_allclose(y, v, rtol=1e-12)
+
+
+def test_decay_resume_from_state():
+    """Running [0, n) then [n, L) from the exported state equals one run."""
+    H, L, n, dv = 2, 20, 7, 3
+    q, k, v = rand(H, L, 16, scale=0.3), rand(H, L, 16, scale=0.3), rand(H, L, dv)
+    g = np.array([0.8, 0.99])
+    full = O.linattn_decay_recurrent(q, k, v, g)[0]
+    _, _, S, z = O.linattn_decay_recurrent(q[:, :n], k[:, :n], v[:, :n], g)
+    rest = O.linattn_decay_quadratic(q[:, n:], k[:, n:], v[:, n:], g, S, z)[0]
+    np.testing.assert_allclose(rest, full[:, n:], rtol=1e-12, atol=1e-12)
