@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 4
+#define BASED_ABI_VERSION 5
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -123,6 +123,25 @@ int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
                       const float* S_in, const float* z_in, float* S_out, float* z_out,
                       int B, int H, int L, int d_k, int d_v, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal Taylor linear attention with a per-head state decay, forward: the
+ * based/train README's optional decay strategy, read (no formula on the
+ * pages) as S_i = gamma_h S_{i-1} + phi(k_i) v_i^T and z_i = gamma_h z_{i-1} +
+ * phi(k_i), y_i = phi(q_i)^T S_i / phi(q_i)^T z_i -- the kernel weight of key j
+ * in row i becomes K_ij gamma_h^(i-j); gamma_h = 1 is based_linattn_fwd.
+ *
+ *   gamma  [H] fp32, device memory, 0 < gamma_h <= 1 (not checked)
+ *   every other argument as for based_linattn_fwd (same workspace size; S_in
+ *   decays like the rest: position i sees gamma^(i+1) S_in).
+ * BASED_BF16 with d_v in {32, 64, 96, 128} only (BASED_ERR_UNSUPPORTED
+ * otherwise); numerics as for based_linattn_fwd, with the per-key decay
+ * weights of the state update rounded to fp16.
+ */
+int based_linattn_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y,
+                            const float* S_in, const float* z_in, float* S_out, float* z_out,
+                            int B, int H, int L, int d_k, int d_v, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Causal sliding-window softmax attention, forward (README intro: exact

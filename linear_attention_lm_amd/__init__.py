@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd", "layer_fwd",
-    "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd", "baseconv_fwd",
+    "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd", "baseconv_fwd", "linattn_decay_fwd",
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
 
@@ -44,6 +44,7 @@ _SIGNATURES = {
     "based_linattn_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
     "based_swa_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
     "based_baseconv_fwd": (_i, [_vp] * 5 + [_i] * 5 + [_vp]),
+    "based_linattn_decay_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
 }
 
 
@@ -147,6 +148,34 @@ def linattn_fwd(q, k, v, S_in=None, z_in=None, *, return_state=False, y=None, S_
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().based_linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in), _ptr(z_in), _ptr(S_out),
                                  _ptr(z_out), B, H, L, dk, dv, dt, _ptr(workspace), wbytes, _stream()))
+    return (y, S_out, z_out) if (return_state or S_out is not None) else y
+
+
+def linattn_decay_fwd(q, k, v, gamma, S_in=None, z_in=None, *, return_state=False, y=None, S_out=None,
+                      z_out=None, workspace=None):
+    """Causal Taylor linear attention with a per-head state decay gamma [H]
+    (fp32, 0 < gamma <= 1): S_i = gamma S_{i-1} + phi(k_i) v_i^T, likewise z.
+    bf16 q, k, v with d_v in {32, 64, 96, 128}.  Returns y, or (y, S, z)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    if gamma.shape != (H,) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be fp32 [H]")
+    _dev(q, k, v, gamma, S_in, z_in, y, S_out, z_out, workspace)
+    if y is None:
+        y = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if return_state and S_out is None:
+        S_out = torch.empty(B, H, DPHI, dv, device=q.device, dtype=torch.float32)
+        z_out = torch.empty(B, H, DPHI, device=q.device, dtype=torch.float32)
+    dt = _dtype_code(q)
+    need = _lib().based_linattn_workspace_bytes(B, H, L, dk, dv, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().based_linattn_decay_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(y), _ptr(S_in), _ptr(z_in),
+                                       _ptr(S_out), _ptr(z_out), B, H, L, dk, dv, dt, _ptr(workspace), wbytes,
+                                       _stream()))
     return (y, S_out, z_out) if (return_state or S_out is not None) else y
 
 

@@ -83,6 +83,37 @@ BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, flo
   return status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 
+BASED_API int based_linattn_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y,
+                                      const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
+                                      int L, int d_k, int d_v, int dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if (dtype != BASED_BF16 || !based::linattn_mfma_supported(d_v)) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (!gamma || (L > 0 && (!q || !k || !v || !y))) return BASED_ERR_NULL;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
+  const void* ptrs[] = {q, k, v, y, S_in, z_in, S_out, z_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t need = based_linattn_workspace_bytes(B, H, L, d_k, d_v, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BASED_ERR_WORKSPACE;
+  const size_t BH = (size_t)B * H, es = elem_size(dtype);
+  const Span ys = span(y, BH * L * d_v * 4);
+  const Span in[] = {span(q, BH * L * d_k * es), span(k, BH * L * d_k * es), span(v, BH * L * d_v * es),
+                     span(S_in, BH * BASED_DPHI * d_v * 4), span(z_in, BH * BASED_DPHI * 4), span(gamma, (size_t)H * 4)};
+  for (const Span& s : in)
+    if (L > 0 && overlap(ys, s)) return BASED_ERR_ALIAS;
+  if (S_out && (overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[0]) ||
+                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[1]) ||
+                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[2])))
+    return BASED_ERR_ALIAS;
+  if (L == 0 && !S_out) return BASED_OK;
+  based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes, gamma};
+  return status_of(based::launch_linattn_decay_mfma(a, (hipStream_t)stream));
+}
+
 BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
                                const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
                                int L, int d_k, int d_v, int window, float scale, int dtype, void* workspace,

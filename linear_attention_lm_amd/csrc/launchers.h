@@ -14,6 +14,7 @@ struct LinattnArgs {
   const float* S_in; const float* z_in; float* S_out; float* z_out;
   int B, H, L, dv;
   void* workspace; size_t workspace_bytes;
+  const float* gamma = nullptr;  // [H] per-head state decay (decayed variant only)
 };
 
 // fp32 (and generic) chunked linear attention on the vector ALUs.
@@ -24,6 +25,8 @@ bool linattn_mfma_supported(int dv);
 size_t linattn_mfma_workspace(int B, int H, int L, int dv);
 void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
+// The decayed variant (per-head gamma in a.gamma), same layouts and workspace.
+hipError_t launch_linattn_decay_mfma(const LinattnArgs& a, hipStream_t stream);
 // The state-only pass alone (zero initial state; bf16, d_v in {32, 64, 96, 128}):
 // compact segment increments at ws, as the main pass's records.
 hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,

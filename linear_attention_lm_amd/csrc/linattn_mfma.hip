@@ -157,7 +157,18 @@ struct Params {
   float* y_swa;     // sliding-window softmax output of the fused layer pass
   int window;
   float swa_scale;
+  const float* gamma;  // [H] state decay per head (decayed variant)
+  int H;
 };
+
+// Decayed variant: log2 of the head's decay factor, and gamma^d from it.
+__device__ __forceinline__ float decay_lg2(const Params& p, size_t bh) { return __log2f(p.gamma[bh % p.H]); }
+__device__ __forceinline__ float gpow(float lg, float d) { return __builtin_amdgcn_exp2f(lg * d); }
+// sum_{d < n} gamma^d, through expm1 so that gamma near 1 keeps its precision
+__device__ __forceinline__ float gsum_pow(float lg, int n) {
+  const float ln = lg * 0.69314718055994531f;
+  return ln == 0.f ? (float)n : expm1f(ln * (float)n) / expm1f(ln);
+}
 
 // LDS of the main pass.  vt is v^T with the 8-position groups of row `col`
 // XOR-swizzled by (col / 8) % 8, so that the transposing writes of a
@@ -320,10 +331,10 @@ __device__ __forceinline__ f16x8 ones8() {
 // State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
 // (every column of a tz tile holds it).
-template <int NT>
+template <int NT, int DEC = 0>
 __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t (*vt)[VT],
                                              f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3], const int (&ia)[3],
-                                             const int (&ib)[3]) {
+                                             const int (&ib)[3], const f16x8* wk = nullptr) {
   constexpr int H = NT / 2;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int n2 = (w & 1) * H;  // first column tile of slot 2
@@ -336,6 +347,7 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
       const f16x8 x = *reinterpret_cast<const f16x8*>(&kt[ia[ms]][32 * ks + 8 * g]);
       const f16x8 y = *reinterpret_cast<const f16x8*>(&kt[ib[ms]][32 * ks + 8 * g]);
       a[ms] = x * y;
+      if constexpr (DEC) a[ms] *= wk[ks];  // decayed variant: each key's weight
     }
     f16x8 bv[NT], bv2[H];
 #pragma unroll
@@ -480,7 +492,7 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
 // else zero.
 template <int NT>
 __device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW],
-                                           int ncompact = 1) {
+                                           int ncompact = 1, const float* wts = nullptr) {
   constexpr int DV = 16 * NT;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -491,7 +503,8 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * m + 4 * g + i;
-      tacc[j][i] = compact ? compact[(size_t)r * DV + c] : (Sin ? compact_from_phi(Sin, r, c, DV) : 0.f);
+      tacc[j][i] = compact ? compact[(size_t)r * DV + c] * (wts ? wts[0] : 1.f)
+                           : (Sin ? compact_from_phi(Sin, r, c, DV) : 0.f);
     }
   }
   // further records (consecutive, (NF + 1) * DV floats apart; at most
@@ -506,7 +519,7 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
         pair_mn<NT>(w, j, m, n);
         const int c = 16 * n + r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tacc[j][i] += rc[(size_t)(16 * m + 4 * g + i) * DV + c];
+        for (int i = 0; i < 4; ++i) tacc[j][i] += (wts ? wts[k] : 1.f) * rc[(size_t)(16 * m + 4 * g + i) * DV + c];
       }
     }
   }
@@ -595,7 +608,7 @@ template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
 // SWA: 0 = linear attention only; 1 = with the window attention, window 64;
 // 2 = with the window attention, any window.
-template <int NT, int SWA>
+template <int NT, int SWA, int DEC = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
@@ -635,27 +648,40 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   Prefetch<NT> pf, pp;
   if (SWA && tok_begin > 0) load_chunk<NT>(rs, tok_begin - C, false, pp);
   if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
+  // decayed variant: record 1 + k (k < seg, no scan) holds segment k's share
+  // at its end, which lies seg_chunks * C * (seg - 1 - k) positions before
+  // this segment's start
+  float lg = 0.f;
+  float wrec[MAX_SUM];
+#pragma unroll
+  for (int k2 = 0; k2 < MAX_SUM; ++k2) wrec[k2] = 1.f;
+  if constexpr (DEC) {
+    lg = decay_lg2(p, bh);
+    if (!scanned)
+#pragma unroll
+      for (int k2 = 0; k2 < MAX_SUM; ++k2) wrec[k2] = gpow(lg, (float)((seg - 1 - k2) * p.seg_chunks * C));
+  }
   f32x4 tacc[Own<NT>::PPW];
-  init_state<NT>(src, Sin, tacc, nsrc);
+  init_state<NT>(src, Sin, tacc, nsrc, DEC ? wrec : nullptr);
   for (int c = tid; c < DV; c += NTHR) {
     float t = 0.f;
 #pragma unroll
     for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (src && k2 < nsrc) t += src[(size_t)k2 * rec + (size_t)NF * DV + c];
+      if (src && k2 < nsrc) t += wrec[k2] * src[(size_t)k2 * rec + (size_t)NF * DV + c];
     S.t0[c] = src ? t : (Sin ? Sin[c] : 0.f);
   }
   for (int r = tid; r < NF; r += NTHR) {
     float t = 0.f;
 #pragma unroll
     for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (srcz && k2 < nsrc) t += srcz[(size_t)k2 * (NF + 1) + r];
+      if (srcz && k2 < nsrc) t += wrec[k2] * srcz[(size_t)k2 * (NF + 1) + r];
     S.zf[r] = srcz ? t : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
   }
   float z0 = 0.f;
   if (srcz) {
 #pragma unroll
     for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (k2 < nsrc) z0 += srcz[(size_t)k2 * (NF + 1) + NF];
+      if (k2 < nsrc) z0 += wrec[k2] * srcz[(size_t)k2 * (NF + 1) + NF];
   } else if (zin) {
     z0 = zin[0];
   }
@@ -711,8 +737,18 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
         for (int j = 0; j < SPAN; j += 8) {
           const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[cur][col][part * SPAN + j]);
+          if constexpr (DEC) {
+            // weight gamma^(n-1-t) of position t (undoing the column swizzle)
 #pragma unroll
-          for (int k2 = 0; k2 < 8; k2 += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[k2], x[k2 + 1]}, f16x2{1, 1}, vs, false);
+            for (int k2 = 0; k2 < 8; ++k2) {
+              const int t = vt_pos(col, part * SPAN + j + k2);
+              vs = __builtin_fmaf((float)x[k2], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
+            }
+          } else {
+#pragma unroll
+            for (int k2 = 0; k2 < 8; k2 += 2)
+              vs = __builtin_amdgcn_fdot2(f16x2{x[k2], x[k2 + 1]}, f16x2{1, 1}, vs, false);
+          }
         }
       }
       S.vpart[tid] = vs;
@@ -761,6 +797,14 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int nn = 0; nn < NT; ++nn) acc[nn] *= up;
       accz *= up;
     }
+    // decayed variant: the state before the chunk reaches position pos
+    // decayed by gamma^(pos + 1)
+    const float cf = DEC ? gpow(lg, (float)(pos + 1)) : 1.f;
+    if constexpr (DEC) {
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) acc[nn] *= cf;
+      accz *= cf;
+    }
 
     // ---- in-chunk causal term: X^T = K Q^T on the keys 0 .. 16w+15, then
     // Y^T += V^T P^T with the weights P = 1 + x + x^2/2 split into fp16 hi + lo
@@ -785,6 +829,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(xc[m][i], __builtin_fmaf(xc[m][i], 0.5f, 1.f), 1.f);
+          if constexpr (DEC)  // gamma^(query - key)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] *= gpow(lg, (float)max(16 * (w - m) + r16 - 4 * g - i, 0));
           if (m == w)  // key after query
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] *= dkeep[i];
@@ -819,15 +866,15 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     // these stores, so waiting for them never waits for the stores (vector
     // memory operations complete in order).
     {
-      const float rden = __builtin_amdgcn_rcpf(z0 + accz[0]);
+      const float rden = __builtin_amdgcn_rcpf(cf * z0 + accz[0]);
       if (pos < n) {
         float* yrow = p.y + (bh * p.L + t0 + pos) * DV + 4 * g;
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
           const float4 c0 = *reinterpret_cast<const float4*>(&S.t0[16 * nn + 4 * g]);
           *reinterpret_cast<float4*>(yrow + 16 * nn) =
-              make_float4((acc[nn][0] + c0.x) * rden, (acc[nn][1] + c0.y) * rden, (acc[nn][2] + c0.z) * rden,
-                          (acc[nn][3] + c0.w) * rden);
+              make_float4((acc[nn][0] + cf * c0.x) * rden, (acc[nn][1] + cf * c0.y) * rden,
+                          (acc[nn][2] + cf * c0.z) * rden, (acc[nn][3] + cf * c0.w) * rden);
         }
       }
     }
@@ -948,15 +995,34 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     }
 
     // ---- state update with this chunk (registers only)
-    update_chunk<NT>(S.kt, S.vt[cur], tacc, tz, ia, ib);
-    z0 += (float)n;
+    float gn = 1.f;  // decay of the carried state over this chunk
+    if constexpr (DEC) {
+      gn = gpow(lg, (float)n);
+#pragma unroll
+      for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
+#pragma unroll
+      for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
+      f16x8 wk[2];  // weight gamma^(n-1-key) of this lane's keys 32 ks + 8 g + i
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = 32 * ks + 8 * g + i;
+          wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+        }
+      update_chunk<NT, 1>(S.kt, S.vt[cur], tacc, tz, ia, ib, wk);
+      z0 = gn * z0 + gsum_pow(lg, n);
+    } else {
+      update_chunk<NT>(S.kt, S.vt[cur], tacc, tz, ia, ib);
+      z0 += (float)n;
+    }
     post_max<NT>(S.wmax, tacc, tz);
     __syncthreads();  // every read of tt, t0 and the chunk buffers done; wmax complete
     if (tid < DV) {
       float vs = 0.f;
 #pragma unroll
       for (int part = 0; part < PARTS; ++part) vs += S.vpart[part * DV + tid];
-      S.t0[tid] += vs;
+      S.t0[tid] = gn * S.t0[tid] + vs;
     }
     e = state_scale(S.wmax, down, up);
     publish_state<NT>(S.tt, tacc, tz, e, down);
@@ -989,7 +1055,7 @@ struct StateSmem {
   alignas(16) float zf[NF];
 };
 
-template <int NT>
+template <int NT, int DEC = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
@@ -1031,18 +1097,52 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 
   // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare`
   // receives t + 3C: three chunks in flight from HBM while one is updated
+  const float lg = DEC ? decay_lg2(p, bh) : 0.f;
+  const int lane = tid & 63, g = lane >> 4;
   auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
     __syncthreads();
     if (t + 3 * C < tok_end) load_chunk<NT>(rs, t + 3 * C, false, spare);
-    if (part < PARTS) {
+    if constexpr (DEC) {
+      // the carried sums decay over the chunk; keys weigh gamma^(n-1-key)
+      const int n = min(C, tok_end - t);
+      const float gn = gpow(lg, (float)n);
+      vs *= gn;
+      z0 = gn * z0 + gsum_pow(lg, n);
+      if (part < PARTS) {
 #pragma unroll
-      for (int j = 0; j < SPAN; j += 8) {
-        const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
+        for (int j = 0; j < SPAN; j += 8) {
+          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
+          for (int e = 0; e < 8; ++e) {
+            const int tp = vt_pos(col, part * SPAN + j + e);
+            vs = __builtin_fmaf((float)x[e], tp < n ? gpow(lg, (float)(n - 1 - tp)) : 0.f, vs);
+          }
+        }
       }
+#pragma unroll
+      for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
+#pragma unroll
+      for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
+      f16x8 wk[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = 32 * ks + 8 * g + i;
+          wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+        }
+      update_chunk<NT, 1>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib, wk);
+    } else {
+      if (part < PARTS) {
+#pragma unroll
+        for (int j = 0; j < SPAN; j += 8) {
+          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
+        }
+      }
+      update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
     }
-    update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
     if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], nullptr, nullptr, next);
   };
   for (int t = tok_begin; t < tok_end; t += 4 * C) {
@@ -1051,13 +1151,13 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
     if (t + 2 * C < tok_end) step(t + 2 * C, 0, p3, p1);
     if (t + 3 * C < tok_end) step(t + 3 * C, 1, p0, p2);
   }
-  z0 += (float)(tok_end - tok_begin);
+  if constexpr (!DEC) z0 += (float)(tok_end - tok_begin);
   __syncthreads();
   S.vpart[tid] = vs;
   store_z<NT>(S.zf, tz);
   __syncthreads();
   if (tid < DV) {
-    float sum = S.t0[tid];
+    float sum = DEC ? gpow(lg, (float)(tok_end - tok_begin)) * S.t0[tid] : S.t0[tid];
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) sum += S.vpart[q * DV + tid];
     S.t0[tid] = sum;
@@ -1070,7 +1170,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 // Prefix over the segment records of each (batch, head): record s holds the
 // increment of segment s-1 (record 1: the initial state plus that
 // increment); after the scan record s is the state at the start of segment s.
-__global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH) {
+__global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH, const float* gamma, int H,
+                                int seg_len) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t per_head = (size_t)rec + (NF + 1);
   if (e >= per_head * BH) return;
@@ -1087,6 +1188,8 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
   // records are loaded 8 at a time before any is written, so the loads of a
   // group are in flight together
   float run = base[stride];
+  // decayed variant: the running state decays over each segment it crosses
+  const float gseg = gamma ? __builtin_amdgcn_exp2f(__log2f(gamma[bh % H]) * (float)seg_len) : 1.f;
   for (int s0 = 2; s0 < nseg; s0 += 8) {
     float x[8];
 #pragma unroll
@@ -1094,7 +1197,7 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (s0 + i < nseg) {
-        run += x[i];
+        run = gseg * run + x[i];
         base[(size_t)(s0 + i) * stride] = run;
       }
     }
@@ -1131,7 +1234,7 @@ size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
   return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
 }
 
-template <int NT, int SWA>
+template <int NT, int SWA, int DEC = 0>
 static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
   constexpr int DV = 16 * NT;
   Params p{};
@@ -1139,21 +1242,22 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
   p.S_in = a.S_in; p.z_in = a.z_in; p.S_out = a.S_out; p.z_out = a.z_out;
   p.L = a.L;
   p.y_swa = y_swa; p.window = window; p.swa_scale = scale;
+  p.gamma = a.gamma; p.H = a.H;
   linattn_mfma_plan(a.B * a.H, a.L, DV, &p.nseg, &p.seg_chunks);
   const int BH = a.B * a.H;
   if (p.nseg > 1) {
     p.ws = (float*)a.workspace;
     p.wsz = p.ws + (size_t)BH * p.nseg * (NF + 1) * DV;
-    hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((linattn_state_kernel<NT, DEC>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (p.nseg > MAX_SUM + 1) {
       const size_t total = (size_t)BH * ((size_t)(NF + 1) * DV + NF + 1);
       hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p.ws, p.wsz,
-                         p.nseg, (NF + 1) * DV, BH);
+                         p.nseg, (NF + 1) * DV, BH, DEC ? p.gamma : nullptr, a.H, p.seg_chunks * C);
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((linattn_mfma_kernel<NT, SWA>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((linattn_mfma_kernel<NT, SWA, DEC>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1180,6 +1284,16 @@ hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws,
     case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, s);
     case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, s);
     case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_linattn_decay_mfma(const LinattnArgs& a, hipStream_t s) {
+  switch (a.dv) {
+    case 32: return launch_nt<2, 0, 1>(a, nullptr, 0, 0.f, s);
+    case 64: return launch_nt<4, 0, 1>(a, nullptr, 0, 0.f, s);
+    case 96: return launch_nt<6, 0, 1>(a, nullptr, 0, 0.f, s);
+    case 128: return launch_nt<8, 0, 1>(a, nullptr, 0, 0.f, s);
   }
   return hipErrorInvalidValue;
 }

@@ -280,6 +280,19 @@ def linattn_decay_recurrent(q, k, v, gamma, S0=None, z0=None):
     return y, den, S, z
 
 
+def linattn_decay_rows(q, k, v, g, rows):
+    """The decayed output of ``linattn_decay_quadratic`` (no initial state) at
+    selected positions of one head, for sequences too long for L x L
+    matrices: y_i = sum_{j<=i} g^(i-j) K_ij v_j / sum_{j<=i} g^(i-j) K_ij.
+    q, k [L, d_k], v [L, d_v], scalar decay g.  Returns [len(rows), d_v]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    out = []
+    for i in rows:
+        w = taylor_kernel(k[: i + 1] @ q[i]) * float(g) ** (i - np.arange(i + 1, dtype=np.float64))
+        out.append(w @ v[: i + 1] / w.sum())
+    return np.array(out)
+
+
 def linattn_bwd(q, k, v, dy):
     """Gradients of the normalised causal linear attention (no initial state)
     with respect to q, k and v, for an upstream gradient dy of y.

@@ -30,7 +30,7 @@ import dataclasses
 import torch
 
 __all__ = ["FwdConfig", "DecodeConfig", "FWD_CONFIGS", "DECODE_CONFIG", "fwd_inputs", "decode_inputs",
-           "upstream_grad", "ConvConfig", "CONV_CONFIGS", "baseconv_inputs"]
+           "upstream_grad", "ConvConfig", "CONV_CONFIGS", "baseconv_inputs", "decay_rates"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -168,3 +168,11 @@ def baseconv_inputs(cfg: ConvConfig, seed: int = 0):
     bias = torch.randn(cfg.D, generator=g) / 10
     dt = _DT[cfg.dtype]
     return x.to(dt).contiguous(), u.to(dt).contiguous(), h.contiguous(), bias.contiguous()
+
+
+def decay_rates(H: int) -> torch.Tensor:
+    """Per-head state decay for the decayed variant (no draw): gamma_h =
+    1 - 2^-(h + 1) cycling over h mod 8, with head 0 undecayed (gamma = 1):
+    1, 0.75, 0.875, ..., 0.9921875, then again."""
+    g = [1.0 if h % 8 == 0 else 1.0 - 2.0 ** -((h % 8) + 1) for h in range(H)]
+    return torch.tensor(g, dtype=torch.float32)

@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 4
+    assert so.based_abi_version() == 5
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -212,3 +212,18 @@ def test_baseconv_validation(so):
     assert call(h=None) == ERR["NULL"]
     assert call(y=x) == ERR["ALIAS"]
     assert call(u=big + 4) == ERR["ALIGN"]
+
+
+def test_decay_validation(so):
+    big = 0x100000
+    q, k, v, gam, y = (big * (i + 1) for i in range(5))
+    need = so.based_linattn_workspace_bytes(1, 2, 5000, 16, 64, 1)
+    call = lambda gam=gam, y=y, dv=64, dt=1, ws=big * 10, wsb=need: so.based_linattn_decay_fwd(
+        q, k, v, gam, y, None, None, None, None, 1, 2, 5000, 16, dv, dt, ws, wsb, None)
+    assert call(dt=0) == ERR["UNSUPPORTED"]   # fp32: not offered
+    assert call(dv=48) == ERR["UNSUPPORTED"]
+    assert call(gam=None) == ERR["NULL"]
+    assert call(y=q) == ERR["ALIAS"]
+    assert call(y=gam) == ERR["ALIAS"]
+    if need:
+        assert call(ws=None) == ERR["WORKSPACE"]

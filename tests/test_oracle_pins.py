@@ -451,3 +451,12 @@ def test_decay_resume_from_state():
     _, _, S, z = O.linattn_decay_recurrent(q[:, :n], k[:, :n], v[:, :n], g)
     rest = O.linattn_decay_quadratic(q[:, n:], k[:, n:], v[:, n:], g, S, z)[0]
     np.testing.assert_allclose(rest, full[:, n:], rtol=1e-12, atol=1e-12)
+
+
+def test_decay_rows_match_quadratic():
+    L, dv = 90, 5
+    q, k, v = rand(1, L, 16, scale=0.3), rand(1, L, 16, scale=0.3), rand(1, L, dv)
+    g = 0.93
+    full = O.linattn_decay_quadratic(q, k, v, np.array([g]))[0][0]
+    rows = [0, 1, 44, 89]
+    np.testing.assert_allclose(O.linattn_decay_rows(q[0], k[0], v[0], g, rows), full[rows], rtol=1e-13)
