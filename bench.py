@@ -98,6 +98,7 @@ OP_SOURCES = {
     "bwd": ["linattn_bwd_mfma.hip", "swa_bwd_mfma.hip", "linattn_mfma.hip", "launchers.h", "based_device.h"],
     "decode": ["decode.hip", "launchers.h", "based_device.h"],
     "baseconv": ["baseconv.hip", "launchers.h", "based_device.h"],
+    "decay": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
@@ -106,6 +107,7 @@ OP_KERNELS = {
             "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>", "swab::zero_kernel"],
     "decode": ["decode_step_kernel"],
     "baseconv": ["baseconv_kernel"],
+    "decay": ["linattn_mfma_kernel<4, 0, 1>", "linattn_state_kernel<4, 1>"],
 }
 # the backward's last launch of each call
 BWD_KERNEL = "key_pass_kernel"
@@ -313,6 +315,33 @@ def bench_baseconv(lal, cfg, steps, warmup, nbuf=8):
             "traffic_bytes_per_call": load_traffic("baseconv")}
 
 
+def bench_decay(lal, cfg, steps, warmup, nbuf=8):
+    """Time the decayed linear attention (per-head decays from
+    synth.decay_rates) over `nbuf` resident input sets."""
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    sets = [tuple(t.to("cuda") for t in (q, k, v)) for _ in range(nbuf)]
+    g = synth.decay_rates(cfg.H).to("cuda")
+    B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
+    y = torch.empty(B, H, L, dv, device="cuda")
+    ws = torch.empty(max(lal.linattn_workspace_bytes(B, H, L, dv), 1), dtype=torch.uint8, device="cuda")
+    for i in range(warmup):
+        lal.linattn_decay_fwd(*sets[i % nbuf], g, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        lal.linattn_decay_fwd(*sets[i % nbuf], g, y=y, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1e3
+    nbytes = lin_bytes(dv) * B * H * L
+    return {"workload": cfg.name + " decayed linear attention", "B": B, "H": H, "L": L, "d_v": dv,
+            "us_per_call": us, "tokens_per_s": B * L / (us * 1e-6), "bytes_per_call": nbytes,
+            "hbm_gbs": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "alg_tflops": lin_flops(dv) * B * H * L / (us * 1e-6) / 1e12,
+            "traffic_bytes_per_call": load_traffic("decay")}
+
+
 def bench_decode(lal, cfg, warmup=5):
     """Prefill (untimed), then cfg.steps decode steps timed as one block."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
@@ -424,10 +453,11 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
     step_end = max(i for (i, n) in fetch_all if STEP_KERNEL in n and i < first_bwd)
     bwd_end = bwd_ids[calls - 1] if len(bwd_ids) >= calls else step_end
     windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60),
-               "baseconv": (bwd_end + 1, 1 << 60)}
+               "baseconv": (bwd_end + 1, 1 << 60), "decay": (bwd_end + 1, 1 << 60)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     workloads = {"layer": "based360m", "bwd": "based360m layer backward (both attentions)",
-                 "decode": "decode (256 x 16 heads)", "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)"}
+                 "decode": "decode (256 x 16 heads)", "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)",
+                 "decay": "based360m decayed linear attention"}
     for op, frags in OP_KERNELS.items():
         tot_f = tot_w = 0.0
         detail = {}
@@ -485,8 +515,8 @@ def summarize_stats(stats_dir, command, calls):
     lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", f"Command: `{command}`", "",
              "Rows marked *step* are the timed layer step (360M-shaped workload, B8 H16 L2048 d_v64 bf16),",
              "rows marked *bwd* the layer backward on the same workload (both attentions' gradients);",
-             "the others are set-up, the separate-call comparison, the 1.3B-shaped and 32k workloads and",
-             "the decode loop.", "",
+             "the others are set-up, the separate-call comparison, the 1.3B-shaped and 32k workloads, the",
+             "BaseConv gate, the decayed linear attention and the decode loop.", "",
              "| kernel | grid (threads) | block | step | calls | avg us | min us | max us |",
              "|---|---|---|---|---|---|---|---|"]
     for (name, grid, blk, phase), d in groups.items():
@@ -534,7 +564,7 @@ def main():
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
-    extra, decode, separate, backward, conv = [], None, None, None, None
+    extra, decode, separate, backward, conv, decay = [], None, None, None, None, None
     if not args.no_extra:
         backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
         del bsets
@@ -550,6 +580,9 @@ def main():
         conv = bench_baseconv(lal, synth.CONV_CONFIGS["baseconv360m"], args.steps, args.warmup)
         print(f"[bench] baseconv: {conv['us_per_call']:.1f} us/call ({conv['hbm_gbs']:.0f} GB/s)", file=sys.stderr,
               flush=True)
+        decay = bench_decay(lal, cfg, args.steps, args.warmup)
+        print(f"[bench] {cfg.name} decayed linear attention: {decay['us_per_call']:.1f} us/call "
+              f"({decay['hbm_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
         decode = bench_decode(lal, synth.DECODE_CONFIG)
         decode["traffic_bytes_per_step"] = load_traffic("decode")
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
@@ -574,6 +607,7 @@ def main():
         "separate_calls": separate,
         "backward": backward,
         "baseconv": conv,
+        "decay": decay,
         "copy_calibration": copy,
         "cpu_baseline": cpu,
         "other_workloads": extra,
