@@ -104,7 +104,7 @@ OP_SOURCES = {
 OP_KERNELS = {
     "layer": ["linattn_mfma_kernel<4, 1, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "dy_dot_y_kernel",
-            "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>", "swab::zero_kernel"],
+            "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>"],
     "decode": ["decode_step_kernel"],
     "baseconv": ["baseconv_kernel"],
     "decay": ["linattn_mfma_kernel<4, 0, 1>", "linattn_state_kernel<4, 1>"],
