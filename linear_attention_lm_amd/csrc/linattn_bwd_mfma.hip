@@ -42,6 +42,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;                // positions per chunk
 constexpr int NTHR = 256;            // 4 wavefronts
@@ -52,12 +53,12 @@ constexpr int NKS = (NF + 31) / 32;  // 9 steps of 32 features (the last half ze
 constexpr int QH = 24;               // fp16 stride of q / k rows
 constexpr int XT = C + 8;            // fp16 stride of transposed chunk rows
 constexpr int RS = SW + 8;           // fp16 stride of slice rows
-constexpr int FS = 32 * NKS + 8;     // fp16 stride of the feature rows of a column-major state copy
 constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for w = 0)
 constexpr int SCALE_TOP = 13;
 constexpr int MAXSEG = 8;            // segments per head at most (records summed directly)
 constexpr int NFC = 160;             // compact slots of the forward's state records
 constexpr int RREC = NF * SW + NF + SW;  // floats of one suffix-state record (R, r, sum g)
+constexpr int NFP = 32 * NKS;        // feature rows of the key pass's state copy (rows NF.. zero)
 
 // Slot of the forward's compact records holding feature f of this layout
 // (f < 16: x_f; f = 16 + 16a + b: x_a x_b).  The compact layout: slot
@@ -114,6 +115,28 @@ __device__ __forceinline__ f16x8 cat44(const half_t* a, const half_t* b) {
   const uint2 x = *reinterpret_cast<const uint2*>(a), y = *reinterpret_cast<const uint2*>(b);
   return __builtin_bit_cast(f16x8, make_uint4(x.x, x.y, y.x, y.y));
 }
+// Transposing LDS read (ds_read_b64_tr_b16): rows r0 .. r0 + 3 of column
+// c0 + (lane % 16) of the row-major fp16 array at `base` (row stride ld).
+// Within each 16-lane block lane t receives element t % 4 of the 4-element
+// segments addressed by lanes t / 4 + 4i, so lane j points at row r0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3.
+__device__ __forceinline__ uint2 tr4(const half_t* base, int r0, int c0, int ld) {
+  const int j = threadIdx.x & 15;
+  const half_t* a = base + (r0 + (j >> 2)) * ld + c0 + 4 * (j & 3);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a);
+  return __builtin_bit_cast(uint2, v);
+}
+// MFMA operand with K = rows r0 .. r0 + 7 of column c0 + (lane % 16)
+__device__ __forceinline__ f16x8 tr8(const half_t* base, int r0, int c0, int ld) {
+  const uint2 a = tr4(base, r0, c0, ld), b = tr4(base, r0 + 4, c0, ld);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// K = rows r0 .. r0 + 3 and r0 + 16 .. r0 + 19 (two 16-row tiles)
+__device__ __forceinline__ f16x8 tr44(const half_t* base, int r0, int c0, int ld) {
+  const uint2 a = tr4(base, r0, c0, ld), b = tr4(base, r0 + 16, c0, ld);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
 __device__ __forceinline__ f16x8 ones8() {
   const uint32_t one2 = 0x3c003c00u;
   return __builtin_bit_cast(f16x8, make_uint4(one2, one2, one2, one2));
@@ -252,7 +275,6 @@ struct QSmem {
   alignas(16) half_t qh[C][QH];            // q rows
   alignas(16) half_t kh[C][QH];            // k rows
   alignas(16) half_t kt[DK][XT];           // k^T
-  alignas(16) half_t vt[SW][XT];           // v^T (slice)
   alignas(16) half_t vh[C][RS];            // v rows (slice)
   alignas(16) half_t gh[C][RS], gl[C][RS];  // g hi / lo (slice)
   alignas(16) half_t st[NF][RS];           // state S, feature rows, scaled by 2^-e
@@ -278,16 +300,12 @@ __device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
   }
   {
     const int r = tid >> 2, cq = tid & 3;
-    const uint4 x = h8_from_bf8(pf.v);
-    *reinterpret_cast<uint4*>(&S.vh[r][8 * cq]) = x;
-    const f16x8 e = __builtin_bit_cast(f16x8, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) S.vt[8 * cq + i][r] = e[i];
+    *reinterpret_cast<uint4*>(&S.vh[r][8 * cq]) = h8_from_bf8(pf.v);
   }
   if (tid < C) S.dys[tid] = pf.aux;
 }
 
-__global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
+__global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
   __shared__ QSmem S;
   const Unit un = unit_of(p);
   const size_t bh = un.bh;
@@ -513,7 +531,7 @@ __global__ __launch_bounds__(NTHR) void query_pass_kernel(Params p) {
           const f16x8 fb = mt == 0 ? kb : ld8(&S.kt[mt - 1][32 * ks + 8 * g]) * kb;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
-            acc[j][nn] = mfma(ld8(&S.vt[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+            acc[j][nn] = mfma(tr8(&S.vh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
           zacc[j] = mfma(ones, fb, zacc[j]);
         }
       }
@@ -530,10 +548,8 @@ struct KSmem {
   alignas(16) half_t kh[C][QH];              // k rows
   alignas(16) half_t vh[C][RS];              // v rows (slice)
   alignas(16) half_t gh[C][RS], gl[C][RS];    // g rows hi / lo (slice)
-  alignas(16) half_t gth[SW][XT], gtl[SW][XT];  // g^T hi / lo
   alignas(16) half_t hh[XT], hl[XT];         // h over the chunk's positions, hi / lo
-  alignas(16) half_t rf[NF][RS];             // state R, feature rows, scaled by 2^-e
-  alignas(16) half_t rc[SW][FS];             // state R, column rows (features 272.. zero), scaled
+  alignas(16) half_t rf[NFP][RS];            // state R, feature rows (rows NF.. zero), scaled by 2^-e
   alignas(16) float rs[NF];                  // state r (fp32)
   alignas(16) float g0[SW];                  // sum of g over the later positions
   alignas(16) float hs[C];                   // h of the chunk's positions
@@ -566,13 +582,6 @@ __device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
     split2(pf.dy1.z * rden, pf.dy1.w * rden, hi[3], lo[3]);
     *reinterpret_cast<uint4*>(&S.gh[r][8 * cq]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *reinterpret_cast<uint4*>(&S.gl[r][8 * cq]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    const f16x8 eh = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-    const f16x8 el = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      S.gth[8 * cq + i][r] = eh[i];
-      S.gtl[8 * cq + i][r] = el[i];
-    }
   }
   if (tid < C) {
     const float hv = pf.aux2;
@@ -596,7 +605,7 @@ __device__ __forceinline__ void k_load(const Params& p, size_t bh, int s, int t0
 // starts from the sum of the increments of the segments after it.
 struct KIncSmem {
   alignas(16) half_t qt[DK][XT];
-  alignas(16) half_t gth[SW][XT], gtl[SW][XT];
+  alignas(16) half_t gh[C][RS], gl[C][RS];  // g rows hi / lo (slice)
   alignas(16) half_t hh[XT], hl[XT];
   float gcol[SW];
 };
@@ -634,14 +643,10 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) split2(gv[2 * e], gv[2 * e + 1], hi[e], lo[e]);
-      const f16x8 eh = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-      const f16x8 el = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+      *reinterpret_cast<uint4*>(&S.gh[r][8 * cq]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&S.gl[r][8 * cq]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        S.gth[8 * cq + i][r] = eh[i];
-        S.gtl[8 * cq + i][r] = el[i];
-        gpart[i] += gv[i];
-      }
+      for (int i = 0; i < 8; ++i) gpart[i] += gv[i];
     }
     if (tid < C) {
       const float hv = pf.aux2;
@@ -661,8 +666,8 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
           const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
-            acc[j][nn] = mfma(ld8(&S.gth[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
-            acc[j][nn] = mfma(ld8(&S.gtl[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+            acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
+            acc[j][nn] = mfma(tr8(&S.gl[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
           }
           if (first) {
             racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
@@ -700,8 +705,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   const int kpos = 16 * w + r16;  // key of the lane in transposed tiles
   const int L = p.L;
 
-  for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
-  for (int e = tid; e < SW * FS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rc[0][0])[e] = 0u;
+  for (int e = tid; e < NFP * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.rs[e] = 0.f;
   if (tid < SW) S.g0[tid] = 0.f;
   f32x4 acc[MAXOWN][2], racc[MAXOWN];
@@ -736,10 +740,6 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
           const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
           *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
-          S.rc[16 * nn + 4 * g + 0][16 * mt + r16] = h01[0];
-          S.rc[16 * nn + 4 * g + 1][16 * mt + r16] = h01[1];
-          S.rc[16 * nn + 4 * g + 2][16 * mt + r16] = h23[0];
-          S.rc[16 * nn + 4 * g + 3][16 * mt + r16] = h23[1];
         }
         if (first && g == 0) S.rs[16 * mt + r16] = racc[j][0];
       }
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           fb = kb8 * ka;
         }
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn) dva[nn] = mfma(ld8(&S.rc[16 * nn + r16][32 * ks + 8 * g]), fb, dva[nn]);
+        for (int nn = 0; nn < 2; ++nn) dva[nn] = mfma(tr8(&S.rf[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, dva[nn]);
       }
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
@@ -862,9 +862,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           dka = mfma(qa, cl, dka);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
-            const int c = 16 * nn + r16;
-            const f16x8 gah = cat44(&S.gth[c][32 * kb + 4 * g], &S.gth[c][32 * kb + 16 + 4 * g]);
-            const f16x8 gal = cat44(&S.gtl[c][32 * kb + 4 * g], &S.gtl[c][32 * kb + 16 + 4 * g]);
+            const f16x8 gah = tr44(&S.gh[0][0], 32 * kb + 4 * g, 16 * nn, RS);
+            const f16x8 gal = tr44(&S.gl[0][0], 32 * kb + 4 * g, 16 * nn, RS);
             dva[nn] = mfma(gah, ah, dva[nn]);
             dva[nn] = mfma(gah, al, dva[nn]);
             dva[nn] = mfma(gal, ah, dva[nn]);
@@ -897,8 +896,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
-            acc[j][nn] = mfma(ld8(&S.gth[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
-            acc[j][nn] = mfma(ld8(&S.gtl[16 * nn + r16][32 * ks + 8 * g]), fb, acc[j][nn]);
+            acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
+            acc[j][nn] = mfma(tr8(&S.gl[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
           }
           if (first) {
             racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
