@@ -243,6 +243,36 @@ __global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __res
 }
 
 // ---------------------------------------------------------------- chunk loads
+// Raw buffer loads through per-head descriptors (scalar registers, 32-bit
+// offsets): reads past the end of the sequence return zero, with no branch
+// and no 64-bit address held in vector registers across the chunk loop.
+struct HeadRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v, dy;
+  __amdgpu_buffer_rsrc_t f1, f2;  // per-position fp32: D (query pass); den and h (key passes)
+};
+constexpr int RSRC_DW3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_DW3);
+}
+__device__ __forceinline__ HeadRsrc head_rsrc(const Params& p, size_t bh, const float* f1, const float* f2) {
+  const size_t L = p.L;
+  HeadRsrc r;
+  r.q = rsrc(p.q + bh * L * DK, L * DK * 2);
+  r.k = rsrc(p.k + bh * L * DK, L * DK * 2);
+  r.v = rsrc(p.v + bh * L * p.dvf, L * p.dvf * 2);
+  r.dy = rsrc(p.dy + bh * L * p.dvf, L * p.dvf * 4);
+  r.f1 = rsrc(f1 + bh * L, L * 4);
+  r.f2 = rsrc(f2 + bh * L, L * 4);
+  return r;
+}
+__device__ __forceinline__ uint4 bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Thread -> data: q (threads 0..127) or k (128..255) row (tid & 127) / 2, 8
 // coordinates; v and dy of the slice: row tid / 4, columns 8 (tid % 4) ..
 struct Pre {
@@ -253,20 +283,18 @@ struct Pre {
   float aux2;  // key pass: h of position tid (tid < 64)
 };
 
-__device__ __forceinline__ void load_common(const Params& p, size_t bh, int s, int t0, Pre& pf) {
-  const int tid = threadIdx.x, L = p.L;
+__device__ __forceinline__ void load_common(const Params& p, const HeadRsrc& rs, int s, int t0, Pre& pf) {
+  const int tid = threadIdx.x;
   {
-    const int r = (tid & 127) >> 1, half = tid & 1, t = t0 + r;
-    const bf16_t* src = (tid < 128 ? p.q : p.k) + ((size_t)bh * L + t) * DK + 8 * half;
-    pf.qk = t < L ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+    const int r = (tid & 127) >> 1, half = tid & 1;
+    pf.qk = bload4(wave_index() < 2 ? rs.q : rs.k, ((t0 + r) * DK + 8 * half) * 2);
   }
   {
-    const int r = tid >> 2, cq = tid & 3, t = t0 + r;
-    const size_t off = ((size_t)bh * L + t) * p.dvf + (size_t)s * SW + 8 * cq;
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    pf.v = t < L ? *reinterpret_cast<const uint4*>(p.v + off) : make_uint4(0u, 0u, 0u, 0u);
-    pf.dy0 = t < L ? *reinterpret_cast<const float4*>(p.dy + off) : z4;
-    pf.dy1 = t < L ? *reinterpret_cast<const float4*>(p.dy + off + 4) : z4;
+    const int r = tid >> 2, cq = tid & 3;
+    const int e = (t0 + r) * p.dvf + s * SW + 8 * cq;
+    pf.v = bload4(rs.v, e * 2);
+    pf.dy0 = __builtin_bit_cast(float4, bload4(rs.dy, e * 4));
+    pf.dy1 = __builtin_bit_cast(float4, bload4(rs.dy, e * 4 + 16));
   }
 }
 
@@ -376,9 +404,10 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     }
     publish();
   }
+  const HeadRsrc rs = head_rsrc(p, bh, p.Dy, p.Dy);
   Pre pf;
-  load_common(p, bh, s, un.t_begin, pf);
-  pf.aux = tid < C && un.t_begin + tid < L ? p.Dy[(size_t)bh * L + un.t_begin + tid] : 0.f;
+  load_common(p, rs, s, un.t_begin, pf);
+  pf.aux = bload1(rs.f1, (un.t_begin + (tid & 63)) * 4);  // D (zero past the end)
   __syncthreads();
   q_store(S, pf);
   const f16x8 zero8 = {};
@@ -389,8 +418,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const float4 dy0 = pf.dy0, dy1 = pf.dy1;  // this chunk's dy (the prefetch below replaces pf)
     __syncthreads();  // chunk inputs and the state copy visible
     if (t0 + C < un.t_end) {
-      load_common(p, bh, s, t0 + C, pf);
-      pf.aux = tid < C && t0 + C + tid < L ? p.Dy[(size_t)bh * L + t0 + C + tid] : 0.f;
+      load_common(p, rs, s, t0 + C, pf);
+      pf.aux = bload1(rs.f1, (t0 + C + (tid & 63)) * 4);
     }
 
     // ---- scores X^T (keys x queries) of the chunk's key tiles m <= w, the
@@ -592,12 +621,13 @@ __device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
   }
 }
 
-__device__ __forceinline__ void k_load(const Params& p, size_t bh, int s, int t0, Pre& pf) {
-  const int tid = threadIdx.x, L = p.L;
-  load_common(p, bh, s, t0, pf);
+__device__ __forceinline__ void k_load(const Params& p, const HeadRsrc& rs, int s, int t0, Pre& pf) {
+  const int tid = threadIdx.x;
+  load_common(p, rs, s, t0, pf);
   const int r = t0 + (tid >> 2);
-  pf.aux = r < L ? p.den[(size_t)bh * L + r] : 1.f;
-  pf.aux2 = tid < C && t0 + tid < L ? p.h[(size_t)bh * L + t0 + tid] : 0.f;
+  const float den = bload1(rs.f1, r * 4);
+  pf.aux = r < p.L ? den : 1.f;  // rows past the end: g = 0
+  pf.aux2 = bload1(rs.f2, (t0 + (tid & 63)) * 4);  // h (zero past the end)
 }
 
 // Suffix-state increment of one segment (>= 1): R += phi(Q)^T G,
@@ -625,8 +655,9 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   }
   float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (tid < SW) S.gcol[tid] = 0.f;
+  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h);
   Pre pf;
-  k_load(p, bh, s, un.t_begin, pf);
+  k_load(p, rs, s, un.t_begin, pf);
   for (int t0 = un.t_begin; t0 < un.t_end; t0 += C) {
     __syncthreads();  // the previous chunk's reads done
     if (tid < 128) {
@@ -655,7 +686,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       S.hl[tid] = (_Float16)(hv - (float)hhi);
     }
     __syncthreads();
-    if (t0 + C < un.t_end) k_load(p, bh, s, t0 + C, pf);
+    if (t0 + C < un.t_end) k_load(p, rs, s, t0 + C, pf);
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
       if (j < own_count(w)) {
@@ -768,8 +799,9 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     publish();
   }
   const int last = un.t_begin + ((un.t_end - 1 - un.t_begin) / C) * C;
+  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h);
   Pre pf;
-  k_load(p, bh, s, last, pf);
+  k_load(p, rs, s, last, pf);
   __syncthreads();
   k_store(S, pf);
   const f16x8 zero8 = {};
@@ -777,7 +809,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   for (int t0 = last; t0 >= un.t_begin; t0 -= C) {
     const int n = min(C, un.t_end - t0);
     __syncthreads();  // chunk inputs and the state copies visible
-    if (t0 - C >= un.t_begin) k_load(p, bh, s, t0 - C, pf);
+    if (t0 - C >= un.t_begin) k_load(p, rs, s, t0 - C, pf);
 
     float kf[DK];
     {
@@ -959,6 +991,7 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
 
 hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   using namespace bwdm;
+  if ((size_t)a.L * a.dv * 4 >= (size_t)1 << 31) return hipErrorInvalidValue;  // 32-bit buffer offsets
   const size_t BH = (size_t)a.B * a.H, npos = BH * a.L;
   Params p{};
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y; p.dy = a.dy;
