@@ -345,10 +345,14 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 
   for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.st[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.zs[e] = 0.f;
-  f32x4 acc[MAXOWN][2], zacc[MAXOWN];
+  // state S of the owned feature tiles; z as one value per lane and tile
+  // (feature 16 mt + r16: the rows of a z tile are all equal)
+  f32x4 acc[MAXOWN][2];
+  float zacc[MAXOWN];
 #pragma unroll
   for (int j = 0; j < MAXOWN; ++j) {
-    acc[j][0] = acc[j][1] = zacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    zacc[j] = 0.f;
   }
   float up = 1.f;
   // largest state magnitude over the workgroup -> scale; state copy to LDS
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           const uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
           *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
         }
-        if (g == 0) S.zs[16 * mt + r16] = zacc[j][0];
+        if (g == 0) S.zs[16 * mt + r16] = zacc[j];
       }
     }
   };
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
             for (int i = 0; i < 4; ++i) acc[j][nn][i] += p.frec[rec * p.dvf + s * SW + 16 * nn + 4 * g + i];
           z += p.frecz[rec];
         }
-        zacc[j] = f32x4{z, z, z, z};
+        zacc[j] = z;
       }
     }
     publish();
@@ -498,8 +502,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     for (int m = 0; m < NFT; ++m) {
       const f16x8 sa = ld8(&S.st[16 * m + r16][8 * g]);
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
-      u = mfma(sa, gbh, u);
-      u = mfma(sa, gbl, u);
+      u = mfma(sa, gbh, u);  // g rounded once: the state copy is fp16 as well
       u *= up;
       if (first) {
         const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[16 * m + 4 * g]);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.vh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-          zacc[j] = mfma(ones, fb, zacc[j]);
+          zacc[j] += mfma(ones, fb, f32x4{0.f, 0.f, 0.f, 0.f})[0];
         }
       }
     }
@@ -577,7 +580,7 @@ struct KSmem {
   alignas(16) half_t kh[C][QH];              // k rows
   alignas(16) half_t vh[C][RS];              // v rows (slice)
   alignas(16) half_t gh[C][RS], gl[C][RS];    // g rows hi / lo (slice)
-  alignas(16) half_t hh[XT], hl[XT];         // h over the chunk's positions, hi / lo
+  alignas(16) half_t hh[XT];                 // h over the chunk's positions, fp16
   alignas(16) half_t rf[NFP][RS];            // state R, feature rows (rows NF.. zero), scaled by 2^-e
   alignas(16) float rs[NF];                  // state r (fp32)
   alignas(16) float g0[SW];                  // sum of g over the later positions
@@ -615,9 +618,7 @@ __device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
   if (tid < C) {
     const float hv = pf.aux2;
     S.hs[tid] = hv;
-    const _Float16 hhi = (_Float16)hv;
-    S.hh[tid] = hhi;
-    S.hl[tid] = (_Float16)(hv - (float)hhi);
+    S.hh[tid] = (_Float16)hv;
   }
 }
 
@@ -635,8 +636,8 @@ __device__ __forceinline__ void k_load(const Params& p, const HeadRsrc& rs, int 
 // starts from the sum of the increments of the segments after it.
 struct KIncSmem {
   alignas(16) half_t qt[DK][XT];
-  alignas(16) half_t gh[C][RS], gl[C][RS];  // g rows hi / lo (slice)
-  alignas(16) half_t hh[XT], hl[XT];
+  alignas(16) half_t gh[C][RS];  // g rows (slice), fp16
+  alignas(16) half_t hh[XT];     // h, fp16
   float gcol[SW];
 };
 
@@ -671,20 +672,14 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       const float rden = 1.f / pf.aux;
       const float gv[8] = {pf.dy0.x * rden, pf.dy0.y * rden, pf.dy0.z * rden, pf.dy0.w * rden,
                            pf.dy1.x * rden, pf.dy1.y * rden, pf.dy1.z * rden, pf.dy1.w * rden};
-      uint32_t hi[4], lo[4];
+      uint32_t hi[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split2(gv[2 * e], gv[2 * e + 1], hi[e], lo[e]);
+      for (int e = 0; e < 4; ++e) hi[e] = u32(__builtin_convertvector((f32x2{gv[2 * e], gv[2 * e + 1]}), f16x2));
       *reinterpret_cast<uint4*>(&S.gh[r][8 * cq]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(&S.gl[r][8 * cq]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) gpart[i] += gv[i];
     }
-    if (tid < C) {
-      const float hv = pf.aux2;
-      const _Float16 hhi = (_Float16)hv;
-      S.hh[tid] = hhi;
-      S.hl[tid] = (_Float16)(hv - (float)hhi);
-    }
+    if (tid < C) S.hh[tid] = (_Float16)pf.aux2;
     __syncthreads();
     if (t0 + C < un.t_end) k_load(p, rs, s, t0 + C, pf);
 #pragma unroll
@@ -696,14 +691,9 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
           const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
           const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
 #pragma unroll
-          for (int nn = 0; nn < 2; ++nn) {
+          for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-            acc[j][nn] = mfma(tr8(&S.gl[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-          }
-          if (first) {
-            racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
-            racc[j] = mfma(ld8(&S.hl[32 * ks + 8 * g]), fb, racc[j]);
-          }
+          if (first) racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
         }
       }
     }
@@ -739,10 +729,14 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   for (int e = tid; e < NFP * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.rs[e] = 0.f;
   if (tid < SW) S.g0[tid] = 0.f;
-  f32x4 acc[MAXOWN][2], racc[MAXOWN];
+  // state R of the owned feature tiles; r as one value per lane and tile
+  // (feature 16 mt + r16: the rows of an r tile are all equal)
+  f32x4 acc[MAXOWN][2];
+  float racc[MAXOWN];
 #pragma unroll
   for (int j = 0; j < MAXOWN; ++j) {
-    acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    racc[j] = 0.f;
   }
   float up = 1.f;
   // largest state magnitude over the workgroup -> scale; both state copies to LDS
@@ -772,7 +766,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
           *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
         }
-        if (first && g == 0) S.rs[16 * mt + r16] = racc[j][0];
+        if (first && g == 0) S.rs[16 * mt + r16] = racc[j];
       }
     }
   };
@@ -922,20 +916,18 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     for (int j = 0; j < MAXOWN; ++j) {
       if (j < own_count(w)) {
         const int mt = own_tile(w, j);
+        // g and h rounded once to fp16 (the state is read back as an fp16 copy)
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
           const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
 #pragma unroll
-          for (int nn = 0; nn < 2; ++nn) {
+          for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-            acc[j][nn] = mfma(tr8(&S.gl[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-          }
-          if (first) {
-            racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
-            racc[j] = mfma(ld8(&S.hl[32 * ks + 8 * g]), fb, racc[j]);
-          }
+          if (first) t = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, t);
         }
+        if (first) racc[j] += t[0];
       }
     }
     {
