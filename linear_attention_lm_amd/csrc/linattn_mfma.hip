@@ -52,6 +52,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;         // positions per chunk
 constexpr int NTHR = 256;     // 4 wavefronts
@@ -59,7 +60,6 @@ constexpr int NF = 160;       // feature slots (linear + quadratic), constant ke
 constexpr int NKB = NF / 32;  // K-blocks of 32 slots in the readout
 constexpr int QH = 24;        // fp16 q / k row stride in LDS (elements)
 constexpr int KT = C + 8;     // fp16 k^T row stride
-constexpr int VT = C + 8;     // fp16 v^T row stride
 constexpr int TT = NF + 8;    // fp16 state^T row stride
 constexpr int ONES = 16;      // k^T row holding 1.0 (second factor of linear features)
 constexpr int SCALE_TOP = 13; // the scaled fp16 state stays below 2^(SCALE_TOP + 1)
@@ -170,11 +170,12 @@ __device__ __forceinline__ float gsum_pow(float lg, int n) {
   return ln == 0.f ? (float)n : expm1f(ln * (float)n) / expm1f(ln);
 }
 
-// LDS of the main pass.  vt is v^T with the 8-position groups of row `col`
-// XOR-swizzled by (col / 8) % 8, so that the transposing writes of a
-// wavefront spread over all banks while 8 consecutive positions stay
-// contiguous for 16-byte reads.  With the sliding window (SWA) the row-major
-// k and v^T keep the previous chunk too (NB = 2 buffers).
+// fp16 row stride of the row-major v chunk in LDS (8 halves of padding keep
+// the transposing reads of four consecutive rows on distinct banks)
+template <int NT> constexpr int vrow() { return 16 * NT + 8; }
+
+// LDS of the main pass.  With the sliding window (SWA) the row-major k and v
+// keep the previous chunk too (NB = 2 buffers).
 template <int NT, int SWA>
 struct Smem {
   static constexpr int DV = 16 * NT;
@@ -182,7 +183,7 @@ struct Smem {
   alignas(16) half_t qh[C][QH];          // q, row-major
   alignas(16) half_t kh[NB][C][QH];      // k, row-major
   alignas(16) half_t kt[DK + 1][KT];     // k^T; row ONES = 1
-  alignas(16) half_t vt[NB][DV][VT];     // v^T, swizzled
+  alignas(16) half_t vh[NB][C][vrow<NT>()];  // v, row-major
   alignas(16) half_t tt[DV + 1][TT];     // scaled state^T; row DV: denominator state
   alignas(16) float t0[DV];              // constant row of the state (sum of v)
   alignas(16) float vpart[NTHR];         // partial column sums of v
@@ -197,8 +198,27 @@ struct Smem {
 // operand registers.
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Column of v^T row `col` holding position t (see Smem).
-__device__ __forceinline__ int vt_pos(int col, int t) { return ((((t >> 3) ^ (col >> 3)) & 7) << 3) | (t & 7); }
+// Transposing LDS read (ds_read_b64_tr_b16): rows r0 .. r0 + 3 of column
+// c0 + (lane % 16) of the row-major fp16 array at `base` (row stride ld).
+// Within each 16-lane block lane t receives element t % 4 of the 4-element
+// segments addressed by lanes t / 4 + 4i, so lane j points at row r0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3.  Every lane of a block must take part.
+__device__ __forceinline__ uint2 tr4(const half_t* base, int r0, int c0, int ld) {
+  const int j = threadIdx.x & 15;
+  const half_t* a = base + (r0 + (j >> 2)) * ld + c0 + 4 * (j & 3);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a);
+  return __builtin_bit_cast(uint2, v);
+}
+// matrix operand with K = rows r0 .. r0 + 7 of column c0 + (lane % 16)
+__device__ __forceinline__ f16x8 tr8(const half_t* base, int r0, int c0, int ld) {
+  const uint2 a = tr4(base, r0, c0, ld), b = tr4(base, r0 + 4, c0, ld);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// K = rows r0 .. r0 + 3 and r0 + 16 .. r0 + 19 (the same rows of two 16-row tiles)
+__device__ __forceinline__ f16x8 tr44(const half_t* base, int r0, int c0, int ld) {
+  const uint2 a = tr4(base, r0, c0, ld), b = tr4(base, r0 + 16, c0, ld);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
 
 __device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -252,9 +272,8 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// Thread -> (position, 8 columns) of the v loads: a wavefront covers 8
-// positions x 8 column groups per load (DV = 64) so that its transposing LDS
-// writes hit distinct banks after the swizzle.  Threads 0..127 load q (when
+// Thread -> (position, 8 columns) of the v loads: consecutive threads take
+// consecutive 16-byte pieces of the chunk's rows.  Threads 0..127 load q (when
 // asked), threads 128..255 load k, 8 elements each.
 template <int NT>
 __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf) {
@@ -277,10 +296,10 @@ __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too
   }
 }
 
-// One chunk from the prefetch registers into LDS as fp16: k^T and v^T, and
-// (when given) the row-major copies of q and k.
+// One chunk from the prefetch registers into LDS as fp16: k^T and the
+// row-major v, and (when given) the row-major copies of q and k.
 template <int NT>
-__device__ __forceinline__ void store_chunk(half_t (*kt)[KT], half_t (*vt)[VT], half_t (*qh)[QH], half_t (*kh)[QH],
+__device__ __forceinline__ void store_chunk(half_t (*kt)[KT], half_t* vh, half_t (*qh)[QH], half_t (*kh)[QH],
                                             const Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
@@ -298,10 +317,7 @@ __device__ __forceinline__ void store_chunk(half_t (*kt)[KT], half_t (*vt)[VT], 
   for (int i = 0; i < Prefetch<NT>::NV; ++i) {
     const int uu = tid + NTHR * i;
     const int jj = uu / (DV / 8), c8 = uu % (DV / 8);
-    const f16x8 e = __builtin_bit_cast(f16x8, h8_from_bf8(pf.v[i]));
-    const int pc = vt_pos(8 * c8, jj);  // the same for the 8 columns of this group
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vt[8 * c8 + c][pc] = e[c];
+    *reinterpret_cast<uint4*>(vh + jj * vrow<NT>() + 8 * c8) = h8_from_bf8(pf.v[i]);
   }
 }
 
@@ -332,12 +348,12 @@ __device__ __forceinline__ f16x8 ones8() {
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
 // (every column of a tz tile holds it).
 template <int NT, int DEC = 0>
-__device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t (*vt)[VT],
+__device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t* vh,
                                              f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3], const int (&ia)[3],
                                              const int (&ib)[3], const f16x8* wk = nullptr) {
   constexpr int H = NT / 2;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
-  const int n2 = (w & 1) * H;  // first column tile of slot 2
+  const bool upper = (w & 1) != 0;  // slot 2 holds the upper half of the column tiles
   const f16x8 ones = ones8();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -349,29 +365,56 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
       a[ms] = x * y;
       if constexpr (DEC) a[ms] *= wk[ks];  // decayed variant: each key's weight
     }
-    f16x8 bv[NT], bv2[H];
+    f16x8 bv[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int col = 16 * n + r16;
-      bv[n] = *reinterpret_cast<const f16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
-    }
-#pragma unroll
-    for (int n = 0; n < H; ++n) {
-      const int col = 16 * (n2 + n) + r16;
-      bv2[n] = *reinterpret_cast<const f16x8*>(&vt[col][vt_pos(col, 32 * ks + 8 * g)]);
-    }
+    for (int n = 0; n < NT; ++n) bv[n] = tr8(vh, 32 * ks + 8 * g, 16 * n, vrow<NT>());
 #pragma unroll
     for (int n = 0; n < NT; ++n) tacc[n] = mfma(a[0], bv[n], tacc[n]);
 #pragma unroll
     for (int n = 0; n < NT; ++n) tacc[NT + n] = mfma(a[1], bv[n], tacc[NT + n]);
+    if (upper) {  // uniform branch (scalar wavefront index)
 #pragma unroll
-    for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(a[2], bv2[n], tacc[2 * NT + n]);
+      for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(a[2], bv[H + n], tacc[2 * NT + n]);
+    } else {
+#pragma unroll
+      for (int n = 0; n < H; ++n) tacc[2 * NT + n] = mfma(a[2], bv[n], tacc[2 * NT + n]);
+    }
     tz[0] = mfma(a[0], ones, tz[0]);
     tz[1] = mfma(a[1], ones, tz[1]);
     if ((w & 1) == 0) tz[2] = mfma(a[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
     // keep the operands of the two K-steps from being live at once
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// This thread's share of the column sums of the chunk's v (row-major in LDS):
+// column tid % DV, rows part * SPAN .. + SPAN - 1 with part = tid / DV, read
+// four rows at a time with the transposing load (a 16-lane block covers 16
+// consecutive columns of one part).  Decayed variant: row t weighs
+// gamma^(n-1-t), rows past n none.
+template <int NT, int DEC>
+__device__ __forceinline__ float vsum_part(const half_t* vh, int n, float lg) {
+  constexpr int DV = 16 * NT;
+  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
+  const int tid = threadIdx.x, col = tid % DV, part = tid / DV;
+  float vs = 0.f;
+  if (part < PARTS) {  // whole wavefronts (DV divides 64 or is a multiple of 32)
+#pragma unroll
+    for (int j = 0; j < SPAN; j += 4) {
+      const f16x4 x = __builtin_bit_cast(f16x4, tr4(vh, part * SPAN + j, col & ~15, vrow<NT>()));
+      if constexpr (DEC) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = part * SPAN + j + e;
+          vs = __builtin_fmaf((float)x[e], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
+        }
+      } else {
+        vs = __builtin_amdgcn_fdot2(f16x2{x[0], x[1]}, f16x2{1, 1}, vs, false);
+        vs = __builtin_amdgcn_fdot2(f16x2{x[2], x[3]}, f16x2{1, 1}, vs, false);
+      }
+    }
+  }
+  return vs;
 }
 
 // DPP move of a lane value (row_mask / bank_mask all, out-of-row sources read 0).
@@ -691,10 +734,10 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   if constexpr (SWA) {
     // the window of the segment's first chunk reaches into the chunk before
     if (tok_begin > 0) {
-      store_chunk<NT>(S.kt, S.vt[1], nullptr, S.kh[1], pp);
+      store_chunk<NT>(S.kt, &S.vh[1][0][0], nullptr, S.kh[1], pp);
     } else {
       for (int j = tid; j < C * QH / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.kh[1][0][0])[j] = 0u;
-      for (int j = tid; j < DV * VT / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.vt[1][0][0])[j] = 0u;
+      for (int j = tid; j < C * vrow<NT>() / 2; j += NTHR) reinterpret_cast<uint32_t*>(&S.vh[1][0][0])[j] = 0u;
     }
   }
   __syncthreads();
@@ -705,7 +748,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   float down, up;
   int e = state_scale(S.wmax, down, up);
   publish_state<NT>(S.tt, tacc, tz, e, down);
-  if (tok_begin < tok_end) store_chunk<NT>(S.kt, S.vt[0], S.qh, S.kh[0], pf);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt, &S.vh[0][0][0], S.qh, S.kh[0], pf);
   int cur = 0;  // buffer of the current chunk's k and v^T (the other: previous chunk)
 
   const f16x8 ones = ones8();
@@ -730,29 +773,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 
     // ---- constant row of the state: column sums of v over the chunk, in
     // PARTS partial sums per column (order within a row is irrelevant)
-    {
-      const int col = tid % DV, part = tid / DV;
-      float vs = 0.f;
-      if (part < PARTS) {
-#pragma unroll
-        for (int j = 0; j < SPAN; j += 8) {
-          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[cur][col][part * SPAN + j]);
-          if constexpr (DEC) {
-            // weight gamma^(n-1-t) of position t (undoing the column swizzle)
-#pragma unroll
-            for (int k2 = 0; k2 < 8; ++k2) {
-              const int t = vt_pos(col, part * SPAN + j + k2);
-              vs = __builtin_fmaf((float)x[k2], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
-            }
-          } else {
-#pragma unroll
-            for (int k2 = 0; k2 < 8; k2 += 2)
-              vs = __builtin_amdgcn_fdot2(f16x2{x[k2], x[k2 + 1]}, f16x2{1, 1}, vs, false);
-          }
-        }
-      }
-      S.vpart[tid] = vs;
-    }
+    S.vpart[tid] = vsum_part<NT, DEC>(&S.vh[cur][0][0], n, lg);
 
     // ---- readout of the state before the chunk, transposed (value columns x
     // positions): acc[nn][i] is column 16nn + 4g + i of position `pos`; every
@@ -852,9 +873,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[cur][col][vt_pos(col, 32 * kb + 4 * g)]);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[cur][col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
-            const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            const f16x8 va = tr44(&S.vh[cur][0][0], 32 * kb + 4 * g, 16 * nn, vrow<NT>());
             acc[nn] = mfma(va, ph, acc[nn]);
             acc[nn] = mfma(va, pl, acc[nn]);
           }
@@ -976,9 +995,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(&S.vt[b][col][vt_pos(col, 32 * kb + 4 * g)]);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(&S.vt[b][col][vt_pos(col, 32 * kb + 16 + 4 * g)]);
-            const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            const f16x8 va = tr44(&S.vh[b][0][0], 32 * kb + 4 * g, 16 * nn, vrow<NT>());
             accs[nn] = mfma(va, ph, accs[nn]);
             accs[nn] = mfma(va, pl, accs[nn]);
           }
@@ -1010,10 +1027,10 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           const int key = 32 * ks + 8 * g + i;
           wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
         }
-      update_chunk<NT, 1>(S.kt, S.vt[cur], tacc, tz, ia, ib, wk);
+      update_chunk<NT, 1>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib, wk);
       z0 = gn * z0 + gsum_pow(lg, n);
     } else {
-      update_chunk<NT>(S.kt, S.vt[cur], tacc, tz, ia, ib);
+      update_chunk<NT>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib);
       z0 += (float)n;
     }
     post_max<NT>(S.wmax, tacc, tz);
@@ -1027,7 +1044,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     e = state_scale(S.wmax, down, up);
     publish_state<NT>(S.tt, tacc, tz, e, down);
     if constexpr (SWA) cur ^= 1;  // the next chunk replaces the previous one
-    if (tn < tok_end) store_chunk<NT>(S.kt, S.vt[cur], S.qh, S.kh[cur], pf);
+    if (tn < tok_end) store_chunk<NT>(S.kt, &S.vh[cur][0][0], S.qh, S.kh[cur], pf);
   }
 
   // ---- the last segment writes the final state
@@ -1049,7 +1066,7 @@ template <int NT>
 struct StateSmem {
   static constexpr int DV = 16 * NT;
   alignas(16) half_t kt[2][DK + 1][KT];
-  alignas(16) half_t vt[2][DV][VT];
+  alignas(16) half_t vh[2][C][vrow<NT>()];
   alignas(16) float vpart[NTHR];
   alignas(16) float t0[DV];
   alignas(16) float zf[NF];
@@ -1093,7 +1110,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 
   const int col = tid % DV, part = tid / DV;
   float vs = 0.f;  // this thread's share of the column sums of v (constant row)
-  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], S.vt[0], nullptr, nullptr, p0);
+  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], &S.vh[0][0][0], nullptr, nullptr, p0);
 
   // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare`
   // receives t + 3C: three chunks in flight from HBM while one is updated
@@ -1106,19 +1123,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
       // the carried sums decay over the chunk; keys weigh gamma^(n-1-key)
       const int n = min(C, tok_end - t);
       const float gn = gpow(lg, (float)n);
-      vs *= gn;
+      vs = gn * vs + vsum_part<NT, 1>(&S.vh[buf][0][0], n, lg);
       z0 = gn * z0 + gsum_pow(lg, n);
-      if (part < PARTS) {
-#pragma unroll
-        for (int j = 0; j < SPAN; j += 8) {
-          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int tp = vt_pos(col, part * SPAN + j + e);
-            vs = __builtin_fmaf((float)x[e], tp < n ? gpow(lg, (float)(n - 1 - tp)) : 0.f, vs);
-          }
-        }
-      }
 #pragma unroll
       for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
 #pragma unroll
@@ -1131,19 +1137,12 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
           const int key = 32 * ks + 8 * g + i;
           wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
         }
-      update_chunk<NT, 1>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib, wk);
+      update_chunk<NT, 1>(S.kt[buf], &S.vh[buf][0][0], tacc, tz, ia, ib, wk);
     } else {
-      if (part < PARTS) {
-#pragma unroll
-        for (int j = 0; j < SPAN; j += 8) {
-          const f16x8 x = *reinterpret_cast<const f16x8*>(&S.vt[buf][col][part * SPAN + j]);
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) vs = __builtin_amdgcn_fdot2(f16x2{x[e], x[e + 1]}, f16x2{1, 1}, vs, false);
-        }
-      }
-      update_chunk<NT>(S.kt[buf], S.vt[buf], tacc, tz, ia, ib);
+      vs += vsum_part<NT, 0>(&S.vh[buf][0][0], C, 0.f);
+      update_chunk<NT>(S.kt[buf], &S.vh[buf][0][0], tacc, tz, ia, ib);
     }
-    if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], S.vt[buf ^ 1], nullptr, nullptr, next);
+    if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], &S.vh[buf ^ 1][0][0], nullptr, nullptr, next);
   };
   for (int t = tok_begin; t < tok_end; t += 4 * C) {
     step(t, 0, p1, p3);
