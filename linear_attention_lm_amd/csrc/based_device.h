@@ -78,4 +78,14 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Segment records of the linear attention's state (workspace of the chunked
+// forward, read by the backward too): the 160 x dv compact state is stored in
+// the order of the matrix-core accumulator fragments, so that a lane moves its
+// four values of a 16 x 16 tile with one 16-byte access.  Element (r, c):
+// tile (r / 16, c / 16), lane 16 ((r % 16) / 4) + c % 16, element r % 4.  The
+// constant row (index 160) follows as a plain row of dv values.
+__host__ __device__ constexpr size_t record_offset(int r, int c, int dv) {
+  return ((size_t)((r >> 4) * (dv >> 4) + (c >> 4)) * 64 + 16 * ((r & 15) >> 2) + (c & 15)) * 4 + (r & 3);
+}
+
 }  // namespace based

@@ -195,7 +195,7 @@ struct Params {
   float* Dy;            // dy . y per position
   float* den; float* h; // per position, from the query pass
   float* gq; float* gk; float* gv;
-  const float* frec;    // [BH][nseg][NFC + 1][dvf] forward records (record s + 1: segment s)
+  const float* frec;    // [BH][nseg] forward records of (NFC + 1) dvf floats, record_offset layout (record s + 1: segment s)
   const float* frecz;   // [BH][nseg][NFC + 1]
   float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
   int L, dvf, nslice, nseg, seg_chunks;
@@ -400,7 +400,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[j][nn][i] += p.frec[rec * p.dvf + s * SW + 16 * nn + 4 * g + i];
+            for (int i = 0; i < 4; ++i)
+              acc[j][nn][i] += p.frec[(rec - slot) * p.dvf + record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf)];
           z += p.frecz[rec];
         }
         zacc[j] = z;

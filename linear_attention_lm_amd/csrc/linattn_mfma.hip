@@ -151,7 +151,7 @@ __device__ __forceinline__ float compact_from_phi(const float* S, int r, int c, 
 struct Params {
   const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
   const float* S_in; const float* z_in; float* S_out; float* z_out;
-  float* ws;        // [BH][nseg][NF+1][DV] compact state records (row NF = constant row)
+  float* ws;        // [BH][nseg] compact state records of (NF+1) DV floats (record_offset; row NF = constant)
   float* wsz;       // [BH][nseg][NF+1] likewise for z (entry NF = constant: token count)
   int L, nseg, seg_chunks;
   float* y_swa;     // sliding-window softmax output of the fused layer pass
@@ -530,9 +530,9 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
       for (int i = 0; i < 4; ++i) zf[16 * mt[ms] + 4 * g + i] = tz[ms][i];
 }
 
-// Initial owned state tiles: from a compact state in the workspace
-// ([NF+1][DV], row NF = constant), else from the caller's phi-layout S_in,
-// else zero.
+// Initial owned state tiles: from a compact state record in the workspace
+// (fragment order, see record_offset; one 16-byte load per owned tile), else
+// from the caller's phi-layout S_in, else zero.
 template <int NT>
 __device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW],
                                            int ncompact = 1, const float* wts = nullptr) {
@@ -542,12 +542,13 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
   for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, n;
     pair_mn<NT>(w, j, m, n);
-    const int c = 16 * n + r16;
+    if (compact) {
+      const float4 x = *reinterpret_cast<const float4*>(compact + record_offset(16 * m + 4 * g, 16 * n + r16, DV));
+      tacc[j] = f32x4{x.x, x.y, x.z, x.w} * (wts ? wts[0] : 1.f);
+    } else {
+      const int c = 16 * n + r16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * m + 4 * g + i;
-      tacc[j][i] = compact ? compact[(size_t)r * DV + c] * (wts ? wts[0] : 1.f)
-                           : (Sin ? compact_from_phi(Sin, r, c, DV) : 0.f);
+      for (int i = 0; i < 4; ++i) tacc[j][i] = Sin ? compact_from_phi(Sin, 16 * m + 4 * g + i, c, DV) : 0.f;
     }
   }
   // further records (consecutive, (NF + 1) * DV floats apart; at most
@@ -560,9 +561,8 @@ __device__ __forceinline__ void init_state(const float* compact, const float* Si
       for (int j = 0; j < Own<NT>::PPW; ++j) {
         int m, n;
         pair_mn<NT>(w, j, m, n);
-        const int c = 16 * n + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tacc[j][i] += (wts ? wts[k] : 1.f) * rc[(size_t)(16 * m + 4 * g + i) * DV + c];
+        const float4 x = *reinterpret_cast<const float4*>(rc + record_offset(16 * m + 4 * g, 16 * n + r16, DV));
+        tacc[j] += f32x4{x.x, x.y, x.z, x.w} * (wts ? wts[k] : 1.f);
       }
     }
   }
@@ -601,8 +601,8 @@ __device__ __forceinline__ void write_compact(const float* t0, const float* zf, 
   for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, nn;
     pair_mn<NT>(w, j, m, nn);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * nn + r16] = tacc[j][i];
+    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, 16 * nn + r16, DV)) =
+        make_float4(tacc[j][0], tacc[j][1], tacc[j][2], tacc[j][3]);
   }
   for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = t0[c];
   for (int r = tid; r < NF; r += NTHR) dz[r] = zf[r];
