@@ -273,8 +273,10 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 
 // Thread -> (position, 8 columns) of the v loads: consecutive threads take
-// consecutive 16-byte pieces of the chunk's rows.  Threads 0..127 load q (when
-// asked), threads 128..255 load k, 8 elements each.
+// consecutive 16-byte pieces of the chunk's rows.  Threads 0..127 load q (k
+// again when q is not wanted), threads 128..255 load k, 8 elements each:
+// every wavefront issues the same loads, so the compiler can count the loads
+// in flight exactly and a deeper prefetch is not drained early.
 template <int NT>
 __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf) {
   constexpr int DV = 16 * NT;
@@ -282,11 +284,7 @@ __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too
   {
     const int u = tid & 127, j = u >> 1, h = u & 1;
     const int off = ((t0 + j) * DK + 8 * h) * 2;
-    if (tid < 128) {
-      if (q_too) pf.qk = bload(r.q, off);
-    } else {
-      pf.qk = bload(r.k, off);
-    }
+    pf.qk = bload(wave_index() < 2 && q_too ? r.q : r.k, off);
   }
 #pragma unroll
   for (int i = 0; i < Prefetch<NT>::NV; ++i) {
@@ -1089,9 +1087,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   // the first three chunks from HBM first, overlapping the state set-up
   const HeadRsrc rs = head_rsrc(p, bh, DV);
   Prefetch<NT> p0, p1, p2, p3;
-  if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, false, p0);
-  if (tok_begin + C < tok_end) load_chunk<NT>(rs, tok_begin + C, false, p1);
-  if (tok_begin + 2 * C < tok_end) load_chunk<NT>(rs, tok_begin + 2 * C, false, p2);
+  load_chunk<NT>(rs, tok_begin, false, p0);
+  load_chunk<NT>(rs, tok_begin + C, false, p1);
+  load_chunk<NT>(rs, tok_begin + 2 * C, false, p2);
   const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
   f32x4 tacc[Own<NT>::PPW];
@@ -1110,16 +1108,21 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 
   const int col = tid % DV, part = tid / DV;
   float vs = 0.f;  // this thread's share of the column sums of v (constant row)
-  if (tok_begin < tok_end) store_chunk<NT>(S.kt[0], &S.vh[0][0][0], nullptr, nullptr, p0);
+  store_chunk<NT>(S.kt[0], &S.vh[0][0][0], nullptr, nullptr, p0);
 
   // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare`
-  // receives t + 3C: three chunks in flight from HBM while one is updated
+  // receives t + 3C: three chunks in flight from HBM while one is updated.
+  // Loads and LDS stores run in every step, also past the segment's end
+  // (range-checked reads, buffers nobody reads), so the number of loads in
+  // flight is the same on every path; only the update is skipped there.
   const float lg = DEC ? decay_lg2(p, bh) : 0.f;
   const int lane = tid & 63, g = lane >> 4;
   auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
     __syncthreads();
-    if (t + 3 * C < tok_end) load_chunk<NT>(rs, t + 3 * C, false, spare);
-    if constexpr (DEC) {
+    load_chunk<NT>(rs, t + 3 * C, false, spare);
+    if (t >= tok_end) {
+      // past the segment: nothing to add
+    } else if constexpr (DEC) {
       // the carried sums decay over the chunk; keys weigh gamma^(n-1-key)
       const int n = min(C, tok_end - t);
       const float gn = gpow(lg, (float)n);
@@ -1142,13 +1145,13 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
       vs += vsum_part<NT, 0>(&S.vh[buf][0][0], C, 0.f);
       update_chunk<NT>(S.kt[buf], &S.vh[buf][0][0], tacc, tz, ia, ib);
     }
-    if (t + C < tok_end) store_chunk<NT>(S.kt[buf ^ 1], &S.vh[buf ^ 1][0][0], nullptr, nullptr, next);
+    store_chunk<NT>(S.kt[buf ^ 1], &S.vh[buf ^ 1][0][0], nullptr, nullptr, next);
   };
   for (int t = tok_begin; t < tok_end; t += 4 * C) {
     step(t, 0, p1, p3);
-    if (t + C < tok_end) step(t + C, 1, p2, p0);
-    if (t + 2 * C < tok_end) step(t + 2 * C, 0, p3, p1);
-    if (t + 3 * C < tok_end) step(t + 3 * C, 1, p0, p2);
+    step(t + C, 1, p2, p0);
+    step(t + 2 * C, 0, p3, p1);
+    step(t + 3 * C, 1, p0, p2);
   }
   if constexpr (!DEC) z0 += (float)(tok_end - tok_begin);
   __syncthreads();
