@@ -342,29 +342,32 @@ def bench_decay(lal, cfg, steps, warmup, nbuf=8):
             "traffic_bytes_per_call": load_traffic("decay")}
 
 
-def bench_decode(lal, cfg, warmup=5):
-    """Prefill (untimed), then cfg.steps decode steps timed as one block."""
+def bench_decode(lal, cfg, warmup=5, decay=False):
+    """Prefill (untimed), then cfg.steps decode steps timed as one block
+    (decay: the decayed linear attention, per-head decays from
+    synth.decay_rates; same bytes per step)."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
-    _, _, st = lal.decode_init(qc.cuda(), kc.cuda(), vc.cuda(), cfg.window)
+    g = synth.decay_rates(cfg.H).cuda() if decay else None
+    _, _, st = lal.decode_init(qc.cuda(), kc.cuda(), vc.cuda(), cfg.window, gamma=g)
     del qc, kc, vc
     qd, kd, vd = qs.cuda(), ks.cuda(), vs.cuda()
     B, H, dv = cfg.B, cfg.H, cfg.dv
     y_lin = torch.empty(B, H, dv, device="cuda")
     y_swa = torch.empty(B, H, dv, device="cuda")
     for s in range(warmup):  # advances the state; the timed steps continue from it
-        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa)
+        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa, gamma=g)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = cfg.steps - warmup
     t0.record()
     for s in range(warmup, cfg.steps):
-        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa)
+        lal.decode_step(st, qd[s], kd[s], vd[s], y_lin=y_lin, y_swa=y_swa, gamma=g)
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / n
     byts = decode_bytes(dv, cfg.window) * B * H
     return {
-        "workload": "decode", "sequences": B, "heads": H, "context": cfg.ctx, "steps_timed": n,
+        "workload": "decode (decayed)" if decay else "decode", "sequences": B, "heads": H, "context": cfg.ctx, "steps_timed": n,
         "us_per_step": us, "tokens_per_s": B / (us * 1e-6), "hbm_gbs": byts / (us * 1e-6) / 1e9,
         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": byts,
     }
@@ -564,7 +567,7 @@ def main():
     main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
-    extra, decode, separate, backward, conv, decay = [], None, None, None, None, None
+    extra, decode, separate, backward, conv, decay, decode_decay = [], None, None, None, None, None, None
     if not args.no_extra:
         backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
         del bsets
@@ -586,6 +589,8 @@ def main():
         decode = bench_decode(lal, synth.DECODE_CONFIG)
         decode["traffic_bytes_per_step"] = load_traffic("decode")
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+        decode_decay = bench_decode(lal, synth.DECODE_CONFIG, decay=True)
+        print(f"[bench] decode (decayed): {decode_decay['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(cfg)
 
     # the step is one operation (state-only pass + segment scan + fused main pass)
@@ -612,6 +617,7 @@ def main():
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "decode": decode,
+        "decode_decay": decode_decay,
     }
     print(json.dumps(out))
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 5
+#define BASED_ABI_VERSION 6
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -288,6 +288,25 @@ int based_decode_step(const void* q, const void* k, const void* v,
                       float* y_lin, float* y_swa,
                       int B, int H, int d_k, int d_v, int window, float scale, int dtype,
                       void* stream);
+
+/*
+ * based_decode_step for the decayed linear attention (the train README's
+ * optional decay strategy, read as a per-head factor on the state, as in
+ * based_linattn_decay_fwd):
+ *   S <- gamma[h] S + phi(k) v^T;  z <- gamma[h] z + phi(k);
+ *   y_lin = phi(q)^T S / phi(q)^T z
+ * gamma: [H] fp32 device pointer, 0 < gamma <= 1 (not checked), read only,
+ * shared by the batch; it must not overlap any output.  The window attention
+ * and the ring are as in based_decode_step.  A state prefilled by
+ * based_linattn_decay_fwd's S_out / z_out over the context continues the
+ * decayed forward exactly.  Both dtypes, d_v in {16..128}.  Errors as
+ * based_decode_step, and BASED_ERR_NULL for a null gamma.
+ */
+int based_decode_step_decay(const void* q, const void* k, const void* v, const float* gamma,
+                            float* S, float* z, void* ring_k, void* ring_v, int32_t* pos,
+                            float* y_lin, float* y_swa,
+                            int B, int H, int d_k, int d_v, int window, float scale, int dtype,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,7 @@ _SIGNATURES = {
     "based_swa_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
     "based_baseconv_fwd": (_i, [_vp] * 5 + [_i] * 5 + [_vp]),
     "based_linattn_decay_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
+    "based_decode_step_decay": (_i, [_vp] * 11 + [_i] * 5 + [_f, _i, _vp]),
 }
 
 
@@ -314,13 +315,19 @@ def decode_prefill(k, v, state: DecodeState) -> None:
                                     B, H, L, dk, v.shape[-1], state.window, _dtype_code(k), _stream()))
 
 
-def decode_init(q, k, v, window: int = 64):
+def decode_init(q, k, v, window: int = 64, gamma=None):
     """Consume a context (q, k, v [B,H,L,.]): returns (y_lin, y_swa, state)
     where the outputs are the context's own layer outputs and ``state`` is
-    ready for :func:`decode_step` at position L."""
+    ready for :func:`decode_step` at position L.  With a per-head decay gamma
+    [H] the linear attention is the decayed one (then continue with
+    decode_step(..., gamma=gamma))."""
     B, H, L, _ = k.shape
     dv = v.shape[-1]
-    y_lin, y_swa, S, z = layer_fwd(q, k, v, window, return_state=True)
+    if gamma is None:
+        y_lin, y_swa, S, z = layer_fwd(q, k, v, window, return_state=True)
+    else:
+        y_lin, S, z = linattn_decay_fwd(q, k, v, gamma, return_state=True)
+        y_swa = swa_fwd(q, k, v, window)
     st = DecodeState(S, z, torch.zeros(B, H, window, DK, device=k.device, dtype=k.dtype),
                      torch.zeros(B, H, window, dv, device=k.device, dtype=k.dtype),
                      torch.zeros(B, device=k.device, dtype=torch.int32))
@@ -328,17 +335,23 @@ def decode_init(q, k, v, window: int = 64):
     return y_lin, y_swa, st
 
 
-def decode_step(state: DecodeState, q, k, v, scale: float = 1.0, *, y_lin=None, y_swa=None):
+def decode_step(state: DecodeState, q, k, v, scale: float = 1.0, *, y_lin=None, y_swa=None, gamma=None):
     """One token per sequence: q, k [B,H,16], v [B,H,dv].  Updates ``state`` in
-    place (including pos += 1) and returns (y_lin, y_swa) [B,H,dv] fp32."""
+    place (including pos += 1) and returns (y_lin, y_swa) [B,H,dv] fp32.  With
+    gamma (fp32 [H]) the state decays: S <- gamma S + phi(k) v^T, likewise z."""
     B, H, dk = q.shape
     dv = v.shape[-1]
-    _dev(q, k, v, state.S, state.z, state.ring_k, state.ring_v, state.pos, y_lin, y_swa)
+    if gamma is not None and (gamma.shape != (H,) or gamma.dtype != torch.float32):
+        raise ValueError("gamma must be fp32 [H]")
+    _dev(q, k, v, state.S, state.z, state.ring_k, state.ring_v, state.pos, y_lin, y_swa, gamma)
     if y_lin is None:
         y_lin = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
     if y_swa is None:
         y_swa = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
-    _check(_lib().based_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(state.S), _ptr(state.z), _ptr(state.ring_k),
-                                 _ptr(state.ring_v), _ptr(state.pos), _ptr(y_lin), _ptr(y_swa), B, H, dk, dv,
-                                 state.window, float(scale), _dtype_code(q), _stream()))
+    common = (_ptr(state.S), _ptr(state.z), _ptr(state.ring_k), _ptr(state.ring_v), _ptr(state.pos), _ptr(y_lin),
+              _ptr(y_swa), B, H, dk, dv, state.window, float(scale), _dtype_code(q), _stream())
+    if gamma is None:
+        _check(_lib().based_decode_step(_ptr(q), _ptr(k), _ptr(v), *common))
+    else:
+        _check(_lib().based_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *common))
     return y_lin, y_swa

@@ -281,9 +281,9 @@ BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, v
                                    (hipStream_t)stream));
 }
 
-BASED_API int based_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* ring_k,
-                                void* ring_v, int32_t* pos, float* y_lin, float* y_swa, int B, int H, int d_k,
-                                int d_v, int window, float scale, int dtype, void* stream) {
+static int decode_step_impl(const void* q, const void* k, const void* v, const float* gamma, float* S, float* z,
+                            void* ring_k, void* ring_v, int32_t* pos, float* y_lin, float* y_swa, int B, int H,
+                            int d_k, int d_v, int window, float scale, int dtype, void* stream) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
   if (B < 1 || H < 1) return BASED_ERR_SHAPE;
   if ((long long)B * H > (1LL << 30) || B > 0x7fffffff) return BASED_ERR_SHAPE;
@@ -305,6 +305,27 @@ BASED_API int based_decode_step(const void* q, const void* k, const void* v, flo
     for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
       if (overlap(outs[i], outs[j])) return BASED_ERR_ALIAS;
   }
-  based::DecodeArgs a{q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_v, window, scale};
+  if (gamma) {
+    const Span g = span(gamma, (size_t)H * 4);
+    for (const Span& o : outs)
+      if (overlap(o, g)) return BASED_ERR_ALIAS;
+  }
+  based::DecodeArgs a{q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_v, window, scale, gamma};
   return status_of(based::launch_decode_step(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
+BASED_API int based_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* ring_k,
+                                void* ring_v, int32_t* pos, float* y_lin, float* y_swa, int B, int H, int d_k,
+                                int d_v, int window, float scale, int dtype, void* stream) {
+  return decode_step_impl(q, k, v, nullptr, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_k, d_v, window, scale,
+                          dtype, stream);
+}
+
+BASED_API int based_decode_step_decay(const void* q, const void* k, const void* v, const float* gamma, float* S,
+                                      float* z, void* ring_k, void* ring_v, int32_t* pos, float* y_lin, float* y_swa,
+                                      int B, int H, int d_k, int d_v, int window, float scale, int dtype,
+                                      void* stream) {
+  if (!gamma) return BASED_ERR_NULL;
+  return decode_step_impl(q, k, v, gamma, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_k, d_v, window, scale,
+                          dtype, stream);
 }

@@ -6,6 +6,9 @@
 // attention over the last 64 tokens):
 //   S += phi(k) v^T, z += phi(k), y_lin = phi(q)^T S / phi(q)^T z
 //   ring slot t mod W <- (k, v); y_swa = softmax window attention over t-W+1..t.
+// Decayed variant (train README's decay strategy, read as a per-head factor
+// on the state): S <- gamma_h S + phi(k) v^T, z <- gamma_h z + phi(k); without
+// gamma the factor is 1 and the update is the same arithmetic as above.
 //
 // The step streams the 273 x d_v fp32 state through once (read, update,
 // write back) and is bound by HBM bandwidth.  Layout of the work: one
@@ -73,7 +76,8 @@ template <typename T, int DV>
 __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ S,
     float* __restrict__ z, T* __restrict__ ring_k, T* __restrict__ ring_v, int32_t* __restrict__ pos,
-    float* __restrict__ y_lin, float* __restrict__ y_swa, int H, int window, float scale) {
+    float* __restrict__ y_lin, float* __restrict__ y_swa, int H, int window, float scale,
+    const float* __restrict__ gamma) {
   constexpr int CG = DV / 4;                     // lanes per state row (4 columns each)
   constexpr int RG = 64 / CG;                    // rows per wavefront instruction
   constexpr int NI = (DPHI + RG - 1) / RG;       // state rows per lane
@@ -103,6 +107,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
 
   for (int h = wave; h < H; h += nw) {
     const size_t bh = (size_t)b * H + h;
+    const float gm = gamma ? gamma[h] : 1.f;  // state decay of the head (gm * x = x exactly when 1)
     const auto rS = rsrc(S + bh * DPHI * DV, DPHI * DV * 4);
     const auto rZ = rsrc(z + bh * DPHI, DPHI * 4);
     const auto rK = rsrc(ring_k + bh * (size_t)window * DK, window * DK * ES);
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
           pq = qk_s[wave][0][a] * qk_s[wave][0][bb] * INV_SQRT2;
         }
         phi_s[wave][f] = make_float2(pk, pq);
-        const float zn = zl[j] + pk;
+        const float zn = gm * zl[j] + pk;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zn), rZ, lane * 4, 256 * j, 0);
         den += pq * zn;
       }
@@ -238,7 +243,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
           const int f = rg + RG * (bt * NB + i);
           if (active && f < DPHI) {
             const float2 ph = phi_s[wave][f];
-            const float4 sn = fma4(ph.x, vr, buf[i]);
+            const float4 sd = make_float4(gm * buf[i].x, gm * buf[i].y, gm * buf[i].z, gm * buf[i].w);
+            const float4 sn = fma4(ph.x, vr, sd);
             bstore_f4(sn, rS, voff_s, RG * (bt * NB + i) * DV * 4);
             num = fma4(ph.y, sn, num);
           }
@@ -295,7 +301,7 @@ hipError_t launch_step(const DecodeArgs& a, hipStream_t s) {
   const int nw = a.H < MAXW ? a.H : MAXW;
   hipLaunchKernelGGL((decode_step_kernel<T, DV>), dim3(a.B), dim3(64 * nw), 0, s, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, a.S, a.z, (T*)a.ring_k, (T*)a.ring_v, a.pos, a.y_lin, a.y_swa, a.H, a.window,
-                     a.scale);
+                     a.scale, a.gamma);
   return hipGetLastError();
 }
 

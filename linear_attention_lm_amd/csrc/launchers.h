@@ -79,6 +79,7 @@ struct DecodeArgs {
   float* S; float* z; void* ring_k; void* ring_v; int32_t* pos;
   float* y_lin; float* y_swa;
   int B, H, dv, window; float scale;
+  const float* gamma = nullptr;  // [H] per-head state decay (decayed variant only)
 };
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16, hipStream_t stream);
 

@@ -448,16 +448,22 @@ class DecodeState:
             rv[:, :, t % window] = v[:, :, t]
         return cls(S, z, rk, rv, np.full(B, n))
 
-    def step(self, q, k, v, scale: float = 1.0):
+    def step(self, q, k, v, scale: float = 1.0, gamma=None):
         """Consume one token per sequence: q, k [B,H,d_k], v [B,H,d_v].
 
         The state is updated with (k, v) first, so the token attends to
         itself; y_lin = phi(q)^T S / phi(q)^T z; (k, v) goes to ring slot
         t mod window; y_swa is the exact softmax over positions
-        max(0, t - window + 1) .. t held in the ring.  Returns (y_lin, y_swa).
+        max(0, t - window + 1) .. t held in the ring.  With a per-head decay
+        gamma [H] (the decayed variant) the state is S <- gamma S + phi(k) v^T,
+        z <- gamma z + phi(k).  Returns (y_lin, y_swa).
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         pk, pq = phi(k), phi(q)
+        if gamma is not None:
+            g = _f64(gamma)
+            self.S *= g[:, None, None]
+            self.z *= g[:, None]
         self.S += pk[..., :, None] * v[..., None, :]
         self.z += pk
         num = np.einsum("bhf,bhfd->bhd", pq, self.S)

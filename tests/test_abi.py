@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 5
+    assert so.based_abi_version() == 6
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -227,3 +227,15 @@ def test_decay_validation(so):
     assert call(y=gam) == ERR["ALIAS"]
     if need:
         assert call(ws=None) == ERR["WORKSPACE"]
+
+
+def test_decode_decay_validation(so):
+    big = 0x100000
+    q, k, v, gam, S, z, rk, rv, pos, yl, ys = (big * (i + 1) for i in range(11))
+    call = lambda gam=gam, S=S, dt=1, dv=64, win=64: so.based_decode_step_decay(
+        q, k, v, gam, S, z, rk, rv, pos, yl, ys, 2, 3, 16, dv, win, 1.0, dt, None)
+    assert call(gam=None) == ERR["NULL"]
+    assert call(dt=5) == ERR["DTYPE"]
+    assert call(dv=20) == ERR["UNSUPPORTED"]
+    assert call(win=65) == ERR["WINDOW"]
+    assert call(gam=S) == ERR["ALIAS"]          # gamma inside the state S

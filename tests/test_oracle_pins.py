@@ -460,3 +460,25 @@ def test_decay_rows_match_quadratic():
     full = O.linattn_decay_quadratic(q, k, v, np.array([g]))[0][0]
     rows = [0, 1, 44, 89]
     np.testing.assert_allclose(O.linattn_decay_rows(q[0], k[0], v[0], g, rows), full[rows], rtol=1e-13)
+
+
+def test_decay_decode_matches_decayed_forward():
+    """Decode steps with a decay, from the decayed recurrence's state after a
+    context, equal the decayed quadratic form over context + steps; gamma = 1
+    is the plain decode."""
+    B, H, n, steps, dv = 2, 3, 20, 9, 5
+    q, k, v = rand(B, H, n + steps, 16, scale=0.4), rand(B, H, n + steps, 16, scale=0.4), rand(B, H, n + steps, dv)
+    g = np.array([1.0, 0.9, 0.6])
+    _, _, S, z = O.linattn_decay_recurrent(q[..., :n, :], k[..., :n, :], v[..., :n, :], g)
+    st = O.DecodeState.prefill(k[..., :n, :], v[..., :n, :], 64)
+    st.S, st.z = S.copy(), z.copy()
+    plain = O.DecodeState.prefill(k[..., :n, :], v[..., :n, :], 64)
+    y_ref = O.linattn_decay_quadratic(q, k, v, g)[0]
+    for s in range(steps):
+        t = n + s
+        yl, ys = st.step(q[..., t, :], k[..., t, :], v[..., t, :], gamma=g)
+        np.testing.assert_allclose(yl, y_ref[..., t, :], rtol=1e-11, atol=1e-12)
+        yp, ysp = plain.step(q[..., t, :], k[..., t, :], v[..., t, :], gamma=np.ones(H))
+        yp0 = O.linattn_quadratic(q, k, v)[0][..., t, :]
+        np.testing.assert_allclose(yp, yp0, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(ys, ysp, rtol=0, atol=0)  # the window part does not decay

@@ -104,3 +104,63 @@ def test_decode_snapshot_restore(based):
     torch.cuda.synchronize()
     for (a1, b1), (a2, b2) in zip(outs_a, outs_b):
         assert torch.equal(a1, a2.cpu()) and torch.equal(b1, b2.cpu())
+
+
+def run_decay_decode(based, cfg):
+    """Decode with a per-head state decay (heads cycle through 1, 0.75,
+    0.875, ...): the context's state from based_linattn_decay_fwd (bf16) or an
+    empty one (ctx = 0), then steps through based_decode_step_decay, against
+    the oracle's decayed recurrence and its DecodeState with gamma."""
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    gd = g.to(DEV)
+    say(f"decay decode B{cfg.B} H{cfg.H} ctx{cfg.ctx} steps{cfg.steps} dv{cfg.dv} {cfg.dtype}")
+    tol = TOL[qc.dtype]
+    ref = O.DecodeState.prefill(kc, vc, cfg.window)
+    if cfg.ctx > 0:
+        _, _, S, z = O.linattn_decay_recurrent(qc, kc, vc, g.numpy())
+        ref.S, ref.z = S, z
+        _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window, gamma=gd)
+    else:
+        ref.S[:], ref.z[:] = 0.0, 0.0
+        B, H = cfg.B, cfg.H
+        st = based.DecodeState(torch.zeros(B, H, O.D_PHI, cfg.dv, device=DEV), torch.zeros(B, H, O.D_PHI, device=DEV),
+                               torch.zeros(B, H, cfg.window, 16, device=DEV, dtype=qc.dtype),
+                               torch.zeros(B, H, cfg.window, cfg.dv, device=DEV, dtype=qc.dtype),
+                               torch.zeros(B, device=DEV, dtype=torch.int32))
+    qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
+    el = es = 0.0
+    for s in range(cfg.steps):
+        yl, ys = based.decode_step(st, qd[s], kd[s], vd[s], gamma=gd)
+        rl, rs = ref.step(qs[s], ks[s], vs[s], gamma=g.numpy())
+        el, es = max(el, rowinf_rel(yl, rl)), max(es, rowinf_rel(ys, rs))
+        assert el <= tol and es <= tol, (s, el, es)
+    torch.cuda.synchronize()
+    report(f"decay decode y_lin ctx{cfg.ctx} {cfg.dtype}", el, tol)
+    report(f"decay decode y_swa ctx{cfg.ctx} {cfg.dtype}", es, tol)
+    assert rowinf_rel(st.S, ref.S) <= tol and rowinf_rel(st.z, ref.z) <= tol
+    assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
+    return st
+
+
+def test_decay_decode_after_context(based):
+    run_decay_decode(based, synth.DecodeConfig("decay", B=2, H=8, ctx=150, steps=70, dtype="bf16"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decay_decode_from_empty_context(based, dtype):
+    run_decay_decode(based, synth.DecodeConfig("decay0", B=2, H=9, ctx=0, steps=40, dv=48, dtype=dtype))
+
+
+def test_decay_decode_gamma_one_is_plain_decode(based):
+    """gamma = 1 on every head: the decayed step is the plain step, bit for bit."""
+    cfg = synth.DecodeConfig("g1", B=2, H=3, ctx=70, steps=5)
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg)
+    ones = torch.ones(cfg.H, device=DEV)
+    _, _, a = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV))
+    _, _, b = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV))
+    for s in range(cfg.steps):
+        ya = based.decode_step(a, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV))
+        yb = based.decode_step(b, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV), gamma=ones)
+        assert torch.equal(ya[0], yb[0]) and torch.equal(ya[1], yb[1])
+    assert torch.equal(a.S, b.S) and torch.equal(a.z, b.z)
