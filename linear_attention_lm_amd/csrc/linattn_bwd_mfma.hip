@@ -19,12 +19,14 @@
 //
 // Passes (chunks of 64 positions; one workgroup of 4 wavefronts per (head,
 // slice of 32 value columns); dq and dk shares of the slices are added
-// atomically when there are several):
-//   dy_dot_y: D_i = dy_i . y_i.
+// atomically when there are several, onto buffers a clearing pass zeroed).
+// Every term in h is linear in h, and h_i = sum over slices of
+// h_i^s = -(dy_i . y_i over the slice's columns) / den_i: each slice adds the
+// terms of its own h^s, so no pass needs the whole row dy_i . y_i.
 //   query pass, chunks in order: den_i (state z plus the in-chunk kernel
-//     sums), h_i and g_i; dq_i from u = S g + z h through the lane-local
+//     sums), h_i^s and g_i; dq_i from u = S g + z h^s through the lane-local
 //     contraction, plus the in-chunk term sum_j dK_ij (1 + x_ij) k_j; then the
-//     state update S += phi(K)^T V, z += phi(K)^T 1.  Writes den and h.
+//     state update S += phi(K)^T V, z += phi(K)^T 1.  Writes den and h^s.
 //   key pass, chunks in reverse: dk_j from u = R v + r, dv_j from
 //   R^T phi~(k_j) + sum_{i later} g_i, plus the in-chunk terms; then
 //   R += phi(Q)^T G, r += phi(Q)^T h.
@@ -192,8 +194,8 @@ __device__ __forceinline__ int scale_exp(float M) {
 
 struct Params {
   const bf16_t* q; const bf16_t* k; const bf16_t* v; const float* y; const float* dy;
-  float* Dy;            // dy . y per position
-  float* den; float* h; // per position, from the query pass
+  float* den; float* h; // per position, from the query pass (h: [nslice][npos], one row per slice)
+  size_t npos;          // B * H * L
   float* gq; float* gk; float* gv;
   const float* frec;    // [BH][nseg] forward records of (NFC + 1) dvf floats, record_offset layout (record s + 1: segment s)
   const float* frecz;   // [BH][nseg][NFC + 1]
@@ -217,28 +219,14 @@ __device__ __forceinline__ Unit unit_of(const Params& p) {
   return u;
 }
 
-// ---------------------------------------------------------------- dy . y
-// 16 lanes per position, four consecutive columns each (64 columns per pass),
-// so that a wavefront reads four whole rows per instruction.  With several
-// value slices it also clears dq and dk, which the slices then add into.
-__global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __restrict__ y, float* __restrict__ D,
-                                size_t n, int dvf, float* __restrict__ gq, float* __restrict__ gk) {
-  const int sub = threadIdx.x & 15;
-  const size_t stride = (size_t)gridDim.x * blockDim.x / 16;
-  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; i < n; i += stride) {
-    if (gq) {
-      gq[i * DK + sub] = 0.f;
-      gk[i * DK + sub] = 0.f;
-    }
-    float s = 0.f;
-    for (int c = 4 * sub; c < dvf; c += 64) {
-      const float4 a = *reinterpret_cast<const float4*>(dy + i * dvf + c);
-      const float4 b = *reinterpret_cast<const float4*>(y + i * dvf + c);
-      s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-    }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
-    if (sub == 0) D[i] = s;
+// ---------------------------------------------------------------- clearing
+// With several value slices dq and dk receive one share per slice (atomic
+// adds): zero them first.
+__global__ void clear_kernel(float4* __restrict__ a, float4* __restrict__ b, size_t n4) {
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    a[i] = z;
+    b[i] = z;
   }
 }
 
@@ -247,8 +235,8 @@ __global__ void dy_dot_y_kernel(const float* __restrict__ dy, const float* __res
 // offsets): reads past the end of the sequence return zero, with no branch
 // and no 64-bit address held in vector registers across the chunk loop.
 struct HeadRsrc {
-  __amdgpu_buffer_rsrc_t q, k, v, dy;
-  __amdgpu_buffer_rsrc_t f1, f2;  // per-position fp32: D (query pass); den and h (key passes)
+  __amdgpu_buffer_rsrc_t q, k, v, dy, y;
+  __amdgpu_buffer_rsrc_t f1, f2;  // per-position fp32: den and the slice's h (key passes)
 };
 constexpr int RSRC_DW3 = 0x00020000;
 
@@ -262,6 +250,7 @@ __device__ __forceinline__ HeadRsrc head_rsrc(const Params& p, size_t bh, const 
   r.k = rsrc(p.k + bh * L * DK, L * DK * 2);
   r.v = rsrc(p.v + bh * L * p.dvf, L * p.dvf * 2);
   r.dy = rsrc(p.dy + bh * L * p.dvf, L * p.dvf * 4);
+  r.y = rsrc(p.y + bh * L * p.dvf, L * p.dvf * 4);
   r.f1 = rsrc(f1 + bh * L, L * 4);
   r.f2 = rsrc(f2 + bh * L, L * 4);
   return r;
@@ -279,8 +268,9 @@ struct Pre {
   uint4 qk;
   uint4 v;
   float4 dy0, dy1;
-  float aux;   // query pass: D of position tid (tid < 64); key pass: den of row tid / 4
-  float aux2;  // key pass: h of position tid (tid < 64)
+  float4 y0, y1;  // query pass: y of the same slice columns
+  float aux;      // key passes: den of row tid / 4
+  float aux2;     // key passes: the slice's h of position tid (tid < 64)
 };
 
 __device__ __forceinline__ void load_common(const Params& p, const HeadRsrc& rs, int s, int t0, Pre& pf) {
@@ -298,6 +288,15 @@ __device__ __forceinline__ void load_common(const Params& p, const HeadRsrc& rs,
   }
 }
 
+// The query pass also reads y over the slice's columns (for dy . y).
+__device__ __forceinline__ void q_load(const Params& p, const HeadRsrc& rs, int s, int t0, Pre& pf) {
+  load_common(p, rs, s, t0, pf);
+  const int tid = threadIdx.x, r = tid >> 2, cq = tid & 3;
+  const int e = (t0 + r) * p.dvf + s * SW + 8 * cq;
+  pf.y0 = __builtin_bit_cast(float4, bload4(rs.y, e * 4));
+  pf.y1 = __builtin_bit_cast(float4, bload4(rs.y, e * 4 + 16));
+}
+
 // ---------------------------------------------------------------- query pass
 struct QSmem {
   alignas(16) half_t qh[C][QH];            // q rows
@@ -307,7 +306,7 @@ struct QSmem {
   alignas(16) half_t gh[C][RS], gl[C][RS];  // g hi / lo (slice)
   alignas(16) half_t st[NF][RS];           // state S, feature rows, scaled by 2^-e
   alignas(16) float zs[NF];                // state z (fp32)
-  float dys[C];                            // D of the chunk's positions
+  float dys[C];                            // dy . y over the slice's columns, per position
   float dens[C];                           // den of the chunk's positions
   float wmax[4];
 };
@@ -330,7 +329,15 @@ __device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
     const int r = tid >> 2, cq = tid & 3;
     *reinterpret_cast<uint4*>(&S.vh[r][8 * cq]) = h8_from_bf8(pf.v);
   }
-  if (tid < C) S.dys[tid] = pf.aux;
+  {
+    // dy . y over the slice's columns: 8 per thread, 4 threads per row
+    const float4 a0 = pf.dy0, a1 = pf.dy1, b0 = pf.y0, b1 = pf.y1;
+    float d = a0.x * b0.x + a0.y * b0.y + a0.z * b0.z + a0.w * b0.w + a1.x * b1.x + a1.y * b1.y + a1.z * b1.z +
+              a1.w * b1.w;
+    d += __shfl_xor(d, 1, 64);
+    d += __shfl_xor(d, 2, 64);
+    if ((tid & 3) == 0) S.dys[tid >> 2] = d;
+  }
 }
 
 __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
@@ -409,10 +416,9 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     }
     publish();
   }
-  const HeadRsrc rs = head_rsrc(p, bh, p.Dy, p.Dy);
+  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.den);
   Pre pf;
-  load_common(p, rs, s, un.t_begin, pf);
-  pf.aux = bload1(rs.f1, (un.t_begin + (tid & 63)) * 4);  // D (zero past the end)
+  q_load(p, rs, s, un.t_begin, pf);
   __syncthreads();
   q_store(S, pf);
   const f16x8 zero8 = {};
@@ -422,10 +428,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const int n = min(C, un.t_end - t0);
     const float4 dy0 = pf.dy0, dy1 = pf.dy1;  // this chunk's dy (the prefetch below replaces pf)
     __syncthreads();  // chunk inputs and the state copy visible
-    if (t0 + C < un.t_end) {
-      load_common(p, rs, s, t0 + C, pf);
-      pf.aux = bload1(rs.f1, (t0 + C + (tid & 63)) * 4);
-    }
+    if (t0 + C < un.t_end) q_load(p, rs, s, t0 + C, pf);
 
     // ---- scores X^T (keys x queries) of the chunk's key tiles m <= w, the
     // kernel weights K = 1 + x + x^2/2 below the diagonal, their row sums
@@ -475,9 +478,9 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const float hval = -S.dys[pos] / den;
     if (g == 0) {
       S.dens[pos] = den;
-      if (first && pos < n) {
-        p.den[(size_t)bh * L + t0 + pos] = den;
-        p.h[(size_t)bh * L + t0 + pos] = hval;
+      if (pos < n) {
+        if (first) p.den[(size_t)bh * L + t0 + pos] = den;
+        p.h[(size_t)s * p.npos + (size_t)bh * L + t0 + pos] = hval;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(sa, gbh, u);  // g rounded once: the state copy is fp16 as well
       u *= up;
-      if (first) {
+      if (p.nslice > 0) {  // always: see the key pass's readout
         const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[16 * m + 4 * g]);
         u += f32x4{z4.x, z4.y, z4.z, z4.w} * hval;
       }
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           da = mfma(va, gbl, da);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float dk = da[i] + (first ? hval : 0.f);
+            const float dk = da[i] + hval;
             cw[m][i] = (m < w || 4 * g + i <= r16) ? dk * (1.f + xc[m][i]) : 0.f;
           }
         }
@@ -648,7 +651,6 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   if (un.seg == 0) return;
   const size_t bh = un.bh;
   const int s = un.s;
-  const bool first = s == 0;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   f32x4 acc[MAXOWN][2], racc[MAXOWN];
 #pragma unroll
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   }
   float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (tid < SW) S.gcol[tid] = 0.f;
-  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h);
+  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h + (size_t)s * p.npos);
   Pre pf;
   k_load(p, rs, s, un.t_begin, pf);
   for (int t0 = un.t_begin; t0 < un.t_end; t0 += C) {
@@ -694,7 +696,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-          if (first) racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
+          racc[j] = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, racc[j]);
         }
       }
     }
@@ -708,7 +710,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       for (int nn = 0; nn < 2; ++nn)
         *reinterpret_cast<float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g) =
             make_float4(acc[j][nn][0], acc[j][nn][1], acc[j][nn][2], acc[j][nn][3]);
-      if (first && g == 0) rec[(size_t)NF * SW + f] = racc[j][0];
+      if (g == 0) rec[(size_t)NF * SW + f] = racc[j][0];
     }
   }
 #pragma unroll
@@ -722,7 +724,6 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   const Unit un = unit_of(p);
   const size_t bh = un.bh;
   const int s = un.s;
-  const bool first = s == 0;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int kpos = 16 * w + r16;  // key of the lane in transposed tiles
   const int L = p.L;
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
           *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
         }
-        if (first && g == 0) S.rs[16 * mt + r16] = racc[j];
+        if (g == 0) S.rs[16 * mt + r16] = racc[j];
       }
     }
   };
@@ -785,7 +786,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
             const float4 x = *reinterpret_cast<const float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g);
             acc[j][nn] += f32x4{x.x, x.y, x.z, x.w};
           }
-          if (first) racc[j] += rec[(size_t)NF * SW + f];
+          racc[j] += rec[(size_t)NF * SW + f];
         }
       }
       if (tid < SW) g0 += rec[(size_t)NF * SW + NF + tid];
@@ -794,7 +795,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     publish();
   }
   const int last = un.t_begin + ((un.t_end - 1 - un.t_begin) / C) * C;
-  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h);
+  const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h + (size_t)s * p.npos);
   Pre pf;
   k_load(p, rs, s, last, pf);
   __syncthreads();
@@ -823,7 +824,10 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(ld8(&S.rf[16 * m + r16][8 * g]), vb, u);
       u *= up;
-      if (first) {
+      // The condition always holds; as a (uniform) branch it ends each
+      // iteration's block, which keeps the compiler from keeping all 17 rows
+      // of r in registers at once: unconditional, the pass spilled ~90 VGPRs.
+      if (p.nslice > 0) {
         const float4 r4 = *reinterpret_cast<const float4*>(&S.rs[16 * m + 4 * g]);
         u += f32x4{r4.x, r4.y, r4.z, r4.w};
       }
@@ -874,7 +878,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
             const bool keep = m > w || 4 * g + i >= r16;
             const float xx = x[i];
             aw[m][i] = keep ? 1.f + xx + 0.5f * xx * xx : 0.f;
-            cw[m][i] = keep ? (da[i] + (first ? hq[i] : 0.f)) * (1.f + xx) : 0.f;
+            cw[m][i] = keep ? (da[i] + hq[i]) * (1.f + xx) : 0.f;
           }
         }
       }
@@ -926,9 +930,9 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
-          if (first) t = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, t);
+          t = mfma(ld8(&S.hh[32 * ks + 8 * g]), fb, t);
         }
-        if (first) racc[j] += t[0];
+        racc[j] += t[0];
       }
     }
     {
@@ -974,7 +978,7 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   int nseg, sc;
   const int BH = B * H;
   linattn_bwd_mfma_plan(BH, L, dv, &nseg, &sc);
-  size_t floats = (size_t)3 * BH * L;  // D, den, h
+  size_t floats = (size_t)(1 + dv / bwdm::SW) * BH * L;  // den, h per slice
   if (nseg > 1) {
     floats += (size_t)BH * nseg * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
     floats += (size_t)BH * (dv / bwdm::SW) * nseg * bwdm::RREC;                      // suffix records
@@ -988,26 +992,28 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   const size_t BH = (size_t)a.B * a.H, npos = BH * a.L;
   Params p{};
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y; p.dy = a.dy;
-  p.Dy = (float*)a.workspace;
-  p.den = p.Dy + npos;
+  p.den = (float*)a.workspace;
   p.h = p.den + npos;
+  p.npos = npos;
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
   linattn_bwd_mfma_plan((int)BH, a.L, a.dv, &p.nseg, &p.seg_chunks);
-  float* frec = p.h + npos;
+  float* frec = p.h + (size_t)p.nslice * npos;
   p.frec = frec;
   p.frecz = frec + BH * p.nseg * (size_t)(NFC + 1) * a.dv;
   p.krec = const_cast<float*>(p.frecz) + BH * p.nseg * (size_t)(NFC + 1);
   const unsigned grid = (unsigned)(BH * p.nslice * p.nseg);
-  const size_t dblocks = (npos * 16 + 255) / 256;
+  const size_t n4 = npos * DK / 4, cblocks = (n4 + 255) / 256;
   if (p.nseg > 1) {
     if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, p.nseg, p.seg_chunks, s);
         e != hipSuccess)
       return e;
   }
-  hipLaunchKernelGGL(dy_dot_y_kernel, dim3((unsigned)(dblocks < 65536 ? dblocks : 65536)), dim3(256), 0, s,
-                     a.dy, a.y, p.Dy, npos, a.dv, p.nslice > 1 ? p.gq : nullptr, p.gk);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (p.nslice > 1) {
+    hipLaunchKernelGGL(clear_kernel, dim3((unsigned)(cblocks < 8192 ? cblocks : 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(p.gq), reinterpret_cast<float4*>(p.gk), n4);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(query_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nseg > 1) {

@@ -747,7 +747,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   int e = state_scale(S.wmax, down, up);
   publish_state<NT>(S.tt, tacc, tz, e, down);
   if (tok_begin < tok_end) store_chunk<NT>(S.kt, &S.vh[0][0][0], S.qh, S.kh[0], pf);
-  int cur = 0;  // buffer of the current chunk's k and v^T (the other: previous chunk)
+  int cur = 0;  // buffer of the current chunk's k and v (the other: previous chunk)
 
   const f16x8 ones = ones8();
   const int pos = 16 * w + r16;  // the chunk position whose outputs this lane holds
@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 // State-only pass over segment s < nseg - 1 of a (batch, head): the segment's
 // increment of the compact state (segment 0 starts from S_in, so its record
 // carries the initial state too).  Update only, so one barrier per chunk:
-// k^T / v^T are double-buffered in LDS and the inputs are prefetched into
+// k^T and the row-major v are double-buffered in LDS and the inputs are prefetched into
 // registers three chunks ahead.
 template <int NT>
 struct StateSmem {
