@@ -9,14 +9,20 @@
 //
 // Layout of the work: a workgroup (4 wavefronts) walks a segment of a
 // (batch, head) sequence in blocks of 64 queries.  The keys/values of the
-// current and the previous block sit in an LDS ring (each K/V row is read
-// from HBM once per segment); wavefront w owns queries 16w..16w+15 of the
-// block, whose keys span 5 tiles of 16.  Scores are computed transposed
-// (keys x queries) so that each lane holds 4 keys of one query: the softmax
-// row statistics need only in-register work plus two cross-lane steps, and
-// the probabilities already sit in the A-operand layout of the P.V product
-// (keys permuted consistently in the B operand).  P is fp32; it enters the
-// matrix product as hi + lo bf16 (exact to ~16 bits), V is exact in bf16.
+// current and the previous block sit in an LDS ring, row-major (each K/V row
+// is read from HBM once per segment); the next block's keys, values and
+// queries are loaded into registers while the current block computes.
+// Wavefront w owns queries 16w..16w+15 of the block, whose keys span 5 tiles
+// of 16.  Scores are computed transposed (keys x queries) so that each lane
+// holds 4 keys of one query: the softmax row statistics need only
+// in-register work plus two cross-lane steps, and the probabilities already
+// sit in the B-operand layout of the product Y^T = V^T P^T (keys permuted
+// consistently in V^T, which the transposing LDS load ds_read_b64_tr_b16
+// reads from the row-major ring: within each 16-lane block, lane t receives
+// element t % 4 of the 4-element row segments addressed by lanes t / 4 + 4i).
+// Y^T leaves each lane with 4 consecutive columns of one query: 16-byte
+// stores.  P is fp32; it enters the product as hi + lo bf16 (exact to ~16
+// bits), V is exact in bf16.
 #include "based_device.h"
 #include "launchers.h"
 
@@ -25,12 +31,12 @@ namespace swa_mfma {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QB = 64;         // queries per block
 constexpr int NTHR = 256;      // 4 wavefronts
 constexpr int RING = 2 * QB;   // key positions held in LDS
-constexpr int VTS = RING + 8;  // v^T row stride (bf16)
 constexpr int SEG_BLOCKS = 8;  // query blocks per workgroup
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -52,12 +58,25 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// Ring column of key position p in v^T row `col`: 8-position groups are
-// XOR-swizzled by (col / 8) so the transposing writes spread over the banks.
-__device__ __forceinline__ int vt_pos(int col, int p) {
-  const int r = p & (RING - 1);
-  return ((((r >> 3) ^ (col >> 3)) & 15) << 3) | (r & 7);
+// Transposing read: rows r0 .. r0 + 3 of column c0 + (lane % 16) of the
+// row-major 16-bit array at `base` (row stride ld); lane j of each 16-lane
+// block addresses row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3.
+__device__ __forceinline__ uint2 tr4(const bf16_t* base, int r0, int c0, int ld) {
+  const int j = threadIdx.x & 15;
+  const bf16_t* a = base + (r0 + (j >> 2)) * ld + c0 + 4 * (j & 3);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a);
+  return __builtin_bit_cast(uint2, v);
 }
+
+// One block's keys, values and queries on their way from HBM to the ring
+// (k and q: d_qk <= 128, at most 4 16-byte pieces per thread).
+template <int NT>
+struct Pre {
+  static constexpr int NV = (NT + 1) / 2;  // 16-byte pieces of v per thread
+  uint4 k[4];
+  uint4 v[NV];
+  uint4 q[4];  // the lane's query row, dims 8g .. in steps of 32
+};
 
 struct Params {
   const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
@@ -65,14 +84,15 @@ struct Params {
   float scale;
 };
 
-// Dynamic LDS: k ring [RING][dqk + 8] bf16, then v^T ring [DV][VTS] bf16.
+// Dynamic LDS: k ring [RING][dqk + 8] bf16, then v ring [RING][DV + 8] bf16.
 template <int NT>
 __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   extern __shared__ __align__(16) unsigned char smem[];
   const int ks_stride = p.dqk + 8;
   bf16_t* kring = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* vt = kring + RING * ks_stride;
+  constexpr int VRS = DV + 8;  // v ring row stride (bf16)
+  bf16_t* vring = kring + RING * ks_stride;
 
   const size_t bh = blockIdx.x / p.nseg;
   const int seg = blockIdx.x % p.nseg;
@@ -86,40 +106,61 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DV), (short)0, p.L * DV * 2, RSRC_DW3);
 
-  // Stage keys/values of block b into the ring (positions 64b .. 64b+63;
-  // positions outside 0..L-1 read as zero and are masked later).
-  auto stage = [&](int b) {
+  // Keys/values of block b (positions 64b .. 64b+63; positions outside
+  // 0..L-1 read as zero and are masked later) and the lane's query row of
+  // block b into registers; then into the ring.
+  const int kchunks = QB * p.dqk / 8;  // 16-byte pieces of a k block
+  auto load_block = [&](int b, Pre<NT>& pr) {
     const int pos0 = b * QB;
-    const int kchunks = QB * p.dqk / 8;  // 16-byte pieces of the k block
-    for (int u = tid; u < kchunks; u += NTHR) {
-      const int j = u / (p.dqk / 8), c8 = u % (p.dqk / 8);
-      const int pos = pos0 + j;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (pos >= 0) x = bload(rk, (pos * p.dqk + 8 * c8) * 2);
-      *reinterpret_cast<uint4*>(&kring[(pos & (RING - 1)) * ks_stride + 8 * c8]) = x;
-    }
-    constexpr int vchunks = QB * DV / 8;
-    for (int u = tid; u < vchunks; u += NTHR) {
-      const int j = u % QB, c8 = u / QB;  // a wavefront writes 64 positions of one column group
-      const int pos = pos0 + j;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (pos >= 0) x = bload(rv, (pos * DV + 8 * c8) * 2);
-      const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-      const int col0 = 8 * c8;
-      const int pc = vt_pos(col0, pos);  // same for the 8 columns of this group
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(col0 + 2 * e) * VTS + pc] = (bf16_t)(wv[e] & 0xffffu);
-        vt[(col0 + 2 * e + 1) * VTS + pc] = (bf16_t)(wv[e] >> 16);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + NTHR * i;
+      const int j = u / (p.dqk / 8), c8 = u % (p.dqk / 8);
+      pr.k[i] = u < kchunks && pos0 + j >= 0 ? bload(rk, ((pos0 + j) * p.dqk + 8 * c8) * 2) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < Pre<NT>::NV; ++i) {
+      const int u = tid + NTHR * i;
+      const int j = u / (DV / 8), c8 = u % (DV / 8);
+      pr.v[i] = u < QB * DV / 8 && pos0 + j >= 0 ? bload(rv, ((pos0 + j) * DV + 8 * c8) * 2) : make_uint4(0, 0, 0, 0);
+    }
+    const int qi = pos0 + 16 * w + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * i + 8 * g;
+      pr.q[i] = d < p.dqk && qi >= 0 ? bload(rq, (qi * p.dqk + d) * 2) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_block = [&](int b, const Pre<NT>& pr) {
+    const int pos0 = b * QB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + NTHR * i;
+      const int j = u / (p.dqk / 8), c8 = u % (p.dqk / 8);
+      if (u < kchunks) *reinterpret_cast<uint4*>(&kring[((pos0 + j) & (RING - 1)) * ks_stride + 8 * c8]) = pr.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Pre<NT>::NV; ++i) {
+      const int u = tid + NTHR * i;
+      const int j = u / (DV / 8), c8 = u % (DV / 8);
+      if (u < QB * DV / 8) *reinterpret_cast<uint4*>(&vring[((pos0 + j) & (RING - 1)) * VRS + 8 * c8]) = pr.v[i];
     }
   };
 
-  if (b_begin < b_end) stage(b_begin - 1);
+  Pre<NT> pr;
+  uint4 qcur[4];
+  if (b_begin < b_end) {
+    load_block(b_begin - 1, pr);
+    store_block(b_begin - 1, pr);
+    load_block(b_begin, pr);
+    store_block(b_begin, pr);
+  }
   const bf16x8 zero8 = {};
   for (int b = b_begin; b < b_end; ++b) {
-    stage(b);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qcur[i] = pr.q[i];  // this block's queries (pr receives the next block)
+    __syncthreads();  // block b's keys and values in the ring
+    if (b + 1 < b_end) load_block(b + 1, pr);
 
     const int q0 = b * QB + 16 * w;  // first query of this wavefront
     const int qi = q0 + r16;         // the query column this lane holds
@@ -127,9 +168,11 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
     f32x4 x[5];
 #pragma unroll
     for (int m = 0; m < 5; ++m) x[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int d0 = 0; d0 < p.dqk; d0 += 32) {
-      const int d = d0 + 8 * g;
-      const bf16x8 qv = d < p.dqk ? __builtin_bit_cast(bf16x8, bload(rq, (qi * p.dqk + d) * 2)) : zero8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * i + 8 * g;
+      if (32 * i >= p.dqk) break;
+      const bf16x8 qv = d < p.dqk ? __builtin_bit_cast(bf16x8, qcur[i]) : zero8;
 #pragma unroll
       for (int m = 0; m < 5; ++m) {
         const int key = q0 - 64 + 16 * m + r16;
@@ -172,7 +215,7 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
 
-    // Y = P V over the three 32-key blocks (tile pairs (0,1), (2,3), (4,-))
+    // Y^T = V^T P^T over the three 32-key blocks (tile pairs (0,1), (2,3), (4,-))
     f32x4 acc[NT];
 #pragma unroll
     for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -184,33 +227,27 @@ __global__ __launch_bounds__(NTHR, 2) void swa_mfma_kernel(Params p) {
         ah[i] = ph[2 * kb][i]; ah[4 + i] = ph[2 * kb + 1][i];
         al[i] = pl[2 * kb][i]; al[4 + i] = pl[2 * kb + 1][i];
       }
-      const int k0 = q0 - 64 + 32 * kb + 4 * g;  // keys of slots 0..3; slots 4..7 are 16 later
+      // keys of K slots 0..3 and (kb < 2) 4..7, 16 later; ring rows of 4 never wrap
+      const int k0 = (q0 - 64 + 32 * kb + 4 * g) & (RING - 1);
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) {
-        const int col = 16 * nn + r16;
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&vt[col * VTS + vt_pos(col, k0)]);
-        bf16x4 v1 = bf16x4{};
-        if (kb < 2) v1 = *reinterpret_cast<const bf16x4*>(&vt[col * VTS + vt_pos(col, k0 + 16)]);
-        bf16x8 bv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { bv[i] = v0[i]; bv[4 + i] = v1[i]; }
-        acc[nn] = mfma(ah, bv, acc[nn]);
-        acc[nn] = mfma(al, bv, acc[nn]);
+        const uint2 v0 = tr4(vring, k0, 16 * nn, VRS);
+        const uint2 v1 = kb < 2 ? tr4(vring, (k0 + 16) & (RING - 1), 16 * nn, VRS) : make_uint2(0u, 0u);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        acc[nn] = mfma(va, ah, acc[nn]);  // [column 16nn + 4g + i][query qi]
+        acc[nn] = mfma(va, al, acc[nn]);
       }
     }
-    float rden[4];
+    if (qi < p.L) {
+      const float rden = __builtin_amdgcn_rcpf(den);
+      float* yrow = p.y + (bh * p.L + qi) * DV + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rden[i] = __builtin_amdgcn_rcpf(__shfl(den, 4 * g + i, 64));
-#pragma unroll
-    for (int nn = 0; nn < NT; ++nn) {
-      const int col = 16 * nn + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qq = q0 + 4 * g + i;
-        if (qq < p.L) p.y[(bh * p.L + qq) * DV + col] = acc[nn][i] * rden[i];
-      }
+      for (int nn = 0; nn < NT; ++nn)
+        *reinterpret_cast<float4*>(yrow + 16 * nn) =
+            make_float4(acc[nn][0] * rden, acc[nn][1] * rden, acc[nn][2] * rden, acc[nn][3] * rden);
     }
-    __syncthreads();  // the ring slot of block b-1 is reused by block b+1
+    __syncthreads();  // every read of the ring slot of block b-1 done
+    if (b + 1 < b_end) store_block(b + 1, pr);
   }
 }
 
@@ -222,7 +259,7 @@ static hipError_t launch_nt(const SwaArgs& a, hipStream_t s) {
   p.L = a.L; p.dqk = a.dqk; p.window = a.window; p.scale = a.scale;
   const int nblk = (a.L + QB - 1) / QB;
   p.nseg = (nblk + SEG_BLOCKS - 1) / SEG_BLOCKS;
-  const size_t lds = (size_t)RING * (a.dqk + 8) * 2 + (size_t)DV * VTS * 2;
+  const size_t lds = (size_t)RING * (a.dqk + 8) * 2 + (size_t)RING * (DV + 8) * 2;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)swa_mfma_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
