@@ -139,6 +139,16 @@ __device__ __forceinline__ f16x8 tr44(const half_t* base, int r0, int c0, int ld
   return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// The thread index as an opaque value: addresses formed from it at their use
+// inside a loop are not hoisted out of it (a hoisted address stays live
+// across the whole loop body, which in the key pass cost spills whose
+// reloads waited for every memory operation in flight).
+__device__ __forceinline__ int tid_here() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ f16x8 ones8() {
   const uint32_t one2 = 0x3c003c00u;
   return __builtin_bit_cast(f16x8, make_uint4(one2, one2, one2, one2));
@@ -458,6 +468,9 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
         qf[8 + i] = (float)q1[i];
       }
     }
+    // zg[i] = z_lin[a] + sum_b z[(a, b)] q_b for a = 4g + i is also the
+    // z h share of dq[a] (times h): z is symmetric in (a, b)
+    f32x4 zg;
     {
       const uint2 qa2 = *reinterpret_cast<const uint2*>(&S.qh[pos][4 * g]);
       const f16x8 qa8 = __builtin_bit_cast(f16x8, make_uint4(qa2.x, qa2.y, 0u, 0u));
@@ -472,6 +485,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           zq += z4.x * qf[b] + z4.y * qf[b + 1] + z4.z * qf[b + 2] + z4.w * qf[b + 3];
         }
         dpart += qa * (S.zs[a] + 0.5f * zq);
+        zg[i] = S.zs[a] + zq;
       }
     }
     const float den = rows_sum(dpart) + (float)t0;
@@ -499,8 +513,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     __builtin_amdgcn_wave_barrier();
 
     // ---- dq from the state: u^T = S^T-readout (features x this position),
-    // plus z h; lane-local contraction into dq[4g + i]
-    f32x4 dqa = {0.f, 0.f, 0.f, 0.f};
+    // lane-local contraction into dq[4g + i]; plus the z h share, h zg
+    f32x4 dqa = zg * hval;
     const f16x8 gbh = ld8(&S.gh[pos][8 * g]), gbl = ld8(&S.gl[pos][8 * g]);
 #pragma unroll
     for (int m = 0; m < NFT; ++m) {
@@ -508,10 +522,6 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(sa, gbh, u);  // g rounded once: the state copy is fp16 as well
       u *= up;
-      if (p.nslice > 0) {  // always: see the key pass's readout
-        const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[16 * m + 4 * g]);
-        u += f32x4{z4.x, z4.y, z4.z, z4.w} * hval;
-      }
       if (m == 0) dqa += u;
       else dqa += u * qf[m - 1];
     }
@@ -621,8 +631,9 @@ __device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
   }
   if (tid < C) {
     const float hv = pf.aux2;
-    S.hs[tid] = hv;
-    S.hh[tid] = (_Float16)hv;
+    const int t = tid_here();
+    S.hs[t] = hv;
+    S.hh[t] = (_Float16)hv;
   }
 }
 
@@ -816,7 +827,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
         kf[8 + i] = (float)k1[i];
       }
     }
-    // ---- dk from the state: u^T = R-readout with v_j (+ r), lane-local contraction
+    // ---- dk from the state: u^T = R-readout with v_j, lane-local contraction
+    // (the r share is added before the store)
     f32x4 dka = {0.f, 0.f, 0.f, 0.f};
     const f16x8 vb = ld8(&S.vh[kpos][8 * g]);
 #pragma unroll
@@ -824,13 +836,6 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(ld8(&S.rf[16 * m + r16][8 * g]), vb, u);
       u *= up;
-      // The condition always holds; as a (uniform) branch it ends each
-      // iteration's block, which keeps the compiler from keeping all 17 rows
-      // of r in registers at once: unconditional, the pass spilled ~90 VGPRs.
-      if (p.nslice > 0) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&S.rs[16 * m + 4 * g]);
-        u += f32x4{r4.x, r4.y, r4.z, r4.w};
-      }
       if (m == 0) dka += u;
       else dka += u * kf[m - 1];
     }
@@ -902,6 +907,22 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
         }
       }
     }
+    // the r share of dk[a], a = 4g + i: r_lin[a] + sum_b r[(a, b)] k_b (r is
+    // symmetric in (a, b)), from the fp32 copy of r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = 4 * g + i;
+      float rk = S.rs[a];
+#pragma unroll
+      for (int b = 0; b < DK; b += 8) {
+        const f16x8 k8 = ld8(&S.kh[kpos][b]);
+        const float4 r0 = *reinterpret_cast<const float4*>(&S.rs[DK + DK * a + b]);
+        const float4 r1 = *reinterpret_cast<const float4*>(&S.rs[DK + DK * a + b + 4]);
+        rk += r0.x * (float)k8[0] + r0.y * (float)k8[1] + r0.z * (float)k8[2] + r0.w * (float)k8[3] +
+              r1.x * (float)k8[4] + r1.y * (float)k8[5] + r1.z * (float)k8[6] + r1.w * (float)k8[7];
+      }
+      dka[i] += rk;
+    }
     if (kpos < n) {
       float* dst = p.gk + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
       if (p.nslice == 1) {
@@ -945,10 +966,11 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     }
     publish();
     if (tid < SW) {
+      const int t = tid_here();
       float gsum = 0.f;
 #pragma unroll
-      for (int part = 0; part < 8; ++part) gsum += S.gpart[part][tid];
-      S.g0[tid] += gsum;
+      for (int part = 0; part < 8; ++part) gsum += S.gpart[part][t];
+      S.g0[t] += gsum;
     }
     if (t0 - C >= un.t_begin) k_store(S, pf);
   }
