@@ -18,8 +18,10 @@
 // quadratic term sits on the side that is not differentiated.
 //
 // Passes (chunks of 64 positions; one workgroup of 4 wavefronts per (head,
-// slice of 32 value columns); dq and dk shares of the slices are added
-// atomically when there are several, onto buffers a clearing pass zeroed).
+// slice of 32 value columns); with several slices each writes its dq and dk
+// shares to a buffer of its own, and a last pass adds them in slice order:
+// float atomics onto one buffer cost far more, and their order would show in
+// the last bits).
 // Every term in h is linear in h, and h_i = sum over slices of
 // h_i^s = -(dy_i . y_i over the slice's columns) / den_i: each slice adds the
 // terms of its own h^s, so no pass needs the whole row dy_i . y_i.
@@ -207,6 +209,7 @@ struct Params {
   float* den; float* h; // per position, from the query pass (h: [nslice][npos], one row per slice)
   size_t npos;          // B * H * L
   float* gq; float* gk; float* gv;
+  float* pq; float* pk;  // with several slices: [nslice][npos][16] shares of dq and dk
   const float* frec;    // [BH][nseg] forward records of (NFC + 1) dvf floats, record_offset layout (record s + 1: segment s)
   const float* frecz;   // [BH][nseg][NFC + 1]
   float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
@@ -229,14 +232,20 @@ __device__ __forceinline__ Unit unit_of(const Params& p) {
   return u;
 }
 
-// ---------------------------------------------------------------- clearing
-// With several value slices dq and dk receive one share per slice (atomic
-// adds): zero them first.
-__global__ void clear_kernel(float4* __restrict__ a, float4* __restrict__ b, size_t n4) {
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+// ---------------------------------------------------------------- slice sums
+// dq = sum over slices of the slices' shares ([nslice][n4] float4 each, in
+// slice order), likewise dk.
+__global__ void slice_sum_kernel(const float4* __restrict__ pq, const float4* __restrict__ pk, float4* __restrict__ gq,
+                                 float4* __restrict__ gk, size_t n4, int nslice) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
-    a[i] = z;
-    b[i] = z;
+    float4 a = pq[i], b = pk[i];
+    for (int s = 1; s < nslice; ++s) {
+      const float4 x = pq[(size_t)s * n4 + i], y = pk[(size_t)s * n4 + i];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+    gq[i] = a;
+    gk[i] = b;
   }
 }
 
@@ -557,13 +566,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       }
     }
     if (pos < n) {
-      float* dst = p.gq + ((size_t)bh * L + t0 + pos) * DK + 4 * g;
-      if (p.nslice == 1) {
-        *reinterpret_cast<float4*>(dst) = make_float4(dqa[0], dqa[1], dqa[2], dqa[3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, dqa[i]);
-      }
+      float* dst = (p.nslice == 1 ? p.gq : p.pq + (size_t)s * p.npos * DK) + ((size_t)bh * L + t0 + pos) * DK + 4 * g;
+      *reinterpret_cast<float4*>(dst) = make_float4(dqa[0], dqa[1], dqa[2], dqa[3]);
     }
 
     // ---- state update with the chunk: S^T += V^T phi(K), z += phi(K)^T 1
@@ -924,13 +928,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       dka[i] += rk;
     }
     if (kpos < n) {
-      float* dst = p.gk + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
-      if (p.nslice == 1) {
-        *reinterpret_cast<float4*>(dst) = make_float4(dka[0], dka[1], dka[2], dka[3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, dka[i]);
-      }
+      float* dst = (p.nslice == 1 ? p.gk : p.pk + (size_t)s * p.npos * DK) + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
+      *reinterpret_cast<float4*>(dst) = make_float4(dka[0], dka[1], dka[2], dka[3]);
       float* dv = p.gv + ((size_t)bh * L + t0 + kpos) * p.dvf + (size_t)s * SW + 4 * g;
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn)
@@ -1000,7 +999,9 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   int nseg, sc;
   const int BH = B * H;
   linattn_bwd_mfma_plan(BH, L, dv, &nseg, &sc);
-  size_t floats = (size_t)(1 + dv / bwdm::SW) * BH * L;  // den, h per slice
+  const int nslice = dv / bwdm::SW;
+  size_t floats = (size_t)(1 + nslice) * BH * L;                           // den, h per slice
+  if (nslice > 1) floats += (size_t)2 * nslice * BH * L * DK;               // dq, dk shares per slice
   if (nseg > 1) {
     floats += (size_t)BH * nseg * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
     floats += (size_t)BH * (dv / bwdm::SW) * nseg * bwdm::RREC;                      // suffix records
@@ -1020,7 +1021,13 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
   linattn_bwd_mfma_plan((int)BH, a.L, a.dv, &p.nseg, &p.seg_chunks);
-  float* frec = p.h + (size_t)p.nslice * npos;
+  float* part = p.h + (size_t)p.nslice * npos;
+  if (p.nslice > 1) {
+    p.pq = part;
+    p.pk = part + (size_t)p.nslice * npos * DK;
+    part += (size_t)2 * p.nslice * npos * DK;
+  }
+  float* frec = part;
   p.frec = frec;
   p.frecz = frec + BH * p.nseg * (size_t)(NFC + 1) * a.dv;
   p.krec = const_cast<float*>(p.frecz) + BH * p.nseg * (size_t)(NFC + 1);
@@ -1031,11 +1038,6 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
         e != hipSuccess)
       return e;
   }
-  if (p.nslice > 1) {
-    hipLaunchKernelGGL(clear_kernel, dim3((unsigned)(cblocks < 8192 ? cblocks : 8192)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(p.gq), reinterpret_cast<float4*>(p.gk), n4);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL(query_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nseg > 1) {
@@ -1043,7 +1045,14 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(key_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (p.nslice > 1) {
+    hipLaunchKernelGGL(slice_sum_kernel, dim3((unsigned)(cblocks < 8192 ? cblocks : 8192)), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(p.pq), reinterpret_cast<const float4*>(p.pk),
+                       reinterpret_cast<float4*>(p.gq), reinterpret_cast<float4*>(p.gk), n4, p.nslice);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace based
