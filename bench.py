@@ -103,14 +103,14 @@ OP_SOURCES = {
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
     "layer": ["linattn_mfma_kernel<4, 1, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
-    "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "dy_dot_y_kernel",
+    "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "slice_sum_kernel",
             "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>"],
     "decode": ["decode_step_kernel"],
     "baseconv": ["baseconv_kernel"],
     "decay": ["linattn_mfma_kernel<4, 0, 1>", "linattn_state_kernel<4, 1>"],
 }
-# the backward's last launch of each call
-BWD_KERNEL = "key_pass_kernel"
+# the backward's last launch of each call (based_linattn_bwd, then based_swa_bwd)
+BWD_KERNEL = "swa_bwd_mfma_kernel"
 # the step's last launch of each call (marks the end of the timed step in a trace)
 STEP_KERNEL = "linattn_mfma_kernel<4, 1, 0>"
 COPY_BYTES = 512 << 20
