@@ -78,6 +78,26 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Workgroups go to the chip's 8 XCDs round-robin by block index, and each XCD
+// has its own L2.  Block b -> (unit u, part s) of a units x parts grid such
+// that all parts of one unit run on one XCD (units 8i + x take the blocks
+// whose index is x mod 8); units past the last multiple of 8 map in plain
+// order.  A bijection for any units, parts.
+constexpr int NXCD = 8;
+__device__ __forceinline__ void xcd_unit_part(int b, int units, int parts, int& u, int& s) {
+  const int units8 = units - units % NXCD;
+  const int full = units8 * parts;
+  if (b < full) {
+    const int x = b % NXCD, local = b / NXCD;
+    u = NXCD * (local / parts) + x;
+    s = local % parts;
+  } else {
+    const int r = b - full;
+    u = units8 + r / parts;
+    s = r % parts;
+  }
+}
+
 // Segment records of the linear attention's state (workspace of the chunked
 // forward, read by the backward too): the 160 x dv compact state is stored in
 // the order of the matrix-core accumulator fragments, so that a lane moves its

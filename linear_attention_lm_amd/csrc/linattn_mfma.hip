@@ -528,42 +528,78 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
       for (int i = 0; i < 4; ++i) zf[16 * mt[ms] + 4 * g + i] = tz[ms][i];
 }
 
-// Initial owned state tiles: from a compact state record in the workspace
-// (fragment order, see record_offset; one 16-byte load per owned tile), else
-// from the caller's phi-layout S_in, else zero.
+// Initial owned state tiles from the caller's phi-layout S_in, else zero
+// (one uniform branch around the whole tile loop).
 template <int NT>
-__device__ __forceinline__ void init_state(const float* compact, const float* Sin, f32x4 (&tacc)[Own<NT>::PPW],
-                                           int ncompact = 1, const float* wts = nullptr) {
+__device__ __forceinline__ void init_state(const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
   constexpr int DV = 16 * NT;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  if (Sin) {
+#pragma unroll
+    for (int j = 0; j < Own<NT>::PPW; ++j) {
+      int m, n;
+      pair_mn<NT>(w, j, m, n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tacc[j][i] = compact_from_phi(Sin, 16 * m + 4 * g + i, 16 * n + r16, DV);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+__device__ __forceinline__ float bload_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// Initial state of a segment from the compact records of earlier segments
+// (record_offset layout, consecutive, (NF + 1) * DV floats apart; their z
+// parts (NF + 1) floats apart): the sum of records 0..n-1 from `first`, record
+// k weighted by wts[k], n <= MAX_SUM.  Owned tiles into tacc, the constant row
+// into t0, the z entries into zf / z0.  Every read goes through a buffer
+// resource that spans exactly the n records, so all MAX_SUM reads of each
+// entry are issued unconditionally (those past the n-th record return zero
+// without touching memory): no branch lies between them and the compiler
+// keeps them in flight together.  wts[k] must be finite for every k.
+template <int NT>
+__device__ __forceinline__ void sum_records(const float* first, const float* firstz, int n, const float (&wts)[MAX_SUM],
+                                            f32x4 (&tacc)[Own<NT>::PPW], float* t0, float* zf, float& z0) {
+  constexpr int DV = 16 * NT;
+  constexpr int REC = (NF + 1) * DV;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)first, (short)0, n * REC * (int)sizeof(float), RSRC_DW3);
+  const __amdgpu_buffer_rsrc_t rz =
+      __builtin_amdgcn_make_buffer_rsrc((void*)firstz, (short)0, n * (NF + 1) * (int)sizeof(float), RSRC_DW3);
 #pragma unroll
   for (int j = 0; j < Own<NT>::PPW; ++j) {
-    int m, n;
-    pair_mn<NT>(w, j, m, n);
-    if (compact) {
-      const float4 x = *reinterpret_cast<const float4*>(compact + record_offset(16 * m + 4 * g, 16 * n + r16, DV));
-      tacc[j] = f32x4{x.x, x.y, x.z, x.w} * (wts ? wts[0] : 1.f);
-    } else {
-      const int c = 16 * n + r16;
+    int m, nn;
+    pair_mn<NT>(w, j, m, nn);
+    const int off = (int)record_offset(16 * m + 4 * g, 16 * nn + r16, DV) * (int)sizeof(float);
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tacc[j][i] = Sin ? compact_from_phi(Sin, 16 * m + 4 * g + i, c, DV) : 0.f;
+    for (int k = 0; k < MAX_SUM; ++k) {
+      const uint4 x = bload(rr, off + k * REC * (int)sizeof(float));
+      sum += __builtin_bit_cast(f32x4, x) * wts[k];
     }
+    tacc[j] = sum;
   }
-  // further records (consecutive, (NF + 1) * DV floats apart; at most
-  // MAX_SUM - 1 of them) are added on, their loads all in flight together
+  for (int c = tid; c < DV; c += NTHR) {
+    float sum = 0.f;
 #pragma unroll
-  for (int k = 1; k < MAX_SUM; ++k) {
-    if (k < ncompact) {
-      const float* rc = compact + (size_t)k * (NF + 1) * DV;
-#pragma unroll
-      for (int j = 0; j < Own<NT>::PPW; ++j) {
-        int m, n;
-        pair_mn<NT>(w, j, m, n);
-        const float4 x = *reinterpret_cast<const float4*>(rc + record_offset(16 * m + 4 * g, 16 * n + r16, DV));
-        tacc[j] += f32x4{x.x, x.y, x.z, x.w} * (wts ? wts[k] : 1.f);
-      }
-    }
+    for (int k = 0; k < MAX_SUM; ++k) sum += wts[k] * bload_f32(rr, (k * REC + NF * DV + c) * (int)sizeof(float));
+    t0[c] = sum;
   }
+  for (int r = tid; r < NF; r += NTHR) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAX_SUM; ++k) sum += wts[k] * bload_f32(rz, (k * (NF + 1) + r) * (int)sizeof(float));
+    zf[r] = sum;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAX_SUM; ++k) sum += wts[k] * bload_f32(rz, (k * (NF + 1) + NF) * (int)sizeof(float));
+  z0 = sum;
 }
 
 // Denominator state of the owned feature tiles from zf (every column).
@@ -655,34 +691,25 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
   __shared__ Smem<NT, SWA> S;
 
-  const size_t bh = blockIdx.x / p.nseg;
-  const int seg = blockIdx.x % p.nseg;
+  // the segments of one (batch, head) share an XCD: the later segments read
+  // the same records of the earlier ones, through that XCD's L2
+  int bhi, seg;
+  xcd_unit_part(blockIdx.x, gridDim.x / p.nseg, p.nseg, bhi, seg);
+  const size_t bh = bhi;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
 
-  // ---- initial state.  One segment: the caller's S_in / z_in.  Several: the
-  // prefix record ws[seg] (the state-only pass and the scan wrote it; S_in is
-  // read only before this pass, so S_out may alias it).
+  // ---- initial state.  Segment 0: the caller's S_in / z_in (or zero).
+  // Segment s > 0: with at most MAX_SUM + 1 segments, the sum of records
+  // 1..s (record 1 holds S_in plus segment 0's increment, record j > 1
+  // segment j-1's increment); with more, the scan has turned record s into
+  // the state at the segment's start.  S_in is read only before this pass,
+  // so S_out may alias it.
   const size_t rec = (size_t)(NF + 1) * DV;
-  const float* src = nullptr;
-  const float* srcz = nullptr;
-  const float* Sin = nullptr;
-  const float* zin = nullptr;
-  // Without the scan (nseg <= MAX_SUM + 1), segment s > 0 starts from the sum
-  // of records 1..s: record 1 holds S_in plus segment 0's increment, record
-  // j > 1 segment j-1's increment.
   const bool scanned = p.nseg > MAX_SUM + 1;
-  int nsrc = 1;
-  if (p.nseg > 1 && (scanned || seg > 0)) {
-    const int first = scanned ? seg : 1;
-    nsrc = scanned ? 1 : seg;
-    src = p.ws + (bh * p.nseg + first) * rec;
-    srcz = p.wsz + (bh * p.nseg + first) * (size_t)(NF + 1);
-  } else {
-    Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
-    zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
-  }
+  const bool from_records = p.nseg > 1 && seg > 0;
+  const int first = scanned ? seg : 1, nsrc = scanned ? 1 : seg;
   // the segment's first chunk (and, with the window, the chunk before it)
   // from HBM first, so that their latency overlaps the state set-up
   const HeadRsrc rs = head_rsrc(p, bh, DV);
@@ -691,7 +718,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   if (tok_begin < tok_end) load_chunk<NT>(rs, tok_begin, true, pf);
   // decayed variant: record 1 + k (k < seg, no scan) holds segment k's share
   // at its end, which lies seg_chunks * C * (seg - 1 - k) positions before
-  // this segment's start
+  // this segment's start; weights of absent records stay finite (their reads
+  // return zero)
   float lg = 0.f;
   float wrec[MAX_SUM];
 #pragma unroll
@@ -700,31 +728,21 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     lg = decay_lg2(p, bh);
     if (!scanned)
 #pragma unroll
-      for (int k2 = 0; k2 < MAX_SUM; ++k2) wrec[k2] = gpow(lg, (float)((seg - 1 - k2) * p.seg_chunks * C));
+      for (int k2 = 0; k2 < MAX_SUM; ++k2)
+        wrec[k2] = k2 < nsrc ? gpow(lg, (float)((seg - 1 - k2) * p.seg_chunks * C)) : 0.f;
   }
   f32x4 tacc[Own<NT>::PPW];
-  init_state<NT>(src, Sin, tacc, nsrc, DEC ? wrec : nullptr);
-  for (int c = tid; c < DV; c += NTHR) {
-    float t = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (src && k2 < nsrc) t += wrec[k2] * src[(size_t)k2 * rec + (size_t)NF * DV + c];
-    S.t0[c] = src ? t : (Sin ? Sin[c] : 0.f);
-  }
-  for (int r = tid; r < NF; r += NTHR) {
-    float t = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (srcz && k2 < nsrc) t += wrec[k2] * srcz[(size_t)k2 * (NF + 1) + r];
-    S.zf[r] = srcz ? t : (zin ? compact_from_phi(zin, r, 0, 1) : 0.f);
-  }
   float z0 = 0.f;
-  if (srcz) {
-#pragma unroll
-    for (int k2 = 0; k2 < MAX_SUM; ++k2)
-      if (k2 < nsrc) z0 += wrec[k2] * srcz[(size_t)k2 * (NF + 1) + NF];
-  } else if (zin) {
-    z0 = zin[0];
+  if (from_records) {
+    sum_records<NT>(p.ws + (bh * p.nseg + first) * rec, p.wsz + (bh * p.nseg + first) * (size_t)(NF + 1), nsrc,
+                    wrec, tacc, S.t0, S.zf, z0);
+  } else {
+    const float* Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
+    const float* zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
+    init_state<NT>(Sin, tacc);
+    for (int c = tid; c < DV; c += NTHR) S.t0[c] = Sin ? Sin[c] : 0.f;
+    for (int r = tid; r < NF; r += NTHR) S.zf[r] = zin ? compact_from_phi(zin, r, 0, 1) : 0.f;
+    z0 = zin ? zin[0] : 0.f;
   }
   for (int j = tid; j < KT; j += NTHR) S.kt[ONES][j] = (half_t)1.f;
   int ia[3], ib[3];
@@ -1077,8 +1095,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   __shared__ StateSmem<NT> S;
 
   const int nsm = p.nseg - 1;
-  const size_t bh = blockIdx.x / nsm;
-  const int seg = blockIdx.x % nsm;
+  int bhi, seg;
+  xcd_unit_part(blockIdx.x, gridDim.x / nsm, nsm, bhi, seg);
+  const size_t bh = bhi;
   const int tid = threadIdx.x;
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
@@ -1090,19 +1109,18 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   load_chunk<NT>(rs, tok_begin, false, p0);
   load_chunk<NT>(rs, tok_begin + C, false, p1);
   load_chunk<NT>(rs, tok_begin + 2 * C, false, p2);
-  const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
-  const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
+  // the segment's increment from zero; segment 0 adds the caller's initial
+  // state after the loop (every term is linear in it), so that no read
+  // other than the chunk prefetches precedes the first update
   f32x4 tacc[Own<NT>::PPW];
-  init_state<NT>(nullptr, Sin, tacc);
-  for (int c = tid; c < DV; c += NTHR) S.t0[c] = Sin ? Sin[c] : 0.f;
-  for (int r = tid; r < NF; r += NTHR) S.zf[r] = zin ? compact_from_phi(zin, r, 0, 1) : 0.f;
-  float z0 = zin ? zin[0] : 0.f;
+  init_state<NT>(nullptr, tacc);
+  for (int c = tid; c < DV; c += NTHR) S.t0[c] = 0.f;
+  for (int r = tid; r < NF; r += NTHR) S.zf[r] = 0.f;
+  float z0 = 0.f;
   for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = (half_t)1.f;
   __syncthreads();
   f32x4 tz[3];
   load_tz(S.zf, tz);
-  if (seg == 0 && p.nseg > MAX_SUM + 1)  // record 0 (for the scan): the initial state of the sequence
-    write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   int ia[3], ib[3];
   slot_rows(ia, ib);
 
@@ -1158,11 +1176,25 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   S.vpart[tid] = vs;
   store_z<NT>(S.zf, tz);
   __syncthreads();
+  // segment 0: the caller's initial state, decayed over the segment
+  const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
+  const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
+  const float gN = DEC ? gpow(lg, (float)(tok_end - tok_begin)) : 1.f;
   if (tid < DV) {
-    float sum = DEC ? gpow(lg, (float)(tok_end - tok_begin)) * S.t0[tid] : S.t0[tid];
+    float sum = Sin ? gN * Sin[tid] : 0.f;
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) sum += S.vpart[q * DV + tid];
     S.t0[tid] = sum;
+  }
+  if (zin) {
+    for (int r = tid; r < NF; r += NTHR) S.zf[r] += gN * compact_from_phi(zin, r, 0, 1);
+    z0 += gN * zin[0];
+  }
+  if (Sin) {
+    f32x4 s0[Own<NT>::PPW];
+    init_state<NT>(Sin, s0);
+#pragma unroll
+    for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] += gN * s0[j];
   }
   __syncthreads();
   write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
