@@ -345,7 +345,7 @@ __device__ __forceinline__ f16x8 ones8() {
 // State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
 // (every column of a tz tile holds it).
-template <int NT, int DEC = 0>
+template <int NT, int DEC = 0, int FREE = 0>
 __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t* vh,
                                              f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3], const int (&ia)[3],
                                              const int (&ib)[3], const f16x8* wk = nullptr) {
@@ -380,8 +380,9 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
     tz[0] = mfma(a[0], ones, tz[0]);
     tz[1] = mfma(a[1], ones, tz[1]);
     if ((w & 1) == 0) tz[2] = mfma(a[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
-    // keep the operands of the two K-steps from being live at once
-    __builtin_amdgcn_sched_barrier(0);
+    // keep the operands of the two K-steps from being live at once (FREE:
+    // the caller has the registers to let the scheduler overlap them)
+    if constexpr (!FREE) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -1074,15 +1075,19 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 
 // ---------------------------------------------------------------------------
 // State-only pass over segment s < nseg - 1 of a (batch, head): the segment's
-// increment of the compact state (segment 0 starts from S_in, so its record
-// carries the initial state too).  Update only, so one barrier per chunk:
-// k^T and the row-major v are double-buffered in LDS and the inputs are prefetched into
-// registers three chunks ahead.
+// increment of the compact state (segment 0's record also carries S_in).
+// Update only, in groups of chunks (SG, half that in the decayed variant):
+// k^T and the row-major v of a whole group sit in LDS together, so a group
+// costs two barriers and its updates run back to back, while the next
+// group's inputs are in flight in registers.  The reads go through buffer resources that end at the
+// segment's end: chunks past it read as zero and add nothing, so every
+// update runs unconditionally.
+constexpr int SG = 4;
 template <int NT>
 struct StateSmem {
   static constexpr int DV = 16 * NT;
-  alignas(16) half_t kt[2][DK + 1][KT];
-  alignas(16) half_t vh[2][C][vrow<NT>()];
+  alignas(16) half_t kt[SG][DK + 1][KT];
+  alignas(16) half_t vh[SG][C][vrow<NT>()];
   alignas(16) float vpart[NTHR];
   alignas(16) float t0[DV];
   alignas(16) float zf[NF];
@@ -1091,7 +1096,10 @@ struct StateSmem {
 template <int NT, int DEC = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
   constexpr int DV = 16 * NT;
-  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
+  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1;
+  // chunks per group (the decayed variant's extra per-chunk registers leave
+  // room for half the prefetches)
+  constexpr int G = DEC ? SG / 2 : SG;
   __shared__ StateSmem<NT> S;
 
   const int nsm = p.nseg - 1;
@@ -1103,73 +1111,68 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
   const size_t rec = (size_t)(NF + 1) * DV;
 
-  // the first three chunks from HBM first, overlapping the state set-up
-  const HeadRsrc rs = head_rsrc(p, bh, DV);
-  Prefetch<NT> p0, p1, p2, p3;
-  load_chunk<NT>(rs, tok_begin, false, p0);
-  load_chunk<NT>(rs, tok_begin + C, false, p1);
-  load_chunk<NT>(rs, tok_begin + 2 * C, false, p2);
+  // the head's k and v up to the segment's end; the first group's loads go
+  // out first, overlapping the state set-up
+  HeadRsrc rs;
+  rs.q = rs.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + bh * p.L * DK), (short)0, tok_end * DK * 2, RSRC_DW3);
+  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DV), (short)0, tok_end * DV * 2, RSRC_DW3);
+  Prefetch<NT> pf[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) load_chunk<NT>(rs, tok_begin + i * C, false, pf[i]);
   // the segment's increment from zero; segment 0 adds the caller's initial
-  // state after the loop (every term is linear in it), so that no read
-  // other than the chunk prefetches precedes the first update
+  // state after the loop (every term is linear in it)
   f32x4 tacc[Own<NT>::PPW];
   init_state<NT>(nullptr, tacc);
-  for (int c = tid; c < DV; c += NTHR) S.t0[c] = 0.f;
-  for (int r = tid; r < NF; r += NTHR) S.zf[r] = 0.f;
-  float z0 = 0.f;
-  for (int j = tid; j < 2 * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = (half_t)1.f;
-  __syncthreads();
   f32x4 tz[3];
-  load_tz(S.zf, tz);
+#pragma unroll
+  for (int ms = 0; ms < 3; ++ms) tz[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float z0 = 0.f;
+  for (int j = tid; j < SG * KT; j += NTHR) S.kt[j / KT][ONES][j % KT] = (half_t)1.f;
   int ia[3], ib[3];
   slot_rows(ia, ib);
 
-  const int col = tid % DV, part = tid / DV;
   float vs = 0.f;  // this thread's share of the column sums of v (constant row)
-  store_chunk<NT>(S.kt[0], &S.vh[0][0][0], nullptr, nullptr, p0);
-
-  // chunk at t (in LDS buffer buf); `next` holds chunk t + C, `spare`
-  // receives t + 3C: three chunks in flight from HBM while one is updated.
-  // Loads and LDS stores run in every step, also past the segment's end
-  // (range-checked reads, buffers nobody reads), so the number of loads in
-  // flight is the same on every path; only the update is skipped there.
   const float lg = DEC ? decay_lg2(p, bh) : 0.f;
   const int lane = tid & 63, g = lane >> 4;
-  auto step = [&](int t, int buf, const Prefetch<NT>& next, Prefetch<NT>& spare) {
-    __syncthreads();
-    load_chunk<NT>(rs, t + 3 * C, false, spare);
-    if (t >= tok_end) {
-      // past the segment: nothing to add
-    } else if constexpr (DEC) {
-      // the carried sums decay over the chunk; keys weigh gamma^(n-1-key)
-      const int n = min(C, tok_end - t);
-      const float gn = gpow(lg, (float)n);
-      vs = gn * vs + vsum_part<NT, 1>(&S.vh[buf][0][0], n, lg);
-      z0 = gn * z0 + gsum_pow(lg, n);
+  for (int t = tok_begin; t < tok_end; t += G * C) {
+    __syncthreads();  // the previous group's reads of LDS done
 #pragma unroll
-      for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
+    for (int i = 0; i < G; ++i) store_chunk<NT>(S.kt[i], &S.vh[i][0][0], nullptr, nullptr, pf[i]);
 #pragma unroll
-      for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
-      f16x8 wk[2];
+    for (int i = 0; i < G; ++i) load_chunk<NT>(rs, t + (G + i) * C, false, pf[i]);
+    __syncthreads();  // the group in LDS
+    if constexpr (DEC) {
+      // (a rolled loop: the decay weights of several chunks at once would
+      // not fit the register budget)
+#pragma unroll 1
+      for (int i = 0; i < G; ++i) {
+        // the carried sums decay over the chunk; keys weigh gamma^(n-1-key);
+        // a chunk past the segment (n = 0) leaves everything unchanged
+        const int n = min(C, max(0, tok_end - (t + i * C)));
+        const float gn = gpow(lg, (float)n);
+        vs = gn * vs + vsum_part<NT, 1>(&S.vh[i][0][0], n, lg);
+        z0 = gn * z0 + gsum_pow(lg, n);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = 32 * ks + 8 * g + i;
-          wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
-        }
-      update_chunk<NT, 1>(S.kt[buf], &S.vh[buf][0][0], tacc, tz, ia, ib, wk);
+        for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
+        f16x8 wk[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = 32 * ks + 8 * g + e;
+            wk[ks][e] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+          }
+        update_chunk<NT, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib, wk);
+      }
     } else {
-      vs += vsum_part<NT, 0>(&S.vh[buf][0][0], C, 0.f);
-      update_chunk<NT>(S.kt[buf], &S.vh[buf][0][0], tacc, tz, ia, ib);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        vs += vsum_part<NT, 0>(&S.vh[i][0][0], C, 0.f);
+        update_chunk<NT, 0, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib);
+      }
     }
-    store_chunk<NT>(S.kt[buf ^ 1], &S.vh[buf ^ 1][0][0], nullptr, nullptr, next);
-  };
-  for (int t = tok_begin; t < tok_end; t += 4 * C) {
-    step(t, 0, p1, p3);
-    step(t + C, 1, p2, p0);
-    step(t + 2 * C, 0, p3, p1);
-    step(t + 3 * C, 1, p0, p2);
   }
   if constexpr (!DEC) z0 += (float)(tok_end - tok_begin);
   __syncthreads();
