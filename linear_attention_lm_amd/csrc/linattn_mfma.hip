@@ -151,7 +151,7 @@ __device__ __forceinline__ float compact_from_phi(const float* S, int r, int c, 
 struct Params {
   const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
   const float* S_in; const float* z_in; float* S_out; float* z_out;
-  float* ws;        // [BH][nseg] compact state records of (NF+1) DV floats (record_offset; row NF = constant)
+  float* ws;        // [BH][nseg] compact state records of (NF+1) DV floats (record_offset; row NF = constant; record 0 unused)
   float* wsz;       // [BH][nseg][NF+1] likewise for z (entry NF = constant: token count)
   int L, nseg, seg_chunks;
   float* y_swa;     // sliding-window softmax output of the fused layer pass
@@ -1204,9 +1204,10 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
                     p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
 }
 
-// Prefix over the segment records of each (batch, head): record s holds the
-// increment of segment s-1 (record 1: the initial state plus that
+// Prefix over the segment records of each (batch, head): record s >= 1 holds
+// the increment of segment s-1 (record 1: the initial state plus that
 // increment); after the scan record s is the state at the start of segment s.
+// Record 0 is not used (segment 0 starts from S_in itself).
 __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH, const float* gamma, int H,
                                 int seg_len) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -89,3 +89,24 @@ def test_decay_resume_state(based):
     gap = rowinf_rel(y2, y_full[:, :, n:].double().cpu().numpy())
     report("decay resume vs one call", gap, TOL[torch.bfloat16])
     assert gap <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("L", [768, 2560])
+def test_decay_initial_state_across_segments(based, L):
+    """S_in with the decay and several segments: the state-only pass adds
+    gamma^n S_in to segment 0's record (three segments), and the scan
+    carries it on (ten)."""
+    cfg = SMALL.replace(L=L, name=f"S_in L{L}")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    _, kp, vp = synth.fwd_inputs(cfg.replace(L=500), 1)  # S_in: a seeded prefix's exported state
+    S0, z0 = (torch.from_numpy(x).float() for x in O.linattn_state(kp, vp))
+    say(f"decay {cfg.name} B{cfg.B} H{cfg.H} with S_in")
+    y = based.linattn_decay_fwd(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), S0.to(DEV), z0.to(DEV))
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (0, 3), (1, 6), (1, 7)]:
+        ref = O.linattn_decay_quadratic(q[b, h][None], k[b, h][None], v[b, h][None], g[h:h + 1].numpy(),
+                                        S0[b, h][None], z0[b, h][None])[0][0]
+        err = rowinf_rel(y[b, h], ref)
+        report(f"decay {cfg.name} head ({b}, {h})", err, TOL[q.dtype])
+        assert err <= TOL[q.dtype], (b, h, err)

@@ -175,6 +175,38 @@ def test_nonsymmetric_initial_state(based):
     assert err <= 1e-5
 
 
+def prefix_state(cfg, n=500, seed=1):
+    """The state a seeded prefix of n positions leaves (what a resumed call
+    receives as S_in), from the oracle."""
+    _, k, v = inputs(cfg.replace(L=n), seed)
+    S0, z0 = O.linattn_state(k, v)
+    return torch.from_numpy(S0).float(), torch.from_numpy(z0).float()
+
+
+@pytest.mark.parametrize("B,H,L", [(2, 3, 768), (2, 3, 2560), (1, 12, 768)])
+def test_initial_state_across_segments(based, B, H, L):
+    """S_in with the sequence split into segments: segment 0 reads S_in,
+    the later ones receive it through the state-only pass's records (three
+    segments) or through the scan (ten); B*H = 12 puts heads on both sides of
+    the XCD-grouped block mapping (eight grouped, four in plain order).  S_in
+    is a prefix's exported state (an arbitrary one is covered in fp32 above:
+    the bf16 path reads the state through an fp16 copy)."""
+    cfg = SMALL.replace(B=B, H=H, L=L, name=f"S_in B{B}H{H}L{L}")
+    q, k, v = inputs(cfg)
+    S0, z0 = prefix_state(cfg)
+    say(f"linattn {cfg.name} with S_in")
+    y, S, z = based.linattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), S0.to(DEV), z0.to(DEV), return_state=True)
+    torch.cuda.synchronize()
+    y_ref, _, S_ref, z_ref = O.linattn_chunked(q, k, v, 64, S0, z0)
+    tol = TOL[q.dtype]
+    err = rowinf_rel(y, y_ref)
+    report(f"linattn y {cfg.name}", err, tol)
+    assert err <= tol
+    errS, errz = rowinf_rel(S, S_ref), rowinf_rel(z, z_ref)
+    report(f"linattn S_out {cfg.name}", max(errS, errz), tol)
+    assert errS <= tol and errz <= tol
+
+
 # ------------------------------------------------------------------ robustness
 def test_no_writes_outside_outputs(based):
     """Guard bands around y and the state stay untouched."""
