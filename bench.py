@@ -13,9 +13,12 @@ separate calls (based_linattn_fwd, based_swa_fwd) for comparison.
 
 Inputs are resident in HBM before timing starts.  Eight copies of the input
 set are cycled so that successive steps do not find their inputs in the
-256 MB last-level (Infinity) cache.  Kernels run on torch's current stream;
-per-kernel durations come from events recorded on that stream around every
-launch in the timed region.
+256 MB last-level (Infinity) cache.  Kernels run on torch's current stream.
+Every timed region is one loop of back-to-back calls of one operation with
+events on that stream at its two ends only (an event pair around every
+launch would cost the GPU several microseconds per call): the step's
+duration is the layer operation's duration, and operations compared side by
+side (the two separate calls, the two backward calls) get a loop each.
 
 Also reported (same JSON line): the roofline of the dominant kernel, the
 layer backward on the step's workload (based_linattn_bwd + based_swa_bwd:
@@ -156,28 +159,24 @@ def load_traffic(op):
     return rec["bytes_per_call"]
 
 
-class StreamTimer:
-    """Events on the current stream around every launch of each named kernel."""
-
-    def __init__(self):
-        self.pairs = {}
-
-    def run(self, name, fn):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        out = fn()
-        e.record()
-        self.pairs.setdefault(name, []).append((s, e))
-        return out
-
-    def mean_ms(self, name):
-        p = self.pairs[name]
-        return sum(s.elapsed_time(e) for s, e in p) / len(p)
+def time_loop(fn, steps):
+    """Mean milliseconds per call of `steps` back-to-back calls fn(i) on the
+    current stream, bracketed by a device synchronize and an event on each
+    side."""
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        fn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
     """Time `steps` layer forwards: one based_layer_fwd call per step, or
-    (fused=False) based_linattn_fwd then based_swa_fwd.  Returns a dict."""
+    (fused=False) based_linattn_fwd and based_swa_fwd, each in a loop of its
+    own (the step's time is their sum).  Returns a dict."""
     q, k, v = synth.fwd_inputs(cfg, 0)
     sets = []
     for i in range(nbuf):
@@ -188,47 +187,39 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
     ws_bytes = lal.linattn_workspace_bytes(B, H, L, dv)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
-    def step(i, timer=None):
+    def layer(i):
         qq, kk, vv = sets[i % nbuf]
-        if fused:
-            f = lambda: lal.layer_fwd(qq, kk, vv, cfg.window, y_lin=y_lin, y_swa=y_swa, workspace=ws)
-            f() if timer is None else timer.run("layer", f)
-            return
-        f1 = lambda: lal.linattn_fwd(qq, kk, vv, y=y_lin, workspace=ws)
-        f2 = lambda: lal.swa_fwd(qq, kk, vv, cfg.window, y=y_swa)
-        if timer is None:
-            f1()
-            f2()
-        else:
-            timer.run("linattn", f1)
-            timer.run("swa", f2)
+        lal.layer_fwd(qq, kk, vv, cfg.window, y_lin=y_lin, y_swa=y_swa, workspace=ws)
+
+    def lin(i):
+        qq, kk, vv = sets[i % nbuf]
+        lal.linattn_fwd(qq, kk, vv, y=y_lin, workspace=ws)
+
+    def swa(i):
+        qq, kk, vv = sets[i % nbuf]
+        lal.swa_fwd(qq, kk, vv, cfg.window, y=y_swa)
 
     for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    timer = StreamTimer()
-    t0.record()
-    for i in range(steps):
-        step(i, timer)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+        if fused:
+            layer(i)
+        else:
+            lin(i)
+            swa(i)
     th = B * H * L
     es = 2 if cfg.dtype == "bf16" else 4
-    out = {"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
-           "dtype": cfg.dtype, "fused": fused, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)}
     if fused:
-        tl = timer.mean_ms("layer")
+        ms = time_loop(layer, steps)
         lb = layer_bytes(dv, es) * th
-        out.update({"layer_us": tl * 1e3, "layer_bytes": lb, "layer_hbm_gbs": lb / (tl * 1e-3) / 1e9,
-                    "layer_alg_tflops": (lin_flops(dv) + swa_flops(dv)) * th / (tl * 1e-3) / 1e12})
+        out = {"layer_us": ms * 1e3, "layer_bytes": lb, "layer_hbm_gbs": lb / (ms * 1e-3) / 1e9,
+               "layer_alg_tflops": (lin_flops(dv) + swa_flops(dv)) * th / (ms * 1e-3) / 1e12}
     else:
-        tl, ts = timer.mean_ms("linattn"), timer.mean_ms("swa")
+        tl, ts = time_loop(lin, steps), time_loop(swa, steps)
+        ms = tl + ts
         lb, sb = lin_bytes(dv, es) * th, swa_bytes(dv, es) * th
-        out.update({"linattn_us": tl * 1e3, "swa_us": ts * 1e3, "linattn_bytes": lb, "swa_bytes": sb,
-                    "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9})
+        out = {"linattn_us": tl * 1e3, "swa_us": ts * 1e3, "linattn_bytes": lb, "swa_bytes": sb,
+               "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9}
+    out.update({"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
+                "dtype": cfg.dtype, "fused": fused, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)})
     return out
 
 
@@ -247,8 +238,9 @@ def bwd_inputs(lal, cfg, nbuf=8):
 
 
 def bench_bwd(lal, cfg, steps, warmup, sets):
-    """Time `steps` layer backwards: based_linattn_bwd then based_swa_bwd on
-    one of the prepared input sets per step.  Returns a dict."""
+    """Time `steps` layer backwards: based_linattn_bwd and based_swa_bwd, each
+    in a loop of its own over the prepared input sets (the step's time is
+    their sum).  Returns a dict."""
     nbuf = len(sets)
     B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
     ws = torch.empty(max(1, lal.linattn_bwd_workspace_bytes(B, H, L, dv)), dtype=torch.uint8, device="cuda")
@@ -256,30 +248,20 @@ def bench_bwd(lal, cfg, steps, warmup, sets):
     gk = torch.empty_like(gq)
     gv = torch.empty(B, H, L, dv, device="cuda")
 
-    def step(i, timer=None):
+    def lin(i):
         qd, kd, vd, dyd, y_lin, y_swa = sets[i % nbuf]
-        f1 = lambda: lal.linattn_bwd(qd, kd, vd, y_lin, dyd, dq=gq, dk=gk, dv=gv, workspace=ws)
-        f2 = lambda: lal.swa_bwd(qd, kd, vd, y_swa, dyd, cfg.window, dq=gq, dk=gk, dv=gv)
-        if timer is None:
-            f1()
-            f2()
-        else:
-            timer.run("linattn_bwd", f1)
-            timer.run("swa_bwd", f2)
+        lal.linattn_bwd(qd, kd, vd, y_lin, dyd, dq=gq, dk=gk, dv=gv, workspace=ws)
+
+    def swa(i):
+        qd, kd, vd, dyd, y_lin, y_swa = sets[i % nbuf]
+        lal.swa_bwd(qd, kd, vd, y_swa, dyd, cfg.window, dq=gq, dk=gk, dv=gv)
 
     for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timer = StreamTimer()
-    t0.record()
-    for i in range(steps):
-        step(i, timer)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+        lin(i)
+        swa(i)
+    tl, ts = time_loop(lin, steps), time_loop(swa, steps)
+    ms = tl + ts
     th = B * H * L
-    tl, ts = timer.mean_ms("linattn_bwd"), timer.mean_ms("swa_bwd")
     b1 = bwd_bytes(dv) * th
     return {"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
             "dtype": cfg.dtype, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
@@ -535,8 +517,9 @@ def summarize_stats(stats_dir, command, calls):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (enough for the GPU clocks to settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and decode")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
