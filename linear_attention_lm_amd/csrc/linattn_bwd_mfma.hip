@@ -233,20 +233,41 @@ __device__ __forceinline__ Unit unit_of(const Params& p) {
 }
 
 // ---------------------------------------------------------------- slice sums
-// dq = sum over slices of the slices' shares ([nslice][n4] float4 each, in
-// slice order), likewise dk.
+// The sum over slices of the slices' shares ([nslice][n4] float4 each), in
+// slice order, for the elements first, first + step, ... below i1; four of
+// them per round, so that their loads are in flight together.
+__device__ __forceinline__ void sum_slices(const float4* __restrict__ part, float4* __restrict__ out, size_t n4,
+                                           int nslice, size_t first, size_t i1, size_t step) {
+  for (size_t i = first; i < i1; i += 4 * step) {
+    float4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t j = i + u * step;
+      a[u] = j < i1 ? part[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int s = 1; s < nslice; ++s) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t j = i + u * step;
+        if (j < i1) {
+          const float4 x = part[(size_t)s * n4 + j];
+          a[u].x += x.x; a[u].y += x.y; a[u].z += x.z; a[u].w += x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * step < i1) out[i + u * step] = a[u];
+  }
+}
+
+// dk = sum of the slices' shares, and dq likewise unless pq is null (the
+// suffix-state pass has summed dq then).
 __global__ void slice_sum_kernel(const float4* __restrict__ pq, const float4* __restrict__ pk, float4* __restrict__ gq,
                                  float4* __restrict__ gk, size_t n4, int nslice) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
-    float4 a = pq[i], b = pk[i];
-    for (int s = 1; s < nslice; ++s) {
-      const float4 x = pq[(size_t)s * n4 + i], y = pk[(size_t)s * n4 + i];
-      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
-    }
-    gq[i] = a;
-    gk[i] = b;
-  }
+  const size_t first = (size_t)blockIdx.x * blockDim.x + threadIdx.x, step = (size_t)gridDim.x * blockDim.x;
+  if (pq) sum_slices(pq, gq, n4, nslice, first, n4, step);
+  sum_slices(pk, gk, n4, nslice, first, n4, step);
 }
 
 // ---------------------------------------------------------------- chunk loads
@@ -663,7 +684,20 @@ struct KIncSmem {
 __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   __shared__ KIncSmem S;
   const Unit un = unit_of(p);
-  if (un.seg == 0) return;
+  if (un.seg == 0) {
+    // Nothing lies before segment 0, so its workgroups have no state to
+    // form: with several slices they sum the dq shares of their head (the
+    // query pass that wrote them has completed), in slice order, workgroup s
+    // taking the s-th part of the head's positions.
+    if (p.nslice > 1) {
+      const size_t n4 = p.npos * DK / 4, per_head = (size_t)p.L * DK / 4;
+      const size_t i0 = un.bh * per_head + per_head * un.s / p.nslice;
+      const size_t i1 = un.bh * per_head + per_head * (un.s + 1) / p.nslice;
+      sum_slices(reinterpret_cast<const float4*>(p.pq), reinterpret_cast<float4*>(p.gq), n4, p.nslice,
+                 i0 + threadIdx.x, i1, NTHR);
+    }
+    return;
+  }
   const size_t bh = un.bh;
   const int s = un.s;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
@@ -1047,8 +1081,10 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(key_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nslice > 1) {
+    // with several segments the suffix-state pass has summed dq
     hipLaunchKernelGGL(slice_sum_kernel, dim3((unsigned)(cblocks < 8192 ? cblocks : 8192)), dim3(256), 0, s,
-                       reinterpret_cast<const float4*>(p.pq), reinterpret_cast<const float4*>(p.pk),
+                       p.nseg > 1 ? nullptr : reinterpret_cast<const float4*>(p.pq),
+                       reinterpret_cast<const float4*>(p.pk),
                        reinterpret_cast<float4*>(p.gq), reinterpret_cast<float4*>(p.gk), n4, p.nslice);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
