@@ -396,11 +396,12 @@ def short_name(kernel):
     return kernel.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
-def summarize_pmc(fetch_dir, write_dir, calls, command):
+def summarize_pmc(fetch_dir, write_dir, calls, command, out_dir=None):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE) into profiles/traffic_<op>.json: HBM bytes per call
-    of each timed operation, scaled by the counters' reading for the copy
-    calibration kernel of known size."""
+    WRITE_SIZE) into <out_dir>/traffic_<op>.json (default: profiles/): HBM
+    bytes per call of each timed operation, scaled by the counters' reading
+    for the copy calibration kernel of known size."""
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     def per_dispatch(rows, counter):
         """(dispatch id, kernel name) -> bytes (summed over the counter's instances)."""
         acc = {}
@@ -439,7 +440,7 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
     bwd_end = bwd_ids[calls - 1] if len(bwd_ids) >= calls else step_end
     windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60),
                "baseconv": (bwd_end + 1, 1 << 60), "decay": (bwd_end + 1, 1 << 60)}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     workloads = {"layer": "based360m", "bwd": "based360m layer backward (both attentions)",
                  "decode": "decode (256 x 16 heads)", "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)",
                  "decay": "based360m decayed linear attention"}
@@ -462,14 +463,14 @@ def summarize_pmc(fetch_dir, write_dir, calls, command):
                "copy_kernel": short_name(cname), "copy_fetch_factor": f_scale, "copy_write_factor": w_scale,
                "bytes_per_call": tot_f + tot_w, "fetch_bytes_per_call": tot_f, "write_bytes_per_call": tot_w,
                "kernels": detail}
-        with open(os.path.join(ROOT, "profiles", f"traffic_{op}.json"), "w") as fh:
+        with open(os.path.join(out_dir, f"traffic_{op}.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec, indent=1))
 
 
-def summarize_stats(stats_dir, command, calls):
-    """profiles/kernel_stats.md from a rocprofv3 --kernel-trace --stats run of
-    this script: average duration of every kernel.  The step workload runs
+def summarize_stats(stats_dir, command, calls, out_dir=None):
+    """<out_dir>/kernel_stats.md (default: profiles/) from a rocprofv3
+    --kernel-trace --stats run of this script: average duration of every kernel.  The step workload runs
     first and ends with its `calls`-th launch of the fused main pass; its
     dispatches are reported apart from the rest."""
     files = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
@@ -507,8 +508,9 @@ def summarize_stats(stats_dir, command, calls):
     for (name, grid, blk, phase), d in groups.items():
         lines.append(f"| `{name}` | {grid} | {blk} | {phase} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
                      f"{max(d):.1f} |")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    out = os.path.join(ROOT, "profiles", "kernel_stats.md")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "kernel_stats.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
