@@ -95,6 +95,80 @@ def phi(x) -> np.ndarray:
     return np.concatenate([np.ones(lead + (1,)), x, quad], axis=-1)
 
 
+# --------------------------------------------------------------------------
+# Compact state  [BLOG, feature-map pseudocode and the paragraph on the state]
+# --------------------------------------------------------------------------
+D_CMP = 1 + D_K + D_K * (D_K + 1) // 2  # 153: constant, linear, unordered pairs
+
+
+def pairs(d: int = D_K):
+    """The unordered index pairs (a, b), a <= b, a outermost."""
+    return [(a, b) for a in range(d) for b in range(a, d)]
+
+
+def _pair_rows():
+    """For each unordered pair: its row (a, b) and row (b, a) in phi's layout,
+    and whether the pair is off the diagonal."""
+    a = np.array([p[0] for p in pairs()])
+    b = np.array([p[1] for p in pairs()])
+    return 1 + D_K + D_K * a + b, 1 + D_K + D_K * b + a, a != b
+
+
+def state_compact(S, z):
+    """A state with one row per unordered pair of the quadratic features.
+
+    phi lists x_a x_b / sqrt(2) under both orders of a pair, so every state the
+    recurrence builds has equal rows (a, b) and (b, a), and phi(q)^T S only uses
+    their sum.  Compact rows: the constant and linear rows as they are, then
+    for each pair of pairs(): S[(a,b)] + S[(b,a)] for a < b, S[(a,a)] for
+    a = b.  S [..., 273, d_v], z [..., 273] -> [..., 153, d_v], [..., 153].
+    """
+    S, z = _f64(S), _f64(z)
+    rab, rba, off = _pair_rows()
+    Sq = S[..., rab, :] + np.where(off[:, None], S[..., rba, :], 0.0)
+    zq = z[..., rab] + np.where(off, z[..., rba], 0.0)
+    return (np.concatenate([S[..., : 1 + D_K, :], Sq], axis=-2),
+            np.concatenate([z[..., : 1 + D_K], zq], axis=-1))
+
+
+def state_expand(Sc, zc):
+    """The 273-row state of a compact one: both ordered rows of an off-diagonal
+    pair get half of the pair row, the diagonal rows the pair row itself."""
+    Sc, zc = _f64(Sc), _f64(zc)
+    rab, rba, off = _pair_rows()
+    lead = Sc.shape[:-2]
+    S = np.zeros(lead + (D_PHI, Sc.shape[-1]))
+    z = np.zeros(zc.shape[:-1] + (D_PHI,))
+    S[..., : 1 + D_K, :] = Sc[..., : 1 + D_K, :]
+    z[..., : 1 + D_K] = zc[..., : 1 + D_K]
+    half = np.where(off, 0.5, 1.0)
+    S[..., rab, :] = Sc[..., 1 + D_K:, :] * half[:, None]
+    S[..., rba, :] = Sc[..., 1 + D_K:, :] * half[:, None]
+    z[..., rab] = zc[..., 1 + D_K:] * half
+    z[..., rba] = zc[..., 1 + D_K:] * half
+    return S, z
+
+
+def phi_compact_key(x) -> np.ndarray:
+    """What a key adds to the compact state's rows: 1, x_a, then per pair
+    sqrt(2) x_a x_b off the diagonal (both ordered rows' x_a x_b / sqrt(2))
+    and x_a^2 / sqrt(2) on it."""
+    x = _f64(x)
+    a = np.array([p[0] for p in pairs()])
+    b = np.array([p[1] for p in pairs()])
+    quad = x[..., a] * x[..., b] * np.where(a != b, np.sqrt(2.0), _INV_SQRT2)
+    return np.concatenate([np.ones(x.shape[:-1] + (1,)), x, quad], axis=-1)
+
+
+def phi_compact_query(x) -> np.ndarray:
+    """Readout weights of the compact state's rows: 1, x_a, then
+    x_a x_b / sqrt(2) per pair (the weight of either ordered row)."""
+    x = _f64(x)
+    a = np.array([p[0] for p in pairs()])
+    b = np.array([p[1] for p in pairs()])
+    return np.concatenate([np.ones(x.shape[:-1] + (1,)), x, x[..., a] * x[..., b] * _INV_SQRT2], axis=-1)
+
+
 def taylor_kernel(s) -> np.ndarray:
     """1 + s + s^2/2: the 2nd-order Taylor expansion of exp(s) [BLOG]."""
     s = _f64(s)

@@ -482,3 +482,61 @@ def test_decay_decode_matches_decayed_forward():
         yp0 = O.linattn_quadratic(q, k, v)[0][..., t, :]
         np.testing.assert_allclose(yp, yp0, rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(ys, ysp, rtol=0, atol=0)  # the window part does not decay
+
+
+# ------------------------------------------------------------ compact state
+def test_compact_layout():
+    """153 rows: constant, 16 linear, then the 136 unordered pairs a <= b with
+    a outermost (the order the header states for the compact decode state)."""
+    assert O.D_CMP == 153 == 1 + 16 + 136
+    P = O.pairs()
+    assert len(P) == 136 and P[0] == (0, 0) and P[1] == (0, 1) and P[15] == (0, 15) and P[16] == (1, 1)
+    assert P[-1] == (15, 15) and len(set(P)) == 136 and all(a <= b for a, b in P)
+
+
+def test_compact_readout_identity_for_any_state():
+    """phi(q)^T S depends on rows (a, b), (b, a) only through their sum, so the
+    compact state read with the compact query weights gives the pages' readout
+    for any S, symmetric or not (numerator and denominator)."""
+    g = np.random.default_rng(21)
+    S = g.normal(size=(3, 273, 8))
+    z = g.normal(size=(3, 273))
+    q = g.normal(size=(3, 16))
+    Sc, zc = O.state_compact(S, z)
+    pq, pqc = O.phi(q), O.phi_compact_query(q)
+    np.testing.assert_allclose(np.einsum("hf,hfd->hd", pqc, Sc), np.einsum("hf,hfd->hd", pq, S), rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose((pqc * zc).sum(-1), (pq * z).sum(-1), rtol=1e-12, atol=1e-12)
+
+
+def test_compact_update_identity():
+    """What a key adds to the 273-row state, compacted, is what the compact key
+    feature adds: compact(phi(k) v^T) = phi_c(k) v^T, compact(phi(k)) = phi_c(k)."""
+    g = np.random.default_rng(22)
+    k, v = g.normal(size=(4, 16)), g.normal(size=(4, 8))
+    Sc, zc = O.state_compact(O.phi(k)[:, :, None] * v[:, None, :], O.phi(k))
+    np.testing.assert_allclose(Sc, O.phi_compact_key(k)[:, :, None] * v[:, None, :], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(zc, O.phi_compact_key(k), rtol=1e-13, atol=1e-15)
+    # a diagonal pair row takes k_a^2 / sqrt2 once, an off-diagonal one sqrt2 k_a k_b
+    x = np.zeros(16)
+    x[2], x[5] = 3.0, 7.0
+    f = O.phi_compact_key(x)
+    row = {p: 17 + i for i, p in enumerate(O.pairs())}
+    assert f[row[(2, 2)]] == pytest.approx(9.0 / np.sqrt(2.0))
+    assert f[row[(2, 5)]] == pytest.approx(21.0 * np.sqrt(2.0))
+    assert f[row[(5, 5)]] == pytest.approx(49.0 / np.sqrt(2.0))
+    assert np.count_nonzero(f[17:]) == 3
+
+
+def test_compact_round_trips():
+    """expand(compact(S)) = S for a state the recurrence builds (its ordered
+    pair rows are equal), and compact(expand(Sc)) = Sc for any compact state,
+    both exactly."""
+    g = np.random.default_rng(23)
+    k, v = g.normal(size=(2, 40, 16)) * 0.25, g.normal(size=(2, 40, 8))
+    S, z = O.linattn_state(k, v)
+    S2, z2 = O.state_expand(*O.state_compact(S, z))
+    assert np.array_equal(S2, S) and np.array_equal(z2, z)
+    Sc, zc = g.normal(size=(2, 153, 8)), g.normal(size=(2, 153))
+    Sc2, zc2 = O.state_compact(*O.state_expand(Sc, zc))
+    assert np.array_equal(Sc2, Sc) and np.array_equal(zc2, zc)
