@@ -53,6 +53,7 @@ MFMA_BF16_PEAK_TFS = 2516.6  # dense bf16 matrix peak
 METRIC = "Based layer fwd tokens/s @L=2k-32k + decode tokens/s; % MFMA/HBM roofline"
 
 D_PHI = 273
+D_CMP = 153  # rows of the compact decode state (one per unordered feature pair)
 
 
 def lin_bytes(dv, es=2):
@@ -87,10 +88,11 @@ def bwd_bytes(dv, es=2):
     return (2 * 16 + dv) * es + 2 * 4 * dv + (2 * 16 + dv) * 4
 
 
-def decode_bytes(dv=64, window=64, es=2):
-    """Per head-step: S and z read + written (fp32), the ring's other
-    window-1 slots read, q/k/v read, one ring slot written, y_lin and y_swa written."""
-    return (2 * D_PHI * dv * 4 + 2 * D_PHI * 4 + (window - 1) * (16 + dv) * es + (2 * 16 + dv) * es
+def decode_bytes(dv=64, window=64, es=2, rows=D_PHI):
+    """Per head-step: S and z read + written (fp32, `rows` state rows: 273,
+    or 153 in the compact layout), the ring's other window-1 slots read,
+    q/k/v read, one ring slot written, y_lin and y_swa written."""
+    return (2 * rows * dv * 4 + 2 * rows * 4 + (window - 1) * (16 + dv) * es + (2 * 16 + dv) * es
             + (16 + dv) * es + 2 * dv * 4)
 
 
@@ -100,6 +102,7 @@ OP_SOURCES = {
     "layer": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
     "bwd": ["linattn_bwd_mfma.hip", "swa_bwd_mfma.hip", "linattn_mfma.hip", "launchers.h", "based_device.h"],
     "decode": ["decode.hip", "launchers.h", "based_device.h"],
+    "decode_compact": ["decode.hip", "launchers.h", "based_device.h"],
     "baseconv": ["baseconv.hip", "launchers.h", "based_device.h"],
     "decay": ["linattn_mfma.hip", "launchers.h", "based_device.h"],
 }
@@ -108,7 +111,8 @@ OP_KERNELS = {
     "layer": ["linattn_mfma_kernel<4, 1, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "slice_sum_kernel",
             "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>"],
-    "decode": ["decode_step_kernel"],
+    "decode": ["decode_step_kernel<unsigned short, 64, 273>"],
+    "decode_compact": ["decode_step_kernel<unsigned short, 64, 153>"],
     "baseconv": ["baseconv_kernel"],
     "decay": ["linattn_mfma_kernel<4, 0, 1>", "linattn_state_kernel<4, 1>"],
 }
@@ -324,13 +328,14 @@ def bench_decay(lal, cfg, steps, warmup, nbuf=8):
             "traffic_bytes_per_call": load_traffic("decay")}
 
 
-def bench_decode(lal, cfg, warmup=5, decay=False):
+def bench_decode(lal, cfg, warmup=5, decay=False, compact=False):
     """Prefill (untimed), then cfg.steps decode steps timed as one block
     (decay: the decayed linear attention, per-head decays from
-    synth.decay_rates; same bytes per step)."""
+    synth.decay_rates; same bytes per step; compact: the state with one row
+    per unordered feature pair, 153 rows instead of 273)."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, 0)
     g = synth.decay_rates(cfg.H).cuda() if decay else None
-    _, _, st = lal.decode_init(qc.cuda(), kc.cuda(), vc.cuda(), cfg.window, gamma=g)
+    _, _, st = lal.decode_init(qc.cuda(), kc.cuda(), vc.cuda(), cfg.window, gamma=g, compact=compact)
     del qc, kc, vc
     qd, kd, vd = qs.cuda(), ks.cuda(), vs.cuda()
     B, H, dv = cfg.B, cfg.H, cfg.dv
@@ -347,9 +352,10 @@ def bench_decode(lal, cfg, warmup=5, decay=False):
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / n
-    byts = decode_bytes(dv, cfg.window) * B * H
+    byts = decode_bytes(dv, cfg.window, rows=D_CMP if compact else D_PHI) * B * H
+    name = "decode" + (" (decayed)" if decay else "") + (", compact state" if compact else "")
     return {
-        "workload": "decode (decayed)" if decay else "decode", "sequences": B, "heads": H, "context": cfg.ctx, "steps_timed": n,
+        "workload": name, "sequences": B, "heads": H, "context": cfg.ctx, "steps_timed": n,
         "us_per_step": us, "tokens_per_s": B / (us * 1e-6), "hbm_gbs": byts / (us * 1e-6) / 1e9,
         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": byts,
     }
@@ -439,10 +445,12 @@ def summarize_pmc(fetch_dir, write_dir, calls, command, out_dir=None):
     step_end = max(i for (i, n) in fetch_all if STEP_KERNEL in n and i < first_bwd)
     bwd_end = bwd_ids[calls - 1] if len(bwd_ids) >= calls else step_end
     windows = {"layer": (0, step_end), "bwd": (step_end + 1, bwd_end), "decode": (bwd_end + 1, 1 << 60),
+               "decode_compact": (bwd_end + 1, 1 << 60),
                "baseconv": (bwd_end + 1, 1 << 60), "decay": (bwd_end + 1, 1 << 60)}
     os.makedirs(out_dir, exist_ok=True)
     workloads = {"layer": "based360m", "bwd": "based360m layer backward (both attentions)",
-                 "decode": "decode (256 x 16 heads)", "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)",
+                 "decode": "decode (256 x 16 heads)", "decode_compact": "decode, compact state (256 x 16 heads)",
+                 "baseconv": "baseconv360m (8 x 2048 x 1024, 3 taps)",
                  "decay": "based360m decayed linear attention"}
     for op, frags in OP_KERNELS.items():
         tot_f = tot_w = 0.0
@@ -553,6 +561,7 @@ def main():
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
     extra, decode, separate, backward, conv, decay, decode_decay = [], None, None, None, None, None, None
+    decode_compact = None
     if not args.no_extra:
         backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
         del bsets
@@ -576,6 +585,10 @@ def main():
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
         decode_decay = bench_decode(lal, synth.DECODE_CONFIG, decay=True)
         print(f"[bench] decode (decayed): {decode_decay['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+        decode_compact = bench_decode(lal, synth.DECODE_CONFIG, compact=True)
+        decode_compact["traffic_bytes_per_step"] = load_traffic("decode_compact")
+        print(f"[bench] decode (compact state): {decode_compact['us_per_step']:.1f} us/step", file=sys.stderr,
+              flush=True)
     cpu = None if args.no_cpu else cpu_baseline(cfg)
 
     # the step is one operation (state-only pass + segment scan + fused main pass)
@@ -603,6 +616,7 @@ def main():
         "other_workloads": extra,
         "decode": decode,
         "decode_decay": decode_decay,
+        "decode_compact": decode_compact,
     }
     print(json.dumps(out))
 

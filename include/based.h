@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 6
+#define BASED_ABI_VERSION 7
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -73,6 +73,7 @@ enum {
 
 #define BASED_DK 16        /* q/k head dimension of the Taylor linear attention */
 #define BASED_DPHI 273     /* 1 + 16 + 16*16 Taylor features                    */
+#define BASED_DCMP 153     /* compact decode state: 1 + 16 + 16*17/2 rows       */
 #define BASED_MAX_WINDOW 64
 #define BASED_MAX_CONV 4     /* longest BaseConv filter (taps)                   */
 
@@ -307,6 +308,47 @@ int based_decode_step_decay(const void* q, const void* k, const void* v, const f
                             float* y_lin, float* y_swa,
                             int B, int H, int d_k, int d_v, int window, float scale, int dtype,
                             void* stream);
+
+/*
+ * based_decode_step (and, with a non-NULL gamma, based_decode_step_decay) on
+ * a state in the compact layout: one row per unordered pair of the quadratic
+ * features.  Every state the recurrence builds has S[(a,b)] = S[(b,a)] for the
+ * rows of the ordered pairs (k_a k_b / sqrt2 both), and the readout and the
+ * update use only their sum, so one row per pair carries the same state
+ * (blog post, paragraph on the state; feature map of the linear attention):
+ *   S  [B,H,153,d_v] fp32: row 0 the constant feature, rows 1..16 the linear
+ *      features, then for a = 0..15, b = a..15 in that order the pair (a, b),
+ *      holding S[(a,b)] + S[(b,a)] for a < b and S[(a,a)] on the diagonal;
+ *   z  [B,H,153] fp32 likewise.
+ * The step moves 56 % of the state bytes of based_decode_step and gives its
+ * results for a symmetric 273-row state up to rounding order (pair rows are
+ * updated once with sqrt2 k_a k_b v instead of twice with k_a k_b v / sqrt2).
+ * Convert with based_state_compact / based_state_expand.  gamma: [H] fp32 or
+ * NULL (no decay), as in based_decode_step_decay.  Every other argument and
+ * every error as in based_decode_step.
+ */
+int based_decode_step_compact(const void* q, const void* k, const void* v, const float* gamma,
+                              float* S, float* z, void* ring_k, void* ring_v, int32_t* pos,
+                              float* y_lin, float* y_swa,
+                              int B, int H, int d_k, int d_v, int window, float scale, int dtype,
+                              void* stream);
+
+/*
+ * State layout conversions for based_decode_step_compact (layouts as there).
+ *   based_state_compact: S [B,H,273,d_v], z [B,H,273] -> Sc [B,H,153,d_v],
+ *     zc [B,H,153]; a pair row is the sum of the two ordered rows.
+ *   based_state_expand: Sc, zc -> S, z; both ordered rows of a pair get half
+ *     the pair row (so expand(compact(S)) = S for a symmetric S, and
+ *     compact(expand(Sc)) = Sc).
+ * All fp32 device pointers; outputs must not overlap inputs or each other.
+ * d_v in {16, 32, ..., 128}.  Errors: BASED_ERR_SHAPE (B, H < 1 or too
+ * large), BASED_ERR_UNSUPPORTED (d_v), BASED_ERR_NULL, BASED_ERR_ALIGN
+ * (pointers not 16-byte aligned), BASED_ERR_ALIAS, BASED_ERR_LAUNCH.
+ */
+int based_state_compact(const float* S, const float* z, float* Sc, float* zc, int B, int H, int d_v,
+                        void* stream);
+int based_state_expand(const float* Sc, const float* zc, float* S, float* z, int B, int H, int d_v,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbased.so")
 DK = 16
 DPHI = 273
+DCMP = 153  # compact decode state rows: constant, 16 linear, 136 unordered pairs
 F32, BF16 = 0, 1
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -46,6 +47,9 @@ _SIGNATURES = {
     "based_baseconv_fwd": (_i, [_vp] * 5 + [_i] * 5 + [_vp]),
     "based_linattn_decay_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
     "based_decode_step_decay": (_i, [_vp] * 11 + [_i] * 5 + [_f, _i, _vp]),
+    "based_decode_step_compact": (_i, [_vp] * 11 + [_i] * 5 + [_f, _i, _vp]),
+    "based_state_compact": (_i, [_vp] * 4 + [_i] * 3 + [_vp]),
+    "based_state_expand": (_i, [_vp] * 4 + [_i] * 3 + [_vp]),
 }
 
 
@@ -294,13 +298,16 @@ def baseconv_fwd(x, u, h, bias=None, *, y=None):
 @dataclass
 class DecodeState:
     """Caller-owned generation state: S [B,H,273,dv] fp32, z [B,H,273] fp32,
-    ring_k [B,H,W,16], ring_v [B,H,W,dv] (input dtype), pos [B] int32."""
+    ring_k [B,H,W,16], ring_v [B,H,W,dv] (input dtype), pos [B] int32.  With
+    ``compact`` the state has one row per unordered feature pair: S
+    [B,H,153,dv], z [B,H,153] (see :func:`state_compact`)."""
 
     S: torch.Tensor
     z: torch.Tensor
     ring_k: torch.Tensor
     ring_v: torch.Tensor
     pos: torch.Tensor
+    compact: bool = False
 
     @property
     def window(self) -> int:
@@ -315,12 +322,13 @@ def decode_prefill(k, v, state: DecodeState) -> None:
                                     B, H, L, dk, v.shape[-1], state.window, _dtype_code(k), _stream()))
 
 
-def decode_init(q, k, v, window: int = 64, gamma=None):
+def decode_init(q, k, v, window: int = 64, gamma=None, compact: bool = False):
     """Consume a context (q, k, v [B,H,L,.]): returns (y_lin, y_swa, state)
     where the outputs are the context's own layer outputs and ``state`` is
     ready for :func:`decode_step` at position L.  With a per-head decay gamma
     [H] the linear attention is the decayed one (then continue with
-    decode_step(..., gamma=gamma))."""
+    decode_step(..., gamma=gamma)).  ``compact``: the state in the compact
+    layout (one row per unordered feature pair)."""
     B, H, L, _ = k.shape
     dv = v.shape[-1]
     if gamma is None:
@@ -328,9 +336,11 @@ def decode_init(q, k, v, window: int = 64, gamma=None):
     else:
         y_lin, S, z = linattn_decay_fwd(q, k, v, gamma, return_state=True)
         y_swa = swa_fwd(q, k, v, window)
+    if compact:
+        S, z = state_compact(S, z)
     st = DecodeState(S, z, torch.zeros(B, H, window, DK, device=k.device, dtype=k.dtype),
                      torch.zeros(B, H, window, dv, device=k.device, dtype=k.dtype),
-                     torch.zeros(B, device=k.device, dtype=torch.int32))
+                     torch.zeros(B, device=k.device, dtype=torch.int32), compact)
     decode_prefill(k, v, st)
     return y_lin, y_swa, st
 
@@ -350,8 +360,33 @@ def decode_step(state: DecodeState, q, k, v, scale: float = 1.0, *, y_lin=None, 
         y_swa = torch.empty(B, H, dv, device=q.device, dtype=torch.float32)
     common = (_ptr(state.S), _ptr(state.z), _ptr(state.ring_k), _ptr(state.ring_v), _ptr(state.pos), _ptr(y_lin),
               _ptr(y_swa), B, H, dk, dv, state.window, float(scale), _dtype_code(q), _stream())
-    if gamma is None:
+    if state.compact:
+        _check(_lib().based_decode_step_compact(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *common))
+    elif gamma is None:
         _check(_lib().based_decode_step(_ptr(q), _ptr(k), _ptr(v), *common))
     else:
         _check(_lib().based_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *common))
     return y_lin, y_swa
+
+
+def state_compact(S, z, *, Sc=None, zc=None):
+    """A state S [B,H,273,dv], z [B,H,273] (fp32) in the compact layout:
+    Sc [B,H,153,dv], zc [B,H,153] -- rows 0..16 as in S, then for a <= b the
+    pair row S[(a,b)] + S[(b,a)] (S[(a,a)] on the diagonal)."""
+    B, H, _, dv = S.shape
+    _dev(S, z, Sc, zc)
+    Sc = torch.empty(B, H, DCMP, dv, device=S.device, dtype=torch.float32) if Sc is None else Sc
+    zc = torch.empty(B, H, DCMP, device=S.device, dtype=torch.float32) if zc is None else zc
+    _check(_lib().based_state_compact(_ptr(S), _ptr(z), _ptr(Sc), _ptr(zc), B, H, dv, _stream()))
+    return Sc, zc
+
+
+def state_expand(Sc, zc, *, S=None, z=None):
+    """The 273-row state of a compact one: each ordered pair row gets half its
+    pair row (the diagonal as is)."""
+    B, H, _, dv = Sc.shape
+    _dev(Sc, zc, S, z)
+    S = torch.empty(B, H, DPHI, dv, device=Sc.device, dtype=torch.float32) if S is None else S
+    z = torch.empty(B, H, DPHI, device=Sc.device, dtype=torch.float32) if z is None else z
+    _check(_lib().based_state_expand(_ptr(Sc), _ptr(zc), _ptr(S), _ptr(z), B, H, dv, _stream()))
+    return S, z

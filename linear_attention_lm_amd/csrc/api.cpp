@@ -283,7 +283,8 @@ BASED_API int based_decode_prefill(const void* k, const void* v, void* ring_k, v
 
 static int decode_step_impl(const void* q, const void* k, const void* v, const float* gamma, float* S, float* z,
                             void* ring_k, void* ring_v, int32_t* pos, float* y_lin, float* y_swa, int B, int H,
-                            int d_k, int d_v, int window, float scale, int dtype, void* stream) {
+                            int d_k, int d_v, int window, float scale, int dtype, void* stream,
+                            bool compact = false) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
   if (B < 1 || H < 1) return BASED_ERR_SHAPE;
   if ((long long)B * H > (1LL << 30) || B > 0x7fffffff) return BASED_ERR_SHAPE;
@@ -295,7 +296,8 @@ static int decode_step_impl(const void* q, const void* k, const void* v, const f
   for (const void* p : ptrs)
     if (!aligned16(p)) return BASED_ERR_ALIGN;
   const size_t BH = (size_t)B * H, es = elem_size(dtype);
-  const Span outs[] = {span(S, BH * BASED_DPHI * d_v * 4), span(z, BH * BASED_DPHI * 4),
+  const size_t rows = compact ? BASED_DCMP : BASED_DPHI;
+  const Span outs[] = {span(S, BH * rows * d_v * 4), span(z, BH * rows * 4),
                        span(ring_k, BH * window * d_k * es), span(ring_v, BH * window * d_v * es),
                        span(pos, (size_t)B * 4), span(y_lin, BH * d_v * 4), span(y_swa, BH * d_v * 4)};
   const Span ins[] = {span(q, BH * d_k * es), span(k, BH * d_k * es), span(v, BH * d_v * es)};
@@ -310,7 +312,7 @@ static int decode_step_impl(const void* q, const void* k, const void* v, const f
     for (const Span& o : outs)
       if (overlap(o, g)) return BASED_ERR_ALIAS;
   }
-  based::DecodeArgs a{q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_v, window, scale, gamma};
+  based::DecodeArgs a{q, k, v, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_v, window, scale, gamma, compact};
   return status_of(based::launch_decode_step(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 
@@ -328,4 +330,43 @@ BASED_API int based_decode_step_decay(const void* q, const void* k, const void* 
   if (!gamma) return BASED_ERR_NULL;
   return decode_step_impl(q, k, v, gamma, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_k, d_v, window, scale,
                           dtype, stream);
+}
+
+BASED_API int based_decode_step_compact(const void* q, const void* k, const void* v, const float* gamma, float* S,
+                                        float* z, void* ring_k, void* ring_v, int32_t* pos, float* y_lin,
+                                        float* y_swa, int B, int H, int d_k, int d_v, int window, float scale,
+                                        int dtype, void* stream) {
+  return decode_step_impl(q, k, v, gamma, S, z, ring_k, ring_v, pos, y_lin, y_swa, B, H, d_k, d_v, window, scale,
+                          dtype, stream, true);
+}
+
+static int state_convert(const float* in, const float* zin, float* out, float* zout, int B, int H, int d_v,
+                         bool to_compact, void* stream) {
+  if (B < 1 || H < 1 || (long long)B * H > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (!valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  const void* ptrs[] = {in, zin, out, zout};
+  for (const void* p : ptrs)
+    if (!p) return BASED_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BASED_ERR_ALIGN;
+  const size_t BH = (size_t)B * H;
+  const size_t rin = to_compact ? BASED_DPHI : BASED_DCMP, rout = to_compact ? BASED_DCMP : BASED_DPHI;
+  const Span ins[] = {span(in, BH * rin * d_v * 4), span(zin, BH * rin * 4)};
+  const Span outs[] = {span(out, BH * rout * d_v * 4), span(zout, BH * rout * 4)};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlap(o, i)) return BASED_ERR_ALIAS;
+  if (overlap(outs[0], outs[1])) return BASED_ERR_ALIAS;
+  return status_of(to_compact ? based::launch_state_compact(in, zin, out, zout, BH, d_v, (hipStream_t)stream)
+                              : based::launch_state_expand(in, zin, out, zout, BH, d_v, (hipStream_t)stream));
+}
+
+BASED_API int based_state_compact(const float* S, const float* z, float* Sc, float* zc, int B, int H, int d_v,
+                                  void* stream) {
+  return state_convert(S, z, Sc, zc, B, H, d_v, true, stream);
+}
+
+BASED_API int based_state_expand(const float* Sc, const float* zc, float* S, float* z, int B, int H, int d_v,
+                                 void* stream) {
+  return state_convert(Sc, zc, S, z, B, H, d_v, false, stream);
 }

@@ -11,7 +11,13 @@
 // gamma the factor is 1 and the update is the same arithmetic as above.
 //
 // The step streams the 273 x d_v fp32 state through once (read, update,
-// write back) and is bound by HBM bandwidth.  Layout of the work: one
+// write back) and is bound by HBM bandwidth.  A second state layout keeps
+// one row per unordered pair (a, b) of the quadratic features: 153 rows
+// (constant, k_a, then the pairs a <= b), the pair row holding
+// S[(a,b)] + S[(b,a)] (S[(a,a)] on the diagonal).  Every state the recurrence
+// builds has S[(a,b)] = S[(b,a)], and the readout and the update only ever
+// use that sum, so the compact step computes the same result from 56 % of
+// the state bytes.  Layout of the work: one
 // workgroup per sequence (so the position counter can be advanced race-free),
 // one wavefront per head at a time (MAXW wavefronts stride over the heads).
 // phi(k) and phi(q) are formed once per head into LDS.  Inside a wavefront,
@@ -72,7 +78,46 @@ __device__ __forceinline__ float4 fma4(float a, float4 x, float4 acc) {
                      __builtin_fmaf(a, x.w, acc.w));
 }
 
-template <typename T, int DV>
+// Rows of the compact state and its pair table: compact row 1 + DK + p holds
+// the pair (a, b) = (pair_a[p], pair_b[p]), a <= b, in row-major order.
+constexpr int DCMP = 1 + DK + DK * (DK + 1) / 2;
+struct PairTable {
+  uint8_t a[DK * (DK + 1) / 2], b[DK * (DK + 1) / 2];
+  constexpr PairTable() : a(), b() {
+    int p = 0;
+    for (int i = 0; i < DK; ++i)
+      for (int j = i; j < DK; ++j) {
+        a[p] = (uint8_t)i;
+        b[p] = (uint8_t)j;
+        ++p;
+      }
+  }
+};
+__constant__ PairTable c_pairs = PairTable();
+
+// (key feature, query feature) of state row f, from q and k in LDS.  Full
+// layout (DPHI rows): 1, x_a, then the ordered pairs x_a x_b / sqrt2.
+// Compact layout (DCMP rows): 1, x_a, then the unordered pairs a <= b; a
+// pair row gathers the updates of both ordered rows, so its key feature is
+// sqrt2 k_a k_b off the diagonal (k_a^2 / sqrt2 on it), and the readout
+// weighs it by q_a q_b / sqrt2 like either ordered row.
+template <int NROW>
+__device__ __forceinline__ float2 row_features(int f, const float* qv, const float* kv) {
+  if (f == 0) return make_float2(1.f, 1.f);
+  if (f < 1 + DK) return make_float2(kv[f - 1], qv[f - 1]);
+  int a, bb;
+  if constexpr (NROW == DPHI) {
+    a = (f - 1 - DK) / DK;
+    bb = (f - 1 - DK) % DK;
+  } else {
+    a = c_pairs.a[f - 1 - DK];
+    bb = c_pairs.b[f - 1 - DK];
+  }
+  const float kf = (NROW != DPHI && a != bb) ? kv[a] * kv[bb] * SQRT2 : kv[a] * kv[bb] * INV_SQRT2;
+  return make_float2(kf, qv[a] * qv[bb] * INV_SQRT2);
+}
+
+template <typename T, int DV, int NROW>
 __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ S,
     float* __restrict__ z, T* __restrict__ ring_k, T* __restrict__ ring_v, int32_t* __restrict__ pos,
@@ -80,15 +125,15 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
     const float* __restrict__ gamma) {
   constexpr int CG = DV / 4;                     // lanes per state row (4 columns each)
   constexpr int RG = 64 / CG;                    // rows per wavefront instruction
-  constexpr int NI = (DPHI + RG - 1) / RG;       // state rows per lane
+  constexpr int NI = (NROW + RG - 1) / RG;       // state rows per lane
   constexpr int NB = 16;                         // state rows per load batch
   constexpr int NBATCH = (NI + NB - 1) / NB;
   constexpr int NR = (64 + RG - 1) / RG;         // ring rows per lane (window <= 64)
   constexpr int RB = 8, NRB = (NR + RB - 1) / RB;  // ring rows per load batch
-  constexpr int NZ = (DPHI + 63) / 64;           // z rows per lane
+  constexpr int NZ = (NROW + 63) / 64;           // z rows per lane
   constexpr int ES = sizeof(T);
   __shared__ float qk_s[MAXW][2][DK];
-  __shared__ float2 phi_s[MAXW][DPHI];  // (phi(k)_f, phi(q)_f) of the wavefront's head
+  __shared__ float2 phi_s[MAXW][NROW];  // (phi(k)_f, phi(q)_f) of the wavefront's head
   __shared__ float4 red_s[MAXW][64];
   __shared__ float p_s[MAXW][64];
   __shared__ int t_s;
@@ -102,14 +147,14 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
   const bool active = rg < RG;
   const int slot = t % window;  // the ring slot of token t (it held token t - window)
   // per-lane byte offsets: row rg, columns 4cg..4cg+3 (inactive lanes past the end)
-  const int voff_s = active ? (rg * DV + 4 * cg) * 4 : DPHI * DV * 4;
+  const int voff_s = active ? (rg * DV + 4 * cg) * 4 : NROW * DV * 4;
   const int voff_r = active ? (rg * DV + 4 * cg) * ES : 64 * DV * ES;
 
   for (int h = wave; h < H; h += nw) {
     const size_t bh = (size_t)b * H + h;
     const float gm = gamma ? gamma[h] : 1.f;  // state decay of the head (gm * x = x exactly when 1)
-    const auto rS = rsrc(S + bh * DPHI * DV, DPHI * DV * 4);
-    const auto rZ = rsrc(z + bh * DPHI, DPHI * 4);
+    const auto rS = rsrc(S + bh * NROW * DV, NROW * DV * 4);
+    const auto rZ = rsrc(z + bh * NROW, NROW * 4);
     const auto rK = rsrc(ring_k + bh * (size_t)window * DK, window * DK * ES);
     const auto rV = rsrc(ring_v + bh * (size_t)window * DV, window * DV * ES);
 
@@ -161,19 +206,10 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
 #pragma unroll
     for (int j = 0; j < NZ; ++j) {
       const int f = lane + 64 * j;
-      if (f < DPHI) {
-        float pk, pq;
-        if (f == 0) {
-          pk = pq = 1.f;
-        } else if (f < 1 + DK) {
-          pk = qk_s[wave][1][f - 1];
-          pq = qk_s[wave][0][f - 1];
-        } else {
-          const int a = (f - 1 - DK) / DK, bb = (f - 1 - DK) % DK;
-          pk = qk_s[wave][1][a] * qk_s[wave][1][bb] * INV_SQRT2;
-          pq = qk_s[wave][0][a] * qk_s[wave][0][bb] * INV_SQRT2;
-        }
-        phi_s[wave][f] = make_float2(pk, pq);
+      if (f < NROW) {
+        const float2 fe = row_features<NROW>(f, qk_s[wave][0], qk_s[wave][1]);
+        const float pk = fe.x, pq = fe.y;
+        phi_s[wave][f] = fe;
         const float zn = gm * zl[j] + pk;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zn), rZ, lane * 4, 256 * j, 0);
         den += pq * zn;
@@ -241,7 +277,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int f = rg + RG * (bt * NB + i);
-          if (active && f < DPHI) {
+          if (active && f < NROW) {
             const float2 ph = phi_s[wave][f];
             const float4 sd = make_float4(gm * buf[i].x, gm * buf[i].y, gm * buf[i].z, gm * buf[i].w);
             const float4 sn = fma4(ph.x, vr, sd);
@@ -299,9 +335,14 @@ __global__ void decode_prefill_kernel(const T* __restrict__ k, const T* __restri
 template <typename T, int DV>
 hipError_t launch_step(const DecodeArgs& a, hipStream_t s) {
   const int nw = a.H < MAXW ? a.H : MAXW;
-  hipLaunchKernelGGL((decode_step_kernel<T, DV>), dim3(a.B), dim3(64 * nw), 0, s, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, a.S, a.z, (T*)a.ring_k, (T*)a.ring_v, a.pos, a.y_lin, a.y_swa, a.H, a.window,
-                     a.scale, a.gamma);
+  if (a.compact)
+    hipLaunchKernelGGL((decode_step_kernel<T, DV, DCMP>), dim3(a.B), dim3(64 * nw), 0, s, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.S, a.z, (T*)a.ring_k, (T*)a.ring_v, a.pos, a.y_lin, a.y_swa,
+                       a.H, a.window, a.scale, a.gamma);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<T, DV, DPHI>), dim3(a.B), dim3(64 * nw), 0, s, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.S, a.z, (T*)a.ring_k, (T*)a.ring_v, a.pos, a.y_lin, a.y_swa,
+                       a.H, a.window, a.scale, a.gamma);
   return hipGetLastError();
 }
 
@@ -320,10 +361,68 @@ hipError_t launch_step_t(const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Layout conversions of a state (n = B*H heads of rows x cols; z: cols 1).
+// Compact row 1 + DK + p of pair (a, b): S[(a,b)] + S[(b,a)] (S[(a,a)]).
+__global__ void state_compact_kernel(const float* __restrict__ S, float* __restrict__ Sc, size_t n, int cols) {
+  const size_t total = n * DCMP * (size_t)cols;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t head = e / ((size_t)DCMP * cols);
+    const int r = (int)(e / cols % DCMP), c = (int)(e % cols);
+    const float* src = S + head * DPHI * cols;
+    float x;
+    if (r < 1 + DK) {
+      x = src[(size_t)r * cols + c];
+    } else {
+      const int a = c_pairs.a[r - 1 - DK], b = c_pairs.b[r - 1 - DK];
+      x = src[(size_t)(1 + DK + DK * a + b) * cols + c];
+      if (a != b) x += src[(size_t)(1 + DK + DK * b + a) * cols + c];
+    }
+    Sc[e] = x;
+  }
+}
+
+// Full row (a, b) of a compact state: the pair row halved (the diagonal as is).
+__global__ void state_expand_kernel(const float* __restrict__ Sc, float* __restrict__ S, size_t n, int cols) {
+  const size_t total = n * DPHI * (size_t)cols;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t head = e / ((size_t)DPHI * cols);
+    const int r = (int)(e / cols % DPHI), c = (int)(e % cols);
+    const float* src = Sc + head * DCMP * cols;
+    float x;
+    if (r < 1 + DK) {
+      x = src[(size_t)r * cols + c];
+    } else {
+      const int a0 = (r - 1 - DK) / DK, b0 = (r - 1 - DK) % DK;
+      const int a = a0 < b0 ? a0 : b0, b = a0 < b0 ? b0 : a0;
+      const int p = a * DK - a * (a - 1) / 2 + (b - a);  // row-major index of a <= b
+      x = src[(size_t)(1 + DK + p) * cols + c];
+      if (a != b) x *= 0.5f;
+    }
+    S[e] = x;
+  }
+}
+
+static unsigned conv_blocks(size_t total) {
+  const size_t b = (total + 255) / 256;
+  return (unsigned)(b < 16384 ? b : 16384);
+}
+
 }  // namespace
 
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_step_t<bf16_t>(a, s) : launch_step_t<float>(a, s);
+}
+
+hipError_t launch_state_compact(const float* S, const float* z, float* Sc, float* zc, size_t n, int dv, hipStream_t s) {
+  hipLaunchKernelGGL(state_compact_kernel, dim3(conv_blocks(n * DCMP * dv)), dim3(256), 0, s, S, Sc, n, dv);
+  hipLaunchKernelGGL(state_compact_kernel, dim3(conv_blocks(n * DCMP)), dim3(256), 0, s, z, zc, n, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_expand(const float* Sc, const float* zc, float* S, float* z, size_t n, int dv, hipStream_t s) {
+  hipLaunchKernelGGL(state_expand_kernel, dim3(conv_blocks(n * DPHI * dv)), dim3(256), 0, s, Sc, S, n, dv);
+  hipLaunchKernelGGL(state_expand_kernel, dim3(conv_blocks(n * DPHI)), dim3(256), 0, s, zc, z, n, 1);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos, int B, int H,

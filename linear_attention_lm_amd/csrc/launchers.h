@@ -80,8 +80,15 @@ struct DecodeArgs {
   float* y_lin; float* y_swa;
   int B, H, dv, window; float scale;
   const float* gamma = nullptr;  // [H] per-head state decay (decayed variant only)
+  bool compact = false;          // S [.,153,dv], z [.,153]: one row per unordered feature pair
 };
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
+// State layout conversions over n heads: 273-row <-> compact 153-row.
+hipError_t launch_state_compact(const float* S, const float* z, float* Sc, float* zc, size_t n, int dv,
+                                hipStream_t stream);
+hipError_t launch_state_expand(const float* Sc, const float* zc, float* S, float* z, size_t n, int dv,
+                               hipStream_t stream);
 
 hipError_t launch_decode_prefill(const void* k, const void* v, void* ring_k, void* ring_v, int32_t* pos,
                                  int B, int H, int L, int dv, int window, bool bf16, hipStream_t stream);

@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 6
+    assert so.based_abi_version() == 7
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -239,3 +239,32 @@ def test_decode_decay_validation(so):
     assert call(dv=20) == ERR["UNSUPPORTED"]
     assert call(win=65) == ERR["WINDOW"]
     assert call(gam=S) == ERR["ALIAS"]          # gamma inside the state S
+
+
+def test_decode_compact_validation(so):
+    """The compact step checks the 153-row state's extent (a z just past a
+    153-row S does not overlap it, one inside it does) and takes a null gamma."""
+    big = 0x100000
+    B, H, dv = 2, 3, 64
+    S = big
+    z_after = S + B * H * 153 * dv * 4
+    q, k, v, rk, rv, pos, yl, ys = (big * (i + 2) * 16 for i in range(8))
+    call = lambda gam=None, z=z_after, dt=1, d=dv: so.based_decode_step_compact(
+        q, k, v, gam, S, z, rk, rv, pos, yl, ys, B, H, 16, d, 64, 1.0, dt, None)
+    assert call(dt=3) == ERR["DTYPE"]
+    assert call(d=24) == ERR["UNSUPPORTED"]
+    assert call(z=z_after - 16) == ERR["ALIAS"]
+    assert call(gam=S + 64) == ERR["ALIAS"]     # gamma inside the state
+
+
+def test_state_conversion_validation(so):
+    big = 0x1000000
+    B, H, dv = 2, 3, 32
+    S, z, Sc, zc = big, 2 * big, 3 * big, 4 * big
+    assert so.based_state_compact(S, z, Sc, zc, 0, H, dv, None) == ERR["SHAPE"]
+    assert so.based_state_compact(S, z, Sc, zc, B, H, 20, None) == ERR["UNSUPPORTED"]
+    assert so.based_state_compact(S, None, Sc, zc, B, H, dv, None) == ERR["NULL"]
+    assert so.based_state_compact(S + 4, z, Sc, zc, B, H, dv, None) == ERR["ALIGN"]
+    assert so.based_state_compact(S, z, S + 16, zc, B, H, dv, None) == ERR["ALIAS"]
+    assert so.based_state_expand(Sc, zc, S, Sc, B, H, dv, None) == ERR["ALIAS"]
+    assert so.based_state_expand(Sc, zc, S, S + B * H * 273 * dv * 4 - 16, B, H, dv, None) == ERR["ALIAS"]

@@ -21,7 +21,8 @@ STATE = "void based::mfma::linattn_state_kernel<4, 0>(based::mfma::Params)"
 MAIN = "void based::mfma::linattn_mfma_kernel<4, 1, 0>(based::mfma::Params)"
 QPASS = "based::bwdm::query_pass_kernel(based::bwdm::Params)"
 SWAB = "void based::swab::swa_bwd_mfma_kernel<4>(based::swab::Params)"
-DECODE = "void based::(anonymous namespace)::decode_step_kernel<unsigned short, 64>(int)"
+DECODE = "void based::(anonymous namespace)::decode_step_kernel<unsigned short, 64, 273>(int)"
+DECODE_C = "void based::(anonymous namespace)::decode_step_kernel<unsigned short, 64, 153>(int)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -39,6 +40,7 @@ def test_algorithmic_bytes():
     assert bench.bwd_bytes(64) == 1088     # q, k, v, y, dy read; dq, dk, dv written
     # per head-step of decode: S and z read and written, the ring, q/k/v, outputs
     assert bench.decode_bytes(64, 64) == 152904
+    assert bench.decode_bytes(64, 64, rows=153) == 152904 - 2 * 120 * (64 + 1) * 4
 
 
 def _write_counters(path, rows):
@@ -60,7 +62,7 @@ def _dispatches():
             (6, STATE, 1200.0, 100.0), (7, MAIN, 3400.0, 900.0),     # step 2
             (8, QPASS, 500.0, 50.0), (9, QPASS, 500.0, 50.0),
             (10, SWAB, 700.0, 70.0), (11, SWAB, 700.0, 70.0),
-            (12, DECODE, 40.0, 40.0)]
+            (12, DECODE, 40.0, 40.0), (13, DECODE_C, 22.0, 22.0)]
 
 
 def test_summarize_pmc_scales_and_windows(tmp_path):
@@ -88,6 +90,9 @@ def test_summarize_pmc_scales_and_windows(tmp_path):
     assert bwd["bytes_per_call"] == pytest.approx(((500 + 700) * 0.5 + 50 + 70) * 1024)
     dec = json.loads((out / "traffic_decode.json").read_text())
     assert dec["bytes_per_call"] == pytest.approx((40 * 0.5 + 40) * 1024)
+    # the two state layouts' decode steps are told apart by the row count
+    dc = json.loads((out / "traffic_decode_compact.json").read_text())
+    assert dc["bytes_per_call"] == pytest.approx((22 * 0.5 + 22) * 1024)
 
 
 def test_summarize_pmc_needs_the_copy(tmp_path):
@@ -121,7 +126,7 @@ def test_summarize_stats_marks_step_and_backward(tmp_path):
     assert "| step | 3 | 58.0 |" in lines["based::mfma::linattn_mfma_kernel<4, 1, 0>"]
     assert "| bwd | 2 | 83.0 |" in lines["based::bwdm::query_pass_kernel"]
     assert "| bwd | 2 | 71.0 |" in lines["based::swab::swa_bwd_mfma_kernel<4>"]
-    assert "|  | 1 | 5.0 |" in lines["based::decode_step_kernel<unsigned short, 64>"]
+    assert "|  | 1 | 5.0 |" in lines["based::decode_step_kernel<unsigned short, 64, 273>"]
 
 
 def test_traffic_is_null_once_the_sources_change(tmp_path, monkeypatch):

@@ -13,15 +13,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_decode(based, cfg, seqs=None, check_steps=None, seed=0):
+def run_decode(based, cfg, seqs=None, check_steps=None, seed=0, compact=False):
     """Prefill on the GPU (linear attention state export + ring fill), then
-    cfg.steps decode steps; compare the sampled sequences with the oracle."""
+    cfg.steps decode steps; compare the sampled sequences with the oracle
+    (compact: the state in the compact layout, compared with the oracle's
+    state compacted)."""
     (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg, seed)
-    say(f"decode B{cfg.B} H{cfg.H} ctx{cfg.ctx} steps{cfg.steps} dv{cfg.dv} {cfg.dtype}")
+    say(f"decode B{cfg.B} H{cfg.H} ctx{cfg.ctx} steps{cfg.steps} dv{cfg.dv} {cfg.dtype}"
+        + (" compact" if compact else ""))
     seqs = list(range(cfg.B)) if seqs is None else seqs
     check_steps = set(range(cfg.steps)) if check_steps is None else set(check_steps)
     tol = TOL[qc.dtype]
-    _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window)
+    _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window, compact=compact)
     ref = O.DecodeState.prefill(kc[seqs], vc[seqs], cfg.window)
     errs = []
     qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
@@ -35,8 +38,9 @@ def run_decode(based, cfg, seqs=None, check_steps=None, seed=0):
     torch.cuda.synchronize()
     report(f"decode y_lin B{cfg.B} ctx{cfg.ctx}", max(e[0] for e in errs), tol)
     report(f"decode y_swa B{cfg.B} ctx{cfg.ctx}", max(e[1] for e in errs), tol)
-    assert rowinf_rel(st.S[seqs], ref.S) <= tol
-    assert rowinf_rel(st.z[seqs], ref.z) <= tol
+    S_ref, z_ref = O.state_compact(ref.S, ref.z) if compact else (ref.S, ref.z)
+    assert rowinf_rel(st.S[seqs], S_ref) <= tol
+    assert rowinf_rel(st.z[seqs], z_ref) <= tol
     assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
     return st
 
@@ -106,7 +110,7 @@ def test_decode_snapshot_restore(based):
         assert torch.equal(a1, a2.cpu()) and torch.equal(b1, b2.cpu())
 
 
-def run_decay_decode(based, cfg):
+def run_decay_decode(based, cfg, compact=False):
     """Decode with a per-head state decay (heads cycle through 1, 0.75,
     0.875, ...): the context's state from based_linattn_decay_fwd (bf16) or an
     empty one (ctx = 0), then steps through based_decode_step_decay, against
@@ -120,14 +124,15 @@ def run_decay_decode(based, cfg):
     if cfg.ctx > 0:
         _, _, S, z = O.linattn_decay_recurrent(qc, kc, vc, g.numpy())
         ref.S, ref.z = S, z
-        _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window, gamma=gd)
+        _, _, st = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), cfg.window, gamma=gd, compact=compact)
     else:
         ref.S[:], ref.z[:] = 0.0, 0.0
         B, H = cfg.B, cfg.H
-        st = based.DecodeState(torch.zeros(B, H, O.D_PHI, cfg.dv, device=DEV), torch.zeros(B, H, O.D_PHI, device=DEV),
+        rows = O.D_CMP if compact else O.D_PHI
+        st = based.DecodeState(torch.zeros(B, H, rows, cfg.dv, device=DEV), torch.zeros(B, H, rows, device=DEV),
                                torch.zeros(B, H, cfg.window, 16, device=DEV, dtype=qc.dtype),
                                torch.zeros(B, H, cfg.window, cfg.dv, device=DEV, dtype=qc.dtype),
-                               torch.zeros(B, device=DEV, dtype=torch.int32))
+                               torch.zeros(B, device=DEV, dtype=torch.int32), compact)
     qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
     el = es = 0.0
     for s in range(cfg.steps):
@@ -138,7 +143,8 @@ def run_decay_decode(based, cfg):
     torch.cuda.synchronize()
     report(f"decay decode y_lin ctx{cfg.ctx} {cfg.dtype}", el, tol)
     report(f"decay decode y_swa ctx{cfg.ctx} {cfg.dtype}", es, tol)
-    assert rowinf_rel(st.S, ref.S) <= tol and rowinf_rel(st.z, ref.z) <= tol
+    S_ref, z_ref = O.state_compact(ref.S, ref.z) if compact else (ref.S, ref.z)
+    assert rowinf_rel(st.S, S_ref) <= tol and rowinf_rel(st.z, z_ref) <= tol
     assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
     return st
 
@@ -164,3 +170,71 @@ def test_decay_decode_gamma_one_is_plain_decode(based):
         yb = based.decode_step(b, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV), gamma=ones)
         assert torch.equal(ya[0], yb[0]) and torch.equal(ya[1], yb[1])
     assert torch.equal(a.S, b.S) and torch.equal(a.z, b.z)
+
+
+# ------------------------------------------------------------- compact state
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compact_decode_small_wraps_ring(based, dtype):
+    cfg = synth.DecodeConfig("small", B=3, H=4, ctx=100, steps=70, dtype=dtype)
+    run_decode(based, cfg, compact=True)
+
+
+@pytest.mark.parametrize("dv,window", [(128, 64), (16, 9), (80, 64)])
+def test_compact_decode_shapes(based, dv, window):
+    cfg = synth.DecodeConfig("shape", B=2, H=20, ctx=37, steps=30, dv=dv, window=window)
+    run_decode(based, cfg, compact=True)
+
+
+def test_compact_decode_full_workload_sampled(based):
+    cfg = synth.DECODE_CONFIG.replace(steps=72)
+    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=[0, 1, 2, 63, 64, 71], compact=True)
+
+
+def test_compact_decay_decode_after_context(based):
+    run_decay_decode(based, synth.DecodeConfig("decay", B=2, H=8, ctx=150, steps=70, dtype="bf16"), compact=True)
+
+
+def test_compact_decay_decode_from_empty_context(based):
+    run_decay_decode(based, synth.DecodeConfig("decay0", B=2, H=9, ctx=0, steps=40, dv=48, dtype="f32"),
+                     compact=True)
+
+
+def test_state_conversions_match_oracle(based):
+    """based_state_compact / based_state_expand against the oracle's
+    definitions: a random (non-symmetric) state compacted (pair rows summed
+    in fp32), and a random compact state expanded (exact halves)."""
+    g = torch.Generator().manual_seed(31)
+    B, H, dv = 2, 5, 48
+    S, z = torch.randn(B, H, 273, dv, generator=g), torch.randn(B, H, 273, generator=g)
+    Sc, zc = based.state_compact(S.to(DEV), z.to(DEV))
+    rS, rz = O.state_compact(S, z)
+    err = max(rowinf_rel(Sc, rS), rowinf_rel(zc, rz))
+    report("state_compact vs oracle", err, 1e-6)
+    assert err <= 1e-6
+    C, cz = torch.randn(B, H, 153, dv, generator=g), torch.randn(B, H, 153, generator=g)
+    S2, z2 = based.state_expand(C.to(DEV), cz.to(DEV))
+    eS, ez = O.state_expand(C, cz)
+    assert np.array_equal(S2.double().cpu().numpy(), eS) and np.array_equal(z2.double().cpu().numpy(), ez)
+    C2, cz2 = based.state_compact(S2, z2)
+    assert torch.equal(C2.cpu(), C) and torch.equal(cz2.cpu(), cz)
+
+
+def test_compact_and_full_decode_agree(based):
+    """The same context and tokens through both layouts: outputs within fp32
+    rounding of each other, and the expanded compact state equals the full
+    one to the same order."""
+    cfg = synth.DecodeConfig("both", B=2, H=6, ctx=90, steps=40, dtype="f32")
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg)
+    _, _, full = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV))
+    _, _, comp = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), compact=True)
+    worst = 0.0
+    for s in range(cfg.steps):
+        a = based.decode_step(full, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV))
+        b = based.decode_step(comp, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV))
+        worst = max(worst, rowinf_rel(b[0], a[0].double().cpu().numpy()))
+        assert torch.equal(a[1], b[1])  # the window attention does not touch the state
+    report("compact vs full decode y_lin", worst, 1e-5)
+    assert worst <= 1e-5
+    S, z = based.state_expand(comp.S, comp.z)
+    assert rowinf_rel(S, full.S.double().cpu().numpy()) <= 1e-5
+    assert torch.all(comp.pos == full.pos)
