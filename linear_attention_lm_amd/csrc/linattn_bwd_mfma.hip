@@ -57,7 +57,7 @@ constexpr int NKS = (NF + 31) / 32;  // 9 steps of 32 features (the last half ze
 constexpr int QH = 24;               // fp16 stride of q / k rows
 constexpr int XT = C + 8;            // fp16 stride of transposed chunk rows
 constexpr int RS = SW + 8;           // fp16 stride of slice rows
-constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for w = 0)
+constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for one)
 constexpr int SCALE_TOP = 13;
 constexpr int MAXSEG = 8;            // segments per head at most (records summed directly)
 constexpr int NFC = 160;             // compact slots of the forward's state records
@@ -107,7 +107,10 @@ static_assert(slots_ok(), "every feature must map to a compact slot");
 __constant__ FeatureSlots c_slots = make_feature_slots();
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-__device__ __forceinline__ int own_count(int w) { return w == 0 ? 5 : 4; }
+// Wavefront w owns feature tiles w, w + 4, w + 8, w + 12; tile 16 goes to
+// wavefront xw, which each pass picks as the one its causal in-chunk work
+// leaves lightest (wavefront 0 in the query pass, 3 in the key pass).
+__device__ __forceinline__ int own_count(int w, int xw) { return w == xw ? 5 : 4; }
 __device__ __forceinline__ int own_tile(int w, int j) { return j < 4 ? w + 4 * j : 16; }
 
 __device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w))
+      if (j < own_count(w, 0))
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     up = __builtin_amdgcn_ldexpf(1.f, e);
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 0)) {
         const int mt = own_tile(w, j);
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const size_t rows = NFC + 1;
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 0)) {
         const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
         float z = 0.f;
         for (int r = 1; r <= un.seg; ++r) {
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     // ---- state update with the chunk: S^T += V^T phi(K), z += phi(K)^T 1
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 0)) {
         const int mt = own_tile(w, j);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -736,7 +739,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
     if (t0 + C < un.t_end) k_load(p, rs, s, t0 + C, pf);
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 0)) {
         const int mt = own_tile(w, j);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + un.seg) * (size_t)RREC;
 #pragma unroll
   for (int j = 0; j < MAXOWN; ++j) {
-    if (j < own_count(w)) {
+    if (j < own_count(w, 0)) {
       const int f = 16 * own_tile(w, j) + r16;
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn)
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w))
+      if (j < own_count(w, 3))
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -808,7 +811,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     up = __builtin_amdgcn_ldexpf(1.f, e);
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 3)) {
         const int mt = own_tile(w, j);
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       const float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + r) * (size_t)RREC;
 #pragma unroll
       for (int j = 0; j < MAXOWN; ++j) {
-        if (j < own_count(w)) {
+        if (j < own_count(w, 3)) {
           const int f = 16 * own_tile(w, j) + r16;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
@@ -973,7 +976,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     // ---- state update with the chunk: R^T += G^T phi(Q), r += phi(Q)^T h
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w)) {
+      if (j < own_count(w, 3)) {
         const int mt = own_tile(w, j);
         // g and h rounded once to fp16 (the state is read back as an fp16 copy)
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
