@@ -28,9 +28,10 @@ hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
 // The decayed variant (per-head gamma in a.gamma), same layouts and workspace.
 hipError_t launch_linattn_decay_mfma(const LinattnArgs& a, hipStream_t stream);
 // The state-only pass alone (zero initial state; bf16, d_v in {32, 64, 96, 128}):
-// compact segment increments at ws, as the main pass's records.
+// compact segment increments at ws, as the main pass's records, for the
+// first nrec segments of each head (nrec <= nseg - 1).
 hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
-                                        int seg_chunks, hipStream_t stream);
+                                        int seg_chunks, int nrec, hipStream_t stream);
 // The same pass with the sliding-window softmax of the same q, k, v fused in
 // (d_qk = d_k = 16), written to y_swa.
 hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t stream);

@@ -213,10 +213,12 @@ struct Params {
   size_t npos;          // B * H * L
   float* gq; float* gk; float* gv;
   float* pq; float* pk;  // with several slices: [nslice][npos][16] shares of dq and dk
-  const float* frec;    // [BH][nseg] forward records of (NFC + 1) dvf floats, record_offset layout (record s + 1: segment s)
-  const float* frecz;   // [BH][nseg][NFC + 1]
+  const float* frec;    // [BH][nseg * rsplit] forward records of (NFC + 1) dvf floats, record_offset layout
+                        // (record s + 1: sub-segment s, seg_chunks / rsplit chunks from s * seg_chunks / rsplit)
+  const float* frecz;   // [BH][nseg * rsplit][NFC + 1]
   float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
   int L, dvf, nslice, nseg, seg_chunks;
+  int rsplit;           // forward-record sub-segments per segment
 };
 
 // Workgroup -> (head, value slice, segment) and the segment's positions.
@@ -445,8 +447,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       if (j < own_count(w, 0)) {
         const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
         float z = 0.f;
-        for (int r = 1; r <= un.seg; ++r) {
-          const size_t rec = (bh * p.nseg + r) * rows + slot;
+        for (int r = 1; r <= un.seg * p.rsplit; ++r) {
+          const size_t rec = (bh * p.nseg * p.rsplit + r) * rows + slot;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -1032,6 +1034,18 @@ void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
   *nseg = nch < 1 ? 1 : (nch + sc - 1) / sc;
 }
 
+// Forward-record sub-segments per backward segment.  With two segments the
+// records cover only the first, as B*H workgroups of the state-only pass:
+// splitting it (down to 8 chunks) brings the pass to one workgroup per CU.
+// With more segments each record adds a step to the query pass's serial
+// record sum, so there is no split.
+static int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks) {
+  int r = 1;
+  if (nseg != 2) return r;
+  while (r < 4 && (long long)BH * 2 * r <= 256 && seg_chunks % (2 * r) == 0 && seg_chunks / (2 * r) >= 8) r *= 2;
+  return r;
+}
+
 size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   int nseg, sc;
   const int BH = B * H;
@@ -1040,7 +1054,8 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   size_t floats = (size_t)(1 + nslice) * BH * L;                           // den, h per slice
   if (nslice > 1) floats += (size_t)2 * nslice * BH * L * DK;               // dq, dk shares per slice
   if (nseg > 1) {
-    floats += (size_t)BH * nseg * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
+    const int rs = linattn_bwd_rec_split(BH, nseg, sc);
+    floats += (size_t)BH * nseg * rs * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
     floats += (size_t)BH * (dv / bwdm::SW) * nseg * bwdm::RREC;                      // suffix records
   }
   return floats * sizeof(float);
@@ -1064,14 +1079,18 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
     p.pk = part + (size_t)p.nslice * npos * DK;
     part += (size_t)2 * p.nslice * npos * DK;
   }
+  p.rsplit = linattn_bwd_rec_split((int)BH, p.nseg, p.seg_chunks);
+  const int nrec_seg = p.nseg * p.rsplit;  // forward-record sub-segments per head
   float* frec = part;
   p.frec = frec;
-  p.frecz = frec + BH * p.nseg * (size_t)(NFC + 1) * a.dv;
-  p.krec = const_cast<float*>(p.frecz) + BH * p.nseg * (size_t)(NFC + 1);
+  p.frecz = frec + BH * nrec_seg * (size_t)(NFC + 1) * a.dv;
+  p.krec = const_cast<float*>(p.frecz) + BH * nrec_seg * (size_t)(NFC + 1);
   const unsigned grid = (unsigned)(BH * p.nslice * p.nseg);
   const size_t n4 = npos * DK / 4, cblocks = (n4 + 255) / 256;
   if (p.nseg > 1) {
-    if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, p.nseg, p.seg_chunks, s);
+    // the sub-segments before the last segment (no segment reads the last one's)
+    if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, nrec_seg,
+                                                    p.seg_chunks / p.rsplit, (p.nseg - 1) * p.rsplit, s);
         e != hipSuccess)
       return e;
   }

@@ -159,6 +159,7 @@ struct Params {
   float swa_scale;
   const float* gamma;  // [H] state decay per head (decayed variant)
   int H;
+  int nrec;            // state-only pass: segments per head it covers (0: nseg - 1)
 };
 
 // Decayed variant: log2 of the head's decay factor, and gamma^d from it.
@@ -1102,7 +1103,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   constexpr int G = DEC ? SG / 2 : SG;
   __shared__ StateSmem<NT> S;
 
-  const int nsm = p.nseg - 1;
+  const int nsm = p.nrec ? p.nrec : p.nseg - 1;
   int bhi, seg;
   xcd_unit_part(blockIdx.x, gridDim.x / nsm, nsm, bhi, seg);
   const size_t bh = bhi;
@@ -1301,27 +1302,29 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
 
 // State-only pass on its own (zero initial state): records [BH][nseg][NF + 1][dv]
 // and [BH][nseg][NF + 1] at ws / wsz, record s + 1 = the compact increment of
-// segment s (s < nseg - 1), slot values sum_t [k_a | k_a^2 | k_a k_b] v_t.
+// segment s for s < nrec (nrec <= nseg - 1), slot values
+// sum_t [k_a | k_a^2 | k_a k_b] v_t.
 template <int NT>
 static hipError_t launch_state_records_nt(const void* k, const void* v, float* ws, int BH, int L, int nseg,
-                                          int seg_chunks, hipStream_t s) {
+                                          int seg_chunks, int nrec, hipStream_t s) {
   Params p{};
   p.k = (const bf16_t*)k; p.v = (const bf16_t*)v;
-  p.L = L; p.nseg = nseg; p.seg_chunks = seg_chunks;
+  p.L = L; p.nseg = nseg; p.seg_chunks = seg_chunks; p.nrec = nrec;
   p.ws = ws;
   p.wsz = ws + (size_t)BH * nseg * (NF + 1) * (16 * NT);
-  hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * (nseg - 1)), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
-                                        int seg_chunks, hipStream_t s) {
-  if (nseg < 2) return hipSuccess;
+                                        int seg_chunks, int nrec, hipStream_t s) {
+  if (nseg < 2 || nrec < 1) return hipSuccess;
+  if (nrec > nseg - 1) return hipErrorInvalidValue;
   switch (dv) {
-    case 32: return launch_state_records_nt<2>(k, v, ws, BH, L, nseg, seg_chunks, s);
-    case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, s);
-    case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, s);
-    case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, s);
+    case 32: return launch_state_records_nt<2>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
+    case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
+    case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
+    case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
   }
   return hipErrorInvalidValue;
 }
