@@ -440,21 +440,51 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
   };
   // the state before the segment: the sum of the forward records of the
   // earlier segments (slot values sum_t [k_a | k_a^2 | k_a k_b] v_t)
+  // (records 1 .. nr of the head, through buffer resources that end at
+  // record nr: an odd first record alone, then two records per round with
+  // both records' loads in flight together)
   if (un.seg > 0) {
-    const size_t rows = NFC + 1;
+    const int rows = NFC + 1, nr = un.seg * p.rsplit;
+    const size_t first = bh * p.nseg * p.rsplit + 1;
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.frec + first * rows * p.dvf), (short)0, nr * rows * p.dvf * (int)sizeof(float), RSRC_DW3);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.frecz + first * rows), (short)0, nr * rows * (int)sizeof(float), RSRC_DW3);
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
       if (j < own_count(w, 0)) {
         const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
         float z = 0.f;
-        for (int r = 1; r <= un.seg * p.rsplit; ++r) {
-          const size_t rec = (bh * p.nseg * p.rsplit + r) * rows + slot;
+        if (nr & 1) {  // record 1 on its own
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[j][nn][i] += p.frec[(rec - slot) * p.dvf + record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf)];
-          z += p.frecz[rec];
+              acc[j][nn][i] += bload1(rf, (int)record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf) *
+                                              (int)sizeof(float));
+          z += bload1(rz, slot * (int)sizeof(float));
+        }
+        for (int r = nr & 1; r < nr; r += 2) {  // pairs (an odd record first, alone)
+          float x[2][2][4], zz[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                x[u][nn][i] = bload1(rf, ((r + u) * rows * p.dvf +
+                                          (int)record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf)) *
+                                             (int)sizeof(float));
+            zz[u] = bload1(rz, ((r + u) * rows + slot) * (int)sizeof(float));
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[j][nn][i] += x[u][nn][i];
+            z += zz[u];
+          }
         }
         zacc[j] = z;
       }
@@ -1035,13 +1065,14 @@ void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
 }
 
 // Forward-record sub-segments per backward segment.  With two segments the
-// records cover only the first, as B*H workgroups of the state-only pass:
-// splitting it (down to 8 chunks) brings the pass to one workgroup per CU.
-// With more segments each record adds a step to the query pass's serial
-// record sum, so there is no split.
+// records cover only the first, as B*H workgroups of the state-only pass;
+// where that leaves most of the CUs idle (B*H <= 64) the record is split
+// (down to 8 chunks, up to one workgroup per CU) and the query pass sums the
+// parts.  Otherwise the extra records cost the query pass about what the
+// shorter pass saves, and with more segments each one adds to that sum.
 static int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks) {
   int r = 1;
-  if (nseg != 2) return r;
+  if (nseg != 2 || BH > 64) return r;
   while (r < 4 && (long long)BH * 2 * r <= 256 && seg_chunks % (2 * r) == 0 && seg_chunks / (2 * r) >= 8) r *= 2;
   return r;
 }
