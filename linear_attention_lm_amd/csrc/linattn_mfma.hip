@@ -346,10 +346,16 @@ __device__ __forceinline__ f16x8 ones8() {
 // State update of one chunk: tacc += psi'(K)^T V over the chunk, and the
 // denominator state of the owned feature tiles, tz[slot] += psi'(K)^T 1
 // (every column of a tz tile holds it).
-template <int NT, int DEC = 0, int FREE = 0>
+//
+// VS: the wavefront with `vs_mine` also adds the chunk's column sums of v to
+// vsum (an all-ones A operand -- the key weights in the decayed variant --
+// against the v fragments the update loads anyway; every row of a vsum tile
+// holds the sums of its 16 columns).
+template <int NT, int DEC = 0, int FREE = 0, int VS = 0>
 __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_t* vh,
                                              f32x4 (&tacc)[Own<NT>::PPW], f32x4 (&tz)[3], const int (&ia)[3],
-                                             const int (&ib)[3], const f16x8* wk = nullptr) {
+                                             const int (&ib)[3], const f16x8* wk = nullptr,
+                                             f32x4* vsum = nullptr, bool vs_mine = false) {
   constexpr int H = NT / 2;
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const bool upper = (w & 1) != 0;  // slot 2 holds the upper half of the column tiles
@@ -381,6 +387,11 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
     tz[0] = mfma(a[0], ones, tz[0]);
     tz[1] = mfma(a[1], ones, tz[1]);
     if ((w & 1) == 0) tz[2] = mfma(a[2], ones, tz[2]);  // z of tile 8 + w/2 kept once
+    if constexpr (VS) {
+      if (vs_mine)  // uniform branch; decayed variant: each key's weight
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vsum[n] = mfma(DEC ? wk[ks] : ones, bv[n], vsum[n]);
+    }
     // keep the operands of the two K-steps from being live at once (FREE:
     // the caller has the registers to let the scheduler overlap them)
     if constexpr (!FREE) __builtin_amdgcn_sched_barrier(0);
@@ -783,15 +794,17 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     dcur[i] = after ? -INFINITY : 0.f;
     dprev[i] = after ? 0.f : -INFINITY;
   }
+  f32x4 vacc[NT];  // wavefront 0: the chunk's column sums of v
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
     const int n = min(C, tok_end - t0);
     __syncthreads();  // chunk inputs, published state, t0 visible
     const int tn = t0 + C;
     if (tn < tok_end) load_chunk<NT>(rs, tn, true, pf);
 
-    // ---- constant row of the state: column sums of v over the chunk, in
-    // PARTS partial sums per column (order within a row is irrelevant)
-    S.vpart[tid] = vsum_part<NT, DEC>(&S.vh[cur][0][0], n, lg);
+    // ---- constant row of the state: column sums of v over the chunk (the
+    // decayed variant here, in PARTS partial sums per column; otherwise
+    // wavefront 0 forms them in the update below)
+    if constexpr (DEC) S.vpart[tid] = vsum_part<NT, DEC>(&S.vh[cur][0][0], n, lg);
 
     // ---- readout of the state before the chunk, transposed (value columns x
     // positions): acc[nn][i] is column 16nn + 4g + i of position `pos`; every
@@ -1048,16 +1061,25 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       update_chunk<NT, 1>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib, wk);
       z0 = gn * z0 + gsum_pow(lg, n);
     } else {
-      update_chunk<NT>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib);
+      // wavefront 0 (the one the causal in-chunk term leaves lightest) adds
+      // the column sums of v (rows past n of a ragged chunk are zero)
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) vacc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      update_chunk<NT, 0, 0, 1>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib, nullptr, vacc, w == 0);
       z0 += (float)n;
     }
     post_max<NT>(S.wmax, tacc, tz);
     __syncthreads();  // every read of tt, t0 and the chunk buffers done; wmax complete
-    if (tid < DV) {
-      float vs = 0.f;
+    if constexpr (DEC) {
+      if (tid < DV) {
+        float vs = 0.f;
 #pragma unroll
-      for (int part = 0; part < PARTS; ++part) vs += S.vpart[part * DV + tid];
-      S.t0[tid] = gn * S.t0[tid] + vs;
+        for (int part = 0; part < PARTS; ++part) vs += S.vpart[part * DV + tid];
+        S.t0[tid] = gn * S.t0[tid] + vs;
+      }
+    } else if (w == 0 && g == 0) {
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) S.t0[16 * nn + r16] += vacc[nn][0];
     }
     e = state_scale(S.wmax, down, up);
     publish_state<NT>(S.tt, tacc, tz, e, down);
@@ -1089,7 +1111,6 @@ struct StateSmem {
   static constexpr int DV = 16 * NT;
   alignas(16) half_t kt[SG][DK + 1][KT];
   alignas(16) half_t vh[SG][C][vrow<NT>()];
-  alignas(16) float vpart[NTHR];
   alignas(16) float t0[DV];
   alignas(16) float zf[NF];
 };
@@ -1097,7 +1118,6 @@ struct StateSmem {
 template <int NT, int DEC = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
   constexpr int DV = 16 * NT;
-  constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1;
   // chunks per group (the decayed variant's extra per-chunk registers leave
   // room for half the prefetches)
   constexpr int G = DEC ? SG / 2 : SG;
@@ -1132,9 +1152,13 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   int ia[3], ib[3];
   slot_rows(ia, ib);
 
-  float vs = 0.f;  // this thread's share of the column sums of v (constant row)
+  // wavefront 0 carries the column sums of v (the constant row), formed in
+  // the updates from the v fragments they load
+  f32x4 vacc[NT];
+#pragma unroll
+  for (int nn = 0; nn < NT; ++nn) vacc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float lg = DEC ? decay_lg2(p, bh) : 0.f;
-  const int lane = tid & 63, g = lane >> 4;
+  const int lane = tid & 63, g = lane >> 4, w = wave_index(), r16 = lane & 15;
   for (int t = tok_begin; t < tok_end; t += G * C) {
     __syncthreads();  // the previous group's reads of LDS done
 #pragma unroll
@@ -1151,8 +1175,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
         // a chunk past the segment (n = 0) leaves everything unchanged
         const int n = min(C, max(0, tok_end - (t + i * C)));
         const float gn = gpow(lg, (float)n);
-        vs = gn * vs + vsum_part<NT, 1>(&S.vh[i][0][0], n, lg);
         z0 = gn * z0 + gsum_pow(lg, n);
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) vacc[nn] *= gn;
 #pragma unroll
         for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
 #pragma unroll
@@ -1165,31 +1190,26 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
             const int key = 32 * ks + 8 * g + e;
             wk[ks][e] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
           }
-        update_chunk<NT, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib, wk);
+        update_chunk<NT, 1, 0, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib, wk, vacc, w == 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        vs += vsum_part<NT, 0>(&S.vh[i][0][0], C, 0.f);
-        update_chunk<NT, 0, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib);
-      }
+      for (int i = 0; i < G; ++i)
+        update_chunk<NT, 0, 1, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib, nullptr, vacc, w == 0);
     }
   }
   if constexpr (!DEC) z0 += (float)(tok_end - tok_begin);
   __syncthreads();
-  S.vpart[tid] = vs;
   store_z<NT>(S.zf, tz);
+  if (w == 0 && g == 0)
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) S.t0[16 * nn + r16] = vacc[nn][0];
   __syncthreads();
   // segment 0: the caller's initial state, decayed over the segment
   const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
   const float gN = DEC ? gpow(lg, (float)(tok_end - tok_begin)) : 1.f;
-  if (tid < DV) {
-    float sum = Sin ? gN * Sin[tid] : 0.f;
-#pragma unroll
-    for (int q = 0; q < PARTS; ++q) sum += S.vpart[q * DV + tid];
-    S.t0[tid] = sum;
-  }
+  if (Sin && tid < DV) S.t0[tid] += gN * Sin[tid];
   if (zin) {
     for (int r = tid; r < NF; r += NTHR) S.zf[r] += gN * compact_from_phi(zin, r, 0, 1);
     z0 += gN * zin[0];
