@@ -187,7 +187,7 @@ struct Smem {
   alignas(16) half_t vh[NB][C][vrow<NT>()];  // v, row-major
   alignas(16) half_t tt[DV + 1][TT];     // scaled state^T; row DV: denominator state
   alignas(16) float t0[DV];              // constant row of the state (sum of v)
-  alignas(16) float vpart[NTHR];         // partial column sums of v
+  alignas(16) float vpart[NTHR];         // partial column sums of v (decayed variant)
   alignas(16) float zf[NF];              // denominator state (set-up and result)
   alignas(16) float wmax[4];             // per-wavefront largest state magnitude
 };
@@ -398,13 +398,14 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
   }
 }
 
-// This thread's share of the column sums of the chunk's v (row-major in LDS):
-// column tid % DV, rows part * SPAN .. + SPAN - 1 with part = tid / DV, read
-// four rows at a time with the transposing load (a 16-lane block covers 16
-// consecutive columns of one part).  Decayed variant: row t weighs
-// gamma^(n-1-t), rows past n none.
-template <int NT, int DEC>
-__device__ __forceinline__ float vsum_part(const half_t* vh, int n, float lg) {
+// Decayed main pass: this thread's share of the weighted column sums of the
+// chunk's v (row-major in LDS), row t weighing gamma^(n-1-t) and rows past n
+// none: column tid % DV, rows part * SPAN .. + SPAN - 1 with part = tid / DV,
+// read four rows at a time with the transposing load (a 16-lane block covers
+// 16 consecutive columns of one part).  (Elsewhere the update forms the
+// column sums with the matrix cores.)
+template <int NT>
+__device__ __forceinline__ float vsum_part_decayed(const half_t* vh, int n, float lg) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
   const int tid = threadIdx.x, col = tid % DV, part = tid / DV;
@@ -413,15 +414,10 @@ __device__ __forceinline__ float vsum_part(const half_t* vh, int n, float lg) {
 #pragma unroll
     for (int j = 0; j < SPAN; j += 4) {
       const f16x4 x = __builtin_bit_cast(f16x4, tr4(vh, part * SPAN + j, col & ~15, vrow<NT>()));
-      if constexpr (DEC) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = part * SPAN + j + e;
-          vs = __builtin_fmaf((float)x[e], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
-        }
-      } else {
-        vs = __builtin_amdgcn_fdot2(f16x2{x[0], x[1]}, f16x2{1, 1}, vs, false);
-        vs = __builtin_amdgcn_fdot2(f16x2{x[2], x[3]}, f16x2{1, 1}, vs, false);
+      for (int e = 0; e < 4; ++e) {
+        const int t = part * SPAN + j + e;
+        vs = __builtin_fmaf((float)x[e], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
       }
     }
   }
@@ -804,7 +800,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     // ---- constant row of the state: column sums of v over the chunk (the
     // decayed variant here, in PARTS partial sums per column; otherwise
     // wavefront 0 forms them in the update below)
-    if constexpr (DEC) S.vpart[tid] = vsum_part<NT, DEC>(&S.vh[cur][0][0], n, lg);
+    if constexpr (DEC) S.vpart[tid] = vsum_part_decayed<NT>(&S.vh[cur][0][0], n, lg);
 
     // ---- readout of the state before the chunk, transposed (value columns x
     // positions): acc[nn][i] is column 16nn + 4g + i of position `pos`; every
