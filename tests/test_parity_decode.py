@@ -238,3 +238,24 @@ def test_compact_and_full_decode_agree(based):
     S, z = based.state_expand(comp.S, comp.z)
     assert rowinf_rel(S, full.S.double().cpu().numpy()) <= 1e-5
     assert torch.all(comp.pos == full.pos)
+
+
+def test_compact_state_hands_over_to_full_decode(based):
+    """Steps on the compact state, then the state expanded and the rest on the
+    273-row step: the outputs follow an all-full run within fp32 rounding."""
+    cfg = synth.DecodeConfig("handover", B=2, H=5, ctx=40, steps=30, dv=32, dtype="f32")
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(cfg)
+    _, _, full = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV))
+    _, _, comp = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), compact=True)
+    worst = 0.0
+    for s in range(cfg.steps):
+        a = based.decode_step(full, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV))
+        if s == 12:  # hand the compact generation over to the full layout
+            S, z = based.state_expand(comp.S, comp.z)
+            comp = based.DecodeState(S, z, comp.ring_k, comp.ring_v, comp.pos)
+        b = based.decode_step(comp, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV))
+        worst = max(worst, rowinf_rel(b[0], a[0].double().cpu().numpy()))
+        assert torch.equal(a[1], b[1])
+    report("compact -> full handover y_lin", worst, 1e-5)
+    assert worst <= 1e-5
+    assert not comp.compact and comp.S.shape[2] == 273
