@@ -411,13 +411,18 @@ __device__ __forceinline__ float vsum_part_decayed(const half_t* vh, int n, floa
   const int tid = threadIdx.x, col = tid % DV, part = tid / DV;
   float vs = 0.f;
   if (part < PARTS) {  // whole wavefronts (DV divides 64 or is a multiple of 32)
+    // the weight of row t, advanced row by row by a factor 1/gamma from the
+    // thread's first row (rows past n are masked, whatever their weight)
+    const float ginv = __builtin_amdgcn_exp2f(-lg);
+    float wt = gpow(lg, (float)(n - 1 - part * SPAN));
 #pragma unroll
     for (int j = 0; j < SPAN; j += 4) {
       const f16x4 x = __builtin_bit_cast(f16x4, tr4(vh, part * SPAN + j, col & ~15, vrow<NT>()));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = part * SPAN + j + e;
-        vs = __builtin_fmaf((float)x[e], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
+        vs = __builtin_fmaf((float)x[e], t < n ? wt : 0.f, vs);
+        wt *= ginv;
       }
     }
   }
