@@ -476,6 +476,101 @@ def summarize_pmc(fetch_dir, write_dir, calls, command, out_dir=None):
         print(json.dumps(rec, indent=1))
 
 
+# Counter passes of the execution summary (each within one rocprofv3 --pmc
+# run's hardware limits: at most 8 SQ counters and 2 GRBM counters).
+COUNTER_PASSES = [
+    ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU_TRANS_F32",
+     "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"],
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+     "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_INSTS_VMEM", "GRBM_GUI_ACTIVE"],
+]
+CU_NUM, SIMD_NUM, NXCD = 256, 1024, 8
+
+
+def summarize_counters(dirs, command, kernels, out_name, out_dir=None):
+    """<out_dir>/<out_name> (default directory: profiles/) from rocprofv3
+    --pmc runs of this script, one directory per pass of COUNTER_PASSES: per
+    kernel whose name contains one of `kernels`, the median over its
+    dispatches of every counter, and from them
+
+      cycles          = GRBM_GUI_ACTIVE / 8 (the counter is summed over the
+                        eight XCDs, each with its own clock counter)
+      MFMA busy %     = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * 1024 SIMDs)
+      VALU busy %     = SQ_ACTIVE_INST_VALU / (cycles * 256 CUs)
+      LDS active %    = SQ_LDS_IDX_ACTIVE / (cycles * 256 CUs)
+      bank conflict   = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      waves per SIMD  = 4 * SQ_WAVE_CYCLES / (cycles * 1024 SIMDs)
+                        (SQ_WAVE_CYCLES counts quad-cycles)
+
+    (the busy formulas are rocprofv3's own MfmaUtil, VALUBusy and LdsUtil,
+    with its max over XCDs taken as the sum / 8) and the instructions each
+    wavefront issued."""
+    vals = {}  # kernel -> counter -> [per-dispatch values]
+    for d in dirs:
+        per = {}
+        for r in _counter_rows(d):
+            name = short_name(r["Kernel_Name"])
+            if not any(k in r["Kernel_Name"] for k in kernels):
+                continue
+            key = (int(r["Dispatch_Id"]), name, r["Counter_Name"])
+            v = float(r["Counter_Value"])
+            # GRBM_GUI_ACTIVE: one clock for the whole GPU (max over instances);
+            # SQ counters: summed over shader engines
+            per[key] = max(per.get(key, 0.0), v) if r["Counter_Name"] == "GRBM_GUI_ACTIVE" else per.get(key, 0.0) + v
+        for (_, name, cn), v in per.items():
+            vals.setdefault(name, {}).setdefault((d, cn), []).append(v)
+    lines = ["# Execution counters (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             "Median per dispatch over every dispatch of the kernel in the run. Derived figures, with",
+             "cycles = GRBM_GUI_ACTIVE / 8 (summed over the 8 XCDs' clock counters): MFMA busy =",
+             "SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); VALU busy = SQ_ACTIVE_INST_VALU /",
+             "(cycles x 256 CUs); LDS active = SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs); bank conflict =",
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; waves/SIMD = 4 x SQ_WAVE_CYCLES / (cycles x 1024",
+             "SIMDs); per-wave instruction counts = SQ_INSTS_* / SQ_WAVES.", "",
+             "| kernel | dispatches | cycles | MFMA busy % | VALU busy % | LDS active % | bank conflict | "
+             "waves/SIMD | VALU/wave | MFMA/wave | LDS/wave | SALU/wave | trans/wave | VMEM/wave |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    out_json = {}
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2] if xs else float("nan")
+
+    for name, cs in sorted(vals.items()):
+        m = {}
+        for (d, cn), xs in cs.items():
+            m[cn if cn != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE@{dirs.index(d)}"] = med(xs)
+        n = max(len(xs) for xs in cs.values())
+        gui0 = m.get("GRBM_GUI_ACTIVE@0", float("nan")) / NXCD
+        gui1 = m.get("GRBM_GUI_ACTIVE@1", float("nan")) / NXCD
+        waves = m.get("SQ_WAVES", float("nan"))
+        row = {
+            "dispatches": n, "gpu_cycles": gui1,
+            "mfma_busy_pct": 100 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui1 * SIMD_NUM),
+            "valu_busy_pct": 100 * m.get("SQ_ACTIVE_INST_VALU", float("nan")) / (gui1 * CU_NUM),
+            "lds_active_pct": 100 * m.get("SQ_LDS_IDX_ACTIVE", float("nan")) / (gui1 * CU_NUM),
+            "bank_conflict": m.get("SQ_LDS_BANK_CONFLICT", float("nan")) / m.get("SQ_LDS_IDX_ACTIVE", float("nan")),
+            "waves_per_simd": 4 * m.get("SQ_WAVE_CYCLES", float("nan")) / (gui0 * SIMD_NUM),
+            "valu_per_wave": m.get("SQ_INSTS_VALU", float("nan")) / waves,
+            "mfma_per_wave": m.get("SQ_INSTS_MFMA", float("nan")) / waves,
+            "lds_per_wave": m.get("SQ_INSTS_LDS", float("nan")) / waves,
+            "salu_per_wave": m.get("SQ_INSTS_SALU", float("nan")) / waves,
+            "trans_per_wave": m.get("SQ_INSTS_VALU_TRANS_F32", float("nan")) / waves,
+            "vmem_per_wave": m.get("SQ_INSTS_VMEM", float("nan")) / waves,
+            "raw": m,
+        }
+        out_json[name] = row
+        lines.append(f"| `{name}` | {n} | {gui1:.0f} | {row['mfma_busy_pct']:.1f} | {row['valu_busy_pct']:.1f} | "
+                     f"{row['lds_active_pct']:.1f} | {row['bank_conflict']:.3f} | {row['waves_per_simd']:.2f} | "
+                     f"{row['valu_per_wave']:.0f} | {row['mfma_per_wave']:.0f} | {row['lds_per_wave']:.0f} | "
+                     f"{row['salu_per_wave']:.0f} | {row['trans_per_wave']:.0f} | {row['vmem_per_wave']:.0f} |")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, out_name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return out_json
+
+
 def summarize_stats(stats_dir, command, calls, out_dir=None):
     """<out_dir>/kernel_stats.md (default: profiles/) from a rocprofv3
     --kernel-trace --stats run of this script: average duration of every kernel.  The step workload runs
@@ -537,7 +632,22 @@ def main():
     ap.add_argument("--pmc-command", default="", help="the command that produced the --pmc runs (recorded)")
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
                     help="write profiles/kernel_stats.md from a rocprofv3 --kernel-trace --stats run of this script")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PASS_DIR",
+                    help="write profiles/<--counters-out> from rocprofv3 --pmc runs of this script, one directory "
+                         "per pass of COUNTER_PASSES, in that order")
+    ap.add_argument("--counters-out", default="counters_layer.md")
+    ap.add_argument("--counter-kernels", default="based::",
+                    help="comma-separated kernel-name fragments to summarise")
+    ap.add_argument("--print-counter-pass", type=int, metavar="I",
+                    help="print the counters of pass I (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
+    if args.print_counter_pass is not None:
+        print(" ".join(COUNTER_PASSES[args.print_counter_pass]))
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.pmc_command, args.counter_kernels.split(","),
+                           args.counters_out)
+        return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.pmc_command, args.steps + args.warmup)
         return

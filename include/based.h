@@ -21,6 +21,11 @@
  * d_v), base pointers 16-byte aligned, living in device memory of the current
  * HIP device.  Inputs q, k, v have the element type `dtype`; outputs and
  * states are fp32.  Causal means inclusive: row i sees positions j <= i.
+ * One (batch, head) block of any [L, d] tensor must span fewer than 2^31
+ * bytes in fp32, L * d * 4 < 2^31 for every d of the call (the kernels
+ * address a head through 32-bit offsets): L < 4,194,304 at d = 128 and
+ * L < 8,388,608 at d = 64; longer sequences return BASED_ERR_SHAPE (split
+ * them with S_in / S_out).
  *
  * State layout (S_in, S_out, decode S: [B, H, 273, d_v]; z: [B, H, 273]):
  * row 0 is the constant feature, row 1 + a the linear feature x_a, row
@@ -109,16 +114,24 @@ size_t based_linattn_workspace_bytes(int B, int H, int L, int d_k, int d_v, int 
  *          bytes (may be NULL when that is 0); contents on entry are ignored.
  *
  * With zero initial state the denominator of row i is at least (i + 1) / 2,
- * so no epsilon is added.  y must not overlap q, k, v, S_in or z_in;
- * S_out/z_out may alias S_in/z_in (in-place state update).
+ * so no epsilon is added.  y must not overlap q, k, v, S_in or z_in.
+ * S_out may be S_in itself and z_out z_in itself (in-place state update);
+ * any other overlap of S_out or z_out with an input, with each other, with
+ * y or with the workspace, and any overlap of the workspace with an input,
+ * returns BASED_ERR_ALIAS.
  *
  * BASED_BF16 with d_v in {32, 64, 96, 128} runs on the matrix cores with fp16
  * operands (bf16 inputs convert exactly): Taylor features and the state copy
  * read out by each chunk are rounded to fp16 once (relative 2^-11; the state
  * is scaled by a power of two, so its size is not limited), the in-chunk
- * weights are split into fp16 hi + lo, and all sums are fp32.  Inputs must
- * stay in fp16 range there: |q|, |k| < 128 per coordinate, |q.k| < 256 and
- * |v| < 32768.  Other d_v, and BASED_F32, use fp32 vector arithmetic.
+ * weights are split into fp16 hi + lo, and all sums are fp32.  With a
+ * non-NULL S_in the readout instead takes both the query features and the
+ * state copy as fp16 hi + lo (three matrix passes), so that a caller's state
+ * of any make-up -- whose readout may cancel over its 272 feature rows -- is
+ * read to the same relative precision as a state the recurrence builds.
+ * Inputs must stay in fp16 range there: |q|, |k| < 128 per coordinate,
+ * |q.k| < 256 and |v| < 32768.  Other d_v, and BASED_F32, use fp32 vector
+ * arithmetic.
  */
 int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
                       const float* S_in, const float* z_in, float* S_out, float* z_out,
@@ -343,7 +356,7 @@ int based_decode_step_compact(const void* q, const void* k, const void* v, const
  * All fp32 device pointers; outputs must not overlap inputs or each other.
  * d_v in {16, 32, ..., 128}.  Errors: BASED_ERR_SHAPE (B, H < 1 or too
  * large), BASED_ERR_UNSUPPORTED (d_v), BASED_ERR_NULL, BASED_ERR_ALIGN
- * (pointers not 16-byte aligned), BASED_ERR_ALIAS, BASED_ERR_LAUNCH.
+ * (pointers not 16-byte aligned), BASED_ERR_ALIAS, BASED_ERR_HIP (launch).
  */
 int based_state_compact(const float* S, const float* z, float* Sc, float* zc, int B, int H, int d_v,
                         void* stream);

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "launchers.h"
 
 #define BASED_API extern "C" __attribute__((visibility("default")))
@@ -22,6 +24,30 @@ Span span(const void* p, size_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p 
 bool overlap(Span a, Span b) { return a.lo && b.lo && a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 size_t elem_size(int dtype) { return dtype == BASED_BF16 ? 2 : 4; }
+
+// Every per-(batch, head) block of an [L, d] tensor spans fewer than 2^31
+// bytes even in fp32: the kernels address a head's rows through 32-bit
+// buffer offsets.
+bool head_extent_ok(long long L, long long d) { return L * d * 4 < (1LL << 31); }
+
+// The forward's state arguments: S_out is S_in itself (in-place update) or
+// shares no byte with it, z_out likewise with z_in; no other overlap among
+// the four, with the workspace, or (for the outputs) with the inputs ins.
+int check_states(const float* S_in, const float* z_in, const float* S_out, const float* z_out, size_t BH, int d_v,
+                 const Span* ins, int nins, Span ws) {
+  const Span si = span(S_in, BH * BASED_DPHI * d_v * 4), zi = span(z_in, BH * BASED_DPHI * 4);
+  const Span so = span(S_out, BH * BASED_DPHI * d_v * 4), zo = span(z_out, BH * BASED_DPHI * 4);
+  if (overlap(so, si) && S_out != S_in) return BASED_ERR_ALIAS;
+  if (overlap(zo, zi) && z_out != z_in) return BASED_ERR_ALIAS;
+  if (overlap(so, zi) || overlap(zo, si) || overlap(so, zo)) return BASED_ERR_ALIAS;
+  for (int i = 0; i < nins; ++i)
+    if (overlap(so, ins[i]) || overlap(zo, ins[i])) return BASED_ERR_ALIAS;
+  for (const Span& s : {si, zi, so, zo})
+    if (overlap(ws, s)) return BASED_ERR_ALIAS;
+  for (int i = 0; i < nins; ++i)
+    if (overlap(ws, ins[i])) return BASED_ERR_ALIAS;
+  return BASED_OK;
+}
 
 int status_of(hipError_t e) { return e == hipSuccess ? BASED_OK : BASED_ERR_HIP; }
 
@@ -58,6 +84,7 @@ BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, flo
   if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v) || !head_extent_ok(L, d_k)) return BASED_ERR_SHAPE;
   if (L > 0 && (!q || !k || !v || !y)) return BASED_ERR_NULL;
   if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
   const void* ptrs[] = {q, k, v, y, S_in, z_in, S_out, z_out};
@@ -71,10 +98,10 @@ BASED_API int based_linattn_fwd(const void* q, const void* k, const void* v, flo
                      span(S_in, BH * BASED_DPHI * d_v * 4), span(z_in, BH * BASED_DPHI * 4)};
   for (const Span& s : in)
     if (L > 0 && overlap(ys, s)) return BASED_ERR_ALIAS;
-  if (S_out && (overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[0]) ||
-                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[1]) ||
-                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[2])))
-    return BASED_ERR_ALIAS;
+  const Span io[] = {in[0], in[1], in[2], ys};
+  if (int st = check_states(S_in, z_in, S_out, z_out, BH, d_v, io, L > 0 ? 4 : 0, span(workspace, need));
+      st != BASED_OK)
+    return st;
 
   based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
   if (L == 0 && !S_out) return BASED_OK;
@@ -92,6 +119,7 @@ BASED_API int based_linattn_decay_fwd(const void* q, const void* k, const void* 
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if (dtype != BASED_BF16 || !based::linattn_mfma_supported(d_v)) return BASED_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v) || !head_extent_ok(L, d_k)) return BASED_ERR_SHAPE;
   if (!gamma || (L > 0 && (!q || !k || !v || !y))) return BASED_ERR_NULL;
   if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
   const void* ptrs[] = {q, k, v, y, S_in, z_in, S_out, z_out};
@@ -105,10 +133,10 @@ BASED_API int based_linattn_decay_fwd(const void* q, const void* k, const void* 
                      span(S_in, BH * BASED_DPHI * d_v * 4), span(z_in, BH * BASED_DPHI * 4), span(gamma, (size_t)H * 4)};
   for (const Span& s : in)
     if (L > 0 && overlap(ys, s)) return BASED_ERR_ALIAS;
-  if (S_out && (overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[0]) ||
-                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[1]) ||
-                overlap(span(S_out, BH * BASED_DPHI * d_v * 4), in[2])))
-    return BASED_ERR_ALIAS;
+  const Span io[] = {in[0], in[1], in[2], in[5], ys};
+  if (int st = check_states(S_in, z_in, S_out, z_out, BH, d_v, io, L > 0 ? 5 : 0, span(workspace, need));
+      st != BASED_OK)
+    return st;
   if (L == 0 && !S_out) return BASED_OK;
   based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes, gamma};
   return status_of(based::launch_linattn_decay_mfma(a, (hipStream_t)stream));
@@ -123,6 +151,7 @@ BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
   if ((long long)B * H * ((L + 31) / 32) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v) || !head_extent_ok(L, d_k)) return BASED_ERR_SHAPE;
   if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
   if (L > 0 && (!q || !k || !v || !y_lin || !y_swa)) return BASED_ERR_NULL;
   if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return BASED_ERR_NULL;
@@ -142,8 +171,10 @@ BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float
       for (const Span& s : ins)
         if (overlap(o, s)) return BASED_ERR_ALIAS;
   }
-  if (S_out && (overlap(ins[5], ins[0]) || overlap(ins[5], ins[1]) || overlap(ins[5], ins[2])))
-    return BASED_ERR_ALIAS;
+  const Span io[] = {ins[0], ins[1], ins[2], outs[0], outs[1]};
+  if (int st = check_states(S_in, z_in, S_out, z_out, BH, d_v, io, L > 0 ? 5 : 0, span(workspace, need));
+      st != BASED_OK)
+    return st;
 
   based::LinattnArgs a{q, k, v, y_lin, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
   if (L == 0 && !S_out) return BASED_OK;
@@ -164,6 +195,7 @@ BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* 
   if (!valid_dv(d_qk) || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
   if ((long long)B * H * ((L + 31) / 32) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v) || !head_extent_ok(L, d_qk)) return BASED_ERR_SHAPE;
   if (L == 0) return BASED_OK;
   if (!q || !k || !v || !y) return BASED_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return BASED_ERR_ALIGN;
@@ -213,6 +245,7 @@ BASED_API int based_linattn_bwd(const void* q, const void* k, const void* v, con
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
   if ((long long)B * H * ((L + 63) / 64) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v)) return BASED_ERR_SHAPE;
   if (L == 0) return BASED_OK;
   if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
   const size_t need = based_linattn_bwd_workspace_bytes(B, H, L, d_k, d_v, dtype);
@@ -238,6 +271,7 @@ BASED_API int based_swa_bwd(const void* q, const void* k, const void* v, const f
   if (d_qk != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
   if (window < 1 || window > BASED_MAX_WINDOW) return BASED_ERR_WINDOW;
   if ((long long)B * H * ((L + 63) / 64) > 0x7fffffffLL || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v)) return BASED_ERR_SHAPE;
   if (L == 0) return BASED_OK;
   if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
   based::SwaBwdArgs a{q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, window, scale};

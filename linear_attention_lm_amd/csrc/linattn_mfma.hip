@@ -151,7 +151,7 @@ __device__ __forceinline__ float compact_from_phi(const float* S, int r, int c, 
 struct Params {
   const bf16_t* q; const bf16_t* k; const bf16_t* v; float* y;
   const float* S_in; const float* z_in; float* S_out; float* z_out;
-  float* ws;        // [BH][nseg] compact state records of (NF+1) DV floats (record_offset; row NF = constant; record 0 unused)
+  float* ws;        // [BH][nseg] compact state records of (NF+1) DV floats (record_offset; row NF = constant; record 0: S_in)
   float* wsz;       // [BH][nseg][NF+1] likewise for z (entry NF = constant: token count)
   int L, nseg, seg_chunks;
   float* y_swa;     // sliding-window softmax output of the fused layer pass
@@ -177,7 +177,7 @@ template <int NT> constexpr int vrow() { return 16 * NT + 8; }
 
 // LDS of the main pass.  With the sliding window (SWA) the row-major k and v
 // keep the previous chunk too (NB = 2 buffers).
-template <int NT, int SWA>
+template <int NT, int SWA, int HI = 0>
 struct Smem {
   static constexpr int DV = 16 * NT;
   static constexpr int NB = SWA ? 2 : 1;
@@ -186,6 +186,7 @@ struct Smem {
   alignas(16) half_t kt[DK + 1][KT];     // k^T; row ONES = 1
   alignas(16) half_t vh[NB][C][vrow<NT>()];  // v, row-major
   alignas(16) half_t tt[DV + 1][TT];     // scaled state^T; row DV: denominator state
+  alignas(16) half_t tl[HI ? DV + 1 : 1][HI ? TT : 8];  // HI: the rounding remainder of tt
   alignas(16) float t0[DV];              // constant row of the state (sum of v)
   alignas(16) float vpart[NTHR];         // partial column sums of v (decayed variant)
   alignas(16) float zf[NF];              // denominator state (set-up and result)
@@ -493,6 +494,40 @@ __device__ __forceinline__ int state_scale(const float* wmax, float& down, float
   return e;
 }
 
+// fp16 hi + lo of four fp32 values: hi = RNE(x), lo = RNE(x - hi).
+__device__ __forceinline__ f16x4 split4(const f32x4& x, f16x4& lo) {
+  const f16x4 hi = __builtin_convertvector(x, f16x4);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), f16x4);
+  return hi;
+}
+
+// High-precision readout (HI): the owned state tiles times `down` as fp16
+// hi into tt and lo into tl.
+template <int NT>
+__device__ __forceinline__ void publish_state_hilo(half_t (*tt)[TT], half_t (*tl)[TT],
+                                                   const f32x4 (&tacc)[Own<NT>::PPW], const f32x4 (&tz)[3],
+                                                   float down) {
+  constexpr int DV = 16 * NT;
+  const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
+  const int mt[3] = {w, w + 4, 8 + (w >> 1)};
+#pragma unroll
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
+    int m, n;
+    pair_mn<NT>(w, j, m, n);
+    f16x4 lo;
+    *reinterpret_cast<f16x4*>(&tt[16 * n + r16][16 * m + 4 * g]) = split4(tacc[j] * down, lo);
+    *reinterpret_cast<f16x4*>(&tl[16 * n + r16][16 * m + 4 * g]) = lo;
+  }
+  if (r16 == 0)
+#pragma unroll
+    for (int ms = 0; ms < 3; ++ms)
+      if (ms < 2 || (w & 1) == 0) {
+        f16x4 lo;
+        *reinterpret_cast<f16x4*>(&tt[DV][16 * mt[ms] + 4 * g]) = split4(tz[ms] * down, lo);
+        *reinterpret_cast<f16x4*>(&tl[DV][16 * mt[ms] + 4 * g]) = lo;
+      }
+}
+
 // Write the owned state tiles (and the denominator state) into tt as fp16,
 // times `down` unless e = 0 (the caller has synchronised: nobody reads tt
 // meanwhile).
@@ -657,6 +692,26 @@ __device__ __forceinline__ void write_compact(const float* t0, const float* zf, 
   if (tid == 0) dz[NF] = z0;
 }
 
+// Record 0 of a head: the caller's initial state in the compact record
+// layout (owned tiles from s0 = init_state of Sin; the constant row and the
+// z entries straight from Sin / zin).
+template <int NT>
+__device__ __forceinline__ void write_initial_record(const float* Sin, const float* zin,
+                                                     const f32x4 (&s0)[Own<NT>::PPW], float* dst, float* dz) {
+  constexpr int DV = 16 * NT;
+  const int tid = threadIdx.x, w = wave_index(), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < Own<NT>::PPW; ++j) {
+    int m, nn;
+    pair_mn<NT>(w, j, m, nn);
+    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, 16 * nn + r16, DV)) =
+        make_float4(s0[j][0], s0[j][1], s0[j][2], s0[j][3]);
+  }
+  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = Sin[c];
+  for (int r = tid; r < NF; r += NTHR) dz[r] = compact_from_phi(zin, r, 0, 1);
+  if (tid == 0) dz[NF] = zin[0];
+}
+
 // The final state in the caller's 273-row phi layout, straight from the
 // accumulator registers: slot r of a pair (a, b) writes rows (a, b) and
 // (b, a) when it is the slot that represents that pair.
@@ -699,11 +754,16 @@ template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
 // SWA: 0 = linear attention only; 1 = with the window attention, window 64;
 // 2 = with the window attention, any window.
-template <int NT, int SWA, int DEC = 0>
+// HI: high-precision readout for an arbitrary initial state -- the query
+// features and the state copy both as fp16 hi + lo, three passes (hi hi,
+// hi lo, lo hi).  A state the recurrence builds is read out accurately by
+// the single pass; one supplied by the caller may cancel over its 272
+// feature rows, where the single rounding of either operand is too coarse.
+template <int NT, int SWA, int DEC = 0, int HI = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
-  __shared__ Smem<NT, SWA> S;
+  __shared__ Smem<NT, SWA, HI> S;
 
   // the segments of one (batch, head) share an XCD: the later segments read
   // the same records of the earlier ones, through that XCD's L2
@@ -714,16 +774,19 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
 
-  // ---- initial state.  Segment 0: the caller's S_in / z_in (or zero).
-  // Segment s > 0: with at most MAX_SUM + 1 segments, the sum of records
-  // 1..s (record 1 holds S_in plus segment 0's increment, record j > 1
-  // segment j-1's increment); with more, the scan has turned record s into
-  // the state at the segment's start.  S_in is read only before this pass,
-  // so S_out may alias it.
+  // ---- initial state.  One segment: the caller's S_in / z_in (or zero),
+  // read by this workgroup before it writes S_out.  Several segments:
+  // segment 0 starts from record 0, the state-only pass's copy of S_in (or
+  // from zero), so that no workgroup of this pass reads S_in and the last
+  // segment may write S_out over it; segment s > 0, with at most MAX_SUM + 1
+  // segments, from the sum of records 1..s (record 1 holds S_in plus
+  // segment 0's increment, record j > 1 segment j-1's increment); with more,
+  // the scan has turned record s into the state at the segment's start.
   const size_t rec = (size_t)(NF + 1) * DV;
   const bool scanned = p.nseg > MAX_SUM + 1;
-  const bool from_records = p.nseg > 1 && seg > 0;
-  const int first = scanned ? seg : 1, nsrc = scanned ? 1 : seg;
+  const bool rec0 = p.nseg > 1 && seg == 0 && p.S_in != nullptr;
+  const bool from_records = (p.nseg > 1 && seg > 0) || rec0;
+  const int first = rec0 ? 0 : (scanned ? seg : 1), nsrc = rec0 ? 1 : (scanned ? 1 : seg);
   // the segment's first chunk (and, with the window, the chunk before it)
   // from HBM first, so that their latency overlaps the state set-up
   const HeadRsrc rs = head_rsrc(p, bh, DV);
@@ -740,7 +803,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   for (int k2 = 0; k2 < MAX_SUM; ++k2) wrec[k2] = 1.f;
   if constexpr (DEC) {
     lg = decay_lg2(p, bh);
-    if (!scanned)
+    if (!scanned && !rec0)
 #pragma unroll
       for (int k2 = 0; k2 < MAX_SUM; ++k2)
         wrec[k2] = k2 < nsrc ? gpow(lg, (float)((seg - 1 - k2) * p.seg_chunks * C)) : 0.f;
@@ -751,8 +814,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     sum_records<NT>(p.ws + (bh * p.nseg + first) * rec, p.wsz + (bh * p.nseg + first) * (size_t)(NF + 1), nsrc,
                     wrec, tacc, S.t0, S.zf, z0);
   } else {
-    const float* Sin = p.S_in ? p.S_in + bh * DPHI * DV : nullptr;
-    const float* zin = p.z_in ? p.z_in + bh * DPHI : nullptr;
+    const bool own_sin = p.nseg == 1 && p.S_in != nullptr;
+    const float* Sin = own_sin ? p.S_in + bh * DPHI * DV : nullptr;
+    const float* zin = own_sin ? p.z_in + bh * DPHI : nullptr;
     init_state<NT>(Sin, tacc);
     for (int c = tid; c < DV; c += NTHR) S.t0[c] = Sin ? Sin[c] : 0.f;
     for (int r = tid; r < NF; r += NTHR) S.zf[r] = zin ? compact_from_phi(zin, r, 0, 1) : 0.f;
@@ -777,7 +841,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   __syncthreads();
   float down, up;
   int e = state_scale(S.wmax, down, up);
-  publish_state<NT>(S.tt, tacc, tz, e, down);
+  if constexpr (HI) publish_state_hilo<NT>(S.tt, S.tl, tacc, tz, down);
+  else publish_state<NT>(S.tt, tacc, tz, e, down);
   if (tok_begin < tok_end) store_chunk<NT>(S.kt, &S.vh[0][0][0], S.qh, S.kh[0], pf);
   int cur = 0;  // buffer of the current chunk's k and v (the other: previous chunk)
 
@@ -843,6 +908,33 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn)
           acc[nn] = mfma(*reinterpret_cast<const f16x8*>(&S.tt[16 * nn + r16][32 * kb + 8 * g]), fb, acc[nn]);
+        if constexpr (HI) {
+          // the features' rounding remainders (exact fp32 products of the
+          // fp16 factors, minus the fp16 features; linear features: zero)
+          uint4 fx, fy;
+          if (kb == 0) {
+            fx = make_uint4(0u, 0u, q2[0], q2[1]);
+            fy = make_uint4(0u, 0u, qh0, qh1);
+          } else {
+            fx = make_uint4(q2[0], q2[1], kb == NKB - 1 ? qh0 : q2[0], kb == NKB - 1 ? qh1 : q2[1]);
+            fy = make_uint4(qo[kb - 1], qo[kb], q2[kb], q2[kb + 1]);
+          }
+          const f16x8 hx = __builtin_bit_cast(f16x8, fx), hy = __builtin_bit_cast(f16x8, fy);
+          f16x8 fl;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float prod = (float)hx[i] * (float)hy[i];
+            fl[i] = (half_t)(prod - (float)fb[i]);
+          }
+          if (kb == 0) { fl[0] = fl[1] = fl[2] = fl[3] = (half_t)0.f; }
+          accz = mfma(*reinterpret_cast<const f16x8*>(&S.tl[DV][32 * kb + 8 * g]), fb, accz);
+          accz = mfma(*reinterpret_cast<const f16x8*>(&S.tt[DV][32 * kb + 8 * g]), fl, accz);
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            acc[nn] = mfma(*reinterpret_cast<const f16x8*>(&S.tl[16 * nn + r16][32 * kb + 8 * g]), fb, acc[nn]);
+            acc[nn] = mfma(*reinterpret_cast<const f16x8*>(&S.tt[16 * nn + r16][32 * kb + 8 * g]), fl, acc[nn]);
+          }
+        }
       }
     }
     if (e != 0) {
@@ -1083,7 +1175,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       for (int nn = 0; nn < NT; ++nn) S.t0[16 * nn + r16] += vacc[nn][0];
     }
     e = state_scale(S.wmax, down, up);
-    publish_state<NT>(S.tt, tacc, tz, e, down);
+    if constexpr (HI) publish_state_hilo<NT>(S.tt, S.tl, tacc, tz, down);
+    else publish_state<NT>(S.tt, tacc, tz, e, down);
     if constexpr (SWA) cur ^= 1;  // the next chunk replaces the previous one
     if (tn < tok_end) store_chunk<NT>(S.kt, &S.vh[cur][0][0], S.qh, S.kh[cur], pf);
   }
@@ -1220,6 +1313,9 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
     init_state<NT>(Sin, s0);
 #pragma unroll
     for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] += gN * s0[j];
+    // record 0: S_in itself, the main pass's start of segment 0 (that pass
+    // then reads no S_in, so S_out may alias it)
+    write_initial_record<NT>(Sin, zin, s0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
   }
   __syncthreads();
   write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
@@ -1229,7 +1325,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 // Prefix over the segment records of each (batch, head): record s >= 1 holds
 // the increment of segment s-1 (record 1: the initial state plus that
 // increment); after the scan record s is the state at the start of segment s.
-// Record 0 is not used (segment 0 starts from S_in itself).
+// Record 0 (the initial state, when there is one) is left as it is.
 __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH, const float* gamma, int H,
                                 int seg_len) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1294,8 +1390,8 @@ size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
   return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
 }
 
-template <int NT, int SWA, int DEC = 0>
-static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+template <int NT, int SWA, int DEC, int HI>
+static hipError_t launch_nt_hi(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
   constexpr int DV = 16 * NT;
   Params p{};
   p.q = (const bf16_t*)a.q; p.k = (const bf16_t*)a.k; p.v = (const bf16_t*)a.v; p.y = a.y;
@@ -1317,8 +1413,15 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((linattn_mfma_kernel<NT, SWA, DEC>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
+  hipLaunchKernelGGL((linattn_mfma_kernel<NT, SWA, DEC, HI>), dim3(BH * p.nseg), dim3(NTHR), 0, s, p);
   return hipGetLastError();
+}
+
+template <int NT, int SWA, int DEC = 0>
+static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+  // a caller's initial state: the high-precision readout
+  if (a.S_in) return launch_nt_hi<NT, SWA, DEC, 1>(a, y_swa, window, scale, s);
+  return launch_nt_hi<NT, SWA, DEC, 0>(a, y_swa, window, scale, s);
 }
 
 // State-only pass on its own (zero initial state): records [BH][nseg][NF + 1][dv]

@@ -35,3 +35,31 @@ def report(name: str, err: float, tol: float) -> None:
 
 def say(msg: str) -> None:
     print(f"[case] {msg}", flush=True)
+
+
+def z_block_rel(z, ref) -> float:
+    """A denominator state [..., 273] (or compact [..., 153]) compared block by
+    block: the constant entry (the token count), the 16 linear entries (sums
+    of k) and the quadratic entries, each block as one row of rowinf_rel.
+    One row over all entries would measure the linear sums against the token
+    count, which dwarfs them."""
+    z = z.detach().to("cpu", torch.float64).numpy() if hasattr(z, "detach") else np.asarray(z, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert z.shape == ref.shape, (z.shape, ref.shape)
+    return max(rowinf_rel(z[..., a:b], ref[..., a:b]) for a, b in ((0, 1), (1, 17), (17, z.shape[-1])))
+
+
+def row_rel_floor(g, ref, frac: float) -> float:
+    """Per-row infinity-norm relative error of a gradient [..., L, d]: each
+    row (one position's gradient vector) against max(its own largest
+    magnitude, frac x the largest magnitude of its head's [L, d] block)."""
+    g = g.detach().to("cpu", torch.float64).numpy() if hasattr(g, "detach") else np.asarray(g, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    if g.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), "non-finite gradient"
+    err = np.abs(g - ref).max(axis=-1)
+    own = np.abs(ref).max(axis=-1)
+    head = np.abs(ref).max(axis=(-1, -2), keepdims=False)[..., None]
+    return float((err / np.maximum(np.maximum(own, frac * head), 1e-30)).max())

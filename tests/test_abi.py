@@ -268,3 +268,52 @@ def test_state_conversion_validation(so):
     assert so.based_state_compact(S, z, S + 16, zc, B, H, dv, None) == ERR["ALIAS"]
     assert so.based_state_expand(Sc, zc, S, Sc, B, H, dv, None) == ERR["ALIAS"]
     assert so.based_state_expand(Sc, zc, S, S + B * H * 273 * dv * 4 - 16, B, H, dv, None) == ERR["ALIAS"]
+
+
+def test_head_extent_limit(so):
+    """Each head's [L, d] block must stay under 2^31 bytes in fp32 (the
+    kernels address it through 32-bit buffer offsets): a longer L is
+    rejected on the host, for every entry point that takes [B,H,L,d]."""
+    big = (1 << 31) // (4 * 128)  # first L whose fp32 block at d = 128 reaches 2^31 bytes
+    assert fwd(so, L=big, dv=128) == ERR["SHAPE"]
+    assert fwd(so, L=big - 1, dv=128, q=None) == ERR["NULL"]  # one less passes the size check
+    assert fwd(so, L=2 * big, dv=64) == ERR["SHAPE"]
+    assert so.based_linattn_decay_fwd(P, 2 * P, 3 * P, 5 * P, 4 * P, None, None, None, None, 1, 1, big, 16, 128, 1,
+                                      None, 0, None) == ERR["SHAPE"]
+    assert so.based_layer_fwd(P, 2 * P, 3 * P, 4 * P, 6 * P, None, None, None, None, 1, 1, big, 16, 128, 64,
+                              ctypes.c_float(1.0), 1, None, 0, None) == ERR["SHAPE"]
+    assert so.based_swa_fwd(P, 2 * P, 3 * P, 4 * P, 1, 1, big, 128, 64, 64, ctypes.c_float(1.0), 1,
+                            None) == ERR["SHAPE"]
+    for fn in (so.based_linattn_bwd, so.based_swa_bwd):
+        if fn is so.based_linattn_bwd:
+            st = fn(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 1, 1, big, 16, 128, 1, None, 0, None)
+        else:
+            st = fn(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 1, 1, big, 16, 128, 64,
+                    ctypes.c_float(1.0), 1, None)
+        assert st == ERR["SHAPE"]
+
+
+def test_state_alias_rules(so):
+    """S_out may be S_in itself (in-place update) but may not overlap it
+    otherwise; z_out likewise; S_out may not overlap z_in, the inputs or
+    the workspace.  (Exact aliasing is exercised on the GPU.)"""
+    B, H, dv = 1, 2, 64
+    nS = B * H * 273 * dv * 4
+    S0, z0 = 100 * P, 200 * P
+    ws_need = so.based_linattn_workspace_bytes(B, H, 256, 16, dv, 1)
+    assert ws_need == 0  # L = 256 on 2 heads: one segment, no workspace
+    assert fwd(so, S_in=S0, z_in=z0, S_out=S0 + 16 * 64, z_out=300 * P) == ERR["ALIAS"]  # shifted S_out
+    assert fwd(so, S_in=S0, z_in=z0, S_out=300 * P, z_out=z0 + 16) == ERR["ALIAS"]  # shifted z_out
+    assert fwd(so, S_in=S0, z_in=z0, S_out=z0, z_out=300 * P) == ERR["ALIAS"]  # S_out over z_in
+    assert fwd(so, S_in=S0, z_in=z0, S_out=300 * P, z_out=S0 + nS - 64) == ERR["ALIAS"]  # z_out over S_in
+    assert fwd(so, S_out=2 * P, z_out=300 * P) == ERR["ALIAS"]  # S_out over k
+    assert fwd(so, S_out=300 * P, z_out=4 * P) == ERR["ALIAS"]  # z_out over y
+    # a workspace that overlaps a state or an input (L = 4096 on 2 heads
+    # needs one); buffers 1 GiB apart so that only the named pair overlaps
+    G = 1 << 30
+    need = so.based_linattn_workspace_bytes(B, H, 4096, 16, dv, 1)
+    assert need > 0
+    far = dict(q=G, k=2 * G, v=3 * G, y=4 * G, L=4096, wsb=need)
+    assert fwd(so, S_in=5 * G, z_in=6 * G, ws=5 * G + 64, **far) == ERR["ALIAS"]
+    assert fwd(so, S_out=5 * G, z_out=6 * G, ws=6 * G - 64, **far) == ERR["ALIAS"]
+    assert fwd(so, ws=2 * G + 128, **far) == ERR["ALIAS"]  # workspace over k

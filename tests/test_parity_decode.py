@@ -7,7 +7,7 @@ import torch
 
 import synth
 from oracle import based_oracle as O
-from parity_util import TOL, report, rowinf_rel, say
+from parity_util import TOL, report, rowinf_rel, say, z_block_rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,7 +40,7 @@ def run_decode(based, cfg, seqs=None, check_steps=None, seed=0, compact=False):
     report(f"decode y_swa B{cfg.B} ctx{cfg.ctx}", max(e[1] for e in errs), tol)
     S_ref, z_ref = O.state_compact(ref.S, ref.z) if compact else (ref.S, ref.z)
     assert rowinf_rel(st.S[seqs], S_ref) <= tol
-    assert rowinf_rel(st.z[seqs], z_ref) <= tol
+    assert z_block_rel(st.z[seqs], z_ref) <= tol
     assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
     return st
 
@@ -85,11 +85,17 @@ def test_decode_sequences_at_different_positions(based):
     assert st.pos.cpu().tolist() == [10 + cfg.steps, 30 + cfg.steps]
 
 
+FULL_DECODE_CHECKS = [0, 1, 2, 62, 63, 64, 65, 500, 999]
+
+
 def test_decode_full_workload_sampled(based):
-    """256 sequences x 16 heads, 2048-token context, d_v 64, bf16 ring: the
-    first 72 steps (past one full ring turn), oracle on sampled sequences."""
-    cfg = synth.DECODE_CONFIG.replace(steps=72)
-    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=[0, 1, 2, 62, 63, 64, 65, 71])
+    """The decode workload as benchmarked: 256 sequences x 16 heads, a
+    2048-token context, d_v 64, bf16 ring, all 1000 steps; the oracle follows
+    sampled sequences, outputs checked around the ring turns and at the end,
+    and the final S, z and positions."""
+    cfg = synth.DECODE_CONFIG
+    assert cfg.steps == 1000
+    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=FULL_DECODE_CHECKS)
 
 
 def test_decode_snapshot_restore(based):
@@ -144,7 +150,7 @@ def run_decay_decode(based, cfg, compact=False):
     report(f"decay decode y_lin ctx{cfg.ctx} {cfg.dtype}", el, tol)
     report(f"decay decode y_swa ctx{cfg.ctx} {cfg.dtype}", es, tol)
     S_ref, z_ref = O.state_compact(ref.S, ref.z) if compact else (ref.S, ref.z)
-    assert rowinf_rel(st.S, S_ref) <= tol and rowinf_rel(st.z, z_ref) <= tol
+    assert rowinf_rel(st.S, S_ref) <= tol and z_block_rel(st.z, z_ref) <= tol
     assert torch.all(st.pos.cpu() == cfg.ctx + cfg.steps)
     return st
 
@@ -186,8 +192,8 @@ def test_compact_decode_shapes(based, dv, window):
 
 
 def test_compact_decode_full_workload_sampled(based):
-    cfg = synth.DECODE_CONFIG.replace(steps=72)
-    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=[0, 1, 2, 63, 64, 71], compact=True)
+    cfg = synth.DECODE_CONFIG
+    run_decode(based, cfg, seqs=[0, 101, 255], check_steps=FULL_DECODE_CHECKS, compact=True)
 
 
 def test_compact_decay_decode_after_context(based):
