@@ -9,8 +9,9 @@ of its head's [L, d] block), with the forward tolerances (fp32 1e-5, bf16
 sum of terms of the head's size that may cancel to far less, and then only
 rounding noise of the head's size remains (dq of position 0 is zero in
 exact arithmetic, since y_0 = v_0 whatever q_0 is; dq and dk vanish at
-L = 1).  Those identically vanishing rows are checked as noise against the
-head's largest dv: at most 100x the tolerance."""
+L = 1).  Those identically vanishing rows (and gradients that vanish everywhere, as dq and dk of
+a window of 1, where y = v) are checked as noise against the head's largest
+dv: at most 100x the tolerance."""
 
 import numpy as np
 import pytest
@@ -54,6 +55,8 @@ def run_case(based, cfg, which, heads=None, window=64, scale=1.0, seed=0):
         # rows that vanish in exact arithmetic (y_0 = v_0 whatever q, k are):
         # dq of position 0, and dk too at L = 1
         zero_rows = cfg.L if (cfg.L == 1 and name != "dv") else (1 if name == "dq" else 0)
+        if np.abs(r).max() == 0:  # vanishes everywhere (window 1: y = v)
+            zero_rows = cfg.L
         if zero_rows:
             err = float(g[..., :zero_rows, :].abs().max().cpu()) / float(floor.max())
             report(f"{which} {name} {cfg.name} (zero rows, noise / max|dv|)", err, 100 * tol)
