@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 7
+#define BASED_ABI_VERSION 8
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -261,6 +261,28 @@ int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, f
                     const float* S_in, const float* z_in, float* S_out, float* z_out,
                     int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * based_layer_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  The segment records live in a static
+ * device array of BASED_NOALLOC_SCRATCH_MB MiB that each GPU the library
+ * runs on holds until the process ends; this entry point allocates nothing
+ * (no hipMalloc, no allocating library call).  That array is larger than
+ * the workspace of every shape the layer splits into segments (at most
+ * about 41 MiB); a shape whose workspace would not fit returns
+ * BASED_ERR_WORKSPACE.  Its contents on entry are ignored, so nothing needs
+ * clearing between calls.  All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (on different streams, or from several host
+ * threads) race, and must be serialised by the caller.  Every other
+ * argument, result and error as for based_layer_fwd; BASED_ERR_HIP if the
+ * array's device address cannot be obtained.
+ */
+#define BASED_NOALLOC_SCRATCH_MB 48
+int based_layer_fwd_noalloc(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
+                            const float* S_in, const float* z_in, float* S_out, float* z_out,
+                            int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
+                            void* stream);
 
 /*
  * Fill the decode ring buffers from a context and set the positions

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "based_linattn_fwd": (_i, [_vp] * 8 + [_i] * 6 + [_vp, _sz, _vp]),
     "based_swa_fwd": (_i, [_vp] * 4 + [_i] * 6 + [_f, _i, _vp]),
     "based_layer_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
+    "based_layer_fwd_noalloc": (_i, [_vp] * 9 + [_i] * 6 + [_f, _i, _vp]),
     "based_decode_prefill": (_i, [_vp] * 5 + [_i] * 7 + [_vp]),
     "based_decode_step": (_i, [_vp] * 10 + [_i] * 5 + [_f, _i, _vp]),
     "based_linattn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -226,6 +227,23 @@ def layer_fwd(q, k, v, window: int = 64, scale: float = 1.0, S_in=None, z_in=Non
                                   _ptr(workspace), wbytes, _stream()))
     if return_state or S_out is not None:
         return y_lin, y_swa, S_out, z_out
+    return y_lin, y_swa
+
+
+def layer_fwd_noalloc(q, k, v, window: int = 64, scale: float = 1.0, S_in=None, z_in=None, *, y_lin, y_swa,
+                      S_out=None, z_out=None):
+    """:func:`layer_fwd` through based_layer_fwd_noalloc: no workspace and no
+    allocation -- the caller passes every output (y_lin, y_swa and, to get
+    the final state, S_out / z_out); the segment records live in the
+    library's static device array (calls overlapping on one GPU race)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    _dev(q, k, v, S_in, z_in, y_lin, y_swa, S_out, z_out)
+    _check(_lib().based_layer_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(y_lin), _ptr(y_swa), _ptr(S_in),
+                                          _ptr(z_in), _ptr(S_out), _ptr(z_out), B, H, L, dk, dv, window,
+                                          float(scale), _dtype_code(q), _stream()))
     return y_lin, y_swa
 
 

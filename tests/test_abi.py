@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 7
+    assert so.based_abi_version() == 8
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
