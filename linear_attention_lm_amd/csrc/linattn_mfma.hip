@@ -239,11 +239,21 @@ __device__ __forceinline__ uint4 h8_from_bf8(const uint4& x) {
   return make_uint4(h2_from_bf2(x.x), h2_from_bf2(x.y), h2_from_bf2(x.z), h2_from_bf2(x.w));
 }
 
-// fp16 hi + lo of two fp32 values: hi = RNE(x), lo = RNE(x - hi).
+// fp16 hi + lo of two fp32 values: hi = RNE(x), lo = RNE(x - hi).  The
+// remainders are formed by v_fma_mix{lo,hi}_f16, which take the fp32 value
+// and the fp16 half of hi as they are (x * 1 - hi in fp32, rounded once to
+// fp16): one instruction per value where the compiler's form (widen hi,
+// subtract, narrow) takes three.  x - hi is exact in fp32, so the result is
+// the same.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   const f16x2 h = __builtin_convertvector((f32x2{a, b}), f16x2);
   hi = u32(h);
-  lo = u32(__builtin_convertvector((f32x2{a - (float)h[0], b - (float)h[1]}), f16x2));
+  uint32_t l = 0;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "+v"(l)
+      : "v"(a), "v"(hi), "v"(b));
+  lo = l;
 }
 
 // Registers holding one chunk's inputs on their way from HBM to LDS.
@@ -436,7 +446,7 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
-// Maximum / sum over the four 16-lane rows of a wavefront (lanes l, l^16,
+// Maximum over the four 16-lane rows of a wavefront (lanes l, l^16,
 // l^32, l^48), by row swaps in registers: v_permlane16_swap pairs rows 0-1
 // and 2-3, v_permlane32_swap the two halves.  Every lane applies the same
 // operand order, so all four get the same bits.
@@ -445,12 +455,6 @@ __device__ __forceinline__ float rows_max(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Largest magnitude of this wavefront's state entries, into wmax[w]: quad and
@@ -1051,10 +1055,19 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           if (m == w)
 #pragma unroll
             for (int i = 0; i < 4; ++i) xc[m][i] = __builtin_fmaf(xc[m][i], c2, dcur[i]);
-          if (m > w) xp[m] = have_prev ? xp[m] * c2 : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          if (m == w)
+        }
+        if (have_prev) {  // uniform: false only for the sequence's first chunk
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xp[m][i] = have_prev ? __builtin_fmaf(xp[m][i], c2, dprev[i]) : -INFINITY;
+          for (int m = 0; m < 4; ++m) {
+            if (m > w) xp[m] *= c2;
+            if (m == w)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) xp[m][i] = __builtin_fmaf(xp[m][i], c2, dprev[i]);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            if (m >= w) xp[m] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
       } else {
         const uint32_t W = (uint32_t)p.window;
@@ -1068,14 +1081,20 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           }
         }
       }
+      // (chains of three-operand maxima)
       float mx = -INFINITY;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        if (m <= w) mx = fmaxf(mx, fmaxf(fmaxf(xc[m][0], xc[m][1]), fmaxf(xc[m][2], xc[m][3])));
-        if (m >= w) mx = fmaxf(mx, fmaxf(fmaxf(xp[m][0], xp[m][1]), fmaxf(xp[m][2], xp[m][3])));
+        if (m <= w) {
+          mx = fmaxf(fmaxf(mx, xc[m][0]), xc[m][1]);
+          mx = fmaxf(fmaxf(mx, xc[m][2]), xc[m][3]);
+        }
+        if (m >= w) {
+          mx = fmaxf(fmaxf(mx, xp[m][0]), xp[m][1]);
+          mx = fmaxf(fmaxf(mx, xp[m][2]), xp[m][3]);
+        }
       }
       mx = rows_max(mx);
-      float den = 0.f;
       // fp16 hi / lo weights per key block: this chunk's blocks, the previous chunk's
       uint4 ch[2], cl[2], qh_[2], ql_[2];
 #pragma unroll
@@ -1088,10 +1107,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
             const f32x4& x = side == 0 ? xc[m] : xp[m];
             float e4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              e4[i] = __builtin_amdgcn_exp2f(x[i] - mx);
-              den += e4[i];
-            }
+            for (int i = 0; i < 4; ++i) e4[i] = __builtin_amdgcn_exp2f(x[i] - mx);
             uint32_t h0, l0, h1, l1;
             split2(e4[0], e4[1], h0, l0);
             split2(e4[2], e4[3], h1, l1);
@@ -1102,10 +1118,12 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           }
         }
       }
-      den = rows_sum(den);
+      // the weighted sums and, from an all-ones operand against the same
+      // weights, the denominator (every entry of accd)
       f32x4 accs[NT];
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn) accs[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 accd = {0.f, 0.f, 0.f, 0.f};
       // key blocks: previous chunk (0,1), (2,3); this chunk (0,1), (2,3)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
@@ -1116,6 +1134,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           const f16x8 ph = __builtin_bit_cast(f16x8, is_prev ? qh_[kb] : ch[kb]);
           const f16x8 pl = __builtin_bit_cast(f16x8, is_prev ? ql_[kb] : cl[kb]);
           const int b = is_prev ? prev : cur;
+          accd = mfma(ones, ph, accd);
+          accd = mfma(ones, pl, accd);
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn) {
             const int col = 16 * nn + r16;
@@ -1125,7 +1145,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           }
         }
       }
-      const float rs_ = __builtin_amdgcn_rcpf(den);
+      const float rs_ = __builtin_amdgcn_rcpf(accd[0]);
       if (pos < n) {
         float* yrow = p.y_swa + (bh * p.L + t0 + pos) * DV + 4 * g;
 #pragma unroll
