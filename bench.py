@@ -108,18 +108,18 @@ OP_SOURCES = {
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
-    "layer": ["linattn_mfma_kernel<4, 1, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
+    "layer": ["linattn_mfma_kernel<4, 1, 0, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "slice_sum_kernel",
             "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>"],
     "decode": ["decode_step_kernel<unsigned short, 64, 273>"],
     "decode_compact": ["decode_step_kernel<unsigned short, 64, 153>"],
     "baseconv": ["baseconv_kernel"],
-    "decay": ["linattn_mfma_kernel<4, 0, 1>", "linattn_state_kernel<4, 1>"],
+    "decay": ["linattn_mfma_kernel<4, 0, 1, 0>", "linattn_state_kernel<4, 1>"],
 }
 # the backward's last launch of each call (based_linattn_bwd, then based_swa_bwd)
 BWD_KERNEL = "swa_bwd_mfma_kernel"
 # the step's last launch of each call (marks the end of the timed step in a trace)
-STEP_KERNEL = "linattn_mfma_kernel<4, 1, 0>"
+STEP_KERNEL = "linattn_mfma_kernel<4, 1, 0, 0>"
 COPY_BYTES = 512 << 20
 
 
@@ -177,10 +177,37 @@ def time_loop(fn, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
+def step_parity(cfg, dev_set, y_lin, y_swa, layer, heads=((0, 0), (-1, -1))):
+    """The step's outputs on its first input set against the fp64 oracle, on
+    sampled (batch, head) pairs: per-row infinity-norm relative error."""
+    import numpy as np
+
+    from oracle import based_oracle as O
+
+    layer(0)
+    torch.cuda.synchronize()
+    q, k, v = (t.cpu() for t in dev_set)
+    worst = {"y_lin": 0.0, "y_swa": 0.0}
+    for b, h in heads:
+        yl = O.linattn_chunked(q[b, h], k[b, h], v[b, h], 64)[0]
+        ys = O.swa(q[b, h], k[b, h], v[b, h], cfg.window)
+        for name, got, ref in (("y_lin", y_lin[b, h], yl), ("y_swa", y_swa[b, h], ys)):
+            g = got.double().cpu().numpy()
+            e = float((np.abs(g - ref).max(-1) / np.abs(ref).max(-1)).max())
+            worst[name] = max(worst[name], e)
+    tol = 2e-3 if cfg.dtype == "bf16" else 1e-5
+    if max(worst.values()) > tol:
+        raise SystemExit(f"step parity failed: {worst} (tolerance {tol})")
+    return {"heads": [list(x) for x in heads], "rowinf_rel": worst, "tol": tol}
+
+
+def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True, settle=0, check=False):
     """Time `steps` layer forwards: one based_layer_fwd call per step, or
     (fused=False) based_linattn_fwd and based_swa_fwd, each in a loop of its
-    own (the step's time is their sum).  Returns a dict."""
+    own (the step's time is their sum).  check: first compare the outputs
+    with the oracle on sampled heads; settle: untimed calls of the same
+    operation before the `warmup` steps, until the GPU clocks settle.
+    Returns a dict."""
     q, k, v = synth.fwd_inputs(cfg, 0)
     sets = []
     for i in range(nbuf):
@@ -203,6 +230,16 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
         qq, kk, vv = sets[i % nbuf]
         lal.swa_fwd(qq, kk, vv, cfg.window, y=y_swa)
 
+    parity = None
+    if check:
+        parity = step_parity(cfg, sets[0], y_lin, y_swa, layer)
+    # untimed calls of the timed operation until the GPU clocks settle
+    for i in range(settle):
+        if fused:
+            layer(i)
+        else:
+            lin(i)
+            swa(i)
     for i in range(warmup):
         if fused:
             layer(i)
@@ -223,8 +260,37 @@ def bench_fwd(lal, cfg, steps, warmup, nbuf=8, fused=True):
         out = {"linattn_us": tl * 1e3, "swa_us": ts * 1e3, "linattn_bytes": lb, "swa_bytes": sb,
                "linattn_hbm_gbs": lb / (tl * 1e-3) / 1e9, "swa_hbm_gbs": sb / (ts * 1e-3) / 1e9}
     out.update({"workload": cfg.name, "B": B, "H": H, "L": L, "d_k": 16, "d_v": dv, "window": cfg.window,
-                "dtype": cfg.dtype, "fused": fused, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)})
+                "dtype": cfg.dtype, "fused": fused, "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+                "settle_calls": settle})
+    if parity is not None:
+        out["parity"] = parity
     return out
+
+
+def bench_tiny(lal, cfg, calls=200):
+    """The tiny fp32 layer (launch-bound): microseconds per call of
+    back-to-back calls, and the latency of one call on an idle stream
+    (median of 50 calls, an event pair around each)."""
+    q, k, v = (t.to("cuda") for t in synth.fwd_inputs(cfg, 0))
+    y_lin = torch.empty(cfg.B, cfg.H, cfg.L, cfg.dv, device="cuda")
+    y_swa = torch.empty_like(y_lin)
+    call = lambda i: lal.layer_fwd(q, k, v, cfg.window, y_lin=y_lin, y_swa=y_swa)
+    for i in range(50):
+        call(i)
+    ms = time_loop(call, calls)
+    lat = []
+    for i in range(50):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        lat.append(e0.elapsed_time(e1) * 1e3)
+    lat.sort()
+    return {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "d_v": cfg.dv, "dtype": cfg.dtype,
+            "us_per_call_back_to_back": ms * 1e3, "us_latency_median": lat[len(lat) // 2],
+            "us_latency_p10": lat[5], "us_latency_p90": lat[45], "calls": calls}
 
 
 def bwd_inputs(lal, cfg, nbuf=8):
@@ -361,32 +427,89 @@ def bench_decode(lal, cfg, warmup=5, decay=False, compact=False):
     }
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The fp64 oracle (chunked linear attention + banded window softmax) on a
-    bounded sample of the step's heads, on this host's cores."""
-    import numpy as np
+def host_info():
+    """This host's CPU model and logical CPU count, and the threads the
+    oracle's BLAS calls use."""
     from threadpoolctl import threadpool_info
 
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas_threads": threads}
+
+
+def oracle_fwd_rate(cfg, budget_s):
+    """Position-heads per second of the fp64 oracle (chunked linear attention
+    + banded window softmax) over whole heads of `cfg`, for about budget_s
+    seconds (at least one head).  Returns (rate, heads done, seconds)."""
     from oracle import based_oracle as O
 
     q, k, v = synth.fwd_inputs(cfg, 0)
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     done = 0
     t0 = time.perf_counter()
-    while done < len(heads) and time.perf_counter() - t0 < budget_s:
+    while done < len(heads) and (done == 0 or time.perf_counter() - t0 < budget_s):
         b, h = heads[done]
         O.linattn_chunked(q[b, h], k[b, h], v[b, h], 64)
         O.swa(q[b, h], k[b, h], v[b, h], cfg.window)
         done += 1
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    tok_heads_per_s = done * cfg.L / dt
+    return done * cfg.L / dt, done, dt
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 oracle (chunked linear attention + banded window softmax) on a
+    bounded sample of the step's heads, on this host's cores."""
+    rate, done, dt = oracle_fwd_rate(cfg, budget_s)
+    info = host_info()
     return {
-        "value": tok_heads_per_s / cfg.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "sample": f"{done} of {len(heads)} (batch, head) pairs of the step workload ({cfg.L} positions each), "
+        "value": rate / cfg.H, "unit": "tokens/s", "cores": info["blas_threads"], "kind": "oracle",
+        "host_cpus": info["host_cpus"], "cpu_model": info["cpu_model"],
+        "sample": f"{done} of {cfg.B * cfg.H} (batch, head) pairs of the step workload ({cfg.L} positions each), "
                   f"fp64 chunked linear attention + banded window softmax, {dt:.1f} s; tokens/s = "
-                  f"position-heads/s / {cfg.H} heads",
+                  f"position-heads/s / {cfg.H} heads; cores = the oracle's BLAS threads",
     }
+
+
+def cpu_oracle_other(budget_s=4.0, decode_steps=3):
+    """The same oracle on the other workloads, each on a bounded sample:
+    whole heads of the 1.3B-shaped and 32k forwards (tokens/s = position-heads
+    per second / heads), and decode: `decode_steps` steps of the full 256 x
+    16-head batch (the fp64 recurrence and the window over the ring), each
+    step costing the same, so tokens/s = 256 sequences per step time.  The
+    decode state starts at zero with a full ring: a step's cost does not
+    depend on the state's values."""
+    import numpy as np
+
+    from oracle import based_oracle as O
+
+    out = {}
+    for name in ("based1p3b", "long32k"):
+        cfg = synth.FWD_CONFIGS[name]
+        rate, done, dt = oracle_fwd_rate(cfg, budget_s)
+        out[name] = {"tokens_per_s": rate / cfg.H, "sample": f"{done} head(s) of {cfg.L} positions, {dt:.1f} s"}
+    cfg = synth.DECODE_CONFIG
+    _, (qs, ks, vs) = synth.decode_inputs(cfg.replace(ctx=0, steps=decode_steps + 1), 0)
+    B, H, W = cfg.B, cfg.H, cfg.window
+    st = O.DecodeState(np.zeros((B, H, O.D_PHI, cfg.dv)), np.zeros((B, H, O.D_PHI)), np.zeros((B, H, W, 16)),
+                       np.zeros((B, H, W, cfg.dv)), np.full(B, cfg.ctx))
+    st.step(qs[0], ks[0], vs[0])  # first touch of the state arrays, untimed
+    t0 = time.perf_counter()
+    for s in range(1, decode_steps + 1):
+        st.step(qs[s], ks[s], vs[s])
+    dt = (time.perf_counter() - t0) / decode_steps
+    out["decode"] = {"tokens_per_s": B / dt, "s_per_step": dt,
+                     "sample": f"{decode_steps} steps of {B} sequences x {H} heads (fp64 state, zero at the "
+                               f"start; a step's cost does not depend on the state's values)"}
+    out.update(host_info())
+    return out
 
 
 def _counter_rows(d):
@@ -625,6 +748,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (enough for the GPU clocks to settle)")
+    ap.add_argument("--settle", type=int, default=300,
+                    help="untimed calls of the step before the warm-up steps, so that the GPU clocks settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and decode")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -667,12 +792,15 @@ def main():
     copy = copy_calibration()
     print(f"[bench] copy calibration: {copy['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     bsets = None if args.no_extra else bwd_inputs(lal, cfg)
-    main_res = bench_fwd(lal, cfg, args.steps, args.warmup)
+    main_res = bench_fwd(lal, cfg, args.steps, args.warmup, settle=args.settle, check=True)
     print(f"[bench] {cfg.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step (layer {main_res['layer_us']:.1f} us)",
           file=sys.stderr, flush=True)
     extra, decode, separate, backward, conv, decay, decode_decay = [], None, None, None, None, None, None
-    decode_compact = None
+    decode_compact = tiny = cpu_other = None
     if not args.no_extra:
+        tiny = bench_tiny(lal, synth.FWD_CONFIGS["tiny"])
+        print(f"[bench] tiny fp32 layer: {tiny['us_per_call_back_to_back']:.1f} us/call back to back, "
+              f"{tiny['us_latency_median']:.1f} us latency", file=sys.stderr, flush=True)
         backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
         del bsets
         print(f"[bench] {cfg.name} backward: linattn {backward['linattn_bwd_us']:.1f} us, swa "
@@ -700,6 +828,8 @@ def main():
         print(f"[bench] decode (compact state): {decode_compact['us_per_step']:.1f} us/step", file=sys.stderr,
               flush=True)
     cpu = None if args.no_cpu else cpu_baseline(cfg)
+    if not args.no_cpu and not args.no_extra:
+        cpu_other = cpu_oracle_other()
 
     # the step is one operation (state-only pass + segment scan + fused main pass)
     achieved = main_res["layer_hbm_gbs"]
@@ -723,6 +853,9 @@ def main():
         "decay": decay,
         "copy_calibration": copy,
         "cpu_baseline": cpu,
+        "cpu_oracle_other_workloads": cpu_other,
+        "tiny_layer_latency": tiny,
+        "step_parity": main_res.get("parity"),
         "other_workloads": extra,
         "decode": decode,
         "decode_decay": decode_decay,

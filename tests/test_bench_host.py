@@ -18,7 +18,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 STATE = "void based::mfma::linattn_state_kernel<4, 0>(based::mfma::Params)"
-MAIN = "void based::mfma::linattn_mfma_kernel<4, 1, 0>(based::mfma::Params)"
+MAIN = "void based::mfma::linattn_mfma_kernel<4, 1, 0, 0>(based::mfma::Params)"
 QPASS = "based::bwdm::query_pass_kernel(based::bwdm::Params)"
 SWAB = "void based::swab::swa_bwd_mfma_kernel<4>(based::swab::Params)"
 DECODE = "void based::(anonymous namespace)::decode_step_kernel<unsigned short, 64, 273>(int)"
@@ -82,7 +82,7 @@ def test_summarize_pmc_scales_and_windows(tmp_path):
     k = layer["kernels"]
     assert k["based::mfma::linattn_state_kernel<4, 0>"]["dispatches"] == 3
     assert k["based::mfma::linattn_state_kernel<4, 0>"]["fetch_bytes"] == pytest.approx(1000.0 * 1024 * 0.5)
-    assert k["based::mfma::linattn_mfma_kernel<4, 1, 0>"]["write_bytes"] == pytest.approx(900.0 * 1024)
+    assert k["based::mfma::linattn_mfma_kernel<4, 1, 0, 0>"]["write_bytes"] == pytest.approx(900.0 * 1024)
     assert layer["bytes_per_call"] == pytest.approx(((1000 + 3000) * 0.5 + 100 + 900) * 1024)
     assert layer["source_hash"] == bench.source_hash("layer")
     bwd = json.loads((out / "traffic_bwd.json").read_text())
@@ -123,7 +123,7 @@ def test_summarize_stats_marks_step_and_backward(tmp_path):
     # the set-up and step calls of the layer are marked step; the backward's
     # calls bwd; decode (after the backward) neither
     assert "| step | 3 | 17.0 |" in lines["based::mfma::linattn_state_kernel<4, 0>"]
-    assert "| step | 3 | 58.0 |" in lines["based::mfma::linattn_mfma_kernel<4, 1, 0>"]
+    assert "| step | 3 | 58.0 |" in lines["based::mfma::linattn_mfma_kernel<4, 1, 0, 0>"]
     assert "| bwd | 2 | 83.0 |" in lines["based::bwdm::query_pass_kernel"]
     assert "| bwd | 2 | 71.0 |" in lines["based::swab::swa_bwd_mfma_kernel<4>"]
     assert "|  | 1 | 5.0 |" in lines["based::decode_step_kernel<unsigned short, 64, 273>"]
