@@ -25,7 +25,9 @@ __all__ = [
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbased.so")
+# The in-tree build; BASED_LIB_PATH names another build of the same ABI (the
+# tests load the sanitized host-only build of the argument checks this way).
+LIB_PATH = os.environ.get("BASED_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbased.so")
 DK = 16
 DPHI = 273
 DCMP = 153  # compact decode state rows: constant, 16 linear, 136 unordered pairs
@@ -60,8 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             f"{path} is missing: build the HIP library first (python -m linear_attention_lm_amd.build)")
     so = ctypes.CDLL(path)
     for name, (res, args) in _SIGNATURES.items():
-        fn = getattr(so, name)
-        fn.restype, fn.argtypes = res, args
+        if hasattr(so, name):  # a host-only build lacks the entry points with device code
+            fn = getattr(so, name)
+            fn.restype, fn.argtypes = res, args
     return so
 
 

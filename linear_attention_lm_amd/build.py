@@ -72,5 +72,30 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(BUILD, "libbased_sanitized.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The C ABI's argument validation alone (api.cpp and the host-side
+    planning, kernel launchers stubbed out) built for the host with
+    AddressSanitizer and UndefinedBehaviorSanitizer: a shared library with
+    every entry point that has no device code of its own, for the ABI tests
+    to run against (loaded with the sanitizer runtimes preloaded)."""
+    os.makedirs(BUILD, exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(PKG, "sanitize", "launch_stubs.cpp"), "-Wl,--no-undefined", "-lasan", "-lubsan",
+           "-o", SANITIZED_LIB]
+    out = _run(cmd)
+    if verbose:
+        print(out or f"built {SANITIZED_LIB}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    if "--sanitized" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose="-q" not in sys.argv)

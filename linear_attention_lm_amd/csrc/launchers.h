@@ -9,6 +9,24 @@
 
 namespace based {
 
+// Layout constants shared by the host-side planning (plan.cpp) and the
+// kernels (each kernel file checks its own constants against these).
+namespace layout {
+constexpr int CHUNK = 64;          // positions per chunk
+constexpr int FWD_SLOTS = 160;     // compact feature slots of the forward's state records
+constexpr int FWD_MAX_SUM = 3;     // segments summed directly by the forward's main pass
+constexpr int BWD_SLICE = 32;      // value columns per backward workgroup
+constexpr int BWD_MAXSEG = 8;      // backward segments per head at most
+constexpr int BWD_NF = 272;        // non-constant feature rows of the backward's states
+constexpr int BWD_RREC = BWD_NF * BWD_SLICE + BWD_NF + BWD_SLICE;  // floats of one suffix-state record
+}  // namespace layout
+
+// Host-side planning (plan.cpp): sequence segments per (batch, head) and
+// workspace sizes.
+void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
+void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
+int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks);
+
 struct LinattnArgs {
   const void* q; const void* k; const void* v; float* y;
   const float* S_in; const float* z_in; float* S_out; float* z_out;
@@ -23,7 +41,6 @@ hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t stre
 // bf16 chunked linear attention on the matrix cores (d_v in {32, 64, 96, 128}).
 bool linattn_mfma_supported(int dv);
 size_t linattn_mfma_workspace(int B, int H, int L, int dv);
-void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
 // The decayed variant (per-head gamma in a.gamma), same layouts and workspace.
 hipError_t launch_linattn_decay_mfma(const LinattnArgs& a, hipStream_t stream);

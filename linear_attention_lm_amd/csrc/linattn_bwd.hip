@@ -209,11 +209,6 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16) {
-  if (bf16 && linattn_bwd_mfma_supported(dv)) return linattn_bwd_mfma_workspace(B, H, L, dv);
-  return (size_t)B * H * L * 2 * sizeof(float);  // den and h per position
-}
-
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
   if (bf16 && linattn_bwd_mfma_supported(a.dv)) return launch_linattn_bwd_mfma(a, s);

@@ -62,7 +62,10 @@ constexpr int SCALE_TOP = 13;
 constexpr int MAXSEG = 8;            // segments per head at most (records summed directly)
 constexpr int NFC = 160;             // compact slots of the forward's state records
 constexpr int RREC = NF * SW + NF + SW;  // floats of one suffix-state record (R, r, sum g)
-constexpr int NFP = 32 * NKS;        // feature rows of the key pass's state copy (rows NF.. zero)
+constexpr int NFP = 32 * NKS;
+static_assert(C == layout::CHUNK && SW == layout::BWD_SLICE && MAXSEG == layout::BWD_MAXSEG && NF == layout::BWD_NF &&
+                  NFC == layout::FWD_SLOTS && RREC == layout::BWD_RREC,
+              "planning constants (plan.cpp) must match the kernels");        // feature rows of the key pass's state copy (rows NF.. zero)
 
 // Slot of the forward's compact records holding feature f of this layout
 // (f < 16: x_f; f = 16 + 16a + b: x_a x_b).  The compact layout: slot
@@ -1045,52 +1048,6 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
 }
 
 }  // namespace bwdm
-
-bool linattn_bwd_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 || dv == 128; }
-
-// Segments per head: enough workgroups for two per CU, at most MAXSEG, and at
-// least four chunks per segment.
-void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
-  const int nch = (L + bwdm::C - 1) / bwdm::C;
-  const int units = BH * (dv / bwdm::SW);
-  int want = (512 + units - 1) / units;
-  if (want > bwdm::MAXSEG) want = bwdm::MAXSEG;
-  int cap = nch / 4;
-  if (cap < 1) cap = 1;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  const int sc = nch < 1 ? 1 : (nch + want - 1) / want;
-  *seg_chunks = sc;
-  *nseg = nch < 1 ? 1 : (nch + sc - 1) / sc;
-}
-
-// Forward-record sub-segments per backward segment.  With two segments the
-// records cover only the first, as B*H workgroups of the state-only pass;
-// where that leaves most of the CUs idle (B*H <= 64) the record is split
-// (down to 8 chunks, up to one workgroup per CU) and the query pass sums the
-// parts.  Otherwise the extra records cost the query pass about what the
-// shorter pass saves, and with more segments each one adds to that sum.
-static int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks) {
-  int r = 1;
-  if (nseg != 2 || BH > 64) return r;
-  while (r < 4 && (long long)BH * 2 * r <= 256 && seg_chunks % (2 * r) == 0 && seg_chunks / (2 * r) >= 8) r *= 2;
-  return r;
-}
-
-size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
-  int nseg, sc;
-  const int BH = B * H;
-  linattn_bwd_mfma_plan(BH, L, dv, &nseg, &sc);
-  const int nslice = dv / bwdm::SW;
-  size_t floats = (size_t)(1 + nslice) * BH * L;                           // den, h per slice
-  if (nslice > 1) floats += (size_t)2 * nslice * BH * L * DK;               // dq, dk shares per slice
-  if (nseg > 1) {
-    const int rs = linattn_bwd_rec_split(BH, nseg, sc);
-    floats += (size_t)BH * nseg * rs * ((size_t)(bwdm::NFC + 1) * dv + (bwdm::NFC + 1));  // forward records
-    floats += (size_t)BH * (dv / bwdm::SW) * nseg * bwdm::RREC;                      // suffix records
-  }
-  return floats * sizeof(float);
-}
 
 hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   using namespace bwdm;

@@ -67,6 +67,8 @@ constexpr int SCALE_TOP = 13; // the scaled fp16 state stays below 2^(SCALE_TOP 
 // increments before its segment itself; beyond, a scan pass writes each
 // segment's starting state.
 constexpr int MAX_SUM = 3;
+static_assert(C == layout::CHUNK && NF == layout::FWD_SLOTS && MAX_SUM == layout::FWD_MAX_SUM,
+              "planning constants (plan.cpp) must match the kernels");
 
 enum SlotType : uint8_t { LIN = 0, DIAG = 1, OFF = 2, HALF = 3 };
 
@@ -1383,32 +1385,6 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
 }  // namespace mfma
 
 using namespace mfma;
-
-// Segments per (batch, head): enough workgroups to fill the GPU's 256
-// compute units (two per CU where they fit: d_v <= 64), each segment at
-// least 4 chunks long.
-void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks) {
-  const int nch = (L + C - 1) / C;
-  const int slots = dv <= 64 ? 512 : 256;
-  int want = (slots + BH - 1) / BH;
-  int cap = nch / 4;
-  if (cap < 1) cap = 1;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  const int sc = (nch + want - 1) / want;
-  *seg_chunks = sc < 1 ? 1 : sc;
-  *nseg = nch == 0 ? 1 : (nch + *seg_chunks - 1) / *seg_chunks;
-}
-
-bool linattn_mfma_supported(int dv) { return dv == 32 || dv == 64 || dv == 96 || dv == 128; }
-
-size_t linattn_mfma_workspace(int B, int H, int L, int dv) {
-  if (!linattn_mfma_supported(dv)) return 0;
-  int nseg, sc;
-  linattn_mfma_plan(B * H, L, dv, &nseg, &sc);
-  if (nseg <= 1) return 0;
-  return (size_t)B * H * nseg * ((size_t)(NF + 1) * dv + (NF + 1)) * sizeof(float);
-}
 
 template <int NT, int SWA, int DEC, int HI>
 static hipError_t launch_nt_hi(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
