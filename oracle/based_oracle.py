@@ -398,6 +398,40 @@ def linattn_bwd(q, k, v, dy):
     return dq, dk, dv
 
 
+def linattn_decay_bwd(q, k, v, gamma, dy):
+    """Gradients of the decayed linear attention (``linattn_decay_quadratic``,
+    no initial state) with respect to q, k and v, for an upstream gradient dy.
+
+    The decayed kernel matrix is A = K * W with W_ij = g^(i-j) for j <= i (0
+    otherwise), g = gamma[head]; W does not depend on q, k, v.  With
+    num = A V, den = A 1 and y = num / den, as in ``linattn_bwd``:
+      g_i = dy_i / den_i,  h_i = -(dy_i . y_i) / den_i,
+      dA_ij = g_i . v_j + h_i  (j <= i),  dV = A^T G,
+      dK = dA * W  (A's derivative in the kernel entries),
+      dX = dK * (1 + X),  dQ = dX K,  dK_keys = dX^T Q.
+    gamma has one entry per head (the axis before L).  Returns (dq, dk, dv).
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    g = _f64(gamma)
+    L = q.shape[-2]
+    i = np.arange(L)
+    d = (i[:, None] - i[None, :]).astype(np.float64)
+    gb = g.reshape(g.shape + (1,) * 2)
+    W = np.where(d >= 0, gb ** np.maximum(d, 0), 0.0)
+    X = q @ np.swapaxes(k, -1, -2)
+    A = taylor_kernel(X) * W
+    den = A.sum(axis=-1)
+    y = (A @ v) / den[..., None]
+    gg = dy / den[..., None]
+    h = -(dy * y).sum(axis=-1) / den
+    dA = (gg @ np.swapaxes(v, -1, -2) + h[..., None]) * (d >= 0)
+    dX = dA * W * (1.0 + X)
+    dq = dX @ k
+    dk = np.swapaxes(dX, -1, -2) @ q
+    dv = np.swapaxes(A, -1, -2) @ gg
+    return dq, dk, dv
+
+
 def linattn_bwd_rows(q, k, v, dy, rows, chunk: int = 256):
     """The gradients of ``linattn_bwd`` at selected positions only, for
     sequences too long for the L x L matrices: dq_i, dk_i and dv_i for each

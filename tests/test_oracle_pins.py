@@ -540,3 +540,51 @@ def test_compact_round_trips():
     Sc, zc = g.normal(size=(2, 153, 8)), g.normal(size=(2, 153))
     Sc2, zc2 = O.state_compact(*O.state_expand(Sc, zc))
     assert np.array_equal(Sc2, Sc) and np.array_equal(zc2, zc)
+
+
+# ------------------------------------------------------------ decayed gradients
+@pytest.mark.parametrize("L,dv,gam", [(1, 3, 0.5), (6, 4, 0.7), (9, 2, 0.95)])
+def test_linattn_decay_bwd_finite_differences(L, dv, gam):
+    """Decayed gradients against central differences of the decayed
+    quadratic forward (itself pinned against the recurrence above); two heads
+    with different decays."""
+    q, k, v, dy = rand(2, L, 16, scale=0.3), rand(2, L, 16, scale=0.3), rand(2, L, dv), rand(2, L, dv)
+    g = np.array([gam, 1.0 - 0.5 * (1.0 - gam)])
+    loss = lambda: float((O.linattn_decay_quadratic(q, k, v, g)[0] * dy).sum())
+    fd = _fd_grads(loss, [q, k, v])
+    for got, want in zip(O.linattn_decay_bwd(q, k, v, g, dy), fd):
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+def test_linattn_decay_bwd_gamma_one_and_autograd():
+    """gamma = 1 gives the undecayed gradients; and torch fp64 autograd
+    through a plain torch decayed forward (the masked Taylor kernel times
+    gamma^(i-j), row-normalised) agrees."""
+    torch = pytest.importorskip("torch")
+    L, dv = 30, 5
+    q, k, v, dy = rand(2, L, 16, scale=0.3), rand(2, L, 16, scale=0.3), rand(2, L, dv), rand(2, L, dv)
+    for got, want in zip(O.linattn_decay_bwd(q, k, v, np.ones(2), dy), O.linattn_bwd(q, k, v, dy)):
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    g = np.array([0.8, 0.97])
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    i, j = torch.arange(L)[:, None], torch.arange(L)[None, :]
+    dec = torch.tensor(g)[:, None, None] ** (i - j).clamp(min=0).double() * (j <= i)
+    x = tq @ tk.transpose(-1, -2)
+    w = (1 + x + x * x / 2) * dec
+    y = (w @ tv) / w.sum(-1, keepdim=True)
+    (y * torch.tensor(dy)).sum().backward()
+    for got, want in zip(O.linattn_decay_bwd(q, k, v, g, dy), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_linattn_decay_bwd_shift_and_vanishing_decay():
+    """The decayed output is still a convex combination of the values:
+    sum_j dv_j = sum_i dy_i.  A vanishing decay leaves each row its own value
+    (y_i -> v_i): dv -> dy and dq, dk -> 0."""
+    L, dv = 40, 6
+    q, k, v, dy = rand(L, 16, scale=0.3), rand(L, 16, scale=0.3), rand(L, dv), rand(L, dv)
+    _, _, dvg = O.linattn_decay_bwd(q[None], k[None], v[None], np.array([0.6]), dy[None])
+    np.testing.assert_allclose(dvg[0].sum(0), dy.sum(0), rtol=1e-12, atol=1e-12)
+    dq, dk, dvs = O.linattn_decay_bwd(q[None], k[None], v[None], np.array([1e-12]), dy[None])
+    np.testing.assert_allclose(dvs[0], dy, rtol=1e-9, atol=1e-9)
+    assert np.abs(dq).max() < 1e-9 and np.abs(dk).max() < 1e-9
