@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 8
+#define BASED_ABI_VERSION 9
 
 /* element type of q, k, v (and of the decode ring buffers) */
 enum {
@@ -148,9 +148,10 @@ int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
  *   gamma  [H] fp32, device memory, 0 < gamma_h <= 1 (not checked)
  *   every other argument as for based_linattn_fwd (same workspace size; S_in
  *   decays like the rest: position i sees gamma^(i+1) S_in).
- * BASED_BF16 with d_v in {32, 64, 96, 128} only (BASED_ERR_UNSUPPORTED
- * otherwise); numerics as for based_linattn_fwd, with the per-key decay
- * weights of the state update rounded to fp16.
+ * BASED_BF16 with d_v in {32, 64, 96, 128} runs on the matrix cores,
+ * numerics as for based_linattn_fwd with the per-key decay weights of the
+ * state update rounded to fp16; BASED_F32 and other d_v use fp32 vector
+ * arithmetic throughout (the decay weights gamma^d from exp2 of d log2 gamma).
  */
 int based_linattn_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y,
                             const float* S_in, const float* z_in, float* S_out, float* z_out,
@@ -201,6 +202,28 @@ size_t based_linattn_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, 
 int based_linattn_bwd(const void* q, const void* k, const void* v, const float* y, const float* dy,
                       float* dq, float* dk, float* dv, int B, int H, int L, int d_k, int d_v, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The decayed linear attention, backward: gradients of based_linattn_decay_fwd's
+ * y (zero initial state) with respect to q, k and v -- based_linattn_bwd with
+ * every kernel entry weighed by gamma_h^(i-j) (K_ij -> K_ij gamma_h^(i-j) in
+ * den_i, dq_i, dk_j and dv_j; the train README's decay strategy, read as for
+ * the forward).
+ *
+ *   gamma      [H] fp32, device memory, 0 < gamma_h <= 1 (not checked)
+ *   q, k, v, y, dy, dq, dk, dv: as for based_linattn_bwd (y from
+ *              based_linattn_decay_fwd with the same gamma)
+ *   workspace: at least 2 * B * H * L * 4 bytes of device memory (never more
+ *              than based_linattn_bwd_workspace_bytes for the same shape);
+ *              contents on entry are ignored.
+ * Both dtypes and every d_v in {16, ..., 128}: the direct form, fp32 vector
+ * arithmetic over every (i, j <= i) pair (work quadratic in L).  Errors as for
+ * based_linattn_bwd, and BASED_ERR_NULL for a null gamma; gamma must not
+ * overlap an output or the workspace.
+ */
+int based_linattn_decay_bwd(const void* q, const void* k, const void* v, const float* gamma, const float* y,
+                            const float* dy, float* dq, float* dk, float* dv, int B, int H, int L, int d_k,
+                            int d_v, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Sliding-window softmax attention, backward: gradients of based_swa_fwd's y
@@ -261,6 +284,21 @@ int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, f
                     const float* S_in, const float* z_in, float* S_out, float* z_out,
                     int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * based_layer_fwd with the linear attention's state decayed per head, as in
+ * based_linattn_decay_fwd (gamma [H] fp32 device memory, 0 < gamma_h <= 1,
+ * not checked; y_lin is based_linattn_decay_fwd's y); the window attention
+ * (y_swa) has no decay.  Every other argument, and the workspace size, as for
+ * based_layer_fwd; BASED_ERR_NULL for a null gamma, BASED_ERR_ALIAS when
+ * gamma overlaps an output.  BASED_BF16 with d_v in {32, 64, 96, 128} is one
+ * fused matrix-core pass; otherwise the two attentions run as separate
+ * kernels.
+ */
+int based_layer_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y_lin,
+                          float* y_swa, const float* S_in, const float* z_in, float* S_out, float* z_out,
+                          int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * based_layer_fwd without a workspace argument, for callers that cannot

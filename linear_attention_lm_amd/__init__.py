@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "abi_version", "linattn_fwd", "linattn_workspace_bytes", "swa_fwd", "layer_fwd",
+    "layer_decay_fwd", "linattn_decay_bwd",
     "linattn_bwd", "linattn_bwd_workspace_bytes", "swa_bwd", "baseconv_fwd", "linattn_decay_fwd",
     "DecodeState", "decode_init", "decode_prefill", "decode_step", "BasedError", "DPHI", "DK",
 ]
@@ -49,6 +50,8 @@ _SIGNATURES = {
     "based_swa_bwd": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
     "based_baseconv_fwd": (_i, [_vp] * 5 + [_i] * 5 + [_vp]),
     "based_linattn_decay_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
+    "based_linattn_decay_bwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
+    "based_layer_decay_fwd": (_i, [_vp] * 10 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
     "based_decode_step_decay": (_i, [_vp] * 11 + [_i] * 5 + [_f, _i, _vp]),
     "based_decode_step_compact": (_i, [_vp] * 11 + [_i] * 5 + [_f, _i, _vp]),
     "based_state_compact": (_i, [_vp] * 4 + [_i] * 3 + [_vp]),
@@ -164,7 +167,7 @@ def linattn_decay_fwd(q, k, v, gamma, S_in=None, z_in=None, *, return_state=Fals
                       z_out=None, workspace=None):
     """Causal Taylor linear attention with a per-head state decay gamma [H]
     (fp32, 0 < gamma <= 1): S_i = gamma S_{i-1} + phi(k_i) v_i^T, likewise z.
-    bf16 q, k, v with d_v in {32, 64, 96, 128}.  Returns y, or (y, S, z)."""
+    Either dtype, d_v in {16, ..., 128}.  Returns y, or (y, S, z)."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -200,6 +203,39 @@ def swa_fwd(q, k, v, window: int = 64, scale: float = 1.0, *, y=None):
     _check(_lib().based_swa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), B, H, L, dqk, dv, window, float(scale),
                              _dtype_code(q), _stream()))
     return y
+
+
+def layer_decay_fwd(q, k, v, gamma, window: int = 64, scale: float = 1.0, S_in=None, z_in=None, *,
+                    return_state=False, y_lin=None, y_swa=None, S_out=None, z_out=None, workspace=None):
+    """:func:`layer_fwd` with the linear attention's state decayed per head
+    by gamma [H] (fp32), as in :func:`linattn_decay_fwd`; the window
+    attention has no decay.  Returns (y_lin, y_swa), plus (S, z) when
+    ``return_state``."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B,H,L,16] and v [B,H,L,dv] of one dtype")
+    if gamma.shape != (H,) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be fp32 [H]")
+    _dev(q, k, v, gamma, S_in, z_in, y_lin, y_swa, S_out, z_out, workspace)
+    if y_lin is None:
+        y_lin = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if y_swa is None:
+        y_swa = torch.empty(B, H, L, dv, device=q.device, dtype=torch.float32)
+    if return_state and S_out is None:
+        S_out = torch.empty(B, H, DPHI, dv, device=q.device, dtype=torch.float32)
+        z_out = torch.empty(B, H, DPHI, device=q.device, dtype=torch.float32)
+    dt = _dtype_code(q)
+    need = _lib().based_linattn_workspace_bytes(B, H, L, dk, dv, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().based_layer_decay_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(y_lin), _ptr(y_swa),
+                                        _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), B, H, L, dk, dv, window,
+                                        float(scale), dt, _ptr(workspace), wbytes, _stream()))
+    if return_state or S_out is not None:
+        return y_lin, y_swa, S_out, z_out
+    return y_lin, y_swa
 
 
 def layer_fwd(q, k, v, window: int = 64, scale: float = 1.0, S_in=None, z_in=None, *, return_state=False,
@@ -281,6 +317,26 @@ def linattn_bwd(q, k, v, y, dy, *, dq=None, dk=None, dv=None, workspace=None):
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().based_linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
                                  B, H, L, dk_, dvw, dt, _ptr(workspace), wbytes, _stream()))
+    return dq, dk, dv
+
+
+def linattn_decay_bwd(q, k, v, gamma, y, dy, *, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv), fp32, of :func:`linattn_decay_fwd`'s output y
+    (zero initial state, per-head decay gamma [H] fp32) for the upstream
+    gradient dy."""
+    _check_bwd_args(q, k, v, y, dy)
+    B, H, L, dk_ = q.shape
+    dvw = v.shape[-1]
+    if gamma.shape != (H,) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be fp32 [H]")
+    _dev(q, k, v, gamma, y, dy, dq, dk, dv, workspace)
+    dq, dk, dv = _grads_out(q, k, v, dq, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(1, 2 * B * H * L * 4), device=q.device, dtype=torch.uint8)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(_lib().based_linattn_decay_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(y), _ptr(dy), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, H, L, dk_, dvw, _dtype_code(q), _ptr(workspace), wbytes,
+                                       _stream()))
     return dq, dk, dv
 
 

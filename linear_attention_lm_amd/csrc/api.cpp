@@ -117,7 +117,6 @@ BASED_API int based_linattn_decay_fwd(const void* q, const void* k, const void* 
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
   if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
-  if (dtype != BASED_BF16 || !based::linattn_mfma_supported(d_v)) return BASED_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
   if (!head_extent_ok(L, d_v) || !head_extent_ok(L, d_k)) return BASED_ERR_SHAPE;
   if (!gamma || (L > 0 && (!q || !k || !v || !y))) return BASED_ERR_NULL;
@@ -139,13 +138,15 @@ BASED_API int based_linattn_decay_fwd(const void* q, const void* k, const void* 
     return st;
   if (L == 0 && !S_out) return BASED_OK;
   based::LinattnArgs a{q, k, v, y, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes, gamma};
-  return status_of(based::launch_linattn_decay_mfma(a, (hipStream_t)stream));
+  if (dtype == BASED_BF16 && based::linattn_mfma_supported(d_v))
+    return status_of(based::launch_linattn_decay_mfma(a, (hipStream_t)stream));
+  return status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 
-BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
-                               const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
-                               int L, int d_k, int d_v, int window, float scale, int dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static int layer_fwd_impl(const void* q, const void* k, const void* v, const float* gamma, float* y_lin,
+                          float* y_swa, const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
+                          int L, int d_k, int d_v, int window, float scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
   if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
   if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
@@ -171,12 +172,14 @@ BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float
       for (const Span& s : ins)
         if (overlap(o, s)) return BASED_ERR_ALIAS;
   }
-  const Span io[] = {ins[0], ins[1], ins[2], outs[0], outs[1]};
-  if (int st = check_states(S_in, z_in, S_out, z_out, BH, d_v, io, L > 0 ? 5 : 0, span(workspace, need));
+  const Span gs = span(gamma, (size_t)H * 4);
+  const Span io[] = {ins[0], ins[1], ins[2], outs[0], outs[1], gs};
+  if (L > 0 && (overlap(outs[0], gs) || overlap(outs[1], gs))) return BASED_ERR_ALIAS;
+  if (int st = check_states(S_in, z_in, S_out, z_out, BH, d_v, io, L > 0 ? 6 : 0, span(workspace, need));
       st != BASED_OK)
     return st;
 
-  based::LinattnArgs a{q, k, v, y_lin, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes};
+  based::LinattnArgs a{q, k, v, y_lin, S_in, z_in, S_out, z_out, B, H, L, d_v, workspace, workspace_bytes, gamma};
   if (L == 0 && !S_out) return BASED_OK;
   if (dtype == BASED_BF16 && based::linattn_mfma_supported(d_v))
     return status_of(based::launch_layer_mfma(a, y_swa, window, scale, (hipStream_t)stream));
@@ -186,6 +189,23 @@ BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float
   based::SwaArgs sa{q, k, v, y_swa, B, H, L, d_k, d_v, window, scale};
   if (dtype == BASED_BF16) return status_of(based::launch_swa_mfma(sa, (hipStream_t)stream));
   return status_of(based::launch_swa_valu(sa, false, (hipStream_t)stream));
+}
+
+BASED_API int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
+                               const float* S_in, const float* z_in, float* S_out, float* z_out, int B, int H,
+                               int L, int d_k, int d_v, int window, float scale, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return layer_fwd_impl(q, k, v, nullptr, y_lin, y_swa, S_in, z_in, S_out, z_out, B, H, L, d_k, d_v, window, scale,
+                        dtype, workspace, workspace_bytes, stream);
+}
+
+BASED_API int based_layer_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y_lin,
+                                     float* y_swa, const float* S_in, const float* z_in, float* S_out, float* z_out,
+                                     int B, int H, int L, int d_k, int d_v, int window, float scale, int dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gamma) return BASED_ERR_NULL;
+  return layer_fwd_impl(q, k, v, gamma, y_lin, y_swa, S_in, z_in, S_out, z_out, B, H, L, d_k, d_v, window, scale,
+                        dtype, workspace, workspace_bytes, stream);
 }
 
 BASED_API int based_swa_fwd(const void* q, const void* k, const void* v, float* y, int B, int H, int L, int d_qk,
@@ -260,6 +280,34 @@ BASED_API int based_linattn_bwd(const void* q, const void* k, const void* v, con
       if (overlap(ws, s)) return BASED_ERR_ALIAS;
   }
   based::LinattnBwdArgs a{q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, workspace, workspace_bytes};
+  return status_of(based::launch_linattn_bwd(a, dtype == BASED_BF16, (hipStream_t)stream));
+}
+
+BASED_API int based_linattn_decay_bwd(const void* q, const void* k, const void* v, const float* gamma, const float* y,
+                                      const float* dy, float* dq, float* dk, float* dv, int B, int H, int L, int d_k,
+                                      int d_v, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 0) return BASED_ERR_SHAPE;
+  if (d_k != BASED_DK || !valid_dv(d_v)) return BASED_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)L > (1LL << 30)) return BASED_ERR_SHAPE;
+  if ((long long)B * H * ((L + 63) / 64) > 0x7fffffffLL) return BASED_ERR_SHAPE;
+  if (!head_extent_ok(L, d_v)) return BASED_ERR_SHAPE;
+  if (!gamma) return BASED_ERR_NULL;
+  if (L == 0) return BASED_OK;
+  if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
+  // the direct form: den and h per position
+  const size_t BH = (size_t)B * H, need = 2 * BH * L * sizeof(float);
+  if (!workspace || workspace_bytes < need) return BASED_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const Span g = span(gamma, (size_t)H * 4), ws = span(workspace, need);
+  const Span all[] = {span(q, BH * L * BASED_DK * es), span(k, BH * L * BASED_DK * es), span(v, BH * L * d_v * es),
+                      span(y, BH * L * d_v * 4), span(dy, BH * L * d_v * 4), span(dq, BH * L * BASED_DK * 4),
+                      span(dk, BH * L * BASED_DK * 4), span(dv, BH * L * d_v * 4), g};
+  for (const Span& s : all)
+    if (overlap(ws, s)) return BASED_ERR_ALIAS;
+  for (int o = 5; o < 8; ++o)
+    if (overlap(all[o], g)) return BASED_ERR_ALIAS;
+  based::LinattnBwdArgs a{q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, workspace, workspace_bytes, gamma};
   return status_of(based::launch_linattn_bwd(a, dtype == BASED_BF16, (hipStream_t)stream));
 }
 

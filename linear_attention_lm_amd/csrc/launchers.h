@@ -77,6 +77,7 @@ struct LinattnBwdArgs {
   float* gq; float* gk; float* gv;
   int B, H, L, dv;
   void* workspace; size_t workspace_bytes;
+  const float* gamma = nullptr;  // [H] per-head state decay (decayed variant: the direct form)
 };
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16);
 // bf16 on the matrix cores for d_v in {32, 64, 96, 128} (slices of 32 columns)

@@ -40,18 +40,19 @@ __device__ __forceinline__ void stage(float (*dst)[STRIDE], const T* src, int r0
 }
 
 // Per query i (one thread): den_i, then g_i (kept in LDS), h_i and dq_i.
-template <typename T, int DV>
+template <typename T, int DV, int DEC>
 __global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const T* __restrict__ v, const float* __restrict__ y,
                                                        const float* __restrict__ dy, float* __restrict__ gq,
                                                        float* __restrict__ den_out, float* __restrict__ h_out, int L,
-                                                       int nblk) {
+                                                       int nblk, const float* __restrict__ gamma, int H) {
   __shared__ float ks[TB][DK + 1];
   __shared__ float vs[TB][DV + 1];
   __shared__ float gs[TB][DV + 1];
   const int t = threadIdx.x;
   const size_t bh = blockIdx.x / nblk;
   const int i0 = (blockIdx.x % nblk) * TB, i = i0 + t;
+  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;  // decay weight of (i, j): 2^(lg (i - j))
   const T* kh = k + bh * L * DK;
   const T* vh = v + bh * (size_t)L * DV;
   float qi[DK];
@@ -74,7 +75,8 @@ __global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, 
       float x = 0.f;
 #pragma unroll
       for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qi[e], ks[jj][e], x);
-      den += 1.f + x + 0.5f * x * x;
+      const float K = 1.f + x + 0.5f * x * x;
+      den += DEC ? K * exp2f(lg * (float)(i - j0 - jj)) : K;
     }
   }
   // g_i, h_i
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, 
       for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qi[e], ks[jj][e], x);
       float gv = h;
       for (int c = 0; c < DV; ++c) gv = __builtin_fmaf(gs[t][c], vs[jj][c], gv);
-      const float cij = gv * (1.f + x);
+      float cij = gv * (1.f + x);
+      if (DEC) cij *= exp2f(lg * (float)(i - j0 - jj));
 #pragma unroll
       for (int e = 0; e < DK; ++e) acc[e] = __builtin_fmaf(cij, ks[jj][e], acc[e]);
     }
@@ -119,11 +122,12 @@ __global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, 
 }
 
 // Per key j (one thread): dk_j and dv_j over the queries i >= j.
-template <typename T, int DV>
+template <typename T, int DV, int DEC>
 __global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const float* __restrict__ dy,
                                                      const float* __restrict__ den_in, const float* __restrict__ h_in,
-                                                     float* __restrict__ gk, float* __restrict__ gv, int L, int nblk) {
+                                                     float* __restrict__ gk, float* __restrict__ gv, int L, int nblk,
+                                                     const float* __restrict__ gamma, int H) {
   __shared__ float qs[TB][DK + 1];
   __shared__ float gs[TB][DV + 1];
   __shared__ float hs[TB];
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, co
   const int t = threadIdx.x;
   const size_t bh = blockIdx.x / nblk;
   const int j0 = (blockIdx.x % nblk) * TB, j = j0 + t;
+  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;
   const T* qh = q + bh * L * DK;
   float kj[DK];
   if (j < L) {
@@ -159,13 +164,14 @@ __global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, co
       float x = 0.f;
 #pragma unroll
       for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qs[ii][e], kj[e], x);
-      const float K = 1.f + x + 0.5f * x * x;
+      const float wd = DEC ? exp2f(lg * (float)(i0 + ii - j)) : 1.f;
+      const float K = (1.f + x + 0.5f * x * x) * wd;
       float gvv = hs[ii];
       for (int c = 0; c < DV; ++c) {
         gvv = __builtin_fmaf(gs[ii][c], vj[t][c], gvv);
         dvj[t][c] = __builtin_fmaf(K, gs[ii][c], dvj[t][c]);
       }
-      const float cij = gvv * (1.f + x);
+      const float cij = gvv * (1.f + x) * wd;
 #pragma unroll
       for (int e = 0; e < DK; ++e) acc[e] = __builtin_fmaf(cij, qs[ii][e], acc[e]);
     }
@@ -178,18 +184,23 @@ __global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, co
   }
 }
 
-template <typename T, int DV>
-hipError_t launch_direct(const LinattnBwdArgs& a, hipStream_t s) {
+template <typename T, int DV, int DEC>
+hipError_t launch_direct_dec(const LinattnBwdArgs& a, hipStream_t s) {
   const int nblk = (a.L + TB - 1) / TB;
   const size_t BH = (size_t)a.B * a.H;
   float* den = (float*)a.workspace;
   float* h = den + BH * a.L;
-  hipLaunchKernelGGL((bwd_query_kernel<T, DV>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, a.y, a.dy, a.gq, den, h, a.L, nblk);
+  hipLaunchKernelGGL((bwd_query_kernel<T, DV, DEC>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, a.y, a.dy, a.gq, den, h, a.L, nblk, a.gamma, a.H);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_key_kernel<T, DV>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, a.dy, den, h, a.gk, a.gv, a.L, nblk);
+  hipLaunchKernelGGL((bwd_key_kernel<T, DV, DEC>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, a.dy, den, h, a.gk, a.gv, a.L, nblk, a.gamma, a.H);
   return hipGetLastError();
+}
+
+template <typename T, int DV>
+hipError_t launch_direct(const LinattnBwdArgs& a, hipStream_t s) {
+  return a.gamma ? launch_direct_dec<T, DV, 1>(a, s) : launch_direct_dec<T, DV, 0>(a, s);
 }
 
 template <typename T>
@@ -211,7 +222,7 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
-  if (bf16 && linattn_bwd_mfma_supported(a.dv)) return launch_linattn_bwd_mfma(a, s);
+  if (!a.gamma && bf16 && linattn_bwd_mfma_supported(a.dv)) return launch_linattn_bwd_mfma(a, s);
   return bf16 ? launch_direct_dv<bf16_t>(a, s) : launch_direct_dv<float>(a, s);
 }
 

@@ -1469,19 +1469,23 @@ hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int SWA>
+template <int SWA, int DEC>
 static hipError_t launch_layer(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
   switch (a.dv) {
-    case 32: return launch_nt<2, SWA>(a, y_swa, window, scale, s);
-    case 64: return launch_nt<4, SWA>(a, y_swa, window, scale, s);
-    case 96: return launch_nt<6, SWA>(a, y_swa, window, scale, s);
-    case 128: return launch_nt<8, SWA>(a, y_swa, window, scale, s);
+    case 32: return launch_nt<2, SWA, DEC>(a, y_swa, window, scale, s);
+    case 64: return launch_nt<4, SWA, DEC>(a, y_swa, window, scale, s);
+    case 96: return launch_nt<6, SWA, DEC>(a, y_swa, window, scale, s);
+    case 128: return launch_nt<8, SWA, DEC>(a, y_swa, window, scale, s);
   }
   return hipErrorInvalidValue;
 }
 
+// The fused layer pass; with a.gamma the linear attention's state decays
+// per head (the window attention has no decay).
 hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
-  return window >= C ? launch_layer<1>(a, y_swa, window, scale, s) : launch_layer<2>(a, y_swa, window, scale, s);
+  if (a.gamma)
+    return window >= C ? launch_layer<1, 1>(a, y_swa, window, scale, s) : launch_layer<2, 1>(a, y_swa, window, scale, s);
+  return window >= C ? launch_layer<1, 0>(a, y_swa, window, scale, s) : launch_layer<2, 0>(a, y_swa, window, scale, s);
 }
 
 }  // namespace based

@@ -11,6 +11,7 @@
 // per unordered feature pair, see based_device.h).
 //
 // One workgroup of 256 threads per (batch, head); chunks run in sequence.
+// A per-head decay of the state (DEC) is the same pass with decay weights.
 #include "based_device.h"
 #include "launchers.h"
 
@@ -49,18 +50,26 @@ __device__ float phi_from_compact(const float* T, int f, int c, int ld) {
   return T[(1 + DK + pair_index(lo, hi)) * ld + c] * INV_SQRT2;
 }
 
-template <typename T, int DV>
+// DEC: the decayed variant (the based/train README's optional decay
+// strategy, read as a per-head factor 0 < gamma <= 1 on the state:
+// S_i = gamma S_{i-1} + phi(k_i) v_i^T, z likewise).  The state entering a
+// chunk reaches its position i (0-based in the chunk) times gamma^(i+1), an
+// in-chunk key j weighs gamma^(i-j), and the update is S <- gamma^n S +
+// sum_j gamma^(n-1-j) phi(k_j) v_j^T over the chunk's n positions.
+template <typename T, int DV, int DEC>
 __global__ __launch_bounds__(NT) void linattn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ y,
-    const float* S_in, const float* z_in, float* S_out, float* z_out, int L) {
+    const float* S_in, const float* z_in, float* S_out, float* z_out, int L, const float* gamma, int H) {
   constexpr int CPT = DV / 4;  // readout columns per thread
   __shared__ float Ts[NCOMPACT][DV];
   __shared__ float zs[NCOMPACT];
   __shared__ float qs[C][DK];
   __shared__ float ks[C][DK];
   __shared__ float vs[C][DV];
+  __shared__ float wk[C];  // decayed variant: weight gamma^(n-1-j) of the chunk's key j in the update
 
   const int bh = blockIdx.x;
+  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;
   const int tid = threadIdx.x;
   const T* qb = q + (size_t)bh * L * DK;
   const T* kb = k + (size_t)bh * L * DK;
@@ -86,6 +95,7 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
       const int j = e / DV, d = e % DV;
       vs[j][d] = j < n ? to_f32(vb[(size_t)(c0 + j) * DV + d]) : 0.f;
     }
+    if (DEC && tid < C) wk[tid] = tid < n ? exp2f(lg * (float)(n - 1 - tid)) : 0.f;
     __syncthreads();
 
     // ---- readout of the state before the chunk + in-chunk masked term
@@ -116,11 +126,18 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
             for (int c = 0; c < CPT; ++c) num[c] += w * Ts[f][col0 + c];
           }
         }
+        if (DEC) {  // the state before the chunk, decayed over positions c0 .. c0 + i
+          const float cf = exp2f(lg * (float)(i + 1));
+          den *= cf;
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) num[c] *= cf;
+        }
         for (int j = 0; j <= i; ++j) {
           float x = 0.f;
 #pragma unroll
           for (int d = 0; d < DK; ++d) x += qr[d] * ks[j][d];
-          const float w = 1.f + x + 0.5f * x * x;
+          float w = 1.f + x + 0.5f * x * x;
+          if (DEC) w *= exp2f(lg * (float)(i - j));
           den += w;
 #pragma unroll
           for (int c = 0; c < CPT; ++c) num[c] += w * vs[j][col0 + c];
@@ -140,29 +157,34 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
     {
       constexpr int FS = NT / DV;  // features handled in parallel per column
       const int c = tid % DV;
+      const float gn = DEC ? exp2f(lg * (float)n) : 1.f;  // decay of the carried state over the chunk
+      auto kw = [&](int j) { return DEC ? wk[j] : 1.f; };
       for (int f = tid / DV; tid < FS * DV && f < NCOMPACT; f += FS) {
         float acc = 0.f;
         if (f == 0) {
-          for (int j = 0; j < n; ++j) acc += vs[j][c];
+          for (int j = 0; j < n; ++j) acc += kw(j) * vs[j][c];
         } else if (f < 1 + DK) {
-          for (int j = 0; j < n; ++j) acc += ks[j][f - 1] * vs[j][c];
+          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][f - 1] * vs[j][c];
         } else {
           const int a = c_pairs.a[f - 1 - DK], b = c_pairs.b[f - 1 - DK];
-          for (int j = 0; j < n; ++j) acc += ks[j][a] * ks[j][b] * vs[j][c];
+          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][a] * ks[j][b] * vs[j][c];
         }
-        Ts[f][c] += acc;
+        Ts[f][c] = DEC ? gn * Ts[f][c] + acc : Ts[f][c] + acc;
       }
       for (int f = tid; f < NCOMPACT; f += NT) {
         float acc = 0.f;
         if (f == 0) {
-          acc = (float)n;
+          if (DEC)
+            for (int j = 0; j < n; ++j) acc += wk[j];
+          else
+            acc = (float)n;
         } else if (f < 1 + DK) {
-          for (int j = 0; j < n; ++j) acc += ks[j][f - 1];
+          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][f - 1];
         } else {
           const int a = c_pairs.a[f - 1 - DK], b = c_pairs.b[f - 1 - DK];
-          for (int j = 0; j < n; ++j) acc += ks[j][a] * ks[j][b];
+          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][a] * ks[j][b];
         }
-        zs[f] += acc;
+        zs[f] = DEC ? gn * zs[f] + acc : zs[f] + acc;
       }
     }
   }
@@ -177,8 +199,12 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
 
 template <typename T, int DV>
 hipError_t launch_dv(const LinattnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((linattn_valu_kernel<T, DV>), dim3(a.B * a.H), dim3(NT), 0, s,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L);
+  if (a.gamma)
+    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 1>), dim3(a.B * a.H), dim3(NT), 0, s, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
+  else
+    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 0>), dim3(a.B * a.H), dim3(NT), 0, s, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
   return hipGetLastError();
 }
 

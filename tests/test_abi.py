@@ -29,7 +29,7 @@ def so():
 
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(so, n), n
 
@@ -41,7 +41,7 @@ def test_header_status_codes_match():
 
 
 def test_version_and_strings(so):
-    assert so.based_abi_version() == 8
+    assert so.based_abi_version() == 9
     for code in [0, *ERR.values(), 12345]:
         s = so.based_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -220,8 +220,11 @@ def test_decay_validation(so):
     need = so.based_linattn_workspace_bytes(1, 2, 5000, 16, 64, 1)
     call = lambda gam=gam, y=y, dv=64, dt=1, ws=big * 10, wsb=need: so.based_linattn_decay_fwd(
         q, k, v, gam, y, None, None, None, None, 1, 2, 5000, 16, dv, dt, ws, wsb, None)
-    assert call(dt=0) == ERR["UNSUPPORTED"]   # fp32: not offered
-    assert call(dv=48) == ERR["UNSUPPORTED"]
+    # fp32 and widths the matrix cores do not take are offered (the vector
+    # path): such calls get as far as the later checks
+    assert call(dt=0, gam=None) == ERR["NULL"]
+    assert call(dv=48, y=q) == ERR["ALIAS"]
+    assert call(dv=24) == ERR["UNSUPPORTED"]
     assert call(gam=None) == ERR["NULL"]
     assert call(y=q) == ERR["ALIAS"]
     assert call(y=gam) == ERR["ALIAS"]
@@ -317,3 +320,25 @@ def test_state_alias_rules(so):
     assert fwd(so, S_in=5 * G, z_in=6 * G, ws=5 * G + 64, **far) == ERR["ALIAS"]
     assert fwd(so, S_out=5 * G, z_out=6 * G, ws=6 * G - 64, **far) == ERR["ALIAS"]
     assert fwd(so, ws=2 * G + 128, **far) == ERR["ALIAS"]  # workspace over k
+
+
+def test_decay_layer_and_backward_validation(so):
+    """based_layer_decay_fwd and based_linattn_decay_bwd: a null gamma, gamma
+    under an output, a short workspace, an unsupported width."""
+    G = 1 << 28
+    q, k, v, gam, y1, y2 = (G * (i + 1) for i in range(6))
+    lay = lambda gam=gam, y1=y1, dv=64, win=64: so.based_layer_decay_fwd(
+        q, k, v, gam, y1, y2, None, None, None, None, 1, 2, 300, 16, dv, win, ctypes.c_float(1.0), 1, None, 0, None)
+    assert lay(gam=None) == ERR["NULL"]
+    assert lay(y1=gam) == ERR["ALIAS"]
+    assert lay(win=0) == ERR["WINDOW"]
+    assert lay(dv=40) == ERR["UNSUPPORTED"]
+    y, dy, dq, dk, dv_ = (G * (i + 7) for i in range(5))
+    bwd = lambda gam=gam, dq=dq, ws=G * 13, wsb=2 * 2 * 300 * 4, dt=1: so.based_linattn_decay_bwd(
+        q, k, v, gam, y, dy, dq, dk, dv_, 1, 2, 300, 16, 64, dt, ws, wsb, None)
+    assert bwd(gam=None) == ERR["NULL"]
+    assert bwd(dq=gam) == ERR["ALIAS"]
+    assert bwd(wsb=100) == ERR["WORKSPACE"]
+    assert bwd(ws=None) == ERR["WORKSPACE"]
+    assert bwd(ws=gam) == ERR["ALIAS"]
+    assert bwd(dt=5) == ERR["DTYPE"]

@@ -110,3 +110,133 @@ def test_decay_initial_state_across_segments(based, L):
         err = rowinf_rel(y[b, h], ref)
         report(f"decay {cfg.name} head ({b}, {h})", err, TOL[q.dtype])
         assert err <= TOL[q.dtype], (b, h, err)
+
+
+# ------------------------------------------- the vector path (fp32, other d_v)
+@pytest.mark.parametrize("dtype,dv,L", [("f32", 64, 256), ("f32", 48, 130), ("f32", 128, 1), ("bf16", 48, 300),
+                                        ("bf16", 80, 65)])
+def test_decay_vector_path(based, dtype, dv, L):
+    """fp32 inputs (the tiny config's dtype, tolerance 1e-5) and widths the
+    matrix-core pass does not take run the decayed chunked pass on the vector
+    ALUs."""
+    run(based, SMALL.replace(L=L, dv=dv, dtype=dtype, name=f"vector {dtype} dv{dv} L{L}"))
+
+
+def test_decay_tiny_config_fp32(based):
+    """The tiny layer configuration (B1 H2 L256 d_v 64, fp32) with decays 1 and
+    0.75: y and the exported state against the recurrence at 1e-5."""
+    cfg = synth.FWD_CONFIGS["tiny"]
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    y, S, z = based.linattn_decay_fwd(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), return_state=True)
+    torch.cuda.synchronize()
+    y_ref, _, S_ref, z_ref = O.linattn_decay_recurrent(q, k, v, g.numpy())
+    err = max(rowinf_rel(y, y_ref), rowinf_rel(S, S_ref))
+    report("decay tiny fp32 y / S_out", err, 1e-5)
+    assert err <= 1e-5
+
+
+def test_decay_vector_path_initial_state(based):
+    """fp32 with an initial state: it decays as gamma^(i+1) at position i."""
+    cfg = SMALL.replace(B=1, H=3, L=200, dtype="f32")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    _, kp, vp = synth.fwd_inputs(cfg.replace(L=100), 1)
+    S0, z0 = (torch.from_numpy(t).float() for t in O.linattn_state(kp, vp))
+    g = synth.decay_rates(cfg.H)
+    y = based.linattn_decay_fwd(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), S0.to(DEV), z0.to(DEV))
+    torch.cuda.synchronize()
+    y_ref = O.linattn_decay_recurrent(q, k, v, g.numpy(), S0, z0)[0]
+    err = rowinf_rel(y, y_ref)
+    report("decay fp32 with S_in", err, 1e-5)
+    assert err <= 1e-5
+
+
+# ------------------------------------------------------------ decayed layer
+@pytest.mark.parametrize("case", ["360m", "window17", "f32", "bf16_dv48"])
+def test_layer_decay(based, case):
+    """based_layer_decay_fwd: y_lin against the decayed oracle and equal to
+    based_linattn_decay_fwd's output (1e-6: the same arithmetic in another
+    kernel), y_swa against the window softmax (no decay).  The 360M shape runs
+    the fused matrix-core pass over four segments; a window of 17 its general
+    window path; fp32 and d_v 48 the separate vector kernels."""
+    cfg, window, heads = {
+        "360m": (synth.FWD_CONFIGS["based360m"], 64, [(0, 1), (7, 14)]),
+        "window17": (SMALL.replace(B=1, H=8, L=700), 17, None),
+        "f32": (SMALL.replace(B=1, H=4, L=300, dtype="f32"), 64, None),
+        "bf16_dv48": (SMALL.replace(B=1, H=4, L=300, dv=48), 64, None),
+    }[case]
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say(f"layer decay {case} B{cfg.B} H{cfg.H} L{cfg.L} dv{cfg.dv} {cfg.dtype} window{window}")
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    y_lin, y_swa = based.layer_decay_fwd(qd, kd, vd, gd, window)
+    y_sep = based.linattn_decay_fwd(qd, kd, vd, gd)
+    torch.cuda.synchronize()
+    gap = rowinf_rel(y_lin, y_sep.double().cpu().numpy())
+    report(f"layer decay {case}: y_lin vs based_linattn_decay_fwd", gap, 1e-6)
+    assert gap <= 1e-6
+    tol = TOL[q.dtype]
+    sel = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if heads is None else heads
+    for b, h in sel:
+        ref = O.linattn_decay_quadratic(q[b, h][None], k[b, h][None], v[b, h][None], g[h:h + 1].numpy())[0][0]
+        assert rowinf_rel(y_lin[b, h], ref) <= tol, (b, h)
+        assert rowinf_rel(y_swa[b, h], O.swa(q[b, h], k[b, h], v[b, h], window)) <= tol, (b, h)
+    report(f"layer decay {case} (oracle, sampled heads)", 0.0, tol)
+
+
+# ---------------------------------------------------------- decayed backward
+FLOOR = {torch.bfloat16: 0.02, torch.float32: 0.1}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L,dv", [(1, 64), (2, 64), (65, 64), (300, 64), (130, 48), (200, 128)])
+def test_decay_bwd(based, dtype, L, dv):
+    """based_linattn_decay_bwd against the oracle's decayed gradients, per
+    row with a floor (as the plain backward's tests), decays 1, 0.75, ...
+    over eight heads; rows that vanish identically (dq of position 0; dq and
+    dk at L = 1) are checked as noise against the head's largest dv."""
+    from parity_util import row_rel_floor
+    cfg = SMALL.replace(B=1, L=L, dv=dv, dtype=dtype, name=f"decay bwd L{L} dv{dv} {dtype}")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say(cfg.name)
+    qd, kd, vd, gd, dyd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), dy.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    grads = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd)
+    torch.cuda.synchronize()
+    refs = O.linattn_decay_bwd(q, k, v, g.numpy(), dy)
+    tol = TOL[q.dtype]
+    dvmax = float(np.abs(refs[2]).max())
+    for name, gr, r in zip(("dq", "dk", "dv"), grads, refs):
+        zero = L if (L == 1 and name != "dv") else (1 if name == "dq" else 0)
+        if zero:
+            noise = float(gr[..., :zero, :].abs().max().cpu()) / dvmax
+            assert noise <= 100 * tol, (name, noise)
+        if zero == L:
+            continue
+        err = row_rel_floor(gr[..., zero:, :], r[..., zero:, :], FLOOR[q.dtype])
+        report(f"{cfg.name} {name}", err, tol)
+        assert err <= tol, (name, err)
+
+
+def test_decay_bwd_360m_sampled_heads(based):
+    """The 360M shape (B 8, H 16, L 2048) through the decayed backward; the
+    oracle on two heads."""
+    from parity_util import row_rel_floor
+    cfg = synth.FWD_CONFIGS["based360m"]
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say("decay bwd 360m")
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    grads = based.linattn_decay_bwd(qd, kd, vd, gd, y, dy.to(DEV))
+    torch.cuda.synchronize()
+    for b, h in ((0, 1), (5, 14)):
+        refs = O.linattn_decay_bwd(q[b, h][None], k[b, h][None], v[b, h][None], g[h:h + 1].numpy(), dy[b, h][None])
+        for name, gr, r in zip(("dq", "dk", "dv"), grads, refs):
+            zero = 1 if name == "dq" else 0
+            err = row_rel_floor(gr[b, h, zero:][None], r[:, zero:], FLOOR[q.dtype])
+            report(f"decay bwd 360m head ({b},{h}) {name}", err, TOL[q.dtype])
+            assert err <= TOL[q.dtype], (name, err)
