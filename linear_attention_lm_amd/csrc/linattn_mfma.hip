@@ -172,6 +172,10 @@ __device__ __forceinline__ float gsum_pow(float lg, int n) {
   const float ln = lg * 0.69314718055994531f;
   return ln == 0.f ? (float)n : expm1f(ln * (float)n) / expm1f(ln);
 }
+// a value that every lane holds alike, moved to a scalar register
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 // fp16 row stride of the row-major v chunk in LDS (8 halves of padding keep
 // the transposing reads of four consecutive rows on distinct banks)
@@ -179,7 +183,7 @@ template <int NT> constexpr int vrow() { return 16 * NT + 8; }
 
 // LDS of the main pass.  With the sliding window (SWA) the row-major k and v
 // keep the previous chunk too (NB = 2 buffers).
-template <int NT, int SWA, int HI = 0>
+template <int NT, int SWA, int HI = 0, int DEC = 0>
 struct Smem {
   static constexpr int DV = 16 * NT;
   static constexpr int NB = SWA ? 2 : 1;
@@ -193,6 +197,13 @@ struct Smem {
   alignas(16) float vpart[NTHR];         // partial column sums of v (decayed variant)
   alignas(16) float zf[NF];              // denominator state (set-up and result)
   alignas(16) float wmax[4];             // per-wavefront largest state magnitude
+  // decayed variant, fixed for the whole pass: the in-chunk weights
+  // gamma^(query - key) of the 16-key tile t tiles before the query's tile,
+  // as lane l of a wavefront holds them (query 16 w + l % 16 against keys
+  // 16 (w - t) + 4 (l / 16) + i; zero for a key after the query), and the
+  // update's key weights gamma^(C - 1 - key) of a whole chunk
+  alignas(16) float dw[DEC ? 4 : 1][DEC ? 64 : 1][4];
+  alignas(16) half_t wkc[DEC ? C : 8];
 };
 
 // Wavefront index as a scalar, so that every branch on it is a uniform
@@ -769,7 +780,7 @@ template <int NT, int SWA, int DEC = 0, int HI = 0>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Params p) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
-  __shared__ Smem<NT, SWA, HI> S;
+  __shared__ Smem<NT, SWA, HI, DEC> S;
 
   // the segments of one (batch, head) share an XCD: the later segments read
   // the same records of the earlier ones, through that XCD's L2
@@ -813,6 +824,23 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
       for (int k2 = 0; k2 < MAX_SUM; ++k2)
         wrec[k2] = k2 < nsrc ? gpow(lg, (float)((seg - 1 - k2) * p.seg_chunks * C)) : 0.f;
+  }
+  // a whole chunk decays the carried state by gnC and adds gsC to its
+  // constant denominator entry
+  float gnC = 1.f, gsC = (float)C;
+  if constexpr (DEC) {
+    gnC = uniform(gpow(lg, (float)C));
+    gsC = uniform(gsum_pow(lg, C));
+    for (int j = tid; j < 4 * 64; j += NTHR) {
+      const int t = j >> 6, l = j & 63, d0 = 16 * t + (l & 15) - 4 * (l >> 4);
+      float4 wv;
+      wv.x = d0 >= 0 ? gpow(lg, (float)d0) : 0.f;
+      wv.y = d0 >= 1 ? gpow(lg, (float)(d0 - 1)) : 0.f;
+      wv.z = d0 >= 2 ? gpow(lg, (float)(d0 - 2)) : 0.f;
+      wv.w = d0 >= 3 ? gpow(lg, (float)(d0 - 3)) : 0.f;
+      *reinterpret_cast<float4*>(&S.dw[t][l][0]) = wv;
+    }
+    for (int j = tid; j < C; j += NTHR) S.wkc[j] = (half_t)gpow(lg, (float)(C - 1 - j));
   }
   f32x4 tacc[Own<NT>::PPW];
   float z0 = 0.f;
@@ -980,12 +1008,16 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(xc[m][i], __builtin_fmaf(xc[m][i], 0.5f, 1.f), 1.f);
-          if constexpr (DEC)  // gamma^(query - key)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] *= gpow(lg, (float)max(16 * (w - m) + r16 - 4 * g - i, 0));
-          if (m == w)  // key after query
+          if constexpr (DEC) {  // gamma^(query - key), zero for a key after the query
+            const float4 dv4 = *reinterpret_cast<const float4*>(&S.dw[w - m][lane][0]);
+            a[0] *= dv4.x;
+            a[1] *= dv4.y;
+            a[2] *= dv4.z;
+            a[3] *= dv4.w;
+          } else if (m == w) {  // key after query
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] *= dkeep[i];
+          }
           uint32_t h0, l0, h1, l1;
           split2(a[0], a[1], h0, l0);
           split2(a[2], a[3], h1, l1);
@@ -1160,21 +1192,30 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     // ---- state update with this chunk (registers only)
     float gn = 1.f;  // decay of the carried state over this chunk
     if constexpr (DEC) {
-      gn = gpow(lg, (float)n);
+      f16x8 wk[2];  // weight gamma^(n-1-key) of this lane's keys 32 ks + 8 g + i
+      float gs;
+      if (n == C) {  // uniform branch: a whole chunk takes the pass's tables
+        gn = gnC;
+        gs = gsC;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) wk[ks] = *reinterpret_cast<const f16x8*>(&S.wkc[32 * ks + 8 * g]);
+      } else {
+        gn = gpow(lg, (float)n);
+        gs = gsum_pow(lg, n);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = 32 * ks + 8 * g + i;
+            wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+          }
+      }
 #pragma unroll
       for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
 #pragma unroll
       for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
-      f16x8 wk[2];  // weight gamma^(n-1-key) of this lane's keys 32 ks + 8 g + i
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = 32 * ks + 8 * g + i;
-          wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
-        }
       update_chunk<NT, 1>(S.kt, &S.vh[cur][0][0], tacc, tz, ia, ib, wk);
-      z0 = gn * z0 + gsum_pow(lg, n);
+      z0 = gn * z0 + gs;
     } else {
       // wavefront 0 (the one the causal in-chunk term leaves lightest) adds
       // the column sums of v (rows past n of a ragged chunk are zero)
@@ -1229,6 +1270,7 @@ struct StateSmem {
   alignas(16) half_t vh[SG][C][vrow<NT>()];
   alignas(16) float t0[DV];
   alignas(16) float zf[NF];
+  alignas(16) half_t wkc[C];  // decayed variant: key weights gamma^(C - 1 - key)
 };
 
 template <int NT, int DEC = 0>
@@ -1275,6 +1317,14 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
   for (int nn = 0; nn < NT; ++nn) vacc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float lg = DEC ? decay_lg2(p, bh) : 0.f;
   const int lane = tid & 63, g = lane >> 4, w = wave_index(), r16 = lane & 15;
+  // a whole chunk decays the carried sums by gnC and adds gsC to the
+  // constant denominator entry
+  float gnC = 1.f, gsC = (float)C;
+  if constexpr (DEC) {
+    gnC = uniform(gpow(lg, (float)C));
+    gsC = uniform(gsum_pow(lg, C));
+    for (int j = tid; j < C; j += NTHR) S.wkc[j] = (half_t)gpow(lg, (float)(C - 1 - j));
+  }
   for (int t = tok_begin; t < tok_end; t += G * C) {
     __syncthreads();  // the previous group's reads of LDS done
 #pragma unroll
@@ -1290,22 +1340,31 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
         // the carried sums decay over the chunk; keys weigh gamma^(n-1-key);
         // a chunk past the segment (n = 0) leaves everything unchanged
         const int n = min(C, max(0, tok_end - (t + i * C)));
-        const float gn = gpow(lg, (float)n);
-        z0 = gn * z0 + gsum_pow(lg, n);
+        f16x8 wk[2];
+        float gn, gs;
+        if (n == C) {  // uniform branch: a whole chunk takes the pass's tables
+          gn = gnC;
+          gs = gsC;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) wk[ks] = *reinterpret_cast<const f16x8*>(&S.wkc[32 * ks + 8 * g]);
+        } else {
+          gn = gpow(lg, (float)n);
+          gs = gsum_pow(lg, n);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = 32 * ks + 8 * g + e;
+              wk[ks][e] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+            }
+        }
+        z0 = gn * z0 + gs;
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) vacc[nn] *= gn;
 #pragma unroll
         for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] *= gn;
 #pragma unroll
         for (int ms = 0; ms < 3; ++ms) tz[ms] *= gn;
-        f16x8 wk[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = 32 * ks + 8 * g + e;
-            wk[ks][e] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
-          }
         update_chunk<NT, 1, 0, 1>(S.kt[i], &S.vh[i][0][0], tacc, tz, ia, ib, wk, vacc, w == 0);
       }
     } else {
