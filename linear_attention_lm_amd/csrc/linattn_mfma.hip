@@ -204,6 +204,7 @@ struct Smem {
   // update's key weights gamma^(C - 1 - key) of a whole chunk
   alignas(16) float dw[DEC ? 4 : 1][DEC ? 64 : 1][4];
   alignas(16) half_t wkc[DEC ? C : 8];
+  alignas(16) float wvc[DEC ? C : 4];  // the same weights in fp32 (column sums of v)
 };
 
 // Wavefront index as a scalar, so that every branch on it is a uniform
@@ -426,15 +427,26 @@ __device__ __forceinline__ void update_chunk(const half_t (*kt)[KT], const half_
 // chunk's v (row-major in LDS), row t weighing gamma^(n-1-t) and rows past n
 // none: column tid % DV, rows part * SPAN .. + SPAN - 1 with part = tid / DV,
 // read four rows at a time with the transposing load (a 16-lane block covers
-// 16 consecutive columns of one part).  (Elsewhere the update forms the
+// 16 consecutive columns of one part).  A whole chunk takes its weights from
+// the pass's table wvc[t] = gamma^(C-1-t).  (Elsewhere the update forms the
 // column sums with the matrix cores.)
 template <int NT>
-__device__ __forceinline__ float vsum_part_decayed(const half_t* vh, int n, float lg) {
+__device__ __forceinline__ float vsum_part_decayed(const half_t* vh, int n, float lg, const float* wvc) {
   constexpr int DV = 16 * NT;
   constexpr int PARTS = NTHR / DV >= 1 ? NTHR / DV : 1, SPAN = C / PARTS;
   const int tid = threadIdx.x, col = tid % DV, part = tid / DV;
   float vs = 0.f;
-  if (part < PARTS) {  // whole wavefronts (DV divides 64 or is a multiple of 32)
+  if (part < PARTS && n == C) {
+#pragma unroll
+    for (int j = 0; j < SPAN; j += 4) {
+      const f16x4 x = __builtin_bit_cast(f16x4, tr4(vh, part * SPAN + j, col & ~15, vrow<NT>()));
+      const float4 wv = *reinterpret_cast<const float4*>(&wvc[part * SPAN + j]);
+      vs = __builtin_fmaf((float)x[0], wv.x, vs);
+      vs = __builtin_fmaf((float)x[1], wv.y, vs);
+      vs = __builtin_fmaf((float)x[2], wv.z, vs);
+      vs = __builtin_fmaf((float)x[3], wv.w, vs);
+    }
+  } else if (part < PARTS) {  // whole wavefronts (DV divides 64 or is a multiple of 32)
     // the weight of row t, advanced row by row by a factor 1/gamma from the
     // thread's first row (rows past n are masked, whatever their weight)
     const float ginv = __builtin_amdgcn_exp2f(-lg);
@@ -840,7 +852,10 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
       wv.w = d0 >= 3 ? gpow(lg, (float)(d0 - 3)) : 0.f;
       *reinterpret_cast<float4*>(&S.dw[t][l][0]) = wv;
     }
-    for (int j = tid; j < C; j += NTHR) S.wkc[j] = (half_t)gpow(lg, (float)(C - 1 - j));
+    for (int j = tid; j < C; j += NTHR) {
+      S.wvc[j] = gpow(lg, (float)(C - 1 - j));
+      S.wkc[j] = (half_t)S.wvc[j];
+    }
   }
   f32x4 tacc[Own<NT>::PPW];
   float z0 = 0.f;
@@ -904,7 +919,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
     // ---- constant row of the state: column sums of v over the chunk (the
     // decayed variant here, in PARTS partial sums per column; otherwise
     // wavefront 0 forms them in the update below)
-    if constexpr (DEC) S.vpart[tid] = vsum_part_decayed<NT>(&S.vh[cur][0][0], n, lg);
+    if constexpr (DEC) S.vpart[tid] = vsum_part_decayed<NT>(&S.vh[cur][0][0], n, lg, S.wvc);
 
     // ---- readout of the state before the chunk, transposed (value columns x
     // positions): acc[nn][i] is column 16nn + 4g + i of position `pos`; every
