@@ -552,12 +552,14 @@ def summarize_pmc(fetch_dir, write_dir, calls, command, out_dir=None):
     write_all = per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
     everything = by_kernel(fetch_all, 0, 1 << 60)
     copy_names = [k for k in everything if "copy" in k.lower() or "elementwise" in k.lower()]
-    big = [k for k in copy_names if max(everything[k]) > 0.5 * COPY_BYTES]
+    big = [k for k in copy_names if max(everything[k]) > 0.25 * COPY_BYTES]
     if not big:
         raise SystemExit("no copy calibration kernel found in the FETCH_SIZE run")
     cname = big[0]
-    cw = by_kernel(write_all, 0, 1 << 60)[cname]
-    f_copy = sorted(everything[cname])[len(everything[cname]) // 2]
+    # the calibration copies only (the same kernel also serves small copies)
+    cf = [x for x in everything[cname] if x > 0.25 * COPY_BYTES]
+    cw = [x for x in by_kernel(write_all, 0, 1 << 60)[cname] if x > 0.25 * COPY_BYTES]
+    f_copy = sorted(cf)[len(cf) // 2]
     w_copy = sorted(cw)[len(cw) // 2]
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     # the step workload runs first; its last dispatch is the calls-th launch of the fused main pass
@@ -718,9 +720,9 @@ def summarize_stats(stats_dir, command, calls, out_dir=None):
         blk = r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"]
         t = int(r["Start_Timestamp"])
         phase = ""
-        if "based" in name and t <= step_end:
+        if t <= step_end and any(fr in name for fr in OP_KERNELS["layer"]):
             phase = "step"
-        elif "based" in name and t <= bwd_end:
+        elif step_end < t <= bwd_end and any(fr in name for fr in OP_KERNELS["bwd"]):
             phase = "bwd"
         groups.setdefault((name, grid, blk, phase), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -762,7 +764,7 @@ def main():
                          "per pass of COUNTER_PASSES, in that order")
     ap.add_argument("--counters-out", default="counters_layer.md")
     ap.add_argument("--counter-kernels", default="based::",
-                    help="comma-separated kernel-name fragments to summarise")
+                    help="semicolon-separated kernel-name fragments to summarise")
     ap.add_argument("--print-counter-pass", type=int, metavar="I",
                     help="print the counters of pass I (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
@@ -770,7 +772,7 @@ def main():
         print(" ".join(COUNTER_PASSES[args.print_counter_pass]))
         return
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.pmc_command, args.counter_kernels.split(","),
+        summarize_counters(args.summarize_counters, args.pmc_command, args.counter_kernels.split(";"),
                            args.counters_out)
         return
     if args.summarize_stats:
