@@ -35,6 +35,8 @@
 // Operands are fp16 (bf16 inputs convert exactly); g, h and the in-chunk
 // weights are split into fp16 hi + lo; the state copies read by the matrix
 // cores are fp16 scaled by a power of two; all sums are fp32.
+#include <type_traits>
+
 #include "based_device.h"
 #include "launchers.h"
 
@@ -426,20 +428,27 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
     const float down = __builtin_amdgcn_ldexpf(1.f, -e);
     up = __builtin_amdgcn_ldexpf(1.f, e);
+    // (two copies of the store loop behind one uniform branch: no scaling
+    // while e = 0, the usual case)
+    auto store_copy = [&](auto scaled) {
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 0)) {
-        const int mt = own_tile(w, j);
+      for (int j = 0; j < MAXOWN; ++j) {
+        if (j < own_count(w, 0)) {
+          const int mt = own_tile(w, j);
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const f32x4 a = acc[j][nn] * down;
-          const uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
-          const uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
-          *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
+          for (int nn = 0; nn < 2; ++nn) {
+            f32x4 a = acc[j][nn];
+            if constexpr (decltype(scaled)::value) a *= down;
+            const uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
+            const uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
+            *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
+          }
+          if (g == 0) S.zs[16 * mt + r16] = zacc[j];
         }
-        if (g == 0) S.zs[16 * mt + r16] = zacc[j];
       }
-    }
+    };
+    if (__builtin_amdgcn_readfirstlane(e) != 0) store_copy(std::true_type{});
+    else store_copy(std::false_type{});
   };
   // the state before the segment: the sum of the forward records of the
   // earlier segments (slot values sum_t [k_a | k_a^2 | k_a k_b] v_t)
@@ -582,6 +591,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 
     // ---- dq from the state: u^T = S^T-readout (features x this position),
     // lane-local contraction into dq[4g + i]; plus the z h share, h zg
+    // (the copy's scale 2^e rides on the q factors: exact, a power of two)
     f32x4 dqa = zg * hval;
     const f16x8 gbh = ld8(&S.gh[pos][8 * g]), gbl = ld8(&S.gl[pos][8 * g]);
 #pragma unroll
@@ -589,9 +599,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       const f16x8 sa = ld8(&S.st[16 * m + r16][8 * g]);
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(sa, gbh, u);  // g rounded once: the state copy is fp16 as well
-      u *= up;
-      if (m == 0) dqa += u;
-      else dqa += u * qf[m - 1];
+      dqa += u * (m == 0 ? up : qf[m - 1] * up);
     }
 
     // ---- in-chunk term: dK^T = V G^T (+ h), c = dK (1 + x) below the
@@ -844,20 +852,25 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     const int e = scale_exp(fmaxf(fmaxf(S.wmax[0], S.wmax[1]), fmaxf(S.wmax[2], S.wmax[3])));
     const float down = __builtin_amdgcn_ldexpf(1.f, -e);
     up = __builtin_amdgcn_ldexpf(1.f, e);
+    auto store_copy = [&](auto scaled) {  // as in the query pass
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 3)) {
-        const int mt = own_tile(w, j);
+      for (int j = 0; j < MAXOWN; ++j) {
+        if (j < own_count(w, 3)) {
+          const int mt = own_tile(w, j);
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const f32x4 a = acc[j][nn] * down;
-          const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
-          const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
-          *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+          for (int nn = 0; nn < 2; ++nn) {
+            f32x4 a = acc[j][nn];
+            if constexpr (decltype(scaled)::value) a *= down;
+            const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
+            const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
+            *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+          }
+          if (g == 0) S.rs[16 * mt + r16] = racc[j];
         }
-        if (g == 0) S.rs[16 * mt + r16] = racc[j];
       }
-    }
+    };
+    if (__builtin_amdgcn_readfirstlane(e) != 0) store_copy(std::true_type{});
+    else store_copy(std::false_type{});
   };
   // the state after the segment: the sum of the increments of the later segments
   if (un.seg < p.nseg - 1) {
@@ -905,15 +918,14 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     }
     // ---- dk from the state: u^T = R-readout with v_j, lane-local contraction
     // (the r share is added before the store)
+    // (the copy's scale 2^e rides on the k factors: exact, a power of two)
     f32x4 dka = {0.f, 0.f, 0.f, 0.f};
     const f16x8 vb = ld8(&S.vh[kpos][8 * g]);
 #pragma unroll
     for (int m = 0; m < NFT; ++m) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(ld8(&S.rf[16 * m + r16][8 * g]), vb, u);
-      u *= up;
-      if (m == 0) dka += u;
-      else dka += u * kf[m - 1];
+      dka += u * (m == 0 ? up : kf[m - 1] * up);
     }
     // ---- dv from the state: R^T phi~(k_j) with phi~ = [k_a, k_a k_b / 2], plus sum g
     f32x4 dva[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
