@@ -145,7 +145,9 @@ int based_linattn_fwd(const void* q, const void* k, const void* v, float* y,
  * phi(k_i), y_i = phi(q_i)^T S_i / phi(q_i)^T z_i -- the kernel weight of key j
  * in row i becomes K_ij gamma_h^(i-j); gamma_h = 1 is based_linattn_fwd.
  *
- *   gamma  [H] fp32, device memory, 0 < gamma_h <= 1 (not checked)
+ *   gamma  [H] fp32, device memory; each gamma_h is taken clamped to [0, 1]
+ *          (NaN reads as 0).  gamma_h = 0 keeps each position's own term
+ *          only (gamma^0 = 1; powers d >= 1 of 0 are flushed below 2^-126)
  *   every other argument as for based_linattn_fwd (same workspace size; S_in
  *   decays like the rest: position i sees gamma^(i+1) S_in).
  * BASED_BF16 with d_v in {32, 64, 96, 128} runs on the matrix cores,
@@ -210,7 +212,8 @@ int based_linattn_bwd(const void* q, const void* k, const void* v, const float* 
  * den_i, dq_i, dk_j and dv_j; the train README's decay strategy, read as for
  * the forward).
  *
- *   gamma      [H] fp32, device memory, 0 < gamma_h <= 1 (not checked)
+ *   gamma      [H] fp32, device memory, clamped to [0, 1] as in
+ *              based_linattn_decay_fwd
  *   q, k, v, y, dy, dq, dk, dv: as for based_linattn_bwd (y from
  *              based_linattn_decay_fwd with the same gamma)
  *   workspace: at least 2 * B * H * L * 4 bytes of device memory (never more
@@ -287,8 +290,8 @@ int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, f
 
 /*
  * based_layer_fwd with the linear attention's state decayed per head, as in
- * based_linattn_decay_fwd (gamma [H] fp32 device memory, 0 < gamma_h <= 1,
- * not checked; y_lin is based_linattn_decay_fwd's y); the window attention
+ * based_linattn_decay_fwd (gamma [H] fp32 device memory, clamped to [0, 1];
+ * y_lin is based_linattn_decay_fwd's y); the window attention
  * (y_swa) has no decay.  Every other argument, and the workspace size, as for
  * based_layer_fwd; BASED_ERR_NULL for a null gamma, BASED_ERR_ALIAS when
  * gamma overlaps an output.  BASED_BF16 with d_v in {32, 64, 96, 128} is one
@@ -369,8 +372,8 @@ int based_decode_step(const void* q, const void* k, const void* v,
  * based_linattn_decay_fwd):
  *   S <- gamma[h] S + phi(k) v^T;  z <- gamma[h] z + phi(k);
  *   y_lin = phi(q)^T S / phi(q)^T z
- * gamma: [H] fp32 device pointer, 0 < gamma <= 1 (not checked), read only,
- * shared by the batch; it must not overlap any output.  The window attention
+ * gamma: [H] fp32 device pointer, each entry taken clamped to [0, 1] (NaN as
+ * 0), read only, shared by the batch; it must not overlap any output.  The window attention
  * and the ring are as in based_decode_step.  A state prefilled by
  * based_linattn_decay_fwd's S_out / z_out over the context continues the
  * decayed forward exactly.  Both dtypes, d_v in {16..128}.  Errors as

@@ -166,7 +166,7 @@ def linattn_fwd(q, k, v, S_in=None, z_in=None, *, return_state=False, y=None, S_
 def linattn_decay_fwd(q, k, v, gamma, S_in=None, z_in=None, *, return_state=False, y=None, S_out=None,
                       z_out=None, workspace=None):
     """Causal Taylor linear attention with a per-head state decay gamma [H]
-    (fp32, 0 < gamma <= 1): S_i = gamma S_{i-1} + phi(k_i) v_i^T, likewise z.
+    (fp32, taken clamped to [0, 1]): S_i = gamma S_{i-1} + phi(k_i) v_i^T, likewise z.
     Either dtype, d_v in {16, ..., 128}.  Returns y, or (y, S, z)."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]

@@ -61,6 +61,13 @@ constexpr int DPHI = 273;
 constexpr int NQUAD = DK * (DK + 1) / 2;  // 136
 constexpr int NCOMPACT = 1 + DK + NQUAD;  // 153
 
+// State decay factors.  A head's gamma is taken clamped to [0, 1] (NaN as
+// 0).  decay_lg2_clamped(log2 gamma) keeps the logarithm in [-126, 0], so
+// that gamma^d = exp2(d lg) is exactly 1 at d = 0 for every gamma (0^0 = 1),
+// at most 2^-126 for gamma = 0 and d >= 1, and never above 1.
+__device__ __forceinline__ float decay_lg2_clamped(float lg) { return fminf(fmaxf(lg, -126.f), 0.f); }
+__device__ __forceinline__ float decay_clamped(float gamma) { return fminf(fmaxf(gamma, 0.f), 1.f); }
+
 // Index of the unordered pair (a <= b) in the row-major upper triangle.
 __host__ __device__ constexpr int pair_index(int a, int b) { return a * DK - a * (a - 1) / 2 + (b - a); }
 

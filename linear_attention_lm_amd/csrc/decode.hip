@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_step_kernel(
 
   for (int h = wave; h < H; h += nw) {
     const size_t bh = (size_t)b * H + h;
-    const float gm = gamma ? gamma[h] : 1.f;  // state decay of the head (gm * x = x exactly when 1)
+    const float gm = gamma ? decay_clamped(gamma[h]) : 1.f;  // state decay of the head (gm * x = x exactly when 1)
     const auto rS = rsrc(S + bh * NROW * DV, NROW * DV * 4);
     const auto rZ = rsrc(z + bh * NROW, NROW * 4);
     const auto rK = rsrc(ring_k + bh * (size_t)window * DK, window * DK * ES);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, 
   const int t = threadIdx.x;
   const size_t bh = blockIdx.x / nblk;
   const int i0 = (blockIdx.x % nblk) * TB, i = i0 + t;
-  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;  // decay weight of (i, j): 2^(lg (i - j))
+  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;  // decay weight of (i, j): 2^(lg (i - j))
   const T* kh = k + bh * L * DK;
   const T* vh = v + bh * (size_t)L * DV;
   float qi[DK];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, co
   const int t = threadIdx.x;
   const size_t bh = blockIdx.x / nblk;
   const int j0 = (blockIdx.x % nblk) * TB, j = j0 + t;
-  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;
+  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
   const T* qh = q + bh * L * DK;
   float kj[DK];
   if (j < L) {

@@ -165,7 +165,9 @@ struct Params {
 };
 
 // Decayed variant: log2 of the head's decay factor, and gamma^d from it.
-__device__ __forceinline__ float decay_lg2(const Params& p, size_t bh) { return __log2f(p.gamma[bh % p.H]); }
+__device__ __forceinline__ float decay_lg2(const Params& p, size_t bh) {
+  return decay_lg2_clamped(__log2f(p.gamma[bh % p.H]));
+}
 __device__ __forceinline__ float gpow(float lg, float d) { return __builtin_amdgcn_exp2f(lg * d); }
 // sum_{d < n} gamma^d, through expm1 so that gamma near 1 keeps its precision
 __device__ __forceinline__ float gsum_pow(float lg, int n) {
@@ -447,18 +449,15 @@ __device__ __forceinline__ float vsum_part_decayed(const half_t* vh, int n, floa
       vs = __builtin_fmaf((float)x[3], wv.w, vs);
     }
   } else if (part < PARTS) {  // whole wavefronts (DV divides 64 or is a multiple of 32)
-    // the weight of row t, advanced row by row by a factor 1/gamma from the
-    // thread's first row (rows past n are masked, whatever their weight)
-    const float ginv = __builtin_amdgcn_exp2f(-lg);
-    float wt = gpow(lg, (float)(n - 1 - part * SPAN));
+    // a ragged chunk: the weight of row t from its own power (rows past n
+    // are masked, whatever their weight)
 #pragma unroll
     for (int j = 0; j < SPAN; j += 4) {
       const f16x4 x = __builtin_bit_cast(f16x4, tr4(vh, part * SPAN + j, col & ~15, vrow<NT>()));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = part * SPAN + j + e;
-        vs = __builtin_fmaf((float)x[e], t < n ? wt : 0.f, vs);
-        wt *= ginv;
+        vs = __builtin_fmaf((float)x[e], t < n ? gpow(lg, (float)(n - 1 - t)) : 0.f, vs);
       }
     }
   }
@@ -1441,7 +1440,8 @@ __global__ void seg_scan_kernel(float* ws, float* wsz, int nseg, int rec, int BH
   // group are in flight together
   float run = base[stride];
   // decayed variant: the running state decays over each segment it crosses
-  const float gseg = gamma ? __builtin_amdgcn_exp2f(__log2f(gamma[bh % H]) * (float)seg_len) : 1.f;
+  const float gseg =
+      gamma ? __builtin_amdgcn_exp2f(decay_lg2_clamped(__log2f(gamma[bh % H])) * (float)seg_len) : 1.f;
   for (int s0 = 2; s0 < nseg; s0 += 8) {
     float x[8];
 #pragma unroll

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
   __shared__ float wk[C];  // decayed variant: weight gamma^(n-1-j) of the chunk's key j in the update
 
   const int bh = blockIdx.x;
-  const float lg = DEC ? log2f(gamma[bh % H]) : 0.f;
+  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
   const int tid = threadIdx.x;
   const T* qb = q + (size_t)bh * L * DK;
   const T* kb = k + (size_t)bh * L * DK;

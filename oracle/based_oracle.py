@@ -43,7 +43,7 @@ Readings where the pages are silent (all listed in the design doc as well):
 * the backward is the exact derivative of these forwards with respect to
   q, k and v (no initial state), as the training views imply;
 * decay (the train README points to an optional decay strategy with no
-  formula on the pages): a per-head factor 0 < gamma <= 1 on the state,
+  formula on the pages): a per-head factor 0 <= gamma <= 1 on the state,
   S_i = gamma S_{i-1} + phi(k_i) v_i^T and z likewise, so the kernel weight of
   key j in row i is K_ij gamma^(i-j); gamma = 1 is the layer without decay;
 * BaseConv's convolution is causal and depthwise (one short filter per

@@ -440,6 +440,10 @@ def test_decay_closed_forms():
     np.testing.assert_allclose(y[0], v[0], rtol=1e-14)
     y = O.linattn_decay_quadratic(q[None], k[None], v[None], np.array([1e-30]))[0][0]
     np.testing.assert_allclose(y, v, rtol=1e-12)
+    # gamma = 0 exactly: gamma^0 = 1 keeps each row's own term and nothing else
+    for form in (O.linattn_decay_quadratic, O.linattn_decay_recurrent):
+        y = form(q[None], k[None], v[None], np.array([0.0]))[0][0]
+        np.testing.assert_allclose(y, v, rtol=1e-14)
 
 
 def test_decay_resume_from_state():
@@ -588,3 +592,7 @@ def test_linattn_decay_bwd_shift_and_vanishing_decay():
     dq, dk, dvs = O.linattn_decay_bwd(q[None], k[None], v[None], np.array([1e-12]), dy[None])
     np.testing.assert_allclose(dvs[0], dy, rtol=1e-9, atol=1e-9)
     assert np.abs(dq).max() < 1e-9 and np.abs(dk).max() < 1e-9
+    # gamma = 0 exactly: y = v whatever q and k are
+    dq, dk, dvs = O.linattn_decay_bwd(q[None], k[None], v[None], np.array([0.0]), dy[None])
+    np.testing.assert_allclose(dvs[0], dy, rtol=1e-14, atol=1e-14)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14

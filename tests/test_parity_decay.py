@@ -240,3 +240,70 @@ def test_decay_bwd_360m_sampled_heads(based):
             err = row_rel_floor(gr[b, h, zero:][None], r[:, zero:], FLOOR[q.dtype])
             report(f"decay bwd 360m head ({b},{h}) {name}", err, TOL[q.dtype])
             assert err <= TOL[q.dtype], (name, err)
+
+
+# ------------------------------------------------ the range of gamma
+# Out-of-range decays read as their clamped values: NaN and negatives as 0,
+# values above 1 as 1.  gamma = 0 leaves each position its own term (y = v).
+RAW = [0.0, -0.5, float("nan"), 1.5, 0.75, 0.0, 1.0, 0.5]
+CLAMPED = [0.0, 0.0, 0.0, 1.0, 0.75, 0.0, 1.0, 0.5]
+
+
+@pytest.mark.parametrize("dtype,dv,L", [("bf16", 64, 1000), ("f32", 48, 130)])
+def test_decay_gamma_clamped(based, dtype, dv, L):
+    """The decayed forward (matrix-core pass over several segments with a
+    ragged last chunk; the vector pass in fp32) and the decayed layer: raw
+    and clamped gammas give the same bits; the gamma = 0 heads equal v."""
+    cfg = SMALL.replace(L=L, dv=dv, dtype=dtype, name=f"gamma range {dtype} dv{dv} L{L}")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    say(cfg.name)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    raw, cl = torch.tensor(RAW, device=DEV), torch.tensor(CLAMPED, device=DEV)
+    ya, Sa, za = based.linattn_decay_fwd(qd, kd, vd, raw, return_state=True)
+    yb, Sb, zb = based.linattn_decay_fwd(qd, kd, vd, cl, return_state=True)
+    la = based.layer_decay_fwd(qd, kd, vd, raw, 64)[0]
+    lb = based.layer_decay_fwd(qd, kd, vd, cl, 64)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(Sa, Sb) and torch.equal(za, zb) and torch.equal(la, lb)
+    assert torch.isfinite(ya).all()
+    tol = TOL[q.dtype]
+    for h in (0, 1, 2, 5):
+        err = rowinf_rel(ya[:, h], v[:, h].double().numpy())
+        assert err <= tol, (h, err)
+    for b, h in [(0, 3), (1, 4), (0, 7)]:
+        ref = O.linattn_decay_quadratic(q[b, h][None], k[b, h][None], v[b, h][None], np.array([CLAMPED[h]]))[0][0]
+        assert rowinf_rel(ya[b, h], ref) <= tol, (b, h)
+    report(f"{cfg.name}: raw = clamped bit for bit, gamma 0 heads = v", 0.0, tol)
+
+
+def test_decay_bwd_and_decode_gamma_clamped(based):
+    """The decayed backward and decode step: raw and clamped gammas give the
+    same bits; at gamma = 0 dv = dy and dq, dk vanish (y = v)."""
+    cfg = SMALL.replace(B=1, L=200, name="gamma range bwd")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    say(cfg.name)
+    qd, kd, vd, dyd = q.to(DEV), k.to(DEV), v.to(DEV), dy.to(DEV)
+    raw, cl = torch.tensor(RAW, device=DEV), torch.tensor(CLAMPED, device=DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, cl)
+    ga = based.linattn_decay_bwd(qd, kd, vd, raw, y, dyd)
+    gb = based.linattn_decay_bwd(qd, kd, vd, cl, y, dyd)
+    torch.cuda.synchronize()
+    for a, b in zip(ga, gb):
+        assert torch.equal(a, b)
+    tol = TOL[q.dtype]
+    dvmax = float(dy.abs().max())
+    for h in (0, 1, 2, 5):
+        assert rowinf_rel(ga[2][:, h], dy[:, h].double().numpy()) <= tol, h
+        assert float(ga[0][:, h].abs().max().cpu()) <= tol * dvmax and float(ga[1][:, h].abs().max().cpu()) <= tol * dvmax
+    dcfg = synth.DecodeConfig("gamma range decode", B=2, H=8, ctx=70, steps=4)
+    (qc, kc, vc), (qs, ks, vs) = synth.decode_inputs(dcfg)
+    _, _, sa = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), gamma=cl)
+    _, _, sb = based.decode_init(qc.to(DEV), kc.to(DEV), vc.to(DEV), gamma=cl)
+    for s in range(dcfg.steps):
+        ya = based.decode_step(sa, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV), gamma=raw)
+        yb = based.decode_step(sb, qs[s].to(DEV), ks[s].to(DEV), vs[s].to(DEV), gamma=cl)
+        assert torch.equal(ya[0], yb[0]) and torch.equal(ya[1], yb[1])
+        assert rowinf_rel(ya[0][:, 0], vs[s][:, 0].double().numpy()) <= tol
+    assert torch.equal(sa.S, sb.S) and torch.equal(sa.z, sb.z)
+    report("gamma range: backward and decode, raw = clamped bit for bit", 0.0, tol)
