@@ -724,7 +724,7 @@ struct KIncSmem {
   alignas(16) half_t qt[DK][XT];
   alignas(16) half_t gh[C][RS];  // g rows (slice), fp16
   alignas(16) half_t hh[XT];     // h, fp16
-  float gcol[SW];
+  alignas(16) float gsum[C][SW];  // per-thread column sums of g (row tid / 4), summed in row order
 };
 
 __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
@@ -753,7 +753,6 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
     acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (tid < SW) S.gcol[tid] = 0.f;
   const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h + (size_t)s * p.npos);
   Pre pf;
   k_load(p, rs, s, un.t_begin, pf);
@@ -808,10 +807,16 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       if (g == 0) rec[(size_t)NF * SW + f] = racc[j][0];
     }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) atomicAdd(&S.gcol[8 * (tid & 3) + i], gpart[i]);
+  // sum g over the segment: the threads' shares added in row order (a fixed
+  // order, so that repeated runs give the same bits)
+  *reinterpret_cast<float4*>(&S.gsum[tid >> 2][8 * (tid & 3)]) = make_float4(gpart[0], gpart[1], gpart[2], gpart[3]);
+  *reinterpret_cast<float4*>(&S.gsum[tid >> 2][8 * (tid & 3) + 4]) = make_float4(gpart[4], gpart[5], gpart[6], gpart[7]);
   __syncthreads();
-  if (tid < SW) rec[(size_t)NF * SW + NF + tid] = S.gcol[tid];
+  if (tid < SW) {
+    float gs = 0.f;
+    for (int r = 0; r < C; ++r) gs += S.gsum[r][tid];
+    rec[(size_t)NF * SW + NF + tid] = gs;
+  }
 }
 
 __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {

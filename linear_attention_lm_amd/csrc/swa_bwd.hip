@@ -17,8 +17,9 @@
 // 64 x 64 tiles P and dS in LDS (4 x 4 register tiles per thread), then
 // dv_c += P^T dY, dk_c += dS^T Q and the chunk's share of dq.  dk and dv of
 // chunk c are written once; dq of a query gets exactly two shares (its own
-// chunk's keys and the previous chunk's), added atomically onto a zeroed dq,
-// so the sum does not depend on their order.
+// chunk's keys and the previous chunk's), added atomically onto a zeroed dq:
+// 0 + a + b and 0 + b + a round to the same value (two addends onto an exact
+// zero), so the result has the same bits whichever share lands first.
 #include "based_device.h"
 #include "launchers.h"
 

@@ -148,3 +148,26 @@ def test_bwd_empty(based):
     for fn in (based.linattn_bwd, based.swa_bwd):
         dq, dk, dv = fn(q, q, v, y, y)
         assert dq.shape == (1, 2, 0, 16) and dv.shape == (1, 2, 0, 64)
+
+
+@pytest.mark.parametrize("which", ["lin", "swa"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_deterministic(based, which, dtype):
+    """Repeated calls give the same bits.  The fp32 window backward adds each
+    query's two dq shares (its own chunk's keys, the previous chunk's) onto a
+    zeroed dq with atomics: two addends onto an exact zero sum to the same
+    value in either order."""
+    cfg = SMALL.replace(B=2, H=4, L=1000, dtype=dtype)
+    q, k, v = (t.to(DEV) for t in synth.fwd_inputs(cfg, 0))
+    dy = synth.upstream_grad(cfg, 0).to(DEV)
+    say(f"{which} bwd determinism {dtype}")
+    if which == "lin":
+        y = based.linattn_fwd(q, k, v)
+        runs = [based.linattn_bwd(q, k, v, y, dy) for _ in range(5)]
+    else:
+        y = based.swa_fwd(q, k, v, 64)
+        runs = [based.swa_bwd(q, k, v, y, dy, 64) for _ in range(5)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
