@@ -18,8 +18,9 @@
 namespace based {
 namespace {
 
-constexpr int C = 64;    // positions per chunk
+constexpr int C = 32;    // positions per chunk
 constexpr int NT = 256;  // threads per workgroup
+constexpr int NFP = 160; // compact feature rows, padded (NCOMPACT used)
 
 struct PairTables {
   uint8_t a[NQUAD], b[NQUAD];
@@ -50,141 +51,241 @@ __device__ float phi_from_compact(const float* T, int f, int c, int ld) {
   return T[(1 + DK + pair_index(lo, hi)) * ld + c] * INV_SQRT2;
 }
 
+// Work split of a chunk among the 256 threads: value columns in NCB blocks
+// of CPT, and the other axis (the chunk's rows for the readout and the
+// in-chunk term, the state's feature rows for the update) in NRB blocks.
+template <int DV>
+struct Split {
+  static constexpr int NCB = DV >= 64 ? 16 : 8;  // column blocks
+  static constexpr int CPT = DV / NCB;           // columns per thread
+  static constexpr int NRB = NT / NCB;           // row / feature blocks
+  static constexpr int RPT = C / NRB;            // chunk rows per thread (readout)
+  static constexpr int FPT = NFP / NRB;          // feature rows per thread (update)
+  static_assert(DV % NCB == 0 && C % NRB == 0 && NFP % NRB == 0, "tiling");
+};
+
+// Compact feature f (< NFP) as c0 + x_a (c1 + c2 x_b): the constant
+// feature 1, the linear ones x_a, the pairs x_a x_b (a <= b) -- with weight
+// 1/2 on the diagonal for a query (QUERY), 1 for a key -- and zero past
+// NCOMPACT.  A thread fills the same two features of every chunk, so it
+// works out their coefficients once.
+struct FeatureCoef {
+  float c0, c1, c2;
+  int a, b;
+};
+template <bool QUERY>
+__device__ __forceinline__ FeatureCoef feature_coef(int f) {
+  FeatureCoef r{0.f, 0.f, 0.f, 0, 0};
+  if (f == 0) {
+    r.c0 = 1.f;
+  } else if (f < 1 + DK) {
+    r.c1 = 1.f;
+    r.a = f - 1;
+  } else if (f < NCOMPACT) {
+    const int pi = f - 1 - DK;
+    r.a = c_pairs.a[pi];
+    r.b = c_pairs.b[pi];
+    r.c2 = QUERY && r.a == r.b ? 0.5f : 1.f;
+  }
+  return r;
+}
+__device__ __forceinline__ float feature(const FeatureCoef& fc, const float* x) {
+  return fc.c0 + x[fc.a] * __builtin_fmaf(fc.c2, x[fc.b], fc.c1);
+}
+
 // DEC: the decayed variant (the based/train README's optional decay
-// strategy, read as a per-head factor 0 < gamma <= 1 on the state:
+// strategy, read as a per-head factor gamma in [0, 1] on the state:
 // S_i = gamma S_{i-1} + phi(k_i) v_i^T, z likewise).  The state entering a
 // chunk reaches its position i (0-based in the chunk) times gamma^(i+1), an
 // in-chunk key j weighs gamma^(i-j), and the update is S <- gamma^n S +
 // sum_j gamma^(n-1-j) phi(k_j) v_j^T over the chunk's n positions.
+//
+// Per chunk of C positions, with the features staged in LDS (fp32):
+//   1. phi(q_i) of the chunk's queries (feature-major), and the in-chunk
+//      weights W_ij = 1 + x + x^2/2 (x = q_i.k_j, j <= i < n; zero otherwise);
+//   2. each thread's RPT rows x CPT columns of phi(Q) T and of W V, and the
+//      rows' denominators, then y;
+//   3. psi(k_j) of the chunk's keys (row-major; zero past n), and the
+//      update T += psi(K)^T V, z += psi(K)^T 1, each thread FPT feature rows
+//      x CPT columns.
 template <typename T, int DV, int DEC>
 __global__ __launch_bounds__(NT) void linattn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ y,
     const float* S_in, const float* z_in, float* S_out, float* z_out, int L, const float* gamma, int H) {
-  constexpr int CPT = DV / 4;  // readout columns per thread
-  __shared__ float Ts[NCOMPACT][DV];
-  __shared__ float zs[NCOMPACT];
-  __shared__ float qs[C][DK];
-  __shared__ float ks[C][DK];
+  using SP = Split<DV>;
+  constexpr int CPT = SP::CPT, RPT = SP::RPT, FPT = SP::FPT;
+  constexpr int FT = C + 4;    // row stride of the feature-major query features
+  constexpr int FK = NFP + 4;  // row stride of the row-major key features
+  static_assert(NFP * FT >= C * FK, "the key features reuse the query features' buffer");
+  __shared__ float Ts[NFP][DV];  // compact state (rows NCOMPACT.. zero)
+  __shared__ float zs[NFP];
+  __shared__ float fbuf[NFP * FT];  // phi(q) [NFP][FT], then psi(k) [C][FK]
+  __shared__ float qs[C][DK + 1];  // (odd stride: rows read down a column)
+  __shared__ float ks[C][DK + 1];
   __shared__ float vs[C][DV];
-  __shared__ float wk[C];  // decayed variant: weight gamma^(n-1-j) of the chunk's key j in the update
+  __shared__ float wt[C][C + 1];  // in-chunk weights, [key][query]
 
   const int bh = blockIdx.x;
   const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
   const int tid = threadIdx.x;
+  const int cb = tid % SP::NCB, ob = tid / SP::NCB;  // column block; row / feature block
+  const int c0 = cb * CPT, r0 = ob * RPT, f0 = ob * FPT;
   const T* qb = q + (size_t)bh * L * DK;
   const T* kb = k + (size_t)bh * L * DK;
   const T* vb = v + (size_t)bh * L * DV;
   float* yb = y + (size_t)bh * L * DV;
-
-  for (int e = tid; e < NCOMPACT * DV; e += NT) {
-    const int f = e / DV, c = e % DV;
-    Ts[f][c] = S_in ? compact_from_phi(S_in + (size_t)bh * DPHI * DV, f, c, DV) : 0.f;
+  // feature fills: item u = tid + NT m (m = 0, 1; u < 2 NFP) is feature u / 2
+  // over rows (u % 2) C/2 .. + C/2 - 1 of the chunk
+  constexpr int HC = C / 2;
+  FeatureCoef fq[2], fk[2];
+  int fu[2], fr[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int u = tid + NT * m;
+    fu[m] = u < 2 * NFP ? u / 2 : -1;
+    fr[m] = (u % 2) * HC;
+    fq[m] = feature_coef<true>(fu[m] < 0 ? 0 : fu[m]);
+    fk[m] = feature_coef<false>(fu[m] < 0 ? 0 : fu[m]);
   }
-  for (int f = tid; f < NCOMPACT; f += NT) zs[f] = z_in ? compact_from_phi(z_in + (size_t)bh * DPHI, f, 0, 1) : 0.f;
 
-  for (int c0 = 0; c0 < L; c0 += C) {
-    const int n = min(C, L - c0);
-    __syncthreads();  // previous chunk's update done
+  for (int e = tid; e < NFP * DV; e += NT) {
+    const int f = e / DV, c = e % DV;
+    Ts[f][c] = S_in && f < NCOMPACT ? compact_from_phi(S_in + (size_t)bh * DPHI * DV, f, c, DV) : 0.f;
+  }
+  for (int f = tid; f < NFP; f += NT)
+    zs[f] = z_in && f < NCOMPACT ? compact_from_phi(z_in + (size_t)bh * DPHI, f, 0, 1) : 0.f;
+
+  for (int t0 = 0; t0 < L; t0 += C) {
+    const int n = min(C, L - t0);
+    __syncthreads();  // the previous chunk's update done
     for (int e = tid; e < C * DK; e += NT) {
       const int j = e / DK, d = e % DK;
       const bool ok = j < n;
-      qs[j][d] = ok ? to_f32(qb[(size_t)(c0 + j) * DK + d]) : 0.f;
-      ks[j][d] = ok ? to_f32(kb[(size_t)(c0 + j) * DK + d]) : 0.f;
+      qs[j][d] = ok ? to_f32(qb[(size_t)(t0 + j) * DK + d]) : 0.f;
+      ks[j][d] = ok ? to_f32(kb[(size_t)(t0 + j) * DK + d]) : 0.f;
     }
     for (int e = tid; e < C * DV; e += NT) {
       const int j = e / DV, d = e % DV;
-      vs[j][d] = j < n ? to_f32(vb[(size_t)(c0 + j) * DV + d]) : 0.f;
+      vs[j][d] = j < n ? to_f32(vb[(size_t)(t0 + j) * DV + d]) : 0.f;
     }
-    if (DEC && tid < C) wk[tid] = tid < n ? exp2f(lg * (float)(n - 1 - tid)) : 0.f;
     __syncthreads();
 
-    // ---- readout of the state before the chunk + in-chunk masked term
+    // ---- 1. query features and in-chunk weights
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      if (fu[m] >= 0)
+        for (int i = fr[m]; i < fr[m] + HC; ++i) fbuf[fu[m] * FT + i] = feature(fq[m], qs[i]);
+    for (int e = tid; e < C * C; e += NT) {
+      const int j = e / C, i = e % C;
+      float x = 0.f;
+#pragma unroll
+      for (int d = 0; d < DK; ++d) x = __builtin_fmaf(qs[i][d], ks[j][d], x);
+      float w = j <= i && j < n ? 1.f + x + 0.5f * x * x : 0.f;
+      if (DEC && j <= i) w *= exp2f(lg * (float)(i - j));
+      wt[j][i] = w;
+    }
+    __syncthreads();
+
+    // ---- 2. readout of the state before the chunk, plus the in-chunk term
     {
-      const int i = tid % C, g = tid / C, col0 = g * CPT;
-      if (i < n) {
-        float qr[DK];
+      float num[RPT][CPT], den[RPT];
 #pragma unroll
-        for (int d = 0; d < DK; ++d) qr[d] = qs[i][d];
-        float num[CPT];
+      for (int r = 0; r < RPT; ++r) {
+        den[r] = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) num[c] = Ts[0][col0 + c];
-        float den = zs[0];
+        for (int c = 0; c < CPT; ++c) num[r][c] = 0.f;
+      }
+#pragma unroll 3
+      for (int f = 0; f < NCOMPACT; ++f) {
+        float ph[RPT], st[CPT];
 #pragma unroll
-        for (int a = 0; a < DK; ++a) {
-          den += qr[a] * zs[1 + a];
+        for (int r = 0; r < RPT; ++r) ph[r] = fbuf[f * FT + r0 + r];
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) num[c] += qr[a] * Ts[1 + a][col0 + c];
+        for (int c = 0; c < CPT; ++c) st[c] = Ts[f][c0 + c];
+        const float zf = zs[f];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          den[r] = __builtin_fmaf(ph[r], zf, den[r]);
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) num[r][c] = __builtin_fmaf(ph[r], st[c], num[r][c]);
         }
+      }
+      if (DEC) {  // the state before the chunk, decayed over positions t0 .. t0 + i
 #pragma unroll
-        for (int a = 0; a < DK; ++a) {
+        for (int r = 0; r < RPT; ++r) {
+          const float cf = exp2f(lg * (float)(r0 + r + 1));
+          den[r] *= cf;
 #pragma unroll
-          for (int b = a; b < DK; ++b) {
-            const int f = 1 + DK + pair_index(a, b);
-            const float w = (a == b) ? 0.5f * qr[a] * qr[a] : qr[a] * qr[b];
-            den += w * zs[f];
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) num[c] += w * Ts[f][col0 + c];
-          }
+          for (int c = 0; c < CPT; ++c) num[r][c] *= cf;
         }
-        if (DEC) {  // the state before the chunk, decayed over positions c0 .. c0 + i
-          const float cf = exp2f(lg * (float)(i + 1));
-          den *= cf;
+      }
+      const int jn = min(n, r0 + RPT);  // keys past the thread's last row weigh zero
+      for (int j = 0; j < jn; ++j) {
+        float w[RPT], vv[CPT];
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) num[c] *= cf;
+        for (int r = 0; r < RPT; ++r) w[r] = wt[j][r0 + r];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vv[c] = vs[j][c0 + c];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          den[r] += w[r];
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) num[r][c] = __builtin_fmaf(w[r], vv[c], num[r][c]);
         }
-        for (int j = 0; j <= i; ++j) {
+      }
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        if (r0 + r < n) {
+          const float rd = 1.f / den[r];
+          float* yr = yb + (size_t)(t0 + r0 + r) * DV + c0;
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) yr[c] = num[r][c] * rd;
+        }
+      }
+    }
+    __syncthreads();  // every read of the query features done
+
+    // ---- 3. key features (weighted by gamma^(n-1-j) when decayed) and the update
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      if (fu[m] >= 0)
+        for (int j = fr[m]; j < fr[m] + HC; ++j) {
           float x = 0.f;
-#pragma unroll
-          for (int d = 0; d < DK; ++d) x += qr[d] * ks[j][d];
-          float w = 1.f + x + 0.5f * x * x;
-          if (DEC) w *= exp2f(lg * (float)(i - j));
-          den += w;
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) num[c] += w * vs[j][col0 + c];
+          if (j < n) {
+            x = feature(fk[m], ks[j]);
+            if (DEC) x *= exp2f(lg * (float)(n - 1 - j));
+          }
+          fbuf[j * FK + fu[m]] = x;
         }
-        const float r = 1.f / den;
-        float* yr = yb + (size_t)(c0 + i) * DV + col0;
-#pragma unroll
-        for (int c = 0; c < CPT; c += 4) {
-          float4 o = {num[c] * r, num[c + 1] * r, num[c + 2] * r, num[c + 3] * r};
-          *reinterpret_cast<float4*>(yr + c) = o;
-        }
-      }
-    }
     __syncthreads();
-
-    // ---- state update with the chunk: T += psi'(K)^T V, z += sum psi'(k)
     {
-      constexpr int FS = NT / DV;  // features handled in parallel per column
-      const int c = tid % DV;
-      const float gn = DEC ? exp2f(lg * (float)n) : 1.f;  // decay of the carried state over the chunk
-      auto kw = [&](int j) { return DEC ? wk[j] : 1.f; };
-      for (int f = tid / DV; tid < FS * DV && f < NCOMPACT; f += FS) {
-        float acc = 0.f;
-        if (f == 0) {
-          for (int j = 0; j < n; ++j) acc += kw(j) * vs[j][c];
-        } else if (f < 1 + DK) {
-          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][f - 1] * vs[j][c];
-        } else {
-          const int a = c_pairs.a[f - 1 - DK], b = c_pairs.b[f - 1 - DK];
-          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][a] * ks[j][b] * vs[j][c];
-        }
-        Ts[f][c] = DEC ? gn * Ts[f][c] + acc : Ts[f][c] + acc;
+      float acc[FPT][CPT], zacc[FPT];
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        zacc[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[i][c] = 0.f;
       }
-      for (int f = tid; f < NCOMPACT; f += NT) {
-        float acc = 0.f;
-        if (f == 0) {
-          if (DEC)
-            for (int j = 0; j < n; ++j) acc += wk[j];
-          else
-            acc = (float)n;
-        } else if (f < 1 + DK) {
-          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][f - 1];
-        } else {
-          const int a = c_pairs.a[f - 1 - DK], b = c_pairs.b[f - 1 - DK];
-          for (int j = 0; j < n; ++j) acc += kw(j) * ks[j][a] * ks[j][b];
+      for (int j = 0; j < n; ++j) {
+        float ps[FPT], vv[CPT];
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) ps[i] = fbuf[j * FK + f0 + i];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vv[c] = vs[j][c0 + c];
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+          zacc[i] += ps[i];
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[i][c] = __builtin_fmaf(ps[i], vv[c], acc[i][c]);
         }
-        zs[f] = DEC ? gn * zs[f] + acc : zs[f] + acc;
+      }
+      const float gn = DEC ? exp2f(lg * (float)n) : 1.f;  // decay of the carried state over the chunk
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Ts[f0 + i][c0 + c] = DEC ? gn * Ts[f0 + i][c0 + c] + acc[i][c]
+                                                              : Ts[f0 + i][c0 + c] + acc[i][c];
+        if (cb == 0) zs[f0 + i] = DEC ? gn * zs[f0 + i] + zacc[i] : zs[f0 + i] + zacc[i];
       }
     }
   }
