@@ -660,6 +660,9 @@ def summarize_counters(dirs, command, kernels, out_name, out_dir=None):
         xs = sorted(xs)
         return xs[len(xs) // 2] if xs else float("nan")
 
+    def ratio(a, b):
+        return a / b if b else float("nan")  # (a kernel without LDS reads no LDS cycles)
+
     for name, cs in sorted(vals.items()):
         m = {}
         for (d, cn), xs in cs.items():
@@ -670,17 +673,17 @@ def summarize_counters(dirs, command, kernels, out_name, out_dir=None):
         waves = m.get("SQ_WAVES", float("nan"))
         row = {
             "dispatches": n, "gpu_cycles": gui1,
-            "mfma_busy_pct": 100 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui1 * SIMD_NUM),
-            "valu_busy_pct": 100 * m.get("SQ_ACTIVE_INST_VALU", float("nan")) / (gui1 * CU_NUM),
-            "lds_active_pct": 100 * m.get("SQ_LDS_IDX_ACTIVE", float("nan")) / (gui1 * CU_NUM),
-            "bank_conflict": m.get("SQ_LDS_BANK_CONFLICT", float("nan")) / m.get("SQ_LDS_IDX_ACTIVE", float("nan")),
-            "waves_per_simd": 4 * m.get("SQ_WAVE_CYCLES", float("nan")) / (gui0 * SIMD_NUM),
-            "valu_per_wave": m.get("SQ_INSTS_VALU", float("nan")) / waves,
-            "mfma_per_wave": m.get("SQ_INSTS_MFMA", float("nan")) / waves,
-            "lds_per_wave": m.get("SQ_INSTS_LDS", float("nan")) / waves,
-            "salu_per_wave": m.get("SQ_INSTS_SALU", float("nan")) / waves,
-            "trans_per_wave": m.get("SQ_INSTS_VALU_TRANS_F32", float("nan")) / waves,
-            "vmem_per_wave": m.get("SQ_INSTS_VMEM", float("nan")) / waves,
+            "mfma_busy_pct": 100 * ratio(m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")), gui1 * SIMD_NUM),
+            "valu_busy_pct": 100 * ratio(m.get("SQ_ACTIVE_INST_VALU", float("nan")), gui1 * CU_NUM),
+            "lds_active_pct": 100 * ratio(m.get("SQ_LDS_IDX_ACTIVE", float("nan")), gui1 * CU_NUM),
+            "bank_conflict": ratio(m.get("SQ_LDS_BANK_CONFLICT", float("nan")), m.get("SQ_LDS_IDX_ACTIVE", float("nan"))),
+            "waves_per_simd": 4 * ratio(m.get("SQ_WAVE_CYCLES", float("nan")), gui0 * SIMD_NUM),
+            "valu_per_wave": ratio(m.get("SQ_INSTS_VALU", float("nan")), waves),
+            "mfma_per_wave": ratio(m.get("SQ_INSTS_MFMA", float("nan")), waves),
+            "lds_per_wave": ratio(m.get("SQ_INSTS_LDS", float("nan")), waves),
+            "salu_per_wave": ratio(m.get("SQ_INSTS_SALU", float("nan")), waves),
+            "trans_per_wave": ratio(m.get("SQ_INSTS_VALU_TRANS_F32", float("nan")), waves),
+            "vmem_per_wave": ratio(m.get("SQ_INSTS_VMEM", float("nan")), waves),
             "raw": m,
         }
         out_json[name] = row
