@@ -307,10 +307,11 @@ def bwd_inputs(lal, cfg, nbuf=8):
     return sets
 
 
-def bench_bwd(lal, cfg, steps, warmup, sets):
+def bench_bwd(lal, cfg, steps, warmup, sets, settle=0):
     """Time `steps` layer backwards: based_linattn_bwd and based_swa_bwd, each
     in a loop of its own over the prepared input sets (the step's time is
-    their sum).  Returns a dict."""
+    their sum), after `settle` + `warmup` untimed calls of each.  Returns a
+    dict."""
     nbuf = len(sets)
     B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
     ws = torch.empty(max(1, lal.linattn_bwd_workspace_bytes(B, H, L, dv)), dtype=torch.uint8, device="cuda")
@@ -326,7 +327,7 @@ def bench_bwd(lal, cfg, steps, warmup, sets):
         qd, kd, vd, dyd, y_lin, y_swa = sets[i % nbuf]
         lal.swa_bwd(qd, kd, vd, y_swa, dyd, cfg.window, dq=gq, dk=gk, dv=gv)
 
-    for i in range(warmup):
+    for i in range(settle + warmup):
         lin(i)
         swa(i)
     tl, ts = time_loop(lin, steps), time_loop(swa, steps)
@@ -342,14 +343,15 @@ def bench_bwd(lal, cfg, steps, warmup, sets):
             "traffic_bytes_per_step": load_traffic("bwd")}
 
 
-def bench_baseconv(lal, cfg, steps, warmup, nbuf=8):
-    """Time the BaseConv gate over `nbuf` resident input sets.  Bytes per
-    element: x and u read once (dtype), y written (fp32)."""
+def bench_baseconv(lal, cfg, steps, warmup, nbuf=8, settle=0):
+    """Time the BaseConv gate over `nbuf` resident input sets, after `settle` +
+    `warmup` untimed calls.  Bytes per element: x and u read once (dtype), y
+    written (fp32)."""
     x, u, h, b = synth.baseconv_inputs(cfg, 0)
     sets = [(x.to("cuda"), u.to("cuda")) for _ in range(nbuf)]
     hd, bd = h.to("cuda"), b.to("cuda")
     y = torch.empty(cfg.B, cfg.L, cfg.D, device="cuda")
-    for i in range(warmup):
+    for i in range(settle + warmup):
         lal.baseconv_fwd(*sets[i % nbuf], hd, bd, y=y)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -367,16 +369,17 @@ def bench_baseconv(lal, cfg, steps, warmup, nbuf=8):
             "traffic_bytes_per_call": load_traffic("baseconv")}
 
 
-def bench_decay(lal, cfg, steps, warmup, nbuf=8):
+def bench_decay(lal, cfg, steps, warmup, nbuf=8, settle=0):
     """Time the decayed linear attention (per-head decays from
-    synth.decay_rates) over `nbuf` resident input sets."""
+    synth.decay_rates) over `nbuf` resident input sets, after `settle` +
+    `warmup` untimed calls."""
     q, k, v = synth.fwd_inputs(cfg, 0)
     sets = [tuple(t.to("cuda") for t in (q, k, v)) for _ in range(nbuf)]
     g = synth.decay_rates(cfg.H).to("cuda")
     B, H, L, dv = cfg.B, cfg.H, cfg.L, cfg.dv
     y = torch.empty(B, H, L, dv, device="cuda")
     ws = torch.empty(max(lal.linattn_workspace_bytes(B, H, L, dv), 1), dtype=torch.uint8, device="cuda")
-    for i in range(warmup):
+    for i in range(settle + warmup):
         lal.linattn_decay_fwd(*sets[i % nbuf], g, y=y, workspace=ws)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -754,7 +757,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (enough for the GPU clocks to settle)")
     ap.add_argument("--settle", type=int, default=300,
-                    help="untimed calls of the step before the warm-up steps, so that the GPU clocks settle")
+                    help="untimed calls of each timed operation before its warm-up calls, so that the GPU clocks "
+                         "settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and decode")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -806,21 +810,22 @@ def main():
         tiny = bench_tiny(lal, synth.FWD_CONFIGS["tiny"])
         print(f"[bench] tiny fp32 layer: {tiny['us_per_call_back_to_back']:.1f} us/call back to back, "
               f"{tiny['us_latency_median']:.1f} us latency", file=sys.stderr, flush=True)
-        backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets)
+        backward = bench_bwd(lal, cfg, args.steps, args.warmup, bsets, settle=args.settle)
         del bsets
         print(f"[bench] {cfg.name} backward: linattn {backward['linattn_bwd_us']:.1f} us, swa "
               f"{backward['swa_bwd_us']:.1f} us", file=sys.stderr, flush=True)
-        separate = bench_fwd(lal, cfg, max(10, args.steps // 2), args.warmup, fused=False)
+        separate = bench_fwd(lal, cfg, max(10, args.steps // 2), args.warmup, fused=False, settle=args.settle)
         print(f"[bench] {cfg.name} separate calls: linattn {separate['linattn_us']:.1f} us, swa "
               f"{separate['swa_us']:.1f} us", file=sys.stderr, flush=True)
         for name in ("based1p3b", "long32k"):
-            r = bench_fwd(lal, synth.FWD_CONFIGS[name], max(10, args.steps // 2), args.warmup, nbuf=4)
+            r = bench_fwd(lal, synth.FWD_CONFIGS[name], max(10, args.steps // 2), args.warmup, nbuf=4,
+                          settle=args.settle)
             extra.append(r)
             print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-        conv = bench_baseconv(lal, synth.CONV_CONFIGS["baseconv360m"], args.steps, args.warmup)
+        conv = bench_baseconv(lal, synth.CONV_CONFIGS["baseconv360m"], args.steps, args.warmup, settle=args.settle)
         print(f"[bench] baseconv: {conv['us_per_call']:.1f} us/call ({conv['hbm_gbs']:.0f} GB/s)", file=sys.stderr,
               flush=True)
-        decay = bench_decay(lal, cfg, args.steps, args.warmup)
+        decay = bench_decay(lal, cfg, args.steps, args.warmup, settle=args.settle)
         print(f"[bench] {cfg.name} decayed linear attention: {decay['us_per_call']:.1f} us/call "
               f"({decay['hbm_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
         decode = bench_decode(lal, synth.DECODE_CONFIG)
