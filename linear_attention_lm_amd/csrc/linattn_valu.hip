@@ -10,7 +10,7 @@
 // update with the chunk.  The state lives in LDS in the compact form (one row
 // per unordered feature pair, see based_device.h).
 //
-// One workgroup of 256 threads per (batch, head); chunks run in sequence.
+// One workgroup of 512 threads per (batch, head); chunks run in sequence.
 // A per-head decay of the state (DEC) is the same pass with decay weights.
 #include "based_device.h"
 #include "launchers.h"
@@ -19,7 +19,6 @@ namespace based {
 namespace {
 
 constexpr int C = 32;    // positions per chunk
-constexpr int NT = 256;  // threads per workgroup
 constexpr int NFP = 160; // compact feature rows, padded (NCOMPACT used)
 
 struct PairTables {
@@ -51,14 +50,20 @@ __device__ float phi_from_compact(const float* T, int f, int c, int ld) {
   return T[(1 + DK + pair_index(lo, hi)) * ld + c] * INV_SQRT2;
 }
 
-// Work split of a chunk among the 256 threads: value columns in NCB blocks
+// Threads per workgroup: two wavefronts per SIMD (four measured slower: the
+// tiny fp32 layer's linear attention 136 us against 94 us).
+template <int DV>
+constexpr int nthreads() { return 512; }
+
+// Work split of a chunk among the NT threads: value columns in NCB blocks
 // of CPT, and the other axis (the chunk's rows for the readout and the
 // in-chunk term, the state's feature rows for the update) in NRB blocks.
 template <int DV>
 struct Split {
-  static constexpr int NCB = DV >= 64 ? 16 : 8;  // column blocks
+  static constexpr int NT = nthreads<DV>();
+  static constexpr int NRB = 32;                 // row / feature blocks
+  static constexpr int NCB = NT / NRB;           // column blocks
   static constexpr int CPT = DV / NCB;           // columns per thread
-  static constexpr int NRB = NT / NCB;           // row / feature blocks
   static constexpr int RPT = C / NRB;            // chunk rows per thread (readout)
   static constexpr int FPT = NFP / NRB;          // feature rows per thread (update)
   static_assert(DV % NCB == 0 && C % NRB == 0 && NFP % NRB == 0, "tiling");
@@ -109,11 +114,11 @@ __device__ __forceinline__ float feature(const FeatureCoef& fc, const float* x) 
 //      update T += psi(K)^T V, z += psi(K)^T 1, each thread FPT feature rows
 //      x CPT columns.
 template <typename T, int DV, int DEC>
-__global__ __launch_bounds__(NT) void linattn_valu_kernel(
+__global__ __launch_bounds__(nthreads<DV>()) void linattn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ y,
     const float* S_in, const float* z_in, float* S_out, float* z_out, int L, const float* gamma, int H) {
   using SP = Split<DV>;
-  constexpr int CPT = SP::CPT, RPT = SP::RPT, FPT = SP::FPT;
+  constexpr int NT = SP::NT, CPT = SP::CPT, RPT = SP::RPT, FPT = SP::FPT;
   constexpr int FT = C + 4;    // row stride of the feature-major query features
   constexpr int FK = NFP + 4;  // row stride of the row-major key features
   static_assert(NFP * FT >= C * FK, "the key features reuse the query features' buffer");
@@ -134,13 +139,13 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
   const T* kb = k + (size_t)bh * L * DK;
   const T* vb = v + (size_t)bh * L * DV;
   float* yb = y + (size_t)bh * L * DV;
-  // feature fills: item u = tid + NT m (m = 0, 1; u < 2 NFP) is feature u / 2
+  // feature fills: item u = tid + NT m (m < NFI; u < 2 NFP) is feature u / 2
   // over rows (u % 2) C/2 .. + C/2 - 1 of the chunk
-  constexpr int HC = C / 2;
-  FeatureCoef fq[2], fk[2];
-  int fu[2], fr[2];
+  constexpr int HC = C / 2, NFI = (2 * NFP + NT - 1) / NT;
+  FeatureCoef fq[NFI], fk[NFI];
+  int fu[NFI], fr[NFI];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < NFI; ++m) {
     const int u = tid + NT * m;
     fu[m] = u < 2 * NFP ? u / 2 : -1;
     fr[m] = (u % 2) * HC;
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
 
     // ---- 1. query features and in-chunk weights
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < NFI; ++m)
       if (fu[m] >= 0)
         for (int i = fr[m]; i < fr[m] + HC; ++i) fbuf[fu[m] * FT + i] = feature(fq[m], qs[i]);
     for (int e = tid; e < C * C; e += NT) {
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
 
     // ---- 3. key features (weighted by gamma^(n-1-j) when decayed) and the update
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < NFI; ++m)
       if (fu[m] >= 0)
         for (int j = fr[m]; j < fr[m] + HC; ++j) {
           float x = 0.f;
@@ -301,10 +306,10 @@ __global__ __launch_bounds__(NT) void linattn_valu_kernel(
 template <typename T, int DV>
 hipError_t launch_dv(const LinattnArgs& a, hipStream_t s) {
   if (a.gamma)
-    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 1>), dim3(a.B * a.H), dim3(NT), 0, s, (const T*)a.q,
+    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 1>), dim3(a.B * a.H), dim3(nthreads<DV>()), 0, s, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
   else
-    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 0>), dim3(a.B * a.H), dim3(NT), 0, s, (const T*)a.q,
+    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 0>), dim3(a.B * a.H), dim3(nthreads<DV>()), 0, s, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
   return hipGetLastError();
 }
