@@ -216,13 +216,16 @@ int based_linattn_bwd(const void* q, const void* k, const void* v, const float* 
  *              based_linattn_decay_fwd
  *   q, k, v, y, dy, dq, dk, dv: as for based_linattn_bwd (y from
  *              based_linattn_decay_fwd with the same gamma)
- *   workspace: at least 2 * B * H * L * 4 bytes of device memory (never more
- *              than based_linattn_bwd_workspace_bytes for the same shape);
- *              contents on entry are ignored.
- * Both dtypes and every d_v in {16, ..., 128}: the direct form, fp32 vector
- * arithmetic over every (i, j <= i) pair (work quadratic in L).  Errors as for
- * based_linattn_bwd, and BASED_ERR_NULL for a null gamma; gamma must not
- * overlap an output or the workspace.
+ *   workspace: at least 2 * B * H * L * 4 bytes of device memory; contents
+ *              on entry are ignored.
+ * With BASED_BF16, d_v in {32, 64, 96, 128} and a workspace of at least
+ * based_linattn_bwd_workspace_bytes for the shape, the matrix-core passes of
+ * based_linattn_bwd with the decay (the carried states decay per position and
+ * per chunk, the in-chunk terms carry gamma^(i-j); the same numerics).
+ * Otherwise (fp32, other widths, or the smaller workspace) the direct form:
+ * fp32 vector arithmetic over every (i, j <= i) pair (work quadratic in L).
+ * Errors as for based_linattn_bwd, and BASED_ERR_NULL for a null gamma; gamma
+ * must not overlap an output or the workspace.
  */
 int based_linattn_decay_bwd(const void* q, const void* k, const void* v, const float* gamma, const float* y,
                             const float* dy, float* dq, float* dk, float* dv, int B, int H, int L, int d_k,

@@ -323,7 +323,10 @@ def linattn_bwd(q, k, v, y, dy, *, dq=None, dk=None, dv=None, workspace=None):
 def linattn_decay_bwd(q, k, v, gamma, y, dy, *, dq=None, dk=None, dv=None, workspace=None):
     """Gradients (dq, dk, dv), fp32, of :func:`linattn_decay_fwd`'s output y
     (zero initial state, per-head decay gamma [H] fp32) for the upstream
-    gradient dy."""
+    gradient dy.  The default workspace is
+    :func:`linattn_bwd_workspace_bytes` (bf16 with d_v in {32, 64, 96, 128}
+    then takes the matrix-core passes); one of 2*B*H*L*4 bytes selects the
+    direct form."""
     _check_bwd_args(q, k, v, y, dy)
     B, H, L, dk_ = q.shape
     dvw = v.shape[-1]
@@ -332,7 +335,8 @@ def linattn_decay_bwd(q, k, v, gamma, y, dy, *, dq=None, dk=None, dv=None, works
     _dev(q, k, v, gamma, y, dy, dq, dk, dv, workspace)
     dq, dk, dv = _grads_out(q, k, v, dq, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(1, 2 * B * H * L * 4), device=q.device, dtype=torch.uint8)
+        need = max(2 * B * H * L * 4, linattn_bwd_workspace_bytes(B, H, L, dvw, q.dtype), 1)
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     wbytes = workspace.numel() * workspace.element_size()
     _check(_lib().based_linattn_decay_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(y), _ptr(dy), _ptr(dq),
                                        _ptr(dk), _ptr(dv), B, H, L, dk_, dvw, _dtype_code(q), _ptr(workspace), wbytes,

@@ -67,6 +67,13 @@ constexpr int NCOMPACT = 1 + DK + NQUAD;  // 153
 // at most 2^-126 for gamma = 0 and d >= 1, and never above 1.
 __device__ __forceinline__ float decay_lg2_clamped(float lg) { return fminf(fmaxf(lg, -126.f), 0.f); }
 __device__ __forceinline__ float decay_clamped(float gamma) { return fminf(fmaxf(gamma, 0.f), 1.f); }
+// gamma^d from lg = log2 gamma (d >= 0)
+__device__ __forceinline__ float gpow(float lg, float d) { return __builtin_amdgcn_exp2f(lg * d); }
+// sum_{d < n} gamma^d, through expm1 so that gamma near 1 keeps its precision
+__device__ __forceinline__ float gsum_pow(float lg, int n) {
+  const float ln = lg * 0.69314718055994531f;
+  return ln == 0.f ? (float)n : expm1f(ln * (float)n) / expm1f(ln);
+}
 
 // Index of the unordered pair (a <= b) in the row-major upper triangle.
 __host__ __device__ constexpr int pair_index(int a, int b) { return a * DK - a * (a - 1) / 2 + (b - a); }

@@ -46,9 +46,10 @@ hipError_t launch_linattn_mfma(const LinattnArgs& a, hipStream_t stream);
 hipError_t launch_linattn_decay_mfma(const LinattnArgs& a, hipStream_t stream);
 // The state-only pass alone (zero initial state; bf16, d_v in {32, 64, 96, 128}):
 // compact segment increments at ws, as the main pass's records, for the
-// first nrec segments of each head (nrec <= nseg - 1).
+// first nrec segments of each head (nrec <= nseg - 1); with a per-head decay
+// gamma [H] (or null), each increment decayed to its segment's end.
 hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
-                                        int seg_chunks, int nrec, hipStream_t stream);
+                                        int seg_chunks, int nrec, const float* gamma, int H, hipStream_t stream);
 // The same pass with the sliding-window softmax of the same q, k, v fused in
 // (d_qk = d_k = 16), written to y_swa.
 hipError_t launch_layer_mfma(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t stream);
@@ -77,7 +78,7 @@ struct LinattnBwdArgs {
   float* gq; float* gk; float* gv;
   int B, H, L, dv;
   void* workspace; size_t workspace_bytes;
-  const float* gamma = nullptr;  // [H] per-head state decay (decayed variant: the direct form)
+  const float* gamma = nullptr;  // [H] per-head state decay (decayed variant)
 };
 size_t linattn_bwd_workspace(int B, int H, int L, int dv, bool bf16);
 // bf16 on the matrix cores for d_v in {32, 64, 96, 128} (slices of 32 columns)

@@ -222,7 +222,11 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
-  if (!a.gamma && bf16 && linattn_bwd_mfma_supported(a.dv)) return launch_linattn_bwd_mfma(a, s);
+  // the decayed variant takes the matrix-core passes when the caller's
+  // workspace holds theirs (it may be as small as the direct form's)
+  if (bf16 && linattn_bwd_mfma_supported(a.dv) &&
+      (!a.gamma || a.workspace_bytes >= linattn_bwd_mfma_workspace(a.B, a.H, a.L, a.dv)))
+    return launch_linattn_bwd_mfma(a, s);
   return bf16 ? launch_direct_dv<bf16_t>(a, s) : launch_direct_dv<float>(a, s);
 }
 

@@ -224,6 +224,8 @@ struct Params {
   float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
   int L, dvf, nslice, nseg, seg_chunks;
   int rsplit;           // forward-record sub-segments per segment
+  const float* gamma;   // decayed variant: [H] per-head state decay
+  int H;
 };
 
 // Workgroup -> (head, value slice, segment) and the segment's positions.
@@ -359,6 +361,12 @@ struct QSmem {
   float dys[C];                            // dy . y over the slice's columns, per position
   float dens[C];                           // den of the chunk's positions
   float wmax[4];
+  // decayed variant: the in-chunk weights gamma^(query - key) as lane l of
+  // wavefront w holds them for the key tile t tiles before its query tile
+  // (query 16 w + l % 16, keys 16 (w - t) + 4 (l / 16) + i; zero for a key
+  // after the query), and the update's key weights gamma^(C - 1 - key)
+  alignas(16) float dw[4][64][4];
+  alignas(16) half_t wkc[C];
 };
 
 __device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
@@ -390,6 +398,13 @@ __device__ __forceinline__ void q_store(QSmem& S, const Pre& pf) {
   }
 }
 
+// DEC: the decayed variant (a per-head gamma on the state: the kernel
+// entry of (i, j) weighs gamma^(i-j)).  The state before a chunk reaches its
+// position pos times gamma^(pos + 1) (readout and den), the in-chunk terms
+// carry gamma^(i-j), and the update is S <- gamma^n S + sum_j gamma^(n-1-j)
+// phi(k_j) v_j^T; the forward records are the segments' decayed increments,
+// summed with the decay over the distance to this segment.
+template <int DEC>
 __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
   __shared__ QSmem S;
   const Unit un = unit_of(p);
@@ -399,6 +414,20 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int pos = 16 * w + r16;  // position (query) of the lane in transposed tiles
   const int L = p.L;
+  const float lg = DEC ? decay_lg2_clamped(__log2f(p.gamma[bh % p.H])) : 0.f;
+  const float cf = DEC ? gpow(lg, (float)(pos + 1)) : 1.f;  // the carried state's weight at pos
+  if constexpr (DEC) {
+    for (int j = tid; j < 4 * 64; j += NTHR) {
+      const int t = j >> 6, l = j & 63, d0 = 16 * t + (l & 15) - 4 * (l >> 4);
+      float4 wv;
+      wv.x = d0 >= 0 ? gpow(lg, (float)d0) : 0.f;
+      wv.y = d0 >= 1 ? gpow(lg, (float)(d0 - 1)) : 0.f;
+      wv.z = d0 >= 2 ? gpow(lg, (float)(d0 - 2)) : 0.f;
+      wv.w = d0 >= 3 ? gpow(lg, (float)(d0 - 3)) : 0.f;
+      *reinterpret_cast<float4*>(&S.dw[t][l][0]) = wv;
+    }
+    for (int j = tid; j < C; j += NTHR) S.wkc[j] = (half_t)gpow(lg, (float)(C - 1 - j));
+  }
 
   for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.st[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.zs[e] = 0.f;
@@ -458,6 +487,10 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
   if (un.seg > 0) {
     const int rows = NFC + 1, nr = un.seg * p.rsplit;
     const size_t first = bh * p.nseg * p.rsplit + 1;
+    // decayed variant: record k (0-based) ends (nr - 1 - k) sub-segments
+    // before this segment starts
+    const int sub = p.seg_chunks * C / p.rsplit;
+    auto rec_w = [&](int k2) { return DEC ? gpow(lg, (float)((nr - 1 - k2) * sub)) : 1.f; };
     const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.frec + first * rows * p.dvf), (short)0, nr * rows * p.dvf * (int)sizeof(float), RSRC_DW3);
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
@@ -468,13 +501,14 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
         const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
         float z = 0.f;
         if (nr & 1) {  // record 1 on its own
+          const float wr = rec_w(0);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[j][nn][i] += bload1(rf, (int)record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf) *
-                                              (int)sizeof(float));
-          z += bload1(rz, slot * (int)sizeof(float));
+              acc[j][nn][i] += wr * bload1(rf, (int)record_offset(slot, s * SW + 16 * nn + 4 * g + i, p.dvf) *
+                                                   (int)sizeof(float));
+          z += wr * bload1(rz, slot * (int)sizeof(float));
         }
         for (int r = nr & 1; r < nr; r += 2) {  // pairs (an odd record first, alone)
           float x[2][2][4], zz[2];
@@ -491,11 +525,12 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           }
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
+            const float wr = rec_w(r + u);
 #pragma unroll
             for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[j][nn][i] += x[u][nn][i];
-            z += zz[u];
+              for (int i = 0; i < 4; ++i) acc[j][nn][i] += wr * x[u][nn][i];
+            z += wr * zz[u];
           }
         }
         zacc[j] = z;
@@ -528,10 +563,20 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       if (m <= w) {
         const f16x8 kv = g < 2 ? ld8(&S.kh[16 * m + r16][8 * g]) : zero8;
         xc[m] = mfma(kv, qv, xc[m]);
+        if constexpr (DEC) {  // gamma^(query - key), zero for a key after the query
+          const float4 dv4 = *reinterpret_cast<const float4*>(&S.dw[w - m][lane][0]);
+          const float wt[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = xc[m][i];
-          if (m < w || 4 * g + i <= r16) dpart += 1.f + x + 0.5f * x * x;
+          for (int i = 0; i < 4; ++i) {
+            const float x = xc[m][i];
+            dpart += wt[i] * (1.f + x + 0.5f * x * x);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = xc[m][i];
+            if (m < w || 4 * g + i <= r16) dpart += 1.f + x + 0.5f * x * x;
+          }
         }
       }
     }
@@ -561,11 +606,12 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           const float4 z4 = *reinterpret_cast<const float4*>(&S.zs[DK + DK * a + b]);
           zq += z4.x * qf[b] + z4.y * qf[b + 1] + z4.z * qf[b + 2] + z4.w * qf[b + 3];
         }
-        dpart += qa * (S.zs[a] + 0.5f * zq);
+        dpart += cf * qa * (S.zs[a] + 0.5f * zq);
         zg[i] = S.zs[a] + zq;
       }
     }
-    const float den = rows_sum(dpart) + (float)t0;
+    // (the constant feature: t0 earlier positions, decayed: cf sum_{d < t0} gamma^d)
+    const float den = rows_sum(dpart) + (DEC ? cf * gsum_pow(lg, t0) : (float)t0);
     const float hval = -S.dys[pos] / den;
     if (g == 0) {
       S.dens[pos] = den;
@@ -592,14 +638,16 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     // ---- dq from the state: u^T = S^T-readout (features x this position),
     // lane-local contraction into dq[4g + i]; plus the z h share, h zg
     // (the copy's scale 2^e rides on the q factors: exact, a power of two)
-    f32x4 dqa = zg * hval;
+    // (decayed: the carried state's weight cf at this position rides along)
+    const float upc = DEC ? up * cf : up;
+    f32x4 dqa = zg * (DEC ? hval * cf : hval);
     const f16x8 gbh = ld8(&S.gh[pos][8 * g]), gbl = ld8(&S.gl[pos][8 * g]);
 #pragma unroll
     for (int m = 0; m < NFT; ++m) {
       const f16x8 sa = ld8(&S.st[16 * m + r16][8 * g]);
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(sa, gbh, u);  // g rounded once: the state copy is fp16 as well
-      dqa += u * (m == 0 ? up : qf[m - 1] * up);
+      dqa += u * (m == 0 ? upc : qf[m - 1] * upc);
     }
 
     // ---- in-chunk term: dK^T = V G^T (+ h), c = dK (1 + x) below the
@@ -614,10 +662,17 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           f32x4 da = {0.f, 0.f, 0.f, 0.f};
           da = mfma(va, gbh, da);
           da = mfma(va, gbl, da);
+          if constexpr (DEC) {
+            const float4 dv4 = *reinterpret_cast<const float4*>(&S.dw[w - m][lane][0]);
+            const float wt[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dk = da[i] + hval;
-            cw[m][i] = (m < w || 4 * g + i <= r16) ? dk * (1.f + xc[m][i]) : 0.f;
+            for (int i = 0; i < 4; ++i) cw[m][i] = wt[i] * (da[i] + hval) * (1.f + xc[m][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float dk = da[i] + hval;
+              cw[m][i] = (m < w || 4 * g + i <= r16) ? dk * (1.f + xc[m][i]) : 0.f;
+            }
           }
         }
       }
@@ -638,6 +693,31 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     }
 
     // ---- state update with the chunk: S^T += V^T phi(K), z += phi(K)^T 1
+    // (decayed: S^T <- gamma^n S^T + V^T diag(gamma^(n-1-j)) phi(K), z likewise)
+    f16x8 wk[2];
+    if constexpr (DEC) {
+      float gn;
+      if (n == C) {  // uniform branch: a whole chunk takes the table
+        gn = gpow(lg, (float)C);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) wk[ks] = ld8(&S.wkc[32 * ks + 8 * g]);
+      } else {
+        gn = gpow(lg, (float)n);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = 32 * ks + 8 * g + i;
+            wk[ks][i] = (half_t)(key < n ? gpow(lg, (float)(n - 1 - key)) : 0.f);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < MAXOWN; ++j) {
+        acc[j][0] *= gn;
+        acc[j][1] *= gn;
+        zacc[j] *= gn;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
       if (j < own_count(w, 0)) {
@@ -645,7 +725,8 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const f16x8 kb = ld8(&S.kt[r16][32 * ks + 8 * g]);
-          const f16x8 fb = mt == 0 ? kb : ld8(&S.kt[mt - 1][32 * ks + 8 * g]) * kb;
+          f16x8 fb = mt == 0 ? kb : ld8(&S.kt[mt - 1][32 * ks + 8 * g]) * kb;
+          if constexpr (DEC) fb *= wk[ks];
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.vh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
@@ -672,6 +753,14 @@ struct KSmem {
   alignas(16) float hs[C];                   // h of the chunk's positions
   float gpart[8][SW];                        // column sums of g over 8-row groups
   float wmax[4];
+  // decayed variant: the in-chunk weights gamma^(query - key) as lane l of
+  // wavefront w holds them for the query tile t tiles after its key tile
+  // (key 16 w + l % 16, queries 16 (w + t) + 4 (l / 16) + i; zero for a
+  // query before the key), and the update's query weights gamma^p over the
+  // chunk's positions p (fp16 for the features, fp32 for the sums of g)
+  alignas(16) float dw[4][64][4];
+  alignas(16) half_t wq[C];
+  alignas(16) float wqf[C];
 };
 
 __device__ __forceinline__ void k_store(KSmem& S, const Pre& pf) {
@@ -727,6 +816,10 @@ struct KIncSmem {
   alignas(16) float gsum[C][SW];  // per-thread column sums of g (row tid / 4), summed in row order
 };
 
+// DEC: the decayed variant -- position i of the segment weighs
+// gamma^(i - start) in the increment (the key pass decays the increments of
+// later segments over the distance to its own).
+template <int DEC>
 __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   __shared__ KIncSmem S;
   const Unit un = unit_of(p);
@@ -753,6 +846,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
     acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float lg = DEC ? decay_lg2_clamped(__log2f(p.gamma[bh % p.H])) : 0.f;
   const HeadRsrc rs = head_rsrc(p, bh, p.den, p.h + (size_t)s * p.npos);
   Pre pf;
   k_load(p, rs, s, un.t_begin, pf);
@@ -766,7 +860,8 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
     }
     {
       const int r = tid >> 2, cq = tid & 3;
-      const float rden = 1.f / pf.aux;
+      float rden = 1.f / pf.aux;
+      if constexpr (DEC) rden *= gpow(lg, (float)(t0 - un.t_begin + r));
       const float gv[8] = {pf.dy0.x * rden, pf.dy0.y * rden, pf.dy0.z * rden, pf.dy0.w * rden,
                            pf.dy1.x * rden, pf.dy1.y * rden, pf.dy1.z * rden, pf.dy1.w * rden};
       uint32_t hi[4];
@@ -776,7 +871,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) gpart[i] += gv[i];
     }
-    if (tid < C) S.hh[tid] = (_Float16)pf.aux2;
+    if (tid < C) S.hh[tid] = (_Float16)(DEC ? pf.aux2 * gpow(lg, (float)(t0 - un.t_begin + tid)) : pf.aux2);
     __syncthreads();
     if (t0 + C < un.t_end) k_load(p, rs, s, t0 + C, pf);
 #pragma unroll
@@ -819,6 +914,13 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   }
 }
 
+// DEC: the decayed variant.  The suffix state R (and r, the sum of g) is
+// kept relative to the start of the chunk after the current one: key p of
+// the chunk reads it times gamma^(C - p), the in-chunk terms carry
+// gamma^(i - j), and the update is R <- gamma^C R + sum_p gamma^p
+// phi(q_p) g_p^T; the later segments' increments are decayed over the
+// distance to this segment's end.
+template <int DEC>
 __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   __shared__ KSmem S;
   const Unit un = unit_of(p);
@@ -827,6 +929,23 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   const int kpos = 16 * w + r16;  // key of the lane in transposed tiles
   const int L = p.L;
+  const float lg = DEC ? decay_lg2_clamped(__log2f(p.gamma[bh % p.H])) : 0.f;
+  const float wkey = DEC ? gpow(lg, (float)(C - kpos)) : 1.f;  // the suffix state's weight at this key
+  if constexpr (DEC) {
+    for (int j = tid; j < 4 * 64; j += NTHR) {
+      const int t = j >> 6, l = j & 63, d0 = 16 * t + 4 * (l >> 4) - (l & 15);
+      float4 wv;
+      wv.x = d0 >= 0 ? gpow(lg, (float)d0) : 0.f;
+      wv.y = d0 >= -1 ? gpow(lg, (float)(d0 + 1)) : 0.f;
+      wv.z = d0 >= -2 ? gpow(lg, (float)(d0 + 2)) : 0.f;
+      wv.w = d0 >= -3 ? gpow(lg, (float)(d0 + 3)) : 0.f;
+      *reinterpret_cast<float4*>(&S.dw[t][l][0]) = wv;
+    }
+    for (int j = tid; j < C; j += NTHR) {
+      S.wqf[j] = gpow(lg, (float)j);
+      S.wq[j] = (half_t)S.wqf[j];
+    }
+  }
 
   for (int e = tid; e < NFP * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.rs[e] = 0.f;
@@ -882,6 +1001,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     float g0 = 0.f;
     for (int r = un.seg + 1; r < p.nseg; ++r) {
       const float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + r) * (size_t)RREC;
+      // decayed: segment r starts (r - seg - 1) segments after this one ends
+      const float wr = DEC ? gpow(lg, (float)((r - un.seg - 1) * p.seg_chunks * C)) : 1.f;
 #pragma unroll
       for (int j = 0; j < MAXOWN; ++j) {
         if (j < own_count(w, 3)) {
@@ -889,12 +1010,12 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
             const float4 x = *reinterpret_cast<const float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g);
-            acc[j][nn] += f32x4{x.x, x.y, x.z, x.w};
+            acc[j][nn] += wr * f32x4{x.x, x.y, x.z, x.w};
           }
-          racc[j] += rec[(size_t)NF * SW + f];
+          racc[j] += wr * rec[(size_t)NF * SW + f];
         }
       }
-      if (tid < SW) g0 += rec[(size_t)NF * SW + NF + tid];
+      if (tid < SW) g0 += wr * rec[(size_t)NF * SW + NF + tid];
     }
     if (tid < SW) S.g0[tid] = g0;
     publish();
@@ -924,13 +1045,15 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     // ---- dk from the state: u^T = R-readout with v_j, lane-local contraction
     // (the r share is added before the store)
     // (the copy's scale 2^e rides on the k factors: exact, a power of two)
+    // (decayed: the suffix state's weight at this key rides along)
+    const float upk = DEC ? up * wkey : up;
     f32x4 dka = {0.f, 0.f, 0.f, 0.f};
     const f16x8 vb = ld8(&S.vh[kpos][8 * g]);
 #pragma unroll
     for (int m = 0; m < NFT; ++m) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
       u = mfma(ld8(&S.rf[16 * m + r16][8 * g]), vb, u);
-      dka += u * (m == 0 ? up : kf[m - 1] * up);
+      dka += u * (m == 0 ? upk : kf[m - 1] * upk);
     }
     // ---- dv from the state: R^T phi~(k_j) with phi~ = [k_a, k_a k_b / 2], plus sum g
     f32x4 dva[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -953,6 +1076,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       for (int nn = 0; nn < 2; ++nn) {
         const float4 g4 = *reinterpret_cast<const float4*>(&S.g0[16 * nn + 4 * g]);
         dva[nn] = dva[nn] * up + f32x4{g4.x, g4.y, g4.z, g4.w};
+        if constexpr (DEC) dva[nn] *= wkey;
       }
     }
     // ---- in-chunk terms: queries i >= j in the query tiles m >= w
@@ -971,12 +1095,23 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
           da = mfma(ld8(&S.gl[16 * m + r16][8 * g]), vb, da);
           const float4 h4 = *reinterpret_cast<const float4*>(&S.hs[16 * m + 4 * g]);
           const float hq[4] = {h4.x, h4.y, h4.z, h4.w};
+          if constexpr (DEC) {  // gamma^(query - key), zero for a query before the key
+            const float4 dv4 = *reinterpret_cast<const float4*>(&S.dw[m - w][lane][0]);
+            const float wt[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool keep = m > w || 4 * g + i >= r16;
-            const float xx = x[i];
-            aw[m][i] = keep ? 1.f + xx + 0.5f * xx * xx : 0.f;
-            cw[m][i] = keep ? (da[i] + hq[i]) * (1.f + xx) : 0.f;
+            for (int i = 0; i < 4; ++i) {
+              const float xx = x[i];
+              aw[m][i] = wt[i] * (1.f + xx + 0.5f * xx * xx);
+              cw[m][i] = wt[i] * (da[i] + hq[i]) * (1.f + xx);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool keep = m > w || 4 * g + i >= r16;
+              const float xx = x[i];
+              aw[m][i] = keep ? 1.f + xx + 0.5f * xx * xx : 0.f;
+              cw[m][i] = keep ? (da[i] + hq[i]) * (1.f + xx) : 0.f;
+            }
           }
         }
       }
@@ -1014,7 +1149,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
         rk += r0.x * (float)k8[0] + r0.y * (float)k8[1] + r0.z * (float)k8[2] + r0.w * (float)k8[3] +
               r1.x * (float)k8[4] + r1.y * (float)k8[5] + r1.z * (float)k8[6] + r1.w * (float)k8[7];
       }
-      dka[i] += rk;
+      dka[i] += DEC ? rk * wkey : rk;
     }
     if (kpos < n) {
       float* dst = (p.nslice == 1 ? p.gk : p.pk + (size_t)s * p.npos * DK) + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
@@ -1026,6 +1161,16 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     }
 
     // ---- state update with the chunk: R^T += G^T phi(Q), r += phi(Q)^T h
+    // (decayed: R^T <- gamma^C R^T + G^T diag(gamma^p) phi(Q), r likewise)
+    const float gC = DEC ? gpow(lg, (float)C) : 1.f;
+    if constexpr (DEC) {
+#pragma unroll
+      for (int j = 0; j < MAXOWN; ++j) {
+        acc[j][0] *= gC;
+        acc[j][1] *= gC;
+        racc[j] *= gC;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < MAXOWN; ++j) {
       if (j < own_count(w, 3)) {
@@ -1035,7 +1180,8 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
-          const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+          f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+          if constexpr (DEC) fb *= ld8(&S.wq[32 * ks + 8 * g]);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
@@ -1049,7 +1195,10 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       const int c = tid & (SW - 1), part = tid / SW;
       float gs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) gs += (float)S.gh[8 * part + r][c] + (float)S.gl[8 * part + r][c];
+      for (int r = 0; r < 8; ++r) {
+        const float gr = (float)S.gh[8 * part + r][c] + (float)S.gl[8 * part + r][c];
+        gs += DEC ? S.wqf[8 * part + r] * gr : gr;
+      }
       S.gpart[part][c] = gs;
     }
     publish();
@@ -1058,7 +1207,7 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       float gsum = 0.f;
 #pragma unroll
       for (int part = 0; part < 8; ++part) gsum += S.gpart[part][t];
-      S.g0[t] += gsum;
+      S.g0[t] = DEC ? gC * S.g0[t] + gsum : S.g0[t] + gsum;
     }
     if (t0 - C >= un.t_begin) k_store(S, pf);
   }
@@ -1077,6 +1226,8 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   p.npos = npos;
   p.gq = a.gq; p.gk = a.gk; p.gv = a.gv;
   p.L = a.L; p.dvf = a.dv; p.nslice = a.dv / SW;
+  p.gamma = a.gamma;
+  p.H = a.H;
   linattn_bwd_mfma_plan((int)BH, a.L, a.dv, &p.nseg, &p.seg_chunks);
   float* part = p.h + (size_t)p.nslice * npos;
   if (p.nslice > 1) {
@@ -1095,17 +1246,22 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   if (p.nseg > 1) {
     // the sub-segments before the last segment (no segment reads the last one's)
     if (hipError_t e = launch_linattn_state_records(a.k, a.v, frec, (int)BH, a.L, a.dv, nrec_seg,
-                                                    p.seg_chunks / p.rsplit, (p.nseg - 1) * p.rsplit, s);
+                                                    p.seg_chunks / p.rsplit, (p.nseg - 1) * p.rsplit, a.gamma,
+                                                    a.H, s);
         e != hipSuccess)
       return e;
   }
-  hipLaunchKernelGGL(query_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
+  const bool dec = a.gamma != nullptr;
+  if (dec) hipLaunchKernelGGL(query_pass_kernel<1>, dim3(grid), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL(query_pass_kernel<0>, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nseg > 1) {
-    hipLaunchKernelGGL(key_state_kernel, dim3(grid), dim3(NTHR), 0, s, p);
+    if (dec) hipLaunchKernelGGL(key_state_kernel<1>, dim3(grid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL(key_state_kernel<0>, dim3(grid), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(key_pass_kernel, dim3(grid), dim3(NTHR), 0, s, p);
+  if (dec) hipLaunchKernelGGL(key_pass_kernel<1>, dim3(grid), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL(key_pass_kernel<0>, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nslice > 1) {
     // with several segments the suffix-state pass has summed dq

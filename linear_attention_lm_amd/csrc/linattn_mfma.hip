@@ -164,15 +164,9 @@ struct Params {
   int nrec;            // state-only pass: segments per head it covers (0: nseg - 1)
 };
 
-// Decayed variant: log2 of the head's decay factor, and gamma^d from it.
+// Decayed variant: log2 of the head's decay factor (gamma^d = gpow(lg, d)).
 __device__ __forceinline__ float decay_lg2(const Params& p, size_t bh) {
   return decay_lg2_clamped(__log2f(p.gamma[bh % p.H]));
-}
-__device__ __forceinline__ float gpow(float lg, float d) { return __builtin_amdgcn_exp2f(lg * d); }
-// sum_{d < n} gamma^d, through expm1 so that gamma near 1 keeps its precision
-__device__ __forceinline__ float gsum_pow(float lg, int n) {
-  const float ln = lg * 0.69314718055994531f;
-  return ln == 0.f ? (float)n : expm1f(ln * (float)n) / expm1f(ln);
 }
 // a value that every lane holds alike, moved to a scalar register
 __device__ __forceinline__ float uniform(float x) {
@@ -1497,28 +1491,32 @@ static hipError_t launch_nt(const LinattnArgs& a, float* y_swa, int window, floa
 // State-only pass on its own (zero initial state): records [BH][nseg][NF + 1][dv]
 // and [BH][nseg][NF + 1] at ws / wsz, record s + 1 = the compact increment of
 // segment s for s < nrec (nrec <= nseg - 1), slot values
-// sum_t [k_a | k_a^2 | k_a k_b] v_t.
+// sum_t [k_a | k_a^2 | k_a k_b] v_t (decayed: weights gamma^(end - 1 - t) over
+// the segment's positions t).
 template <int NT>
 static hipError_t launch_state_records_nt(const void* k, const void* v, float* ws, int BH, int L, int nseg,
-                                          int seg_chunks, int nrec, hipStream_t s) {
+                                          int seg_chunks, int nrec, const float* gamma, int H, hipStream_t s) {
   Params p{};
   p.k = (const bf16_t*)k; p.v = (const bf16_t*)v;
   p.L = L; p.nseg = nseg; p.seg_chunks = seg_chunks; p.nrec = nrec;
   p.ws = ws;
   p.wsz = ws + (size_t)BH * nseg * (NF + 1) * (16 * NT);
-  hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
+  p.gamma = gamma;
+  p.H = H;
+  if (gamma) hipLaunchKernelGGL((linattn_state_kernel<NT, 1>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_linattn_state_records(const void* k, const void* v, float* ws, int BH, int L, int dv, int nseg,
-                                        int seg_chunks, int nrec, hipStream_t s) {
+                                        int seg_chunks, int nrec, const float* gamma, int H, hipStream_t s) {
   if (nseg < 2 || nrec < 1) return hipSuccess;
   if (nrec > nseg - 1) return hipErrorInvalidValue;
   switch (dv) {
-    case 32: return launch_state_records_nt<2>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
-    case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
-    case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
-    case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, nrec, s);
+    case 32: return launch_state_records_nt<2>(k, v, ws, BH, L, nseg, seg_chunks, nrec, gamma, H, s);
+    case 64: return launch_state_records_nt<4>(k, v, ws, BH, L, nseg, seg_chunks, nrec, gamma, H, s);
+    case 96: return launch_state_records_nt<6>(k, v, ws, BH, L, nseg, seg_chunks, nrec, gamma, H, s);
+    case 128: return launch_state_records_nt<8>(k, v, ws, BH, L, nseg, seg_chunks, nrec, gamma, H, s);
   }
   return hipErrorInvalidValue;
 }

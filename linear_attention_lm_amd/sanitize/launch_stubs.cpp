@@ -14,7 +14,8 @@ hipError_t none() { return hipErrorNotSupported; }
 hipError_t launch_linattn_valu(const LinattnArgs&, bool, hipStream_t) { return none(); }
 hipError_t launch_linattn_mfma(const LinattnArgs&, hipStream_t) { return none(); }
 hipError_t launch_linattn_decay_mfma(const LinattnArgs&, hipStream_t) { return none(); }
-hipError_t launch_linattn_state_records(const void*, const void*, float*, int, int, int, int, int, int, hipStream_t) {
+hipError_t launch_linattn_state_records(const void*, const void*, float*, int, int, int, int, int, int, const float*,
+                                        int, hipStream_t) {
   return none();
 }
 hipError_t launch_layer_mfma(const LinattnArgs&, float*, int, float, hipStream_t) { return none(); }

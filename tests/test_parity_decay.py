@@ -307,3 +307,52 @@ def test_decay_bwd_and_decode_gamma_clamped(based):
         assert rowinf_rel(ya[0][:, 0], vs[s][:, 0].double().numpy()) <= tol
     assert torch.equal(sa.S, sb.S) and torch.equal(sa.z, sb.z)
     report("gamma range: backward and decode, raw = clamped bit for bit", 0.0, tol)
+
+
+@pytest.mark.parametrize("L,dv", [(2500, 64), (1500, 96), (700, 128)])
+def test_decay_bwd_matrix_core_segments(based, L, dv):
+    """bf16 decayed backward on the matrix-core passes over several segments
+    per head (decayed forward records, decayed suffix records) with a ragged
+    last chunk, d_v 64 / 96 / 128: heads with decays 1, 0.75, 0.5 and 0.875
+    against the oracle, per row with the floor."""
+    from parity_util import row_rel_floor
+    cfg = SMALL.replace(B=1, L=L, dv=dv, name=f"decay bwd segments L{L} dv{dv}")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say(cfg.name)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    grads = based.linattn_decay_bwd(qd, kd, vd, gd, y, dy.to(DEV))
+    torch.cuda.synchronize()
+    for h in (0, 1, 2, 7):
+        refs = O.linattn_decay_bwd(q[0, h][None], k[0, h][None], v[0, h][None], g[h:h + 1].numpy(), dy[0, h][None])
+        for name, gr, r in zip(("dq", "dk", "dv"), grads, refs):
+            zero = 1 if name == "dq" else 0
+            err = row_rel_floor(gr[0, h, zero:][None], r[:, zero:], FLOOR[q.dtype])
+            report(f"{cfg.name} head {h} (gamma {float(g[h])}) {name}", err, TOL[q.dtype])
+            assert err <= TOL[q.dtype], (h, name, err)
+
+
+def test_decay_bwd_direct_form_with_small_workspace(based):
+    """A workspace of 2 B H L 4 bytes selects the direct form for bf16 as
+    well; both forms match the oracle and each other."""
+    from parity_util import row_rel_floor
+    cfg = SMALL.replace(B=1, L=300, name="decay bwd direct vs matrix core")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say(cfg.name)
+    qd, kd, vd, gd, dyd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), dy.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    small = torch.empty(2 * cfg.B * cfg.H * cfg.L * 4, dtype=torch.uint8, device=DEV)
+    direct = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd, workspace=small)
+    mfma = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd)
+    torch.cuda.synchronize()
+    refs = O.linattn_decay_bwd(q, k, v, g.numpy(), dy)
+    for name, a, b, r in zip(("dq", "dk", "dv"), direct, mfma, refs):
+        zero = 1 if name == "dq" else 0
+        for label, gr in (("direct", a), ("matrix core", b)):
+            err = row_rel_floor(gr[..., zero:, :], r[..., zero:, :], FLOOR[q.dtype])
+            report(f"{cfg.name}: {label} {name}", err, TOL[q.dtype])
+            assert err <= TOL[q.dtype], (label, name, err)
