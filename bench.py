@@ -390,11 +390,24 @@ def bench_decay(lal, cfg, steps, warmup, nbuf=8, settle=0):
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) / steps * 1e3
     nbytes = lin_bytes(dv) * B * H * L
+    # the decayed backward on the same inputs, a seeded dy and the forward's y
+    dy = synth.upstream_grad(cfg, 0).to("cuda")
+    ys = [lal.linattn_decay_fwd(*sets[i], g) for i in range(nbuf)]
+    bws = torch.empty(max(1, lal.linattn_bwd_workspace_bytes(B, H, L, dv)), dtype=torch.uint8, device="cuda")
+    gq = torch.empty(B, H, L, 16, device="cuda")
+    gk = torch.empty_like(gq)
+    gv = torch.empty(B, H, L, dv, device="cuda")
+    bwd = lambda i: lal.linattn_decay_bwd(*sets[i % nbuf], g, ys[i % nbuf], dy, dq=gq, dk=gk, dv=gv, workspace=bws)
+    for i in range(settle + warmup):
+        bwd(i)
+    bus = time_loop(bwd, steps) * 1e3
+    b1 = bwd_bytes(dv) * B * H * L
     return {"workload": cfg.name + " decayed linear attention", "B": B, "H": H, "L": L, "d_v": dv,
             "us_per_call": us, "tokens_per_s": B * L / (us * 1e-6), "bytes_per_call": nbytes,
             "hbm_gbs": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "alg_tflops": lin_flops(dv) * B * H * L / (us * 1e-6) / 1e12,
-            "traffic_bytes_per_call": load_traffic("decay")}
+            "traffic_bytes_per_call": load_traffic("decay"),
+            "bwd_us_per_call": bus, "bwd_bytes_per_call": b1, "bwd_hbm_gbs": b1 / (bus * 1e-6) / 1e9}
 
 
 def bench_decode(lal, cfg, warmup=5, decay=False, compact=False):
@@ -827,7 +840,8 @@ def main():
               flush=True)
         decay = bench_decay(lal, cfg, args.steps, args.warmup, settle=args.settle)
         print(f"[bench] {cfg.name} decayed linear attention: {decay['us_per_call']:.1f} us/call "
-              f"({decay['hbm_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+              f"({decay['hbm_gbs']:.0f} GB/s), backward {decay['bwd_us_per_call']:.1f} us/call", file=sys.stderr,
+              flush=True)
         decode = bench_decode(lal, synth.DECODE_CONFIG)
         decode["traffic_bytes_per_step"] = load_traffic("decode")
         print(f"[bench] decode: {decode['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
