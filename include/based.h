@@ -222,8 +222,8 @@ int based_linattn_bwd(const void* q, const void* k, const void* v, const float* 
  * based_linattn_bwd_workspace_bytes for the shape, the matrix-core passes of
  * based_linattn_bwd with the decay (the carried states decay per position and
  * per chunk, the in-chunk terms carry gamma^(i-j); the same numerics).
- * Otherwise (fp32, other widths, or the smaller workspace) the direct form:
- * fp32 vector arithmetic over every (i, j <= i) pair (work quadratic in L).
+ * Otherwise (fp32, other widths, or the smaller workspace) the chunked fp32
+ * vector form of based_linattn_bwd with the same decay weights.
  * Errors as for based_linattn_bwd, and BASED_ERR_NULL for a null gamma; gamma
  * must not overlap an output or the workspace.
  */

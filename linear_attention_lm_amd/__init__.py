@@ -326,7 +326,7 @@ def linattn_decay_bwd(q, k, v, gamma, y, dy, *, dq=None, dk=None, dv=None, works
     gradient dy.  The default workspace is
     :func:`linattn_bwd_workspace_bytes` (bf16 with d_v in {32, 64, 96, 128}
     then takes the matrix-core passes); one of 2*B*H*L*4 bytes selects the
-    direct form."""
+    fp32 vector form."""
     _check_bwd_args(q, k, v, y, dy)
     B, H, L, dk_ = q.shape
     dvw = v.shape[-1]

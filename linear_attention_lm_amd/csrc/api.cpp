@@ -295,7 +295,7 @@ BASED_API int based_linattn_decay_bwd(const void* q, const void* k, const void* 
   if (!gamma) return BASED_ERR_NULL;
   if (L == 0) return BASED_OK;
   if (int st = check_bwd(q, k, v, y, dy, dq, dk, dv, B, H, L, d_v, dtype); st != BASED_OK) return st;
-  // the direct form: den and h per position
+  // the vector form: den and h per position (the matrix-core form takes more, see the dispatch)
   const size_t BH = (size_t)B * H, need = 2 * BH * L * sizeof(float);
   if (!workspace || workspace_bytes < need) return BASED_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);

@@ -78,6 +78,41 @@ __device__ __forceinline__ float gsum_pow(float lg, int n) {
 // Index of the unordered pair (a <= b) in the row-major upper triangle.
 __host__ __device__ constexpr int pair_index(int a, int b) { return a * DK - a * (a - 1) / 2 + (b - a); }
 
+// Compact feature f (< padded row count) of a query or key, as
+// c0 + x_a (c1 + c2 x_b): the constant feature 1, the linear ones x_a, the
+// pairs x_a x_b (a <= b) -- weight 1/2 on the diagonal for a query (QUERY:
+// phi'(q), so that phi'(q).psi'(k) = 1 + q.k + (q.k)^2 / 2), 1 for a key
+// (psi'(k)) -- and zero past NCOMPACT.  The fp32 kernels fill the same
+// features of every chunk from each thread, so they work out the
+// coefficients once.
+struct FeatureCoef {
+  float c0, c1, c2;
+  int a, b;
+};
+template <bool QUERY>
+__device__ __forceinline__ FeatureCoef feature_coef(int f) {
+  FeatureCoef r{0.f, 0.f, 0.f, 0, 0};
+  if (f == 0) {
+    r.c0 = 1.f;
+  } else if (f < 1 + DK) {
+    r.c1 = 1.f;
+    r.a = f - 1;
+  } else if (f < NCOMPACT) {
+    int pi = f - 1 - DK, a = 0;
+    while (pi >= DK - a) {  // row a of the upper triangle holds DK - a pairs
+      pi -= DK - a;
+      ++a;
+    }
+    r.a = a;
+    r.b = a + pi;
+    r.c2 = QUERY && r.a == r.b ? 0.5f : 1.f;
+  }
+  return r;
+}
+__device__ __forceinline__ float feature(const FeatureCoef& fc, const float* x) {
+  return fc.c0 + x[fc.a] * __builtin_fmaf(fc.c2, x[fc.b], fc.c1);
+}
+
 constexpr float SQRT2 = 1.41421356237309505f;
 constexpr float INV_SQRT2 = 0.70710678118654752f;
 

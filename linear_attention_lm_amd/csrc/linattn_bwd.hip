@@ -1,5 +1,5 @@
-// Causal Taylor linear attention, backward: the direct form (fp32 vector
-// arithmetic, any input dtype and d_v).
+// Causal Taylor linear attention, backward on the vector ALUs in fp32 (any
+// input dtype, d_v in {16, ..., 128}), chunked like the forward.
 //
 // Gradients of y_i = sum_{j<=i} K_ij v_j / den_i, K_ij = 1 + x + x^2/2 with
 // x = q_i.k_j and den_i = sum_{j<=i} K_ij (blog post "Базированная модель,
@@ -8,212 +8,479 @@
 // h_i = -(dy_i . y_i) / den_i:
 //   dK_ij = g_i . v_j + h_i,  c_ij = dK_ij (1 + x_ij)          (j <= i)
 //   dq_i = sum_{j<=i} c_ij k_j,  dk_j = sum_{i>=j} c_ij q_i,  dv_j = sum_{i>=j} K_ij g_i.
+// In compact features, K_ij = phi'(q_i) . psi'(k_j) (phi' weighs the square
+// pairs 1/2, see FeatureCoef), and the earlier (later) chunks enter through
+// states:
+//   query pass, chunks in order, S = sum_j psi'(k_j) v_j^T, z = sum_j psi'(k_j):
+//     den_i = phi'(q_i).z + in-chunk;  dq_i = J_phi'(q_i)^T (S g_i + z h_i) + in-chunk;
+//   key pass, chunks in reverse, R = sum_i phi'(q_i) g_i^T, r = sum_i phi'(q_i) h_i:
+//     dv_j = R^T psi'(k_j) + in-chunk;  dk_j = J_psi'(k_j)^T (R v_j + r) + in-chunk.
+// (The constant feature is row 0 of every state: z's counts the earlier
+// positions, R's sums their g.)
+// The Jacobian contractions in compact form: dq_a = U_a + sum_b U_(ab) q_b
+// (U = S g + z h; U_(ab) the pair's entry, the diagonal included once) and
+// dk_a = U'_a + sum_{b != a} U'_(ab) k_b + 2 U'_(aa) k_a.
+// The query pass writes den and h per position to the workspace for the
+// key pass.  One workgroup of 512 threads per (batch, head) and pass; chunks
+// of 32 positions; states, features and the in-chunk weights in LDS.
 //
-// Two kernels, each sweeping 64-row tiles of the other side through LDS:
-// per query (den, then g, h and dq; den and h go to the workspace), then per
-// key (dk, dv).  Work is quadratic in L: this form serves fp32 inputs and
-// widths the matrix-core passes do not take.
+// DEC: the decayed variant (a per-head gamma on the state; the kernel entry
+// of (i, j) weighs gamma^(i-j)): the query pass's state reaches position p
+// of a chunk times gamma^(p+1) and decays as in the forward; the key pass
+// keeps R and r relative to the start of the next chunk, read by key p
+// times gamma^(C-p) and updated as R <- gamma^C R + sum_p gamma^p phi'(q_p) g_p^T.
 #include "based_device.h"
 #include "launchers.h"
 
 namespace based {
 namespace {
 
-constexpr int TB = 64;  // rows per tile and threads per workgroup
+constexpr int C = 32;        // positions per chunk
+constexpr int NT = 512;      // threads per workgroup
+constexpr int NFP = 160;     // compact feature rows, padded (NCOMPACT used)
+constexpr int FT = C + 4;    // row stride of feature-major features ([NFP][FT])
+constexpr int FU = C + 1;    // row stride of the per-position contractions ([NFP][FU])
+constexpr int FK = NFP + 4;  // row stride of row-major features ([C][FK])
+constexpr int FBS = 10;      // feature rows per thread in (features x positions) products
+static_assert(NFP * FT >= C * FK && NFP * FT >= NFP * FU, "one buffer serves every feature layout");
+static_assert((NFP / FBS) * C == NT, "features x positions: 16 blocks of 10 rows x 32 positions");
 
-__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 ld4(const bf16_t* p) {
-  const uint2 t = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
-                     __uint_as_float(t.y & 0xffff0000u));
+// Work split of the (positions x value columns) products: 32 positions x 16
+// column blocks of CPT; the state updates (features x value columns): 32
+// feature blocks of FPT x the same column blocks.
+template <int DV>
+struct Split {
+  static constexpr int NCB = 16, CPT = DV / NCB, FPT = NFP / 32;
+  static_assert(DV % NCB == 0, "d_v in multiples of 16");
+};
+
+// Compact feature index of the pair (a, b) (either order).
+__device__ __forceinline__ int pair_feature(int a, int b) {
+  return 1 + DK + (a < b ? pair_index(a, b) : pair_index(b, a));
 }
 
-// rows [r0, r0 + TB) of a [L, D] tensor into an fp32 LDS tile (zeros past L)
-template <int D, int STRIDE, typename T>
-__device__ __forceinline__ void stage(float (*dst)[STRIDE], const T* src, int r0, int L) {
-  constexpr int G = D / 4;
-  for (int e = threadIdx.x; e < TB * G; e += blockDim.x) {
-    const int r = e / G, c = 4 * (e % G);
-    const float4 x = r0 + r < L ? ld4(src + (size_t)(r0 + r) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    dst[r][c] = x.x; dst[r][c + 1] = x.y; dst[r][c + 2] = x.z; dst[r][c + 3] = x.w;
+// Feature fills: item u = tid + NT m (u < 2 NFP) is feature u / 2 over the
+// chunk rows (u % 2) C/2 .. + C/2 - 1; a thread keeps its items' coefficients.
+struct FillItem {
+  FeatureCoef fq, fk;
+  int f, r0;
+};
+__device__ __forceinline__ FillItem fill_item(int tid) {
+  FillItem it;
+  it.f = tid < 2 * NFP ? tid / 2 : -1;
+  it.r0 = (tid % 2) * (C / 2);
+  it.fq = feature_coef<true>(it.f < 0 ? 0 : it.f);
+  it.fk = feature_coef<false>(it.f < 0 ? 0 : it.f);
+  return it;
+}
+
+// rows t0 .. t0 + C - 1 of q and k (zero from row n on) into fp32 LDS rows
+template <typename T>
+__device__ __forceinline__ void load_qk(float (*qs)[DK + 1], float (*ks)[DK + 1], const T* qb, const T* kb, int t0,
+                                        int n) {
+  const int tid = threadIdx.x, j = tid / DK, d = tid % DK;  // C * DK == NT
+  const bool ok = j < n;
+  qs[j][d] = ok ? to_f32(qb[(size_t)(t0 + j) * DK + d]) : 0.f;
+  ks[j][d] = ok ? to_f32(kb[(size_t)(t0 + j) * DK + d]) : 0.f;
+}
+
+template <typename T, int DV>
+__device__ __forceinline__ void load_v(float (*vs)[DV], const T* vb, int t0, int n) {
+  for (int e = threadIdx.x; e < C * DV; e += NT) {
+    const int j = e / DV, c = e % DV;
+    vs[j][c] = j < n ? to_f32(vb[(size_t)(t0 + j) * DV + c]) : 0.f;
   }
 }
 
-// Per query i (one thread): den_i, then g_i (kept in LDS), h_i and dq_i.
+// Sum over the 16 consecutive lanes of a row group (every lane gets it).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ------------------------------------------------------------- query pass
 template <typename T, int DV, int DEC>
-__global__ __launch_bounds__(TB) void bwd_query_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(NT) void bwd_query_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const T* __restrict__ v, const float* __restrict__ y,
                                                        const float* __restrict__ dy, float* __restrict__ gq,
                                                        float* __restrict__ den_out, float* __restrict__ h_out, int L,
-                                                       int nblk, const float* __restrict__ gamma, int H) {
-  __shared__ float ks[TB][DK + 1];
-  __shared__ float vs[TB][DV + 1];
-  __shared__ float gs[TB][DV + 1];
-  const int t = threadIdx.x;
-  const size_t bh = blockIdx.x / nblk;
-  const int i0 = (blockIdx.x % nblk) * TB, i = i0 + t;
-  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;  // decay weight of (i, j): 2^(lg (i - j))
-  const T* kh = k + bh * L * DK;
-  const T* vh = v + bh * (size_t)L * DV;
-  float qi[DK];
-  if (i < L) {
-    load_row<DK>(q + (bh * L + i) * DK, qi);
-  } else {
-#pragma unroll
-    for (int e = 0; e < DK; ++e) qi[e] = 0.f;
-  }
-  const int jend = min(L, i0 + TB);  // keys this block's queries see
+                                                       const float* __restrict__ gamma, int H) {
+  using SP = Split<DV>;
+  constexpr int CPT = SP::CPT, FPT = SP::FPT;
+  __shared__ float Ts[NFP][DV];    // S (rows NCOMPACT.. zero)
+  __shared__ float zs[NFP];
+  __shared__ float fbuf[NFP * FT];  // phi'(q) [NFP][FT]; then U [NFP][FU]; then psi'(k) [C][FK]
+  __shared__ float qs[C][DK + 1];
+  __shared__ float ks[C][DK + 1];
+  __shared__ float vs[C][DV];
+  __shared__ float gs[C][DV + 1];   // dy rows, then g rows
+  __shared__ float wt[C][C + 1];    // [key][query]: K_ij (masked, decayed), then c_ij
+  __shared__ float xt[C][C + 1];    // [key][query]: 1 + x_ij
+  __shared__ float hs[C];
 
-  // den_i = sum_{j<=i} K_ij
-  float den = 0.f;
-  for (int j0 = 0; j0 < jend; j0 += TB) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
+  const T* qb = q + (size_t)bh * L * DK;
+  const T* kb = k + (size_t)bh * L * DK;
+  const T* vb = v + (size_t)bh * L * DV;
+  const float* yb = y + (size_t)bh * L * DV;
+  const float* dyb = dy + (size_t)bh * L * DV;
+  const FillItem it = fill_item(tid);
+  // (positions x value columns) and (features x value columns) tiles
+  const int pr = tid / SP::NCB, cb = tid % SP::NCB, c0 = cb * CPT, f0u = pr * FPT;
+  // (features x positions) tiles
+  const int fb = tid / C, pc = tid % C;
+
+  for (int e = tid; e < NFP * DV; e += NT) Ts[e / DV][e % DV] = 0.f;
+  for (int f = tid; f < NFP; f += NT) zs[f] = 0.f;
+
+  for (int t0 = 0; t0 < L; t0 += C) {
+    const int n = min(C, L - t0);
+    __syncthreads();  // the previous chunk's update done
+    load_qk(qs, ks, qb, kb, t0, n);
+    load_v<T, DV>(vs, vb, t0, n);
+    float dys;  // dy . y of row pr over the row group's 16 lanes
+    {
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const bool ok = pr < n;
+        const float a = ok ? dyb[(size_t)(t0 + pr) * DV + c0 + c] : 0.f;
+        const float b = ok ? yb[(size_t)(t0 + pr) * DV + c0 + c] : 0.f;
+        gs[pr][c0 + c] = a;
+        part = __builtin_fmaf(a, b, part);
+      }
+      dys = sum16(part);
+    }
     __syncthreads();
-    stage<DK, DK + 1>(ks, kh, j0, L);
-    __syncthreads();
-    const int n = min(TB, i + 1 - j0);
-    for (int jj = 0; jj < n; ++jj) {
+
+    // ---- query features; in-chunk weights K_ij and 1 + x_ij
+    if (it.f >= 0)
+      for (int i = it.r0; i < it.r0 + C / 2; ++i) fbuf[it.f * FT + i] = feature(it.fq, qs[i]);
+    for (int e = tid; e < C * C; e += NT) {
+      const int j = e / C, i = e % C;
       float x = 0.f;
 #pragma unroll
-      for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qi[e], ks[jj][e], x);
-      const float K = 1.f + x + 0.5f * x * x;
-      den += DEC ? K * exp2f(lg * (float)(i - j0 - jj)) : K;
+      for (int d = 0; d < DK; ++d) x = __builtin_fmaf(qs[i][d], ks[j][d], x);
+      float w = j <= i && j < n ? 1.f + x + 0.5f * x * x : 0.f;
+      if (DEC && j <= i) w *= gpow(lg, (float)(i - j));
+      wt[j][i] = w;
+      xt[j][i] = 1.f + x;
     }
-  }
-  // g_i, h_i
-  float h = 0.f;
-  if (i < L) {
-    const float rden = 1.f / den;
-    float dot = 0.f;
-    for (int c = 0; c < DV; c += 4) {
-      const float4 a = ld4(dy + (bh * L + i) * DV + c), b = ld4(y + (bh * L + i) * DV + c);
-      dot += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-      gs[t][c] = a.x * rden; gs[t][c + 1] = a.y * rden; gs[t][c + 2] = a.z * rden; gs[t][c + 3] = a.w * rden;
-    }
-    h = -dot * rden;
-    den_out[bh * L + i] = den;
-    h_out[bh * L + i] = h;
-  }
-  // dq_i = sum_{j<=i} (g_i . v_j + h_i)(1 + x_ij) k_j
-  float acc[DK];
-#pragma unroll
-  for (int e = 0; e < DK; ++e) acc[e] = 0.f;
-  for (int j0 = 0; j0 < jend; j0 += TB) {
     __syncthreads();
-    stage<DK, DK + 1>(ks, kh, j0, L);
-    stage<DV, DV + 1>(vs, vh, j0, L);
+
+    // ---- den, g, h of position pr (16 lanes per position)
+    const float cf = DEC ? gpow(lg, (float)(pr + 1)) : 1.f;  // the carried state's weight at pr
+    {
+      float part = 0.f, own = 0.f;
+      for (int f = cb; f < NCOMPACT; f += SP::NCB) part = __builtin_fmaf(fbuf[f * FT + pr], zs[f], part);
+      for (int j = cb; j < C; j += SP::NCB) own += wt[j][pr];
+      const float den = sum16(cf * part + own);  // (z's constant row counts the earlier positions)
+      const float rden = 1.f / den;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) gs[pr][c0 + c] *= rden;
+      const float h = -dys * rden;
+      if (cb == 0) {
+        hs[pr] = h;
+        if (pr < n) {
+          den_out[(size_t)bh * L + t0 + pr] = den;
+          h_out[(size_t)bh * L + t0 + pr] = h;
+        }
+      }
+    }
     __syncthreads();
-    const int n = min(TB, i + 1 - j0);
-    for (int jj = 0; jj < n; ++jj) {
-      float x = 0.f;
+
+    // ---- U = cf (S g + z h) over the chunk's positions, into fbuf [NFP][FU];
+    // in-chunk c_ij = (g_i . v_j + h_i)(1 + x_ij), masked and decayed, into wt
+    {
+      float u[FBS];
 #pragma unroll
-      for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qi[e], ks[jj][e], x);
-      float gv = h;
-      for (int c = 0; c < DV; ++c) gv = __builtin_fmaf(gs[t][c], vs[jj][c], gv);
-      float cij = gv * (1.f + x);
-      if (DEC) cij *= exp2f(lg * (float)(i - j0 - jj));
+      for (int i = 0; i < FBS; ++i) u[i] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < DV; ++c) {
+        const float gv = gs[pc][c];
 #pragma unroll
-      for (int e = 0; e < DK; ++e) acc[e] = __builtin_fmaf(cij, ks[jj][e], acc[e]);
+        for (int i = 0; i < FBS; ++i) u[i] = __builtin_fmaf(Ts[fb * FBS + i][c], gv, u[i]);
+      }
+      const float cfp = DEC ? gpow(lg, (float)(pc + 1)) : 1.f, hp = hs[pc];
+      float cw[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int e = tid + NT * m, j = e / C, i = e % C;
+        float d = hs[i];
+#pragma unroll 8
+        for (int c = 0; c < DV; ++c) d = __builtin_fmaf(gs[i][c], vs[j][c], d);
+        float w = j <= i && j < n ? d * xt[j][i] : 0.f;
+        if (DEC && j <= i) w *= gpow(lg, (float)(i - j));
+        cw[m] = w;
+      }
+      __syncthreads();  // every read of phi'(q), wt and the K weights done
+#pragma unroll
+      for (int i = 0; i < FBS; ++i) {
+        const int f = fb * FBS + i;
+        fbuf[f * FU + pc] = cfp * __builtin_fmaf(zs[f], hp, u[i]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int e = tid + NT * m;
+        wt[e / C][e % C] = cw[m];
+      }
+    }
+    __syncthreads();
+
+    // ---- dq_a of position pr, a = cb: the state's share through the
+    // Jacobian, plus sum_j c_ij k_j[a]
+    {
+      const int a = cb;
+      float dq = fbuf[(1 + a) * FU + pr];
+#pragma unroll
+      for (int b = 0; b < DK; ++b) dq = __builtin_fmaf(fbuf[pair_feature(a, b) * FU + pr], qs[pr][b], dq);
+      for (int j = 0; j < C; ++j) dq = __builtin_fmaf(wt[j][pr], ks[j][a], dq);
+      if (pr < n) gq[((size_t)bh * L + t0 + pr) * DK + a] = dq;
+    }
+    __syncthreads();  // every read of U done
+
+    // ---- key features (decayed: times gamma^(n-1-j)); update S, z
+    if (it.f >= 0)
+      for (int j = it.r0; j < it.r0 + C / 2; ++j) {
+        float x = 0.f;
+        if (j < n) {
+          x = feature(it.fk, ks[j]);
+          if (DEC) x *= gpow(lg, (float)(n - 1 - j));
+        }
+        fbuf[j * FK + it.f] = x;
+      }
+    __syncthreads();
+    {
+      float acc[FPT][CPT], za[FPT];
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        za[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[i][c] = 0.f;
+      }
+      for (int j = 0; j < n; ++j) {
+        float ps[FPT], vv[CPT];
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) ps[i] = fbuf[j * FK + f0u + i];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vv[c] = vs[j][c0 + c];
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+          za[i] += ps[i];
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[i][c] = __builtin_fmaf(ps[i], vv[c], acc[i][c]);
+        }
+      }
+      const float gn = DEC ? gpow(lg, (float)n) : 1.f;
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Ts[f0u + i][c0 + c] = __builtin_fmaf(gn, Ts[f0u + i][c0 + c], acc[i][c]);
+        if (cb == 0) zs[f0u + i] = __builtin_fmaf(gn, zs[f0u + i], za[i]);
+      }
     }
   }
-  if (i < L)
-#pragma unroll
-    for (int e = 0; e < DK; e += 4)
-      *reinterpret_cast<float4*>(gq + (bh * L + i) * DK + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
 }
 
-// Per key j (one thread): dk_j and dv_j over the queries i >= j.
+// --------------------------------------------------------------- key pass
 template <typename T, int DV, int DEC>
-__global__ __launch_bounds__(TB) void bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(NT) void bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const float* __restrict__ dy,
                                                      const float* __restrict__ den_in, const float* __restrict__ h_in,
-                                                     float* __restrict__ gk, float* __restrict__ gv, int L, int nblk,
+                                                     float* __restrict__ gk, float* __restrict__ gv, int L,
                                                      const float* __restrict__ gamma, int H) {
-  __shared__ float qs[TB][DK + 1];
-  __shared__ float gs[TB][DV + 1];
-  __shared__ float hs[TB];
-  __shared__ float vj[TB][DV + 1];
-  __shared__ float dvj[TB][DV + 1];
-  const int t = threadIdx.x;
-  const size_t bh = blockIdx.x / nblk;
-  const int j0 = (blockIdx.x % nblk) * TB, j = j0 + t;
+  using SP = Split<DV>;
+  constexpr int CPT = SP::CPT, FPT = SP::FPT;
+  __shared__ float Rs[NFP][DV];    // R (rows NCOMPACT.. zero)
+  __shared__ float rs[NFP];
+  __shared__ float fbuf[NFP * FT];  // psi'(k) [NFP][FT]; then U' [NFP][FU]; then phi'(q) [C][FK]
+  __shared__ float qs[C][DK + 1];
+  __shared__ float ks[C][DK + 1];
+  __shared__ float vs[C][DV];
+  __shared__ float gs[C][DV + 1];   // g rows
+  __shared__ float wt[C][C + 1];    // [key][query]: K_ij (masked, decayed)
+  __shared__ float ct[C][C + 1];    // [key][query]: c_ij (masked, decayed)
+  __shared__ float hs[C];
+
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
-  const T* qh = q + bh * L * DK;
-  float kj[DK];
-  if (j < L) {
-    load_row<DK>(k + (bh * L + j) * DK, kj);
-  } else {
+  const T* qb = q + (size_t)bh * L * DK;
+  const T* kb = k + (size_t)bh * L * DK;
+  const T* vb = v + (size_t)bh * L * DV;
+  const float* dyb = dy + (size_t)bh * L * DV;
+  const FillItem it = fill_item(tid);
+  const int pr = tid / SP::NCB, cb = tid % SP::NCB, c0 = cb * CPT, f0u = pr * FPT;
+  const int fb = tid / C, pc = tid % C;
+  const float gC = DEC ? gpow(lg, (float)C) : 1.f;
+
+  for (int e = tid; e < NFP * DV; e += NT) Rs[e / DV][e % DV] = 0.f;
+  for (int f = tid; f < NFP; f += NT) rs[f] = 0.f;
+
+  const int last = ((L - 1) / C) * C;
+  for (int t0 = last; t0 >= 0; t0 -= C) {
+    const int n = min(C, L - t0);
+    __syncthreads();  // the previous chunk's update done
+    load_qk(qs, ks, qb, kb, t0, n);
+    load_v<T, DV>(vs, vb, t0, n);
+    {
+      const bool ok = pr < n;
+      const float rden = ok ? 1.f / den_in[(size_t)bh * L + t0 + pr] : 0.f;
 #pragma unroll
-    for (int e = 0; e < DK; ++e) kj[e] = 0.f;
-  }
-  stage<DV, DV + 1>(vj, v + bh * (size_t)L * DV, j0, L);
-  for (int c = 0; c < DV; ++c) dvj[t][c] = 0.f;
-  float acc[DK];
-#pragma unroll
-  for (int e = 0; e < DK; ++e) acc[e] = 0.f;
-  for (int i0 = j0; i0 < L; i0 += TB) {
-    __syncthreads();
-    stage<DK, DK + 1>(qs, qh, i0, L);
-    for (int e = t; e < TB * DV; e += TB) {
-      const int r = e / DV, c = e % DV, i = i0 + r;
-      gs[r][c] = i < L ? dy[(bh * L + i) * DV + c] / den_in[bh * L + i] : 0.f;
+      for (int c = 0; c < CPT; ++c) gs[pr][c0 + c] = ok ? dyb[(size_t)(t0 + pr) * DV + c0 + c] * rden : 0.f;
+      if (cb == 0) hs[pr] = ok ? h_in[(size_t)bh * L + t0 + pr] : 0.f;
     }
-    hs[t] = i0 + t < L ? h_in[bh * L + i0 + t] : 0.f;
     __syncthreads();
-    const int n = min(TB, L - i0);
-    for (int ii = max(0, j - i0); ii < n; ++ii) {
+
+    // ---- key features; in-chunk K_ij and c_ij
+    if (it.f >= 0)
+      for (int j = it.r0; j < it.r0 + C / 2; ++j) fbuf[it.f * FT + j] = feature(it.fk, ks[j]);
+    for (int e = tid; e < C * C; e += NT) {
+      const int j = e / C, i = e % C;
+      const bool keep = j <= i && i < n;
       float x = 0.f;
 #pragma unroll
-      for (int e = 0; e < DK; ++e) x = __builtin_fmaf(qs[ii][e], kj[e], x);
-      const float wd = DEC ? exp2f(lg * (float)(i0 + ii - j)) : 1.f;
-      const float K = (1.f + x + 0.5f * x * x) * wd;
-      float gvv = hs[ii];
-      for (int c = 0; c < DV; ++c) {
-        gvv = __builtin_fmaf(gs[ii][c], vj[t][c], gvv);
-        dvj[t][c] = __builtin_fmaf(K, gs[ii][c], dvj[t][c]);
-      }
-      const float cij = gvv * (1.f + x) * wd;
-#pragma unroll
-      for (int e = 0; e < DK; ++e) acc[e] = __builtin_fmaf(cij, qs[ii][e], acc[e]);
+      for (int d = 0; d < DK; ++d) x = __builtin_fmaf(qs[i][d], ks[j][d], x);
+      float d = hs[i];
+#pragma unroll 8
+      for (int c = 0; c < DV; ++c) d = __builtin_fmaf(gs[i][c], vs[j][c], d);
+      const float wd = DEC && keep ? gpow(lg, (float)(i - j)) : 1.f;
+      wt[j][i] = keep ? wd * (1.f + x + 0.5f * x * x) : 0.f;
+      ct[j][i] = keep ? wd * d * (1.f + x) : 0.f;
     }
-  }
-  if (j < L) {
+    __syncthreads();
+
+    // ---- dv of key pr: gamma^(C-p) R^T psi'(k), plus sum_i K_ij g_i
+    const float wkey = DEC ? gpow(lg, (float)(C - pr)) : 1.f;
+    {
+      float acc[CPT];
 #pragma unroll
-    for (int e = 0; e < DK; e += 4)
-      *reinterpret_cast<float4*>(gk + (bh * L + j) * DK + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-    for (int c = 0; c < DV; ++c) gv[(bh * L + j) * DV + c] = dvj[t][c];
+      for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+      for (int f = 0; f < NCOMPACT; ++f) {
+        const float ps = fbuf[f * FT + pr];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(ps, Rs[f][c0 + c], acc[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] *= wkey;
+      for (int i = 0; i < C; ++i) {
+        const float w = wt[pr][i];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(w, gs[i][c0 + c], acc[c]);
+      }
+      if (pr < n) {
+        float* dst = gv + ((size_t)bh * L + t0 + pr) * DV + c0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) dst[c] = acc[c];
+      }
+    }
+    // ---- U' = gamma^(C-p) (R v_p + r) over the chunk's keys, into fbuf [NFP][FU]
+    {
+      float u[FBS];
+#pragma unroll
+      for (int i = 0; i < FBS; ++i) u[i] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < DV; ++c) {
+        const float vv = vs[pc][c];
+#pragma unroll
+        for (int i = 0; i < FBS; ++i) u[i] = __builtin_fmaf(Rs[fb * FBS + i][c], vv, u[i]);
+      }
+      const float wk = DEC ? gpow(lg, (float)(C - pc)) : 1.f;
+      __syncthreads();  // every read of the key features done
+#pragma unroll
+      for (int i = 0; i < FBS; ++i) {
+        const int f = fb * FBS + i;
+        fbuf[f * FU + pc] = wk * (u[i] + rs[f]);
+      }
+    }
+    __syncthreads();
+
+    // ---- dk_a of key pr, a = cb: the state's share through psi's Jacobian,
+    // plus sum_i c_ij q_i[a]
+    {
+      const int a = cb;
+      float dk = fbuf[(1 + a) * FU + pr];
+#pragma unroll
+      for (int b = 0; b < DK; ++b)
+        dk = __builtin_fmaf((b == a ? 2.f : 1.f) * fbuf[pair_feature(a, b) * FU + pr], ks[pr][b], dk);
+      for (int i = 0; i < C; ++i) dk = __builtin_fmaf(ct[pr][i], qs[i][a], dk);
+      if (pr < n) gk[((size_t)bh * L + t0 + pr) * DK + a] = dk;
+    }
+    __syncthreads();  // every read of U' done
+
+    // ---- query features (decayed: times gamma^p); R <- gamma^C R + sum_p phi'(q_p) g_p^T
+    if (it.f >= 0)
+      for (int i = it.r0; i < it.r0 + C / 2; ++i) {
+        float x = 0.f;
+        if (i < n) {
+          x = feature(it.fq, qs[i]);
+          if (DEC) x *= gpow(lg, (float)i);
+        }
+        fbuf[i * FK + it.f] = x;
+      }
+    __syncthreads();
+    {
+      float acc[FPT][CPT], ra[FPT];
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        ra[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[i][c] = 0.f;
+      }
+      for (int i = 0; i < n; ++i) {
+        float ps[FPT], gg[CPT];
+#pragma unroll
+        for (int u = 0; u < FPT; ++u) ps[u] = fbuf[i * FK + f0u + u];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) gg[c] = gs[i][c0 + c];
+        const float hv = hs[i];
+#pragma unroll
+        for (int u = 0; u < FPT; ++u) {
+          ra[u] = __builtin_fmaf(ps[u], hv, ra[u]);
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[u][c] = __builtin_fmaf(ps[u], gg[c], acc[u][c]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < FPT; ++u) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Rs[f0u + u][c0 + c] = __builtin_fmaf(gC, Rs[f0u + u][c0 + c], acc[u][c]);
+        if (cb == 0) rs[f0u + u] = __builtin_fmaf(gC, rs[f0u + u], ra[u]);
+      }
+    }
   }
 }
 
 template <typename T, int DV, int DEC>
-hipError_t launch_direct_dec(const LinattnBwdArgs& a, hipStream_t s) {
-  const int nblk = (a.L + TB - 1) / TB;
+hipError_t launch_chunked_dec(const LinattnBwdArgs& a, hipStream_t s) {
   const size_t BH = (size_t)a.B * a.H;
   float* den = (float*)a.workspace;
   float* h = den + BH * a.L;
-  hipLaunchKernelGGL((bwd_query_kernel<T, DV, DEC>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, a.y, a.dy, a.gq, den, h, a.L, nblk, a.gamma, a.H);
+  hipLaunchKernelGGL((bwd_query_kernel<T, DV, DEC>), dim3((unsigned)BH), dim3(NT), 0, s, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, a.y, a.dy, a.gq, den, h, a.L, a.gamma, a.H);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_key_kernel<T, DV, DEC>), dim3((unsigned)(BH * nblk)), dim3(TB), 0, s, (const T*)a.q,
-                     (const T*)a.k, (const T*)a.v, a.dy, den, h, a.gk, a.gv, a.L, nblk, a.gamma, a.H);
+  hipLaunchKernelGGL((bwd_key_kernel<T, DV, DEC>), dim3((unsigned)BH), dim3(NT), 0, s, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, a.dy, den, h, a.gk, a.gv, a.L, a.gamma, a.H);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
-hipError_t launch_direct(const LinattnBwdArgs& a, hipStream_t s) {
-  return a.gamma ? launch_direct_dec<T, DV, 1>(a, s) : launch_direct_dec<T, DV, 0>(a, s);
+hipError_t launch_chunked(const LinattnBwdArgs& a, hipStream_t s) {
+  return a.gamma ? launch_chunked_dec<T, DV, 1>(a, s) : launch_chunked_dec<T, DV, 0>(a, s);
 }
 
 template <typename T>
-hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
+hipError_t launch_chunked_dv(const LinattnBwdArgs& a, hipStream_t s) {
   switch (a.dv) {
-    case 16: return launch_direct<T, 16>(a, s);
-    case 32: return launch_direct<T, 32>(a, s);
-    case 48: return launch_direct<T, 48>(a, s);
-    case 64: return launch_direct<T, 64>(a, s);
-    case 80: return launch_direct<T, 80>(a, s);
-    case 96: return launch_direct<T, 96>(a, s);
-    case 112: return launch_direct<T, 112>(a, s);
-    case 128: return launch_direct<T, 128>(a, s);
+    case 16: return launch_chunked<T, 16>(a, s);
+    case 32: return launch_chunked<T, 32>(a, s);
+    case 48: return launch_chunked<T, 48>(a, s);
+    case 64: return launch_chunked<T, 64>(a, s);
+    case 80: return launch_chunked<T, 80>(a, s);
+    case 96: return launch_chunked<T, 96>(a, s);
+    case 112: return launch_chunked<T, 112>(a, s);
+    case 128: return launch_chunked<T, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -223,11 +490,11 @@ hipError_t launch_direct_dv(const LinattnBwdArgs& a, hipStream_t s) {
 hipError_t launch_linattn_bwd(const LinattnBwdArgs& a, bool bf16, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
   // the decayed variant takes the matrix-core passes when the caller's
-  // workspace holds theirs (it may be as small as the direct form's)
+  // workspace holds theirs (it may be as small as the vector form's)
   if (bf16 && linattn_bwd_mfma_supported(a.dv) &&
       (!a.gamma || a.workspace_bytes >= linattn_bwd_mfma_workspace(a.B, a.H, a.L, a.dv)))
     return launch_linattn_bwd_mfma(a, s);
-  return bf16 ? launch_direct_dv<bf16_t>(a, s) : launch_direct_dv<float>(a, s);
+  return bf16 ? launch_chunked_dv<bf16_t>(a, s) : launch_chunked_dv<float>(a, s);
 }
 
 }  // namespace based

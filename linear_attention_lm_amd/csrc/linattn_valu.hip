@@ -69,34 +69,6 @@ struct Split {
   static_assert(DV % NCB == 0 && C % NRB == 0 && NFP % NRB == 0, "tiling");
 };
 
-// Compact feature f (< NFP) as c0 + x_a (c1 + c2 x_b): the constant
-// feature 1, the linear ones x_a, the pairs x_a x_b (a <= b) -- with weight
-// 1/2 on the diagonal for a query (QUERY), 1 for a key -- and zero past
-// NCOMPACT.  A thread fills the same two features of every chunk, so it
-// works out their coefficients once.
-struct FeatureCoef {
-  float c0, c1, c2;
-  int a, b;
-};
-template <bool QUERY>
-__device__ __forceinline__ FeatureCoef feature_coef(int f) {
-  FeatureCoef r{0.f, 0.f, 0.f, 0, 0};
-  if (f == 0) {
-    r.c0 = 1.f;
-  } else if (f < 1 + DK) {
-    r.c1 = 1.f;
-    r.a = f - 1;
-  } else if (f < NCOMPACT) {
-    const int pi = f - 1 - DK;
-    r.a = c_pairs.a[pi];
-    r.b = c_pairs.b[pi];
-    r.c2 = QUERY && r.a == r.b ? 0.5f : 1.f;
-  }
-  return r;
-}
-__device__ __forceinline__ float feature(const FeatureCoef& fc, const float* x) {
-  return fc.c0 + x[fc.a] * __builtin_fmaf(fc.c2, x[fc.b], fc.c1);
-}
 
 // DEC: the decayed variant (the based/train README's optional decay
 // strategy, read as a per-head factor gamma in [0, 1] on the state:

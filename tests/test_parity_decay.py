@@ -334,11 +334,11 @@ def test_decay_bwd_matrix_core_segments(based, L, dv):
             assert err <= TOL[q.dtype], (h, name, err)
 
 
-def test_decay_bwd_direct_form_with_small_workspace(based):
-    """A workspace of 2 B H L 4 bytes selects the direct form for bf16 as
-    well; both forms match the oracle and each other."""
+def test_decay_bwd_vector_form_with_small_workspace(based):
+    """A workspace of 2 B H L 4 bytes selects the fp32 vector form for bf16
+    as well; both forms match the oracle."""
     from parity_util import row_rel_floor
-    cfg = SMALL.replace(B=1, L=300, name="decay bwd direct vs matrix core")
+    cfg = SMALL.replace(B=1, L=300, name="decay bwd vector form vs matrix core")
     q, k, v = synth.fwd_inputs(cfg, 0)
     dy = synth.upstream_grad(cfg, 0)
     g = synth.decay_rates(cfg.H)
@@ -346,13 +346,13 @@ def test_decay_bwd_direct_form_with_small_workspace(based):
     qd, kd, vd, gd, dyd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), dy.to(DEV)
     y = based.linattn_decay_fwd(qd, kd, vd, gd)
     small = torch.empty(2 * cfg.B * cfg.H * cfg.L * 4, dtype=torch.uint8, device=DEV)
-    direct = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd, workspace=small)
+    vec = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd, workspace=small)
     mfma = based.linattn_decay_bwd(qd, kd, vd, gd, y, dyd)
     torch.cuda.synchronize()
     refs = O.linattn_decay_bwd(q, k, v, g.numpy(), dy)
-    for name, a, b, r in zip(("dq", "dk", "dv"), direct, mfma, refs):
+    for name, a, b, r in zip(("dq", "dk", "dv"), vec, mfma, refs):
         zero = 1 if name == "dq" else 0
-        for label, gr in (("direct", a), ("matrix core", b)):
+        for label, gr in (("vector form", a), ("matrix core", b)):
             err = row_rel_floor(gr[..., zero:, :], r[..., zero:, :], FLOOR[q.dtype])
             report(f"{cfg.name}: {label} {name}", err, TOL[q.dtype])
             assert err <= TOL[q.dtype], (label, name, err)
