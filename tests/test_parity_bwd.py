@@ -171,3 +171,12 @@ def test_bwd_deterministic(based, which, dtype):
     for r in runs[1:]:
         for a, b in zip(runs[0], r):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,dv", [("f32", 64), ("f32", 128), ("bf16", 48)])
+def test_vector_bwd_long_sequence(based, dtype, dv):
+    """The vector backward (fp32, and widths the matrix cores do not take)
+    over 4000 positions -- 125 chunks per pass and a ragged tail -- on whole
+    heads against the oracle's gradients, per row with the floor."""
+    cfg = synth.FwdConfig(f"vector bwd long {dtype} dv{dv}", B=1, H=2, L=4000, dv=dv, dtype=dtype)
+    run_case(based, cfg, "lin")

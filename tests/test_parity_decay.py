@@ -356,3 +356,25 @@ def test_decay_bwd_vector_form_with_small_workspace(based):
             err = row_rel_floor(gr[..., zero:, :], r[..., zero:, :], FLOOR[q.dtype])
             report(f"{cfg.name}: {label} {name}", err, TOL[q.dtype])
             assert err <= TOL[q.dtype], (label, name, err)
+
+
+def test_decay_bwd_vector_form_long(based):
+    """The fp32 decayed backward over 3000 positions (94 chunks per pass):
+    heads with decays 1, 0.75, 0.5 and 0.875 against the oracle."""
+    from parity_util import row_rel_floor
+    cfg = SMALL.replace(B=1, L=3000, dtype="f32", name="decay bwd fp32 long")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say(cfg.name)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    grads = based.linattn_decay_bwd(qd, kd, vd, gd, y, dy.to(DEV))
+    torch.cuda.synchronize()
+    for h in (0, 1, 2, 7):
+        refs = O.linattn_decay_bwd(q[0, h][None], k[0, h][None], v[0, h][None], g[h:h + 1].numpy(), dy[0, h][None])
+        for name, gr, r in zip(("dq", "dk", "dv"), grads, refs):
+            zero = 1 if name == "dq" else 0
+            err = row_rel_floor(gr[0, h, zero:][None], r[:, zero:], FLOOR[q.dtype])
+            report(f"{cfg.name} head {h} {name}", err, TOL[q.dtype])
+            assert err <= TOL[q.dtype], (h, name, err)

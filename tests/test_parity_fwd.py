@@ -367,3 +367,11 @@ def test_bf16_near_fp16_range(based):
     e3 = max(rowinf_rel(S, S_ref), z_block_rel(z, z_ref))
     report("near fp16 range: y_lin / y_swa / state", max(e1, e2, e3), 2e-3)
     assert e1 <= 2e-3 and e2 <= 2e-3 and e3 <= 2e-3
+
+
+@pytest.mark.parametrize("dtype,dv", [("f32", 64), ("f32", 128), ("bf16", 48)])
+def test_vector_pass_long_sequence(based, dtype, dv):
+    """The vector pass (fp32, and widths the matrix cores do not take) over
+    6000 positions -- 188 chunks in sequence and a ragged tail -- on whole
+    heads: y and the exported state against the chunked oracle."""
+    check_linattn(based, synth.FwdConfig(f"vector long {dtype} dv{dv}", B=1, H=2, L=6000, dv=dv, dtype=dtype))
