@@ -108,13 +108,13 @@ OP_SOURCES = {
 }
 # rocprofv3 kernel-name fragments of each operation's launches
 OP_KERNELS = {
-    "layer": ["linattn_mfma_kernel<4, 1, 0, 0>", "linattn_state_kernel<4, 0>", "seg_scan_kernel"],
+    "layer": ["linattn_mfma_kernel<4, 1, 0, 0>", "linattn_state_kernel<4, 0, 1>", "seg_scan_kernel"],
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "slice_sum_kernel",
-            "linattn_state_kernel<4, 0>", "swa_bwd_mfma_kernel<4>"],
+            "linattn_state_kernel<4, 0, 1>", "swa_bwd_mfma_kernel<4>"],
     "decode": ["decode_step_kernel<unsigned short, 64, 273>"],
     "decode_compact": ["decode_step_kernel<unsigned short, 64, 153>"],
     "baseconv": ["baseconv_kernel"],
-    "decay": ["linattn_mfma_kernel<4, 0, 1, 0>", "linattn_state_kernel<4, 1>"],
+    "decay": ["linattn_mfma_kernel<4, 0, 1, 0>", "linattn_state_kernel<4, 1, 1>"],
 }
 # the backward's last launch of each call (based_linattn_bwd, then based_swa_bwd)
 BWD_KERNEL = "swa_bwd_mfma_kernel"

@@ -299,8 +299,8 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // again when q is not wanted), threads 128..255 load k, 8 elements each:
 // every wavefront issues the same loads, so the compiler can count the loads
 // in flight exactly and a deeper prefetch is not drained early.
-template <int NT>
-__device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf) {
+template <int NT, int DVS = 16 * NT>
+__device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too, Prefetch<NT>& pf, int col0 = 0) {
   constexpr int DV = 16 * NT;
   const int tid = threadIdx.x;
   {
@@ -312,7 +312,7 @@ __device__ __forceinline__ void load_chunk(const HeadRsrc& r, int t0, bool q_too
   for (int i = 0; i < Prefetch<NT>::NV; ++i) {
     const int u = tid + NTHR * i;
     const int j = u / (DV / 8), c8 = u % (DV / 8);
-    pf.v[i] = bload(r.v, ((t0 + j) * DV + 8 * c8) * 2);
+    pf.v[i] = bload(r.v, ((t0 + j) * DVS + col0 + 8 * c8) * 2);
   }
 }
 
@@ -602,8 +602,8 @@ __device__ __forceinline__ void store_z(float* zf, const f32x4 (&tz)[3]) {
 // Initial owned state tiles from the caller's phi-layout S_in, else zero
 // (one uniform branch around the whole tile loop).
 template <int NT>
-__device__ __forceinline__ void init_state(const float* Sin, f32x4 (&tacc)[Own<NT>::PPW]) {
-  constexpr int DV = 16 * NT;
+__device__ __forceinline__ void init_state(const float* Sin, f32x4 (&tacc)[Own<NT>::PPW], int col0 = 0,
+                                           int ld = 16 * NT) {
   const int lane = threadIdx.x & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
   if (Sin) {
 #pragma unroll
@@ -611,7 +611,7 @@ __device__ __forceinline__ void init_state(const float* Sin, f32x4 (&tacc)[Own<N
       int m, n;
       pair_mn<NT>(w, j, m, n);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tacc[j][i] = compact_from_phi(Sin, 16 * m + 4 * g + i, 16 * n + r16, DV);
+      for (int i = 0; i < 4; ++i) tacc[j][i] = compact_from_phi(Sin, 16 * m + 4 * g + i, col0 + 16 * n + r16, ld);
     }
   } else {
 #pragma unroll
@@ -697,41 +697,46 @@ __device__ __forceinline__ void slot_rows(int (&ia)[3], int (&ib)[3]) {
   }
 }
 
-template <int NT>
+template <int NT, int CS = 1>
 __device__ __forceinline__ void write_compact(const float* t0, const float* zf, const f32x4 (&tacc)[Own<NT>::PPW],
-                                              float z0, float* dst, float* dz) {
-  constexpr int DV = 16 * NT;
+                                              float z0, float* dst, float* dz, int col0 = 0) {
+  constexpr int DV = 16 * NT, DVF = DV * CS;
   const int tid = threadIdx.x, w = wave_index(), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, nn;
     pair_mn<NT>(w, j, m, nn);
-    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, 16 * nn + r16, DV)) =
+    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, col0 + 16 * nn + r16, DVF)) =
         make_float4(tacc[j][0], tacc[j][1], tacc[j][2], tacc[j][3]);
   }
-  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = t0[c];
-  for (int r = tid; r < NF; r += NTHR) dz[r] = zf[r];
-  if (tid == 0) dz[NF] = z0;
+  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DVF + col0 + c] = t0[c];
+  if (col0 == 0) {
+    for (int r = tid; r < NF; r += NTHR) dz[r] = zf[r];
+    if (tid == 0) dz[NF] = z0;
+  }
 }
 
 // Record 0 of a head: the caller's initial state in the compact record
 // layout (owned tiles from s0 = init_state of Sin; the constant row and the
 // z entries straight from Sin / zin).
-template <int NT>
+template <int NT, int CS = 1>
 __device__ __forceinline__ void write_initial_record(const float* Sin, const float* zin,
-                                                     const f32x4 (&s0)[Own<NT>::PPW], float* dst, float* dz) {
-  constexpr int DV = 16 * NT;
+                                                     const f32x4 (&s0)[Own<NT>::PPW], float* dst, float* dz,
+                                                     int col0 = 0) {
+  constexpr int DV = 16 * NT, DVF = DV * CS;
   const int tid = threadIdx.x, w = wave_index(), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < Own<NT>::PPW; ++j) {
     int m, nn;
     pair_mn<NT>(w, j, m, nn);
-    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, 16 * nn + r16, DV)) =
+    *reinterpret_cast<float4*>(dst + record_offset(16 * m + 4 * g, col0 + 16 * nn + r16, DVF)) =
         make_float4(s0[j][0], s0[j][1], s0[j][2], s0[j][3]);
   }
-  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DV + c] = Sin[c];
-  for (int r = tid; r < NF; r += NTHR) dz[r] = compact_from_phi(zin, r, 0, 1);
-  if (tid == 0) dz[NF] = zin[0];
+  for (int c = tid; c < DV; c += NTHR) dst[(size_t)NF * DVF + col0 + c] = Sin[col0 + c];
+  if (col0 == 0 && zin) {
+    for (int r = tid; r < NF; r += NTHR) dz[r] = compact_from_phi(zin, r, 0, 1);
+    if (tid == 0) dz[NF] = zin[0];
+  }
 }
 
 // The final state in the caller's 273-row phi layout, straight from the
@@ -1281,31 +1286,38 @@ struct StateSmem {
   alignas(16) half_t wkc[C];  // decayed variant: key weights gamma^(C - 1 - key)
 };
 
-template <int NT, int DEC = 0>
+// CS: the value columns split over CS workgroups per segment (each takes
+// DV = 16 NT of the DVF = CS DV columns of the records; the first also writes
+// the denominator record).  Splitting halves a workgroup's accumulators and
+// doubles the workgroups, which pays at d_v = 128 (segments too few to fill
+// the chip) but not at d_v = 64.
+template <int NT, int DEC = 0, int CS = 1>
 __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Params p) {
-  constexpr int DV = 16 * NT;
+  constexpr int DV = 16 * NT, DVF = DV * CS;
   // chunks per group (the decayed variant's extra per-chunk registers leave
   // room for half the prefetches)
   constexpr int G = DEC ? SG / 2 : SG;
   __shared__ StateSmem<NT> S;
 
   const int nsm = p.nrec ? p.nrec : p.nseg - 1;
-  int bhi, seg;
-  xcd_unit_part(blockIdx.x, gridDim.x / nsm, nsm, bhi, seg);
+  int bhi, part;
+  xcd_unit_part(blockIdx.x, gridDim.x / (nsm * CS), nsm * CS, bhi, part);
+  const int seg = part / CS, col0 = (part % CS) * DV;
   const size_t bh = bhi;
   const int tid = threadIdx.x;
   const int tok_begin = seg * p.seg_chunks * C;
   const int tok_end = min(p.L, tok_begin + p.seg_chunks * C);
-  const size_t rec = (size_t)(NF + 1) * DV;
+  const size_t rec = (size_t)(NF + 1) * DVF;
 
   // the head's k and v up to the segment's end; the first group's loads go
   // out first, overlapping the state set-up
   HeadRsrc rs;
   rs.q = rs.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + bh * p.L * DK), (short)0, tok_end * DK * 2, RSRC_DW3);
-  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DV), (short)0, tok_end * DV * 2, RSRC_DW3);
+  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + bh * (size_t)p.L * DVF), (short)0, tok_end * DVF * 2,
+                                           RSRC_DW3);
   Prefetch<NT> pf[G];
 #pragma unroll
-  for (int i = 0; i < G; ++i) load_chunk<NT>(rs, tok_begin + i * C, false, pf[i]);
+  for (int i = 0; i < G; ++i) load_chunk<NT, DVF>(rs, tok_begin + i * C, false, pf[i], col0);
   // the segment's increment from zero; segment 0 adds the caller's initial
   // state after the loop (every term is linear in it)
   f32x4 tacc[Own<NT>::PPW];
@@ -1338,7 +1350,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
 #pragma unroll
     for (int i = 0; i < G; ++i) store_chunk<NT>(S.kt[i], &S.vh[i][0][0], nullptr, nullptr, pf[i]);
 #pragma unroll
-    for (int i = 0; i < G; ++i) load_chunk<NT>(rs, t + (G + i) * C, false, pf[i]);
+    for (int i = 0; i < G; ++i) load_chunk<NT, DVF>(rs, t + (G + i) * C, false, pf[i], col0);
     __syncthreads();  // the group in LDS
     if constexpr (DEC) {
       // (a rolled loop: the decay weights of several chunks at once would
@@ -1389,26 +1401,27 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_state_kernel(Par
     for (int nn = 0; nn < NT; ++nn) S.t0[16 * nn + r16] = vacc[nn][0];
   __syncthreads();
   // segment 0: the caller's initial state, decayed over the segment
-  const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DV : nullptr;
+  const float* Sin = (seg == 0 && p.S_in) ? p.S_in + bh * DPHI * DVF : nullptr;
   const float* zin = (seg == 0 && p.z_in) ? p.z_in + bh * DPHI : nullptr;
   const float gN = DEC ? gpow(lg, (float)(tok_end - tok_begin)) : 1.f;
-  if (Sin && tid < DV) S.t0[tid] += gN * Sin[tid];
+  if (Sin && tid < DV) S.t0[tid] += gN * Sin[col0 + tid];
   if (zin) {
     for (int r = tid; r < NF; r += NTHR) S.zf[r] += gN * compact_from_phi(zin, r, 0, 1);
     z0 += gN * zin[0];
   }
   if (Sin) {
     f32x4 s0[Own<NT>::PPW];
-    init_state<NT>(Sin, s0);
+    init_state<NT>(Sin, s0, col0, DVF);
 #pragma unroll
     for (int j = 0; j < Own<NT>::PPW; ++j) tacc[j] += gN * s0[j];
     // record 0: S_in itself, the main pass's start of segment 0 (that pass
     // then reads no S_in, so S_out may alias it)
-    write_initial_record<NT>(Sin, zin, s0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1));
+    write_initial_record<NT, CS>(Sin, zin, s0, p.ws + bh * p.nseg * rec, p.wsz + bh * p.nseg * (size_t)(NF + 1),
+                                 col0);
   }
   __syncthreads();
-  write_compact<NT>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
-                    p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1));
+  write_compact<NT, CS>(S.t0, S.zf, tacc, z0, p.ws + (bh * p.nseg + seg + 1) * rec,
+                        p.wsz + (bh * p.nseg + seg + 1) * (size_t)(NF + 1), col0);
 }
 
 // Prefix over the segment records of each (batch, head): record s >= 1 holds
@@ -1468,7 +1481,10 @@ static hipError_t launch_nt_hi(const LinattnArgs& a, float* y_swa, int window, f
   if (p.nseg > 1) {
     p.ws = (float*)a.workspace;
     p.wsz = p.ws + (size_t)BH * p.nseg * (NF + 1) * DV;
-    hipLaunchKernelGGL((linattn_state_kernel<NT, DEC>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
+    if constexpr (NT == 8)
+      hipLaunchKernelGGL((linattn_state_kernel<NT / 2, DEC, 2>), dim3(BH * (p.nseg - 1) * 2), dim3(NTHR), 0, s, p);
+    else
+      hipLaunchKernelGGL((linattn_state_kernel<NT, DEC>), dim3(BH * (p.nseg - 1)), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     if (p.nseg > MAX_SUM + 1) {
       const size_t total = (size_t)BH * ((size_t)(NF + 1) * DV + NF + 1);

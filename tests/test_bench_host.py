@@ -17,7 +17,7 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-STATE = "void based::mfma::linattn_state_kernel<4, 0>(based::mfma::Params)"
+STATE = "void based::mfma::linattn_state_kernel<4, 0, 1>(based::mfma::Params)"
 MAIN = "void based::mfma::linattn_mfma_kernel<4, 1, 0, 0>(based::mfma::Params)"
 QPASS = "based::bwdm::query_pass_kernel(based::bwdm::Params)"
 SWAB = "void based::swab::swa_bwd_mfma_kernel<4>(based::swab::Params)"
@@ -80,8 +80,8 @@ def test_summarize_pmc_scales_and_windows(tmp_path):
     assert layer["copy_fetch_factor"] == pytest.approx(0.5)
     assert layer["copy_write_factor"] == pytest.approx(1.0)
     k = layer["kernels"]
-    assert k["based::mfma::linattn_state_kernel<4, 0>"]["dispatches"] == 3
-    assert k["based::mfma::linattn_state_kernel<4, 0>"]["fetch_bytes"] == pytest.approx(1000.0 * 1024 * 0.5)
+    assert k["based::mfma::linattn_state_kernel<4, 0, 1>"]["dispatches"] == 3
+    assert k["based::mfma::linattn_state_kernel<4, 0, 1>"]["fetch_bytes"] == pytest.approx(1000.0 * 1024 * 0.5)
     assert k["based::mfma::linattn_mfma_kernel<4, 1, 0, 0>"]["write_bytes"] == pytest.approx(900.0 * 1024)
     assert layer["bytes_per_call"] == pytest.approx(((1000 + 3000) * 0.5 + 100 + 900) * 1024)
     assert layer["source_hash"] == bench.source_hash("layer")
@@ -122,7 +122,7 @@ def test_summarize_stats_marks_step_and_backward(tmp_path):
     lines = {ln.split("|")[1].strip().strip("`"): ln for ln in text.splitlines() if ln.startswith("| `")}
     # the set-up and step calls of the layer are marked step; the backward's
     # calls bwd; decode (after the backward) neither
-    assert "| step | 3 | 17.0 |" in lines["based::mfma::linattn_state_kernel<4, 0>"]
+    assert "| step | 3 | 17.0 |" in lines["based::mfma::linattn_state_kernel<4, 0, 1>"]
     assert "| step | 3 | 58.0 |" in lines["based::mfma::linattn_mfma_kernel<4, 1, 0, 0>"]
     assert "| bwd | 2 | 83.0 |" in lines["based::bwdm::query_pass_kernel"]
     assert "| bwd | 2 | 71.0 |" in lines["based::swab::swa_bwd_mfma_kernel<4>"]
