@@ -147,6 +147,20 @@ __device__ __forceinline__ void xcd_unit_part(int b, int units, int parts, int& 
   }
 }
 
+// Issue priority by progress.  Where two workgroups share a CU, the wavefront
+// arbiter favours the older wavefronts: one workgroup of the pair runs ahead
+// and ends several microseconds before the other, which then runs alone at a
+// fraction of the CU's throughput.  A wavefront that lowers its priority as
+// it passes each quarter of its work (done of total) lets the one behind
+// catch up, so that the two end closer together.
+__device__ __forceinline__ void progress_priority(long long done, long long total) {
+  const int q4 = total > 0 ? (int)(4 * done / total) : 0;
+  if (q4 <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Segment records of the linear attention's state (workspace of the chunked
 // forward, read by the backward too): the 160 x dv compact state is stored in
 // the order of the matrix-core accumulator fragments, so that a lane moves its

@@ -909,6 +909,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
   }
   f32x4 vacc[NT];  // wavefront 0: the chunk's column sums of v
   for (int t0 = tok_begin; t0 < tok_end; t0 += C) {
+    if constexpr (Occ<NT>::value > 1) progress_priority(t0 - tok_begin, tok_end - tok_begin);
     const int n = min(C, tok_end - t0);
     __syncthreads();  // chunk inputs, published state, t0 visible
     const int tn = t0 + C;

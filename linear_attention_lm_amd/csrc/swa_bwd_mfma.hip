@@ -234,6 +234,7 @@ __global__ __launch_bounds__(NTHR, NT <= 4 ? 2 : 1) void swa_bwd_mfma_kernel(Par
 
   f32x4 carry = z4;  // dq share of query tile w of the next chunk
   for (int c = c0; c < c_end; ++c) {
+    if constexpr (NT <= 4) progress_priority(c - c0, c_end - c0);  // two workgroups per CU
     __syncthreads();  // this step's chunks staged; the previous step's reads done
     const bool more = c + 1 < c_end;
     if (more) load_step<NT>(rs, c + 2, c + 1, pf);
