@@ -346,6 +346,41 @@ def test_bf16_arbitrary_initial_state(based, B, H, L, op):
     assert errS <= TOL[q.dtype] and errz <= TOL[q.dtype]
 
 
+@pytest.mark.parametrize("dv", [32, 96, 128])
+@pytest.mark.parametrize("op", ["linattn", "layer", "decay"])
+def test_value_dims_across_segments(based, dv, op):
+    """The other matrix-core widths with the sequence split into segments (L =
+    1000 on six heads: four per head) and an arbitrary bf16 S_in: the
+    state-only pass with its initial-state record (at d_v = 128 split over
+    two workgroups by value columns), the record sums of the later segments,
+    plain, fused with the window and decayed.  Same bounds as the d_v = 64
+    case."""
+    cfg = SMALL.replace(L=1000, dv=dv, name=f"segments {op} dv{dv}")
+    q, k, v = inputs(cfg)
+    S0, z0 = random_state(cfg)
+    say(cfg.name)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    if op == "linattn":
+        y, S, z = based.linattn_fwd(qd, kd, vd, S0.to(DEV), z0.to(DEV), return_state=True)
+        y_ref, _, S_ref, z_ref = O.linattn_chunked(q, k, v, 64, S0, z0)
+    elif op == "layer":
+        y, ys, S, z = based.layer_fwd(qd, kd, vd, 64, 1.0, S0.to(DEV), z0.to(DEV), return_state=True)
+        y_ref, _, S_ref, z_ref = O.linattn_chunked(q, k, v, 64, S0, z0)
+        assert rowinf_rel(ys, O.swa(q, k, v, 64)) <= TOL[q.dtype]
+    else:
+        g = synth.decay_rates(cfg.H)
+        y, S, z = based.linattn_decay_fwd(qd, kd, vd, g.to(DEV), S0.to(DEV), z0.to(DEV), return_state=True)
+        y_ref, _, S_ref, z_ref = O.linattn_decay_recurrent(q, k, v, g.numpy(), S0, z0)
+    torch.cuda.synchronize()
+    err = rowinf_rel(y, y_ref)
+    report(f"{cfg.name} y", err, 1e-3)
+    assert err <= 1e-3
+    S_ref, z_ref = symmetrized(S_ref, z_ref)
+    errS, errz = rowinf_rel(S, S_ref), z_block_rel(z, z_ref)
+    report(f"{cfg.name} S_out / z_out", max(errS, errz), TOL[q.dtype])
+    assert errS <= TOL[q.dtype] and errz <= TOL[q.dtype]
+
+
 def test_bf16_near_fp16_range(based):
     """Inputs near the bound the header states for the bf16 path (|q.k| < 256,
     |v| < 32768): every coordinate of k is +-3.5 and q_i = k_{i-5}, so that
