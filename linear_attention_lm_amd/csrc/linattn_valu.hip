@@ -10,8 +10,10 @@
 // update with the chunk.  The state lives in LDS in the compact form (one row
 // per unordered feature pair, see based_device.h).
 //
-// One workgroup of 512 threads per (batch, head); chunks run in sequence.
-// A per-head decay of the state (DEC) is the same pass with decay weights.
+// One workgroup of 512 threads per (batch, head) and slice of DVS value
+// columns (few heads: 16-column slices, so that more CUs share the work;
+// many: the whole row); chunks run in sequence.  A per-head decay of the
+// state (DEC) is the same pass with decay weights.
 #include "based_device.h"
 #include "launchers.h"
 
@@ -85,32 +87,37 @@ struct Split {
 //   3. psi(k_j) of the chunk's keys (row-major; zero past n), and the
 //      update T += psi(K)^T V, z += psi(K)^T 1, each thread FPT feature rows
 //      x CPT columns.
-template <typename T, int DV, int DEC>
-__global__ __launch_bounds__(nthreads<DV>()) void linattn_valu_kernel(
+// DVS: value columns of a workgroup (DV / DVS workgroups per head, slice
+// blockIdx.x % (DV / DVS)); every slice forms the chunk's features, in-chunk
+// weights and denominators itself, slice 0 writes z_out.
+template <typename T, int DV, int DVS, int DEC>
+__global__ __launch_bounds__(nthreads<DVS>()) void linattn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ y,
     const float* S_in, const float* z_in, float* S_out, float* z_out, int L, const float* gamma, int H) {
-  using SP = Split<DV>;
+  static_assert(DV % DVS == 0, "whole slices");
+  using SP = Split<DVS>;
   constexpr int NT = SP::NT, CPT = SP::CPT, RPT = SP::RPT, FPT = SP::FPT;
   constexpr int FT = C + 4;    // row stride of the feature-major query features
   constexpr int FK = NFP + 4;  // row stride of the row-major key features
   static_assert(NFP * FT >= C * FK, "the key features reuse the query features' buffer");
-  __shared__ float Ts[NFP][DV];  // compact state (rows NCOMPACT.. zero)
+  __shared__ float Ts[NFP][DVS];  // compact state of the slice (rows NCOMPACT.. zero)
   __shared__ float zs[NFP];
   __shared__ float fbuf[NFP * FT];  // phi(q) [NFP][FT], then psi(k) [C][FK]
   __shared__ float qs[C][DK + 1];  // (odd stride: rows read down a column)
   __shared__ float ks[C][DK + 1];
-  __shared__ float vs[C][DV];
+  __shared__ float vs[C][DVS];
   __shared__ float wt[C][C + 1];  // in-chunk weights, [key][query]
 
-  const int bh = blockIdx.x;
+  constexpr int NS = DV / DVS;
+  const int bh = blockIdx.x / NS, col0 = (blockIdx.x % NS) * DVS;
   const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
   const int tid = threadIdx.x;
   const int cb = tid % SP::NCB, ob = tid / SP::NCB;  // column block; row / feature block
   const int c0 = cb * CPT, r0 = ob * RPT, f0 = ob * FPT;
   const T* qb = q + (size_t)bh * L * DK;
   const T* kb = k + (size_t)bh * L * DK;
-  const T* vb = v + (size_t)bh * L * DV;
-  float* yb = y + (size_t)bh * L * DV;
+  const T* vb = v + (size_t)bh * L * DV + col0;
+  float* yb = y + (size_t)bh * L * DV + col0;
   // feature fills: item u = tid + NT m (m < NFI; u < 2 NFP) is feature u / 2
   // over rows (u % 2) C/2 .. + C/2 - 1 of the chunk
   constexpr int HC = C / 2, NFI = (2 * NFP + NT - 1) / NT;
@@ -125,9 +132,9 @@ __global__ __launch_bounds__(nthreads<DV>()) void linattn_valu_kernel(
     fk[m] = feature_coef<false>(fu[m] < 0 ? 0 : fu[m]);
   }
 
-  for (int e = tid; e < NFP * DV; e += NT) {
-    const int f = e / DV, c = e % DV;
-    Ts[f][c] = S_in && f < NCOMPACT ? compact_from_phi(S_in + (size_t)bh * DPHI * DV, f, c, DV) : 0.f;
+  for (int e = tid; e < NFP * DVS; e += NT) {
+    const int f = e / DVS, c = e % DVS;
+    Ts[f][c] = S_in && f < NCOMPACT ? compact_from_phi(S_in + (size_t)bh * DPHI * DV, f, col0 + c, DV) : 0.f;
   }
   for (int f = tid; f < NFP; f += NT)
     zs[f] = z_in && f < NCOMPACT ? compact_from_phi(z_in + (size_t)bh * DPHI, f, 0, 1) : 0.f;
@@ -141,8 +148,8 @@ __global__ __launch_bounds__(nthreads<DV>()) void linattn_valu_kernel(
       qs[j][d] = ok ? to_f32(qb[(size_t)(t0 + j) * DK + d]) : 0.f;
       ks[j][d] = ok ? to_f32(kb[(size_t)(t0 + j) * DK + d]) : 0.f;
     }
-    for (int e = tid; e < C * DV; e += NT) {
-      const int j = e / DV, d = e % DV;
+    for (int e = tid; e < C * DVS; e += NT) {
+      const int j = e / DVS, d = e % DVS;
       vs[j][d] = j < n ? to_f32(vb[(size_t)(t0 + j) * DV + d]) : 0.f;
     }
     __syncthreads();
@@ -268,22 +275,34 @@ __global__ __launch_bounds__(nthreads<DV>()) void linattn_valu_kernel(
   }
   __syncthreads();
   if (S_out) {
-    float* So = S_out + (size_t)bh * DPHI * DV;
-    for (int e = tid; e < DPHI * DV; e += NT) So[e] = phi_from_compact(&Ts[0][0], e / DV, e % DV, DV);
-    float* zo = z_out + (size_t)bh * DPHI;
-    for (int f = tid; f < DPHI; f += NT) zo[f] = phi_from_compact(zs, f, 0, 1);
+    float* So = S_out + (size_t)bh * DPHI * DV + col0;
+    for (int e = tid; e < DPHI * DVS; e += NT)
+      So[(size_t)(e / DVS) * DV + e % DVS] = phi_from_compact(&Ts[0][0], e / DVS, e % DVS, DVS);
+    if (col0 == 0) {
+      float* zo = z_out + (size_t)bh * DPHI;
+      for (int f = tid; f < DPHI; f += NT) zo[f] = phi_from_compact(zs, f, 0, 1);
+    }
   }
 }
 
+template <typename T, int DV, int DVS, int DEC>
+hipError_t launch_slices(const LinattnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((linattn_valu_kernel<T, DV, DVS, DEC>), dim3(a.B * a.H * (DV / DVS)), dim3(nthreads<DVS>()), 0,
+                     s, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L,
+                     a.gamma, a.H);
+  return hipGetLastError();
+}
+
+// Few heads: 16-column slices where they still fit one workgroup per CU
+// (more, and the slices' repeated feature work costs more than they gain:
+// 128 heads of 2048 positions, d_v 64: 794 -> 912 us).  Not for an in-place
+// update (z_out = z_in): every slice reads z_in at its start and slice 0
+// writes z_out at its end, in no fixed order.
 template <typename T, int DV>
 hipError_t launch_dv(const LinattnArgs& a, hipStream_t s) {
-  if (a.gamma)
-    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 1>), dim3(a.B * a.H), dim3(nthreads<DV>()), 0, s, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
-  else
-    hipLaunchKernelGGL((linattn_valu_kernel<T, DV, 0>), dim3(a.B * a.H), dim3(nthreads<DV>()), 0, s, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, a.y, a.S_in, a.z_in, a.S_out, a.z_out, a.L, a.gamma, a.H);
-  return hipGetLastError();
+  const bool split = DV > 16 && (long long)a.B * a.H * (DV / 16) <= 256 && !(a.z_out && a.z_out == a.z_in);
+  if (a.gamma) return split ? launch_slices<T, DV, 16, 1>(a, s) : launch_slices<T, DV, DV, 1>(a, s);
+  return split ? launch_slices<T, DV, 16, 0>(a, s) : launch_slices<T, DV, DV, 0>(a, s);
 }
 
 template <typename T>

@@ -381,6 +381,40 @@ def test_value_dims_across_segments(based, dv, op):
     assert errS <= TOL[q.dtype] and errz <= TOL[q.dtype]
 
 
+@pytest.mark.parametrize("mode", ["separate", "S in place", "S and z in place", "decayed"])
+def test_fp32_column_slices(based, mode):
+    """fp32 inputs on few heads: the vector pass splits each head's value
+    columns over 16-column workgroups (each reads its columns of S_in and
+    writes them to S_out, slice 0 writes z_out), except for an in-place z
+    (z_out = z_in: one workgroup per head).  An arbitrary S_in, z_in; y and
+    the exported state against the oracle."""
+    cfg = SMALL.replace(L=150, dtype="f32", name=f"fp32 slices {mode}")
+    q, k, v = inputs(cfg)
+    S0, z0 = random_state(cfg)
+    say(cfg.name)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    S, z = S0.clone().to(DEV), z0.clone().to(DEV)
+    if mode == "decayed":
+        g = synth.decay_rates(cfg.H)
+        y, S, z = based.linattn_decay_fwd(qd, kd, vd, g.to(DEV), S, z, return_state=True)
+        y_ref, _, S_ref, z_ref = O.linattn_decay_recurrent(q, k, v, g.numpy(), S0, z0)
+    else:
+        if mode == "separate":
+            y, S, z = based.linattn_fwd(qd, kd, vd, S, z, return_state=True)
+        elif mode == "S in place":
+            z_out = torch.empty_like(z)
+            y = based.linattn_fwd(qd, kd, vd, S, z, S_out=S, z_out=z_out)[0]
+            z = z_out
+        else:
+            y = based.linattn_fwd(qd, kd, vd, S, z, S_out=S, z_out=z)[0]
+        y_ref, _, S_ref, z_ref = O.linattn_recurrent(q, k, v, S0, z0)
+    torch.cuda.synchronize()
+    S_ref, z_ref = symmetrized(S_ref, z_ref)
+    err, errS, errz = rowinf_rel(y, y_ref), rowinf_rel(S, S_ref), z_block_rel(z, z_ref)
+    report(f"{cfg.name} y / S / z", max(err, errS, errz), 1e-5)
+    assert err <= 1e-5 and errS <= 1e-5 and errz <= 1e-5
+
+
 def test_bf16_near_fp16_range(based):
     """Inputs near the bound the header states for the bf16 path (|q.k| < 256,
     |v| < 32768): every coordinate of k is +-3.5 and q_i = k_{i-5}, so that
