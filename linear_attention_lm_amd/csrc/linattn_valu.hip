@@ -139,19 +139,43 @@ __global__ __launch_bounds__(nthreads<DVS>()) void linattn_valu_kernel(
   for (int f = tid; f < NFP; f += NT)
     zs[f] = z_in && f < NCOMPACT ? compact_from_phi(z_in + (size_t)bh * DPHI, f, 0, 1) : 0.f;
 
+  // the chunk's q, k, v in registers, the next chunk's loads in flight while
+  // this one is processed (element e = tid + NT i of the chunk; zero past L)
+  constexpr int NQK = (C * DK + NT - 1) / NT, NVV = (C * DVS + NT - 1) / NT;
+  float pq[NQK], pk[NQK], pv[NVV];
+  auto prefetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int e = tid + NT * i, j = e / DK, d = e % DK;
+      const bool ok = e < C * DK && t0 + j < L;
+      pq[i] = ok ? to_f32(qb[(size_t)(t0 + j) * DK + d]) : 0.f;
+      pk[i] = ok ? to_f32(kb[(size_t)(t0 + j) * DK + d]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NVV; ++i) {
+      const int e = tid + NT * i, j = e / DVS, d = e % DVS;
+      pv[i] = e < C * DVS && t0 + j < L ? to_f32(vb[(size_t)(t0 + j) * DV + d]) : 0.f;
+    }
+  };
+  prefetch(0);
+
   for (int t0 = 0; t0 < L; t0 += C) {
     const int n = min(C, L - t0);
     __syncthreads();  // the previous chunk's update done
-    for (int e = tid; e < C * DK; e += NT) {
-      const int j = e / DK, d = e % DK;
-      const bool ok = j < n;
-      qs[j][d] = ok ? to_f32(qb[(size_t)(t0 + j) * DK + d]) : 0.f;
-      ks[j][d] = ok ? to_f32(kb[(size_t)(t0 + j) * DK + d]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int e = tid + NT * i;
+      if (e < C * DK) {
+        qs[e / DK][e % DK] = pq[i];
+        ks[e / DK][e % DK] = pk[i];
+      }
     }
-    for (int e = tid; e < C * DVS; e += NT) {
-      const int j = e / DVS, d = e % DVS;
-      vs[j][d] = j < n ? to_f32(vb[(size_t)(t0 + j) * DV + d]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NVV; ++i) {
+      const int e = tid + NT * i;
+      if (e < C * DVS) vs[e / DVS][e % DVS] = pv[i];
     }
+    if (t0 + C < L) prefetch(t0 + C);
     __syncthreads();
 
     // ---- 1. query features and in-chunk weights
