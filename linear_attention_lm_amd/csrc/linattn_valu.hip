@@ -309,6 +309,120 @@ __global__ __launch_bounds__(nthreads<DVS>()) void linattn_valu_kernel(
   }
 }
 
+// Short sequences without a state argument: the quadratic form of the same
+// attention (the pages' views are interchangeable; every view gives
+// y_i = sum_{j<=i} W_ij v_j / sum_{j<=i} W_ij with W_ij = 1 + x + x^2/2,
+// x = q_i.k_j, times gamma^(i-j) when decayed).  Per position it costs
+// L/2 (d_k + d_v) products against about C (d_k + d_v) + 2 * 153 d_v for the
+// chunked pass, so below a few hundred positions it is the cheaper form, and
+// its workgroups (one per 32 queries) run side by side instead of walking
+// the chunks in order.
+constexpr int QB = 32;            // queries per workgroup (and keys per block)
+constexpr int QNT = 256;          // threads: 8 lanes per query
+constexpr int QG = QNT / QB;
+constexpr int QUAD_MAX_L = 512;   // longest sequence that takes this form
+template <typename T, int DV, int DEC>
+__global__ __launch_bounds__(QNT) void linattn_quad_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, float* __restrict__ y, int L,
+                                                          const float* gamma, int H) {
+  constexpr int CPL = DV / QG;  // value columns per lane, contiguous
+  static_assert(DV % (2 * QG) == 0, "pairs of columns per lane");
+  __shared__ float Ks[QB][DK + 1];
+  __shared__ float Vs[QB][DV];
+  __shared__ float W[QB][QB + 1];  // [query][key] weights of the current key block
+
+  const int nblk = (L + QB - 1) / QB;
+  const int bh = blockIdx.x / nblk, i0 = (blockIdx.x % nblk) * QB;
+  const int tid = threadIdx.x, i = tid / QG, g = tid % QG, qpos = i0 + i;
+  const float lg = DEC ? decay_lg2_clamped(log2f(gamma[bh % H])) : 0.f;
+  const T* kb = k + (size_t)bh * L * DK;
+  const T* vb = v + (size_t)bh * L * DV;
+  float qr[DK];
+#pragma unroll
+  for (int d = 0; d < DK; ++d) qr[d] = qpos < L ? to_f32(q[((size_t)bh * L + qpos) * DK + d]) : 0.f;
+
+  // a key block's k and v in registers (element e = tid + QNT i; zero past
+  // L), the next block's loads in flight while this one is processed
+  constexpr int NK = QB * DK / QNT, NV = QB * DV / QNT;
+  static_assert(QB * DK % QNT == 0 && QB * DV % QNT == 0, "whole rounds");
+  float pk[NK], pv[NV];
+  auto prefetch = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < NK; ++r) {
+      const int e = tid + QNT * r;
+      pk[r] = j0 + e / DK < L ? to_f32(kb[(size_t)j0 * DK + e]) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int e = tid + QNT * r;
+      pv[r] = j0 + e / DV < L ? to_f32(vb[(size_t)j0 * DV + e]) : 0.f;
+    }
+  };
+  prefetch(0);
+
+  float num[CPL], den = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) num[c] = 0.f;
+  for (int j0 = 0; j0 <= i0; j0 += QB) {
+    __syncthreads();  // the previous block's reads done
+#pragma unroll
+    for (int r = 0; r < NK; ++r) {
+      const int e = tid + QNT * r;
+      Ks[e / DK][e % DK] = pk[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int e = tid + QNT * r;
+      Vs[e / DV][e % DV] = pv[r];
+    }
+    if (j0 + QB <= i0) prefetch(j0 + QB);
+    __syncthreads();
+    // this lane's keys j = g + QG m of the block
+#pragma unroll
+    for (int m = 0; m < QB / QG; ++m) {
+      const int j = g + QG * m, kpos = j0 + j;
+      float x = 0.f;
+#pragma unroll
+      for (int d = 0; d < DK; ++d) x = __builtin_fmaf(qr[d], Ks[j][d], x);
+      float w = kpos <= qpos && kpos < L ? 1.f + x + 0.5f * x * x : 0.f;
+      if (DEC && kpos <= qpos) w *= exp2f(lg * (float)(qpos - kpos));
+      W[i][j] = w;
+    }
+    __syncthreads();
+    // the block's share, summed apart before it joins the running sums
+    float nb[CPL], db = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) nb[c] = 0.f;
+    for (int j = 0; j < QB; ++j) {
+      const float w = W[i][j];
+      db += w;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 2) {
+        const float2 vv = *reinterpret_cast<const float2*>(&Vs[j][CPL * g + c]);
+        nb[c] = __builtin_fmaf(w, vv.x, nb[c]);
+        nb[c + 1] = __builtin_fmaf(w, vv.y, nb[c + 1]);
+      }
+    }
+    den += db;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) num[c] += nb[c];
+  }
+  if (qpos < L) {
+    const float rd = 1.f / den;
+    float* yr = y + ((size_t)bh * L + qpos) * DV + CPL * g;
+#pragma unroll
+    for (int c = 0; c < CPL; c += 2) *reinterpret_cast<float2*>(yr + c) = make_float2(num[c] * rd, num[c + 1] * rd);
+  }
+}
+
+template <typename T, int DV, int DEC>
+hipError_t launch_quad(const LinattnArgs& a, hipStream_t s) {
+  const unsigned nblk = (unsigned)((a.L + QB - 1) / QB);
+  hipLaunchKernelGGL((linattn_quad_kernel<T, DV, DEC>), dim3(nblk * (unsigned)(a.B * a.H)), dim3(QNT), 0, s,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.L, a.gamma, a.H);
+  return hipGetLastError();
+}
+
 template <typename T, int DV, int DVS, int DEC>
 hipError_t launch_slices(const LinattnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((linattn_valu_kernel<T, DV, DVS, DEC>), dim3(a.B * a.H * (DV / DVS)), dim3(nthreads<DVS>()), 0,
@@ -324,6 +438,10 @@ hipError_t launch_slices(const LinattnArgs& a, hipStream_t s) {
 // writes z_out at its end, in no fixed order.
 template <typename T, int DV>
 hipError_t launch_dv(const LinattnArgs& a, hipStream_t s) {
+  if (!a.S_in && !a.S_out && a.L <= QUAD_MAX_L) {
+    if (a.L == 0) return hipSuccess;
+    return a.gamma ? launch_quad<T, DV, 1>(a, s) : launch_quad<T, DV, 0>(a, s);
+  }
   const bool split = DV > 16 && (long long)a.B * a.H * (DV / 16) <= 256 && !(a.z_out && a.z_out == a.z_in);
   if (a.gamma) return split ? launch_slices<T, DV, 16, 1>(a, s) : launch_slices<T, DV, DV, 1>(a, s);
   return split ? launch_slices<T, DV, 16, 0>(a, s) : launch_slices<T, DV, DV, 0>(a, s);

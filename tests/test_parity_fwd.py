@@ -415,6 +415,36 @@ def test_fp32_column_slices(based, mode):
     assert err <= 1e-5 and errS <= 1e-5 and errz <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,dv", [("f32", 64), ("bf16", 48), ("f32", 128)])
+@pytest.mark.parametrize("L", [1, 31, 33, 256, 512])
+@pytest.mark.parametrize("decayed", [False, True])
+def test_quadratic_form_short(based, dtype, dv, L, decayed):
+    """The vector path's quadratic form (no state argument, L <= 512): one
+    workgroup per 32 queries against every earlier key block, plain and
+    decayed, against the oracle's recurrent form; and, with a state argument
+    (the chunked vector pass), the same y within fp32 rounding."""
+    cfg = SMALL.replace(L=L, dv=dv, dtype=dtype, name=f"quadratic {dtype} dv{dv} L{L} decayed={decayed}")
+    q, k, v = inputs(cfg)
+    say(cfg.name)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    if decayed:
+        g = synth.decay_rates(cfg.H)
+        y = based.linattn_decay_fwd(qd, kd, vd, g.to(DEV))
+        y_chunked = based.linattn_decay_fwd(qd, kd, vd, g.to(DEV), return_state=True)[0]
+        y_ref = O.linattn_decay_recurrent(q, k, v, g.numpy())[0]
+    else:
+        y = based.linattn_fwd(qd, kd, vd)
+        y_chunked = based.linattn_fwd(qd, kd, vd, return_state=True)[0]
+        y_ref = O.linattn_recurrent(q, k, v)[0]
+    torch.cuda.synchronize()
+    err = rowinf_rel(y, y_ref)
+    report(cfg.name, err, TOL[q.dtype])
+    assert err <= TOL[q.dtype]
+    gap = rowinf_rel(y, y_chunked.double().cpu().numpy())
+    report(f"{cfg.name} vs the chunked pass", gap, 1e-5)
+    assert gap <= 1e-5
+
+
 def test_bf16_near_fp16_range(based):
     """Inputs near the bound the header states for the bf16 path (|q.k| < 256,
     |v| < 32768): every coordinate of k is +-3.5 and q_i = k_{i-5}, so that

@@ -23,7 +23,8 @@ def check_layer(based, cfg, heads=None, window=64, scale=1.0, seed=0):
     say(f"layer {cfg.name} B{cfg.B} H{cfg.H} L{cfg.L} dv{cfg.dv} {cfg.dtype} window{window} scale{scale}")
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     y_lin, y_swa, S, z = based.layer_fwd(qd, kd, vd, window, scale, return_state=True)
-    y_sep = based.linattn_fwd(qd, kd, vd)
+    # the same arguments (the final state asked for): the same evaluation
+    y_sep = based.linattn_fwd(qd, kd, vd, return_state=True)[0]
     torch.cuda.synchronize()
     gap = rowinf_rel(y_lin, y_sep.double().cpu().numpy())
     report(f"layer y_lin vs based_linattn_fwd {cfg.name}", gap, 1e-6)
