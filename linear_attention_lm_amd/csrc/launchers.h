@@ -18,7 +18,7 @@ constexpr int FWD_MAX_SUM = 3;     // segments summed directly by the forward's 
 constexpr int BWD_SLICE = 32;      // value columns per backward workgroup
 constexpr int BWD_MAXSEG = 8;      // backward segments per head at most
 constexpr int BWD_NF = 272;        // non-constant feature rows of the backward's states
-constexpr int BWD_RREC = BWD_NF * BWD_SLICE + BWD_NF + BWD_SLICE;  // floats of one suffix-state record
+constexpr int BWD_RREC = FWD_SLOTS * BWD_SLICE + FWD_SLOTS + BWD_SLICE;  // floats of one suffix-state record (compact slots)
 }  // namespace layout
 
 // Host-side planning (plan.cpp): sequence segments per (batch, head) and

@@ -59,64 +59,89 @@ constexpr int NKS = (NF + 31) / 32;  // 9 steps of 32 features (the last half ze
 constexpr int QH = 24;               // fp16 stride of q / k rows
 constexpr int XT = C + 8;            // fp16 stride of transposed chunk rows
 constexpr int RS = SW + 8;           // fp16 stride of slice rows
-constexpr int MAXOWN = 5;            // feature tiles owned by a wavefront (w, w+4, w+8, w+12; 16 for one)
 constexpr int SCALE_TOP = 13;
 constexpr int MAXSEG = 8;            // segments per head at most (records summed directly)
 constexpr int NFC = 160;             // compact slots of the forward's state records
-constexpr int RREC = NF * SW + NF + SW;  // floats of one suffix-state record (R, r, sum g)
+constexpr int RREC = NFC * SW + NFC + SW;  // floats of one suffix-state record (R, r in compact slots, sum g)
 constexpr int NFP = 32 * NKS;
 static_assert(C == layout::CHUNK && SW == layout::BWD_SLICE && MAXSEG == layout::BWD_MAXSEG && NF == layout::BWD_NF &&
                   NFC == layout::FWD_SLOTS && RREC == layout::BWD_RREC,
               "planning constants (plan.cpp) must match the kernels");        // feature rows of the key pass's state copy (rows NF.. zero)
 
-// Slot of the forward's compact records holding feature f of this layout
-// (f < 16: x_f; f = 16 + 16a + b: x_a x_b).  The compact layout: slot
-// r = 32 kb + 8 g + s holds pattern (kb, s) with both coordinates shifted by
-// 4g: kb = 0 gives x_a (s < 4) and x_a^2 (s >= 4) for a = s % 4; kb >= 1
-// gives x_a x_{a+d} for a = s % 4, d = 2 (kb - 1) + 1 + s / 4 (mod 16).  A
-// record holds sum_t [k_a | k_a^2 | k_a k_b] v_t in every slot.
-struct FeatureSlots {
-  int16_t slot[NF];
+// The forward's compact record layout: slot r = 32 kb + 8 g + s holds
+// pattern (kb, s) with both coordinates shifted by 4g: kb = 0 gives x_a
+// (s < 4) and x_a^2 (s >= 4) for a = s % 4; kb >= 1 gives x_a x_{a+d} for
+// a = s % 4, d = 2 (kb - 1) + 1 + s / 4 (mod 16).  A record holds
+// sum_t [k_a | k_a^2 | k_a k_b] v_t in every slot.
+
+// The states are symmetric in (a, b), so every pass accumulates them in the
+// forward's 160 compact slots and expands them to the 272 rows of this
+// layout only in the fp16 copy the readouts use.  Per slot r, packed: the
+// two transposed-chunk rows whose product is its feature (bits 0-4, 5-9; row
+// DK holds ones, the linear slots' second factor) and the one or two rows of
+// this layout that hold it (bits 10-18, 19-27; NOROW for none): x_a x_b and
+// x_b x_a for a pair, one row for a linear feature, a square, or a pair at
+// distance 8 (whose two orientations are both slots).
+constexpr int NCT = NFC / 16;  // compact slot tiles
+constexpr int MAXC = 3;        // compact slot tiles owned by a wavefront
+constexpr uint32_t NOROW = 511;
+struct SlotInfo {
+  uint32_t x[NFC];
 };
-constexpr FeatureSlots make_feature_slots() {
-  FeatureSlots t{};
-  int sa[NFC] = {}, sb[NFC] = {}, lin[NFC] = {};
+constexpr SlotInfo make_slot_info() {
+  SlotInfo t{};
   for (int r = 0; r < NFC; ++r) {
     const int kb = r / 32, g = (r % 32) / 8, s2 = r % 8;
-    int A = s2 % 4, B = A;
-    if (kb > 0) B = A + 2 * (kb - 1) + 1 + s2 / 4;
-    sa[r] = (A + 4 * g) % 16;
-    sb[r] = (B + 4 * g) % 16;
-    lin[r] = kb == 0 && s2 < 4;
-  }
-  for (int f = 0; f < NF; ++f) {
-    t.slot[f] = -1;
-    for (int r = 0; r < NFC && t.slot[f] < 0; ++r) {
-      if (f < 16) {
-        if (lin[r] && sa[r] == f) t.slot[f] = (int16_t)r;
-      } else {
-        const int a = (f - 16) / 16, b = (f - 16) % 16;
-        if (!lin[r] && ((sa[r] == a && sb[r] == b) || (sa[r] == b && sb[r] == a))) t.slot[f] = (int16_t)r;
-      }
+    const int A = s2 % 4, B = kb > 0 ? A + 2 * (kb - 1) + 1 + s2 / 4 : A;
+    const bool lin = kb == 0 && s2 < 4;
+    const uint32_t a = (uint32_t)((A + 4 * g) % 16), b = (uint32_t)((B + 4 * g) % 16);
+    uint32_t r1 = 0, r2 = NOROW;
+    if (lin) r1 = a;
+    else {
+      r1 = 16 + 16 * a + b;
+      if (a != b && (b + 16 - a) % 16 != 8) r2 = 16 + 16 * b + a;
     }
+    t.x[r] = a | (lin ? (uint32_t)DK : b) << 5 | r1 << 10 | r2 << 19;
   }
   return t;
 }
-constexpr FeatureSlots kSlots = make_feature_slots();
-constexpr bool slots_ok() {
+constexpr SlotInfo kSlotInfo = make_slot_info();
+// every row of this layout is written from exactly one slot
+constexpr bool slot_rows_ok() {
+  int hits[NF] = {};
+  for (int r = 0; r < NFC; ++r) {
+    const uint32_t r1 = (kSlotInfo.x[r] >> 10) & 511u, r2 = kSlotInfo.x[r] >> 19;
+    if (r1 >= (uint32_t)NF) return false;
+    ++hits[r1];
+    if (r2 != NOROW) {
+      if (r2 >= (uint32_t)NF) return false;
+      ++hits[r2];
+    }
+  }
   for (int f = 0; f < NF; ++f)
-    if (kSlots.slot[f] < 0) return false;
+    if (hits[f] != 1) return false;
   return true;
 }
-static_assert(slots_ok(), "every feature must map to a compact slot");
-__constant__ FeatureSlots c_slots = make_feature_slots();
+static_assert(slot_rows_ok(), "the compact slots must cover every feature row once");
+__constant__ SlotInfo c_sinfo = make_slot_info();
+__device__ __forceinline__ int sl_a(uint32_t x) { return (int)(x & 31u); }
+__device__ __forceinline__ int sl_b(uint32_t x) { return (int)((x >> 5) & 31u); }
+__device__ __forceinline__ int sl_r1(uint32_t x) { return (int)((x >> 10) & 511u); }
+__device__ __forceinline__ uint32_t sl_r2(uint32_t x) { return x >> 19; }
+// Compact slot tiles: wavefront w owns tiles w and w + 4, and tile
+// 8 + (w & 1) if it is one of the two that the pass's causal in-chunk work
+// leaves lightest (XLO: wavefronts 0 and 1, else 2 and 3).
+template <bool XLO>
+__device__ __forceinline__ int cown_count(int w) { return (XLO ? w < 2 : w >= 2) ? 3 : 2; }
+__device__ __forceinline__ int cown_tile(int w, int j) { return j < 2 ? w + 4 * j : 8 + (w & 1); }
+// the lane's slot info for its owned tiles (read once, from constant memory)
+template <bool XLO>
+__device__ __forceinline__ void slot_info(int w, int r16, uint32_t (&x)[MAXC]) {
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) x[j] = j < cown_count<XLO>(w) ? c_sinfo.x[16 * cown_tile(w, j) + r16] : 0u;
+}
 
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-// Wavefront w owns feature tiles w, w + 4, w + 8, w + 12; tile 16 goes to
-// wavefront xw, which each pass picks as the one its causal in-chunk work
-// leaves lightest (wavefront 0 in the query pass, 3 in the key pass).
-__device__ __forceinline__ int own_count(int w, int xw) { return w == xw ? 5 : 4; }
-__device__ __forceinline__ int own_tile(int w, int j) { return j < 4 ? w + 4 * j : 16; }
 
 __device__ __forceinline__ f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -221,7 +246,7 @@ struct Params {
   const float* frec;    // [BH][nseg * rsplit] forward records of (NFC + 1) dvf floats, record_offset layout
                         // (record s + 1: sub-segment s, seg_chunks / rsplit chunks from s * seg_chunks / rsplit)
   const float* frecz;   // [BH][nseg * rsplit][NFC + 1]
-  float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NF][SW], r [NF], sum g [SW]
+  float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NFC][SW], r [NFC] (compact slots), sum g [SW]
   int L, dvf, nslice, nseg, seg_chunks;
   int rsplit;           // forward-record sub-segments per segment
   const float* gamma;   // decayed variant: [H] per-head state decay
@@ -353,7 +378,7 @@ __device__ __forceinline__ void q_load(const Params& p, const HeadRsrc& rs, int 
 struct QSmem {
   alignas(16) half_t qh[C][QH];            // q rows
   alignas(16) half_t kh[C][QH];            // k rows
-  alignas(16) half_t kt[DK][XT];           // k^T
+  alignas(16) half_t kt[DK + 1][XT];       // k^T; row DK all ones
   alignas(16) half_t vh[C][RS];            // v rows (slice)
   alignas(16) half_t gh[C][RS], gl[C][RS];  // g hi / lo (slice)
   alignas(16) half_t st[NF][RS];           // state S, feature rows, scaled by 2^-e
@@ -431,22 +456,27 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 
   for (int e = tid; e < NF * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.st[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.zs[e] = 0.f;
-  // state S of the owned feature tiles; z as one value per lane and tile
-  // (feature 16 mt + r16: the rows of a z tile are all equal)
-  f32x4 acc[MAXOWN][2];
-  float zacc[MAXOWN];
+  for (int e = tid; e < XT; e += NTHR) S.kt[DK][e] = (half_t)1.f;
+  // state S of the owned compact slot tiles; z as one value per lane and
+  // tile (slot 16 t + r16: the rows of a z tile are all equal)
+  const int nown = cown_count<true>(w);
+  uint32_t si[MAXC];
+  slot_info<true>(w, r16, si);
+  f32x4 acc[MAXC][2];
+  float zacc[MAXC];
 #pragma unroll
-  for (int j = 0; j < MAXOWN; ++j) {
+  for (int j = 0; j < MAXC; ++j) {
     acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     zacc[j] = 0.f;
   }
   float up = 1.f;
   // largest state magnitude over the workgroup -> scale; state copy to LDS
+  // (each slot to its one or two rows)
   auto publish = [&]() {
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w, 0))
+    for (int j = 0; j < MAXC; ++j)
+      if (j < nown)
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -461,18 +491,23 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     // while e = 0, the usual case)
     auto store_copy = [&](auto scaled) {
 #pragma unroll
-      for (int j = 0; j < MAXOWN; ++j) {
-        if (j < own_count(w, 0)) {
-          const int mt = own_tile(w, j);
+      for (int j = 0; j < MAXC; ++j) {
+        if (j < nown) {
+          const int r1 = sl_r1(si[j]);
+          const uint32_t r2 = sl_r2(si[j]);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
             f32x4 a = acc[j][nn];
             if constexpr (decltype(scaled)::value) a *= down;
             const uint32_t w0 = u32(__builtin_convertvector((f32x2{a[0], a[1]}), f16x2));
             const uint32_t w1 = u32(__builtin_convertvector((f32x2{a[2], a[3]}), f16x2));
-            *reinterpret_cast<uint2*>(&S.st[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(&S.st[r1][16 * nn + 4 * g]) = make_uint2(w0, w1);
+            if (r2 != NOROW) *reinterpret_cast<uint2*>(&S.st[r2][16 * nn + 4 * g]) = make_uint2(w0, w1);
           }
-          if (g == 0) S.zs[16 * mt + r16] = zacc[j];
+          if (g == 0) {
+            S.zs[r1] = zacc[j];
+            if (r2 != NOROW) S.zs[r2] = zacc[j];
+          }
         }
       }
     };
@@ -496,9 +531,9 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.frecz + first * rows), (short)0, nr * rows * (int)sizeof(float), RSRC_DW3);
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 0)) {
-        const int slot = c_slots.slot[16 * own_tile(w, j) + r16];
+    for (int j = 0; j < MAXC; ++j) {
+      if (j < nown) {
+        const int slot = 16 * cown_tile(w, j) + r16;
         float z = 0.f;
         if (nr & 1) {  // record 1 on its own
           const float wr = rec_w(0);
@@ -712,20 +747,18 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
           }
       }
 #pragma unroll
-      for (int j = 0; j < MAXOWN; ++j) {
+      for (int j = 0; j < MAXC; ++j) {
         acc[j][0] *= gn;
         acc[j][1] *= gn;
         zacc[j] *= gn;
       }
     }
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 0)) {
-        const int mt = own_tile(w, j);
+    for (int j = 0; j < MAXC; ++j) {
+      if (j < nown) {  // uniform branch
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 kb = ld8(&S.kt[r16][32 * ks + 8 * g]);
-          f16x8 fb = mt == 0 ? kb : ld8(&S.kt[mt - 1][32 * ks + 8 * g]) * kb;
+          f16x8 fb = ld8(&S.kt[sl_a(si[j])][32 * ks + 8 * g]) * ld8(&S.kt[sl_b(si[j])][32 * ks + 8 * g]);
           if constexpr (DEC) fb *= wk[ks];
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
@@ -742,7 +775,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
 // ---------------------------------------------------------------- key pass
 struct KSmem {
   alignas(16) half_t qh[C][QH];              // q rows
-  alignas(16) half_t qt[DK][XT];             // q^T
+  alignas(16) half_t qt[DK + 1][XT];         // q^T; row DK all ones
   alignas(16) half_t kh[C][QH];              // k rows
   alignas(16) half_t vh[C][RS];              // v rows (slice)
   alignas(16) half_t gh[C][RS], gl[C][RS];    // g rows hi / lo (slice)
@@ -810,7 +843,7 @@ __device__ __forceinline__ void k_load(const Params& p, const HeadRsrc& rs, int 
 // r += phi(Q)^T h and sum g over its positions; the key pass of segment s
 // starts from the sum of the increments of the segments after it.
 struct KIncSmem {
-  alignas(16) half_t qt[DK][XT];
+  alignas(16) half_t qt[DK + 1][XT];  // q^T; row DK all ones
   alignas(16) half_t gh[C][RS];  // g rows (slice), fp16
   alignas(16) half_t hh[XT];     // h, fp16
   alignas(16) float gsum[C][SW];  // per-thread column sums of g (row tid / 4), summed in row order
@@ -840,9 +873,15 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   const size_t bh = un.bh;
   const int s = un.s;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index(), g = lane >> 4, r16 = lane & 15;
-  f32x4 acc[MAXOWN][2], racc[MAXOWN];
+  // the increment in compact slots (written as such: the key pass reads them
+  // into its compact accumulators)
+  const int nown = cown_count<true>(w);
+  uint32_t si[MAXC];
+  slot_info<true>(w, r16, si);
+  for (int e = tid; e < XT; e += NTHR) S.qt[DK][e] = (half_t)1.f;
+  f32x4 acc[MAXC][2], racc[MAXC];
 #pragma unroll
-  for (int j = 0; j < MAXOWN; ++j) {
+  for (int j = 0; j < MAXC; ++j) {
     acc[j][0] = acc[j][1] = racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -875,13 +914,11 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
     __syncthreads();
     if (t0 + C < un.t_end) k_load(p, rs, s, t0 + C, pf);
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 0)) {
-        const int mt = own_tile(w, j);
+    for (int j = 0; j < MAXC; ++j) {
+      if (j < nown) {  // uniform branch
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
-          const f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+          const f16x8 fb = ld8(&S.qt[sl_a(si[j])][32 * ks + 8 * g]) * ld8(&S.qt[sl_b(si[j])][32 * ks + 8 * g]);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[j][nn] = mfma(tr8(&S.gh[0][0], 32 * ks + 8 * g, 16 * nn, RS), fb, acc[j][nn]);
@@ -892,14 +929,14 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   }
   float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + un.seg) * (size_t)RREC;
 #pragma unroll
-  for (int j = 0; j < MAXOWN; ++j) {
-    if (j < own_count(w, 0)) {
-      const int f = 16 * own_tile(w, j) + r16;
+  for (int j = 0; j < MAXC; ++j) {
+    if (j < nown) {
+      const int slot = 16 * cown_tile(w, j) + r16;
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn)
-        *reinterpret_cast<float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g) =
+        *reinterpret_cast<float4*>(rec + (size_t)slot * SW + 16 * nn + 4 * g) =
             make_float4(acc[j][nn][0], acc[j][nn][1], acc[j][nn][2], acc[j][nn][3]);
-      if (g == 0) rec[(size_t)NF * SW + f] = racc[j][0];
+      if (g == 0) rec[(size_t)NFC * SW + slot] = racc[j][0];
     }
   }
   // sum g over the segment: the threads' shares added in row order (a fixed
@@ -910,7 +947,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   if (tid < SW) {
     float gs = 0.f;
     for (int r = 0; r < C; ++r) gs += S.gsum[r][tid];
-    rec[(size_t)NF * SW + NF + tid] = gs;
+    rec[(size_t)NFC * SW + NFC + tid] = gs;
   }
 }
 
@@ -949,23 +986,28 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
 
   for (int e = tid; e < NFP * RS / 2; e += NTHR) reinterpret_cast<uint32_t*>(&S.rf[0][0])[e] = 0u;
   for (int e = tid; e < NF; e += NTHR) S.rs[e] = 0.f;
+  for (int e = tid; e < XT; e += NTHR) S.qt[DK][e] = (half_t)1.f;
   if (tid < SW) S.g0[tid] = 0.f;
-  // state R of the owned feature tiles; r as one value per lane and tile
-  // (feature 16 mt + r16: the rows of an r tile are all equal)
-  f32x4 acc[MAXOWN][2];
-  float racc[MAXOWN];
+  // state R of the owned compact slot tiles; r as one value per lane and
+  // tile (slot 16 t + r16: the rows of an r tile are all equal)
+  const int nown = cown_count<false>(w);
+  uint32_t si[MAXC];
+  slot_info<false>(w, r16, si);
+  f32x4 acc[MAXC][2];
+  float racc[MAXC];
 #pragma unroll
-  for (int j = 0; j < MAXOWN; ++j) {
+  for (int j = 0; j < MAXC; ++j) {
     acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     racc[j] = 0.f;
   }
   float up = 1.f;
-  // largest state magnitude over the workgroup -> scale; both state copies to LDS
+  // largest state magnitude over the workgroup -> scale; both state copies to
+  // LDS (each slot to its one or two rows)
   auto publish = [&]() {
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j)
-      if (j < own_count(w, 3))
+    for (int j = 0; j < MAXC; ++j)
+      if (j < nown)
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -978,18 +1020,23 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     up = __builtin_amdgcn_ldexpf(1.f, e);
     auto store_copy = [&](auto scaled) {  // as in the query pass
 #pragma unroll
-      for (int j = 0; j < MAXOWN; ++j) {
-        if (j < own_count(w, 3)) {
-          const int mt = own_tile(w, j);
+      for (int j = 0; j < MAXC; ++j) {
+        if (j < nown) {
+          const int r1 = sl_r1(si[j]);
+          const uint32_t r2 = sl_r2(si[j]);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
             f32x4 a = acc[j][nn];
             if constexpr (decltype(scaled)::value) a *= down;
             const f16x2 h01 = __builtin_convertvector((f32x2{a[0], a[1]}), f16x2);
             const f16x2 h23 = __builtin_convertvector((f32x2{a[2], a[3]}), f16x2);
-            *reinterpret_cast<uint2*>(&S.rf[16 * mt + r16][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+            *reinterpret_cast<uint2*>(&S.rf[r1][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
+            if (r2 != NOROW) *reinterpret_cast<uint2*>(&S.rf[r2][16 * nn + 4 * g]) = make_uint2(u32(h01), u32(h23));
           }
-          if (g == 0) S.rs[16 * mt + r16] = racc[j];
+          if (g == 0) {
+            S.rs[r1] = racc[j];
+            if (r2 != NOROW) S.rs[r2] = racc[j];
+          }
         }
       }
     };
@@ -1004,18 +1051,18 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
       // decayed: segment r starts (r - seg - 1) segments after this one ends
       const float wr = DEC ? gpow(lg, (float)((r - un.seg - 1) * p.seg_chunks * C)) : 1.f;
 #pragma unroll
-      for (int j = 0; j < MAXOWN; ++j) {
-        if (j < own_count(w, 3)) {
-          const int f = 16 * own_tile(w, j) + r16;
+      for (int j = 0; j < MAXC; ++j) {
+        if (j < nown) {
+          const int slot = 16 * cown_tile(w, j) + r16;
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) {
-            const float4 x = *reinterpret_cast<const float4*>(rec + (size_t)f * SW + 16 * nn + 4 * g);
+            const float4 x = *reinterpret_cast<const float4*>(rec + (size_t)slot * SW + 16 * nn + 4 * g);
             acc[j][nn] += wr * f32x4{x.x, x.y, x.z, x.w};
           }
-          racc[j] += wr * rec[(size_t)NF * SW + f];
+          racc[j] += wr * rec[(size_t)NFC * SW + slot];
         }
       }
-      if (tid < SW) g0 += wr * rec[(size_t)NF * SW + NF + tid];
+      if (tid < SW) g0 += wr * rec[(size_t)NFC * SW + NFC + tid];
     }
     if (tid < SW) S.g0[tid] = g0;
     publish();
@@ -1165,22 +1212,20 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     const float gC = DEC ? gpow(lg, (float)C) : 1.f;
     if constexpr (DEC) {
 #pragma unroll
-      for (int j = 0; j < MAXOWN; ++j) {
+      for (int j = 0; j < MAXC; ++j) {
         acc[j][0] *= gC;
         acc[j][1] *= gC;
         racc[j] *= gC;
       }
     }
 #pragma unroll
-    for (int j = 0; j < MAXOWN; ++j) {
-      if (j < own_count(w, 3)) {
-        const int mt = own_tile(w, j);
+    for (int j = 0; j < MAXC; ++j) {
+      if (j < nown) {  // uniform branch
         // g and h rounded once to fp16 (the state is read back as an fp16 copy)
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 qb = ld8(&S.qt[r16][32 * ks + 8 * g]);
-          f16x8 fb = mt == 0 ? qb : ld8(&S.qt[mt - 1][32 * ks + 8 * g]) * qb;
+          f16x8 fb = ld8(&S.qt[sl_a(si[j])][32 * ks + 8 * g]) * ld8(&S.qt[sl_b(si[j])][32 * ks + 8 * g]);
           if constexpr (DEC) fb *= ld8(&S.wq[32 * ks + 8 * g]);
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
