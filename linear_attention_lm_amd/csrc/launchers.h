@@ -26,6 +26,7 @@ constexpr int BWD_RREC = FWD_SLOTS * BWD_SLICE + FWD_SLOTS + BWD_SLICE;  // floa
 void linattn_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 void linattn_bwd_mfma_plan(int BH, int L, int dv, int* nseg, int* seg_chunks);
 int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks);
+int linattn_bwd_key_split(int BH, int dv, int nseg, int seg_chunks);
 
 struct LinattnArgs {
   const void* q; const void* k; const void* v; float* y;

@@ -246,9 +246,11 @@ struct Params {
   const float* frec;    // [BH][nseg * rsplit] forward records of (NFC + 1) dvf floats, record_offset layout
                         // (record s + 1: sub-segment s, seg_chunks / rsplit chunks from s * seg_chunks / rsplit)
   const float* frecz;   // [BH][nseg * rsplit][NFC + 1]
-  float* krec;          // [BH][nslice][nseg] suffix-state increments: R [NFC][SW], r [NFC] (compact slots), sum g [SW]
+  float* krec;          // [BH][nslice][nseg][ksplit] suffix-state increments of a segment's parts: R [NFC][SW],
+                        // r [NFC] (compact slots), sum g [SW]
   int L, dvf, nslice, nseg, seg_chunks;
   int rsplit;           // forward-record sub-segments per segment
+  int ksplit;           // suffix-state sub-records per segment ([BH][nslice][nseg][ksplit] records)
   const float* gamma;   // decayed variant: [H] per-head state decay
   int H;
 };
@@ -855,7 +857,20 @@ struct KIncSmem {
 template <int DEC>
 __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   __shared__ KIncSmem S;
-  const Unit un = unit_of(p);
+  // workgroup -> (head, slice, part): part 0 sums dq; part 1 + i is
+  // sub-record i % ksplit of segment 1 + i / ksplit (sc chunks each)
+  const int per_hs = 1 + (p.nseg - 1) * p.ksplit, sc = (p.seg_chunks + p.ksplit - 1) / p.ksplit;
+  Unit un;
+  un.bh = blockIdx.x / (p.nslice * per_hs);
+  un.s = (blockIdx.x / per_hs) % p.nslice;
+  const int part = blockIdx.x % per_hs;
+  un.seg = part == 0 ? 0 : 1 + (part - 1) / p.ksplit;
+  const int sub = part == 0 ? 0 : (part - 1) % p.ksplit;
+  {
+    const int seg_end = min(p.L, (un.seg + 1) * p.seg_chunks * C);
+    un.t_begin = min(seg_end, un.seg * p.seg_chunks * C + sub * sc * C);
+    un.t_end = min(seg_end, un.t_begin + sc * C);
+  }
   if (un.seg == 0) {
     // Nothing lies before segment 0, so its workgroups have no state to
     // form: with several slices they sum the dq shares of their head (the
@@ -927,7 +942,7 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
       }
     }
   }
-  float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + un.seg) * (size_t)RREC;
+  float* rec = p.krec + (((bh * p.nslice + s) * p.nseg + un.seg) * p.ksplit + sub) * (size_t)RREC;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     if (j < nown) {
@@ -1046,10 +1061,13 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
   // the state after the segment: the sum of the increments of the later segments
   if (un.seg < p.nseg - 1) {
     float g0 = 0.f;
-    for (int r = un.seg + 1; r < p.nseg; ++r) {
-      const float* rec = p.krec + ((bh * p.nslice + s) * p.nseg + r) * (size_t)RREC;
-      // decayed: segment r starts (r - seg - 1) segments after this one ends
-      const float wr = DEC ? gpow(lg, (float)((r - un.seg - 1) * p.seg_chunks * C)) : 1.f;
+    const int sc = (p.seg_chunks + p.ksplit - 1) / p.ksplit;
+    for (int rr = (un.seg + 1) * p.ksplit; rr < p.nseg * p.ksplit; ++rr) {
+      const int r = rr / p.ksplit, sub = rr % p.ksplit;
+      const float* rec = p.krec + (((bh * p.nslice + s) * p.nseg + r) * p.ksplit + sub) * (size_t)RREC;
+      // decayed: part sub of segment r starts (r - seg - 1) segments and sub
+      // parts after this one ends
+      const float wr = DEC ? gpow(lg, (float)((r - un.seg - 1) * p.seg_chunks * C + sub * sc * C)) : 1.f;
 #pragma unroll
       for (int j = 0; j < MAXC; ++j) {
         if (j < nown) {
@@ -1281,6 +1299,7 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
     part += (size_t)2 * p.nslice * npos * DK;
   }
   p.rsplit = linattn_bwd_rec_split((int)BH, p.nseg, p.seg_chunks);
+  p.ksplit = linattn_bwd_key_split((int)BH, a.dv, p.nseg, p.seg_chunks);
   const int nrec_seg = p.nseg * p.rsplit;  // forward-record sub-segments per head
   float* frec = part;
   p.frec = frec;
@@ -1301,8 +1320,9 @@ hipError_t launch_linattn_bwd_mfma(const LinattnBwdArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL(query_pass_kernel<0>, dim3(grid), dim3(NTHR), 0, s, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (p.nseg > 1) {
-    if (dec) hipLaunchKernelGGL(key_state_kernel<1>, dim3(grid), dim3(NTHR), 0, s, p);
-    else hipLaunchKernelGGL(key_state_kernel<0>, dim3(grid), dim3(NTHR), 0, s, p);
+    const unsigned kgrid = (unsigned)(BH * p.nslice * (1 + (p.nseg - 1) * p.ksplit));
+    if (dec) hipLaunchKernelGGL(key_state_kernel<1>, dim3(kgrid), dim3(NTHR), 0, s, p);
+    else hipLaunchKernelGGL(key_state_kernel<0>, dim3(kgrid), dim3(NTHR), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   if (dec) hipLaunchKernelGGL(key_pass_kernel<1>, dim3(grid), dim3(NTHR), 0, s, p);

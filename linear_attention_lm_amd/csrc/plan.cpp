@@ -67,6 +67,18 @@ int linattn_bwd_rec_split(int BH, int nseg, int seg_chunks) {
   return r;
 }
 
+// Suffix-state sub-records per segment: the suffix-state pass has one
+// workgroup per (head, slice, segment >= 1, sub-record) beside the B*H*slices
+// that sum dq; a segment's increment is split (down to 4 chunks) while the
+// pass stays within three workgroups per CU.
+int linattn_bwd_key_split(int BH, int dv, int nseg, int seg_chunks) {
+  const long long units = (long long)BH * (dv / BWD_SLICE) * (nseg - 1), sum_units = (long long)BH * (dv / BWD_SLICE);
+  int r = 1;
+  if (nseg < 2) return r;
+  while (r < 4 && units * 2 * r + sum_units <= 768 && seg_chunks % (2 * r) == 0 && seg_chunks / (2 * r) >= 4) r *= 2;
+  return r;
+}
+
 size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   int nseg, sc;
   const int BH = B * H;
@@ -77,7 +89,7 @@ size_t linattn_bwd_mfma_workspace(int B, int H, int L, int dv) {
   if (nseg > 1) {
     const int rs = linattn_bwd_rec_split(BH, nseg, sc);
     floats += (size_t)BH * nseg * rs * ((size_t)(FWD_SLOTS + 1) * dv + (FWD_SLOTS + 1));  // forward records
-    floats += (size_t)BH * nslice * nseg * BWD_RREC;                                        // suffix records
+    floats += (size_t)BH * nslice * nseg * linattn_bwd_key_split(BH, dv, nseg, sc) * BWD_RREC;  // suffix records
   }
   return floats * sizeof(float);
 }
