@@ -1520,6 +1520,15 @@ static hipError_t launch_state_records_nt(const void* k, const void* v, float* w
   p.wsz = ws + (size_t)BH * nseg * (NF + 1) * (16 * NT);
   p.gamma = gamma;
   p.H = H;
+  // with at most one record per two CUs, each record's value columns are
+  // split over two workgroups (same records)
+  if constexpr (NT % 4 == 0) {
+    if ((long long)BH * nrec <= 128) {
+      if (gamma) hipLaunchKernelGGL((linattn_state_kernel<NT / 2, 1, 2>), dim3(BH * nrec * 2), dim3(NTHR), 0, s, p);
+      else hipLaunchKernelGGL((linattn_state_kernel<NT / 2, 0, 2>), dim3(BH * nrec * 2), dim3(NTHR), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (gamma) hipLaunchKernelGGL((linattn_state_kernel<NT, 1>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
   else hipLaunchKernelGGL((linattn_state_kernel<NT>), dim3(BH * nrec), dim3(NTHR), 0, s, p);
   return hipGetLastError();
