@@ -729,8 +729,10 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
       *reinterpret_cast<float4*>(dst) = make_float4(dqa[0], dqa[1], dqa[2], dqa[3]);
     }
 
-    // ---- state update with the chunk: S^T += V^T phi(K), z += phi(K)^T 1
+    // ---- state update with the chunk (none after the segment's last: no
+    // later chunk reads it): S^T += V^T phi(K), z += phi(K)^T 1
     // (decayed: S^T <- gamma^n S^T + V^T diag(gamma^(n-1-j)) phi(K), z likewise)
+    if (t0 + C >= un.t_end) break;  // uniform
     f16x8 wk[2];
     if constexpr (DEC) {
       float gn;
@@ -1225,8 +1227,10 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
         *reinterpret_cast<float4*>(dv + 16 * nn) = make_float4(dva[nn][0], dva[nn][1], dva[nn][2], dva[nn][3]);
     }
 
-    // ---- state update with the chunk: R^T += G^T phi(Q), r += phi(Q)^T h
+    // ---- state update with the chunk (none after the segment's first, the
+    // last one processed): R^T += G^T phi(Q), r += phi(Q)^T h
     // (decayed: R^T <- gamma^C R^T + G^T diag(gamma^p) phi(Q), r likewise)
+    if (t0 - C < un.t_begin) break;  // uniform
     const float gC = DEC ? gpow(lg, (float)C) : 1.f;
     if constexpr (DEC) {
 #pragma unroll
