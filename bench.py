@@ -110,7 +110,7 @@ OP_SOURCES = {
 OP_KERNELS = {
     "layer": ["linattn_mfma_kernel<4, 1, 0, 0>", "linattn_state_kernel<4, 0, 1>", "seg_scan_kernel"],
     "bwd": ["query_pass_kernel", "key_pass_kernel", "key_state_kernel", "slice_sum_kernel",
-            "linattn_state_kernel<4, 0, 1>", "swa_bwd_mfma_kernel<4>"],
+            "linattn_state_kernel<4, 0, 1>", "linattn_state_kernel<2, 0, 2>", "swa_bwd_mfma_kernel<4>"],
     "decode": ["decode_step_kernel<unsigned short, 64, 273>"],
     "decode_compact": ["decode_step_kernel<unsigned short, 64, 153>"],
     "baseconv": ["baseconv_kernel"],
