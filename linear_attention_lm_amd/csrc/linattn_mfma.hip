@@ -779,6 +779,17 @@ __device__ __forceinline__ void write_phi_state(const float* t0, const float* zf
 // allows it (d_v <= 64), one otherwise.
 template <int NT> struct Occ { static constexpr int value = NT <= 4 ? 2 : 1; };
 
+// Four outputs of a position.  The one-workgroup-per-CU kernels (d_v 96,
+// 128) store them non-temporally (straight to memory, not kept in L2): the
+// 1.3B-shaped layer 143 -> 137 us; the two-per-CU kernels keep plain stores
+// (non-temporal ones made the 360M layer 3.5 us and the 32k layer 9 us
+// slower).
+template <int NT>
+__device__ __forceinline__ void store_y(float* dst, const f32x4& v) {
+  if constexpr (Occ<NT>::value == 1) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+  else *reinterpret_cast<f32x4*>(dst) = v;
+}
+
 // SWA: 0 = linear attention only; 1 = with the window attention, window 64;
 // 2 = with the window attention, any window.
 // HI: high-precision readout for an arbitrary initial state -- the query
@@ -1067,9 +1078,8 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
           const float4 c0 = *reinterpret_cast<const float4*>(&S.t0[16 * nn + 4 * g]);
-          *reinterpret_cast<float4*>(yrow + 16 * nn) =
-              make_float4((acc[nn][0] + cf * c0.x) * rden, (acc[nn][1] + cf * c0.y) * rden,
-                          (acc[nn][2] + cf * c0.z) * rden, (acc[nn][3] + cf * c0.w) * rden);
+          store_y<NT>(yrow + 16 * nn, f32x4{(acc[nn][0] + cf * c0.x) * rden, (acc[nn][1] + cf * c0.y) * rden,
+                                            (acc[nn][2] + cf * c0.z) * rden, (acc[nn][3] + cf * c0.w) * rden});
         }
       }
     }
@@ -1198,8 +1208,7 @@ __global__ __launch_bounds__(NTHR, Occ<NT>::value) void linattn_mfma_kernel(Para
         float* yrow = p.y_swa + (bh * p.L + t0 + pos) * DV + 4 * g;
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn)
-          *reinterpret_cast<float4*>(yrow + 16 * nn) =
-              make_float4(accs[nn][0] * rs_, accs[nn][1] * rs_, accs[nn][2] * rs_, accs[nn][3] * rs_);
+          store_y<NT>(yrow + 16 * nn, accs[nn] * rs_);
       }
     }
 
