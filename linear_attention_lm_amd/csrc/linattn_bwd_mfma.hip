@@ -726,7 +726,7 @@ __global__ __launch_bounds__(NTHR, 2) void query_pass_kernel(Params p) {
     }
     if (pos < n) {
       float* dst = (p.nslice == 1 ? p.gq : p.pq + (size_t)s * p.npos * DK) + ((size_t)bh * L + t0 + pos) * DK + 4 * g;
-      *reinterpret_cast<float4*>(dst) = make_float4(dqa[0], dqa[1], dqa[2], dqa[3]);
+      __builtin_nontemporal_store(dqa, reinterpret_cast<f32x4*>(dst));  // (see the key pass's stores)
     }
 
     // ---- state update with the chunk (none after the segment's last: no
@@ -1220,11 +1220,13 @@ __global__ __launch_bounds__(NTHR, 2) void key_pass_kernel(Params p) {
     }
     if (kpos < n) {
       float* dst = (p.nslice == 1 ? p.gk : p.pk + (size_t)s * p.npos * DK) + ((size_t)bh * L + t0 + kpos) * DK + 4 * g;
-      *reinterpret_cast<float4*>(dst) = make_float4(dka[0], dka[1], dka[2], dka[3]);
+      // gradients leave non-temporally (straight to memory, not kept in L2):
+      // 360M backward 206.7 -> 204.5 us, decayed 218.0 -> 214.9 us
+      __builtin_nontemporal_store(dka, reinterpret_cast<f32x4*>(dst));
       float* dv = p.gv + ((size_t)bh * L + t0 + kpos) * p.dvf + (size_t)s * SW + 4 * g;
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn)
-        *reinterpret_cast<float4*>(dv + 16 * nn) = make_float4(dva[nn][0], dva[nn][1], dva[nn][2], dva[nn][3]);
+        __builtin_nontemporal_store(dva[nn], reinterpret_cast<f32x4*>(dv + 16 * nn));
     }
 
     // ---- state update with the chunk (none after the segment's first, the
