@@ -262,10 +262,13 @@ struct Unit {
 };
 __device__ __forceinline__ Unit unit_of(const Params& p) {
   Unit u;
+  // a head's workgroups share an XCD (its L2): the slices read the same q, k
   const int per_head = p.nslice * p.nseg;
-  u.bh = blockIdx.x / per_head;
-  u.s = (blockIdx.x % per_head) / p.nseg;
-  u.seg = blockIdx.x % p.nseg;
+  int bh, part;
+  xcd_unit_part(blockIdx.x, gridDim.x / per_head, per_head, bh, part);
+  u.bh = bh;
+  u.s = part / p.nseg;
+  u.seg = part % p.nseg;
   u.t_begin = u.seg * p.seg_chunks * C;
   u.t_end = min(p.L, u.t_begin + p.seg_chunks * C);
   return u;
@@ -863,9 +866,11 @@ __global__ __launch_bounds__(NTHR) void key_state_kernel(Params p) {
   // sub-record i % ksplit of segment 1 + i / ksplit (sc chunks each)
   const int per_hs = 1 + (p.nseg - 1) * p.ksplit, sc = (p.seg_chunks + p.ksplit - 1) / p.ksplit;
   Unit un;
-  un.bh = blockIdx.x / (p.nslice * per_hs);
-  un.s = (blockIdx.x / per_hs) % p.nslice;
-  const int part = blockIdx.x % per_hs;
+  int bhi, hp;
+  xcd_unit_part(blockIdx.x, gridDim.x / (p.nslice * per_hs), p.nslice * per_hs, bhi, hp);
+  un.bh = bhi;
+  un.s = hp / per_hs;
+  const int part = hp % per_hs;
   un.seg = part == 0 ? 0 : 1 + (part - 1) / p.ksplit;
   const int sub = part == 0 ? 0 : (part - 1) % p.ksplit;
   {
