@@ -346,12 +346,11 @@ __global__ __launch_bounds__(NTHR, NT <= 4 ? 2 : 1) void swa_bwd_mfma_kernel(Par
           }
         }
         if (kg < L) {  // lane: key kpos, dims / columns 4g .. 4g + 3
-          *reinterpret_cast<float4*>(p.gk + ((size_t)bh * L + kg) * DK + 4 * g) =
-              make_float4(p.scale * dka[0], p.scale * dka[1], p.scale * dka[2], p.scale * dka[3]);
+          // gradients leave non-temporally (straight to memory): 72.6 -> 71.7 us
+          __builtin_nontemporal_store(dka * p.scale, reinterpret_cast<f32x4*>(p.gk + ((size_t)bh * L + kg) * DK + 4 * g));
 #pragma unroll
           for (int n = 0; n < NT; ++n)
-            *reinterpret_cast<float4*>(p.gv + ((size_t)bh * L + kg) * DV + 16 * n + 4 * g) =
-                make_float4(dva[n][0], dva[n][1], dva[n][2], dva[n][3]);
+            __builtin_nontemporal_store(dva[n], reinterpret_cast<f32x4*>(p.gv + ((size_t)bh * L + kg) * DV + 16 * n + 4 * g));
         }
       }
     }
@@ -390,8 +389,7 @@ __global__ __launch_bounds__(NTHR, NT <= 4 ? 2 : 1) void swa_bwd_mfma_kernel(Par
         const int qg = c * C + 16 * w + r16;
         if (qg < L) {
           const f32x4 t = carry + share[0];
-          *reinterpret_cast<float4*>(p.gq + ((size_t)bh * L + qg) * DK + 4 * g) =
-              make_float4(p.scale * t[0], p.scale * t[1], p.scale * t[2], p.scale * t[3]);
+          __builtin_nontemporal_store(t * p.scale, reinterpret_cast<f32x4*>(p.gq + ((size_t)bh * L + qg) * DK + 4 * g));
         }
       }
       carry = share[1];
