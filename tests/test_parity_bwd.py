@@ -103,6 +103,15 @@ def test_bwd_full_size_sampled_heads(based, name, heads):
     run_case(based, cfg, "swa", heads)
 
 
+def test_bwd_split_records_ragged_end(based):
+    """B 8, H 16, L 2000: two segments whose forward record is split over two
+    half-width workgroups and whose suffix-state increment is split into two
+    sub-records, the second ending inside a chunk (L is not a multiple of 64);
+    the oracle on two heads."""
+    cfg = synth.FWD_CONFIGS["based360m"].replace(L=2000, name="split2000")
+    run_case(based, cfg, "lin", [(0, 0), (7, 15)])
+
+
 def test_bwd_long_sampled_rows(based):
     """32k positions: the window backward on whole sampled heads; the linear
     attention backward at sampled positions (row-wise oracle)."""

@@ -242,6 +242,29 @@ def test_decay_bwd_360m_sampled_heads(based):
             assert err <= TOL[q.dtype], (name, err)
 
 
+def test_decay_bwd_split_records_ragged_end(based):
+    """The decayed backward at B 8, H 16, L 2000: split forward records and
+    suffix-state sub-records weighted by their distance, the last one ending
+    inside a chunk; the oracle on two heads."""
+    from parity_util import row_rel_floor
+    cfg = synth.FWD_CONFIGS["based360m"].replace(L=2000, name="split2000")
+    q, k, v = synth.fwd_inputs(cfg, 0)
+    dy = synth.upstream_grad(cfg, 0)
+    g = synth.decay_rates(cfg.H)
+    say("decay bwd split2000")
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    y = based.linattn_decay_fwd(qd, kd, vd, gd)
+    grads = based.linattn_decay_bwd(qd, kd, vd, gd, y, dy.to(DEV))
+    torch.cuda.synchronize()
+    for b, h in ((0, 1), (6, 13)):
+        refs = O.linattn_decay_bwd(q[b, h][None], k[b, h][None], v[b, h][None], g[h:h + 1].numpy(), dy[b, h][None])
+        for name, gr, r in zip(("dq", "dk", "dv"), grads, refs):
+            zero = 1 if name == "dq" else 0
+            err = row_rel_floor(gr[b, h, zero:][None], r[:, zero:], FLOOR[q.dtype])
+            report(f"decay bwd split2000 head ({b},{h}) {name}", err, TOL[q.dtype])
+            assert err <= TOL[q.dtype], (name, err)
+
+
 # ------------------------------------------------ the range of gamma
 # Out-of-range decays read as their clamped values: NaN and negatives as 0,
 # values above 1 as 1.  gamma = 0 leaves each position its own term (y = v).
