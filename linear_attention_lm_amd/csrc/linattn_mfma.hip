@@ -290,8 +290,12 @@ __device__ __forceinline__ HeadRsrc head_rsrc(const Params& p, size_t bh, int DV
   return r;
 }
 
+// 16-byte loads of the chunk inputs and the segment records, with the
+// non-temporal hint (cache policy bit 1): each is read by few workgroups,
+// and streaming them leaves the L2 to the rest; 32k layer 147 -> 137-143 us,
+// 1.3B 135 -> 133.6 us, 360M unchanged (three A/B pairs on one box)
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
 }
 
 // Thread -> (position, 8 columns) of the v loads: consecutive threads take
