@@ -15,7 +15,10 @@
 // quadratic block of every state is symmetric in (a, b) and the Jacobian
 // contractions are lane-local: a lane holding u[(b, a)] for its four a and
 // every b adds u[(b, a)] x_b into the gradient of x_a.  The 1/2 of the
-// quadratic term sits on the side that is not differentiated.
+// quadratic term sits on the side that is not differentiated.  The states
+// are accumulated in the 160 compact slots of the forward's records (one per
+// unordered pair) and expanded to these rows only in the fp16 copies that the
+// readouts and contractions read.
 //
 // Passes (chunks of 64 positions; one workgroup of 4 wavefronts per (head,
 // slice of 32 value columns); with several slices each writes its dq and dk
