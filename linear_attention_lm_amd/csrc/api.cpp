@@ -183,6 +183,8 @@ static int layer_fwd_impl(const void* q, const void* k, const void* v, const flo
   if (L == 0 && !S_out) return BASED_OK;
   if (dtype == BASED_BF16 && based::linattn_mfma_supported(d_v))
     return status_of(based::launch_layer_mfma(a, y_swa, window, scale, (hipStream_t)stream));
+  if (based::layer_valu_fused(a))
+    return status_of(based::launch_layer_valu(a, y_swa, window, scale, dtype == BASED_BF16, (hipStream_t)stream));
   if (int st = status_of(based::launch_linattn_valu(a, dtype == BASED_BF16, (hipStream_t)stream)); st != BASED_OK)
     return st;
   if (L == 0) return BASED_OK;

@@ -38,6 +38,11 @@ struct LinattnArgs {
 
 // fp32 (and generic) chunked linear attention on the vector ALUs.
 hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t stream);
+// Both attentions of the layer in one vector-ALU pass (short sequences
+// without a state argument: layer_valu_fused), the window's output in y_swa.
+bool layer_valu_fused(const LinattnArgs& a);
+hipError_t launch_layer_valu(const LinattnArgs& a, float* y_swa, int window, float scale, bool bf16,
+                             hipStream_t stream);
 
 // bf16 chunked linear attention on the matrix cores (d_v in {32, 64, 96, 128}).
 bool linattn_mfma_supported(int dv);

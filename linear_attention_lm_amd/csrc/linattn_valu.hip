@@ -321,15 +321,22 @@ constexpr int QB = 32;            // queries per workgroup (and keys per block)
 constexpr int QNT = 256;          // threads: 8 lanes per query
 constexpr int QG = QNT / QB;
 constexpr int QUAD_MAX_L = 512;   // longest sequence that takes this form
-template <typename T, int DV, int DEC>
+// SWA: the fused layer pass -- the window softmax of the same queries
+// (scores s = scale q.k over keys i - window + 1 .. i, the window attention's
+// definition: HazyResearch/based README, introduction) from the same q.k of
+// the key blocks that reach into the workgroup's windows, with a running
+// maximum per query (earlier sums rescaled when it grows), into y_swa.
+template <typename T, int DV, int DEC, int SWA = 0>
 __global__ __launch_bounds__(QNT) void linattn_quad_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                           const T* __restrict__ v, float* __restrict__ y, int L,
-                                                          const float* gamma, int H) {
+                                                          const float* gamma, int H, float* __restrict__ y_swa = nullptr,
+                                                          int window = 0, float scale = 0.f) {
   constexpr int CPL = DV / QG;  // value columns per lane, contiguous
   static_assert(DV % (2 * QG) == 0, "pairs of columns per lane");
   __shared__ float Ks[QB][DK + 1];
   __shared__ float Vs[QB][DV];
   __shared__ float W[QB][QB + 1];  // [query][key] weights of the current key block
+  __shared__ float Ws[SWA ? QB : 1][QB + 1];  // window softmax weights of the block
 
   const int nblk = (L + QB - 1) / QB;
   const int bh = blockIdx.x / nblk, i0 = (blockIdx.x % nblk) * QB;
@@ -363,6 +370,11 @@ __global__ __launch_bounds__(QNT) void linattn_quad_kernel(const T* __restrict__
   float num[CPL], den = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) num[c] = 0.f;
+  // window softmax: running maximum (base-2 scores), sum and weighted sums
+  const float c2 = scale * 1.4426950408889634f;
+  float msw = -INFINITY, dsw = 0.f, nsw[SWA ? CPL : 1];
+#pragma unroll
+  for (int c = 0; c < (SWA ? CPL : 1); ++c) nsw[c] = 0.f;
   for (int j0 = 0; j0 <= i0; j0 += QB) {
     __syncthreads();  // the previous block's reads done
 #pragma unroll
@@ -378,15 +390,42 @@ __global__ __launch_bounds__(QNT) void linattn_quad_kernel(const T* __restrict__
     if (j0 + QB <= i0) prefetch(j0 + QB);
     __syncthreads();
     // this lane's keys j = g + QG m of the block
+    // (uniform: the block reaches into the window of the workgroup's first query)
+    const bool swa_live = SWA && j0 + QB - 1 > i0 - window;
+    float xs[QB / QG];
 #pragma unroll
     for (int m = 0; m < QB / QG; ++m) {
       const int j = g + QG * m, kpos = j0 + j;
       float x = 0.f;
 #pragma unroll
       for (int d = 0; d < DK; ++d) x = __builtin_fmaf(qr[d], Ks[j][d], x);
+      xs[m] = x;
       float w = kpos <= qpos && kpos < L ? 1.f + x + 0.5f * x * x : 0.f;
       if (DEC && kpos <= qpos) w *= exp2f(lg * (float)(qpos - kpos));
       W[i][j] = w;
+    }
+    if constexpr (SWA) {
+      if (swa_live) {
+        float sc[QB / QG], bm = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < QB / QG; ++m) {
+          const int kpos = j0 + g + QG * m;
+          sc[m] = kpos <= qpos && qpos - kpos < window && kpos < L ? c2 * xs[m] : -INFINITY;
+          bm = fmaxf(bm, sc[m]);
+        }
+        // the maximum over the query's QG lanes (consecutive threads)
+#pragma unroll
+        for (int o = 1; o < QG; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+        const float mn = fmaxf(msw, bm);
+        // earlier sums rescaled to the new maximum (none yet: all zero)
+        const float rs = mn == -INFINITY || msw == -INFINITY ? 0.f : exp2f(msw - mn);
+        dsw *= rs;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) nsw[c] *= rs;
+        msw = mn;
+#pragma unroll
+        for (int m = 0; m < QB / QG; ++m) Ws[i][g + QG * m] = sc[m] == -INFINITY ? 0.f : exp2f(sc[m] - mn);
+      }
     }
     __syncthreads();
     // the block's share, summed apart before it joins the running sums
@@ -406,21 +445,68 @@ __global__ __launch_bounds__(QNT) void linattn_quad_kernel(const T* __restrict__
     den += db;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) num[c] += nb[c];
+    if constexpr (SWA) {
+      if (swa_live) {
+        for (int j = 0; j < QB; ++j) {
+          const float w = Ws[i][j];
+          dsw += w;
+#pragma unroll
+          for (int c = 0; c < CPL; c += 2) {
+            const float2 vv = *reinterpret_cast<const float2*>(&Vs[j][CPL * g + c]);
+            nsw[c] = __builtin_fmaf(w, vv.x, nsw[c]);
+            nsw[c + 1] = __builtin_fmaf(w, vv.y, nsw[c + 1]);
+          }
+        }
+      }
+    }
   }
   if (qpos < L) {
     const float rd = 1.f / den;
     float* yr = y + ((size_t)bh * L + qpos) * DV + CPL * g;
 #pragma unroll
     for (int c = 0; c < CPL; c += 2) *reinterpret_cast<float2*>(yr + c) = make_float2(num[c] * rd, num[c + 1] * rd);
+    if constexpr (SWA) {
+      const float rw = 1.f / dsw;  // key qpos is always in its window: dsw >= 1
+      float* ys = y_swa + ((size_t)bh * L + qpos) * DV + CPL * g;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 2)
+        *reinterpret_cast<float2*>(ys + c) = make_float2(nsw[c] * rw, nsw[c + 1] * rw);
+    }
   }
 }
 
 template <typename T, int DV, int DEC>
-hipError_t launch_quad(const LinattnArgs& a, hipStream_t s) {
+hipError_t launch_quad(const LinattnArgs& a, hipStream_t s, float* y_swa = nullptr, int window = 0,
+                       float scale = 0.f) {
   const unsigned nblk = (unsigned)((a.L + QB - 1) / QB);
-  hipLaunchKernelGGL((linattn_quad_kernel<T, DV, DEC>), dim3(nblk * (unsigned)(a.B * a.H)), dim3(QNT), 0, s,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.L, a.gamma, a.H);
+  if (y_swa)
+    hipLaunchKernelGGL((linattn_quad_kernel<T, DV, DEC, 1>), dim3(nblk * (unsigned)(a.B * a.H)), dim3(QNT), 0, s,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.L, a.gamma, a.H, y_swa, window, scale);
+  else
+    hipLaunchKernelGGL((linattn_quad_kernel<T, DV, DEC>), dim3(nblk * (unsigned)(a.B * a.H)), dim3(QNT), 0, s,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.y, a.L, a.gamma, a.H, nullptr, 0, 0.f);
   return hipGetLastError();
+}
+
+// The fused layer pass on the vector ALUs (both attentions from one pass
+// over the key blocks): short sequences without a state argument.
+template <typename T, int DV>
+hipError_t launch_layer_dv(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+  return a.gamma ? launch_quad<T, DV, 1>(a, s, y_swa, window, scale) : launch_quad<T, DV, 0>(a, s, y_swa, window, scale);
+}
+template <typename T>
+hipError_t launch_layer_t(const LinattnArgs& a, float* y_swa, int window, float scale, hipStream_t s) {
+  switch (a.dv) {
+    case 16: return launch_layer_dv<T, 16>(a, y_swa, window, scale, s);
+    case 32: return launch_layer_dv<T, 32>(a, y_swa, window, scale, s);
+    case 48: return launch_layer_dv<T, 48>(a, y_swa, window, scale, s);
+    case 64: return launch_layer_dv<T, 64>(a, y_swa, window, scale, s);
+    case 80: return launch_layer_dv<T, 80>(a, y_swa, window, scale, s);
+    case 96: return launch_layer_dv<T, 96>(a, y_swa, window, scale, s);
+    case 112: return launch_layer_dv<T, 112>(a, y_swa, window, scale, s);
+    case 128: return launch_layer_dv<T, 128>(a, y_swa, window, scale, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int DV, int DVS, int DEC>
@@ -466,6 +552,13 @@ hipError_t launch_t(const LinattnArgs& a, hipStream_t s) {
 
 hipError_t launch_linattn_valu(const LinattnArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_t<bf16_t>(a, s) : launch_t<float>(a, s);
+}
+
+bool layer_valu_fused(const LinattnArgs& a) { return !a.S_in && !a.S_out && a.L >= 1 && a.L <= QUAD_MAX_L; }
+
+hipError_t launch_layer_valu(const LinattnArgs& a, float* y_swa, int window, float scale, bool bf16, hipStream_t s) {
+  if (!layer_valu_fused(a) || !y_swa) return hipErrorInvalidValue;
+  return bf16 ? launch_layer_t<bf16_t>(a, y_swa, window, scale, s) : launch_layer_t<float>(a, y_swa, window, scale, s);
 }
 
 }  // namespace based

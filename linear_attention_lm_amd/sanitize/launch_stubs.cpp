@@ -12,6 +12,8 @@ hipError_t none() { return hipErrorNotSupported; }
 }  // namespace
 
 hipError_t launch_linattn_valu(const LinattnArgs&, bool, hipStream_t) { return none(); }
+bool layer_valu_fused(const LinattnArgs&) { return false; }
+hipError_t launch_layer_valu(const LinattnArgs&, float*, int, float, bool, hipStream_t) { return none(); }
 hipError_t launch_linattn_mfma(const LinattnArgs&, hipStream_t) { return none(); }
 hipError_t launch_linattn_decay_mfma(const LinattnArgs&, hipStream_t) { return none(); }
 hipError_t launch_linattn_state_records(const void*, const void*, float*, int, int, int, int, int, int, const float*,

@@ -82,6 +82,70 @@ def test_layer_segments_and_window(based):
     check_layer(based, synth.FwdConfig("seg", B=1, H=1, L=8192 + 37, dv=64), window=5)
 
 
+def check_layer_vector_fused(based, cfg, window=64, scale=1.0, decay=False, seed=0):
+    """The vector path's one-pass layer (short sequences, no state argument):
+    y_lin and y_swa against the oracle and against the separate calls."""
+    q, k, v = synth.fwd_inputs(cfg, seed)
+    say(f"vector layer {cfg.name} B{cfg.B} H{cfg.H} L{cfg.L} dv{cfg.dv} {cfg.dtype} window{window} scale{scale}"
+        f" decay{int(decay)}")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    if decay:
+        g = synth.decay_rates(cfg.H)
+        y_lin, y_swa = based.layer_decay_fwd(qd, kd, vd, g.to(DEV), window, scale)
+        y_sep = based.linattn_decay_fwd(qd, kd, vd, g.to(DEV))
+    else:
+        y_lin, y_swa = based.layer_fwd(qd, kd, vd, window, scale)
+        y_sep = based.linattn_fwd(qd, kd, vd)
+    s_sep = based.swa_fwd(qd, kd, vd, window, scale)
+    torch.cuda.synchronize()
+    tol = TOL[q.dtype]
+    # y_lin: the separate call takes the same one-pass form (1e-6); y_swa: the
+    # separate window kernel sums and exponentiates differently (fp32), or
+    # runs on the matrix cores (bf16), so the oracle's tolerance
+    for name, got, sep, bound in (("y_lin", y_lin, y_sep, 1e-6), ("y_swa", y_swa, s_sep, tol)):
+        gap = rowinf_rel(got, sep.double().cpu().numpy())
+        report(f"vector layer {name} vs the separate call {cfg.name}", gap, bound)
+        assert gap <= bound
+    if decay:
+        y_ref = O.linattn_decay_quadratic(q, k, v, g.numpy())[0]
+    else:
+        y_ref = O.linattn_chunked(q, k, v, 64)[0]
+    err = rowinf_rel(y_lin, y_ref)
+    report(f"vector layer y_lin {cfg.name}", err, tol)
+    assert err <= tol
+    err = rowinf_rel(y_swa, O.swa(q, k, v, window, scale))
+    report(f"vector layer y_swa {cfg.name} w{window}", err, tol)
+    assert err <= tol
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 63, 64, 65, 130, 256, 300, 512])
+def test_layer_vector_fused_lengths(based, L):
+    """fp32, lengths around the 32-query blocks up to the longest one-pass
+    length (512)."""
+    check_layer_vector_fused(based, SMALL.replace(L=L, dtype="f32", name=f"L{L}"))
+
+
+@pytest.mark.parametrize("window,scale", [(1, 1.0), (17, 0.37), (33, 2.0), (63, 1.0), (64, 0.25)])
+def test_layer_vector_fused_windows(based, window, scale):
+    check_layer_vector_fused(based, SMALL.replace(L=300, dtype="f32", name=f"w{window}"), window, scale)
+
+
+@pytest.mark.parametrize("dtype,dv", [("f32", 16), ("f32", 128), ("bf16", 48), ("bf16", 112)])
+def test_layer_vector_fused_value_dims(based, dtype, dv):
+    """Other widths; bf16 inputs at the widths the matrix-core pass does not take."""
+    check_layer_vector_fused(based, SMALL.replace(L=200, dtype=dtype, dv=dv, name=f"dv{dv}"))
+
+
+@pytest.mark.parametrize("L", [45, 512])
+def test_layer_vector_fused_decay(based, L):
+    check_layer_vector_fused(based, SMALL.replace(L=L, dtype="f32", name=f"decay{L}"), 64, 1.0, decay=True)
+
+
+def test_layer_vector_fused_tiny_config(based):
+    """The tiny fp32 workload (B 1, H 2, L 256) as the bench times it."""
+    check_layer_vector_fused(based, synth.FWD_CONFIGS["tiny"])
+
+
 def test_layer_resume_state(based):
     """The linear-attention state threads through layer calls like through
     based_linattn_fwd (the window restarts with each call)."""
