@@ -283,8 +283,9 @@ int based_baseconv_fwd(const void* x, const void* u, const float* h, const float
  *   window, scale: as for based_swa_fwd.
  * Neither output may overlap an input, a state or the other output.
  * BASED_BF16 with d_v in {32, 64, 96, 128} is one fused matrix-core pass (with
- * the input ranges of based_linattn_fwd); otherwise the two attentions run
- * as separate kernels.
+ * the input ranges of based_linattn_fwd); otherwise L <= 512 with no S_in and
+ * no S_out is one fused vector pass (fp32 arithmetic), and the rest runs the
+ * two attentions as separate kernels.
  */
 int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, float* y_swa,
                     const float* S_in, const float* z_in, float* S_out, float* z_out,
@@ -298,7 +299,8 @@ int based_layer_fwd(const void* q, const void* k, const void* v, float* y_lin, f
  * (y_swa) has no decay.  Every other argument, and the workspace size, as for
  * based_layer_fwd; BASED_ERR_NULL for a null gamma, BASED_ERR_ALIAS when
  * gamma overlaps an output.  BASED_BF16 with d_v in {32, 64, 96, 128} is one
- * fused matrix-core pass; otherwise the two attentions run as separate
+ * fused matrix-core pass; otherwise L <= 512 with no S_in and no S_out is one
+ * fused vector pass, and the rest runs the two attentions as separate
  * kernels.
  */
 int based_layer_decay_fwd(const void* q, const void* k, const void* v, const float* gamma, float* y_lin,
